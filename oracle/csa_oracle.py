@@ -1,0 +1,368 @@
+"""Plain CPU fp64 oracle for CSA / HCA hybrid compressed attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only the test-suite, the package smoke check and the
+benchmark's CPU-baseline leg use it.  It shares no code with the HIP library.
+
+Every function is a direct, unblocked statement of a definition from the
+pages, in float64 numpy.  A library primitive (matmul, argsort, exp) may serve
+as a step; there is no fusion or reordering beyond what the definition states.
+
+Citation keys used below (page title, then where on the page):
+  [R]  "DeepSeek-V4 技术解读报告" (juejin.cn/post/7631898635937497134),
+       section 2.3 "混合注意力架构 (CSA + HCA)", equations 9-23 and 27.
+  [A]  "DeepSeek-V4：算法架构" (1zeryu.github.io/p/deepseek-v4/), the
+       "Q, K, V 映射与位置编码注入", "Sparse Attention", "CSA 选择器层代码
+       实现" (classes Compressor and Indexer), "HCA 选择函数代码实现" and
+       "输出投影" code excerpts.
+
+Readings where the pages are silent or ambiguous (each is also listed in the
+design notes of the repository):
+  * visibility: compressed entry s is visible to 0-indexed query t iff
+    s < floor((t+1)/m), i.e. its block ends at or before t ([A] Indexer causal
+    mask; [R] eq 16 read with a 1-indexed t);
+  * overlap column packing: the first c columns of an overlapped projection
+    are the b-series (feed block i+1), the last c the a-series ([A] Compressor
+    constructor comment and overlap transform);
+  * window: the n_win most recent positions including t itself;
+  * RoPE: adjacent pairs (2p, 2p+1) of the last r dims, angle pos*theta^(-2p/r);
+    entry i sits at position m*i; the output is rotated back by -t;
+  * QK-RMSNorm has unit weight; core-attention scale is passed in (c^-1/2);
+  * rounding (bf16 configs): pooling / norm / RoPE in high precision, one
+    round-to-nearest-even at store; attention output rounded once.
+
+Parity pins for every function live in tests/test_oracle_pins.py.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F64 = np.float64
+
+
+# ---------------------------------------------------------------------------
+# number formats
+# ---------------------------------------------------------------------------
+def round_bf16(x):
+    """Round float64 values to the nearest bfloat16 (ties to even), returned
+    as float64.  bfloat16 keeps 8 significant bits and fp32's exponent range;
+    frexp gives x = f * 2**e with 0.5 <= |f| < 1, so rounding f*2**8 to an
+    integer (numpy rounds half to even) keeps exactly 8 significant bits.
+    Values in fp32's subnormal range are not produced by any workload here."""
+    x = np.asarray(x, dtype=F64)
+    f, e = np.frexp(x)
+    r = np.ldexp(np.round(f * 256.0), e - 8)
+    big = np.abs(r) > 3.3895313892515355e38  # beyond bf16's largest finite
+    return np.where(big, np.copysign(np.inf, x), r)
+
+
+def round_to(x, dtype: str):
+    """One rounding to the storage type ('f32' or 'bf16'), back in float64."""
+    if dtype == "f32":
+        return np.asarray(x, dtype=F64).astype(np.float32).astype(F64)
+    if dtype == "bf16":
+        return round_bf16(x)
+    if dtype == "f64":
+        return np.asarray(x, dtype=F64)
+    raise ValueError(dtype)
+
+
+# ---------------------------------------------------------------------------
+# O1: projections  ([R] eq 9-10 for CSA, eq 20-21 for HCA)
+# ---------------------------------------------------------------------------
+def project(H, W):
+    """C = H . W (and Z = H . W_Z): rows are tokens, columns channels."""
+    return np.asarray(H, F64) @ np.asarray(W, F64)
+
+
+# ---------------------------------------------------------------------------
+# O2: block softmax pooling  ([R] eq 11-12, eq 22-23; [A] Compressor)
+# ---------------------------------------------------------------------------
+def pool_terms(C, Z, ape, m: int, overlap: bool):
+    """The logits and values that enter each compressed entry.
+
+    Returns (logits, values), both [n_c, L, c] with L = m (no overlap) or
+    2m (overlap).  For overlap, rows 0..m-1 of L are block i's a-series
+    (Z_a + B_a, C_a) and rows m..2m-1 are block i-1's b-series
+    (Z_b + B_b, C_b); for i = 0 the b-terms are -inf logits with zero values
+    ([R] text under eq 12).  Only complete blocks are pooled."""
+    C = np.asarray(C, F64)
+    Z = np.asarray(Z, F64)
+    ape = np.asarray(ape, F64)
+    n = C.shape[0]
+    nc = n // m
+    if not overlap:
+        c = C.shape[1]
+        vals = C[: nc * m].reshape(nc, m, c)
+        logits = Z[: nc * m].reshape(nc, m, c) + ape[None, :, :]
+        return logits, vals
+    c = C.shape[1] // 2
+    Cb, Ca = C[:, :c], C[:, c:]
+    Zb, Za = Z[:, :c], Z[:, c:]
+    Bb, Ba = ape[:, :c], ape[:, c:]
+    la = Za[: nc * m].reshape(nc, m, c) + Ba[None]
+    va = Ca[: nc * m].reshape(nc, m, c)
+    lb = np.full((nc, m, c), -np.inf)
+    vb = np.zeros((nc, m, c))
+    if nc > 1:
+        lb[1:] = Zb[: (nc - 1) * m].reshape(nc - 1, m, c) + Bb[None]
+        vb[1:] = Cb[: (nc - 1) * m].reshape(nc - 1, m, c)
+    return np.concatenate([la, lb], axis=1), np.concatenate([va, vb], axis=1)
+
+
+def softmax(x, axis):
+    """Softmax with the maximum subtracted (exact in exact arithmetic)."""
+    x = np.asarray(x, F64)
+    mx = np.max(x, axis=axis, keepdims=True)
+    e = np.exp(x - mx)
+    return e / np.sum(e, axis=axis, keepdims=True)
+
+
+def pool_weights(C, Z, ape, m, overlap):
+    """S of eq 11 / eq 22: per (block, channel) softmax over its L rows."""
+    logits, _ = pool_terms(C, Z, ape, m, overlap)
+    return softmax(logits, axis=1)
+
+
+def pool(C, Z, ape, m, overlap):
+    """C^Comp_i = sum_j S_j (.) C_j  (eq 12 / eq 23) for every complete block."""
+    logits, vals = pool_terms(C, Z, ape, m, overlap)
+    return np.sum(softmax(logits, axis=1) * vals, axis=1)
+
+
+# ---------------------------------------------------------------------------
+# O3: entry epilogue - QK RMSNorm and partial RoPE ([R] 2.3.3; [A] Compressor)
+# ---------------------------------------------------------------------------
+def rms_norm(x, eps):
+    """x / sqrt(mean(x^2) + eps) over the last axis, unit weight."""
+    x = np.asarray(x, F64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+def rope(x, pos, rope_dims: int, theta: float, inverse: bool = False):
+    """Rotate the last `rope_dims` channels of x by position `pos`.
+
+    Pairs are adjacent channels (2p, 2p+1) of that tail, rotated by the angle
+    pos * theta^(-2p/r) (negated when inverse).  `pos` broadcasts against the
+    leading axes of x (one position per row)."""
+    x = np.array(x, F64, copy=True)
+    r = rope_dims
+    if r == 0:
+        return x
+    c = x.shape[-1]
+    pos = np.asarray(pos, F64)
+    p = np.arange(r // 2, dtype=F64)
+    freq = theta ** (-2.0 * p / r)
+    ang = pos[..., None] * freq  # [..., r/2]
+    if inverse:
+        ang = -ang
+    cos, sin = np.cos(ang), np.sin(ang)
+    while cos.ndim < x.ndim:  # broadcast over any axes between rows and channels
+        cos = cos[..., None, :]
+        sin = sin[..., None, :]
+    x0 = x[..., c - r :: 2].copy()
+    x1 = x[..., c - r + 1 :: 2].copy()
+    x[..., c - r :: 2] = x0 * cos - x1 * sin
+    x[..., c - r + 1 :: 2] = x0 * sin + x1 * cos
+    return x
+
+
+def entry_epilogue(x, positions, qk_norm, eps, rope_dims, theta, store):
+    """Normalise, rotate at the entry's position, round once to storage."""
+    y = rms_norm(x, eps) if qk_norm else np.asarray(x, F64)
+    y = rope(y, positions, rope_dims, theta)
+    return round_to(y, store)
+
+
+def compress_prefill(H, W_kv, W_z, ape, m, overlap, qk_norm=True, eps=1e-6,
+                     rope_dims=0, theta=10000.0, store="f32"):
+    """Compressed entries of one sequence: O1 -> O2 -> O3.  Entry i sits at
+    position m*i for RoPE ([A] Compressor: positions 0, m, 2m, ...)."""
+    C = project(H, W_kv)
+    Z = project(H, W_z)
+    ent = pool(C, Z, ape, m, overlap)
+    pos = m * np.arange(ent.shape[0], dtype=F64)
+    return entry_epilogue(ent, pos, qk_norm, eps, rope_dims, theta, store)
+
+
+def window_rows(H, W_win, qk_norm=True, eps=1e-6, rope_dims=0, theta=10000.0,
+                store="f32", pos0=0):
+    """Uncompressed per-token KV for the sliding window ([A] attention wkv ->
+    kv_norm -> RoPE at the token's own position)."""
+    V = project(H, W_win)
+    pos = pos0 + np.arange(V.shape[0], dtype=F64)
+    return entry_epilogue(V, pos, qk_norm, eps, rope_dims, theta, store)
+
+
+# ---------------------------------------------------------------------------
+# O5 / O6: lightning indexer and top-k  ([R] eq 16-17; [A] Indexer)
+# ---------------------------------------------------------------------------
+def visible_entries(t, m):
+    """Number of compressed entries visible to 0-indexed token t."""
+    return (np.asarray(t) + 1) // m
+
+
+def index_scores(qI, wI, KI, m, t0=0):
+    """I[t, s] = sum_h w[t,h] * ReLU(q[t,h] . K[s]) for visible s, -inf
+    otherwise.  qI [n, hI, cI], wI [n, hI], KI [n_e, cI]; rows are tokens
+    t0 .. t0+n-1."""
+    qI = np.asarray(qI, F64)
+    wI = np.asarray(wI, F64)
+    KI = np.asarray(KI, F64)
+    dots = np.einsum("thd,sd->ths", qI, KI)
+    I = np.einsum("th,ths->ts", wI, np.maximum(dots, 0.0))
+    t = t0 + np.arange(qI.shape[0])
+    vis = visible_entries(t, m)
+    s = np.arange(KI.shape[0])
+    return np.where(s[None, :] < vis[:, None], I, -np.inf)
+
+
+def topk(scores, k, m, t0=0):
+    """Per row, the k_t = min(k, visible) entries of largest score, ties to
+    the smaller index; slots k_t..k-1 hold -1.  Row order: descending score."""
+    scores = np.asarray(scores, F64)
+    n, ne = scores.shape
+    out = np.full((n, k), -1, dtype=np.int64)
+    for r in range(n):
+        v = int(min(ne, visible_entries(t0 + r, m)))
+        kt = min(k, v)
+        if kt == 0:
+            continue
+        order = np.argsort(-scores[r, :v], kind="stable")
+        out[r, :kt] = order[:kt]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# O7 - O10: shared-KV MQA with window and sink  ([R] eq 18-19, 27; 2.3.3)
+# ---------------------------------------------------------------------------
+def query_prologue(q, pos, qk_norm, eps, rope_dims, theta):
+    """Per-head RMSNorm, then RoPE of the last r dims at the query position.
+    q [rows, nh, c]; pos [rows]."""
+    y = rms_norm(q, eps) if qk_norm else np.asarray(q, F64)
+    return rope(y, np.asarray(pos, F64), rope_dims, theta)
+
+
+def attention_probs(qh, kv, sink, scale):
+    """Eq 27: p_j = exp(z_j) / (sum_k exp(z_k) + exp(z')), z = scale q.kv.
+    qh [nh, c], kv [N, c], sink [nh].  Returns (p [nh, N], p_sink [nh])."""
+    z = scale * (np.asarray(qh, F64) @ np.asarray(kv, F64).T)
+    zs = np.asarray(sink, F64)
+    M = np.maximum(np.max(z, axis=1, initial=-np.inf), zs)
+    e = np.exp(z - M[:, None])
+    es = np.exp(zs - M)
+    den = np.sum(e, axis=1) + es
+    return e / den[:, None], es / den
+
+
+def attend(qh, kv, sink, scale):
+    """o_h = sum_j p_j kv_j: each candidate is both key and value (eq 19)."""
+    kv = np.asarray(kv, F64)
+    if kv.shape[0] == 0:
+        return np.zeros(np.shape(qh))
+    p, _ = attention_probs(qh, kv, sink, scale)
+    return p @ kv
+
+
+def window_range(t, n_win):
+    """Positions of the uncompressed window of token t: [t-n_win+1, t]."""
+    return np.arange(max(0, t - n_win + 1), t + 1)
+
+
+def output_epilogue(o, pos, rope_dims, theta, store):
+    """Inverse RoPE on the last r dims at the query position, then round."""
+    return round_to(rope(o, np.asarray(pos, F64), rope_dims, theta, inverse=True), store)
+
+
+def sparse_mqa_prefill(q, win_kv, comp, idx, sink, n_win, scale, qk_norm=True,
+                       eps=1e-6, rope_dims=0, theta=10000.0, store="f32", rows=None):
+    """CSA core attention: window rows of t plus the selected entries idx[t]
+    (-1 = empty slot); no de-duplication between the two ([A] topk_idxs
+    concatenation).  q [n, nh, c]; win_kv [n, c]; comp [n_e, c]; idx [n, k]."""
+    q = np.asarray(q, F64)
+    n, nh, c = q.shape
+    rows = range(n) if rows is None else rows
+    out = np.zeros((len(rows), nh, c))
+    for i, t in enumerate(rows):
+        qh = query_prologue(q[t][None], [t], qk_norm, eps, rope_dims, theta)[0]
+        sel = [s for s in np.asarray(idx[t]).tolist() if s >= 0]
+        kv = np.concatenate([np.asarray(win_kv, F64)[window_range(t, n_win)],
+                             np.asarray(comp, F64)[sel]], axis=0)
+        out[i] = attend(qh, kv, sink, scale)
+        out[i] = output_epilogue(out[i][None], [t], rope_dims, theta, "f64")[0]
+    return round_to(out, store)
+
+
+def dense_mqa_prefill(q, win_kv, comp, sink, m, n_win, scale, qk_norm=True,
+                      eps=1e-6, rope_dims=0, theta=10000.0, store="f32", rows=None):
+    """HCA core attention: window rows plus every visible entry
+    s < floor((t+1)/m) ([A] HCA selection rule)."""
+    q = np.asarray(q, F64)
+    n, nh, c = q.shape
+    rows = range(n) if rows is None else rows
+    comp = np.asarray(comp, F64)
+    out = np.zeros((len(rows), nh, c))
+    for i, t in enumerate(rows):
+        qh = query_prologue(q[t][None], [t], qk_norm, eps, rope_dims, theta)[0]
+        v = int(min(comp.shape[0], visible_entries(t, m)))
+        kv = np.concatenate([np.asarray(win_kv, F64)[window_range(t, n_win)], comp[:v]], axis=0)
+        o = attend(qh, kv, sink, scale)
+        out[i] = output_epilogue(o[None], [t], rope_dims, theta, "f64")[0]
+    return round_to(out, store)
+
+
+# ---------------------------------------------------------------------------
+# OD: decode - the pages' stateful compressor  ([A] Compressor decode branch)
+# ---------------------------------------------------------------------------
+class CompressorDecodeOracle:
+    """Token-at-a-time compressor.  Keeps the raw projected rows (C, Z + B)
+    of the current block and, under overlap, of the previous block; when the
+    token at `pos` closes a block ((pos+1) mod m == 0) it pools that block
+    (plus the previous block's b-series) and returns the finished entry.
+
+    Written independently of `pool`: the prefill/decode agreement is a pin."""
+
+    def __init__(self, c, m, overlap, ape, qk_norm=True, eps=1e-6,
+                 rope_dims=0, theta=10000.0, store="f32"):
+        self.c, self.m, self.overlap = c, m, bool(overlap)
+        self.ape = np.asarray(ape, F64)
+        self.cfg = (qk_norm, eps, rope_dims, theta, store)
+        self.rows = {}  # block index -> list of (C row, Z+B row) per position
+
+    def append(self, pos, c_row, z_row):
+        m = self.m
+        blk, r = divmod(int(pos), m)
+        c_row = np.asarray(c_row, F64)
+        lg = np.asarray(z_row, F64) + self.ape[r]
+        self.rows.setdefault(blk, []).append((c_row, lg))
+        assert len(self.rows[blk]) == r + 1, "tokens must arrive in order"
+        for old in [b for b in self.rows if b < blk - 1]:
+            del self.rows[old]
+        if r != m - 1:
+            return None
+        c = self.c
+        if self.overlap:
+            vals = [cr[c:] for cr, _ in self.rows[blk]]
+            logs = [lg[c:] for _, lg in self.rows[blk]]
+            if blk >= 1:
+                vals += [cr[:c] for cr, _ in self.rows[blk - 1]]
+                logs += [lg[:c] for _, lg in self.rows[blk - 1]]
+        else:
+            vals = [cr for cr, _ in self.rows[blk]]
+            logs = [lg for _, lg in self.rows[blk]]
+        vals = np.stack(vals)
+        logs = np.stack(logs)
+        w = np.exp(logs - logs.max(axis=0))
+        ent = (w * vals).sum(axis=0) / w.sum(axis=0)
+        qk_norm, eps, rd, theta, store = self.cfg
+        return entry_epilogue(ent[None], [m * blk], qk_norm, eps, rd, theta, store)[0]
+
+
+def attend_decode_row(q_row, pos, win_rows, entries, sink, scale, qk_norm=True,
+                      eps=1e-6, rope_dims=0, theta=10000.0, store="f32"):
+    """One decode query at position `pos`: the window rows (positions
+    pos-n_win+1..pos, oldest first) plus the given compressed entries."""
+    qh = query_prologue(np.asarray(q_row, F64)[None], [pos], qk_norm, eps, rope_dims, theta)[0]
+    kv = np.concatenate([np.asarray(win_rows, F64), np.asarray(entries, F64)], axis=0)
+    o = attend(qh, kv, sink, scale)
+    return round_to(output_epilogue(o[None], [pos], rope_dims, theta, "f64")[0], store)

@@ -1,0 +1,383 @@
+"""Pins for the CPU fp64 oracle: each test ties an oracle function to something
+other than itself -- a hand-derived worked example, a closed form, an
+invariant, a textbook/library routine, or brute force on tiny inputs.
+
+Citation keys: [R] = page "DeepSeek-V4 技术解读报告" (juejin.cn), section 2.3;
+[A] = page "DeepSeek-V4：算法架构" (1zeryu.github.io), code excerpts."""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import csa_oracle as O
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_examples.json")))
+RNG = np.random.default_rng(1234)
+
+
+# --------------------------------------------------------------- pooling (O2)
+def test_pool_hand_no_overlap():
+    g = GOLD["pool_no_overlap"]
+    out = O.pool(np.array(g["C"]), np.array(g["Z"]), np.array(g["ape"]), g["m"], g["overlap"])
+    np.testing.assert_allclose(out, g["expected"], rtol=0, atol=1e-12)
+
+
+def test_pool_hand_overlap():
+    g = GOLD["pool_overlap"]
+    out = O.pool(np.array(g["C"]), np.array(g["Z"]), np.array(g["ape"]), g["m"], g["overlap"])
+    np.testing.assert_allclose(out, g["expected"], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("m,overlap", [(1, False), (3, False), (4, False), (2, True), (3, True), (4, True)])
+def test_pool_weights_sum_to_one(m, overlap):
+    n, c = 5 * m + 2, 6
+    w = 2 if overlap else 1
+    C = RNG.normal(size=(n, w * c))
+    Z = RNG.normal(size=(n, w * c)) * 3
+    ape = RNG.normal(size=(m, w * c))
+    S = O.pool_weights(C, Z, ape, m, overlap)
+    assert S.shape == (n // m, (2 if overlap else 1) * m, c)
+    np.testing.assert_allclose(S.sum(axis=1), 1.0, atol=1e-12)
+    assert np.all(S >= 0)
+    if overlap:  # block 0 takes nothing from the (absent) previous block
+        assert np.all(S[0, m:] == 0)
+
+
+def test_pool_m1_is_identity():
+    C = RNG.normal(size=(7, 4))
+    Z = RNG.normal(size=(7, 4))
+    out = O.pool(C, Z, RNG.normal(size=(1, 4)), 1, False)
+    np.testing.assert_allclose(out, C, atol=1e-15)
+
+
+def test_pool_constant_logits_give_mean():
+    m, c = 4, 3
+    C = RNG.normal(size=(8, c))
+    Z = np.full((8, c), 0.7)
+    out = O.pool(C, Z, np.zeros((m, c)), m, False)
+    np.testing.assert_allclose(out, C.reshape(2, m, c).mean(axis=1), atol=1e-14)
+
+
+def test_overlap_with_empty_b_series_equals_plain_pooling():
+    m, c, n = 4, 5, 16
+    Ca, Za = RNG.normal(size=(n, c)), RNG.normal(size=(n, c))
+    Cb = RNG.normal(size=(n, c))
+    Zb = np.full((n, c), -np.inf)
+    ape_a = RNG.normal(size=(m, c))
+    out_ov = O.pool(np.hstack([Cb, Ca]), np.hstack([Zb, Za]), np.hstack([np.zeros((m, c)), ape_a]), m, True)
+    out_plain = O.pool(Ca, Za, ape_a, m, False)
+    np.testing.assert_allclose(out_ov, out_plain, atol=1e-13)
+
+
+def test_overlap_block_uses_previous_block_b_series():
+    """Entry i of the overlapped compressor equals the plain softmax pool of
+    the 2m rows (block i's a-series, block i-1's b-series) built by hand."""
+    m, c, n = 3, 2, 9
+    C = RNG.normal(size=(n, 2 * c))
+    Z = RNG.normal(size=(n, 2 * c))
+    ape = RNG.normal(size=(m, 2 * c))
+    out = O.pool(C, Z, ape, m, True)
+    i = 2
+    logits = np.concatenate([Z[m * i:m * i + m, c:] + ape[:, c:], Z[m * (i - 1):m * i, :c] + ape[:, :c]])
+    vals = np.concatenate([C[m * i:m * i + m, c:], C[m * (i - 1):m * i, :c]])
+    wts = np.exp(logits) / np.exp(logits).sum(axis=0)
+    np.testing.assert_allclose(out[i], (wts * vals).sum(axis=0), atol=1e-13)
+
+
+# ------------------------------------------------------ norm / RoPE (O3, O7)
+def test_rms_norm_hand():
+    g = GOLD["rms_norm"]
+    np.testing.assert_allclose(O.rms_norm(np.array(g["x"], float), g["eps"]), g["expected"], atol=1e-12)
+
+
+def test_rms_norm_unit_rms_and_scale_invariance():
+    x = RNG.normal(size=(10, 64)) * 5
+    y = O.rms_norm(x, 0.0)
+    np.testing.assert_allclose(np.sqrt((y * y).mean(-1)), 1.0, atol=1e-12)
+    np.testing.assert_allclose(O.rms_norm(3.7 * x, 0.0), y, atol=1e-12)
+
+
+@pytest.mark.parametrize("case", range(2))
+def test_rope_hand(case):
+    g = GOLD["rope"]["cases"][case]
+    out = O.rope(np.array([g["x"]], float), [g["pos"]], g["rope_dims"], g["theta"])[0]
+    np.testing.assert_allclose(out, g["expected"], atol=1e-12)
+
+
+def test_rope_inverse_norm_and_relative_position():
+    r, c, theta = 8, 12, 10000.0
+    x = RNG.normal(size=(3, c))
+    pos = np.array([0.0, 5.0, 1234.0])
+    y = O.rope(x, pos, r, theta)
+    np.testing.assert_allclose(O.rope(y, pos, r, theta, inverse=True), x, atol=1e-12)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), atol=1e-12)
+    np.testing.assert_array_equal(y[:, : c - r], x[:, : c - r])
+    # score between rotated q (pos a) and k (pos b) depends only on a - b
+    q, k = RNG.normal(size=(1, c)), RNG.normal(size=(1, c))
+    s1 = O.rope(q, [100.0], r, theta) @ O.rope(k, [40.0], r, theta).T
+    s2 = O.rope(q, [1060.0], r, theta) @ O.rope(k, [1000.0], r, theta).T
+    np.testing.assert_allclose(s1, s2, atol=1e-10)
+
+
+def test_rope_three_axis_broadcast():
+    x = RNG.normal(size=(4, 3, 16))
+    pos = np.arange(4.0) * 7
+    y = O.rope(x, pos, 8, 10000.0)
+    for t in range(4):
+        for h in range(3):
+            np.testing.assert_allclose(y[t, h], O.rope(x[t, h][None], [pos[t]], 8, 10000.0)[0], atol=1e-14)
+
+
+# ------------------------------------------------------------- number format
+def test_bf16_rounding_hand():
+    g = GOLD["bf16"]
+    np.testing.assert_array_equal(O.round_bf16(np.array(g["inputs"])), g["expected"])
+
+
+def test_bf16_rounding_matches_torch_for_fp32_inputs():
+    torch = pytest.importorskip("torch")
+    x = (RNG.normal(size=20000) * np.exp(RNG.normal(size=20000) * 4)).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.round_bf16(x.astype(np.float64)), ref)
+
+
+# ------------------------------------------------------- indexer (O5, O6)
+def test_index_scores_and_topk_hand():
+    g = GOLD["index_scores"]
+    n = g["n_tokens"]
+    qI = np.array([g["q_per_token"]] * n, float)
+    wI = np.array([g["w_per_token"]] * n, float)
+    KI = np.array(g["K"], float)
+    sc = O.index_scores(qI, wI, KI, g["m"])
+    exp = np.array([[np.nan if v is None else v for v in row] for row in g["expected_scores"]])
+    np.testing.assert_allclose(np.where(np.isinf(sc), np.nan, sc), exp, atol=1e-12)
+    assert np.all(np.isneginf(sc[np.isnan(exp)]))
+    np.testing.assert_array_equal(O.topk(sc, g["k"], g["m"]), g["expected_idx"])
+
+
+def test_index_scores_nonneg_and_head_permutation():
+    n, h, d, m = 9, 4, 8, 2
+    qI = RNG.normal(size=(n, h, d))
+    wI = RNG.uniform(size=(n, h))
+    KI = RNG.normal(size=(n // m, d))
+    sc = O.index_scores(qI, wI, KI, m)
+    fin = np.isfinite(sc)
+    assert np.all(sc[fin] >= 0)
+    perm = RNG.permutation(h)
+    np.testing.assert_allclose(O.index_scores(qI[:, perm], wI[:, perm], KI, m), sc, atol=1e-12)
+
+
+def test_index_mask_is_causal_block_end():
+    """Entry s is visible to t exactly when its last token m(s+1)-1 <= t."""
+    n, m = 23, 4
+    sc = O.index_scores(RNG.normal(size=(n, 1, 3)), np.ones((n, 1)), RNG.normal(size=(n // m, 3)), m)
+    for t in range(n):
+        for s in range(n // m):
+            assert np.isfinite(sc[t, s]) == (m * (s + 1) - 1 <= t)
+
+
+@pytest.mark.parametrize("trial", range(20))
+def test_topk_brute_force_subsets(trial):
+    """Exhaustive check on tiny rows: the chosen set is the unique k_t-subset
+    that beats every other subset in (score, then smaller index) order."""
+    rng = np.random.default_rng(trial)
+    m, ne, k = 1, 7, 3
+    n = ne
+    sc = rng.integers(0, 4, size=(n, ne)).astype(float)  # many ties on purpose
+    t = np.arange(n)
+    s = np.arange(ne)
+    sc = np.where(s[None] < (t[:, None] + 1) // m, sc, -np.inf)
+    idx = O.topk(sc, k, m)
+    for r in range(n):
+        v = (r + 1) // m
+        kt = min(k, v)
+        assert np.all(idx[r, kt:] == -1)
+        got = set(idx[r, :kt].tolist())
+
+        def key(j):
+            return (sc[r, j], -j)
+
+        # every subset whose members all beat every non-member; must be unique
+        valid = [set(S) for S in itertools.combinations(range(v), kt)
+                 if all(key(a) > key(b) for a in S for b in range(v) if b not in S)]
+        assert valid == [got]
+
+
+def test_topk_padding_count_and_causality():
+    n, m, k = 40, 4, 6
+    sc = O.index_scores(RNG.normal(size=(n, 2, 4)), RNG.uniform(size=(n, 2)), RNG.normal(size=(n // m, 4)), m)
+    idx = O.topk(sc, k, m)
+    for t in range(n):
+        v = (t + 1) // m
+        assert np.sum(idx[t] == -1) == k - min(k, v)
+        sel = idx[t][idx[t] >= 0]
+        assert np.all(m * (sel + 1) - 1 <= t)
+
+
+# ------------------------------------------------------ attention (O7-O10)
+def test_attention_sink_hand():
+    g = GOLD["attention_sink"]
+    p, ps = O.attention_probs(np.array(g["q"]), np.array(g["kv"]), np.array(g["sink"]), g["scale"])
+    np.testing.assert_allclose(p, g["expected_p"], atol=1e-15)
+    np.testing.assert_allclose(ps, g["expected_p_sink"], atol=1e-15)
+    np.testing.assert_allclose(O.attend(np.array(g["q"]), np.array(g["kv"]), np.array(g["sink"]), g["scale"]),
+                               g["expected_o"], atol=1e-15)
+
+
+def test_attention_probabilities_sum_to_one():
+    qh, kv = RNG.normal(size=(5, 16)), RNG.normal(size=(30, 16))
+    sink = RNG.normal(size=5)
+    p, ps = O.attention_probs(qh, kv, sink, 0.25)
+    np.testing.assert_allclose(p.sum(1) + ps, 1.0, atol=1e-14)
+
+
+def test_attention_equal_logits_closed_form_and_huge_sink():
+    N, c = 11, 8
+    kv = RNG.normal(size=(N, c))
+    sink = np.array([0.3, -1.2])
+    o = O.attend(np.zeros((2, c)), kv, sink, 1.0)  # all logits 0
+    expect = (N / (N + np.exp(sink)))[:, None] * kv.mean(0)[None]
+    np.testing.assert_allclose(o, expect, atol=1e-14)
+    o_big = O.attend(RNG.normal(size=(1, c)), kv, np.array([80.0]), 0.1)
+    assert np.max(np.abs(o_big)) < 1e-30
+
+
+def _sdpa_causal(q, k, v):
+    torch = pytest.importorskip("torch")
+    F = torch.nn.functional
+    Q = torch.from_numpy(q).permute(1, 0, 2)[None]  # [1, nh, n, c]
+    K = torch.from_numpy(k)[None, None].expand(1, q.shape[1], -1, -1)
+    V = torch.from_numpy(v)[None, None].expand(1, q.shape[1], -1, -1)
+    out = F.scaled_dot_product_attention(Q, K, V, is_causal=True, scale=1.0)
+    lse = torch.logsumexp((Q @ K.transpose(-1, -2)).masked_fill(
+        torch.ones(q.shape[0], q.shape[0], dtype=torch.bool).triu(1), float("-inf")), dim=-1)
+    return out[0].permute(1, 0, 2).numpy(), lse[0].permute(1, 0).numpy()
+
+
+@pytest.mark.parametrize("overlap", [False])
+def test_csa_m1_all_entries_no_window_is_dense_causal_mqa(overlap):
+    """m = 1, k >= n, n_win = 0, no RoPE: CSA is dense causal shared-KV MQA
+    over the normalised per-token rows, including the token itself.  Checked
+    against torch's scaled_dot_product_attention (fp64, CPU) with the sink
+    folded in through the closed form o_sink = o * S / (S + e^z')."""
+    n, d, c, nh = 12, 10, 8, 3
+    H = RNG.normal(size=(n, d))
+    Wkv, Wz = RNG.normal(size=(d, c)), RNG.normal(size=(d, c))
+    comp = O.compress_prefill(H, Wkv, Wz, np.zeros((1, c)), 1, overlap, qk_norm=True, eps=1e-6, store="f64")
+    q = RNG.normal(size=(n, nh, c))
+    sc = O.index_scores(RNG.normal(size=(n, 2, c)), RNG.uniform(size=(n, 2)), comp, 1)
+    idx = O.topk(sc, n, 1)
+    sink = RNG.normal(size=nh)
+    scale = c ** -0.5
+    out = O.sparse_mqa_prefill(q, np.zeros((n, c)), comp, idx, sink, 0, scale, qk_norm=True, store="f64")
+    qn = O.rms_norm(q, 1e-6) * scale
+    ref, lse = _sdpa_causal(qn, comp, comp)
+    S = np.exp(lse)
+    ref = ref * (S / (S + np.exp(sink)[None]))[..., None]
+    np.testing.assert_allclose(out, ref, atol=1e-12)
+    # with the sink pushed to -inf the result is exactly softmax attention
+    out_ns = O.sparse_mqa_prefill(q, np.zeros((n, c)), comp, idx, np.full(nh, -np.inf), 0, scale, store="f64")
+    np.testing.assert_allclose(out_ns, _sdpa_causal(qn, comp, comp)[0], atol=1e-12)
+
+
+def test_sparse_with_all_entries_equals_dense_hca():
+    n, c, nh, m, n_win = 37, 8, 2, 4, 5
+    q = RNG.normal(size=(n, nh, c))
+    win = RNG.normal(size=(n, c))
+    comp = RNG.normal(size=(n // m, c))
+    sink = RNG.normal(size=nh)
+    idx = np.full((n, n), -1)
+    for t in range(n):
+        v = (t + 1) // m
+        idx[t, :v] = RNG.permutation(v)  # order of the selected set is irrelevant
+    a = O.sparse_mqa_prefill(q, win, comp, idx, sink, n_win, 0.3, rope_dims=4, store="f64")
+    b = O.dense_mqa_prefill(q, win, comp, sink, m, n_win, 0.3, rope_dims=4, store="f64")
+    np.testing.assert_allclose(a, b, atol=1e-13)
+
+
+def test_window_extent_and_dense_hand_count():
+    """With identical candidates the output is N/(N+e^z') times the row, where
+    N = window rows + visible entries; this pins the candidate counting."""
+    n, c, m, n_win = 20, 4, 4, 3
+    row = RNG.normal(size=c)
+    win = np.tile(row, (n, 1))
+    comp = np.tile(row, (n // m, 1))
+    sink = np.array([0.5])
+    q = RNG.normal(size=(n, 1, c))
+    out = O.dense_mqa_prefill(q, win, comp, sink, m, n_win, 0.7, qk_norm=False, store="f64")
+    for t in range(n):
+        N = min(n_win, t + 1) + (t + 1) // m
+        z = 0.7 * q[t, 0] @ row  # every candidate has this same logit
+        np.testing.assert_allclose(out[t, 0], N / (N + np.exp(0.5 - z)) * row, atol=1e-13)
+
+
+def test_output_inverse_rope_makes_output_relative():
+    """Shifting every position by the same offset leaves the output unchanged
+    when entries, window rows and queries are all rotated consistently
+    ([R] 2.3.3: inverse RoPE at the query position)."""
+    n, c, nh, r = 6, 16, 2, 8
+    q0 = RNG.normal(size=(n, nh, c))
+    raw = RNG.normal(size=(n, c))
+    sink = RNG.normal(size=nh)
+
+    def run(shift):
+        win = O.rope(raw, shift + np.arange(n, dtype=float), r, 100.0)
+        outs = []
+        for t in range(n):
+            qh = O.rope(q0[t][None], [shift + t], r, 100.0)[0]
+            o = O.attend(qh, win[: t + 1], sink, 0.5)
+            outs.append(O.rope(o[None], [shift + t], r, 100.0, inverse=True)[0])
+        return np.array(outs)
+
+    np.testing.assert_allclose(run(0.0), run(37.0), atol=1e-10)
+
+
+# --------------------------------------------------------- decode (OD)
+@pytest.mark.parametrize("overlap,m", [(False, 4), (True, 4), (False, 8), (True, 3)])
+def test_stateful_decode_equals_prefill(overlap, m):
+    """The pages' token-at-a-time compressor emits, block by block, exactly
+    the prefill entries (prefill(n) followed by decode steps == prefill(n+s))."""
+    n, d, c = 6 * m + 1, 12, 8
+    w = 2 if overlap else 1
+    H = RNG.normal(size=(n, d))
+    Wkv, Wz = RNG.normal(size=(d, w * c)), RNG.normal(size=(d, w * c))
+    ape = RNG.normal(size=(m, w * c))
+    ref = O.compress_prefill(H, Wkv, Wz, ape, m, overlap, rope_dims=4, store="f64")
+    dec = O.CompressorDecodeOracle(c, m, overlap, ape, rope_dims=4, store="f64")
+    C, Z = O.project(H, Wkv), O.project(H, Wz)
+    got = []
+    for t in range(n):
+        e = dec.append(t, C[t], Z[t])
+        assert (e is not None) == ((t + 1) % m == 0)
+        if e is not None:
+            got.append(e)
+    np.testing.assert_allclose(np.array(got), ref, atol=1e-12)
+
+
+def test_causality_perturbation():
+    """Changing token j's hidden state leaves every output row t < j unchanged."""
+    n, d, c, nh, m, k, n_win = 24, 10, 8, 2, 4, 3, 4
+    H = RNG.normal(size=(n, d))
+    W = [RNG.normal(size=(d, 2 * c)) for _ in range(2)] + [RNG.normal(size=(d, c))]
+    WI = [RNG.normal(size=(d, 2 * 4)) for _ in range(2)]
+    ape, apeI = RNG.normal(size=(m, 2 * c)), RNG.normal(size=(m, 2 * 4))
+    q, qI, wI = RNG.normal(size=(n, nh, c)), RNG.normal(size=(n, 2, 4)), RNG.uniform(size=(n, 2))
+    sink = RNG.normal(size=nh)
+
+    def layer(Hx):
+        comp = O.compress_prefill(Hx, W[0], W[1], ape, m, True, rope_dims=4, store="f64")
+        KI = O.compress_prefill(Hx, WI[0], WI[1], apeI, m, True, store="f64")
+        win = O.window_rows(Hx, W[2], rope_dims=4, store="f64")
+        idx = O.topk(O.index_scores(qI, wI, KI, m), k, m)
+        return O.sparse_mqa_prefill(q, win, comp, idx, sink, n_win, 0.35, rope_dims=4, store="f64")
+
+    base = layer(H)
+    j = 13
+    H2 = H.copy()
+    H2[j] += 5.0
+    pert = layer(H2)
+    np.testing.assert_array_equal(pert[:j], base[:j])
+    assert np.max(np.abs(pert[j:] - base[j:])) > 1e-6
