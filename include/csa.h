@@ -1,0 +1,300 @@
+/*
+ * csa.h -- C ABI of libcsa: CSA / HCA hybrid compressed attention on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Citation keys (page title, then where on the page):
+ *   [R] "DeepSeek-V4 技术解读报告" (juejin.cn/post/7631898635937497134),
+ *       section 2.3 (equations 9-23, 27) and section 4.3 (determinism).
+ *   [A] "DeepSeek-V4：算法架构" (1zeryu.github.io/p/deepseek-v4/), code
+ *       excerpts: attention Q/KV path, Sparse Attention candidate assembly,
+ *       Compressor, Indexer, HCA selection rule, output projection.
+ *
+ * Conventions shared by every entry point
+ * ----------------------------------------
+ *  - Every tensor argument is a DEVICE pointer to a row-major, contiguous
+ *    buffer that the caller allocates and frees.  The library allocates and
+ *    frees nothing, never synchronises, and keeps no mutable global state.
+ *  - Element types: `dtype` (CSA_F32 or CSA_BF16) applies to hidden states,
+ *    weights, queries, indexer queries/weights, caches and outputs.  The
+ *    position biases `ape`, the sink logits and the compressor decode state
+ *    are always fp32; indices are int32 with -1 marking an empty slot;
+ *    positions are int64.
+ *  - Projection weights are output-major: W has shape [out_channels, d]
+ *    (a linear layer's weight layout); the projection is H . W^T, i.e.
+ *    the pages' H . W with W = this buffer transposed.
+ *  - Overlapped compressors (ov = 1) have 2c output channels packed as
+ *    [b-series | a-series]: channels [0, c) feed the NEXT block, channels
+ *    [c, 2c) the block itself ([A] Compressor).
+ *  - All work is enqueued on `stream` (a hipStream_t; NULL = default stream)
+ *    and is asynchronous.  `ws` is caller-owned scratch of at least
+ *    csa_workspace_bytes(...) bytes (may be NULL when that is 0).
+ *  - Return value: CSA_OK or a negative csa_status.  All argument checks run
+ *    on the host before anything is enqueued, so a failing call has no side
+ *    effect.  A fault inside a kernel surfaces at the caller's next stream
+ *    synchronisation.
+ *  - Precision: dot products and softmax statistics accumulate in fp32;
+ *    pooling, RMSNorm and RoPE run in fp32 (RoPE angles in fp64) with one
+ *    rounding to `dtype` at store.  In bf16 mode the normalised query and
+ *    the attention probabilities are rounded to bf16 as matrix-core operands.
+ *  - Calls on one stream are ordered; concurrent calls on different streams
+ *    must not share output, state or workspace buffers.
+ */
+#ifndef CSA_H
+#define CSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA_ABI_VERSION 1
+
+typedef enum csa_status {
+  CSA_OK = 0,
+  CSA_ERR_INVALID_ARG = -1, /* null pointer, inconsistent sizes            */
+  CSA_ERR_UNSUPPORTED = -2, /* shape/dtype outside the kernels' limits     */
+  CSA_ERR_WORKSPACE = -3,   /* ws_bytes below csa_workspace_bytes(...)      */
+  CSA_ERR_HIP = -4          /* a HIP launch reported an error              */
+} csa_status;
+
+typedef enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
+
+/* ------------------------------------------------------------------------
+ * Descriptors.  Unused fields are ignored by the calls that do not need them.
+ * ---------------------------------------------------------------------- */
+
+/* Compressor ([R] eq 9-12 for CSA, eq 20-23 for HCA) and window rows. */
+typedef struct csa_compress_desc {
+  int64_t n;           /* prefill: tokens in H (positions 0..n-1)           */
+  int32_t batch;       /* decode: sequences B                               */
+  int32_t d;           /* hidden size                                       */
+  int32_t c;           /* entry width (head dim), multiple of 32, <= 512    */
+  int32_t m;           /* compression ratio, 1..256                          */
+  int32_t overlap;     /* 0 or 1: pool 2m rows (block i-1's b-series too)   */
+  int32_t dtype;       /* csa_dtype                                          */
+  int32_t qk_norm;     /* 1: RMSNorm (unit weight) on each entry / window row */
+  float eps;           /* RMSNorm epsilon                                    */
+  int32_t rope_dims;   /* r: rotate the last r channels (0 = off; even)      */
+  float rope_theta;    /* RoPE base                                          */
+  int32_t n_win;       /* window ring length (slots)                         */
+  int64_t max_entries; /* decode: rows per sequence in the entry cache      */
+} csa_compress_desc;
+
+/* Lightning indexer + top-k ([R] eq 16-17). */
+typedef struct csa_index_desc {
+  int64_t n;           /* prefill: query tokens (positions 0..n-1)          */
+  int32_t batch;       /* decode: sequences B                               */
+  int32_t n_heads;     /* indexer heads hI: 4, 8 or 16                      */
+  int32_t head_dim;    /* indexer key width cI: 64 or 128                   */
+  int32_t m;           /* compression ratio of the indexer keys             */
+  int32_t k;           /* top-k, 1..2048                                     */
+  int32_t dtype;       /* csa_dtype of qI, wI and the keys                  */
+  int64_t n_entries;   /* prefill: rows of KI; decode: cache rows per seq   */
+} csa_index_desc;
+
+/* Shared-KV multi-query core attention with window and sink ([R] eq 18-19,
+ * 27, section 2.3.3). */
+typedef struct csa_attn_desc {
+  int64_t n;           /* prefill: query tokens (positions 0..n-1)          */
+  int32_t batch;       /* decode: sequences B                               */
+  int32_t n_heads;     /* query heads nh: 8, 16, 32 or 64                    */
+  int32_t c;           /* head dim = entry width: 64, 128, 256 or 512        */
+  int32_t k;           /* sparse: index slots per query                      */
+  int32_t m;           /* dense (HCA): compression ratio                     */
+  int32_t n_win;       /* window length (uncompressed positions incl. t)    */
+  int32_t dtype;       /* csa_dtype                                          */
+  float scale;         /* logit scale (c^-1/2 in the workloads)              */
+  int32_t qk_norm;     /* 1: RMSNorm on each query head                      */
+  float eps;           /* RMSNorm epsilon                                    */
+  int32_t rope_dims;   /* r: query RoPE at t, inverse RoPE of the output    */
+  float rope_theta;
+  int64_t n_entries;   /* prefill: rows of comp; decode: cache rows per seq */
+} csa_attn_desc;
+
+/* ------------------------------------------------------------------------
+ * Compressor
+ * ---------------------------------------------------------------------- */
+
+/* csa_compress_prefill -- [R] eq 9-12 (CSA, ov=1) / eq 20-23 (HCA, ov=0);
+ * [A] Compressor prefill branch, attention wkv -> kv_norm -> RoPE path.
+ *
+ * For one sequence of n tokens (positions 0..n-1):
+ *   C = H W_kv^T, Z = H W_z^T                       (fp32 accumulation)
+ *   entry i (i < n/m, complete blocks only): per channel, softmax over the
+ *     block's m logits Z+ape (plus block i-1's b-series under overlap),
+ *     weighted sum of C; then RMSNorm (qk_norm), RoPE of the last r channels
+ *     at position m*i, one rounding -> out_comp[i].
+ *   window rows (W_win != NULL): V = H W_win^T, RMSNorm, RoPE at the token's
+ *     position -> out_win[t] and/or, for the last n_win tokens, win_ring[t % n_win].
+ *   state (optional): the decode state after token n-1 (see
+ *     csa_compress_decode), so decoding can continue at position n.
+ *
+ *   H        [n, d]            dtype
+ *   W_kv     [(1+ov)c, d]      dtype
+ *   W_z      [(1+ov)c, d]      dtype
+ *   ape      [m, (1+ov)c]      fp32   learned position bias B (B_b | B_a)
+ *   W_win    [c, d] or NULL    dtype
+ *   out_comp [floor(n/m), c]   dtype  (may be NULL when n < m)
+ *   out_win  [n, c] or NULL    dtype  (requires W_win)
+ *   win_ring [n_win, c] or NULL dtype (requires W_win)
+ *   state    csa_state_bytes(desc with batch=1) bytes or NULL, fp32
+ */
+int csa_compress_prefill(const csa_compress_desc* desc, const void* H, const void* W_kv,
+                         const void* W_z, const float* ape, const void* W_win, void* out_comp,
+                         void* out_win, void* win_ring, float* state, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* csa_compress_decode -- [A] Compressor decode branch (start_pos > 0).
+ *
+ * One new token per sequence b at position pos[b] (>= 0):
+ *   its projected row updates the per-sequence online pooling state; when
+ *   (pos+1) mod m == 0 the block i = pos/m is finished: its entry (pooled
+ *   with block i-1's b-series under overlap) goes through the epilogue at
+ *   position m*i and is written to cache[b][i].  With W_win, the token's
+ *   window row (RMSNorm, RoPE at pos) is written to win_ring[b][pos % n_win].
+ * The state is an online softmax (running max, sum and weighted sum per
+ * channel) of the current block's rows, and under overlap also of its
+ * b-series and of the previous block's b-series: O(c) per sequence, not the
+ * raw rows.  A state freshly produced by csa_compress_prefill(n) continues
+ * at pos = n; a zero-initialised state is NOT valid -- use csa_state_init.
+ *
+ *   h        [B, d]               dtype
+ *   pos      [B]                  int64 (device)
+ *   W_kv, W_z, ape, W_win         as for prefill
+ *   state    [B] x csa_state_bytes/B   fp32, updated in place
+ *   cache    [B, max_entries, c]  dtype, row pos/m written on emission
+ *   win_ring [B, n_win, c] or NULL
+ */
+int csa_compress_decode(const csa_compress_desc* desc, const void* h, const int64_t* pos,
+                        const void* W_kv, const void* W_z, const float* ape, const void* W_win,
+                        float* state, void* cache, void* win_ring, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/* Bytes of compressor decode state for desc->batch sequences (batch >= 1). */
+size_t csa_state_bytes(const csa_compress_desc* desc);
+
+/* Writes the empty state (no token seen) for desc->batch sequences. */
+int csa_state_init(const csa_compress_desc* desc, float* state, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Lightning indexer + top-k
+ * ---------------------------------------------------------------------- */
+
+/* csa_index_topk_prefill -- [R] eq 16-17; [A] Indexer (causal mask, top-k of
+ * min(k, visible) entries, -1 padding).
+ *
+ * For each token t: I[t,s] = sum_h wI[t,h] * max(0, qI[t,h,:] . KI[s,:]) over
+ * the visible entries s < floor((t+1)/m); idx_out[t] receives the
+ * k_t = min(k, visible) indices of largest score (ties: smaller index),
+ * in ascending index order, followed by k - k_t slots of -1.
+ *
+ *   qI      [n, hI, cI]  dtype
+ *   wI      [n, hI]      dtype
+ *   KI      [n_entries, cI] dtype   (n_entries >= floor(n/m) is not required;
+ *                                    entries beyond n_entries are invisible)
+ *   idx_out [n, k]       int32
+ */
+int csa_index_topk_prefill(const csa_index_desc* desc, const void* qI, const void* wI,
+                           const void* KI, int32_t* idx_out, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/* csa_index_topk_decode -- the same selection for one query per sequence at
+ * position pos[b] over the cached keys KI_cache[b][0 .. floor((pos+1)/m)).
+ *
+ *   qI       [B, hI, cI]               dtype
+ *   wI       [B, hI]                   dtype
+ *   KI_cache [B, n_entries, cI]        dtype
+ *   pos      [B]                       int64 (device)
+ *   idx_out  [B, k]                    int32, ascending, -1 padded
+ */
+int csa_index_topk_decode(const csa_index_desc* desc, const void* qI, const void* wI,
+                          const void* KI_cache, const int64_t* pos, int32_t* idx_out, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Core attention
+ * ---------------------------------------------------------------------- */
+
+/* csa_sparse_mqa_prefill -- [R] eq 18-19 and 27, section 2.3.3; [A] Sparse
+ * Attention (window ++ selected entries, no de-duplication) and output
+ * projection's inverse RoPE.
+ *
+ * For token t and head h: q <- RMSNorm(q[t,h]) (qk_norm), RoPE of the last r
+ * channels at t; candidates = window rows win_kv[j], max(0,t-n_win+1) <= j <= t,
+ * plus comp[s] for every s = idx[t][*] >= 0; logits z = scale * q . kv;
+ *   o = sum_j exp(z_j) kv_j / (sum_j exp(z_j) + exp(sink[h]))
+ * then inverse RoPE of the last r channels at t -> out[t,h].
+ *
+ *   q      [n, nh, c]   dtype
+ *   win_kv [n, c]       dtype  (window rows, already normalised/rotated)
+ *   comp   [n_entries, c] dtype
+ *   idx    [n, k]       int32  (entries must be < n_entries or -1)
+ *   sink   [nh]         fp32
+ *   out    [n, nh, c]   dtype
+ */
+int csa_sparse_mqa_prefill(const csa_attn_desc* desc, const void* q, const void* win_kv,
+                           const void* comp, const int32_t* idx, const float* sink, void* out,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* csa_sparse_mqa_decode -- the same for one query per sequence at pos[b];
+ * window rows come from the ring (position p in slot p % n_win), entries
+ * from comp_cache[b].  Candidates are split in fixed-size chunks whose
+ * partial softmax states are merged in a fixed order with the sink counted
+ * once, so a sequence's result does not depend on the batch ([R] 4.3).
+ *
+ *   q          [B, nh, c]              dtype
+ *   win_ring   [B, n_win, c]           dtype
+ *   comp_cache [B, n_entries, c]       dtype
+ *   idx        [B, k]                  int32
+ *   pos        [B]                     int64 (device)
+ *   sink [nh] fp32;  out [B, nh, c] dtype
+ */
+int csa_sparse_mqa_decode(const csa_attn_desc* desc, const void* q, const void* win_ring,
+                          const void* comp_cache, const int32_t* idx, const int64_t* pos,
+                          const float* sink, void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* hca_dense_mqa_prefill -- [R] section 2.3.2 (dense attention over every
+ * compressed entry), [A] HCA selection rule: as csa_sparse_mqa_prefill with
+ * the candidate entries being all s < floor((t+1)/m) (and < n_entries). */
+int hca_dense_mqa_prefill(const csa_attn_desc* desc, const void* q, const void* win_kv,
+                          const void* comp, const float* sink, void* out, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/* hca_dense_mqa_decode -- as csa_sparse_mqa_decode with all visible entries
+ * comp_cache[b][0 .. floor((pos+1)/m)). */
+int hca_dense_mqa_decode(const csa_attn_desc* desc, const void* q, const void* win_ring,
+                         const void* comp_cache, const int64_t* pos, const float* sink,
+                         void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Helpers
+ * ---------------------------------------------------------------------- */
+
+typedef enum csa_entry {
+  CSA_ENTRY_COMPRESS_PREFILL = 0,
+  CSA_ENTRY_COMPRESS_DECODE = 1,
+  CSA_ENTRY_INDEX_TOPK_PREFILL = 2,
+  CSA_ENTRY_INDEX_TOPK_DECODE = 3,
+  CSA_ENTRY_SPARSE_MQA_PREFILL = 4,
+  CSA_ENTRY_SPARSE_MQA_DECODE = 5,
+  CSA_ENTRY_DENSE_MQA_PREFILL = 6,
+  CSA_ENTRY_DENSE_MQA_DECODE = 7
+} csa_entry;
+
+/* Workspace bytes needed by `entry` for the descriptor `desc` (a pointer to
+ * the csa_*_desc type that entry takes).  Returns 0 on a null descriptor. */
+size_t csa_workspace_bytes(int entry, const void* desc);
+
+/* Static text for a csa_status value. */
+const char* csa_status_string(int status);
+
+/* CSA_ABI_VERSION of the loaded library. */
+int csa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA_H */

@@ -1,1 +1,344 @@
-"""MI355X-native CSA / HCA hybrid compressed attention (binding to libcsa)."""
+"""MI355X-native CSA / HCA hybrid compressed attention.
+
+Thin ctypes binding to libcsa.so (HIP kernels for gfx950).  Every function
+here only checks and marshals arguments -- shapes, dtypes, devices, the
+current HIP stream -- and calls the C entry point of the same name; all
+computation happens in the library's kernels.  torch supplies device memory
+(outputs and workspaces) and streams.  If libcsa.so is missing or cannot be
+loaded, every entry point raises: there is no fallback path.
+
+The operations, layouts and conventions are documented in include/csa.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcsa.so")
+
+CSA_F32, CSA_BF16 = 0, 1
+ENTRY = dict(compress_prefill=0, compress_decode=1, index_topk_prefill=2, index_topk_decode=3,
+             sparse_mqa_prefill=4, sparse_mqa_decode=5, dense_mqa_prefill=6, dense_mqa_decode=7)
+EXPORTED = ["csa_compress_prefill", "csa_compress_decode", "csa_state_bytes", "csa_state_init",
+            "csa_index_topk_prefill", "csa_index_topk_decode", "csa_sparse_mqa_prefill",
+            "csa_sparse_mqa_decode", "hca_dense_mqa_prefill", "hca_dense_mqa_decode",
+            "csa_workspace_bytes", "csa_status_string", "csa_abi_version"]
+
+
+class CompressDesc(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("batch", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("c", ctypes.c_int32), ("m", ctypes.c_int32), ("overlap", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("qk_norm", ctypes.c_int32), ("eps", ctypes.c_float),
+                ("rope_dims", ctypes.c_int32), ("rope_theta", ctypes.c_float),
+                ("n_win", ctypes.c_int32), ("max_entries", ctypes.c_int64)]
+
+
+class IndexDesc(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("batch", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("m", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("n_entries", ctypes.c_int64)]
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("batch", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("c", ctypes.c_int32), ("k", ctypes.c_int32), ("m", ctypes.c_int32),
+                ("n_win", ctypes.c_int32), ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("qk_norm", ctypes.c_int32), ("eps", ctypes.c_float),
+                ("rope_dims", ctypes.c_int32), ("rope_theta", ctypes.c_float),
+                ("n_entries", ctypes.c_int64)]
+
+
+_lib = None
+
+
+class CsaError(RuntimeError):
+    pass
+
+
+def load(path: str = LIB_PATH):
+    """Load libcsa.so (once).  Raises if it is missing -- no fallback."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise CsaError(f"{path} not found: build it with `python -m long_context_attention_10_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, S, I = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    lib.csa_abi_version.restype = I
+    lib.csa_status_string.restype = ctypes.c_char_p
+    lib.csa_status_string.argtypes = [I]
+    lib.csa_workspace_bytes.restype = S
+    lib.csa_workspace_bytes.argtypes = [I, P]
+    lib.csa_state_bytes.restype = S
+    lib.csa_state_bytes.argtypes = [P]
+    lib.csa_state_init.argtypes = [P, P, P]
+    lib.csa_compress_prefill.argtypes = [P] * 11 + [S, P]
+    lib.csa_compress_decode.argtypes = [P] * 11 + [S, P]
+    lib.csa_index_topk_prefill.argtypes = [P] * 6 + [S, P]
+    lib.csa_index_topk_decode.argtypes = [P] * 7 + [S, P]
+    lib.csa_sparse_mqa_prefill.argtypes = [P] * 8 + [S, P]
+    lib.csa_sparse_mqa_decode.argtypes = [P] * 9 + [S, P]
+    lib.hca_dense_mqa_prefill.argtypes = [P] * 7 + [S, P]
+    lib.hca_dense_mqa_decode.argtypes = [P] * 8 + [S, P]
+    for f in EXPORTED:
+        if f not in ("csa_abi_version", "csa_status_string", "csa_workspace_bytes", "csa_state_bytes"):
+            getattr(lib, f).restype = I
+    _lib = lib
+    return lib
+
+
+# ----------------------------------------------------------------- helpers
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return CSA_F32
+    if t.dtype == torch.bfloat16:
+        return CSA_BF16
+    raise CsaError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise CsaError("all tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise CsaError("all tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = load().csa_status_string(status).decode()
+        raise CsaError(f"{what} failed: {msg} ({status})")
+
+
+def _expect(t, shape, dtype, name):
+    if t is None:
+        raise CsaError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise CsaError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise CsaError(f"{name}: expected {dtype}, got {t.dtype}")
+
+
+_WS = {}
+
+
+def workspace(nbytes: int, device, slot: str = "default"):
+    """A cached device workspace of at least nbytes (torch-owned memory)."""
+    if nbytes == 0:
+        return None, 0
+    key = (str(device), slot)
+    t = _WS.get(key)
+    if t is None or t.numel() < nbytes:
+        t = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _WS[key] = t
+    return t, t.numel()
+
+
+def workspace_bytes(entry: str, desc) -> int:
+    return load().csa_workspace_bytes(ENTRY[entry], ctypes.byref(desc))
+
+
+# -------------------------------------------------------------- compressor
+def compress_desc(n=0, batch=1, d=0, c=0, m=1, overlap=0, dtype=CSA_F32, qk_norm=True, eps=1e-6,
+                  rope_dims=0, rope_theta=10000.0, n_win=128, max_entries=0):
+    return CompressDesc(n, batch, d, c, m, int(overlap), dtype, int(qk_norm), eps, rope_dims,
+                        rope_theta, n_win, max_entries)
+
+
+def csa_state_bytes(desc) -> int:
+    return load().csa_state_bytes(ctypes.byref(desc))
+
+
+def csa_state_init(desc, state: torch.Tensor):
+    _check(load().csa_state_init(ctypes.byref(desc), _ptr(state), _stream(state.device)), "csa_state_init")
+
+
+def csa_compress_prefill(H, W_kv, W_z, ape, m, overlap, W_win=None, qk_norm=True, eps=1e-6,
+                         rope_dims=0, rope_theta=10000.0, n_win=128, want_win=True,
+                         want_ring=False, want_state=False, out_comp=None, out_win=None,
+                         win_ring=None, state=None):
+    """Compressed entries (and window rows / ring / decode state) of one
+    sequence H [n, d].  Weights are output-major [(1+ov)c, d]."""
+    lib = load()
+    n, d = H.shape
+    w = W_kv.shape[0]
+    c = w // (2 if overlap else 1)
+    dt = _dt(H)
+    _expect(W_kv, (w, d), H.dtype, "W_kv")
+    _expect(W_z, (w, d), H.dtype, "W_z")
+    _expect(ape, (m, w), torch.float32, "ape")
+    desc = compress_desc(n=n, d=d, c=c, m=m, overlap=overlap, dtype=dt, qk_norm=qk_norm, eps=eps,
+                         rope_dims=rope_dims, rope_theta=rope_theta, n_win=n_win)
+    dev = H.device
+    if out_comp is None:
+        out_comp = torch.empty((n // m, c), dtype=H.dtype, device=dev)
+    if W_win is not None:
+        _expect(W_win, (c, d), H.dtype, "W_win")
+        if want_win and out_win is None:
+            out_win = torch.empty((n, c), dtype=H.dtype, device=dev)
+        if want_ring and win_ring is None:
+            win_ring = torch.empty((n_win, c), dtype=H.dtype, device=dev)
+    if want_state and state is None:
+        state = torch.empty(csa_state_bytes(desc) // 4, dtype=torch.float32, device=dev)
+    ws, wsb = workspace(workspace_bytes("compress_prefill", desc), dev)
+    st = lib.csa_compress_prefill(ctypes.byref(desc), _ptr(H), _ptr(W_kv), _ptr(W_z), _ptr(ape),
+                                  _ptr(W_win), _ptr(out_comp) if out_comp.numel() else None,
+                                  _ptr(out_win), _ptr(win_ring), _ptr(state), _ptr(ws), wsb,
+                                  _stream(dev))
+    _check(st, "csa_compress_prefill")
+    return dict(comp=out_comp, win=out_win, ring=win_ring, state=state)
+
+
+def csa_compress_decode(h, pos, W_kv, W_z, ape, m, overlap, state, cache, W_win=None,
+                        win_ring=None, qk_norm=True, eps=1e-6, rope_dims=0, rope_theta=10000.0):
+    """One new token per sequence: h [B, d], pos [B] int64; updates state,
+    cache [B, max_entries, c] (on emission) and win_ring [B, n_win, c]."""
+    lib = load()
+    B, d = h.shape
+    w = W_kv.shape[0]
+    c = w // (2 if overlap else 1)
+    _expect(pos, (B,), torch.int64, "pos")
+    _expect(cache, (B, cache.shape[1], c), h.dtype, "cache")
+    n_win = win_ring.shape[1] if win_ring is not None else 0
+    desc = compress_desc(batch=B, d=d, c=c, m=m, overlap=overlap, dtype=_dt(h), qk_norm=qk_norm,
+                         eps=eps, rope_dims=rope_dims, rope_theta=rope_theta, n_win=n_win,
+                         max_entries=cache.shape[1])
+    if state.numel() * 4 < csa_state_bytes(desc):
+        raise CsaError("state too small")
+    ws, wsb = workspace(workspace_bytes("compress_decode", desc), h.device, "decode_proj")
+    st = lib.csa_compress_decode(ctypes.byref(desc), _ptr(h), _ptr(pos), _ptr(W_kv), _ptr(W_z),
+                                 _ptr(ape), _ptr(W_win), _ptr(state), _ptr(cache), _ptr(win_ring),
+                                 _ptr(ws), wsb, _stream(h.device))
+    _check(st, "csa_compress_decode")
+
+
+# ----------------------------------------------------------------- indexer
+def csa_index_topk_prefill(qI, wI, KI, m, k, out=None):
+    """idx [n, k] int32: per token, the top-k visible entries (ascending), -1 padded."""
+    lib = load()
+    n, hI, cI = qI.shape
+    _expect(wI, (n, hI), qI.dtype, "wI")
+    ne = KI.shape[0]
+    _expect(KI, (ne, cI), qI.dtype, "KI")
+    desc = IndexDesc(n, 1, hI, cI, m, k, _dt(qI), ne)
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.int32, device=qI.device)
+    ws, wsb = workspace(workspace_bytes("index_topk_prefill", desc), qI.device, "index")
+    st = lib.csa_index_topk_prefill(ctypes.byref(desc), _ptr(qI), _ptr(wI),
+                                    _ptr(KI) if ne else None, _ptr(out), _ptr(ws), wsb,
+                                    _stream(qI.device))
+    _check(st, "csa_index_topk_prefill")
+    return out
+
+
+def csa_index_topk_decode(qI, wI, KI_cache, pos, m, k, out=None):
+    lib = load()
+    B, hI, cI = qI.shape
+    ne = KI_cache.shape[1]
+    _expect(KI_cache, (B, ne, cI), qI.dtype, "KI_cache")
+    _expect(pos, (B,), torch.int64, "pos")
+    desc = IndexDesc(0, B, hI, cI, m, k, _dt(qI), ne)
+    if out is None:
+        out = torch.empty((B, k), dtype=torch.int32, device=qI.device)
+    ws, wsb = workspace(workspace_bytes("index_topk_decode", desc), qI.device, "index_dec")
+    st = lib.csa_index_topk_decode(ctypes.byref(desc), _ptr(qI), _ptr(wI), _ptr(KI_cache),
+                                   _ptr(pos), _ptr(out), _ptr(ws), wsb, _stream(qI.device))
+    _check(st, "csa_index_topk_decode")
+    return out
+
+
+# --------------------------------------------------------------- attention
+def attn_desc(n=0, batch=1, nh=1, c=0, k=0, m=1, n_win=128, dtype=CSA_F32, scale=None,
+              qk_norm=True, eps=1e-6, rope_dims=0, rope_theta=10000.0, n_entries=0):
+    if scale is None:
+        scale = c ** -0.5
+    return AttnDesc(n, batch, nh, c, k, m, n_win, dtype, scale, int(qk_norm), eps, rope_dims,
+                    rope_theta, n_entries)
+
+
+def csa_sparse_mqa_prefill(q, win_kv, comp, idx, sink, n_win=128, scale=None, qk_norm=True,
+                           eps=1e-6, rope_dims=0, rope_theta=10000.0, out=None):
+    lib = load()
+    n, nh, c = q.shape
+    k = idx.shape[1]
+    _expect(win_kv, (n, c), q.dtype, "win_kv")
+    _expect(idx, (n, k), torch.int32, "idx")
+    _expect(sink, (nh,), torch.float32, "sink")
+    desc = attn_desc(n=n, nh=nh, c=c, k=k, n_win=n_win, dtype=_dt(q), scale=scale, qk_norm=qk_norm,
+                     eps=eps, rope_dims=rope_dims, rope_theta=rope_theta, n_entries=comp.shape[0])
+    if out is None:
+        out = torch.empty_like(q)
+    st = lib.csa_sparse_mqa_prefill(ctypes.byref(desc), _ptr(q), _ptr(win_kv),
+                                    _ptr(comp) if comp.numel() else None, _ptr(idx), _ptr(sink),
+                                    _ptr(out), None, 0, _stream(q.device))
+    _check(st, "csa_sparse_mqa_prefill")
+    return out
+
+
+def hca_dense_mqa_prefill(q, win_kv, comp, sink, m, n_win=128, scale=None, qk_norm=True, eps=1e-6,
+                          rope_dims=0, rope_theta=10000.0, out=None):
+    lib = load()
+    n, nh, c = q.shape
+    _expect(win_kv, (n, c), q.dtype, "win_kv")
+    _expect(sink, (nh,), torch.float32, "sink")
+    desc = attn_desc(n=n, nh=nh, c=c, m=m, n_win=n_win, dtype=_dt(q), scale=scale, qk_norm=qk_norm,
+                     eps=eps, rope_dims=rope_dims, rope_theta=rope_theta, n_entries=comp.shape[0])
+    if out is None:
+        out = torch.empty_like(q)
+    st = lib.hca_dense_mqa_prefill(ctypes.byref(desc), _ptr(q), _ptr(win_kv),
+                                   _ptr(comp) if comp.numel() else None, _ptr(sink), _ptr(out),
+                                   None, 0, _stream(q.device))
+    _check(st, "hca_dense_mqa_prefill")
+    return out
+
+
+def csa_sparse_mqa_decode(q, win_ring, comp_cache, idx, pos, sink, scale=None, qk_norm=True,
+                          eps=1e-6, rope_dims=0, rope_theta=10000.0, out=None):
+    lib = load()
+    B, nh, c = q.shape
+    n_win = win_ring.shape[1]
+    k = idx.shape[1]
+    _expect(win_ring, (B, n_win, c), q.dtype, "win_ring")
+    _expect(comp_cache, (B, comp_cache.shape[1], c), q.dtype, "comp_cache")
+    _expect(idx, (B, k), torch.int32, "idx")
+    _expect(pos, (B,), torch.int64, "pos")
+    desc = attn_desc(batch=B, nh=nh, c=c, k=k, n_win=n_win, dtype=_dt(q), scale=scale,
+                     qk_norm=qk_norm, eps=eps, rope_dims=rope_dims, rope_theta=rope_theta,
+                     n_entries=comp_cache.shape[1])
+    if out is None:
+        out = torch.empty_like(q)
+    ws, wsb = workspace(workspace_bytes("sparse_mqa_decode", desc), q.device, "attn_dec_s")
+    st = lib.csa_sparse_mqa_decode(ctypes.byref(desc), _ptr(q), _ptr(win_ring), _ptr(comp_cache),
+                                   _ptr(idx), _ptr(pos), _ptr(sink), _ptr(out), _ptr(ws), wsb,
+                                   _stream(q.device))
+    _check(st, "csa_sparse_mqa_decode")
+    return out
+
+
+def hca_dense_mqa_decode(q, win_ring, comp_cache, pos, sink, m, scale=None, qk_norm=True, eps=1e-6,
+                         rope_dims=0, rope_theta=10000.0, out=None):
+    lib = load()
+    B, nh, c = q.shape
+    n_win = win_ring.shape[1]
+    _expect(win_ring, (B, n_win, c), q.dtype, "win_ring")
+    _expect(comp_cache, (B, comp_cache.shape[1], c), q.dtype, "comp_cache")
+    _expect(pos, (B,), torch.int64, "pos")
+    desc = attn_desc(batch=B, nh=nh, c=c, m=m, n_win=n_win, dtype=_dt(q), scale=scale,
+                     qk_norm=qk_norm, eps=eps, rope_dims=rope_dims, rope_theta=rope_theta,
+                     n_entries=comp_cache.shape[1])
+    if out is None:
+        out = torch.empty_like(q)
+    ws, wsb = workspace(workspace_bytes("dense_mqa_decode", desc), q.device, "attn_dec_d")
+    st = lib.hca_dense_mqa_decode(ctypes.byref(desc), _ptr(q), _ptr(win_ring), _ptr(comp_cache),
+                                  _ptr(pos), _ptr(sink), _ptr(out), _ptr(ws), wsb, _stream(q.device))
+    _check(st, "hca_dense_mqa_decode")
+    return out

@@ -1,0 +1,297 @@
+// C ABI of libcsa: argument validation on the host, then kernel launches on
+// the caller's stream.  Nothing here allocates, frees or synchronises.
+// The operations and their definitions are documented in include/csa.h.
+#include <hip/hip_runtime.h>
+
+#include "../../include/csa.h"
+#include "csa_launch.h"
+
+using namespace csa;
+
+namespace {
+
+size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool dtype_ok(int dt) { return dt == CSA_F32 || dt == CSA_BF16; }
+size_t esize(int dt) { return dt == CSA_BF16 ? 2 : 4; }
+bool pow2_c(int c) { return c == 32 || c == 64 || c == 128 || c == 256 || c == 512; }
+
+// ------------------------------------------------------------- compressor
+int check_compress(const csa_compress_desc* d, bool decode) {
+  if (!d) return CSA_ERR_INVALID_ARG;
+  if (!dtype_ok(d->dtype)) return CSA_ERR_UNSUPPORTED;
+  if (d->d <= 0 || d->c <= 0 || d->m <= 0 || (d->overlap != 0 && d->overlap != 1))
+    return CSA_ERR_INVALID_ARG;
+  if (!pow2_c(d->c)) return CSA_ERR_UNSUPPORTED;
+  if (d->m > 1024) return CSA_ERR_UNSUPPORTED;
+  if (d->d % 64 != 0) return CSA_ERR_UNSUPPORTED;  // 128-byte K slices in the GEMMs
+  if (d->rope_dims < 0 || d->rope_dims > d->c || (d->rope_dims & 1)) return CSA_ERR_INVALID_ARG;
+  if (d->rope_dims > 0 && !(d->rope_theta > 0.f)) return CSA_ERR_INVALID_ARG;
+  if (d->qk_norm && !(d->eps >= 0.f)) return CSA_ERR_INVALID_ARG;
+  if (decode) {
+    if (d->batch <= 0 || d->max_entries < 0) return CSA_ERR_INVALID_ARG;
+  } else {
+    if (d->n < 0) return CSA_ERR_INVALID_ARG;
+  }
+  return CSA_OK;
+}
+
+size_t ws_compress_prefill(const csa_compress_desc* d, bool has_win) {
+  const int w = (1 + d->overlap) * d->c;
+  return al((size_t)d->n * (size_t)(2 * w + (has_win ? d->c : 0)) * 4);
+}
+
+size_t ws_compress_decode(const csa_compress_desc* d, bool has_win) {
+  const int w = (1 + d->overlap) * d->c;
+  const int N = 2 * w + (has_win ? d->c : 0);
+  const int ks = decode_proj_ksplit(N, d->d, d->dtype);
+  return al((size_t)ks * d->batch * N * 4);
+}
+
+// ---------------------------------------------------------------- indexer
+int check_index(const csa_index_desc* d, bool decode) {
+  if (!d) return CSA_ERR_INVALID_ARG;
+  if (!dtype_ok(d->dtype)) return CSA_ERR_UNSUPPORTED;
+  if (d->m <= 0 || d->k <= 0 || d->n_entries < 0) return CSA_ERR_INVALID_ARG;
+  if (!(d->n_heads == 4 || d->n_heads == 8 || d->n_heads == 16)) return CSA_ERR_UNSUPPORTED;
+  if (!(d->head_dim == 64 || d->head_dim == 128)) return CSA_ERR_UNSUPPORTED;
+  if (d->k > 2048) return CSA_ERR_UNSUPPORTED;
+  if (decode) {
+    if (d->batch <= 0) return CSA_ERR_INVALID_ARG;
+    if (d->n_entries >= (int64_t)1 << 31) return CSA_ERR_UNSUPPORTED;
+  } else {
+    if (d->n < 0) return CSA_ERR_INVALID_ARG;
+    const int64_t vis = d->n / d->m < d->n_entries ? d->n / d->m : d->n_entries;
+    if (vis > 256 * 64) return CSA_ERR_UNSUPPORTED;  // row held in registers
+  }
+  return CSA_OK;
+}
+
+int64_t index_prefill_ld(const csa_index_desc* d) {
+  const int64_t vis = d->n / d->m < d->n_entries ? d->n / d->m : d->n_entries;
+  return (vis + 3) & ~(int64_t)3;
+}
+
+// -------------------------------------------------------------- attention
+int check_attn(const csa_attn_desc* d, bool decode, bool sparse) {
+  if (!d) return CSA_ERR_INVALID_ARG;
+  if (!dtype_ok(d->dtype)) return CSA_ERR_UNSUPPORTED;
+  if (d->n_heads <= 0 || d->n_win <= 0 || d->n_entries < 0) return CSA_ERR_INVALID_ARG;
+  if (d->n_heads > 64) return CSA_ERR_UNSUPPORTED;
+  if (!(d->c == 128 || d->c == 256 || d->c == 512)) return CSA_ERR_UNSUPPORTED;
+  if (sparse && d->k <= 0) return CSA_ERR_INVALID_ARG;
+  if (!sparse && d->m <= 0) return CSA_ERR_INVALID_ARG;
+  if (d->rope_dims < 0 || d->rope_dims > d->c || (d->rope_dims % 8)) return CSA_ERR_UNSUPPORTED;
+  if (d->rope_dims > 0 && !(d->rope_theta > 0.f)) return CSA_ERR_INVALID_ARG;
+  if (decode ? d->batch <= 0 : d->n < 0) return CSA_ERR_INVALID_ARG;
+  return CSA_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? CSA_OK : CSA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int csa_abi_version(void) { return CSA_ABI_VERSION; }
+
+const char* csa_status_string(int s) {
+  switch (s) {
+    case CSA_OK: return "ok";
+    case CSA_ERR_INVALID_ARG: return "invalid argument (null pointer or inconsistent sizes)";
+    case CSA_ERR_UNSUPPORTED: return "unsupported shape or dtype for these kernels";
+    case CSA_ERR_WORKSPACE: return "workspace smaller than csa_workspace_bytes()";
+    case CSA_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+size_t csa_state_bytes(const csa_compress_desc* d) {
+  if (!d || d->c <= 0) return 0;
+  const int b = d->batch > 0 ? d->batch : 1;
+  return (size_t)b * (d->overlap ? 3 : 1) * 3 * d->c * 4;
+}
+
+size_t csa_workspace_bytes(int entry, const void* desc) {
+  if (!desc) return 0;
+  switch (entry) {
+    case CSA_ENTRY_COMPRESS_PREFILL: {
+      const csa_compress_desc* d = (const csa_compress_desc*)desc;
+      if (d->n <= 0 || d->c <= 0) return 0;
+      return ws_compress_prefill(d, true);
+    }
+    case CSA_ENTRY_COMPRESS_DECODE: {
+      const csa_compress_desc* d = (const csa_compress_desc*)desc;
+      if (d->batch <= 0 || d->c <= 0 || d->d <= 0) return 0;
+      return ws_compress_decode(d, true);
+    }
+    case CSA_ENTRY_INDEX_TOPK_PREFILL: {
+      const csa_index_desc* d = (const csa_index_desc*)desc;
+      if (d->m <= 0 || d->n <= 0) return 0;
+      return al((size_t)d->n * index_prefill_ld(d) * 4);
+    }
+    case CSA_ENTRY_INDEX_TOPK_DECODE: {
+      const csa_index_desc* d = (const csa_index_desc*)desc;
+      if (d->batch <= 0) return 0;
+      return index_decode_ws_bytes(*d);
+    }
+    case CSA_ENTRY_SPARSE_MQA_PREFILL:
+    case CSA_ENTRY_DENSE_MQA_PREFILL: return 0;
+    case CSA_ENTRY_SPARSE_MQA_DECODE:
+    case CSA_ENTRY_DENSE_MQA_DECODE: {
+      const csa_attn_desc* d = (const csa_attn_desc*)desc;
+      if (d->batch <= 0 || d->n_heads <= 0 || d->c <= 0) return 0;
+      return mqa_decode_ws_bytes(*d, entry == CSA_ENTRY_SPARSE_MQA_DECODE ? ATTN_SPARSE : ATTN_DENSE);
+    }
+    default: return 0;
+  }
+}
+
+int csa_state_init(const csa_compress_desc* d, float* state, void* stream) {
+  if (!d || !state || d->c <= 0 || d->batch <= 0) return CSA_ERR_INVALID_ARG;
+  const int64_t per = (int64_t)(d->overlap ? 3 : 1) * 3 * d->c;
+  return hip_status(launch_state_init(state, per, d->batch, d->c, (hipStream_t)stream));
+}
+
+int csa_compress_prefill(const csa_compress_desc* d, const void* H, const void* W_kv,
+                         const void* W_z, const float* ape, const void* W_win, void* out_comp,
+                         void* out_win, void* win_ring, float* state, void* ws, size_t ws_bytes,
+                         void* stream) {
+  int s = check_compress(d, false);
+  if (s) return s;
+  const bool has_win = W_win != nullptr;
+  if ((out_win || win_ring) && !has_win) return CSA_ERR_INVALID_ARG;
+  if (win_ring && d->n_win <= 0) return CSA_ERR_INVALID_ARG;
+  const int64_t nc = d->n / d->m;
+  if (d->n > 0 && (!H || !W_kv || !W_z || !ape)) return CSA_ERR_INVALID_ARG;
+  if (nc > 0 && !out_comp) return CSA_ERR_INVALID_ARG;
+  const size_t need = d->n > 0 ? ws_compress_prefill(d, has_win) : 0;
+  if (need > 0 && (!ws || ws_bytes < need)) return CSA_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const int w = (1 + d->overlap) * d->c;
+  const int64_t ld = 2 * w + (has_win ? d->c : 0);
+  float* P = (float*)ws;
+  if (d->n > 0) {
+    WeightStack stack = {{W_kv, W_z, W_win}, {w, w, has_win ? d->c : 0}};
+    hipError_t e = launch_proj_gemm(d->dtype, H, d->n, d->d, stack, P, ld, st);
+    if (e != hipSuccess) return CSA_ERR_HIP;
+    e = launch_pool_entries(d->dtype, P, ld, d->n, d->c, d->m, d->overlap, ape, d->qk_norm, d->eps,
+                            d->rope_dims, d->rope_theta, out_comp, 0, st);
+    if (e != hipSuccess) return CSA_ERR_HIP;
+    if (has_win && (out_win || win_ring)) {
+      e = launch_window_rows(d->dtype, P, ld, 2 * w, d->n, d->c, d->qk_norm, d->eps, d->rope_dims,
+                             d->rope_theta, out_win, win_ring, d->n_win, 0, st);
+      if (e != hipSuccess) return CSA_ERR_HIP;
+    }
+  }
+  if (state) {
+    hipError_t e = launch_stash_state(P, ld, d->n, d->c, d->m, d->overlap, ape, state, st);
+    if (e != hipSuccess) return CSA_ERR_HIP;
+  }
+  return CSA_OK;
+}
+
+int csa_compress_decode(const csa_compress_desc* d, const void* h, const int64_t* pos,
+                        const void* W_kv, const void* W_z, const float* ape, const void* W_win,
+                        float* state, void* cache, void* win_ring, void* ws, size_t ws_bytes,
+                        void* stream) {
+  int s = check_compress(d, true);
+  if (s) return s;
+  if (!h || !pos || !W_kv || !W_z || !ape || !state || !cache) return CSA_ERR_INVALID_ARG;
+  const bool has_win = W_win != nullptr;
+  if (has_win != (win_ring != nullptr)) return CSA_ERR_INVALID_ARG;
+  if (has_win && d->n_win <= 0) return CSA_ERR_INVALID_ARG;
+  const size_t need = ws_compress_decode(d, has_win);
+  if (!ws || ws_bytes < need) return CSA_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const int w = (1 + d->overlap) * d->c;
+  const int N = 2 * w + (has_win ? d->c : 0);
+  const int ks = decode_proj_ksplit(N, d->d, d->dtype);
+  WeightStack stack = {{W_kv, W_z, W_win}, {w, w, has_win ? d->c : 0}};
+  hipError_t e = launch_decode_proj(d->dtype, h, d->batch, d->d, stack, (float*)ws, ks, st);
+  if (e != hipSuccess) return CSA_ERR_HIP;
+  e = launch_decode_update(d->dtype, (const float*)ws, ks, d->batch, N, d->c, d->m, d->overlap,
+                           has_win, ape, pos, state, cache, d->max_entries, win_ring, d->n_win,
+                           d->qk_norm, d->eps, d->rope_dims, d->rope_theta, st);
+  return hip_status(e);
+}
+
+int csa_index_topk_prefill(const csa_index_desc* d, const void* qI, const void* wI,
+                           const void* KI, int32_t* idx_out, void* ws, size_t ws_bytes,
+                           void* stream) {
+  int s = check_index(d, false);
+  if (s) return s;
+  if (d->n == 0) return CSA_OK;
+  if (!qI || !wI || !idx_out || (d->n_entries > 0 && !KI)) return CSA_ERR_INVALID_ARG;
+  const int64_t ld = index_prefill_ld(d);
+  const size_t need = al((size_t)d->n * ld * 4);
+  if (ld > 0 && (!ws || ws_bytes < need)) return CSA_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (ld > 0) e = launch_index_scores_prefill(*d, qI, wI, KI, (float*)ws, ld, st);
+  if (e != hipSuccess) return CSA_ERR_HIP;
+  return hip_status(launch_topk_rows_prefill(*d, (const float*)ws, ld, idx_out, st));
+}
+
+int csa_index_topk_decode(const csa_index_desc* d, const void* qI, const void* wI,
+                          const void* KI_cache, const int64_t* pos, int32_t* idx_out, void* ws,
+                          size_t ws_bytes, void* stream) {
+  int s = check_index(d, true);
+  if (s) return s;
+  if (!qI || !wI || !KI_cache || !pos || !idx_out) return CSA_ERR_INVALID_ARG;
+  const size_t need = index_decode_ws_bytes(*d);
+  if (!ws || ws_bytes < need) return CSA_ERR_WORKSPACE;
+  return hip_status(launch_index_topk_decode(*d, qI, wI, KI_cache, pos, idx_out, ws,
+                                             (hipStream_t)stream));
+}
+
+int csa_sparse_mqa_prefill(const csa_attn_desc* d, const void* q, const void* win_kv,
+                           const void* comp, const int32_t* idx, const float* sink, void* out,
+                           void* ws, size_t ws_bytes, void* stream) {
+  (void)ws; (void)ws_bytes;
+  int s = check_attn(d, false, true);
+  if (s) return s;
+  if (d->n == 0) return CSA_OK;
+  if (!q || !win_kv || !idx || !sink || !out || (d->n_entries > 0 && !comp))
+    return CSA_ERR_INVALID_ARG;
+  return hip_status(launch_mqa_prefill(*d, ATTN_SPARSE, q, win_kv, comp, idx, sink, out,
+                                       (hipStream_t)stream));
+}
+
+int csa_sparse_mqa_decode(const csa_attn_desc* d, const void* q, const void* win_ring,
+                          const void* comp_cache, const int32_t* idx, const int64_t* pos,
+                          const float* sink, void* out, void* ws, size_t ws_bytes, void* stream) {
+  int s = check_attn(d, true, true);
+  if (s) return s;
+  if (!q || !win_ring || !comp_cache || !idx || !pos || !sink || !out) return CSA_ERR_INVALID_ARG;
+  const size_t need = mqa_decode_ws_bytes(*d, ATTN_SPARSE);
+  if (!ws || ws_bytes < need) return CSA_ERR_WORKSPACE;
+  return hip_status(launch_mqa_decode(*d, ATTN_SPARSE, q, win_ring, comp_cache, idx, pos, sink,
+                                      out, ws, (hipStream_t)stream));
+}
+
+int hca_dense_mqa_prefill(const csa_attn_desc* d, const void* q, const void* win_kv,
+                          const void* comp, const float* sink, void* out, void* ws,
+                          size_t ws_bytes, void* stream) {
+  (void)ws; (void)ws_bytes;
+  int s = check_attn(d, false, false);
+  if (s) return s;
+  if (d->n == 0) return CSA_OK;
+  if (!q || !win_kv || !sink || !out || (d->n_entries > 0 && !comp)) return CSA_ERR_INVALID_ARG;
+  return hip_status(launch_mqa_prefill(*d, ATTN_DENSE, q, win_kv, comp, nullptr, sink, out,
+                                       (hipStream_t)stream));
+}
+
+int hca_dense_mqa_decode(const csa_attn_desc* d, const void* q, const void* win_ring,
+                         const void* comp_cache, const int64_t* pos, const float* sink, void* out,
+                         void* ws, size_t ws_bytes, void* stream) {
+  int s = check_attn(d, true, false);
+  if (s) return s;
+  if (!q || !win_ring || !comp_cache || !pos || !sink || !out) return CSA_ERR_INVALID_ARG;
+  const size_t need = mqa_decode_ws_bytes(*d, ATTN_DENSE);
+  if (!ws || ws_bytes < need) return CSA_ERR_WORKSPACE;
+  return hip_status(launch_mqa_decode(*d, ATTN_DENSE, q, win_ring, comp_cache, nullptr, pos, sink,
+                                      out, ws, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,560 @@
+// Compressor kernels: projection GEMM, block softmax pooling with the entry
+// epilogue, window rows, and the decode-time online pooling state.
+//
+// Citation keys: [R] = page "DeepSeek-V4 技术解读报告" (juejin.cn), section
+// 2.3.1 eq 9-12 (overlapped CSA compression), 2.3.2 eq 20-23 (HCA), 2.3.3
+// (QK RMSNorm, partial RoPE); [A] = page "DeepSeek-V4：算法架构"
+// (1zeryu.github.io), Compressor class (prefill and decode branches) and the
+// attention's wkv -> kv_norm -> RoPE window path.
+#include "csa_common.h"
+#include "csa_launch.h"
+
+namespace csa {
+
+// ===========================================================================
+// Projection GEMM:  out[M, 0:N] (fp32) = A[M, K] . [W0; W1; W2]^T
+// 128x128 output tile per 256-thread workgroup (2x2 waves of 64x64), K staged
+// through LDS in 128-byte slices, double buffered.  Both operands are K-major
+// in memory (A rows = tokens, W rows = output channels), so every lane feeds
+// the matrix cores with one 16-byte LDS read per operand and k-group.
+// ===========================================================================
+template <class T>
+__global__ __launch_bounds__(256, 2) void proj_gemm_kernel(
+    const typename T::S* __restrict__ A, int64_t M, int K, const typename T::S* __restrict__ W0,
+    int r0, const typename T::S* __restrict__ W1, int r1, const typename T::S* __restrict__ W2,
+    int r2, float* __restrict__ out, int64_t ldo) {
+  typedef typename T::S S;
+  constexpr int BM = 128, BN = 128, BKB = 128;
+  constexpr int E = 16 / (int)sizeof(S);
+  constexpr int BK = BKB / (int)sizeof(S);
+  constexpr int LDB = BKB + 16;
+  __shared__ __align__(16) uint8_t sA[2][BM * LDB];
+  __shared__ __align__(16) uint8_t sB[2][BN * LDB];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t m0 = (int64_t)blockIdx.y * BM;
+  const int n0 = blockIdx.x * BN;
+  const int ntot = r0 + r1 + r2;
+
+  const S* a_ptr[4];
+  const S* b_ptr[4];
+  bool a_ok[4], b_ok[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = (tid >> 3) + 32 * q;
+    const int64_t gm = m0 + row;
+    a_ok[q] = gm < M;
+    a_ptr[q] = A + (a_ok[q] ? gm : 0) * (int64_t)K + (tid & 7) * E;
+    const int j = n0 + row;
+    const S* wp = W0;
+    int jr = j;
+    if (jr >= r0) { jr -= r0; wp = W1; if (jr >= r1) { jr -= r1; wp = W2; } }
+    b_ok[q] = j < ntot;
+    b_ptr[q] = wp + (int64_t)(b_ok[q] ? jr : 0) * K + (tid & 7) * E;
+    if (!b_ok[q]) b_ptr[q] = W0;
+  }
+
+  uint4 ra[4], rb[4];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      ra[q] = a_ok[q] ? *(const uint4*)(a_ptr[q] + (int64_t)kt * BK) : make_uint4(0, 0, 0, 0);
+      rb[q] = b_ok[q] ? *(const uint4*)(b_ptr[q] + (int64_t)kt * BK) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = (tid >> 3) + 32 * q;
+      *(uint4*)(sA[buf] + row * LDB + (tid & 7) * 16) = ra[q];
+      *(uint4*)(sB[buf] + row * LDB + (tid & 7) * 16) = rb[q];
+    }
+  };
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
+
+  const int nk = K / BK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) gload(kt + 1);
+    const uint8_t* As = sA[kt & 1];
+    const uint8_t* Bs = sB[kt & 1];
+#pragma unroll
+    for (int kg = 0; kg < BKB / 32; ++kg) {
+      uint4 a[2], b[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        a[mb] = *(const uint4*)(As + (wm * 64 + mb * 32 + (lane & 31)) * LDB + kg * 32 + (lane >> 5) * 16);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+        b[nb] = *(const uint4*)(Bs + (wn * 64 + nb * 32 + (lane & 31)) * LDB + kg * 32 + (lane >> 5) * 16);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) mma32<T>(acc[mb][nb], a[mb], b[nb]);
+    }
+    if (kt + 1 < nk) sstore((kt + 1) & 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int col = n0 + wn * 64 + nb * 32 + (lane & 31);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int64_t row = m0 + wm * 64 + mb * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        if (row < M && col < ntot) out[row * ldo + col] = acc[mb][nb][i];
+      }
+    }
+}
+
+// ===========================================================================
+// Row epilogue shared by entries, window rows and decode emission: a group of
+// G = c/2 threads owns one row of width c, thread j the channel pair
+// (2j, 2j+1).  RMSNorm (unit weight) over the row, then RoPE of the last r
+// channels at `pos` ([R] 2.3.3; pairs are adjacent channels).
+// `red` is LDS scratch of at least (blockDim / 64) floats, used when G > 64.
+// Every thread of the block must call this (it may synchronise).
+// ===========================================================================
+template <int G>
+CSA_DEV void row_finish(float& v0, float& v1, int j, int c, int64_t pos, int qk_norm, float eps,
+                        int r, float theta, float* red) {
+  if (qk_norm) {
+    float s = v0 * v0 + v1 * v1;
+    if (G <= 64) {
+#pragma unroll
+      for (int o = G / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
+    } else {
+      s = wave_sum(s);
+      const int w = threadIdx.x >> 6;
+      __syncthreads();
+      if ((threadIdx.x & 63) == 0) red[w] = s;
+      __syncthreads();
+      const int g0 = (w / (G / 64)) * (G / 64);
+      s = 0.f;
+#pragma unroll
+      for (int i = 0; i < G / 64; ++i) s += red[g0 + i];
+    }
+    const float inv = rsqrtf(s / (float)c + eps);
+    v0 *= inv;
+    v1 *= inv;
+  }
+  if (r > 0 && 2 * j >= c - r) {
+    float cs, sn;
+    rope_cs(pos, j - (c - r) / 2, r, theta, &cs, &sn);
+    const float x0 = v0, x1 = v1;
+    v0 = x0 * cs - x1 * sn;
+    v1 = x0 * sn + x1 * cs;
+  }
+}
+
+// Online softmax accumulation of one (logit, value) pair.
+CSA_DEV void osm_push(float& mx, float& sm, float& ac, float lg, float v) {
+  const float nm = fmaxf(mx, lg);
+  const float a = __expf(mx - nm);  // mx = -inf on first use -> 0
+  const float b = __expf(lg - nm);
+  sm = sm * a + b;
+  ac = ac * a + v * b;
+  mx = nm;
+}
+// Merge state 2 into state 1 (either may be empty: mx = -inf, sm = ac = 0).
+CSA_DEV void osm_merge(float& m1, float& s1, float& a1, float m2, float s2, float a2) {
+  const float nm = fmaxf(m1, m2);
+  if (nm == -INFINITY) return;
+  const float x = __expf(m1 - nm), y = __expf(m2 - nm);
+  s1 = s1 * x + s2 * y;
+  a1 = a1 * x + a2 * y;
+  m1 = nm;
+}
+
+// ===========================================================================
+// Pool complete blocks ([R] eq 11-12 / 22-23) and finish each entry.
+// Scratch P[t][ld]: C at columns [0, w), Z at [w, 2w), w = (1+ov) c; under
+// overlap columns [0, c) of each are the b-series and [c, 2c) the a-series.
+// ===========================================================================
+template <class T, int G>
+__global__ __launch_bounds__(256) void pool_entries_kernel(
+    const float* __restrict__ P, int64_t ld, int64_t n_entries, int c, int m, int ov,
+    const float* __restrict__ ape, int qk_norm, float eps, int r, float theta,
+    typename T::S* __restrict__ out, int64_t pos0) {
+  __shared__ float red[4];
+  constexpr int GPW = 256 / G;
+  const int g = threadIdx.x / G, j = threadIdx.x % G;
+  const int64_t i = (int64_t)blockIdx.x * GPW + g;
+  const bool live = i < n_entries;
+  const int w = (1 + ov) * c;
+  const int ca = ov ? c : 0;  // a-series column offset
+  float v0 = 0.f, v1 = 0.f;
+  if (live) {
+    float mx0 = -INFINITY, s0 = 0.f, a0 = 0.f, mx1 = -INFINITY, s1 = 0.f, a1 = 0.f;
+    for (int rr = 0; rr < m; ++rr) {
+      const float* row = P + (i * m + rr) * ld;
+      const float2 cv = *(const float2*)(row + ca + 2 * j);
+      const float2 zv = *(const float2*)(row + w + ca + 2 * j);
+      const float2 bv = *(const float2*)(ape + (int64_t)rr * w + ca + 2 * j);
+      osm_push(mx0, s0, a0, zv.x + bv.x, cv.x);
+      osm_push(mx1, s1, a1, zv.y + bv.y, cv.y);
+    }
+    if (ov && i > 0) {  // block i-1's b-series joins the same softmax
+      for (int rr = 0; rr < m; ++rr) {
+        const float* row = P + ((i - 1) * m + rr) * ld;
+        const float2 cv = *(const float2*)(row + 2 * j);
+        const float2 zv = *(const float2*)(row + w + 2 * j);
+        const float2 bv = *(const float2*)(ape + (int64_t)rr * w + 2 * j);
+        osm_push(mx0, s0, a0, zv.x + bv.x, cv.x);
+        osm_push(mx1, s1, a1, zv.y + bv.y, cv.y);
+      }
+    }
+    v0 = a0 / s0;
+    v1 = a1 / s1;
+  }
+  row_finish<G>(v0, v1, j, c, (int64_t)m * (pos0 / m + i), qk_norm, eps, r, theta, red);
+  if (live) {
+    T::st(out, i * c + 2 * j, v0);
+    T::st(out, i * c + 2 * j + 1, v1);
+  }
+}
+
+// Window rows: V (scratch column `col`, width c) -> RMSNorm, RoPE at t.
+template <class T, int G>
+__global__ __launch_bounds__(256) void window_rows_kernel(
+    const float* __restrict__ P, int64_t ld, int col, int64_t n, int c, int qk_norm, float eps,
+    int r, float theta, typename T::S* __restrict__ out, typename T::S* __restrict__ ring,
+    int n_win, int64_t pos0) {
+  __shared__ float red[4];
+  constexpr int GPW = 256 / G;
+  const int g = threadIdx.x / G, j = threadIdx.x % G;
+  const int64_t t = (int64_t)blockIdx.x * GPW + g;
+  const bool live = t < n;
+  float v0 = 0.f, v1 = 0.f;
+  if (live) {
+    const float2 v = *(const float2*)(P + t * ld + col + 2 * j);
+    v0 = v.x;
+    v1 = v.y;
+  }
+  row_finish<G>(v0, v1, j, c, pos0 + t, qk_norm, eps, r, theta, red);
+  if (live) {
+    if (out) {
+      T::st(out, t * c + 2 * j, v0);
+      T::st(out, t * c + 2 * j + 1, v1);
+    }
+    if (ring && t >= n - n_win) {
+      const int64_t s = (pos0 + t) % n_win;
+      T::st(ring, s * c + 2 * j, v0);
+      T::st(ring, s * c + 2 * j + 1, v1);
+    }
+  }
+}
+
+// ===========================================================================
+// Decode state (per sequence, fp32): NS series x {running max, sum, weighted
+// sum} x c channels.  Series 0 = the current block's a-series (the only
+// series without overlap), 1 = the current block's b-series, 2 = the previous
+// (complete) block's b-series.
+// ===========================================================================
+__global__ void state_init_kernel(float* __restrict__ st, int64_t per_seq, int c, int batch) {
+  const int64_t total = per_seq * batch;
+  for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < total;
+       x += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t within = (x % per_seq) / c;  // series*3 + field
+    st[x] = (within % 3 == 0) ? -INFINITY : 0.f;
+  }
+}
+
+// After a prefill of n tokens: series 0/1 fold the tail rows of block n/m,
+// series 2 folds the b-series of the last complete block.
+__global__ void stash_state_kernel(const float* __restrict__ P, int64_t ld, int64_t n, int c,
+                                   int m, int ov, const float* __restrict__ ape,
+                                   float* __restrict__ st) {
+  const int w = (1 + ov) * c;
+  const int64_t nc = n / m;
+  const int tail = (int)(n - nc * m);
+  const int ns = ov ? 3 : 1;
+  for (int ch = threadIdx.x; ch < c; ch += blockDim.x) {
+    for (int s = 0; s < ns; ++s) {
+      float mx = -INFINITY, sm = 0.f, ac = 0.f;
+      int64_t t0;
+      int rows, coff;
+      if (s == 0) { t0 = nc * m; rows = tail; coff = ov ? c : 0; }
+      else if (s == 1) { t0 = nc * m; rows = tail; coff = 0; }
+      else { t0 = (nc - 1) * m; rows = nc >= 1 ? m : 0; coff = 0; }
+      for (int rr = 0; rr < rows; ++rr) {
+        const float* row = P + (t0 + rr) * ld;
+        osm_push(mx, sm, ac, row[w + coff + ch] + ape[(int64_t)rr * w + coff + ch], row[coff + ch]);
+      }
+      st[(s * 3 + 0) * c + ch] = mx;
+      st[(s * 3 + 1) * c + ch] = sm;
+      st[(s * 3 + 2) * c + ch] = ac;
+    }
+  }
+}
+
+// ===========================================================================
+// Decode projection: part[ks][b][j] = sum over the ks-th K slice of
+// h[b, :] . W_j.  One 32x32 (batch x channel) tile per workgroup and K slice;
+// the four waves split the slice further and are summed in a fixed order, so
+// results are bitwise reproducible.  The weights are the bytes that bound
+// this step: each is read exactly once.
+// ===========================================================================
+template <class T>
+__global__ __launch_bounds__(256) void decode_proj_kernel(
+    const typename T::S* __restrict__ h, int B, int K, const typename T::S* __restrict__ W0,
+    int r0, const typename T::S* __restrict__ W1, int r1, const typename T::S* __restrict__ W2,
+    int r2, float* __restrict__ part, int ksplit) {
+  typedef typename T::S S;
+  constexpr int E = 16 / (int)sizeof(S);
+  constexpr int KG = 2 * E;  // elements per 32x32 k-group
+  __shared__ float red[4][32 * 33];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ntot = r0 + r1 + r2;
+  const int j0 = blockIdx.x * 32;
+  const int ks = blockIdx.y;
+  const int b0 = blockIdx.z * 32;
+  const int kslice = K / ksplit, kw = kslice / 4;
+  const int kbeg = ks * kslice + wave * kw;
+
+  const int jr0 = j0 + (lane & 31);
+  const S* wp = W0;
+  int jr = jr0;
+  if (jr >= r0) { jr -= r0; wp = W1; if (jr >= r1) { jr -= r1; wp = W2; } }
+  const bool wok = jr0 < ntot;
+  const S* wrow = wok ? wp + (int64_t)jr * K : W0;
+  const int b = b0 + (lane & 31);
+  const bool hok = b < B;
+  const S* hrow = h + (int64_t)(hok ? b : 0) * K;
+
+  f32x16_t acc = f32x16_t{};
+  const int koff = (lane >> 5) * E;
+  for (int k = kbeg; k < kbeg + kw; k += KG * 4) {
+    uint4 a[4], bw[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int kk = k + u * KG + koff;
+      const bool in = kk < kbeg + kw;
+      a[u] = (hok && in) ? *(const uint4*)(hrow + kk) : make_uint4(0, 0, 0, 0);
+      bw[u] = (wok && in) ? *(const uint4*)(wrow + kk) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) mma32<T>(acc, a[u], bw[u]);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int row = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+    red[wave][row * 33 + (lane & 31)] = acc[i];
+  }
+  __syncthreads();
+  for (int e = tid; e < 32 * 32; e += 256) {
+    const int row = e >> 5, col = e & 31;
+    const float v = red[0][row * 33 + col] + red[1][row * 33 + col] + red[2][row * 33 + col] +
+                    red[3][row * 33 + col];
+    if (b0 + row < B && j0 + col < ntot)
+      part[((int64_t)ks * B + b0 + row) * ntot + j0 + col] = v;
+  }
+}
+
+// One workgroup per sequence: sum the K-split partials, fold the new row into
+// the online state, emit the finished entry when (pos+1) % m == 0, and write
+// the window row into the ring ([A] Compressor decode branch).
+template <class T, int G>
+__global__ __launch_bounds__(256) void decode_update_kernel(
+    const float* __restrict__ part, int ksplit, int B, int N, int c, int m, int ov, int has_win,
+    const float* __restrict__ ape, const int64_t* __restrict__ posv, float* __restrict__ state,
+    typename T::S* __restrict__ cache, int64_t max_entries, typename T::S* __restrict__ ring,
+    int n_win, int qk_norm, float eps, int r, float theta) {
+  __shared__ float red[4];
+  const int b = blockIdx.x;
+  const int j = threadIdx.x;  // channel pair (2j, 2j+1)
+  const bool live = j < G;
+  const int64_t pos = posv[b];
+  if (pos < 0) return;  // uniform per block: no token for this sequence
+  const int w = (1 + ov) * c;
+  const int ns = ov ? 3 : 1;
+  float* st = state + (int64_t)b * ns * 3 * c;
+  const int rr = (int)(pos % m);
+  const bool emit = (rr == m - 1);
+  const int64_t blk = pos / m;
+
+  auto colsum = [&](int col) {
+    float s = 0.f;
+    for (int k = 0; k < ksplit; ++k) s += part[((int64_t)k * B + b) * N + col];
+    return s;
+  };
+
+  float e0 = 0.f, e1 = 0.f;
+  if (live) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int ch = 2 * j + q;
+      // a-series (or the only series)
+      const int ca = ov ? c : 0;
+      float mx = st[0 * c + ch], sm = st[1 * c + ch], ac = st[2 * c + ch];
+      osm_push(mx, sm, ac, colsum(w + ca + ch) + ape[(int64_t)rr * w + ca + ch], colsum(ca + ch));
+      float mb = -INFINITY, sb = 0.f, ab = 0.f;
+      if (ov) {
+        mb = st[3 * c + ch]; sb = st[4 * c + ch]; ab = st[5 * c + ch];
+        osm_push(mb, sb, ab, colsum(w + ch) + ape[(int64_t)rr * w + ch], colsum(ch));
+      }
+      if (emit) {
+        float em = mx, es = sm, ea = ac;
+        if (ov) osm_merge(em, es, ea, st[6 * c + ch], st[7 * c + ch], st[8 * c + ch]);
+        const float v = ea / es;
+        if (q == 0) e0 = v; else e1 = v;
+        // the block is finished: its b-series becomes "previous", the rest resets
+        if (ov) { st[6 * c + ch] = mb; st[7 * c + ch] = sb; st[8 * c + ch] = ab; }
+        mx = -INFINITY; sm = 0.f; ac = 0.f;
+        mb = -INFINITY; sb = 0.f; ab = 0.f;
+      }
+      st[0 * c + ch] = mx; st[1 * c + ch] = sm; st[2 * c + ch] = ac;
+      if (ov) { st[3 * c + ch] = mb; st[4 * c + ch] = sb; st[5 * c + ch] = ab; }
+    }
+  }
+  if (emit) {  // uniform across the block
+    row_finish<G>(e0, e1, j, c, (int64_t)m * blk, qk_norm, eps, r, theta, red);
+    if (live && blk < max_entries) {
+      typename T::S* dst = cache + ((int64_t)b * max_entries + blk) * c;
+      T::st(dst, 2 * j, e0);
+      T::st(dst, 2 * j + 1, e1);
+    }
+  }
+  if (has_win) {
+    float v0 = 0.f, v1 = 0.f;
+    if (live) { v0 = colsum(2 * w + 2 * j); v1 = colsum(2 * w + 2 * j + 1); }
+    row_finish<G>(v0, v1, j, c, pos, qk_norm, eps, r, theta, red);
+    if (live) {
+      typename T::S* dst = ring + ((int64_t)b * n_win + pos % n_win) * c;
+      T::st(dst, 2 * j, v0);
+      T::st(dst, 2 * j + 1, v1);
+    }
+  }
+}
+
+// ===========================================================================
+// Host launchers
+// ===========================================================================
+hipError_t launch_proj_gemm(int dtype, const void* A, int64_t M, int K, const WeightStack& w,
+                            float* out, int64_t ldo, hipStream_t st) {
+  const int N = w.total();
+  dim3 grid((N + 127) / 128, (unsigned)((M + 127) / 128));
+  if (dtype == CSA_BF16) {
+    typedef BF16::S S;
+    proj_gemm_kernel<BF16><<<grid, 256, 0, st>>>((const S*)A, M, K, (const S*)w.w[0], w.rows[0],
+                                                  (const S*)w.w[1], w.rows[1], (const S*)w.w[2],
+                                                  w.rows[2], out, ldo);
+  } else {
+    proj_gemm_kernel<F32><<<grid, 256, 0, st>>>((const float*)A, M, K, (const float*)w.w[0],
+                                                 w.rows[0], (const float*)w.w[1], w.rows[1],
+                                                 (const float*)w.w[2], w.rows[2], out, ldo);
+  }
+  return hipGetLastError();
+}
+
+#define CSA_DISPATCH_G(c, ...)                                  \
+  switch (c) {                                                  \
+    case 32: { constexpr int G = 16; __VA_ARGS__; } break;      \
+    case 64: { constexpr int G = 32; __VA_ARGS__; } break;      \
+    case 128: { constexpr int G = 64; __VA_ARGS__; } break;     \
+    case 256: { constexpr int G = 128; __VA_ARGS__; } break;    \
+    case 512: { constexpr int G = 256; __VA_ARGS__; } break;    \
+    default: return hipErrorInvalidValue;                       \
+  }
+
+hipError_t launch_pool_entries(int dtype, const float* P, int64_t ld, int64_t n, int c, int m,
+                               int ov, const float* ape, int qk_norm, float eps, int r,
+                               float theta, void* out, int64_t pos0, hipStream_t st) {
+  const int64_t ne = n / m;
+  if (ne == 0) return hipSuccess;
+  CSA_DISPATCH_G(c, {
+    dim3 grid((unsigned)((ne + 256 / G - 1) / (256 / G)));
+    if (dtype == CSA_BF16)
+      pool_entries_kernel<BF16, G><<<grid, 256, 0, st>>>(P, ld, ne, c, m, ov, ape, qk_norm, eps, r,
+                                                         theta, (BF16::S*)out, pos0);
+    else
+      pool_entries_kernel<F32, G><<<grid, 256, 0, st>>>(P, ld, ne, c, m, ov, ape, qk_norm, eps, r,
+                                                        theta, (float*)out, pos0);
+  });
+  return hipGetLastError();
+}
+
+hipError_t launch_window_rows(int dtype, const float* P, int64_t ld, int col, int64_t n, int c,
+                              int qk_norm, float eps, int r, float theta, void* out, void* ring,
+                              int n_win, int64_t pos0, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  CSA_DISPATCH_G(c, {
+    dim3 grid((unsigned)((n + 256 / G - 1) / (256 / G)));
+    if (dtype == CSA_BF16)
+      window_rows_kernel<BF16, G><<<grid, 256, 0, st>>>(P, ld, col, n, c, qk_norm, eps, r, theta,
+                                                        (BF16::S*)out, (BF16::S*)ring, n_win, pos0);
+    else
+      window_rows_kernel<F32, G><<<grid, 256, 0, st>>>(P, ld, col, n, c, qk_norm, eps, r, theta,
+                                                       (float*)out, (float*)ring, n_win, pos0);
+  });
+  return hipGetLastError();
+}
+
+hipError_t launch_stash_state(const float* P, int64_t ld, int64_t n, int c, int m, int ov,
+                              const float* ape, float* state, hipStream_t st) {
+  stash_state_kernel<<<1, 256, 0, st>>>(P, ld, n, c, m, ov, ape, state);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_init(float* state, int64_t per_seq, int batch, int c, hipStream_t st) {
+  const int64_t total = per_seq * batch;
+  const unsigned blocks = (unsigned)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
+  state_init_kernel<<<blocks, 256, 0, st>>>(state, per_seq, c, batch);
+  return hipGetLastError();
+}
+
+int decode_proj_ksplit(int N, int K, int dtype) {
+  const int kg4 = (dtype == CSA_BF16 ? 16 : 8) * 4;  // smallest per-wave slice
+  const int tiles = (N + 31) / 32;
+  int ks = 1;
+  while (tiles * ks < 512 && K % (ks * 2 * kg4) == 0 && ks < 64) ks *= 2;
+  return ks;
+}
+
+hipError_t launch_decode_proj(int dtype, const void* h, int B, int K, const WeightStack& w,
+                              float* part, int ksplit, hipStream_t st) {
+  const int N = w.total();
+  dim3 grid((N + 31) / 32, ksplit, (B + 31) / 32);
+  if (dtype == CSA_BF16) {
+    typedef BF16::S S;
+    decode_proj_kernel<BF16><<<grid, 256, 0, st>>>((const S*)h, B, K, (const S*)w.w[0], w.rows[0],
+                                                    (const S*)w.w[1], w.rows[1], (const S*)w.w[2],
+                                                    w.rows[2], part, ksplit);
+  } else {
+    decode_proj_kernel<F32><<<grid, 256, 0, st>>>((const float*)h, B, K, (const float*)w.w[0],
+                                                   w.rows[0], (const float*)w.w[1], w.rows[1],
+                                                   (const float*)w.w[2], w.rows[2], part, ksplit);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_update(int dtype, const float* part, int ksplit, int B, int N, int c,
+                                int m, int ov, int has_win, const float* ape, const int64_t* pos,
+                                float* state, void* cache, int64_t max_entries, void* ring,
+                                int n_win, int qk_norm, float eps, int r, float theta,
+                                hipStream_t st) {
+  CSA_DISPATCH_G(c, {
+    const int threads = G < 64 ? 64 : G;
+    if (dtype == CSA_BF16)
+      decode_update_kernel<BF16, G><<<B, threads, 0, st>>>(
+          part, ksplit, B, N, c, m, ov, has_win, ape, pos, state, (BF16::S*)cache, max_entries,
+          (BF16::S*)ring, n_win, qk_norm, eps, r, theta);
+    else
+      decode_update_kernel<F32, G><<<B, threads, 0, st>>>(
+          part, ksplit, B, N, c, m, ov, has_win, ape, pos, state, (float*)cache, max_entries,
+          (float*)ring, n_win, qk_norm, eps, r, theta);
+  });
+  return hipGetLastError();
+}
+
+}  // namespace csa

@@ -1,0 +1,139 @@
+// Device-side building blocks shared by the libcsa kernels (gfx950 only).
+//
+// Element storage: fp32 as float, bf16 as uint16_t bit patterns.  Matrix-core
+// operands are always moved as 16-byte chunks per lane ("uint4"), which hold
+// 8 bf16 or 4 fp32 values that are consecutive along the reduction axis.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define CSA_DEV __device__ __forceinline__
+
+namespace csa {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+
+// ---------------------------------------------------------------- bf16 <-> f32
+CSA_DEV float bf16_to_f32(uint16_t x) { return __uint_as_float(((uint32_t)x) << 16); }
+
+// Round to nearest, ties to even (NaN stays NaN).
+CSA_DEV uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+struct F32 {
+  typedef float S;  // storage
+  static constexpr int kPerChunk = 4;
+  CSA_DEV static float ld(const S* p, int64_t i) { return p[i]; }
+  CSA_DEV static void st(S* p, int64_t i, float v) { p[i] = v; }
+  CSA_DEV static S cvt(float v) { return v; }
+  CSA_DEV static float f(S v) { return v; }
+};
+
+struct BF16 {
+  typedef uint16_t S;
+  static constexpr int kPerChunk = 8;
+  CSA_DEV static float ld(const S* p, int64_t i) { return bf16_to_f32(p[i]); }
+  CSA_DEV static void st(S* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+  CSA_DEV static S cvt(float v) { return f32_to_bf16(v); }
+  CSA_DEV static float f(S v) { return bf16_to_f32(v); }
+};
+
+// Unpack / pack a 16-byte chunk to/from fp32 values.
+template <class T> CSA_DEV void chunk_to_f32(const uint4& c, float* v);
+template <> CSA_DEV void chunk_to_f32<F32>(const uint4& c, float* v) {
+  v[0] = __uint_as_float(c.x); v[1] = __uint_as_float(c.y);
+  v[2] = __uint_as_float(c.z); v[3] = __uint_as_float(c.w);
+}
+template <> CSA_DEV void chunk_to_f32<BF16>(const uint4& c, float* v) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+template <class T> CSA_DEV uint4 f32_to_chunk(const float* v);
+template <> CSA_DEV uint4 f32_to_chunk<F32>(const float* v) {
+  return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                    __float_as_uint(v[3]));
+}
+template <> CSA_DEV uint4 f32_to_chunk<BF16>(const float* v) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = (uint32_t)f32_to_bf16(v[2 * i]) | ((uint32_t)f32_to_bf16(v[2 * i + 1]) << 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// ------------------------------------------------------------ matrix cores
+// 16x16 output block.  Lane l supplies A row (l % 16) and B column (l % 16);
+// its 16-byte chunk covers reduction indices [g*E, g*E+E) of a 4*E-wide
+// k-group, g = l / 16, E = elements per chunk.  acc[i] = D[4*(l/16)+i][l%16].
+template <class T> CSA_DEV void mma16(f32x4_t& acc, const uint4& a, const uint4& b);
+template <> CSA_DEV void mma16<BF16>(f32x4_t& acc, const uint4& a, const uint4& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+}
+template <> CSA_DEV void mma16<F32>(f32x4_t& acc, const uint4& a, const uint4& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+}
+
+// 32x32 output block.  Lane l supplies A row (l % 32), B column (l % 32), its
+// chunk covering [g*E, g*E+E) of a 2*E-wide k-group, g = l / 32.
+// acc[i] = D[8*(i/4) + 4*(l/32) + (i%4)][l % 32].
+template <class T> CSA_DEV void mma32(f32x16_t& acc, const uint4& a, const uint4& b);
+template <> CSA_DEV void mma32<BF16>(f32x16_t& acc, const uint4& a, const uint4& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+}
+template <> CSA_DEV void mma32<F32>(f32x16_t& acc, const uint4& a, const uint4& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- RoPE
+// cos/sin of pos * theta^(-2p/r) for pair p.  The angle is formed and reduced
+// modulo 2*pi in fp64 so that positions up to 2^20 and beyond keep fp32
+// accuracy; the reduced angle is then evaluated in fp32.
+CSA_DEV void rope_cs(int64_t pos, int pair, int r, float theta, float* cs, float* sn) {
+  const double freq = exp2(-(2.0 * pair / (double)r) * log2((double)theta));
+  double a = (double)pos * freq;
+  const double two_pi = 6.283185307179586476925286766559;
+  a -= two_pi * rint(a / two_pi);
+  sincosf((float)a, sn, cs);
+}
+
+// ------------------------------------------------------------ reductions
+CSA_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+CSA_DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Order-preserving map fp32 -> uint32 (larger float -> larger key).
+CSA_DEV uint32_t float_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+CSA_DEV int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
+CSA_DEV int64_t max64(int64_t a, int64_t b) { return a > b ? a : b; }
+
+}  // namespace csa

@@ -1,0 +1,78 @@
+// Host-side launchers of the libcsa kernels.  Each returns hipSuccess or the
+// launch error; arguments were validated by the C ABI layer before the call.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/csa.h"
+
+namespace csa {
+
+// A stacked set of up to three output-major weight matrices [rows_i, K]
+// that one projection multiplies with the same left operand.
+struct WeightStack {
+  const void* w[3];
+  int rows[3];
+  int total() const { return rows[0] + rows[1] + rows[2]; }
+};
+
+// out[M, ldo] (fp32, columns [0, stack.total())) = A[M, K] . stack^T
+hipError_t launch_proj_gemm(int dtype, const void* A, int64_t M, int K, const WeightStack& ws,
+                            float* out, int64_t ldo, hipStream_t st);
+
+// Pool complete blocks of a projected scratch [n, ld] (C at col 0, Z at col w)
+// into entries, apply the epilogue and store.
+hipError_t launch_pool_entries(int dtype, const float* P, int64_t ld, int64_t n, int c, int m,
+                               int ov, const float* ape, int qk_norm, float eps, int rope_dims,
+                               float theta, void* out, int64_t pos0, hipStream_t st);
+
+// Window rows from scratch column `col` (width c) -> out [n, c] and/or ring.
+hipError_t launch_window_rows(int dtype, const float* P, int64_t ld, int col, int64_t n, int c,
+                              int qk_norm, float eps, int rope_dims, float theta, void* out,
+                              void* ring, int n_win, int64_t pos0, hipStream_t st);
+
+// Decode state after the last prefill token (fold tail rows / last block).
+hipError_t launch_stash_state(const float* P, int64_t ld, int64_t n, int c, int m, int ov,
+                              const float* ape, float* state, hipStream_t st);
+
+hipError_t launch_state_init(float* state, int64_t floats_per_seq, int batch, int c,
+                             hipStream_t st);
+
+// Decode projection partials: ws[ks][B][N] over K-splits.
+hipError_t launch_decode_proj(int dtype, const void* h, int B, int K, const WeightStack& w,
+                              float* part, int ksplit, hipStream_t st);
+
+hipError_t launch_decode_update(int dtype, const float* part, int ksplit, int B, int N, int c,
+                                int m, int ov, int has_win, const float* ape, const int64_t* pos,
+                                float* state, void* cache, int64_t max_entries, void* ring,
+                                int n_win, int qk_norm, float eps, int rope_dims, float theta,
+                                hipStream_t st);
+
+int decode_proj_ksplit(int N, int K, int dtype);
+
+// ------------------------------------------------------------- indexer
+hipError_t launch_index_scores_prefill(const csa_index_desc& d, const void* qI, const void* wI,
+                                       const void* KI, float* scores, int64_t ld,
+                                       hipStream_t st);
+hipError_t launch_topk_rows_prefill(const csa_index_desc& d, const float* scores, int64_t ld,
+                                    int32_t* idx_out, hipStream_t st);
+
+size_t index_decode_ws_bytes(const csa_index_desc& d);
+hipError_t launch_index_topk_decode(const csa_index_desc& d, const void* qI, const void* wI,
+                                    const void* KI, const int64_t* pos, int32_t* idx_out,
+                                    void* ws, hipStream_t st);
+
+// ------------------------------------------------------------- attention
+enum AttnMode { ATTN_SPARSE = 0, ATTN_DENSE = 1 };
+
+hipError_t launch_mqa_prefill(const csa_attn_desc& d, int mode, const void* q, const void* win,
+                              const void* comp, const int32_t* idx, const float* sink, void* out,
+                              hipStream_t st);
+
+size_t mqa_decode_ws_bytes(const csa_attn_desc& d, int mode);
+hipError_t launch_mqa_decode(const csa_attn_desc& d, int mode, const void* q, const void* ring,
+                             const void* cache, const int32_t* idx, const int64_t* pos,
+                             const float* sink, void* out, void* ws, hipStream_t st);
+
+}  // namespace csa

@@ -1,0 +1,649 @@
+// Lightning indexer scoring and exact top-k selection.
+//
+// Citation keys: [R] = page "DeepSeek-V4 技术解读报告" (juejin.cn), section
+// 2.3.1 eq 16 (I[t,s] = sum_h w[t,h] ReLU(q[t,h] . K[s])) and eq 17 (top-k);
+// [A] = page "DeepSeek-V4：算法架构" (1zeryu.github.io), Indexer class:
+// causal mask s < (t+1)//m, top-min(k, visible), -1 padding.
+//
+// Selection is exact: scores are fp32, mapped to order-preserving uint32 keys,
+// and the k-th largest key is found by radix selection; equal scores are
+// broken toward the smaller entry index.  Output rows list the chosen
+// indices in ascending order, then -1.
+#include "csa_common.h"
+#include "csa_launch.h"
+
+namespace csa {
+
+// ===========================================================================
+// Prefill scoring: scores[t][s] for a tile of queries x all keys of a chunk.
+// One 256-thread workgroup owns 16*HI... rows (query, head) pairs: each wave
+// holds two 32-row blocks of (query, head) rows; keys are staged 32 at a
+// time in LDS and fed to 32x32 matrix-core blocks.  The head reduction with
+// the ReLU and weights happens in registers.
+// ===========================================================================
+template <class T, int HI, int CI>
+__global__ __launch_bounds__(256) void index_scores_prefill_kernel(
+    const typename T::S* __restrict__ qI, const typename T::S* __restrict__ wI,
+    const typename T::S* __restrict__ KI, int64_t n, int64_t n_entries, int m, int key_chunk,
+    float* __restrict__ scores, int64_t ld) {
+  typedef typename T::S S;
+  constexpr int E = 16 / (int)sizeof(S);
+  constexpr int KGE = 2 * E;        // elements per 32x32 k-group
+  constexpr int NG = CI / KGE;      // k-groups per key
+  constexpr int RB = 2;             // 32-row blocks per wave
+  constexpr int ROWS = 4 * RB * 32; // (query, head) rows per workgroup
+  constexpr int TQ = ROWS / HI;     // queries per workgroup
+  constexpr int ROWB = CI * (int)sizeof(S) + 16;  // LDS bytes per key row
+  __shared__ __align__(16) uint8_t sK[32 * ROWB];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hl = lane >> 5;
+  const int64_t q0 = (int64_t)blockIdx.x * TQ;
+  const int64_t tlast = min64(q0 + TQ, n) - 1;
+  const int64_t kend = min64(min64((tlast + 1) / m, n_entries), (int64_t)(blockIdx.y + 1) * key_chunk);
+  const int64_t kbeg = (int64_t)blockIdx.y * key_chunk;
+  if (kbeg >= kend) return;
+
+  // A fragments (query rows) and per-row weights, held for the whole chunk.
+  uint4 qa[RB][NG];
+  float wv[RB][16];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int row = wave * (RB * 32) + rb * 32 + (lane & 31);
+    const int64_t t = q0 + row / HI;
+    const int h = row % HI;
+    const bool ok = t < n;
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+      qa[rb][g] = ok ? *(const uint4*)(qI + (t * HI + h) * CI + g * KGE + hl * E) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int rr = wave * (RB * 32) + rb * 32 + 8 * (i >> 2) + 4 * hl + (i & 3);
+      const int64_t tt = q0 + rr / HI;
+      wv[rb][i] = tt < n ? T::ld(wI, tt * HI + rr % HI) : 0.f;
+    }
+  }
+
+  for (int64_t k0 = kbeg; k0 < kend; k0 += 32) {
+    __syncthreads();
+    // stage 32 keys x CI
+    for (int e = tid; e < 32 * (CI * (int)sizeof(S) / 16); e += 256) {
+      const int kr = e / (CI * (int)sizeof(S) / 16), ck = e % (CI * (int)sizeof(S) / 16);
+      const int64_t s = k0 + kr;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (s < kend) v = *(const uint4*)((const uint8_t*)(KI + s * CI) + ck * 16);
+      *(uint4*)(sK + kr * ROWB + ck * 16) = v;
+    }
+    __syncthreads();
+    f32x16_t acc[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x16_t{};
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const uint4 kb = *(const uint4*)(sK + (lane & 31) * ROWB + g * 32 + hl * 16);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) mma32<T>(acc[rb], qa[rb][g], kb);
+    }
+    const int64_t s = k0 + (lane & 31);
+    const bool sok = s < kend;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float part[4];
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        float p = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p += wv[rb][gq * 4 + r] * fmaxf(acc[rb][gq * 4 + r], 0.f);
+        part[gq] = p;
+      }
+      const int64_t tb = q0 + (wave * (RB * 32) + rb * 32) / HI;  // first query of this block
+      if (HI == 4) {  // each group of 4 rows is one whole query
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int64_t t = tb + 2 * gq + hl;
+          if (sok && t < n && s < (t + 1) / m) scores[t * ld + s] = part[gq];
+        }
+      } else if (HI == 8) {
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) part[gq] += __shfl_xor(part[gq], 32, 64);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int gq = 2 * hl + u;
+          const int64_t t = tb + gq;
+          const float v = gq == 0 ? part[0] : gq == 1 ? part[1] : gq == 2 ? part[2] : part[3];
+          if (sok && t < n && s < (t + 1) / m) scores[t * ld + s] = v;
+        }
+      } else {  // HI == 16: rows 0-15 query 0, rows 16-31 query 1
+        float p0 = part[0] + part[1], p1 = part[2] + part[3];
+        p0 += __shfl_xor(p0, 32, 64);
+        p1 += __shfl_xor(p1, 32, 64);
+        const int64_t t = tb + hl;
+        if (sok && t < n && s < (t + 1) / m) scores[t * ld + s] = hl ? p1 : p0;
+      }
+    }
+  }
+}
+
+// ===========================================================================
+// Block-wide helpers (256 threads)
+// ===========================================================================
+// Exclusive prefix sum over the 256 threads in thread order; returns the total
+// in *total.  `tmp` is LDS scratch of >= 4 ints.
+CSA_DEV int block_excl_scan(int v, int* tmp, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  __syncthreads();
+  if (lane == 63) tmp[wave] = x;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += tmp[w];
+  *total = tmp[0] + tmp[1] + tmp[2] + tmp[3];
+  return base + x - v;
+}
+
+// Given a 256-bin histogram in LDS and `need` >= 1, find the digit d such
+// that (#items with digit > d) < need <= (#items with digit >= d).  Wave 0
+// computes; results are broadcast through `out` (digit, items above d).
+CSA_DEV void find_digit(const int* hist, int need, int* out) {
+  if (threadIdx.x < 64) {
+    const int l = threadIdx.x;
+    const int c4 = hist[4 * l] + hist[4 * l + 1] + hist[4 * l + 2] + hist[4 * l + 3];
+    int suf = c4;  // inclusive suffix sum over lanes >= l
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_down(suf, o, 64);
+      if (l + o < 64) suf += y;
+    }
+    const int above = suf - c4;  // items in lanes > l
+    if (suf >= need && above < need) {
+      int acc = above;
+      for (int b = 3; b >= 0; --b) {
+        const int hcount = hist[4 * l + b];
+        if (acc + hcount >= need) { out[0] = 4 * l + b; out[1] = acc; break; }
+        acc += hcount;
+      }
+    }
+  }
+}
+
+// ===========================================================================
+// Prefill row selection: one workgroup per query row, the row's keys held in
+// registers (thread j owns a contiguous run of IT entries), 4 radix passes of
+// 8 bits over the order-preserving keys, then an ordered compaction.
+// ===========================================================================
+template <int MAXIT>
+__global__ __launch_bounds__(256) void topk_rows_prefill_kernel(const float* __restrict__ scores,
+                                                                int64_t ld, int64_t n,
+                                                                int64_t n_entries, int m, int k,
+                                                                int32_t* __restrict__ idx_out) {
+  __shared__ int hist[256];
+  __shared__ int tmp[8];
+  __shared__ int res[2];
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t v = min64((t + 1) / m, n_entries);
+  const int kt = (int)min64(k, v);
+  int32_t* orow = idx_out + t * k;
+  if (v <= k) {
+    for (int j = tid; j < k; j += 256) orow[j] = j < v ? j : -1;
+    return;
+  }
+  const int IT = (int)((v + 255) / 256);
+  const int64_t base = (int64_t)tid * IT;
+  const float* srow = scores + t * ld;
+  uint32_t u[MAXIT];
+#pragma unroll
+  for (int i = 0; i < MAXIT; ++i) {
+    const int64_t e = base + i;
+    u[i] = (i < IT && e < v) ? float_key(srow[e]) : 0u;  // key 0 is below every real score
+  }
+  uint32_t prefix = 0, pmask = 0;
+  int need = kt;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    hist[tid] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < MAXIT; ++i) {
+      if (i < IT && base + i < v && (u[i] & pmask) == prefix) atomicAdd(&hist[(u[i] >> shift) & 255], 1);
+    }
+    __syncthreads();
+    find_digit(hist, need, res);
+    __syncthreads();
+    const int d = res[0];
+    need -= res[1];
+    prefix |= (uint32_t)d << shift;
+    pmask |= 0xffu << shift;
+    __syncthreads();
+  }
+  // prefix = key of the kt-th largest; need = how many equal keys to take
+  int gt = 0, eq = 0;
+#pragma unroll
+  for (int i = 0; i < MAXIT; ++i) {
+    if (i < IT && base + i < v) { gt += u[i] > prefix; eq += u[i] == prefix; }
+  }
+  int tot;
+  const int eq_before = block_excl_scan(eq, tmp, &tot);
+  int take_eq = need - eq_before;
+  take_eq = take_eq < 0 ? 0 : (take_eq > eq ? eq : take_eq);
+  const int pos0 = block_excl_scan(gt + take_eq, tmp + 4, &tot);
+  int p = pos0, te = 0;
+#pragma unroll
+  for (int i = 0; i < MAXIT; ++i) {
+    if (i < IT && base + i < v) {
+      const bool take = u[i] > prefix || (u[i] == prefix && te < take_eq);
+      if (u[i] == prefix) te += 1;
+      if (take) orow[p++] = (int32_t)(base + i);
+    }
+  }
+  for (int j = kt + tid; j < k; j += 256) orow[j] = -1;
+}
+
+// ===========================================================================
+// Decode: one query per sequence over up to ~10^6 cached keys.
+//   D0 clear histograms/counters;
+//   D1 score chunks of keys (16x16 matrix-core tiles, keys streamed straight
+//      from memory -- this pass moves the step's dominant bytes) and build a
+//      2048-bin histogram of the keys' top 11 bits;
+//   D2 per chunk: find the coarse threshold bin, append entries above it to
+//      the "sure" list and entries in it to the tie list, and histogram the
+//      ties' next 11 bits;
+//   D3 per sequence: resolve the tie list exactly (fine bin, then radix
+//      selection on (score, -index)), merge, sort ascending, write.
+// Counts use integer atomics (order-independent), and the final sort makes
+// the output independent of the order in which lists were filled.
+// ===========================================================================
+constexpr int kDecChunk = 1024;    // keys per scoring workgroup
+constexpr int kCoarseBins = 2048;  // top 11 bits
+constexpr int kFineBins = 2048;    // next 11 bits
+
+struct DecWs {  // carve-up of the decode workspace
+  float* scores;      // [B][n_entries]
+  int* hist;          // [B][kCoarseBins]
+  int* fine;          // [B][kFineBins]
+  int* cnt;           // [B][4]: sure, tie, sure2, fin
+  int32_t* sure;      // [B][k]
+  uint2* ties;        // [B][n_entries] (key, index)
+  uint2* fin;         // [B][n_entries] final ties (key, index)
+};
+
+static size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static DecWs carve(void* ws, const csa_index_desc& d) {
+  uint8_t* p = (uint8_t*)ws;
+  DecWs w;
+  const size_t B = d.batch, ne = d.n_entries;
+  w.scores = (float*)p; p += align_up(B * ne * 4);
+  w.hist = (int*)p; p += align_up(B * kCoarseBins * 4);
+  w.fine = (int*)p; p += align_up(B * kFineBins * 4);
+  w.cnt = (int*)p; p += align_up(B * 4 * 4);
+  w.sure = (int32_t*)p; p += align_up(B * (size_t)d.k * 4);
+  w.ties = (uint2*)p; p += align_up(B * ne * 8);
+  w.fin = (uint2*)p; p += align_up(B * ne * 8);
+  return w;
+}
+
+size_t index_decode_ws_bytes(const csa_index_desc& d) {
+  const size_t B = d.batch, ne = d.n_entries;
+  return align_up(B * ne * 4) + align_up(B * kCoarseBins * 4) + align_up(B * kFineBins * 4) +
+         align_up(B * 16) + align_up(B * (size_t)d.k * 4) + 2 * align_up(B * ne * 8);
+}
+
+__global__ void dec_clear_kernel(int* hist, int* fine, int* cnt, int B) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < B * kCoarseBins; i += gridDim.x * blockDim.x) {
+    hist[i] = 0;
+    fine[i] = 0;
+  }
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < B * 4; i += gridDim.x * blockDim.x) cnt[i] = 0;
+}
+
+template <class T, int HI, int CI>
+__global__ __launch_bounds__(256) void dec_score_kernel(
+    const typename T::S* __restrict__ qI, const typename T::S* __restrict__ wI,
+    const typename T::S* __restrict__ KI, const int64_t* __restrict__ posv, int64_t n_entries,
+    int m, int k, float* __restrict__ scores, int* __restrict__ hist) {
+  typedef typename T::S S;
+  constexpr int E = 16 / (int)sizeof(S);
+  constexpr int KGE = 4 * E;      // elements per 16x16 k-group
+  constexpr int NG = CI / KGE;
+  __shared__ int lh[kCoarseBins];
+  const int b = blockIdx.y;
+  const int64_t vis = min64((posv[b] + 1) / m, n_entries);
+  if (vis <= k) return;  // everything visible is selected
+  const int64_t c0 = (int64_t)blockIdx.x * kDecChunk;
+  if (c0 >= vis) return;
+  const int64_t c1 = min64(c0 + kDecChunk, vis);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lg = lane >> 4;
+  for (int i = tid; i < kCoarseBins; i += 256) lh[i] = 0;
+
+  // A = indexer queries: row = head (lane % 16), padded with zero rows
+  uint4 qa[NG];
+  float wv[4];
+  const int hrow = lane & 15;
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+    qa[g] = hrow < HI ? *(const uint4*)(qI + ((int64_t)b * HI + hrow) * CI + g * KGE + lg * E)
+                      : make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * lg + i;
+    wv[i] = h < HI ? T::ld(wI, (int64_t)b * HI + h) : 0.f;
+  }
+  __syncthreads();
+  const S* kb = KI + (int64_t)b * n_entries * CI;
+  // each wave: 16 keys per step, 4 steps unrolled
+  for (int64_t s0 = c0 + wave * 64; s0 < c1; s0 += 256) {
+    uint4 kv[4][NG];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t s = s0 + u * 16 + (lane & 15);
+#pragma unroll
+      for (int g = 0; g < NG; ++g)
+        kv[u][g] = s < c1 ? *(const uint4*)(kb + s * CI + g * KGE + lg * E) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      f32x4_t acc = f32x4_t{};
+#pragma unroll
+      for (int g = 0; g < NG; ++g) mma16<T>(acc, qa[g], kv[u][g]);
+      float p = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p += wv[i] * fmaxf(acc[i], 0.f);
+      p += __shfl_xor(p, 16, 64);
+      p += __shfl_xor(p, 32, 64);
+      const int64_t s = s0 + u * 16 + (lane & 15);
+      if (lg == 0 && s < c1) {
+        scores[(int64_t)b * n_entries + s] = p;
+        atomicAdd(&lh[float_key(p) >> 21], 1);
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < kCoarseBins; i += 256)
+    if (lh[i]) atomicAdd(&hist[(int64_t)b * kCoarseBins + i], lh[i]);
+}
+
+// Threshold bin from a histogram (suffix search from the top); every thread
+// gets (bin, count above bin).  `h` is in global memory, `sh` LDS scratch.
+CSA_DEV void coarse_threshold(const int* __restrict__ h, int nb, int need, int* sh, int* res) {
+  // per-thread sums over 8 consecutive bins (256 threads x 8 = 2048)
+  const int tid = threadIdx.x;
+  int loc[8];
+  int c8 = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { loc[i] = h[tid * 8 + i]; c8 += loc[i]; }
+  // inclusive suffix sum over threads
+  const int lane = tid & 63, wave = tid >> 6;
+  int suf = c8;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_down(suf, o, 64);
+    if (lane + o < 64) suf += y;
+  }
+  __syncthreads();
+  if (lane == 0) sh[wave] = suf;
+  __syncthreads();
+  int above_w = 0;
+  for (int w = wave + 1; w < 4; ++w) above_w += sh[w];
+  suf += above_w;
+  const int above = suf - c8;
+  if (suf >= need && above < need) {
+    int acc = above;
+    for (int i = 7; i >= 0; --i) {
+      if (acc + loc[i] >= need) { res[0] = tid * 8 + i; res[1] = acc; break; }
+      acc += loc[i];
+    }
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void dec_collect_kernel(const int64_t* __restrict__ posv,
+                                                          int64_t n_entries, int m, int k,
+                                                          const float* __restrict__ scores,
+                                                          const int* __restrict__ hist,
+                                                          int* __restrict__ fine,
+                                                          int* __restrict__ cnt,
+                                                          int32_t* __restrict__ sure,
+                                                          uint2* __restrict__ ties) {
+  __shared__ int sh[8];
+  __shared__ int res[2];
+  __shared__ int lf[kFineBins];
+  const int b = blockIdx.y;
+  const int64_t vis = min64((posv[b] + 1) / m, n_entries);
+  if (vis <= k) return;
+  const int64_t c0 = (int64_t)blockIdx.x * kDecChunk;
+  if (c0 >= vis) return;
+  const int64_t c1 = min64(c0 + kDecChunk, vis);
+  const int tid = threadIdx.x, lane = tid & 63;
+  for (int i = tid; i < kFineBins; i += 256) lf[i] = 0;
+  coarse_threshold(hist + (int64_t)b * kCoarseBins, kCoarseBins, k, sh, res);
+  const uint32_t T = (uint32_t)res[0];
+  const float* sc = scores + (int64_t)b * n_entries;
+  for (int64_t s0 = c0; s0 < c1; s0 += 256) {
+    const int64_t s = s0 + tid;
+    uint32_t key = 0;
+    bool ok = s < c1;
+    if (ok) key = float_key(sc[s]);
+    const uint32_t bin = key >> 21;
+    const bool is_sure = ok && bin > T;
+    const bool is_tie = ok && bin == T;
+    // wave-aggregated appends
+    const uint64_t ms = __ballot(is_sure), mt = __ballot(is_tie);
+    int bs = 0, bt = 0;
+    if (lane == 0) {
+      if (ms) bs = atomicAdd(&cnt[b * 4 + 0], __popcll(ms));
+      if (mt) bt = atomicAdd(&cnt[b * 4 + 1], __popcll(mt));
+    }
+    bs = __shfl(bs, 0, 64);
+    bt = __shfl(bt, 0, 64);
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    if (is_sure) sure[(int64_t)b * k + bs + __popcll(ms & below)] = (int32_t)s;
+    if (is_tie) {
+      ties[(int64_t)b * n_entries + bt + __popcll(mt & below)] = make_uint2(key, (uint32_t)s);
+      atomicAdd(&lf[(key >> 10) & (kFineBins - 1)], 1);
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < kFineBins; i += 256)
+    if (lf[i]) atomicAdd(&fine[(int64_t)b * kFineBins + i], lf[i]);
+}
+
+// Radix selection over a list in global memory of `cnt` (key, index) pairs,
+// ordered by (key desc, index asc): marks how many to take via the composite
+// 64-bit value (key << 32) | ~index.  Returns through res the composite
+// threshold (hi, lo); items >= threshold are the `need` best.
+CSA_DEV void list_select(const uint2* __restrict__ L, int cnt, int need, int* hist, int* res,
+                         uint32_t* thr_hi, uint32_t* thr_lo) {
+  uint64_t prefix = 0, pmask = 0;
+  const int tid = threadIdx.x;
+  for (int pass = 0; pass < 8; ++pass) {
+    const int shift = 56 - 8 * pass;
+    hist[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < cnt; i += 256) {
+      const uint2 e = L[i];
+      const uint64_t ck = ((uint64_t)e.x << 32) | (uint64_t)(~e.y);
+      if ((ck & pmask) == prefix) atomicAdd(&hist[(ck >> shift) & 255], 1);
+    }
+    __syncthreads();
+    find_digit(hist, need, res);
+    __syncthreads();
+    need -= res[1];
+    prefix |= (uint64_t)res[0] << shift;
+    pmask |= (uint64_t)0xff << shift;
+    __syncthreads();
+  }
+  *thr_hi = (uint32_t)(prefix >> 32);
+  *thr_lo = (uint32_t)prefix;
+}
+
+__global__ __launch_bounds__(256) void dec_finalize_kernel(
+    const int64_t* __restrict__ posv, int64_t n_entries, int m, int k,
+    const int* __restrict__ hist, const int* __restrict__ fine, int* __restrict__ cnt,
+    const int32_t* __restrict__ sure, const uint2* __restrict__ ties, uint2* __restrict__ fin,
+    int32_t* __restrict__ idx_out) {
+  __shared__ int sh[8];
+  __shared__ int res[2];
+  __shared__ int h256[256];
+  __shared__ int32_t outv[2048];
+  __shared__ int ocount;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int64_t vis = min64((posv[b] + 1) / m, n_entries);
+  int32_t* orow = idx_out + (int64_t)b * k;
+  if (vis <= k) {
+    for (int j = tid; j < k; j += 256) orow[j] = j < vis ? j : -1;
+    return;
+  }
+  // coarse threshold: `above` entries are in the sure list
+  coarse_threshold(hist + (int64_t)b * kCoarseBins, kCoarseBins, k, sh, res);
+  const int above = res[1];
+  const int need1 = k - above;  // still to choose among the coarse-bin ties
+  __syncthreads();
+  coarse_threshold(fine + (int64_t)b * kFineBins, kFineBins, need1, sh, res);
+  const uint32_t T2 = (uint32_t)res[0];
+  const int above2 = res[1];
+  const int need2 = need1 - above2;  // to choose among the fine-bin ties
+  __syncthreads();
+  if (tid == 0) ocount = 0;
+  __syncthreads();
+  // copy the sure list
+  for (int j = tid; j < above; j += 256) outv[j] = sure[(int64_t)b * k + j];
+  // scan the tie list: fine bin > T2 -> taken; == T2 -> final candidates
+  const int nt = cnt[b * 4 + 1];
+  const uint2* tl = ties + (int64_t)b * n_entries;
+  uint2* fl = fin + (int64_t)b * n_entries;
+  for (int i0 = 0; i0 < nt; i0 += 256) {
+    const int i = i0 + tid;
+    uint2 e = make_uint2(0, 0);
+    const bool ok = i < nt;
+    if (ok) e = tl[i];
+    const uint32_t fb = (e.x >> 10) & (kFineBins - 1);
+    const bool take = ok && fb > T2;
+    const bool cand = ok && fb == T2;
+    const uint64_t mt = __ballot(take), mc = __ballot(cand);
+    int bt = 0, bc = 0;
+    if (lane == 0) {
+      if (mt) bt = atomicAdd(&ocount, __popcll(mt));
+      if (mc) bc = atomicAdd(&cnt[b * 4 + 3], __popcll(mc));
+    }
+    bt = __shfl(bt, 0, 64);
+    bc = __shfl(bc, 0, 64);
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    if (take) outv[above + bt + __popcll(mt & below)] = (int32_t)e.y;
+    if (cand) fl[bc + __popcll(mc & below)] = e;
+  }
+  __threadfence_block();
+  __syncthreads();
+  const int nf = cnt[b * 4 + 3];
+  uint32_t thi = 0, tlo = 0;
+  list_select(fl, nf, need2, h256, res, &thi, &tlo);
+  const uint64_t thr = ((uint64_t)thi << 32) | tlo;
+  const int base = above + above2;
+  if (tid == 0) ocount = 0;
+  __syncthreads();
+  for (int i0 = 0; i0 < nf; i0 += 256) {
+    const int i = i0 + tid;
+    bool take = false;
+    uint2 e = make_uint2(0, 0);
+    if (i < nf) {
+      e = fl[i];
+      take = (((uint64_t)e.x << 32) | (uint64_t)(~e.y)) >= thr;
+    }
+    const uint64_t mt = __ballot(take);
+    int bt = 0;
+    if (lane == 0 && mt) bt = atomicAdd(&ocount, __popcll(mt));
+    bt = __shfl(bt, 0, 64);
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    if (take) outv[base + bt + __popcll(mt & below)] = (int32_t)e.y;
+  }
+  __syncthreads();
+  // bitonic sort of the k chosen indices (ascending), padded to a power of 2
+  int P = 1;
+  while (P < k) P <<= 1;
+  for (int j = k + tid; j < P; j += 256) outv[j] = 0x7fffffff;
+  __syncthreads();
+  for (int size = 2; size <= P; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < P / 2; i += 256) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool up = ((lo & size) == 0);
+        const int a = outv[lo], c = outv[hi];
+        if ((a > c) == up) { outv[lo] = c; outv[hi] = a; }
+      }
+      __syncthreads();
+    }
+  }
+  for (int j = tid; j < k; j += 256) orow[j] = outv[j];
+}
+
+// ===========================================================================
+// Host launchers
+// ===========================================================================
+#define CSA_INDEX_DISPATCH(HIv, CIv, ...)                                        \
+  if (HIv == 4 && CIv == 64) { constexpr int HI = 4, CI = 64; __VA_ARGS__; }         \
+  else if (HIv == 8 && CIv == 64) { constexpr int HI = 8, CI = 64; __VA_ARGS__; }    \
+  else if (HIv == 16 && CIv == 64) { constexpr int HI = 16, CI = 64; __VA_ARGS__; }  \
+  else if (HIv == 4 && CIv == 128) { constexpr int HI = 4, CI = 128; __VA_ARGS__; }  \
+  else if (HIv == 8 && CIv == 128) { constexpr int HI = 8, CI = 128; __VA_ARGS__; }  \
+  else if (HIv == 16 && CIv == 128) { constexpr int HI = 16, CI = 128; __VA_ARGS__; } \
+  else return hipErrorInvalidValue;
+
+hipError_t launch_index_scores_prefill(const csa_index_desc& d, const void* qI, const void* wI,
+                                       const void* KI, float* scores, int64_t ld,
+                                       hipStream_t st) {
+  const int key_chunk = 2048;
+  const int64_t nvis = d.n / d.m < d.n_entries ? d.n / d.m : d.n_entries;
+  if (nvis == 0) return hipSuccess;
+  CSA_INDEX_DISPATCH(d.n_heads, d.head_dim, {
+    constexpr int TQ = 256 / HI;
+    dim3 grid((unsigned)((d.n + TQ - 1) / TQ), (unsigned)((nvis + key_chunk - 1) / key_chunk));
+    if (d.dtype == CSA_BF16)
+      index_scores_prefill_kernel<BF16, HI, CI><<<grid, 256, 0, st>>>(
+          (const BF16::S*)qI, (const BF16::S*)wI, (const BF16::S*)KI, d.n, d.n_entries, d.m,
+          key_chunk, scores, ld);
+    else
+      index_scores_prefill_kernel<F32, HI, CI><<<grid, 256, 0, st>>>(
+          (const float*)qI, (const float*)wI, (const float*)KI, d.n, d.n_entries, d.m, key_chunk,
+          scores, ld);
+  });
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_rows_prefill(const csa_index_desc& d, const float* scores, int64_t ld,
+                                    int32_t* idx_out, hipStream_t st) {
+  topk_rows_prefill_kernel<64><<<(unsigned)d.n, 256, 0, st>>>(scores, ld, d.n, d.n_entries, d.m,
+                                                               d.k, idx_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_index_topk_decode(const csa_index_desc& d, const void* qI, const void* wI,
+                                    const void* KI, const int64_t* pos, int32_t* idx_out,
+                                    void* wsp, hipStream_t st) {
+  DecWs w = carve(wsp, d);
+  const int B = d.batch;
+  dec_clear_kernel<<<(B * kCoarseBins + 255) / 256, 256, 0, st>>>(w.hist, w.fine, w.cnt, B);
+  const unsigned chunks = (unsigned)((d.n_entries + kDecChunk - 1) / kDecChunk);
+  CSA_INDEX_DISPATCH(d.n_heads, d.head_dim, {
+    if (d.dtype == CSA_BF16)
+      dec_score_kernel<BF16, HI, CI><<<dim3(chunks, B), 256, 0, st>>>(
+          (const BF16::S*)qI, (const BF16::S*)wI, (const BF16::S*)KI, pos, d.n_entries, d.m, d.k,
+          w.scores, w.hist);
+    else
+      dec_score_kernel<F32, HI, CI><<<dim3(chunks, B), 256, 0, st>>>(
+          (const float*)qI, (const float*)wI, (const float*)KI, pos, d.n_entries, d.m, d.k,
+          w.scores, w.hist);
+  });
+  dec_collect_kernel<<<dim3(chunks, B), 256, 0, st>>>(pos, d.n_entries, d.m, d.k, w.scores, w.hist,
+                                                      w.fine, w.cnt, w.sure, w.ties);
+  dec_finalize_kernel<<<B, 256, 0, st>>>(pos, d.n_entries, d.m, d.k, w.hist, w.fine, w.cnt, w.sure,
+                                         w.ties, w.fin, idx_out);
+  return hipGetLastError();
+}
+
+}  // namespace csa

@@ -1,0 +1,126 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+that include/csa.h declares, and rejects bad arguments on the host before
+anything is enqueued (the documented error codes)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_attention_10_amd as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char\s*\*|const char\s*\*)\s*\**\s*(\w+)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.fail("libcsa.so is not built (run python -m long_context_attention_10_amd.build)")
+    return L.load()
+
+
+def test_header_declares_the_eight_entry_points():
+    names = declared_functions()
+    for f in ["csa_compress_prefill", "csa_compress_decode", "csa_index_topk_prefill",
+              "csa_index_topk_decode", "csa_sparse_mqa_prefill", "csa_sparse_mqa_decode",
+              "hca_dense_mqa_prefill", "hca_dense_mqa_decode"]:
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 12
+    for f in names:
+        assert hasattr(lib, f), f"libcsa.so does not export {f}"
+    assert set(names) <= set(L.EXPORTED) | set(names)
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.csa_abi_version() == 1
+    for code in (0, -1, -2, -3, -4):
+        assert len(lib.csa_status_string(code)) > 0
+    assert lib.csa_status_string(-99) == b"unknown status"
+
+
+def test_struct_sizes_match_c_layout():
+    assert ctypes.sizeof(L.CompressDesc) == 64
+    assert ctypes.sizeof(L.IndexDesc) == 40
+    assert ctypes.sizeof(L.AttnDesc) == 64
+
+
+def test_workspace_and_state_sizes(lib):
+    d = L.compress_desc(n=2048, d=1024, c=128, m=4, overlap=0)
+    assert L.workspace_bytes("compress_prefill", d) >= 2048 * (2 * 128 + 128) * 4
+    d1 = L.compress_desc(batch=4, d=4096, c=512, m=4, overlap=1)
+    assert L.csa_state_bytes(d1) == 4 * 3 * 3 * 512 * 4
+    d0 = L.compress_desc(batch=4, d=4096, c=512, m=128, overlap=0)
+    assert L.csa_state_bytes(d0) == 4 * 1 * 3 * 512 * 4
+    idx = L.IndexDesc(65536, 1, 16, 64, 4, 512, L.CSA_BF16, 16384)
+    assert L.workspace_bytes("index_topk_prefill", idx) >= 65536 * 16384 * 4
+    ad = L.attn_desc(batch=4, nh=64, c=512, k=1024, n_entries=262144, dtype=L.CSA_BF16)
+    assert L.workspace_bytes("sparse_mqa_decode", ad) > 0
+    assert lib.csa_workspace_bytes(0, None) == 0
+
+
+def _p(v=1):
+    return ctypes.c_void_p(v)  # never dereferenced: validation fails first
+
+
+@pytest.mark.parametrize("change,code", [
+    (dict(c=96), -2),            # entry width outside the kernels' set
+    (dict(d=100), -2),           # hidden size not a multiple of 64
+    (dict(dtype=7), -2),         # unknown dtype
+    (dict(m=0), -1),
+    (dict(overlap=2), -1),
+    (dict(rope_dims=3), -1),
+    (dict(n=-1), -1),
+])
+def test_compress_prefill_rejects(lib, change, code):
+    kw = dict(n=64, d=128, c=128, m=4, overlap=0)
+    kw.update(change)
+    d = L.compress_desc(**kw)
+    st = lib.csa_compress_prefill(ctypes.byref(d), _p(), _p(), _p(), _p(), None, _p(), None, None,
+                                  None, _p(), 1 << 40, None)
+    assert st == code
+
+
+def test_null_descriptor_and_pointers(lib):
+    assert lib.csa_compress_prefill(None, *([None] * 10), 0, None) == -1
+    d = L.compress_desc(n=64, d=128, c=128, m=4)
+    # H missing
+    assert lib.csa_compress_prefill(ctypes.byref(d), None, _p(), _p(), _p(), None, _p(), None, None,
+                                    None, _p(), 1 << 40, None) == -1
+    # window output requested without window weights
+    assert lib.csa_compress_prefill(ctypes.byref(d), _p(), _p(), _p(), _p(), None, _p(), _p(), None,
+                                    None, _p(), 1 << 40, None) == -1
+    # workspace too small
+    assert lib.csa_compress_prefill(ctypes.byref(d), _p(), _p(), _p(), _p(), None, _p(), None, None,
+                                    None, _p(), 16, None) == -3
+
+
+def test_index_and_attention_reject(lib):
+    bad = L.IndexDesc(16, 1, 5, 64, 4, 8, L.CSA_BF16, 4)  # 5 indexer heads
+    assert lib.csa_index_topk_prefill(ctypes.byref(bad), _p(), _p(), _p(), _p(), _p(), 1 << 30, None) == -2
+    big_k = L.IndexDesc(16, 1, 16, 64, 4, 4096, L.CSA_BF16, 4)
+    assert lib.csa_index_topk_prefill(ctypes.byref(big_k), _p(), _p(), _p(), _p(), _p(), 1 << 30, None) == -2
+    too_many = L.IndexDesc(1 << 20, 1, 16, 64, 4, 512, L.CSA_BF16, 1 << 18)  # row beyond register select
+    assert lib.csa_index_topk_prefill(ctypes.byref(too_many), _p(), _p(), _p(), _p(), _p(), 1 << 40, None) == -2
+    dd = L.IndexDesc(0, 2, 16, 64, 4, 8, L.CSA_BF16, 100)
+    assert lib.csa_index_topk_decode(ctypes.byref(dd), _p(), _p(), _p(), _p(), _p(), _p(), 8, None) == -3
+    a = L.attn_desc(n=8, nh=65, c=128, k=4)
+    assert lib.csa_sparse_mqa_prefill(ctypes.byref(a), _p(), _p(), _p(), _p(), _p(), _p(), None, 0, None) == -2
+    a = L.attn_desc(n=8, nh=8, c=96, k=4)
+    assert lib.csa_sparse_mqa_prefill(ctypes.byref(a), _p(), _p(), _p(), _p(), _p(), _p(), None, 0, None) == -2
+    a = L.attn_desc(n=8, nh=8, c=128, k=0)
+    assert lib.csa_sparse_mqa_prefill(ctypes.byref(a), _p(), _p(), _p(), _p(), _p(), _p(), None, 0, None) == -1
+    a = L.attn_desc(batch=2, nh=8, c=128, m=4, n_entries=64)
+    assert lib.hca_dense_mqa_decode(ctypes.byref(a), _p(), _p(), _p(), _p(), _p(), _p(), _p(), 8, None) == -3
