@@ -1,0 +1,342 @@
+"""Benchmark: CSA/HCA hybrid compressed attention on one MI355X.
+
+Headline (`value`): prefill tokens/s of one CSA layer at 64K tokens (bf16,
+d=4096, m=4 overlapped compression, 16x64 indexer, top-512, 64 query heads of
+width 512, partial RoPE on 64 dims, window 128, sinks).  One step = the whole
+prefill hot path on one synthetic sequence: compressor projections + pooling
+(main entries, window rows, indexer keys), indexer scoring + top-k, sparse
+shared-KV MQA.  Inputs are resident in HBM before timing starts.
+
+Also reported (`decode`): one CSA+HCA decode step (both layers, one new token
+per sequence) at batch 32 x 128K context and batch 4 x 1M context, in us per
+step and us per token, with the caches built beforehand by the library's own
+prefill from seeded N(0,1) hidden states.
+
+`roofline` is measured live for the dominant kernel (sparse MQA prefill) with
+HIP events on the stream it runs on; `cpu_baseline` times the CPU fp64 oracle
+on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode]
+                       [--no-cpu-baseline] [--profile-mode]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import long_context_attention_10_amd as L  # noqa: E402
+from long_context_attention_10_amd import configs, inputs as I  # noqa: E402
+
+PEAK_BF16 = 2.5e15      # dense bf16 matrix FLOP/s, MI355X
+PEAK_HBM = 8.0e12       # HBM3E bytes/s, MI355X
+
+
+# --------------------------------------------------------------------------
+# prefill (headline)
+# --------------------------------------------------------------------------
+class CsaPrefill:
+    def __init__(self, cfg, device="cuda"):
+        self.cfg = cfg
+        self.t = I.csa_prefill_inputs(cfg, device=device)
+        n, c, m, k, nh = cfg["n"], cfg["c"], cfg["m"], cfg["k"], cfg["nh"]
+        dt = I.TORCH_DTYPES[cfg["dtype"]]
+        self.comp = torch.empty((n // m, c), dtype=dt, device=device)
+        self.win = torch.empty((n, c), dtype=dt, device=device)
+        self.kI = torch.empty((n // m, cfg["cI"]), dtype=dt, device=device)
+        self.idx = torch.empty((n, k), dtype=torch.int32, device=device)
+        self.out = torch.empty((n, nh, c), dtype=dt, device=device)
+
+    def compress(self):
+        c, t = self.cfg, self.t
+        L.csa_compress_prefill(t["H"], t["W_kv"], t["W_z"], t["ape"], c["m"], c["overlap"],
+                               W_win=t["W_win"], rope_dims=c["rope_dims"], out_comp=self.comp,
+                               out_win=self.win)
+        L.csa_compress_prefill(t["H"], t["WI_kv"], t["WI_z"], t["apeI"], c["m"], c["overlap"],
+                               out_comp=self.kI)
+
+    def index(self):
+        c, t = self.cfg, self.t
+        L.csa_index_topk_prefill(t["qI"], t["wI"], self.kI, c["m"], c["k"], out=self.idx)
+
+    def attend(self):
+        c, t = self.cfg, self.t
+        L.csa_sparse_mqa_prefill(t["q"], self.win, self.comp, self.idx, t["sink"],
+                                 n_win=c["n_win"], rope_dims=c["rope_dims"], out=self.out)
+
+    def step(self):
+        self.compress()
+        self.index()
+        self.attend()
+
+    def attn_flops(self):
+        """Algorithmic FLOPs of the sparse MQA: 2 matmuls x 2 FLOP per
+        multiply-add x heads x width, per (token, candidate) pair."""
+        c = self.cfg
+        t = np.arange(c["n"], dtype=np.int64)
+        pairs = np.minimum(c["n_win"], t + 1) + np.minimum(c["k"], (t + 1) // c["m"])
+        return 4.0 * c["nh"] * c["c"] * float(pairs.sum()), int(pairs.sum())
+
+
+def time_region(fn, steps, warmup, flush=None):
+    """Per-step event times (ms) on the current stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    times = []
+    if flush is None:
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(steps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return [s.elapsed_time(e) / steps] * steps
+    for _ in range(steps):
+        flush()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        torch.cuda.synchronize()
+        times.append(s.elapsed_time(e))
+    return times
+
+
+# --------------------------------------------------------------------------
+# decode (CSA layer + HCA layer, one token per sequence)
+# --------------------------------------------------------------------------
+class HybridDecode:
+    """State for B sequences at position t = ctx-1 (caches hold [0, t))."""
+
+    def __init__(self, cfg, device="cuda", seed=0):
+        self.cfg = cfg
+        B, ctx, d, c, m, ov = cfg["batch"], cfg["ctx"], cfg["d"], cfg["c"], cfg["m"], cfg["overlap"]
+        mh, hI, cI, nh, nw = cfg["m_hca"], cfg["hI"], cfg["cI"], cfg["nh"], cfg["n_win"]
+        r = cfg["rope_dims"]
+        name = cfg["name"]
+        dt = I.TORCH_DTYPES[cfg["dtype"]]
+        sd = d ** -0.5
+        kw = dict(dtype=cfg["dtype"], device=device)
+        w, wI = (1 + ov) * c, (1 + ov) * cI
+        g = {}
+        for lay in ("csa", "hca"):
+            wl = w if lay == "csa" else c
+            g[lay + "_Wkv"] = I.normal((wl, d), (seed, name, lay, "Wkv"), std=sd, **kw)
+            g[lay + "_Wz"] = I.normal((wl, d), (seed, name, lay, "Wz"), std=sd, **kw)
+            g[lay + "_ape"] = I.normal((m if lay == "csa" else mh, wl), (seed, name, lay, "ape"), device=device)
+            g[lay + "_Wwin"] = I.normal((c, d), (seed, name, lay, "Wwin"), std=sd, **kw)
+            g[lay + "_q"] = I.normal((B, nh, c), (seed, name, lay, "q"), **kw)
+            g[lay + "_sink"] = I.normal((nh,), (seed, name, lay, "sink"), device=device)
+        g["WI_kv"] = I.normal((wI, d), (seed, name, "WI_kv"), std=sd, **kw)
+        g["WI_z"] = I.normal((wI, d), (seed, name, "WI_z"), std=sd, **kw)
+        g["apeI"] = I.normal((m, wI), (seed, name, "apeI"), device=device)
+        g["qI"] = I.normal((B, hI, cI), (seed, name, "qI"), **kw)
+        g["wI"] = I.uniform((B, hI), (seed, name, "wI"), **kw)
+        self.g = g
+        t = ctx - 1
+        self.pos = torch.full((B,), t, dtype=torch.int64, device=device)
+        self.h = torch.empty((B, d), dtype=dt, device=device)
+        self.cache = torch.empty((B, ctx // m, c), dtype=dt, device=device)
+        self.kcache = torch.empty((B, ctx // m, cI), dtype=dt, device=device)
+        self.hcache = torch.empty((B, ctx // mh, c), dtype=dt, device=device)
+        self.ring = torch.empty((B, nw, c), dtype=dt, device=device)
+        self.hring = torch.empty((B, nw, c), dtype=dt, device=device)
+        dsc = L.compress_desc(batch=B, d=d, c=c, m=m, overlap=ov)
+        dsi = L.compress_desc(batch=B, d=d, c=cI, m=m, overlap=ov)
+        dsh = L.compress_desc(batch=B, d=d, c=c, m=mh, overlap=0)
+        self.st = torch.empty(L.csa_state_bytes(dsc) // 4, dtype=torch.float32, device=device)
+        self.sti = torch.empty(L.csa_state_bytes(dsi) // 4, dtype=torch.float32, device=device)
+        self.sth = torch.empty(L.csa_state_bytes(dsh) // 4, dtype=torch.float32, device=device)
+        self.idx = torch.empty((B, cfg["k"]), dtype=torch.int32, device=device)
+        self.out_c = torch.empty((B, nh, c), dtype=dt, device=device)
+        self.out_h = torch.empty((B, nh, c), dtype=dt, device=device)
+        # build the caches: prefill of tokens [0, t) for every sequence
+        ps, psi, psh = self.st.numel() // B, self.sti.numel() // B, self.sth.numel() // B
+        for b in range(B):
+            Hb = I.normal((t + 1, d), (seed, name, "H", b), chunk_rows=65536, **kw)
+            self.h[b] = Hb[t]
+            Hp = Hb[:t]
+            a = L.csa_compress_prefill(Hp, g["csa_Wkv"], g["csa_Wz"], g["csa_ape"], m, ov,
+                                       W_win=g["csa_Wwin"], rope_dims=r, n_win=nw, want_win=False,
+                                       want_ring=True, want_state=True, out_comp=self.cache[b, : t // m])
+            self.ring[b].copy_(a["ring"])
+            self.st[b * ps:(b + 1) * ps].copy_(a["state"])
+            a = L.csa_compress_prefill(Hp, g["WI_kv"], g["WI_z"], g["apeI"], m, ov, want_state=True,
+                                       out_comp=self.kcache[b, : t // m])
+            self.sti[b * psi:(b + 1) * psi].copy_(a["state"])
+            a = L.csa_compress_prefill(Hp, g["hca_Wkv"], g["hca_Wz"], g["hca_ape"], mh, 0,
+                                       W_win=g["hca_Wwin"], rope_dims=r, n_win=nw, want_win=False,
+                                       want_ring=True, want_state=True, out_comp=self.hcache[b, : t // mh])
+            self.hring[b].copy_(a["ring"])
+            self.sth[b * psh:(b + 1) * psh].copy_(a["state"])
+            del Hb, Hp, a
+        torch.cuda.synchronize()
+        for key in [k for k in L._WS if k[1] == "default"]:  # free the build scratch
+            L._WS.pop(key)
+        torch.cuda.empty_cache()
+
+    def step(self):
+        c, g = self.cfg, self.g
+        m, ov, r = c["m"], c["overlap"], c["rope_dims"]
+        L.csa_compress_decode(self.h, self.pos, g["csa_Wkv"], g["csa_Wz"], g["csa_ape"], m, ov,
+                              self.st, self.cache, W_win=g["csa_Wwin"], win_ring=self.ring, rope_dims=r)
+        L.csa_compress_decode(self.h, self.pos, g["WI_kv"], g["WI_z"], g["apeI"], m, ov, self.sti,
+                              self.kcache)
+        L.csa_compress_decode(self.h, self.pos, g["hca_Wkv"], g["hca_Wz"], g["hca_ape"], c["m_hca"], 0,
+                              self.sth, self.hcache, W_win=g["hca_Wwin"], win_ring=self.hring,
+                              rope_dims=r)
+        L.csa_index_topk_decode(g["qI"], g["wI"], self.kcache, self.pos, m, c["k"], out=self.idx)
+        L.csa_sparse_mqa_decode(g["csa_q"], self.ring, self.cache, self.idx, self.pos, g["csa_sink"],
+                                rope_dims=r, out=self.out_c)
+        L.hca_dense_mqa_decode(g["hca_q"], self.hring, self.hcache, self.pos, g["hca_sink"], c["m_hca"],
+                               rope_dims=r, out=self.out_h)
+
+    def algorithmic_bytes(self):
+        """Bytes a decode step must move at least once (bf16 = 2 B)."""
+        c = self.cfg
+        B, ctx, d, cc, m, ov = c["batch"], c["ctx"], c["d"], c["c"], c["m"], c["overlap"]
+        t = ctx - 1
+        vis, vis_h = (t + 1) // m, (t + 1) // c["m_hca"]
+        nw = min(c["n_win"], t + 1)
+        e = 2
+        w, wI = (1 + ov) * cc, (1 + ov) * c["cI"]
+        weights = d * (2 * w + cc + 2 * wI + 2 * cc + cc) * e
+        keys = B * vis * c["cI"] * e
+        csa = B * (nw + min(c["k"], vis)) * cc * e
+        hca = B * (nw + vis_h) * cc * e
+        qo = 4 * B * c["nh"] * cc * e + B * (c["hI"] * c["cI"] + c["hI"]) * e + B * d * e
+        return weights + keys + csa + hca + qo
+
+
+def cpu_baseline(pf, sample_tokens=2048, sample_rows=48):
+    """Time the CPU fp64 oracle on a bounded sample of the prefill workload and
+    scale to tokens/s: compressor on the first `sample_tokens` tokens, indexer
+    + top-k and core attention on `sample_rows` query rows spread over the
+    sequence (reusing the GPU's entries as the stage inputs)."""
+    from oracle import csa_oracle as O
+    cfg, t = pf.cfg, pf.t
+    n, m, ov, r, k = cfg["n"], cfg["m"], cfg["overlap"], cfg["rope_dims"], cfg["k"]
+    cores = len(os.sched_getaffinity(0))
+    f = lambda x: x.detach().to("cpu", torch.float64).numpy()  # noqa: E731
+    H = f(t["H"][:sample_tokens])
+    Wkv, Wz, Ww, WIk, WIz = (f(t[x]).T for x in ("W_kv", "W_z", "W_win", "WI_kv", "WI_z"))
+    ape, apeI = f(t["ape"]), f(t["apeI"])
+    t0 = time.perf_counter()
+    O.compress_prefill(H, Wkv, Wz, ape, m, ov, rope_dims=r, store="bf16")
+    O.window_rows(H, Ww, rope_dims=r, store="bf16")
+    O.compress_prefill(H, WIk, WIz, apeI, m, ov, store="bf16")
+    t_comp = (time.perf_counter() - t0) / sample_tokens
+    rows = np.linspace(n // 8, n - 1, sample_rows).astype(np.int64)
+    KI = f(pf.kI)
+    comp, win = f(pf.comp), f(pf.win)
+    qI, wI = f(t["qI"][rows]), f(t["wI"][rows])
+    q, sink = f(t["q"][rows]), f(t["sink"])
+    t0 = time.perf_counter()
+    idx = np.full((len(rows), k), -1, dtype=np.int64)
+    for i, tok in enumerate(rows):
+        sc = O.index_scores(qI[i][None], wI[i][None], KI[: (tok + 1) // m], m, t0=int(tok))
+        idx[i] = O.topk(sc, k, m, t0=int(tok))[0]
+    t_idx = (time.perf_counter() - t0) / len(rows)
+    t0 = time.perf_counter()
+    for i, tok in enumerate(rows):
+        sel = idx[i][idx[i] >= 0]
+        lo = max(0, tok - cfg["n_win"] + 1)
+        O.attend_decode_row(q[i], int(tok), win[lo:tok + 1], comp[sel], sink, cfg["c"] ** -0.5,
+                            rope_dims=r, store="bf16")
+    t_att = (time.perf_counter() - t0) / len(rows)
+    per_tok = t_comp + t_idx + t_att
+    return {"value": 1.0 / per_tok, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"CPU fp64 oracle, {cores} host threads: compressor (main, window, indexer) on "
+                      f"the first {sample_tokens} tokens; indexer+top-k and sparse MQA on "
+                      f"{sample_rows} query rows spread over the 64K sequence; per-token stage "
+                      f"times summed (compress {t_comp * 1e3:.3f} ms, index {t_idx * 1e3:.3f} ms, "
+                      f"attention {t_att * 1e3:.3f} ms per token)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-mode", action="store_true",
+                    help="fewer repetitions; for runs under rocprofv3")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {a.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    L.load()
+    dev = "cuda"
+    cfg = configs.get("csa_prefill_64k_bf16")
+    print(f"[bench] building inputs for {cfg['name']}", file=sys.stderr, flush=True)
+    pf = CsaPrefill(cfg, dev)
+    torch.cuda.synchronize()
+    print("[bench] timing prefill steps", file=sys.stderr, flush=True)
+    times = time_region(pf.step, a.steps, a.warmup)
+    ms = float(np.mean(times))
+    n = cfg["n"]
+    # dominant kernel, timed live with events on the stream it runs on
+    att_t = time_region(pf.attend, max(3, a.steps), 1)
+    att_ms = float(np.mean(att_t))
+    flops, pairs = pf.attn_flops()
+    comp_ms = float(np.mean(time_region(pf.compress, max(3, a.steps), 1)))
+    idx_ms = float(np.mean(time_region(pf.index, max(3, a.steps), 1)))
+    achieved = flops / (att_ms * 1e-3)
+    rec = {
+        "metric": "CSA prefill tokens/s at 64K (1 GPU); decode us/token at 128K and 1M context",
+        "value": n / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) / U(0,1) inputs)",
+        "config": {"workload": cfg["name"], "layer": "CSA", "n": n, "d": cfg["d"], "c": cfg["c"],
+                   "m": cfg["m"], "overlap": cfg["overlap"], "indexer": f"{cfg['hI']}x{cfg['cI']}",
+                   "k": cfg["k"], "nh": cfg["nh"], "n_win": cfg["n_win"],
+                   "rope_dims": cfg["rope_dims"], "parallelism": "none (1 GPU)"},
+        "stages_ms": {"compress": comp_ms, "index_topk": idx_ms, "sparse_mqa": att_ms},
+        "roofline": {"kernel": "mqa_kernel (csa_sparse_mqa_prefill)", "bound": "mfma",
+                     "achieved": achieved / 1e12, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16, "traffic": None,
+                     "algorithmic": f"{flops:.4g} FLOP per launch = 4 x 64 heads x 512 x "
+                                    f"{pairs} (token, candidate) pairs"},
+    }
+    del att_t
+    if not a.no_decode:
+        dec = {}
+        flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+        def flush():
+            flush_buf.random_(0, 255)  # overwrites the 256 MiB last-level cache
+
+        for wname in ("decode_b32_128k_bf16", "decode_b4_1m_bf16"):
+            dc = configs.get(wname)
+            print(f"[bench] building decode state for {wname}", file=sys.stderr, flush=True)
+            hd = HybridDecode(dc, dev)
+            print(f"[bench] timing {wname}", file=sys.stderr, flush=True)
+            tt = time_region(hd.step, max(3, a.steps), 2, flush=flush)
+            tw = time_region(hd.step, max(3, a.steps), 1)
+            us = float(np.median(tt)) * 1e3
+            byts = hd.algorithmic_bytes()
+            dec[wname] = {"us_per_step": us, "us_per_token": us / dc["batch"],
+                          "us_per_step_warm_cache": float(np.mean(tw)) * 1e3,
+                          "batch": dc["batch"], "ctx": dc["ctx"], "k": dc["k"],
+                          "hbm_bytes_algorithmic": byts,
+                          "hbm_frac": byts / (us * 1e-6) / PEAK_HBM}
+            del hd
+            torch.cuda.empty_cache()
+        rec["decode"] = dec
+    if not a.no_cpu_baseline:
+        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(pf)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
