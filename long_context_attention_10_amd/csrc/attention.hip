@@ -439,6 +439,8 @@ hipError_t launch_mqa_prefill(const csa_attn_desc& d, int mode, const void* q, c
                               const void* comp, const int32_t* idx, const float* sink, void* out,
                               hipStream_t st) {
   if (d.n == 0) return hipSuccess;
+  if (d.dtype == CSA_BF16 && (mode == ATTN_DENSE || d.k <= 1024))
+    return launch_mqa_prefill_bf16(d, mode, q, win, comp, idx, sink, out, st);
   if (d.dtype == CSA_BF16)
     return mode == ATTN_SPARSE
                ? dispatch_prefill<BF16, MODE_PREFILL_SPARSE>(d, q, win, comp, idx, sink, out, st)

@@ -69,6 +69,10 @@ enum AttnMode { ATTN_SPARSE = 0, ATTN_DENSE = 1 };
 hipError_t launch_mqa_prefill(const csa_attn_desc& d, int mode, const void* q, const void* win,
                               const void* comp, const int32_t* idx, const float* sink, void* out,
                               hipStream_t st);
+// bf16 fast path (head dims 128/256/512, up to 1024 index slots)
+hipError_t launch_mqa_prefill_bf16(const csa_attn_desc& d, int mode, const void* q, const void* win,
+                                   const void* comp, const int32_t* idx, const float* sink,
+                                   void* out, hipStream_t st);
 
 size_t mqa_decode_ws_bytes(const csa_attn_desc& d, int mode);
 hipError_t launch_mqa_decode(const csa_attn_desc& d, int mode, const void* q, const void* ring,
