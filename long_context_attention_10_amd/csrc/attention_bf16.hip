@@ -31,7 +31,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
 namespace {
 
 constexpr int kT = 32;            // candidates per tile
-constexpr int kPad = 16;          // bytes of padding per LDS row
+constexpr int kPad = 32;          // bytes of padding per 1 KiB LDS burst
 constexpr int kMaxK = 1024;       // index slots staged in LDS
 
 template <int C>
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256, 2) void mqa_prefill_bf16_kernel(
   }
 
   // ------------------------------------------ q prologue: norm, RoPE, regs
-  uint4 qf[NKG];
+  bf16x8_t qf[NKG];
   const int head = wave * 16 + lc;
   {
     const uint8_t* qs = smem + G::off(head) + lg * 16;
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(256, 2) void mqa_prefill_bf16_kernel(
           }
         }
       }
-      qf[g] = f32_to_chunk<BF16>(v);
+      qf[g] = __builtin_bit_cast(bf16x8_t, f32_to_chunk<BF16>(v));
     }
   }
   __syncthreads();  // q staging area is reused for candidate tiles
@@ -181,23 +181,31 @@ __global__ __launch_bounds__(256, 2) void mqa_prefill_bf16_kernel(
   wait_vmem();
   __syncthreads();
 
+  // Candidate slot permutation.  Lane group lg (lanes 16*lg..16*lg+15) holds,
+  // after the logits, the 8 tile rows pi(lg, h, i) = 16*(lg/2) + 8*h + 4*(lg%2) + i
+  // (h = 0, 1; i = 0..3); those rows are also its PV reduction slots 8*lg+4*h+i.
+  // With 1056-byte LDS rows (8 banks apart) both the 16-byte K reads (rows
+  // pi(lc/4, b, lc%4) for lanes lc) and the transpose reads (4 consecutive
+  // rows per 16-lane group) touch distinct banks.
+  auto pi = [](int g, int h, int i) { return 16 * (g >> 1) + 8 * h + 4 * (g & 1) + i; };
+  const int koff0 = G::off(pi(lc >> 2, 0, lc & 3)) + lg * 16;
+  const int koff1 = G::off(pi(lc >> 2, 1, lc & 3)) + lg * 16;
+  const int troff0 = G::off(pi(lg, 0, lc >> 2)) + 8 * (lc & 3);
+  const int troff1 = G::off(pi(lg, 1, lc >> 2)) + 8 * (lc & 3);
+
   for (int ti = 0; ti < ntiles; ++ti) {
     const int buf = ti & 1;
     if (ti + 1 < ntiles) issue_tile(ti + 1, buf ^ 1);
     const uint8_t* kv = smem + buf * G::TILE;
 
-    // S^T for 32 candidates: block b row rr <-> candidate 8*(rr/4) + 4*b + rr%4,
-    // so lane group lg ends up holding candidates 8*lg .. 8*lg+7.
+    // S^T = K Q^T for the tile: block b's A rows are K rows pi(lc/4, b, lc%4)
     f32x4_t s[2] = {f32x4_t{}, f32x4_t{}};
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int cand = 8 * (lc >> 2) + 4 * b + (lc & 3);
-      const uint8_t* krow = kv + G::off(cand) + lg * 16;
-#pragma unroll
-      for (int g = 0; g < NKG; ++g) {
-        const uint4 a = *(const uint4*)(krow + g * 64);
-        mma16<BF16>(s[b], a, qf[g]);
-      }
+    for (int g = 0; g < NKG; ++g) {
+      const bf16x8_t a0 = *(const bf16x8_t*)(kv + koff0 + g * 64);
+      const bf16x8_t a1 = *(const bf16x8_t*)(kv + koff1 + g * 64);
+      s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[g], s[0], 0, 0, 0);
+      s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[g], s[1], 0, 0, 0);
     }
     // online softmax for head `head` (this lane's column) in log2 units
     float z[8];
@@ -206,8 +214,7 @@ __global__ __launch_bounds__(256, 2) void mqa_prefill_bf16_kernel(
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int cand = 8 * lg + 4 * b + i;
-        const float zz = valid[buf][cand] ? s[b][i] * sl2 : -INFINITY;
+        const float zz = valid[buf][pi(lg, b, i)] ? s[b][i] * sl2 : -INFINITY;
         z[4 * b + i] = zz;
         mx = fmaxf(mx, zz);
       }
@@ -216,7 +223,7 @@ __global__ __launch_bounds__(256, 2) void mqa_prefill_bf16_kernel(
     const bool need = mx > run_m + 8.f;
     if (__any(need)) {  // wave-uniform rescale of O
       const float nm = fmaxf(run_m, mx);
-      const float alpha = exp2f(run_m - nm);
+      const float alpha = __builtin_amdgcn_exp2f(run_m - nm);
       run_l *= alpha;
       run_m = nm;
 #pragma unroll
@@ -230,31 +237,28 @@ __global__ __launch_bounds__(256, 2) void mqa_prefill_bf16_kernel(
           for (int i = 0; i < 4; ++i) o_hi[cb][i] *= alpha;
       }
     }
-    float p[8];
+    f32x8_t p;
     float ps = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      p[j] = exp2f(z[j] - run_m);
+      p[j] = __builtin_amdgcn_exp2f(z[j] - run_m);
       ps += p[j];
     }
     ps += __shfl_xor(ps, 16, 64);
     ps += __shfl_xor(ps, 32, 64);
     run_l += ps;
-    const uint4 pb = f32_to_chunk<BF16>(p);  // B operand: slots 8*lg+j <-> candidate 8*lg+j
+    const bf16x8_t pb = __builtin_convertvector(p, bf16x8_t);  // B operand, slots 8*lg+j
 
     // O^T += V^T P^T over the 16-channel blocks; V^T fragments by transpose read:
-    // lane (lg, lc) reads row 8*lg + 4*h + lc/4, channels cb*16 + 4*(lc%4) .. +3.
+    // lane (lg, lc) reads row pi(lg, h, lc/4), channels cb*16 + 4*(lc%4) .. +3,
+    // and receives V[pi(lg, h, j)][cb*16 + lc] for j = 0..3.
     auto pv = [&](int cb, f32x4_t& acc) {
-      uint2 va[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int row = 8 * lg + 4 * h + (lc >> 2);
-        const uint8_t* pvp = kv + G::off(row) + (cb * 16 + 4 * (lc & 3)) * 2;
-        const bf16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((CSA_LDS bf16x4_t*)pvp);
-        va[h] = __builtin_bit_cast(uint2, x);
-      }
-      const uint4 a = make_uint4(va[0].x, va[0].y, va[1].x, va[1].y);
-      mma16<BF16>(acc, a, pb);
+      const bf16x4_t x0 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((CSA_LDS bf16x4_t*)(kv + troff0 + cb * 32));
+      const bf16x4_t x1 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((CSA_LDS bf16x4_t*)(kv + troff1 + cb * 32));
+      const bf16x8_t a = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, acc, 0, 0, 0);
     };
 #pragma unroll
     for (int cb = 0; cb < NLO; ++cb) pv(cb, o_lo[cb]);

@@ -19,13 +19,9 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 // ---------------------------------------------------------------- bf16 <-> f32
 CSA_DEV float bf16_to_f32(uint16_t x) { return __uint_as_float(((uint32_t)x) << 16); }
 
-// Round to nearest, ties to even (NaN stays NaN).
-CSA_DEV uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (uint16_t)((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
+// Round to nearest, ties to even: gfx950's hardware conversion
+// (v_cvt_pk_bf16_f32).
+CSA_DEV uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 struct F32 {
   typedef float S;  // storage
@@ -64,12 +60,10 @@ template <> CSA_DEV uint4 f32_to_chunk<F32>(const float* v) {
   return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
                     __float_as_uint(v[3]));
 }
+typedef __attribute__((__vector_size__(8 * sizeof(float)))) float f32x8_t;
 template <> CSA_DEV uint4 f32_to_chunk<BF16>(const float* v) {
-  uint32_t w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    w[i] = (uint32_t)f32_to_bf16(v[2 * i]) | ((uint32_t)f32_to_bf16(v[2 * i + 1]) << 16);
-  return make_uint4(w[0], w[1], w[2], w[3]);
+  const f32x8_t f = {v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]};
+  return __builtin_bit_cast(uint4, __builtin_convertvector(f, bf16x8_t));
 }
 
 // ------------------------------------------------------------ matrix cores
