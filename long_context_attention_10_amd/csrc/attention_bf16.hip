@@ -65,6 +65,7 @@ __global__ __launch_bounds__(256, 2) void mqa_prefill_bf16_kernel(
   __shared__ __align__(16) uint8_t smem[G::BUF];
   __shared__ int valid[2][kT];
   __shared__ int sidx[SPARSE ? kMaxK : 1];
+  __shared__ float2 rope_tab[C / 2];  // (cos, sin) of this token's RoPE pairs
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lc = lane & 15, lg = lane >> 4;
@@ -82,60 +83,25 @@ __global__ __launch_bounds__(256, 2) void mqa_prefill_bf16_kernel(
   const int32_t* irow = SPARSE ? idx + t * (int64_t)k : nullptr;
   const uint16_t* qrow = q + t * (int64_t)nh * C;
 
-  // ---------------------------------- q -> LDS (rows padded), index row -> LDS
+  // ------------------------ index row and RoPE angles -> LDS; q -> registers
   if (SPARSE)
     for (int j = tid; j < k; j += 256) sidx[j] = irow[j];
-  {
-    const int bursts = (nh + G::RPI - 1) / G::RPI;
-    for (int bi = wave; bi < bursts; bi += 4) {
-      const int h = bi * G::RPI + lane / (64 / G::RPI);
-      const int hh = h < nh ? h : 0;
-      const uint8_t* src = (const uint8_t*)(qrow + (int64_t)hh * C) + (lane % (64 / G::RPI)) * 16;
-      lds_dma16(src, (CSA_LDS void*)(smem + bi * G::BURST));
-    }
-    wait_vmem();
-    __syncthreads();
+  if (tid < r / 2) {  // one angle per RoPE pair, shared by prologue and epilogue
+    float cs, sn;
+    rope_cs(t, tid, r, theta, &cs, &sn);
+    rope_tab[tid] = make_float2(cs, sn);
   }
-
-  // ------------------------------------------ q prologue: norm, RoPE, regs
-  bf16x8_t qf[NKG];
+  // lane (lg, lc) holds Q[head][32g + 8lg .. +8] for g = 0..C/32-1: the B
+  // operand of S^T = K Q^T.  Loaded straight from global memory so that the
+  // first candidate tile can stream into LDS at the same time.
   const int head = wave * 16 + lc;
+  uint4 qraw[NKG];
   {
-    const uint8_t* qs = smem + G::off(head) + lg * 16;
-    float ss = 0.f;
+    const uint16_t* qh = qrow + (int64_t)(head < nh ? head : 0) * C + lg * 8;
 #pragma unroll
-    for (int g = 0; g < NKG; ++g) {  // pass 1: sum of squares over the head dim
-      float v[8];
-      chunk_to_f32<BF16>(*(const uint4*)(qs + g * 64), v);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
-    }
-    ss += __shfl_xor(ss, 16, 64);
-    ss += __shfl_xor(ss, 32, 64);
-    const float inv = qk_norm ? rsqrtf(ss / (float)C + eps) : 1.f;
-#pragma unroll
-    for (int g = 0; g < NKG; ++g) {  // pass 2: scale, rotate, round to bf16
-      float v[8];
-      chunk_to_f32<BF16>(*(const uint4*)(qs + g * 64), v);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] *= inv;
-      if (r > 0) {
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const int ch = g * 32 + lg * 8 + e;
-          if (ch >= C - r) {
-            float cs, sn;
-            rope_cs(t, (ch - (C - r)) >> 1, r, theta, &cs, &sn);
-            const float x0 = v[e], x1 = v[e + 1];
-            v[e] = x0 * cs - x1 * sn;
-            v[e + 1] = x0 * sn + x1 * cs;
-          }
-        }
-      }
-      qf[g] = __builtin_bit_cast(bf16x8_t, f32_to_chunk<BF16>(v));
-    }
+    for (int g = 0; g < NKG; ++g) qraw[g] = *(const uint4*)(qh + g * 32);
   }
-  __syncthreads();  // q staging area is reused for candidate tiles
+  __syncthreads();  // sidx and rope_tab are visible
 
   // ------------------------------------------------ candidate tile loader
   auto issue_tile = [&](int ti, int buf) {
@@ -161,6 +127,44 @@ __global__ __launch_bounds__(256, 2) void mqa_prefill_bf16_kernel(
     }
   };
 
+  if (ntiles > 0) issue_tile(0, 0);
+
+  // --------------------------------- q prologue: RMSNorm, RoPE, bf16 regs
+  bf16x8_t qf[NKG];
+  {
+    float ss = 0.f;
+#pragma unroll
+    for (int g = 0; g < NKG; ++g) {
+      float v[8];
+      chunk_to_f32<BF16>(qraw[g], v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+    }
+    ss += __shfl_xor(ss, 16, 64);
+    ss += __shfl_xor(ss, 32, 64);
+    const float inv = qk_norm ? rsqrtf(ss / (float)C + eps) : 1.f;
+#pragma unroll
+    for (int g = 0; g < NKG; ++g) {
+      float v[8];
+      chunk_to_f32<BF16>(qraw[g], v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] *= inv;
+      if (r > 0) {
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const int ch = g * 32 + lg * 8 + e;
+          if (ch >= C - r) {
+            const float2 cs = rope_tab[(ch - (C - r)) >> 1];
+            const float x0 = v[e], x1 = v[e + 1];
+            v[e] = x0 * cs.x - x1 * cs.y;
+            v[e + 1] = x0 * cs.y + x1 * cs.x;
+          }
+        }
+      }
+      qf[g] = __builtin_bit_cast(bf16x8_t, f32_to_chunk<BF16>(v));
+    }
+  }
+
   // ----------------------------------------------------- softmax state
   constexpr float LOG2E = 1.4426950408889634f;
   const float sl2 = scale * LOG2E;
@@ -177,8 +181,7 @@ __global__ __launch_bounds__(256, 2) void mqa_prefill_bf16_kernel(
 #pragma unroll
   for (int cb = 0; cb < NHI; ++cb) o_hi[cb] = f32x4_t{};
 
-  if (ntiles > 0) issue_tile(0, 0);
-  wait_vmem();
+  wait_vmem();  // tile 0 (and q) have landed
   __syncthreads();
 
   // Candidate slot permutation.  Lane group lg (lanes 16*lg..16*lg+15) holds,
@@ -282,11 +285,10 @@ __global__ __launch_bounds__(256, 2) void mqa_prefill_bf16_kernel(
     if (r > 0 && ch0 >= C - r) {
 #pragma unroll
       for (int i = 0; i < 4; i += 2) {
-        float cs, sn;
-        rope_cs(t, (ch0 + i - (C - r)) >> 1, r, theta, &cs, &sn);
+        const float2 cs = rope_tab[(ch0 + i - (C - r)) >> 1];
         const float x0 = v[i], x1 = v[i + 1];
-        v[i] = x0 * cs + x1 * sn;      // rotate by -t
-        v[i + 1] = -x0 * sn + x1 * cs;
+        v[i] = x0 * cs.x + x1 * cs.y;      // rotate by -t
+        v[i + 1] = -x0 * cs.y + x1 * cs.x;
       }
     }
     const uint32_t w0 = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
