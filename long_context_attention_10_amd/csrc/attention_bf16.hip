@@ -45,8 +45,23 @@ struct Geo {
   CSA_DEV static int off(int r) { return (r / RPI) * BURST + (r % RPI) * ROW; }
 };
 
-CSA_DEV void lds_dma16(const void* g, CSA_LDS void* l) {
-  __builtin_amdgcn_global_load_lds((const void*)g, l, 16, 0, 0);
+// 16 bytes per lane from global memory straight into LDS (global_load_lds):
+// lane l's bytes land at lds_base + 16*l, lds_base wave-uniform (in M0).
+// Written as inline asm so that the compiler does not track it -- with the
+// builtin it conservatively waits for the load before every LDS read, which
+// serialises the gather with the compute.  This kernel enforces completion
+// itself (wait_vmem, then a barrier) before a filled buffer is read, and no
+// other code in it uses M0.
+CSA_DEV void lds_dma16(const void* g, const void* lds_dst) {
+  const uint32_t base =
+      __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(CSA_LDS const void*)lds_dst);
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(g), "s"(base)
+      : "memory");
 }
 
 CSA_DEV void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
@@ -121,8 +136,7 @@ __global__ __launch_bounds__(256, 2) void mqa_prefill_bf16_kernel(
           if (e >= 0 && e < n_entries) { src = comp + e * C; ok = true; }
         }
       }
-      lds_dma16((const uint8_t*)src + (lane % (64 / G::RPI)) * 16,
-                (CSA_LDS void*)(base + bi * G::BURST));
+      lds_dma16((const uint8_t*)src + (lane % (64 / G::RPI)) * 16, base + bi * G::BURST);
       if ((lane % (64 / G::RPI)) == 0) valid[buf][row] = ok;
     }
   };
