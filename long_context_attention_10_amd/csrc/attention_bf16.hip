@@ -82,7 +82,8 @@ __global__ __launch_bounds__(256, 2) void mqa_prefill_bf16_kernel(
   __shared__ int sidx[SPARSE ? kMaxK : 1];
   __shared__ float2 rope_tab[C / 2];  // (cos, sin) of this token's RoPE pairs
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int lc = lane & 15, lg = lane >> 4;
 
   // XCD-aware order: the 8 dies each take a contiguous range of tokens, so a
@@ -121,24 +122,30 @@ __global__ __launch_bounds__(256, 2) void mqa_prefill_bf16_kernel(
   // ------------------------------------------------ candidate tile loader
   auto issue_tile = [&](int ti, int buf) {
     uint8_t* base = smem + buf * G::TILE;
-    const int bursts = kT / G::RPI;
-    for (int bi = wave; bi < bursts; bi += 4) {
+    constexpr int BPW = kT / G::RPI / 4;  // bursts (1 KiB each) per wave
+    const uint8_t* src[BPW];
+    // resolve every row first, then issue the loads back to back
+#pragma unroll
+    for (int u = 0; u < BPW; ++u) {
+      const int bi = wave + 4 * u;
       const int row = bi * G::RPI + lane / (64 / G::RPI);
       const int64_t j = (int64_t)ti * kT + row;
-      const uint16_t* src = win;  // a valid row for masked candidates
+      const uint16_t* r = win;  // a valid row for masked candidates
       bool ok = false;
       if (j < ncand) {
         if (j < nwin) {
-          src = win + (t - nwin + 1 + j) * C;
+          r = win + (t - nwin + 1 + j) * C;
           ok = true;
         } else {
           const int64_t e = SPARSE ? (int64_t)sidx[j - nwin] : j - nwin;
-          if (e >= 0 && e < n_entries) { src = comp + e * C; ok = true; }
+          if (e >= 0 && e < n_entries) { r = comp + e * C; ok = true; }
         }
       }
-      lds_dma16((const uint8_t*)src + (lane % (64 / G::RPI)) * 16, base + bi * G::BURST);
+      src[u] = (const uint8_t*)r + (lane % (64 / G::RPI)) * 16;
       if ((lane % (64 / G::RPI)) == 0) valid[buf][row] = ok;
     }
+#pragma unroll
+    for (int u = 0; u < BPW; ++u) lds_dma16(src[u], base + (wave + 4 * u) * G::BURST);
   };
 
   if (ntiles > 0) issue_tile(0, 0);
