@@ -516,8 +516,10 @@ hipError_t launch_state_init(float* state, int64_t per_seq, int batch, int c, hi
 int decode_proj_ksplit(int N, int K, int dtype) {
   const int kg4 = (dtype == CSA_BF16 ? 16 : 8) * 4;  // smallest per-wave slice
   const int tiles = (N + 31) / 32;
+  // At most 8 K slices: the update kernel sums the slices per column with one
+  // workgroup per sequence, so more slices would make that sum latency-bound.
   int ks = 1;
-  while (tiles * ks < 512 && K % (ks * 2 * kg4) == 0 && ks < 64) ks *= 2;
+  while (tiles * ks < 512 && K % (ks * 2 * kg4) == 0 && ks < 8) ks *= 2;
   return ks;
 }
 

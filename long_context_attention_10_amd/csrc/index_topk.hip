@@ -260,6 +260,7 @@ __global__ __launch_bounds__(256) void topk_rows_prefill_kernel(const float* __r
 constexpr int kDecChunk = 1024;    // keys per scoring workgroup
 constexpr int kCoarseBins = 2048;  // top 11 bits
 constexpr int kFineBins = 2048;    // next 11 bits
+constexpr int kBitmapEntries = 262144;  // index spaces sorted through an LDS bitmap
 
 struct DecWs {  // carve-up of the decode workspace
   float* scores;      // [B][n_entries]
@@ -423,28 +424,39 @@ __global__ __launch_bounds__(256) void dec_collect_kernel(const int64_t* __restr
   coarse_threshold(hist + (int64_t)b * kCoarseBins, kCoarseBins, k, sh, res);
   const uint32_t T = (uint32_t)res[0];
   const float* sc = scores + (int64_t)b * n_entries;
-  for (int64_t s0 = c0; s0 < c1; s0 += 256) {
-    const int64_t s = s0 + tid;
-    uint32_t key = 0;
-    bool ok = s < c1;
-    if (ok) key = float_key(sc[s]);
-    const uint32_t bin = key >> 21;
-    const bool is_sure = ok && bin > T;
-    const bool is_tie = ok && bin == T;
-    // wave-aggregated appends
-    const uint64_t ms = __ballot(is_sure), mt = __ballot(is_tie);
-    int bs = 0, bt = 0;
-    if (lane == 0) {
-      if (ms) bs = atomicAdd(&cnt[b * 4 + 0], __popcll(ms));
-      if (mt) bt = atomicAdd(&cnt[b * 4 + 1], __popcll(mt));
-    }
-    bs = __shfl(bs, 0, 64);
-    bt = __shfl(bt, 0, 64);
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    if (is_sure) sure[(int64_t)b * k + bs + __popcll(ms & below)] = (int32_t)s;
-    if (is_tie) {
-      ties[(int64_t)b * n_entries + bt + __popcll(mt & below)] = make_uint2(key, (uint32_t)s);
-      atomicAdd(&lf[(key >> 10) & (kFineBins - 1)], 1);
+  // each thread classifies a contiguous run of 4 entries; one block-wide
+  // prefix sum per list turns the per-thread counts into positions, so each
+  // workgroup makes a single atomic reservation per list (the lists are
+  // shared by every workgroup of the sequence).
+  constexpr int PER = kDecChunk / 256;
+  uint32_t key[PER];
+  int ns = 0, nt = 0;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int64_t s = c0 + tid * PER + u;
+    key[u] = s < c1 ? float_key(sc[s]) : 0u;
+    const uint32_t bin = key[u] >> 21;
+    ns += (s < c1 && bin > T);
+    nt += (s < c1 && bin == T);
+  }
+  int totS, totT;
+  const int ps = block_excl_scan(ns, sh, &totS);
+  const int pt = block_excl_scan(nt, sh + 4, &totT);
+  if (tid == 0) {
+    res[0] = totS ? atomicAdd(&cnt[b * 4 + 0], totS) : 0;
+    res[1] = totT ? atomicAdd(&cnt[b * 4 + 1], totT) : 0;
+  }
+  __syncthreads();
+  int os = res[0] + ps, ot = res[1] + pt;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int64_t s = c0 + tid * PER + u;
+    if (s >= c1) continue;
+    const uint32_t bin = key[u] >> 21;
+    if (bin > T) sure[(int64_t)b * k + os++] = (int32_t)s;
+    else if (bin == T) {
+      ties[(int64_t)b * n_entries + ot++] = make_uint2(key[u], (uint32_t)s);
+      atomicAdd(&lf[(key[u] >> 10) & (kFineBins - 1)], 1);
     }
   }
   __syncthreads();
@@ -491,6 +503,9 @@ __global__ __launch_bounds__(256) void dec_finalize_kernel(
   __shared__ int h256[256];
   __shared__ int32_t outv[2048];
   __shared__ int ocount;
+  __shared__ uint64_t fk[256];
+  __shared__ uint64_t fk64_thr;
+  __shared__ uint32_t bm[kBitmapEntries / 32];
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
   const int64_t vis = min64((posv[b] + 1) / m, n_entries);
@@ -540,9 +555,28 @@ __global__ __launch_bounds__(256) void dec_finalize_kernel(
   __threadfence_block();
   __syncthreads();
   const int nf = cnt[b * 4 + 3];
-  uint32_t thi = 0, tlo = 0;
-  list_select(fl, nf, need2, h256, res, &thi, &tlo);
-  const uint64_t thr = ((uint64_t)thi << 32) | tlo;
+  // threshold on the composite key (score key << 32 | ~index) of the need2-th
+  // best final candidate; 0 takes all of them
+  uint64_t thr = 0;
+  if (nf > need2 && nf <= 256) {  // small set: rank every candidate directly
+    uint64_t ck = 0;
+    if (tid < nf) {
+      const uint2 e = fl[tid];
+      ck = ((uint64_t)e.x << 32) | (uint64_t)(~e.y);
+      fk[tid] = ck;
+    }
+    __syncthreads();
+    int rank = 0;
+    if (tid < nf)
+      for (int j = 0; j < nf; ++j) rank += fk[j] > ck;
+    if (tid < nf && rank == need2 - 1) fk64_thr = ck;  // keys are distinct
+    __syncthreads();
+    thr = fk64_thr;
+  } else if (nf > need2) {
+    uint32_t thi = 0, tlo = 0;
+    list_select(fl, nf, need2, h256, res, &thi, &tlo);
+    thr = ((uint64_t)thi << 32) | tlo;
+  }
   const int base = above + above2;
   if (tid == 0) ocount = 0;
   __syncthreads();
@@ -562,7 +596,31 @@ __global__ __launch_bounds__(256) void dec_finalize_kernel(
     if (take) outv[base + bt + __popcll(mt & below)] = (int32_t)e.y;
   }
   __syncthreads();
-  // bitonic sort of the k chosen indices (ascending), padded to a power of 2
+  if (vis <= kBitmapEntries) {
+    // ascending order from a bitmap of the chosen entries: per-thread runs of
+    // words, popcounts, one block-wide prefix sum, then in-order emission
+    const int W = (int)((vis + 31) >> 5);
+    for (int w = tid; w < W; w += 256) bm[w] = 0u;
+    __syncthreads();
+    for (int j = tid; j < k; j += 256) atomicOr(&bm[outv[j] >> 5], 1u << (outv[j] & 31));
+    __syncthreads();
+    const int WPT = (W + 255) / 256;
+    const int w0 = tid * WPT, w1 = min(w0 + WPT, W);
+    int c = 0;
+    for (int w = w0; w < w1; ++w) c += __popc(bm[w]);
+    int tot;
+    int p = block_excl_scan(c, sh, &tot);
+    for (int w = w0; w < w1; ++w) {
+      uint32_t bits = bm[w];
+      while (bits) {
+        const int bit = __ffs(bits) - 1;
+        orow[p++] = w * 32 + bit;
+        bits &= bits - 1;
+      }
+    }
+    return;
+  }
+  // larger index spaces: bitonic sort of the k chosen indices (ascending)
   int P = 1;
   while (P < k) P <<= 1;
   for (int j = k + tid; j < P; j += 256) outv[j] = 0x7fffffff;
