@@ -452,7 +452,8 @@ hipError_t launch_mqa_prefill(const csa_attn_desc& d, int mode, const void* q, c
 
 static int decode_nsplit(const csa_attn_desc& d, int mode) {
   const int64_t maxc = (int64_t)d.n_win + (mode == ATTN_SPARSE ? d.k : d.n_entries);
-  return (int)((maxc + kDecSplit - 1) / kDecSplit);
+  const int spl = d.dtype == CSA_BF16 ? mqa_decode_bf16_split(mode) : kDecSplit;
+  return (int)((maxc + spl - 1) / spl);
 }
 
 size_t mqa_decode_ws_bytes(const csa_attn_desc& d, int mode) {
@@ -492,6 +493,14 @@ hipError_t launch_mqa_decode(const csa_attn_desc& d, int mode, const void* q, co
                              const void* cache, const int32_t* idx, const int64_t* pos,
                              const float* sink, void* out, void* ws, hipStream_t st) {
   if (d.batch == 0) return hipSuccess;
+  if (d.dtype == CSA_BF16) {
+    const int S_ = decode_nsplit(d, mode);
+    const size_t rows = (size_t)d.batch * S_ * d.n_heads;
+    float* ws_o = (float*)ws;
+    float2* ws_ml = (float2*)((uint8_t*)ws + ((rows * d.c * 4 + 255) & ~(size_t)255));
+    return launch_mqa_decode_bf16(d, mode, q, ring, cache, idx, pos, sink, out, ws_o, ws_ml, S_,
+                                  st);
+  }
   if (d.dtype == CSA_BF16)
     return mode == ATTN_SPARSE
                ? dispatch_decode<BF16, MODE_DECODE_SPARSE>(d, q, ring, cache, idx, pos, sink, out, ws, mode, st)

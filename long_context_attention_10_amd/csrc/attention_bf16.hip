@@ -25,8 +25,6 @@
 
 namespace csa {
 
-typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
-#define CSA_LDS __attribute__((address_space(3)))
 
 namespace {
 
@@ -45,35 +43,23 @@ struct Geo {
   CSA_DEV static int off(int r) { return (r / RPI) * BURST + (r % RPI) * ROW; }
 };
 
-// 16 bytes per lane from global memory straight into LDS (global_load_lds):
-// lane l's bytes land at lds_base + 16*l, lds_base wave-uniform (in M0).
-// Written as inline asm so that the compiler does not track it -- with the
-// builtin it conservatively waits for the load before every LDS read, which
-// serialises the gather with the compute.  This kernel enforces completion
-// itself (wait_vmem, then a barrier) before a filled buffer is read, and no
-// other code in it uses M0.
-CSA_DEV void lds_dma16(const void* g, const void* lds_dst) {
-  const uint32_t base =
-      __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(CSA_LDS const void*)lds_dst);
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, off"
-      :
-      : "v"(g), "s"(base)
-      : "memory");
-}
-
-CSA_DEV void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
 
 }  // namespace
 
-template <int C, bool SPARSE>
-__global__ __launch_bounds__(256, 2) void mqa_prefill_bf16_kernel(
+// DEC = false: prefill, one workgroup per query token, normalised output.
+// DEC = true: decode split-K, one workgroup per (candidate chunk `spl` wide,
+// sequence); the query of sequence b sits at position posv[b], window rows come
+// from the ring (position p in slot p % n_win) and the workgroup writes its
+// unnormalised partial O with (running max in log2 units, running sum), the
+// sink left to the combine.
+template <int C, bool SPARSE, bool DEC>
+__global__ __launch_bounds__(256, 2) void mqa_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ win,
     const uint16_t* __restrict__ comp, const int32_t* __restrict__ idx,
     const float* __restrict__ sink, uint16_t* __restrict__ out, int64_t n, int nh, int k, int m,
-    int n_win, float scale, int qk_norm, float eps, int r, float theta, int64_t n_entries) {
+    int n_win, float scale, int qk_norm, float eps, int r, float theta, int64_t n_entries,
+    const int64_t* __restrict__ posv, float* __restrict__ ws_o, float2* __restrict__ ws_ml,
+    int nsplit, int spl) {
   typedef Geo<C> G;
   constexpr int NKG = C / 32;   // 32-wide k-groups of the head dim
   constexpr int NCB = C / 16;   // 16-channel output blocks
@@ -86,66 +72,110 @@ __global__ __launch_bounds__(256, 2) void mqa_prefill_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int lc = lane & 15, lg = lane >> 4;
 
-  // XCD-aware order: the 8 dies each take a contiguous range of tokens, so a
-  // die's L2 keeps the window rows its consecutive tokens share.
-  const int64_t per = (n + 7) >> 3;
-  const int64_t t = (int64_t)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  if (t >= n) return;
+  int64_t t, qr;  // query position, query row
+  int split = 0;
+  if constexpr (DEC) {
+    qr = blockIdx.y;
+    split = blockIdx.x;
+  } else {
+    // XCD-aware order: the 8 dies each take a contiguous range of tokens, so a
+    // die's L2 keeps the window rows its consecutive tokens share.
+    const int64_t per = (n + 7) >> 3;
+    qr = (int64_t)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    if (qr >= n) return;
+  }
 
-  const int nwin = (int)min64(n_win, t + 1);
-  const int64_t ncomp = SPARSE ? (int64_t)k : min64((t + 1) / m, n_entries);
+  // lane (lg, lc) holds Q[head][32g + 8lg .. +8] for g = 0..C/32-1: the B
+  // operand of S^T = K Q^T.  Loaded straight from global memory, first, so
+  // that the first candidate tile can stream into LDS at the same time.
+  const int head = wave * 16 + lc;
+  uint4 qraw[NKG];
+  {
+    const uint16_t* qh = q + (qr * nh + (head < nh ? head : 0)) * C + lg * 8;
+#pragma unroll
+    for (int g = 0; g < NKG; ++g) qraw[g] = *(const uint4*)(qh + g * 32);
+  }
+
+  t = DEC ? posv[qr] : qr;
+  const int nwin = DEC ? (int)max64(0, min64(n_win, t + 1)) : (int)min64(n_win, t + 1);
+  const int64_t ncomp = SPARSE ? (int64_t)k
+                               : (DEC ? max64(0, min64((t + 1) / m, n_entries))
+                                      : min64((t + 1) / m, n_entries));
   const int64_t ncand = nwin + ncomp;
-  const int ntiles = (int)((ncand + kT - 1) / kT);
-  const int32_t* irow = SPARSE ? idx + t * (int64_t)k : nullptr;
-  const uint16_t* qrow = q + t * (int64_t)nh * C;
+  int64_t cbeg = 0, cend = ncand;
+  if constexpr (DEC) {
+    cbeg = (int64_t)split * spl;
+    cend = min64(cbeg + spl, ncand);
+    if (cbeg >= cend) return;  // nothing in this chunk; the combine skips it
+  }
+  const int ntiles = (int)((cend - cbeg + kT - 1) / kT);
+  const int32_t* irow = SPARSE ? idx + qr * (int64_t)k : nullptr;
+  const uint16_t* wbase = DEC ? win + qr * (int64_t)n_win * C : win;
+  const uint16_t* cbase = DEC ? comp + qr * n_entries * C : comp;
+  const int64_t s0 = DEC ? max64(cbeg - nwin, 0) : 0;  // first index slot staged
+  // decode: ring slot of the oldest window position (candidate j at w0 + j mod n_win)
+  const int w0 = (DEC && nwin > 0) ? (int)((t - nwin + 1) % n_win) : 0;
 
-  // ------------------------ index row and RoPE angles -> LDS; q -> registers
-  if (SPARSE)
-    for (int j = tid; j < k; j += 256) sidx[j] = irow[j];
+  // ------------------------------- index row slice and RoPE angles -> LDS
+  if (SPARSE) {
+    if constexpr (DEC) {
+      for (int64_t j = s0 + tid; j < cend - nwin; j += 256) sidx[j - s0] = irow[j];
+    } else {
+      for (int j = tid; j < k; j += 256) sidx[j] = irow[j];
+    }
+  }
   if (tid < r / 2) {  // one angle per RoPE pair, shared by prologue and epilogue
     float cs, sn;
     rope_cs(t, tid, r, theta, &cs, &sn);
     rope_tab[tid] = make_float2(cs, sn);
   }
-  // lane (lg, lc) holds Q[head][32g + 8lg .. +8] for g = 0..C/32-1: the B
-  // operand of S^T = K Q^T.  Loaded straight from global memory so that the
-  // first candidate tile can stream into LDS at the same time.
-  const int head = wave * 16 + lc;
-  uint4 qraw[NKG];
-  {
-    const uint16_t* qh = qrow + (int64_t)(head < nh ? head : 0) * C + lg * 8;
-#pragma unroll
-    for (int g = 0; g < NKG; ++g) qraw[g] = *(const uint4*)(qh + g * 32);
-  }
   __syncthreads();  // sidx and rope_tab are visible
 
   // ------------------------------------------------ candidate tile loader
+  // Wave w fills bursts w, w+4, ... of the tile.  Lane L < 8 resolves the
+  // wave's L-th row (address and validity flag); each burst's DMA takes its
+  // row address from that lane.
   auto issue_tile = [&](int ti, int buf) {
     uint8_t* base = smem + buf * G::TILE;
     constexpr int BPW = kT / G::RPI / 4;  // bursts (1 KiB each) per wave
-    const uint8_t* src[BPW];
-    // resolve every row first, then issue the loads back to back
-#pragma unroll
-    for (int u = 0; u < BPW; ++u) {
-      const int bi = wave + 4 * u;
-      const int row = bi * G::RPI + lane / (64 / G::RPI);
-      const int64_t j = (int64_t)ti * kT + row;
-      const uint16_t* r = win;  // a valid row for masked candidates
+    constexpr int LPR = 64 / G::RPI;      // lanes per row within a burst
+    const uint16_t* rp = wbase;           // a valid row for masked candidates
+    if (lane < BPW * G::RPI) {
+      const int row = (wave + 4 * (lane / G::RPI)) * G::RPI + lane % G::RPI;
+      const int64_t j = cbeg + (int64_t)ti * kT + row;
       bool ok = false;
-      if (j < ncand) {
+      if (j < cend) {
         if (j < nwin) {
-          r = win + (t - nwin + 1 + j) * C;
+          if constexpr (DEC) {
+            int slot = w0 + (int)j;
+            if (slot >= n_win) slot -= n_win;
+            rp = wbase + (int64_t)slot * C;
+          } else {
+            rp = wbase + (t - nwin + 1 + j) * C;
+          }
           ok = true;
         } else {
-          const int64_t e = SPARSE ? (int64_t)sidx[j - nwin] : j - nwin;
-          if (e >= 0 && e < n_entries) { r = comp + e * C; ok = true; }
+          const int64_t e = SPARSE ? (int64_t)sidx[j - nwin - s0] : j - nwin;
+          if (e >= 0 && e < n_entries) { rp = cbase + e * C; ok = true; }
         }
       }
-      src[u] = (const uint8_t*)r + (lane % (64 / G::RPI)) * 16;
-      if ((lane % (64 / G::RPI)) == 0) valid[buf][row] = ok;
+      valid[buf][row] = ok;
     }
+    const uint32_t ra_lo = (uint32_t)(size_t)rp, ra_hi = (uint32_t)((size_t)rp >> 32);
 #pragma unroll
-    for (int u = 0; u < BPW; ++u) lds_dma16(src[u], base + (wave + 4 * u) * G::BURST);
+    for (int u = 0; u < BPW; ++u) {
+      uint32_t lo, hi;
+      if constexpr (G::RPI == 1) {
+        lo = __builtin_amdgcn_readlane(ra_lo, u);
+        hi = __builtin_amdgcn_readlane(ra_hi, u);
+      } else {
+        const int src = u * G::RPI + lane / LPR;
+        lo = __shfl((int)ra_lo, src, 64);
+        hi = __shfl((int)ra_hi, src, 64);
+      }
+      const uint8_t* g = (const uint8_t*)(size_t)(((uint64_t)hi << 32) | lo) + (lane % LPR) * 16;
+      lds_dma16(g, base + (wave + 4 * u) * G::BURST);
+    }
   };
 
   if (ntiles > 0) issue_tile(0, 0);
@@ -190,7 +220,7 @@ __global__ __launch_bounds__(256, 2) void mqa_prefill_bf16_kernel(
   constexpr float LOG2E = 1.4426950408889634f;
   const float sl2 = scale * LOG2E;
   float run_m = (head < nh ? sink[head] : 0.f) * LOG2E;  // log2 units
-  float run_l = 1.f;
+  float run_l = DEC ? 0.f : 1.f;  // decode partials leave the sink to the combine
 
   // O accumulators in two halves of at most 16 blocks: the compiler keeps
   // fully unrolled 16-entry arrays in registers, not 32-entry ones.
@@ -296,6 +326,20 @@ __global__ __launch_bounds__(256, 2) void mqa_prefill_bf16_kernel(
 
   // ------------------------------------------------------------ epilogue
   // O^T lane layout: block cb, element i = O[head][cb*16 + 4*lg + i]
+  if constexpr (DEC) {
+    if (head < nh) {
+      const int64_t row = (qr * nsplit + split) * nh + head;
+      float* po = ws_o + row * C + 4 * lg;
+#pragma unroll
+      for (int cb = 0; cb < NLO; ++cb) *(f32x4_t*)(po + cb * 16) = o_lo[cb];
+      if constexpr (NCB > 16) {
+#pragma unroll
+        for (int cb = 0; cb < NHI; ++cb) *(f32x4_t*)(po + (NLO + cb) * 16) = o_hi[cb];
+      }
+      if (lg == 0) ws_ml[row] = make_float2(run_m, run_l);
+    }
+    return;
+  }
   const float inv = 1.f / run_l;
   uint8_t* ostage = smem;  // [head][C] bf16, padded like q
   auto emit = [&](int cb, const f32x4_t& acc) {
@@ -323,7 +367,7 @@ __global__ __launch_bounds__(256, 2) void mqa_prefill_bf16_kernel(
     for (int cb = 0; cb < NHI; ++cb) emit(NLO + cb, o_hi[cb]);
   }
   __syncthreads();
-  uint16_t* orow = out + t * (int64_t)nh * C;
+  uint16_t* orow = out + qr * (int64_t)nh * C;
   const int chunks = nh * C / 8;  // 16-byte chunks of this token's output
   for (int ci = tid; ci < chunks; ci += 256) {
     const int h = ci / (C / 8), cc = ci % (C / 8);
@@ -338,19 +382,137 @@ hipError_t launch_mqa_prefill_bf16(const csa_attn_desc& d, int mode, const void*
 #define CSA_FAST(CC)                                                                          \
   if (d.c == CC) {                                                                           \
     if (mode == ATTN_SPARSE)                                                                 \
-      mqa_prefill_bf16_kernel<CC, true><<<grid, 256, 0, st>>>(                               \
+      mqa_bf16_kernel<CC, true, false><<<grid, 256, 0, st>>>(                               \
           (const uint16_t*)q, (const uint16_t*)win, (const uint16_t*)comp, idx, sink,         \
           (uint16_t*)out, d.n, d.n_heads, d.k, d.m, d.n_win, d.scale, d.qk_norm, d.eps,       \
-          d.rope_dims, d.rope_theta, d.n_entries);                                            \
+          d.rope_dims, d.rope_theta, d.n_entries, nullptr, nullptr, nullptr, 0, 0);           \
     else                                                                                     \
-      mqa_prefill_bf16_kernel<CC, false><<<grid, 256, 0, st>>>(                              \
+      mqa_bf16_kernel<CC, false, false><<<grid, 256, 0, st>>>(                              \
           (const uint16_t*)q, (const uint16_t*)win, (const uint16_t*)comp, idx, sink,         \
           (uint16_t*)out, d.n, d.n_heads, d.k, d.m, d.n_win, d.scale, d.qk_norm, d.eps,       \
-          d.rope_dims, d.rope_theta, d.n_entries);                                            \
+          d.rope_dims, d.rope_theta, d.n_entries, nullptr, nullptr, nullptr, 0, 0);           \
     return hipGetLastError();                                                                \
   }
   CSA_FAST(128) CSA_FAST(256) CSA_FAST(512)
 #undef CSA_FAST
+  return hipErrorInvalidValue;
+}
+
+// Fixed-order merge of the chunk partials of one sequence with the sink, then
+// normalisation and the inverse RoPE at the query position.  One wave per
+// (sequence, head); lane l owns channels [CPL*l, CPL*l + CPL).  Chunks are
+// read eight at a time and folded in index order with a running max.
+template <int C>
+__global__ __launch_bounds__(256) void mqa_decode_combine_kernel(
+    const float* __restrict__ ws_o, const float2* __restrict__ ws_ml,
+    const int64_t* __restrict__ posv, const float* __restrict__ sink, uint16_t* __restrict__ out,
+    int nh, int nsplit, int spl, int sparse, int k, int m, int n_win, int64_t n_entries, int r,
+    float theta) {
+  constexpr int CPL = C / 64;
+  constexpr int U = 8;
+  constexpr float LOG2E = 1.4426950408889634f;
+  const int lane = threadIdx.x & 63;
+  const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int64_t b = blockIdx.x;
+  if (h >= nh) return;  // whole wave
+  const int64_t pos = posv[b];
+  const int64_t nwin = max64(0, min64(n_win, pos + 1));
+  const int64_t ncomp = sparse ? (int64_t)k : max64(0, min64((pos + 1) / m, n_entries));
+  const int ns = (int)((nwin + ncomp + spl - 1) / spl);  // chunks that hold candidates
+  const float2* ml = ws_ml + (int64_t)b * nsplit * nh + h;
+  const float* po = ws_o + ((int64_t)b * nsplit * nh + h) * C + lane * CPL;
+  float M = sink[h] * LOG2E;
+  float den = 1.f;  // exp2(sink - M)
+  float acc[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) acc[i] = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += U) {
+    float2 mv[U];
+    float ov[U][CPL];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + u;
+      mv[u] = make_float2(-INFINITY, 0.f);
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) ov[u][i] = 0.f;
+      if (s < ns) {
+        mv[u] = ml[(int64_t)s * nh];
+        const float* p = po + (int64_t)s * nh * C;
+#pragma unroll
+        for (int i = 0; i < CPL; i += 2) {
+          const float2 v = *(const float2*)(p + i);
+          ov[u][i] = v.x;
+          ov[u][i + 1] = v.y;
+        }
+      }
+    }
+    float cm = M;
+#pragma unroll
+    for (int u = 0; u < U; ++u) cm = fmaxf(cm, mv[u].x);
+    const float a = __builtin_amdgcn_exp2f(M - cm);
+    den *= a;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) acc[i] *= a;
+    M = cm;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float f = __builtin_amdgcn_exp2f(mv[u].x - M);
+      den += f * mv[u].y;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) acc[i] += f * ov[u][i];
+    }
+  }
+  const float inv = 1.f / den;
+  float v[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) v[i] = acc[i] * inv;
+  const int ch0 = lane * CPL;
+  if (r > 0 && ch0 >= C - r) {
+#pragma unroll
+    for (int i = 0; i < CPL; i += 2) {
+      float cs, sn;
+      rope_cs(pos, (ch0 + i - (C - r)) >> 1, r, theta, &cs, &sn);
+      const float x0 = v[i], x1 = v[i + 1];
+      v[i] = x0 * cs + x1 * sn;  // rotate by -pos
+      v[i + 1] = -x0 * sn + x1 * cs;
+    }
+  }
+  uint16_t* o = out + (b * nh + h) * C + ch0;
+#pragma unroll
+  for (int i = 0; i < CPL; i += 2)
+    *(uint32_t*)(o + i) = (uint32_t)f32_to_bf16(v[i]) | ((uint32_t)f32_to_bf16(v[i + 1]) << 16);
+}
+
+int mqa_decode_bf16_split(int mode) { return mode == ATTN_SPARSE ? 128 : 256; }
+
+hipError_t launch_mqa_decode_bf16(const csa_attn_desc& d, int mode, const void* q,
+                                  const void* ring, const void* cache, const int32_t* idx,
+                                  const int64_t* pos, const float* sink, void* out, float* ws_o,
+                                  float2* ws_ml, int nsplit, hipStream_t st) {
+  const int spl = mqa_decode_bf16_split(mode);
+  const dim3 grid((unsigned)nsplit, (unsigned)d.batch);
+  const dim3 cgrid((unsigned)d.batch, (unsigned)((d.n_heads + 3) / 4));
+#define CSA_DEC(CC)                                                                            \
+  if (d.c == CC) {                                                                            \
+    if (mode == ATTN_SPARSE)                                                                  \
+      mqa_bf16_kernel<CC, true, true><<<grid, 256, 0, st>>>(                                  \
+          (const uint16_t*)q, (const uint16_t*)ring, (const uint16_t*)cache, idx, sink, nullptr, \
+          d.batch, d.n_heads, d.k, d.m, d.n_win, d.scale, d.qk_norm, d.eps, d.rope_dims,         \
+          d.rope_theta, d.n_entries, pos, ws_o, ws_ml, nsplit, spl);                           \
+    else                                                                                      \
+      mqa_bf16_kernel<CC, false, true><<<grid, 256, 0, st>>>(                                 \
+          (const uint16_t*)q, (const uint16_t*)ring, (const uint16_t*)cache, idx, sink, nullptr, \
+          d.batch, d.n_heads, d.k, d.m, d.n_win, d.scale, d.qk_norm, d.eps, d.rope_dims,         \
+          d.rope_theta, d.n_entries, pos, ws_o, ws_ml, nsplit, spl);                           \
+    hipError_t e = hipGetLastError();                                                         \
+    if (e != hipSuccess) return e;                                                            \
+    mqa_decode_combine_kernel<CC><<<cgrid, 256, 0, st>>>(                                     \
+        ws_o, ws_ml, pos, sink, (uint16_t*)out, d.n_heads, nsplit, spl, mode == ATTN_SPARSE,    \
+        d.k, d.m, d.n_win, d.n_entries, d.rope_dims, d.rope_theta);                            \
+    return hipGetLastError();                                                                 \
+  }
+  CSA_DEC(128) CSA_DEC(256) CSA_DEC(512)
+#undef CSA_DEC
   return hipErrorInvalidValue;
 }
 

@@ -15,6 +15,8 @@ namespace csa {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
+#define CSA_LDS __attribute__((address_space(3)))
 
 // ---------------------------------------------------------------- bf16 <-> f32
 CSA_DEV float bf16_to_f32(uint16_t x) { return __uint_as_float(((uint32_t)x) << 16); }
@@ -126,6 +128,28 @@ CSA_DEV uint32_t float_key(float f) {
   uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+
+// 16 bytes per lane from global memory straight into LDS (global_load_lds):
+// lane l's bytes land at lds_base + 16*l, lds_base wave-uniform (in M0).
+// Written as inline asm so that the compiler does not track it -- with the
+// builtin it conservatively waits for the load before every LDS read, which
+// serialises a gather with the compute that overlaps it.  Kernels using it
+// enforce completion themselves (wait_vmem, then a barrier) before a filled
+// buffer is read, and no other code in them uses M0.
+CSA_DEV void lds_dma16(const void* g, const void* lds_dst) {
+  const uint32_t base =
+      __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(CSA_LDS const void*)lds_dst);
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(g), "s"(base)
+      : "memory");
+}
+
+// Wait for every outstanding memory operation of the wave.
+CSA_DEV void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
 
 CSA_DEV int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
 CSA_DEV int64_t max64(int64_t a, int64_t b) { return a > b ? a : b; }

@@ -75,6 +75,12 @@ hipError_t launch_mqa_prefill_bf16(const csa_attn_desc& d, int mode, const void*
                                    void* out, hipStream_t st);
 
 size_t mqa_decode_ws_bytes(const csa_attn_desc& d, int mode);
+// bf16 decode: split-K chunk width (candidates) and the split-K launcher
+int mqa_decode_bf16_split(int mode);
+hipError_t launch_mqa_decode_bf16(const csa_attn_desc& d, int mode, const void* q,
+                                  const void* ring, const void* cache, const int32_t* idx,
+                                  const int64_t* pos, const float* sink, void* out, float* ws_o,
+                                  float2* ws_ml, int nsplit, hipStream_t st);
 hipError_t launch_mqa_decode(const csa_attn_desc& d, int mode, const void* q, const void* ring,
                              const void* cache, const int32_t* idx, const int64_t* pos,
                              const float* sink, void* out, void* ws, hipStream_t st);

@@ -130,6 +130,7 @@ def _ring_rows(ring_b, pos, n_win):
     ("bf16", 64, 512, 512, 4, 4000, 128, 64, [15999, 100, 3, 700]),
     ("f32", 8, 128, 64, 4, 300, 128, 0, [1199, 20]),
     ("bf16", 64, 128, 100, 128, 1100, 128, 0, [140799, 127, 128]),
+    ("bf16", 40, 256, 300, 4, 2500, 64, 32, [9999, 0, 255, 64, 1300]),
 ])
 def test_mqa_decode(lib, sparse, dtype, nh, c, k, m, ne, n_win, r, pos):
     _say("mqa_decode", sparse, dtype, nh, c, k, m, ne, n_win, r, pos)
