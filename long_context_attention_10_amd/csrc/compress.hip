@@ -11,6 +11,10 @@
 
 namespace csa {
 
+// Most K slices of a decode projection (the update sums them per column with
+// all loads in flight at once).
+constexpr int kMaxKSplit = 8;
+
 // ===========================================================================
 // Projection GEMM:  out[M, 0:N] (fp32) = A[M, K] . [W0; W1; W2]^T
 // 128x128 output tile per 256-thread workgroup (2x2 waves of 64x64), K staged
@@ -383,25 +387,47 @@ __global__ __launch_bounds__(256) void decode_update_kernel(
   const bool emit = (rr == m - 1);
   const int64_t blk = pos / m;
 
-  auto colsum = [&](int col) {
-    float s = 0.f;
-    for (int k = 0; k < ksplit; ++k) s += part[((int64_t)k * B + b) * N + col];
-    return s;
+  // Sum of the K-slice partials of columns (col, col+1), slices in order.  All
+  // columns this thread needs are summed up front so that their loads are in
+  // flight together.
+  // (Loads are unconditional -- slices past ksplit re-read the last one and
+  // add zero -- so that no branch separates them.)
+  auto colsum2 = [&](int col) {
+    float2 v[kMaxKSplit];
+#pragma unroll
+    for (int k = 0; k < kMaxKSplit; ++k)
+      v[k] = *(const float2*)(part + ((int64_t)min(k, ksplit - 1) * B + b) * N + col);
+    float2 acc = v[0];  // ksplit >= 1
+#pragma unroll
+    for (int k = 1; k < kMaxKSplit; ++k) {
+      acc.x += k < ksplit ? v[k].x : 0.f;
+      acc.y += k < ksplit ? v[k].y : 0.f;
+    }
+    return acc;
   };
+  const int ca = ov ? c : 0;  // a-series (or the only series) columns
+  float2 kva = make_float2(0.f, 0.f), za = kva, kvb = kva, zb = kva, wn = kva;
+  if (live) {
+    kva = colsum2(ca + 2 * j);
+    za = colsum2(w + ca + 2 * j);
+    if (ov) {
+      kvb = colsum2(2 * j);
+      zb = colsum2(w + 2 * j);
+    }
+    if (has_win) wn = colsum2(2 * w + 2 * j);
+  }
 
   float e0 = 0.f, e1 = 0.f;
   if (live) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int ch = 2 * j + q;
-      // a-series (or the only series)
-      const int ca = ov ? c : 0;
       float mx = st[0 * c + ch], sm = st[1 * c + ch], ac = st[2 * c + ch];
-      osm_push(mx, sm, ac, colsum(w + ca + ch) + ape[(int64_t)rr * w + ca + ch], colsum(ca + ch));
+      osm_push(mx, sm, ac, (q ? za.y : za.x) + ape[(int64_t)rr * w + ca + ch], q ? kva.y : kva.x);
       float mb = -INFINITY, sb = 0.f, ab = 0.f;
       if (ov) {
         mb = st[3 * c + ch]; sb = st[4 * c + ch]; ab = st[5 * c + ch];
-        osm_push(mb, sb, ab, colsum(w + ch) + ape[(int64_t)rr * w + ch], colsum(ch));
+        osm_push(mb, sb, ab, (q ? zb.y : zb.x) + ape[(int64_t)rr * w + ch], q ? kvb.y : kvb.x);
       }
       if (emit) {
         float em = mx, es = sm, ea = ac;
@@ -426,8 +452,7 @@ __global__ __launch_bounds__(256) void decode_update_kernel(
     }
   }
   if (has_win) {
-    float v0 = 0.f, v1 = 0.f;
-    if (live) { v0 = colsum(2 * w + 2 * j); v1 = colsum(2 * w + 2 * j + 1); }
+    float v0 = wn.x, v1 = wn.y;
     row_finish<G>(v0, v1, j, c, pos, qk_norm, eps, r, theta, red);
     if (live) {
       typename T::S* dst = ring + ((int64_t)b * n_win + pos % n_win) * c;
@@ -516,10 +541,10 @@ hipError_t launch_state_init(float* state, int64_t per_seq, int batch, int c, hi
 int decode_proj_ksplit(int N, int K, int dtype) {
   const int kg4 = (dtype == CSA_BF16 ? 16 : 8) * 4;  // smallest per-wave slice
   const int tiles = (N + 31) / 32;
-  // At most 8 K slices: the update kernel sums the slices per column with one
-  // workgroup per sequence, so more slices would make that sum latency-bound.
+  // At most kMaxKSplit slices: the update kernel sums the slices of a column in
+  // one workgroup per sequence, so more slices would make that sum slower.
   int ks = 1;
-  while (tiles * ks < 512 && K % (ks * 2 * kg4) == 0 && ks < 8) ks *= 2;
+  while (tiles * ks < 512 && K % (ks * 2 * kg4) == 0 && ks < kMaxKSplit) ks *= 2;
   return ks;
 }
 

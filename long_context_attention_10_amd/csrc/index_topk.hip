@@ -266,10 +266,9 @@ struct DecWs {  // carve-up of the decode workspace
   float* scores;      // [B][n_entries]
   int* hist;          // [B][kCoarseBins]
   int* fine;          // [B][kFineBins]
-  int* cnt;           // [B][4]: sure, tie, sure2, fin
+  int* cnt;           // [B][4]: sure count, tie count, unused x2
   int32_t* sure;      // [B][k]
   uint2* ties;        // [B][n_entries] (key, index)
-  uint2* fin;         // [B][n_entries] final ties (key, index)
 };
 
 static size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -284,14 +283,13 @@ static DecWs carve(void* ws, const csa_index_desc& d) {
   w.cnt = (int*)p; p += align_up(B * 4 * 4);
   w.sure = (int32_t*)p; p += align_up(B * (size_t)d.k * 4);
   w.ties = (uint2*)p; p += align_up(B * ne * 8);
-  w.fin = (uint2*)p; p += align_up(B * ne * 8);
   return w;
 }
 
 size_t index_decode_ws_bytes(const csa_index_desc& d) {
   const size_t B = d.batch, ne = d.n_entries;
   return align_up(B * ne * 4) + align_up(B * kCoarseBins * 4) + align_up(B * kFineBins * 4) +
-         align_up(B * 16) + align_up(B * (size_t)d.k * 4) + 2 * align_up(B * ne * 8);
+         align_up(B * 16) + align_up(B * (size_t)d.k * 4) + align_up(B * ne * 8);
 }
 
 __global__ void dec_clear_kernel(int* hist, int* fine, int* cnt, int B) {
@@ -402,14 +400,13 @@ CSA_DEV void coarse_threshold(const int* __restrict__ h, int nb, int need, int* 
   __syncthreads();
 }
 
-__global__ __launch_bounds__(256) void dec_collect_kernel(const int64_t* __restrict__ posv,
-                                                          int64_t n_entries, int m, int k,
-                                                          const float* __restrict__ scores,
-                                                          const int* __restrict__ hist,
-                                                          int* __restrict__ fine,
-                                                          int* __restrict__ cnt,
-                                                          int32_t* __restrict__ sure,
-                                                          uint2* __restrict__ ties) {
+// Second histogram level: entries in the coarse threshold bin T are counted by
+// the next 11 bits of their key.
+__global__ __launch_bounds__(256) void dec_refine_kernel(const int64_t* __restrict__ posv,
+                                                         int64_t n_entries, int m, int k,
+                                                         const float* __restrict__ scores,
+                                                         const int* __restrict__ hist,
+                                                         int* __restrict__ fine) {
   __shared__ int sh[8];
   __shared__ int res[2];
   __shared__ int lf[kFineBins];
@@ -419,15 +416,49 @@ __global__ __launch_bounds__(256) void dec_collect_kernel(const int64_t* __restr
   const int64_t c0 = (int64_t)blockIdx.x * kDecChunk;
   if (c0 >= vis) return;
   const int64_t c1 = min64(c0 + kDecChunk, vis);
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x;
   for (int i = tid; i < kFineBins; i += 256) lf[i] = 0;
   coarse_threshold(hist + (int64_t)b * kCoarseBins, kCoarseBins, k, sh, res);
   const uint32_t T = (uint32_t)res[0];
   const float* sc = scores + (int64_t)b * n_entries;
-  // each thread classifies a contiguous run of 4 entries; one block-wide
-  // prefix sum per list turns the per-thread counts into positions, so each
-  // workgroup makes a single atomic reservation per list (the lists are
-  // shared by every workgroup of the sequence).
+  for (int64_t s = c0 + tid; s < c1; s += 256) {
+    const uint32_t key = float_key(sc[s]);
+    if ((key >> 21) == T) atomicAdd(&lf[(key >> 10) & (kFineBins - 1)], 1);
+  }
+  __syncthreads();
+  for (int i = tid; i < kFineBins; i += 256)
+    if (lf[i]) atomicAdd(&fine[(int64_t)b * kFineBins + i], lf[i]);
+}
+
+// With the 22-bit threshold prefix P of the k-th key known from both
+// histogram levels, every entry whose prefix is above P is in the top k (the
+// "sure" list) and those equal to P are the final candidates (the tie list).
+// Each thread classifies a contiguous run of entries; one block-wide prefix
+// sum per list turns its counts into positions, so a workgroup makes a single
+// atomic reservation per list.
+__global__ __launch_bounds__(256) void dec_collect_kernel(const int64_t* __restrict__ posv,
+                                                          int64_t n_entries, int m, int k,
+                                                          const float* __restrict__ scores,
+                                                          const int* __restrict__ hist,
+                                                          const int* __restrict__ fine,
+                                                          int* __restrict__ cnt,
+                                                          int32_t* __restrict__ sure,
+                                                          uint2* __restrict__ ties) {
+  __shared__ int sh[8];
+  __shared__ int res[2];
+  const int b = blockIdx.y;
+  const int64_t vis = min64((posv[b] + 1) / m, n_entries);
+  if (vis <= k) return;
+  const int64_t c0 = (int64_t)blockIdx.x * kDecChunk;
+  if (c0 >= vis) return;
+  const int64_t c1 = min64(c0 + kDecChunk, vis);
+  const int tid = threadIdx.x;
+  coarse_threshold(hist + (int64_t)b * kCoarseBins, kCoarseBins, k, sh, res);
+  const uint32_t T = (uint32_t)res[0];
+  const int above = res[1];
+  coarse_threshold(fine + (int64_t)b * kFineBins, kFineBins, k - above, sh, res);
+  const uint32_t P = (T << 11) | (uint32_t)res[0];
+  const float* sc = scores + (int64_t)b * n_entries;
   constexpr int PER = kDecChunk / 256;
   uint32_t key[PER];
   int ns = 0, nt = 0;
@@ -435,9 +466,9 @@ __global__ __launch_bounds__(256) void dec_collect_kernel(const int64_t* __restr
   for (int u = 0; u < PER; ++u) {
     const int64_t s = c0 + tid * PER + u;
     key[u] = s < c1 ? float_key(sc[s]) : 0u;
-    const uint32_t bin = key[u] >> 21;
-    ns += (s < c1 && bin > T);
-    nt += (s < c1 && bin == T);
+    const uint32_t pre = key[u] >> 10;
+    ns += (s < c1 && pre > P);
+    nt += (s < c1 && pre == P);
   }
   int totS, totT;
   const int ps = block_excl_scan(ns, sh, &totS);
@@ -452,16 +483,10 @@ __global__ __launch_bounds__(256) void dec_collect_kernel(const int64_t* __restr
   for (int u = 0; u < PER; ++u) {
     const int64_t s = c0 + tid * PER + u;
     if (s >= c1) continue;
-    const uint32_t bin = key[u] >> 21;
-    if (bin > T) sure[(int64_t)b * k + os++] = (int32_t)s;
-    else if (bin == T) {
-      ties[(int64_t)b * n_entries + ot++] = make_uint2(key[u], (uint32_t)s);
-      atomicAdd(&lf[(key[u] >> 10) & (kFineBins - 1)], 1);
-    }
+    const uint32_t pre = key[u] >> 10;
+    if (pre > P) sure[(int64_t)b * k + os++] = (int32_t)s;
+    else if (pre == P) ties[(int64_t)b * n_entries + ot++] = make_uint2(key[u], (uint32_t)s);
   }
-  __syncthreads();
-  for (int i = tid; i < kFineBins; i += 256)
-    if (lf[i]) atomicAdd(&fine[(int64_t)b * kFineBins + i], lf[i]);
 }
 
 // Radix selection over a list in global memory of `cnt` (key, index) pairs,
@@ -495,8 +520,8 @@ CSA_DEV void list_select(const uint2* __restrict__ L, int cnt, int need, int* hi
 
 __global__ __launch_bounds__(256) void dec_finalize_kernel(
     const int64_t* __restrict__ posv, int64_t n_entries, int m, int k,
-    const int* __restrict__ hist, const int* __restrict__ fine, int* __restrict__ cnt,
-    const int32_t* __restrict__ sure, const uint2* __restrict__ ties, uint2* __restrict__ fin,
+    const int* __restrict__ hist, const int* __restrict__ fine, const int* __restrict__ cnt,
+    const int32_t* __restrict__ sure, const uint2* __restrict__ ties,
     int32_t* __restrict__ idx_out) {
   __shared__ int sh[8];
   __shared__ int res[2];
@@ -514,78 +539,41 @@ __global__ __launch_bounds__(256) void dec_finalize_kernel(
     for (int j = tid; j < k; j += 256) orow[j] = j < vis ? j : -1;
     return;
   }
-  // coarse threshold: `above` entries are in the sure list
-  coarse_threshold(hist + (int64_t)b * kCoarseBins, kCoarseBins, k, sh, res);
-  const int above = res[1];
-  const int need1 = k - above;  // still to choose among the coarse-bin ties
-  __syncthreads();
-  coarse_threshold(fine + (int64_t)b * kFineBins, kFineBins, need1, sh, res);
-  const uint32_t T2 = (uint32_t)res[0];
-  const int above2 = res[1];
-  const int need2 = need1 - above2;  // to choose among the fine-bin ties
-  __syncthreads();
-  if (tid == 0) ocount = 0;
-  __syncthreads();
-  // copy the sure list
-  for (int j = tid; j < above; j += 256) outv[j] = sure[(int64_t)b * k + j];
-  // scan the tie list: fine bin > T2 -> taken; == T2 -> final candidates
-  const int nt = cnt[b * 4 + 1];
+  const int ns = cnt[b * 4 + 0];  // sure entries: k - need of them
+  const int nt = cnt[b * 4 + 1];  // final candidates sharing the threshold prefix
+  const int need = k - ns;        // >= 1 by the threshold construction
+  for (int j = tid; j < ns; j += 256) outv[j] = sure[(int64_t)b * k + j];
   const uint2* tl = ties + (int64_t)b * n_entries;
-  uint2* fl = fin + (int64_t)b * n_entries;
-  for (int i0 = 0; i0 < nt; i0 += 256) {
-    const int i = i0 + tid;
-    uint2 e = make_uint2(0, 0);
-    const bool ok = i < nt;
-    if (ok) e = tl[i];
-    const uint32_t fb = (e.x >> 10) & (kFineBins - 1);
-    const bool take = ok && fb > T2;
-    const bool cand = ok && fb == T2;
-    const uint64_t mt = __ballot(take), mc = __ballot(cand);
-    int bt = 0, bc = 0;
-    if (lane == 0) {
-      if (mt) bt = atomicAdd(&ocount, __popcll(mt));
-      if (mc) bc = atomicAdd(&cnt[b * 4 + 3], __popcll(mc));
-    }
-    bt = __shfl(bt, 0, 64);
-    bc = __shfl(bc, 0, 64);
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    if (take) outv[above + bt + __popcll(mt & below)] = (int32_t)e.y;
-    if (cand) fl[bc + __popcll(mc & below)] = e;
-  }
-  __threadfence_block();
-  __syncthreads();
-  const int nf = cnt[b * 4 + 3];
-  // threshold on the composite key (score key << 32 | ~index) of the need2-th
-  // best final candidate; 0 takes all of them
+  // composite key (score key << 32 | ~index): larger is better, all distinct;
+  // thr = the need-th largest among the candidates (0 takes all of them)
   uint64_t thr = 0;
-  if (nf > need2 && nf <= 256) {  // small set: rank every candidate directly
+  if (nt > need && nt <= 256) {  // small set: rank every candidate directly
     uint64_t ck = 0;
-    if (tid < nf) {
-      const uint2 e = fl[tid];
+    if (tid < nt) {
+      const uint2 e = tl[tid];
       ck = ((uint64_t)e.x << 32) | (uint64_t)(~e.y);
       fk[tid] = ck;
     }
     __syncthreads();
     int rank = 0;
-    if (tid < nf)
-      for (int j = 0; j < nf; ++j) rank += fk[j] > ck;
-    if (tid < nf && rank == need2 - 1) fk64_thr = ck;  // keys are distinct
+    if (tid < nt)
+      for (int j = 0; j < nt; ++j) rank += fk[j] > ck;
+    if (tid < nt && rank == need - 1) fk64_thr = ck;
     __syncthreads();
     thr = fk64_thr;
-  } else if (nf > need2) {
+  } else if (nt > need) {
     uint32_t thi = 0, tlo = 0;
-    list_select(fl, nf, need2, h256, res, &thi, &tlo);
+    list_select(tl, nt, need, h256, res, &thi, &tlo);
     thr = ((uint64_t)thi << 32) | tlo;
   }
-  const int base = above + above2;
   if (tid == 0) ocount = 0;
   __syncthreads();
-  for (int i0 = 0; i0 < nf; i0 += 256) {
+  for (int i0 = 0; i0 < nt; i0 += 256) {
     const int i = i0 + tid;
     bool take = false;
     uint2 e = make_uint2(0, 0);
-    if (i < nf) {
-      e = fl[i];
+    if (i < nt) {
+      e = tl[i];
       take = (((uint64_t)e.x << 32) | (uint64_t)(~e.y)) >= thr;
     }
     const uint64_t mt = __ballot(take);
@@ -593,7 +581,7 @@ __global__ __launch_bounds__(256) void dec_finalize_kernel(
     if (lane == 0 && mt) bt = atomicAdd(&ocount, __popcll(mt));
     bt = __shfl(bt, 0, 64);
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    if (take) outv[base + bt + __popcll(mt & below)] = (int32_t)e.y;
+    if (take) outv[ns + bt + __popcll(mt & below)] = (int32_t)e.y;
   }
   __syncthreads();
   if (vis <= kBitmapEntries) {
@@ -697,10 +685,12 @@ hipError_t launch_index_topk_decode(const csa_index_desc& d, const void* qI, con
           (const float*)qI, (const float*)wI, (const float*)KI, pos, d.n_entries, d.m, d.k,
           w.scores, w.hist);
   });
+  dec_refine_kernel<<<dim3(chunks, B), 256, 0, st>>>(pos, d.n_entries, d.m, d.k, w.scores, w.hist,
+                                                     w.fine);
   dec_collect_kernel<<<dim3(chunks, B), 256, 0, st>>>(pos, d.n_entries, d.m, d.k, w.scores, w.hist,
                                                       w.fine, w.cnt, w.sure, w.ties);
   dec_finalize_kernel<<<B, 256, 0, st>>>(pos, d.n_entries, d.m, d.k, w.hist, w.fine, w.cnt, w.sure,
-                                         w.ties, w.fin, idx_out);
+                                         w.ties, idx_out);
   return hipGetLastError();
 }
 
