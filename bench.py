@@ -13,12 +13,18 @@ step and us per token, with the caches built beforehand by the library's own
 prefill from seeded N(0,1) hidden states.
 
 `roofline` is measured live for the dominant kernel (sparse MQA prefill) with
-HIP events on the stream it runs on; `cpu_baseline` times the CPU fp64 oracle
-on a bounded sample of the same workload.
+HIP events on the stream it runs on; its `traffic` (HBM bytes per launch) is
+read from the committed rocprofv3 counter summary of that kernel, and is null
+when the kernel source no longer matches the one the counters were taken on.
+`cpu_baseline` times the CPU fp64 oracle on a bounded sample of the same
+workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode]
-                       [--no-cpu-baseline] [--profile-mode]
+                       [--no-cpu-baseline] [--pmc-probe]
+  --pmc-probe: run only a 1 GiB device copy (the counter scale reference)
+               and the sparse MQA prefill, for rocprofv3 --pmc passes.
 """
+import hashlib
 import argparse
 import json
 import os
@@ -36,6 +42,8 @@ from long_context_attention_10_amd import configs, inputs as I  # noqa: E402
 
 PEAK_BF16 = 2.5e15      # dense bf16 matrix FLOP/s, MI355X
 PEAK_HBM = 8.0e12       # HBM3E bytes/s, MI355X
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mqa_prefill_bf16_64k_traffic.txt")
+MQA_SOURCE = os.path.join(ROOT, "long_context_attention_10_amd", "csrc", "attention_bf16.hip")
 
 
 # --------------------------------------------------------------------------
@@ -107,6 +115,58 @@ def time_region(fn, steps, warmup, flush=None):
         torch.cuda.synchronize()
         times.append(s.elapsed_time(e))
     return times
+
+
+def graph_of(fn):
+    """Capture fn (after a warm call that sizes every workspace) in a HIP graph."""
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def measured_traffic():
+    """HBM bytes per sparse-MQA-prefill launch from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, each scaled by the factor a plain 1 GiB
+    copy gives), or None if that summary is absent or was taken on another
+    version of the kernel source."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as fh:
+            for line in fh:
+                if ":" in line and not line.startswith("#"):
+                    a, b = line.split(":", 1)
+                    kv[a.strip()] = b.strip()
+        with open(MQA_SOURCE, "rb") as fh:
+            sha = hashlib.sha256(fh.read()).hexdigest()
+        if kv.get("source_sha256") != sha:
+            return None
+        return float(kv["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def pmc_probe():
+    """One 1 GiB device-to-device copy (counter scale reference), then the
+    sparse MQA prefill of the 64K workload twice."""
+    dev = "cuda"
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    pf = CsaPrefill(configs.get("csa_prefill_64k_bf16"), dev)
+    pf.compress()
+    pf.index()
+    torch.cuda.synchronize()
+    for _ in range(2):
+        pf.attend()
+    torch.cuda.synchronize()
+    print("[bench] pmc probe done: 1 GiB copy, 2 x sparse MQA prefill", flush=True)
 
 
 # --------------------------------------------------------------------------
@@ -267,14 +327,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--profile-mode", action="store_true",
-                    help="fewer repetitions; for runs under rocprofv3")
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="only the copy reference and the MQA prefill, for counter passes")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {a.gpus}).",
               file=sys.stderr)
         sys.exit(2)
     L.load()
+    if a.pmc_probe:
+        pmc_probe()
+        return
     dev = "cuda"
     cfg = configs.get("csa_prefill_64k_bf16")
     print(f"[bench] building inputs for {cfg['name']}", file=sys.stderr, flush=True)
@@ -303,7 +366,7 @@ def main():
         "stages_ms": {"compress": comp_ms, "index_topk": idx_ms, "sparse_mqa": att_ms},
         "roofline": {"kernel": "mqa_kernel (csa_sparse_mqa_prefill)", "bound": "mfma",
                      "achieved": achieved / 1e12, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16, "traffic": None,
+                     "frac": achieved / PEAK_BF16, "traffic": measured_traffic(),
                      "algorithmic": f"{flops:.4g} FLOP per launch = 4 x 64 heads x 512 x "
                                     f"{pairs} (token, candidate) pairs"},
     }
@@ -322,13 +385,21 @@ def main():
             print(f"[bench] timing {wname}", file=sys.stderr, flush=True)
             tt = time_region(hd.step, max(3, a.steps), 2, flush=flush)
             tw = time_region(hd.step, max(3, a.steps), 1)
+            g = graph_of(hd.step)  # the same step, launched as one HIP graph
+            tg = time_region(g.replay, max(3, a.steps), 2, flush=flush)
+            tgw = time_region(g.replay, max(3, a.steps), 1)
             us = float(np.median(tt)) * 1e3
+            ug = float(np.median(tg)) * 1e3
             byts = hd.algorithmic_bytes()
             dec[wname] = {"us_per_step": us, "us_per_token": us / dc["batch"],
                           "us_per_step_warm_cache": float(np.mean(tw)) * 1e3,
+                          "graph_us_per_step": ug, "graph_us_per_token": ug / dc["batch"],
+                          "graph_us_per_step_warm_cache": float(np.mean(tgw)) * 1e3,
                           "batch": dc["batch"], "ctx": dc["ctx"], "k": dc["k"],
                           "hbm_bytes_algorithmic": byts,
-                          "hbm_frac": byts / (us * 1e-6) / PEAK_HBM}
+                          "hbm_frac": byts / (us * 1e-6) / PEAK_HBM,
+                          "graph_hbm_frac": byts / (ug * 1e-6) / PEAK_HBM}
+            del g
             del hd
             torch.cuda.empty_cache()
         rec["decode"] = dec

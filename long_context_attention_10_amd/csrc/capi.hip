@@ -67,6 +67,7 @@ int check_index(const csa_index_desc* d, bool decode) {
   return CSA_OK;
 }
 
+// Row stride of the prefill score workspace (a multiple of 4 floats).
 int64_t index_prefill_ld(const csa_index_desc* d) {
   const int64_t vis = d->n / d->m < d->n_entries ? d->n / d->m : d->n_entries;
   return (vis + 3) & ~(int64_t)3;

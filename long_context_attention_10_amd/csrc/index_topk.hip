@@ -170,61 +170,204 @@ CSA_DEV void find_digit(const int* hist, int need, int* out) {
   }
 }
 
+// Threshold bin from a histogram (suffix search from the top): the bin T with
+// (#items in bins > T) < need <= (#items in bins >= T); every thread gets
+// res = (T, #items above T).  `h` holds NB bins (global memory or LDS), `sh`
+// is LDS scratch of 4 ints; 256 threads.
+template <int NB>
+CSA_DEV void bin_threshold(const int* __restrict__ h, int need, int* sh, int* res) {
+  constexpr int PER = NB / 256;  // consecutive bins per thread
+  const int tid = threadIdx.x;
+  int loc[PER];
+  int cs = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) { loc[i] = h[tid * PER + i]; cs += loc[i]; }
+  // inclusive suffix sum over threads
+  const int lane = tid & 63, wave = tid >> 6;
+  int suf = cs;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_down(suf, o, 64);
+    if (lane + o < 64) suf += y;
+  }
+  __syncthreads();
+  if (lane == 0) sh[wave] = suf;
+  __syncthreads();
+  int above_w = 0;
+  for (int w = wave + 1; w < 4; ++w) above_w += sh[w];
+  suf += above_w;
+  const int above = suf - cs;
+  if (suf >= need && above < need) {
+    int acc = above;
+    for (int i = PER - 1; i >= 0; --i) {
+      if (acc + loc[i] >= need) { res[0] = tid * PER + i; res[1] = acc; break; }
+      acc += loc[i];
+    }
+  }
+  __syncthreads();
+}
+
+CSA_DEV void coarse_threshold(const int* __restrict__ h, int nb, int need, int* sh, int* res) {
+  bin_threshold<2048>(h, need, sh, res);
+}
+
 // ===========================================================================
-// Prefill row selection: one workgroup per query row, the row's keys held in
-// registers (thread j owns a contiguous run of IT entries), 4 radix passes of
-// 8 bits over the order-preserving keys, then an ordered compaction.
+// Prefill row selection: one workgroup per query row; the row's keys (order-
+// preserving uint32 images of the scores) are staged once in LDS.
+//   1. keys are binned linearly by score VALUE between the row minimum and
+//      maximum (1024 bins; the map is monotone, so each bin is a key
+//      interval, whose smallest key is recorded) and the threshold bin T is
+//      found from the histogram -- raw float bits would pile most of a row
+//      into the few bins of its common exponent;
+//   2. the entries of bin T are resolved exactly: ranked directly on
+//      (key, -index) when at most 256, else by radix selection over
+//      x = key - (smallest key of T) in 10-bit digits;
+//   3. an ordered compaction over contiguous runs writes the chosen indices
+//      ascending.
 // ===========================================================================
+constexpr int kSelBins = 1024;
+constexpr int kRankMax = 256;
+
+CSA_DEV float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
 template <int MAXIT>
 __global__ __launch_bounds__(256) void topk_rows_prefill_kernel(const float* __restrict__ scores,
                                                                 int64_t ld, int64_t n,
                                                                 int64_t n_entries, int m, int k,
                                                                 int32_t* __restrict__ idx_out) {
-  __shared__ int hist[256];
+  __shared__ uint32_t kbuf[MAXIT * 256 + MAXIT * 4];  // entry e at e + e/64
+  __shared__ int hist[kSelBins];
+  __shared__ uint32_t bmin[kSelBins];
   __shared__ int tmp[8];
   __shared__ int res[2];
-  const int64_t t = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int64_t v = min64((t + 1) / m, n_entries);
-  const int kt = (int)min64(k, v);
-  int32_t* orow = idx_out + t * k;
+  __shared__ uint32_t red[8];
+  __shared__ int ncand;
+  __shared__ uint64_t cand[kRankMax];
+  __shared__ uint64_t cthr;
+  const int t = (int)blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int v = (int)min64((int64_t)(t + 1) / m, n_entries);
+  const int kt = min(k, v);
+  int32_t* orow = idx_out + (int64_t)t * k;
   if (v <= k) {
     for (int j = tid; j < k; j += 256) orow[j] = j < v ? j : -1;
     return;
   }
-  const int IT = (int)((v + 255) / 256);
-  const int64_t base = (int64_t)tid * IT;
-  const float* srow = scores + t * ld;
-  uint32_t u[MAXIT];
+  // load with 16-byte coalesced reads (row start 16-byte aligned, ld % 4 == 0)
+  const float* srow = scores + (int64_t)t * ld;
+  uint32_t lo = 0xffffffffu, hi = 0u;
+  for (int e = 4 * tid; e < v; e += 1024) {
+    const float4 x = *(const float4*)(srow + e);
+    const uint32_t k4[4] = {float_key(x.x), float_key(x.y), float_key(x.z), float_key(x.w)};
+    uint32_t* d = kbuf + e + (e >> 6);
 #pragma unroll
-  for (int i = 0; i < MAXIT; ++i) {
-    const int64_t e = base + i;
-    u[i] = (i < IT && e < v) ? float_key(srow[e]) : 0u;  // key 0 is below every real score
+    for (int j = 0; j < 4; ++j) {
+      d[j] = k4[j];
+      if (e + j < v) { lo = min(lo, k4[j]); hi = max(hi, k4[j]); }
+    }
   }
-  uint32_t prefix = 0, pmask = 0;
-  int need = kt;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    hist[tid] = 0;
-    __syncthreads();
+  for (int i = tid; i < kSelBins; i += 256) { hist[i] = 0; bmin[i] = 0xffffffffu; }
+  if (tid == 0) ncand = 0;
 #pragma unroll
-    for (int i = 0; i < MAXIT; ++i) {
-      if (i < IT && base + i < v && (u[i] & pmask) == prefix) atomicAdd(&hist[(u[i] >> shift) & 255], 1);
+  for (int o = 32; o >= 1; o >>= 1) {
+    lo = min(lo, (uint32_t)__shfl_xor((int)lo, o, 64));
+    hi = max(hi, (uint32_t)__shfl_xor((int)hi, o, 64));
+  }
+  if (lane == 0) { red[wave] = lo; red[4 + wave] = hi; }
+  __syncthreads();
+  lo = min(min(red[0], red[1]), min(red[2], red[3]));
+  hi = max(max(red[4], red[5]), max(red[6], red[7]));
+  const float fmin = key_float(lo), fmax = key_float(hi);
+  float scale = (float)kSelBins / (fmax - fmin);
+  if (!(scale < INFINITY)) scale = 0.f;  // equal or non-finite range: one bin
+  auto vbin = [&](uint32_t key) {
+    const float f = (key_float(key) - fmin) * scale;
+    return f >= (float)(kSelBins - 1) ? kSelBins - 1 : (f > 0.f ? (int)f : 0);
+  };
+
+  // 1. value histogram (with each bin's smallest key) and threshold bin
+  for (int e = tid; e < v; e += 256) {
+    const uint32_t key = kbuf[e + (e >> 6)];
+    const int b = vbin(key);
+    atomicAdd(&hist[b], 1);
+    atomicMin(&bmin[b], key);
+  }
+  __syncthreads();
+  bin_threshold<kSelBins>(hist, kt, tmp, res);
+  const int T = res[0];
+  int need = kt - res[1];  // to take from bin T (>= 1)
+  const int nT = hist[T];
+  // bin T = keys in [tlo, thi): thi = smallest key of the next non-empty bin
+  const uint32_t tlo = bmin[T];
+  uint32_t nx = 0xffffffffu;
+  for (int b = T + 1 + tid; b < kSelBins; b += 256) nx = min(nx, bmin[b]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) nx = min(nx, (uint32_t)__shfl_xor((int)nx, o, 64));
+  if (lane == 0) red[wave] = nx;
+  __syncthreads();
+  const uint64_t thi = T == kSelBins - 1 ? (uint64_t)hi + 1
+                                          : (uint64_t)min(min(red[0], red[1]), min(red[2], red[3]));
+  auto in_t = [&](uint32_t key) { return key >= tlo && (uint64_t)key < thi; };
+
+  // 2. resolve bin T exactly: key thr of the last one taken, and how many
+  //    entries with that key to take (in index order)
+  uint32_t thr;
+  if (nT <= kRankMax) {
+    for (int e = tid; e < v; e += 256) {
+      const uint32_t key = kbuf[e + (e >> 6)];
+      if (in_t(key)) cand[atomicAdd(&ncand, 1)] = ((uint64_t)key << 32) | (uint32_t)(~(uint32_t)e);
     }
     __syncthreads();
-    find_digit(hist, need, res);
+    if (tid < nT) {
+      const uint64_t c = cand[tid];
+      int rank = 0;
+      for (int j = 0; j < nT; ++j) rank += cand[j] > c;
+      if (rank == need - 1) cthr = c;
+    }
     __syncthreads();
-    const int d = res[0];
-    need -= res[1];
-    prefix |= (uint32_t)d << shift;
-    pmask |= 0xffu << shift;
-    __syncthreads();
+    const uint64_t c = cthr;
+    thr = (uint32_t)(c >> 32);
+    // equal keys are taken in index order up to the chosen one
+    const int eqn = tid < nT && (uint32_t)(cand[tid] >> 32) == thr && cand[tid] >= c;
+    int tot;
+    block_excl_scan(eqn, tmp, &tot);
+    need = tot;
+  } else {
+    // many entries in one value bin (ties or a degenerate range): radix
+    // selection on x = key - tlo over the keys of bin T
+    const uint32_t range = (uint32_t)(thi - 1 - tlo);
+    const int nbits = range ? 32 - __clz(range) : 0;
+    uint32_t prefix = 0, pmask = 0;
+    for (int top = nbits; top > 0; top -= 10) {
+      const int shift = top > 10 ? top - 10 : 0;
+      const uint32_t dmask = (1u << (top - shift)) - 1u;
+      __syncthreads();
+      for (int i = tid; i < kSelBins; i += 256) hist[i] = 0;
+      __syncthreads();
+      for (int e = tid; e < v; e += 256) {
+        const uint32_t key = kbuf[e + (e >> 6)];
+        const uint32_t x = key - tlo;
+        if (in_t(key) && (x & pmask) == prefix) atomicAdd(&hist[(x >> shift) & dmask], 1);
+      }
+      __syncthreads();
+      bin_threshold<kSelBins>(hist, need, tmp, res);
+      need -= res[1];
+      prefix |= (uint32_t)res[0] << shift;
+      pmask |= dmask << shift;
+    }
+    thr = tlo + prefix;
   }
-  // prefix = key of the kt-th largest; need = how many equal keys to take
+
+  // 3. ordered compaction: keys above thr, then the first `need` equal to it
+  const int IT = (v + 255) / 256;
+  const int e0 = tid * IT, e1 = min(e0 + IT, v);
   int gt = 0, eq = 0;
-#pragma unroll
-  for (int i = 0; i < MAXIT; ++i) {
-    if (i < IT && base + i < v) { gt += u[i] > prefix; eq += u[i] == prefix; }
+  for (int e = e0; e < e1; ++e) {
+    const uint32_t key = kbuf[e + (e >> 6)];
+    gt += key > thr;
+    eq += key == thr;
   }
   int tot;
   const int eq_before = block_excl_scan(eq, tmp, &tot);
@@ -232,13 +375,11 @@ __global__ __launch_bounds__(256) void topk_rows_prefill_kernel(const float* __r
   take_eq = take_eq < 0 ? 0 : (take_eq > eq ? eq : take_eq);
   const int pos0 = block_excl_scan(gt + take_eq, tmp + 4, &tot);
   int p = pos0, te = 0;
-#pragma unroll
-  for (int i = 0; i < MAXIT; ++i) {
-    if (i < IT && base + i < v) {
-      const bool take = u[i] > prefix || (u[i] == prefix && te < take_eq);
-      if (u[i] == prefix) te += 1;
-      if (take) orow[p++] = (int32_t)(base + i);
-    }
+  for (int e = e0; e < e1; ++e) {
+    const uint32_t key = kbuf[e + (e >> 6)];
+    const bool take = key > thr || (key == thr && te < take_eq);
+    te += key == thr;
+    if (take) orow[p++] = e;
   }
   for (int j = kt + tid; j < k; j += 256) orow[j] = -1;
 }
@@ -249,13 +390,14 @@ __global__ __launch_bounds__(256) void topk_rows_prefill_kernel(const float* __r
 //   D1 score chunks of keys (16x16 matrix-core tiles, keys streamed straight
 //      from memory -- this pass moves the step's dominant bytes) and build a
 //      2048-bin histogram of the keys' top 11 bits;
-//   D2 per chunk: find the coarse threshold bin, append entries above it to
-//      the "sure" list and entries in it to the tie list, and histogram the
-//      ties' next 11 bits;
-//   D3 per sequence: resolve the tie list exactly (fine bin, then radix
-//      selection on (score, -index)), merge, sort ascending, write.
-// Counts use integer atomics (order-independent), and the final sort makes
-// the output independent of the order in which lists were filled.
+//   D2 per chunk: find the coarse threshold bin T and histogram the next 11
+//      bits of the keys in T;
+//   D3 per chunk: with the 22-bit threshold prefix P known, append entries
+//      above P to the "sure" list and entries equal to P to the tie list;
+//   D4 per sequence: resolve the tie list exactly on (score, -index), merge,
+//      emit ascending indices through a bitmap.
+// Counts use integer atomics (order-independent), and the final ordering
+// makes the output independent of the order in which lists were filled.
 // ===========================================================================
 constexpr int kDecChunk = 1024;    // keys per scoring workgroup
 constexpr int kCoarseBins = 2048;  // top 11 bits
@@ -366,39 +508,6 @@ __global__ __launch_bounds__(256) void dec_score_kernel(
     if (lh[i]) atomicAdd(&hist[(int64_t)b * kCoarseBins + i], lh[i]);
 }
 
-// Threshold bin from a histogram (suffix search from the top); every thread
-// gets (bin, count above bin).  `h` is in global memory, `sh` LDS scratch.
-CSA_DEV void coarse_threshold(const int* __restrict__ h, int nb, int need, int* sh, int* res) {
-  // per-thread sums over 8 consecutive bins (256 threads x 8 = 2048)
-  const int tid = threadIdx.x;
-  int loc[8];
-  int c8 = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) { loc[i] = h[tid * 8 + i]; c8 += loc[i]; }
-  // inclusive suffix sum over threads
-  const int lane = tid & 63, wave = tid >> 6;
-  int suf = c8;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_down(suf, o, 64);
-    if (lane + o < 64) suf += y;
-  }
-  __syncthreads();
-  if (lane == 0) sh[wave] = suf;
-  __syncthreads();
-  int above_w = 0;
-  for (int w = wave + 1; w < 4; ++w) above_w += sh[w];
-  suf += above_w;
-  const int above = suf - c8;
-  if (suf >= need && above < need) {
-    int acc = above;
-    for (int i = 7; i >= 0; --i) {
-      if (acc + loc[i] >= need) { res[0] = tid * 8 + i; res[1] = acc; break; }
-      acc += loc[i];
-    }
-  }
-  __syncthreads();
-}
 
 // Second histogram level: entries in the coarse threshold bin T are counted by
 // the next 11 bits of their key.
