@@ -64,7 +64,7 @@ __global__ __launch_bounds__(256, 2) void mqa_bf16_kernel(
   constexpr int NKG = C / 32;   // 32-wide k-groups of the head dim
   constexpr int NCB = C / 16;   // 16-channel output blocks
   __shared__ __align__(16) uint8_t smem[G::BUF];
-  __shared__ int valid[2][kT];
+  __shared__ __align__(16) int valid[2][kT];
   __shared__ int sidx[SPARSE ? kMaxK : 1];
   __shared__ float2 rope_tab[C / 2];  // (cos, sin) of this token's RoPE pairs
 
@@ -116,21 +116,6 @@ __global__ __launch_bounds__(256, 2) void mqa_bf16_kernel(
   // decode: ring slot of the oldest window position (candidate j at w0 + j mod n_win)
   const int w0 = (DEC && nwin > 0) ? (int)((t - nwin + 1) % n_win) : 0;
 
-  // ------------------------------- index row slice and RoPE angles -> LDS
-  if (SPARSE) {
-    if constexpr (DEC) {
-      for (int64_t j = s0 + tid; j < cend - nwin; j += 256) sidx[j - s0] = irow[j];
-    } else {
-      for (int j = tid; j < k; j += 256) sidx[j] = irow[j];
-    }
-  }
-  if (tid < r / 2) {  // one angle per RoPE pair, shared by prologue and epilogue
-    float cs, sn;
-    rope_cs(t, tid, r, theta, &cs, &sn);
-    rope_tab[tid] = make_float2(cs, sn);
-  }
-  __syncthreads();  // sidx and rope_tab are visible
-
   // ------------------------------------------------ candidate tile loader
   // Wave w fills bursts w, w+4, ... of the tile.  Lane L < 8 resolves the
   // wave's L-th row (address and validity flag); each burst's DMA takes its
@@ -178,7 +163,27 @@ __global__ __launch_bounds__(256, 2) void mqa_bf16_kernel(
     }
   };
 
-  if (ntiles > 0) issue_tile(0, 0);
+  // The first tile holds only window rows whenever the window covers it; its
+  // gather then need not wait for the index row.
+  const bool early0 = ntiles > 0 && cbeg + kT <= nwin;
+  if (early0) issue_tile(0, 0);
+
+  // ------------------------------- index row slice and RoPE angles -> LDS
+  if (SPARSE) {
+    if constexpr (DEC) {
+      for (int64_t j = s0 + tid; j < cend - nwin; j += 256) sidx[j - s0] = irow[j];
+    } else {
+      for (int j = tid; j < k; j += 256) sidx[j] = irow[j];
+    }
+  }
+  if (tid < r / 2) {  // one angle per RoPE pair, shared by prologue and epilogue
+    float cs, sn;
+    rope_cs(t, tid, r, theta, &cs, &sn);
+    rope_tab[tid] = make_float2(cs, sn);
+  }
+  __syncthreads();  // sidx and rope_tab are visible
+  if (ntiles > 0 && !early0) issue_tile(0, 0);
+
 
   // --------------------------------- q prologue: RMSNorm, RoPE, bf16 regs
   bf16x8_t qf[NKG];
@@ -265,15 +270,17 @@ __global__ __launch_bounds__(256, 2) void mqa_bf16_kernel(
     float z[8];
     float mx = -INFINITY;
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 2; ++b) {
+      const int4 vf = *(const int4*)&valid[buf][pi(lg, b, 0)];  // rows pi(lg, b, 0..3)
+      const int vfl[4] = {vf.x, vf.y, vf.z, vf.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float zz = valid[buf][pi(lg, b, i)] ? s[b][i] * sl2 : -INFINITY;
+        const float zz = vfl[i] ? s[b][i] * sl2 : -INFINITY;
         z[4 * b + i] = zz;
         mx = fmaxf(mx, zz);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    }
+    mx = xlane_max(mx);
     const bool need = mx > run_m + 8.f;
     if (__any(need)) {  // wave-uniform rescale of O
       const float nm = fmaxf(run_m, mx);
@@ -298,8 +305,7 @@ __global__ __launch_bounds__(256, 2) void mqa_bf16_kernel(
       p[j] = __builtin_amdgcn_exp2f(z[j] - run_m);
       ps += p[j];
     }
-    ps += __shfl_xor(ps, 16, 64);
-    ps += __shfl_xor(ps, 32, 64);
+    ps = xlane_sum(ps);
     run_l += ps;
     const bf16x8_t pb = __builtin_convertvector(p, bf16x8_t);  // B operand, slots 8*lg+j
 

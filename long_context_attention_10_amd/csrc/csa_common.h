@@ -123,6 +123,22 @@ CSA_DEV float wave_max(float v) {
   return v;
 }
 
+// Max / sum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48)
+// with the permlane swaps: every lane gets the same, bitwise identical value,
+// and no LDS instruction is involved.
+CSA_DEV float xlane_max(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+CSA_DEV float xlane_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Order-preserving map fp32 -> uint32 (larger float -> larger key).
 CSA_DEV uint32_t float_key(float f) {
   uint32_t u = __float_as_uint(f);
