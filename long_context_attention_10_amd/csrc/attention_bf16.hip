@@ -258,13 +258,20 @@ __global__ __launch_bounds__(256, 2) void mqa_bf16_kernel(
     const uint8_t* kv = smem + buf * G::TILE;
 
     // S^T = K Q^T for the tile: block b's A rows are K rows pi(lc/4, b, lc%4)
+    // (fragments of k-group g+1 are read while g's products issue, so the LDS
+    // latency overlaps the matrix cores)
     f32x4_t s[2] = {f32x4_t{}, f32x4_t{}};
+    bf16x8_t a0[2], a1[2];
+    a0[0] = *(const bf16x8_t*)(kv + koff0);
+    a1[0] = *(const bf16x8_t*)(kv + koff1);
 #pragma unroll
     for (int g = 0; g < NKG; ++g) {
-      const bf16x8_t a0 = *(const bf16x8_t*)(kv + koff0 + g * 64);
-      const bf16x8_t a1 = *(const bf16x8_t*)(kv + koff1 + g * 64);
-      s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[g], s[0], 0, 0, 0);
-      s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[g], s[1], 0, 0, 0);
+      if (g + 1 < NKG) {
+        a0[(g + 1) & 1] = *(const bf16x8_t*)(kv + koff0 + (g + 1) * 64);
+        a1[(g + 1) & 1] = *(const bf16x8_t*)(kv + koff1 + (g + 1) * 64);
+      }
+      s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[g & 1], qf[g], s[0], 0, 0, 0);
+      s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[g & 1], qf[g], s[1], 0, 0, 0);
     }
     // online softmax for head `head` (this lane's column) in log2 units
     float z[8];
