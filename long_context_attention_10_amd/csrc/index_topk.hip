@@ -212,18 +212,19 @@ CSA_DEV void coarse_threshold(const int* __restrict__ h, int nb, int need, int* 
 }
 
 // ===========================================================================
-// Prefill row selection: one workgroup per query row; the row's keys (order-
-// preserving uint32 images of the scores) are staged once in LDS.
+// Prefill row selection: one workgroup per query row over its v <= 16384
+// visible scores, held in registers as order-preserving uint32 keys (thread
+// j owns entries 4(j + 256 i) + 0..3).  Entries are ordered by the composite
+// (key << 32 | ~index): higher score first, ties to the smaller index.
 //   1. keys are binned linearly by score VALUE between the row minimum and
 //      maximum (1024 bins; the map is monotone, so each bin is a key
-//      interval, whose smallest key is recorded) and the threshold bin T is
-//      found from the histogram -- raw float bits would pile most of a row
-//      into the few bins of its common exponent;
-//   2. the entries of bin T are resolved exactly: ranked directly on
-//      (key, -index) when at most 256, else by radix selection over
-//      x = key - (smallest key of T) in 10-bit digits;
-//   3. an ordered compaction over contiguous runs writes the chosen indices
-//      ascending.
+//      interval, whose smallest key is recorded) and the bin T holding the
+//      k-th largest is found from the histogram -- raw float bits would pile
+//      most of a row into the few bins of its common exponent;
+//   2. T is resolved exactly: its composites are ranked directly when at
+//      most 256, else selected by an 8-bit radix over the composites of T;
+//   3. the winners are marked in an LDS bitmap over the row, which is
+//      emitted in ascending index order.
 // ===========================================================================
 constexpr int kSelBins = 1024;
 constexpr int kRankMax = 256;
@@ -231,21 +232,25 @@ constexpr int kRankMax = 256;
 CSA_DEV float key_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
+CSA_DEV uint64_t composite(uint32_t key, uint32_t idx) {
+  return ((uint64_t)key << 32) | (uint32_t)~idx;
+}
 
 template <int MAXIT>
 __global__ __launch_bounds__(256) void topk_rows_prefill_kernel(const float* __restrict__ scores,
                                                                 int64_t ld, int64_t n,
                                                                 int64_t n_entries, int m, int k,
                                                                 int32_t* __restrict__ idx_out) {
-  __shared__ uint32_t kbuf[MAXIT * 256 + MAXIT * 4];  // entry e at e + e/64
+  constexpr int NQ = MAXIT / 4;  // 4-entry groups per thread
   __shared__ int hist[kSelBins];
   __shared__ uint32_t bmin[kSelBins];
+  __shared__ uint32_t bits[MAXIT * 256 / 32];
+  __shared__ uint64_t cand[kRankMax];
+  __shared__ uint64_t cthr;
   __shared__ int tmp[8];
   __shared__ int res[2];
   __shared__ uint32_t red[8];
   __shared__ int ncand;
-  __shared__ uint64_t cand[kRankMax];
-  __shared__ uint64_t cthr;
   const int t = (int)blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int v = (int)min64((int64_t)(t + 1) / m, n_entries);
@@ -255,21 +260,34 @@ __global__ __launch_bounds__(256) void topk_rows_prefill_kernel(const float* __r
     for (int j = tid; j < k; j += 256) orow[j] = j < v ? j : -1;
     return;
   }
-  // load with 16-byte coalesced reads (row start 16-byte aligned, ld % 4 == 0)
+  // keys (coalesced 16-byte loads, all in flight together; the row start is
+  // 16-byte aligned and ld % 4 == 0).  Entries past v get key 0, below every
+  // real key.
   const float* srow = scores + (int64_t)t * ld;
-  uint32_t lo = 0xffffffffu, hi = 0u;
-  for (int e = 4 * tid; e < v; e += 1024) {
-    const float4 x = *(const float4*)(srow + e);
-    const uint32_t k4[4] = {float_key(x.x), float_key(x.y), float_key(x.z), float_key(x.w)};
-    uint32_t* d = kbuf + e + (e >> 6);
+  uint32_t u[MAXIT];
+  {
+    float4 xs[NQ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      d[j] = k4[j];
-      if (e + j < v) { lo = min(lo, k4[j]); hi = max(hi, k4[j]); }
+    for (int q = 0; q < NQ; ++q) {
+      const int e = 4 * (tid + 256 * q);
+      if (e < v) xs[q] = *(const float4*)(srow + e);
+    }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int e = 4 * (tid + 256 * q);
+      const float x4[4] = {xs[q].x, xs[q].y, xs[q].z, xs[q].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) u[4 * q + j] = e + j < v ? float_key(x4[j]) : 0u;
     }
   }
+  auto idx_of = [&](int i) { return 4 * (tid + 256 * (i >> 2)) + (i & 3); };
   for (int i = tid; i < kSelBins; i += 256) { hist[i] = 0; bmin[i] = 0xffffffffu; }
+  for (int w = tid; w < MAXIT * 256 / 32; w += 256) bits[w] = 0u;
   if (tid == 0) ncand = 0;
+  uint32_t lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+  for (int i = 0; i < MAXIT; ++i)
+    if (u[i]) { lo = min(lo, u[i]); hi = max(hi, u[i]); }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     lo = min(lo, (uint32_t)__shfl_xor((int)lo, o, 64));
@@ -287,13 +305,14 @@ __global__ __launch_bounds__(256) void topk_rows_prefill_kernel(const float* __r
     return f >= (float)(kSelBins - 1) ? kSelBins - 1 : (f > 0.f ? (int)f : 0);
   };
 
-  // 1. value histogram (with each bin's smallest key) and threshold bin
-  for (int e = tid; e < v; e += 256) {
-    const uint32_t key = kbuf[e + (e >> 6)];
-    const int b = vbin(key);
-    atomicAdd(&hist[b], 1);
-    atomicMin(&bmin[b], key);
-  }
+  // 1. value histogram with each bin's smallest key; threshold bin T
+#pragma unroll
+  for (int i = 0; i < MAXIT; ++i)
+    if (u[i]) {
+      const int b = vbin(u[i]);
+      atomicAdd(&hist[b], 1);
+      atomicMin(&bmin[b], u[i]);
+    }
   __syncthreads();
   bin_threshold<kSelBins>(hist, kt, tmp, res);
   const int T = res[0];
@@ -311,75 +330,63 @@ __global__ __launch_bounds__(256) void topk_rows_prefill_kernel(const float* __r
                                           : (uint64_t)min(min(red[0], red[1]), min(red[2], red[3]));
   auto in_t = [&](uint32_t key) { return key >= tlo && (uint64_t)key < thi; };
 
-  // 2. resolve bin T exactly: key thr of the last one taken, and how many
-  //    entries with that key to take (in index order)
-  uint32_t thr;
+  // 2. the need-th largest composite of bin T
+  uint64_t thr;
   if (nT <= kRankMax) {
-    for (int e = tid; e < v; e += 256) {
-      const uint32_t key = kbuf[e + (e >> 6)];
-      if (in_t(key)) cand[atomicAdd(&ncand, 1)] = ((uint64_t)key << 32) | (uint32_t)(~(uint32_t)e);
-    }
+#pragma unroll
+    for (int i = 0; i < MAXIT; ++i)
+      if (u[i] && in_t(u[i])) cand[atomicAdd(&ncand, 1)] = composite(u[i], idx_of(i));
     __syncthreads();
     if (tid < nT) {
       const uint64_t c = cand[tid];
       int rank = 0;
       for (int j = 0; j < nT; ++j) rank += cand[j] > c;
-      if (rank == need - 1) cthr = c;
+      if (rank == need - 1) cthr = c;  // composites are distinct
     }
     __syncthreads();
-    const uint64_t c = cthr;
-    thr = (uint32_t)(c >> 32);
-    // equal keys are taken in index order up to the chosen one
-    const int eqn = tid < nT && (uint32_t)(cand[tid] >> 32) == thr && cand[tid] >= c;
-    int tot;
-    block_excl_scan(eqn, tmp, &tot);
-    need = tot;
+    thr = cthr;
   } else {
-    // many entries in one value bin (ties or a degenerate range): radix
-    // selection on x = key - tlo over the keys of bin T
-    const uint32_t range = (uint32_t)(thi - 1 - tlo);
-    const int nbits = range ? 32 - __clz(range) : 0;
-    uint32_t prefix = 0, pmask = 0;
-    for (int top = nbits; top > 0; top -= 10) {
-      const int shift = top > 10 ? top - 10 : 0;
-      const uint32_t dmask = (1u << (top - shift)) - 1u;
+    uint64_t prefix = 0, pmask = 0;
+    for (int pass = 0; pass < 8; ++pass) {
+      const int shift = 56 - 8 * pass;
       __syncthreads();
-      for (int i = tid; i < kSelBins; i += 256) hist[i] = 0;
+      hist[tid] = 0;
       __syncthreads();
-      for (int e = tid; e < v; e += 256) {
-        const uint32_t key = kbuf[e + (e >> 6)];
-        const uint32_t x = key - tlo;
-        if (in_t(key) && (x & pmask) == prefix) atomicAdd(&hist[(x >> shift) & dmask], 1);
+#pragma unroll
+      for (int i = 0; i < MAXIT; ++i) {
+        const uint64_t c = composite(u[i], idx_of(i));
+        if (u[i] && in_t(u[i]) && (c & pmask) == prefix) atomicAdd(&hist[(c >> shift) & 255], 1);
       }
       __syncthreads();
-      bin_threshold<kSelBins>(hist, need, tmp, res);
+      bin_threshold<256>(hist, need, tmp, res);
       need -= res[1];
-      prefix |= (uint32_t)res[0] << shift;
-      pmask |= dmask << shift;
+      prefix |= (uint64_t)res[0] << shift;
+      pmask |= (uint64_t)0xff << shift;
     }
-    thr = tlo + prefix;
+    thr = prefix;
   }
 
-  // 3. ordered compaction: keys above thr, then the first `need` equal to it
-  const int IT = (v + 255) / 256;
-  const int e0 = tid * IT, e1 = min(e0 + IT, v);
-  int gt = 0, eq = 0;
-  for (int e = e0; e < e1; ++e) {
-    const uint32_t key = kbuf[e + (e >> 6)];
-    gt += key > thr;
-    eq += key == thr;
-  }
+  // 3. winners -> bitmap -> ascending indices
+#pragma unroll
+  for (int i = 0; i < MAXIT; ++i)
+    if (u[i] && composite(u[i], idx_of(i)) >= thr) {
+      const int e = idx_of(i);
+      atomicOr(&bits[e >> 5], 1u << (e & 31));
+    }
+  __syncthreads();
+  const int W = (v + 31) / 32;
+  const int WPT = (W + 255) / 256;
+  const int w0 = tid * WPT, w1 = min(w0 + WPT, W);
+  int cnt = 0;
+  for (int w = w0; w < w1; ++w) cnt += __popc(bits[w]);
   int tot;
-  const int eq_before = block_excl_scan(eq, tmp, &tot);
-  int take_eq = need - eq_before;
-  take_eq = take_eq < 0 ? 0 : (take_eq > eq ? eq : take_eq);
-  const int pos0 = block_excl_scan(gt + take_eq, tmp + 4, &tot);
-  int p = pos0, te = 0;
-  for (int e = e0; e < e1; ++e) {
-    const uint32_t key = kbuf[e + (e >> 6)];
-    const bool take = key > thr || (key == thr && te < take_eq);
-    te += key == thr;
-    if (take) orow[p++] = e;
+  int p = block_excl_scan(cnt, tmp + 4, &tot);
+  for (int w = w0; w < w1; ++w) {
+    uint32_t b = bits[w];
+    while (b) {
+      orow[p++] = w * 32 + __ffs(b) - 1;
+      b &= b - 1;
+    }
   }
   for (int j = kt + tid; j < k; j += 256) orow[j] = -1;
 }
