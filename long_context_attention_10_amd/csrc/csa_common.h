@@ -139,6 +139,12 @@ CSA_DEV float xlane_sum(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// v + v[lane ^ 32] (the same value, bitwise, in both lanes of each pair).
+CSA_DEV float swap32_add(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+
 // Order-preserving map fp32 -> uint32 (larger float -> larger key).
 CSA_DEV uint32_t float_key(float f) {
   uint32_t u = __float_as_uint(f);

@@ -16,10 +16,13 @@ namespace csa {
 
 // ===========================================================================
 // Prefill scoring: scores[t][s] for a tile of queries x all keys of a chunk.
-// One 256-thread workgroup owns 16*HI... rows (query, head) pairs: each wave
-// holds two 32-row blocks of (query, head) rows; keys are staged 32 at a
-// time in LDS and fed to 32x32 matrix-core blocks.  The head reduction with
-// the ReLU and weights happens in registers.
+// One 256-thread workgroup owns 16*HI... (query, head) rows: each wave holds
+// two 32-row blocks of them as matrix-core A operands for the whole chunk.
+// Keys stream through LDS in blocks of KB by direct global->LDS loads into a
+// double buffer (the next block loads while the current one is consumed).
+// Key rows are stored unpadded with their 16-byte granules XOR-permuted, so
+// the 16 lanes of a B-fragment read (16 keys, one granule each) hit distinct
+// banks.  The head reduction with the ReLU and weights happens in registers.
 // ===========================================================================
 template <class T, int HI, int CI>
 __global__ __launch_bounds__(256) void index_scores_prefill_kernel(
@@ -33,15 +36,36 @@ __global__ __launch_bounds__(256) void index_scores_prefill_kernel(
   constexpr int RB = 2;             // 32-row blocks per wave
   constexpr int ROWS = 4 * RB * 32; // (query, head) rows per workgroup
   constexpr int TQ = ROWS / HI;     // queries per workgroup
-  constexpr int ROWB = CI * (int)sizeof(S) + 16;  // LDS bytes per key row
-  __shared__ __align__(16) uint8_t sK[32 * ROWB];
+  constexpr int RBYTES = CI * (int)sizeof(S);   // bytes per key row
+  constexpr int GR = RBYTES / 16;               // granules per key row
+  constexpr int KB = RBYTES <= 128 ? 128 : 64;  // keys per staged block
+  constexpr int KPI = 1024 / RBYTES;            // keys per 64-lane DMA
+  constexpr int DPW = KB / KPI / 4;             // DMA instructions per wave per block
+  static_assert(GR >= 8 && DPW >= 1, "key row layout");
+  __shared__ __align__(16) uint8_t sK[2][KB * RBYTES];
+  auto swz = [](int key) { return GR == 8 ? (key >> 1) & 7 : key & 15; };
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hl = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t q0 = (int64_t)blockIdx.x * TQ;
   const int64_t tlast = min64(q0 + TQ, n) - 1;
   const int64_t kend = min64(min64((tlast + 1) / m, n_entries), (int64_t)(blockIdx.y + 1) * key_chunk);
   const int64_t kbeg = (int64_t)blockIdx.y * key_chunk;
   if (kbeg >= kend) return;
+
+  // keys past kend are read from the last key; their scores are not stored
+  auto issue_block = [&](int64_t k0, int buf) {
+#pragma unroll
+    for (int u = 0; u < DPW; ++u) {
+      const int d = wave + 4 * u;             // DMA index within the block
+      const int key = d * KPI + lane / GR;    // key within the block
+      const int pos = lane % GR;              // LDS granule position
+      const int64_t sidx = min64(k0 + key, kend - 1);
+      const uint8_t* src = (const uint8_t*)(KI + sidx * CI) + 16 * (pos ^ swz(key));
+      lds_dma16(src, &sK[buf][d * 1024]);
+    }
+  };
+  issue_block(kbeg, 0);
 
   // A fragments (query rows) and per-row weights, held for the whole chunk.
   uint4 qa[RB][NG];
@@ -62,64 +86,65 @@ __global__ __launch_bounds__(256) void index_scores_prefill_kernel(
       wv[rb][i] = tt < n ? T::ld(wI, tt * HI + rr % HI) : 0.f;
     }
   }
+  wait_vmem();
+  __syncthreads();
 
-  for (int64_t k0 = kbeg; k0 < kend; k0 += 32) {
-    __syncthreads();
-    // stage 32 keys x CI
-    for (int e = tid; e < 32 * (CI * (int)sizeof(S) / 16); e += 256) {
-      const int kr = e / (CI * (int)sizeof(S) / 16), ck = e % (CI * (int)sizeof(S) / 16);
-      const int64_t s = k0 + kr;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (s < kend) v = *(const uint4*)((const uint8_t*)(KI + s * CI) + ck * 16);
-      *(uint4*)(sK + kr * ROWB + ck * 16) = v;
-    }
-    __syncthreads();
-    f32x16_t acc[RB];
+  const int nblk = (int)((kend - kbeg + KB - 1) / KB);
+  for (int bi = 0; bi < nblk; ++bi) {
+    const int buf = bi & 1;
+    const int64_t kb0 = kbeg + (int64_t)bi * KB;
+    if (bi + 1 < nblk) issue_block(kb0 + KB, buf ^ 1);
+    const int nsub = (int)min64(KB / 32, (kend - kb0 + 31) / 32);
+    for (int sb = 0; sb < nsub; ++sb) {
+      const int kk = sb * 32 + (lane & 31);  // this lane's key within the block
+      const uint8_t* krow = &sK[buf][kk * RBYTES];
+      f32x16_t acc[RB];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x16_t{};
+      for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x16_t{};
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      const uint4 kb = *(const uint4*)(sK + (lane & 31) * ROWB + g * 32 + hl * 16);
+      for (int g = 0; g < NG; ++g) {
+        const uint4 kb = *(const uint4*)(krow + 16 * ((2 * g + hl) ^ swz(kk)));
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) mma32<T>(acc[rb], qa[rb][g], kb);
-    }
-    const int64_t s = k0 + (lane & 31);
-    const bool sok = s < kend;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      float part[4];
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        float p = 0.f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) p += wv[rb][gq * 4 + r] * fmaxf(acc[rb][gq * 4 + r], 0.f);
-        part[gq] = p;
+        for (int rb = 0; rb < RB; ++rb) mma32<T>(acc[rb], qa[rb][g], kb);
       }
-      const int64_t tb = q0 + (wave * (RB * 32) + rb * 32) / HI;  // first query of this block
-      if (HI == 4) {  // each group of 4 rows is one whole query
+      const int64_t s = kb0 + kk;
+      const bool sok = s < kend;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        float part[4];
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
-          const int64_t t = tb + 2 * gq + hl;
-          if (sok && t < n && s < (t + 1) / m) scores[t * ld + s] = part[gq];
-        }
-      } else if (HI == 8) {
+          float p = 0.f;
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) part[gq] += __shfl_xor(part[gq], 32, 64);
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int gq = 2 * hl + u;
-          const int64_t t = tb + gq;
-          const float v = gq == 0 ? part[0] : gq == 1 ? part[1] : gq == 2 ? part[2] : part[3];
-          if (sok && t < n && s < (t + 1) / m) scores[t * ld + s] = v;
+          for (int r = 0; r < 4; ++r) p += wv[rb][gq * 4 + r] * fmaxf(acc[rb][gq * 4 + r], 0.f);
+          part[gq] = p;
         }
-      } else {  // HI == 16: rows 0-15 query 0, rows 16-31 query 1
-        float p0 = part[0] + part[1], p1 = part[2] + part[3];
-        p0 += __shfl_xor(p0, 32, 64);
-        p1 += __shfl_xor(p1, 32, 64);
-        const int64_t t = tb + hl;
-        if (sok && t < n && s < (t + 1) / m) scores[t * ld + s] = hl ? p1 : p0;
+        const int64_t tb = q0 + (wave * (RB * 32) + rb * 32) / HI;  // first query of this block
+        if (HI == 4) {  // each group of 4 rows is one whole query
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const int64_t t = tb + 2 * gq + hl;
+            if (sok && t < n && s < (t + 1) / m) scores[t * ld + s] = part[gq];
+          }
+        } else if (HI == 8) {
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) part[gq] = swap32_add(part[gq]);
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int gq = 2 * hl + u;
+            const int64_t t = tb + gq;
+            const float v = gq == 0 ? part[0] : gq == 1 ? part[1] : gq == 2 ? part[2] : part[3];
+            if (sok && t < n && s < (t + 1) / m) scores[t * ld + s] = v;
+          }
+        } else {  // HI == 16: rows 0-15 query 0, rows 16-31 query 1
+          const float p0 = swap32_add(part[0] + part[1]), p1 = swap32_add(part[2] + part[3]);
+          const int64_t t = tb + hl;
+          if (sok && t < n && s < (t + 1) / m) scores[t * ld + s] = hl ? p1 : p0;
+        }
       }
     }
+    wait_vmem();
+    __syncthreads();
   }
 }
 
