@@ -86,6 +86,18 @@ __global__ __launch_bounds__(256) void index_scores_prefill_kernel(
       wv[rb][i] = tt < n ? T::ld(wI, tt * HI + rr % HI) : 0.f;
     }
   }
+  // per stored query: its visible-entry count (0 past the last token), so the
+  // causal test in the loop is one compare
+  int64_t vis[RB][4];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int64_t tb = q0 + (wave * (RB * 32) + rb * 32) / HI;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t t = HI == 4 ? tb + 2 * j + hl : HI == 8 ? tb + 2 * hl + (j & 1) : tb + hl;
+      vis[rb][j] = t < n ? (t + 1) / m : 0;
+    }
+  }
   wait_vmem();
   __syncthreads();
 
@@ -124,7 +136,7 @@ __global__ __launch_bounds__(256) void index_scores_prefill_kernel(
 #pragma unroll
           for (int gq = 0; gq < 4; ++gq) {
             const int64_t t = tb + 2 * gq + hl;
-            if (sok && t < n && s < (t + 1) / m) scores[t * ld + s] = part[gq];
+            if (sok && s < vis[rb][gq]) scores[t * ld + s] = part[gq];
           }
         } else if (HI == 8) {
 #pragma unroll
@@ -134,12 +146,12 @@ __global__ __launch_bounds__(256) void index_scores_prefill_kernel(
             const int gq = 2 * hl + u;
             const int64_t t = tb + gq;
             const float v = gq == 0 ? part[0] : gq == 1 ? part[1] : gq == 2 ? part[2] : part[3];
-            if (sok && t < n && s < (t + 1) / m) scores[t * ld + s] = v;
+            if (sok && s < vis[rb][u]) scores[t * ld + s] = v;
           }
         } else {  // HI == 16: rows 0-15 query 0, rows 16-31 query 1
           const float p0 = swap32_add(part[0] + part[1]), p1 = swap32_add(part[2] + part[3]);
           const int64_t t = tb + hl;
-          if (sok && t < n && s < (t + 1) / m) scores[t * ld + s] = hl ? p1 : p0;
+          if (sok && s < vis[rb][0]) scores[t * ld + s] = hl ? p1 : p0;
         }
       }
     }
