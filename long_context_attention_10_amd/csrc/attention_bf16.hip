@@ -46,23 +46,200 @@ struct Geo {
 
 }  // namespace
 
-// DEC = false: prefill, one workgroup per query token, normalised output.
-// DEC = true: decode split-K, one workgroup per (candidate chunk `spl` wide,
-// sequence); the query of sequence b sits at position posv[b], window rows come
-// from the ring (position p in slot p % n_win) and the workgroup writes its
-// unnormalised partial O with (running max in log2 units, running sum), the
-// sink left to the combine.
-template <int C, bool SPARSE, bool DEC>
-__global__ __launch_bounds__(256, 2) void mqa_bf16_kernel(
+
+// O accumulators are split in two halves of at most 16 blocks: the compiler
+// keeps fully unrolled 16-entry arrays in registers, not 32-entry ones.
+template <int C>
+struct OAcc {
+  static constexpr int NCB = C / 16;  // 16-channel output blocks
+  static constexpr int NLO = NCB > 16 ? 16 : NCB;
+  static constexpr int NHI = NCB > 16 ? NCB - 16 : 1;
+  f32x4_t lo[NLO], hi[NHI];
+};
+
+// Candidate slot permutation.  Lane group lg (lanes 16*lg..16*lg+15) holds,
+// after the logits, the 8 tile rows pi(lg, h, i) = 16*(lg/2) + 8*h + 4*(lg%2) + i
+// (h = 0, 1; i = 0..3); those rows are also its PV reduction slots 8*lg+4*h+i.
+// With 1056-byte LDS rows (8 banks apart) both the 16-byte K reads (rows
+// pi(lc/4, b, lc%4) for lanes lc) and the transpose reads (4 consecutive
+// rows per 16-lane group) touch distinct banks.
+CSA_DEV int slot_pi(int g, int h, int i) { return 16 * (g >> 1) + 8 * h + 4 * (g & 1) + i; }
+
+// One 32-candidate tile for this wave's 16 heads: S^T = K Q^T, the online
+// softmax update (log2 units), O^T += V^T P^T.
+template <int C>
+CSA_DEV void mqa_tile(const uint8_t* kv, const int* vflags, const bf16x8_t* qf, OAcc<C>& o,
+                      float& run_m, float& run_l, float sl2, int koff0, int koff1, int troff0,
+                      int troff1, int lg) {
+  constexpr int NKG = C / 32;
+  typedef OAcc<C> A;
+  // S^T for the tile: block b's A rows are K rows pi(lc/4, b, lc%4).  The
+  // fragments of k-group g+1 are read while g's products issue, so the LDS
+  // latency overlaps the matrix cores.
+  f32x4_t s[2] = {f32x4_t{}, f32x4_t{}};
+  bf16x8_t a0[2], a1[2];
+  a0[0] = *(const bf16x8_t*)(kv + koff0);
+  a1[0] = *(const bf16x8_t*)(kv + koff1);
+#pragma unroll
+  for (int g = 0; g < NKG; ++g) {
+    if (g + 1 < NKG) {
+      a0[(g + 1) & 1] = *(const bf16x8_t*)(kv + koff0 + (g + 1) * 64);
+      a1[(g + 1) & 1] = *(const bf16x8_t*)(kv + koff1 + (g + 1) * 64);
+    }
+    s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[g & 1], qf[g], s[0], 0, 0, 0);
+    s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[g & 1], qf[g], s[1], 0, 0, 0);
+  }
+  // online softmax for head `head` (this lane's column) in log2 units
+  float z[8];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int4 vf = *(const int4*)&vflags[slot_pi(lg, b, 0)];  // rows pi(lg, b, 0..3)
+    const int vfl[4] = {vf.x, vf.y, vf.z, vf.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float zz = vfl[i] ? s[b][i] * sl2 : -INFINITY;
+      z[4 * b + i] = zz;
+      mx = fmaxf(mx, zz);
+    }
+  }
+  mx = xlane_max(mx);
+  if (__any(mx > run_m + 8.f)) {  // wave-uniform rescale of O
+    const float nm = fmaxf(run_m, mx);
+    const float alpha = __builtin_amdgcn_exp2f(run_m - nm);
+    run_l *= alpha;
+    run_m = nm;
+#pragma unroll
+    for (int cb = 0; cb < A::NLO; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o.lo[cb][i] *= alpha;
+    if constexpr (A::NCB > 16) {
+#pragma unroll
+      for (int cb = 0; cb < A::NHI; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o.hi[cb][i] *= alpha;
+    }
+  }
+  f32x8_t p;
+  float ps = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    p[j] = __builtin_amdgcn_exp2f(z[j] - run_m);
+    ps += p[j];
+  }
+  run_l += xlane_sum(ps);
+  const bf16x8_t pb = __builtin_convertvector(p, bf16x8_t);  // B operand, slots 8*lg+j
+
+  // O^T += V^T P^T over the 16-channel blocks; V^T fragments by transpose read:
+  // lane (lg, lc) reads row pi(lg, h, lc/4), channels cb*16 + 4*(lc%4) .. +3,
+  // and receives V[pi(lg, h, j)][cb*16 + lc] for j = 0..3.
+  auto pv = [&](int cb, f32x4_t& acc) {
+    const bf16x4_t x0 =
+        __builtin_amdgcn_ds_read_tr16_b64_v4bf16((CSA_LDS bf16x4_t*)(kv + troff0 + cb * 32));
+    const bf16x4_t x1 =
+        __builtin_amdgcn_ds_read_tr16_b64_v4bf16((CSA_LDS bf16x4_t*)(kv + troff1 + cb * 32));
+    const bf16x8_t a = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, acc, 0, 0, 0);
+  };
+#pragma unroll
+  for (int cb = 0; cb < A::NLO; ++cb) pv(cb, o.lo[cb]);
+  if constexpr (A::NCB > 16) {
+#pragma unroll
+    for (int cb = 0; cb < A::NHI; ++cb) pv(A::NLO + cb, o.hi[cb]);
+  }
+}
+
+// q prologue: per-head RMSNorm over the row held by the 4 lane groups, RoPE
+// of the last r channels from the token's angle table, bf16 MFMA operands.
+template <int C>
+CSA_DEV void q_prologue(const uint4* qraw, bf16x8_t* qf, const float2* rtab, int qk_norm, float eps,
+                        int r, int lg) {
+  constexpr int NKG = C / 32;
+  float ss = 0.f;
+#pragma unroll
+  for (int g = 0; g < NKG; ++g) {
+    float v[8];
+    chunk_to_f32<BF16>(qraw[g], v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+  }
+  ss = xlane_sum(ss);
+  const float inv = qk_norm ? rsqrtf(ss / (float)C + eps) : 1.f;
+#pragma unroll
+  for (int g = 0; g < NKG; ++g) {
+    float v[8];
+    chunk_to_f32<BF16>(qraw[g], v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] *= inv;
+    if (r > 0) {
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const int ch = g * 32 + lg * 8 + e;
+        if (ch >= C - r) {
+          const float2 cs = rtab[(ch - (C - r)) >> 1];
+          const float x0 = v[e], x1 = v[e + 1];
+          v[e] = x0 * cs.x - x1 * cs.y;
+          v[e + 1] = x0 * cs.y + x1 * cs.x;
+        }
+      }
+    }
+    qf[g] = __builtin_bit_cast(bf16x8_t, f32_to_chunk<BF16>(v));
+  }
+}
+
+// Lane L < 8 of wave w resolves tile row (w + 4*(L / RPI)) * RPI + L % RPI
+// (address and validity flag); each 1 KiB burst's DMA then takes its row
+// address from that lane (readlane), so the gather costs one LDS index read
+// and a few scalar moves per row.  `row_of(j)` gives (row pointer, valid) for
+// candidate j of the tile's range.
+template <int C, class RowOf>
+CSA_DEV void issue_tile_rows(uint8_t* base, int* vflags, int lane, int wave, int64_t j0,
+                             RowOf row_of) {
+  typedef Geo<C> G;
+  constexpr int BPW = kT / G::RPI / 4;  // bursts (1 KiB each) per wave
+  constexpr int LPR = 64 / G::RPI;      // lanes per row within a burst
+  const uint16_t* rp = nullptr;
+  if (lane < BPW * G::RPI) {
+    const int row = (wave + 4 * (lane / G::RPI)) * G::RPI + lane % G::RPI;
+    bool ok;
+    rp = row_of(j0 + row, ok);
+    vflags[row] = ok;
+  }
+  const uint32_t ra_lo = (uint32_t)(size_t)rp, ra_hi = (uint32_t)((size_t)rp >> 32);
+#pragma unroll
+  for (int u = 0; u < BPW; ++u) {
+    uint32_t lo, hi;
+    if constexpr (G::RPI == 1) {
+      lo = __builtin_amdgcn_readlane(ra_lo, u);
+      hi = __builtin_amdgcn_readlane(ra_hi, u);
+    } else {
+      const int src = u * G::RPI + lane / LPR;
+      lo = __shfl((int)ra_lo, src, 64);
+      hi = __shfl((int)ra_hi, src, 64);
+    }
+    const uint8_t* g = (const uint8_t*)(size_t)(((uint64_t)hi << 32) | lo) + (lane % LPR) * 16;
+    lds_dma16(g, base + (wave + 4 * u) * G::BURST);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Prefill: one workgroup per query token.  XCD-aware order: the 8 dies each
+// take a contiguous range of tokens, so a die's L2 keeps the window rows its
+// consecutive tokens share.  The first tile holds only window rows whenever
+// the window covers it; its gather then starts before the index row is in.
+// The running max starts at the sink logit and the running sum at 1, which
+// adds exp(sink) to the denominator exactly once.  The output goes through
+// LDS so that HBM sees whole-row stores.
+// ---------------------------------------------------------------------------
+template <int C, bool SPARSE>
+__global__ __launch_bounds__(256, 2) void mqa_prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ win,
     const uint16_t* __restrict__ comp, const int32_t* __restrict__ idx,
     const float* __restrict__ sink, uint16_t* __restrict__ out, int64_t n, int nh, int k, int m,
-    int n_win, float scale, int qk_norm, float eps, int r, float theta, int64_t n_entries,
-    const int64_t* __restrict__ posv, float* __restrict__ ws_o, float2* __restrict__ ws_ml,
-    int nsplit, int spl) {
+    int n_win, float scale, int qk_norm, float eps, int r, float theta, int64_t n_entries) {
   typedef Geo<C> G;
-  constexpr int NKG = C / 32;   // 32-wide k-groups of the head dim
-  constexpr int NCB = C / 16;   // 16-channel output blocks
+  typedef OAcc<C> A;
+  constexpr int NKG = C / 32;
   __shared__ __align__(16) uint8_t smem[G::BUF];
   __shared__ __align__(16) int valid[2][kT];
   __shared__ int sidx[SPARSE ? kMaxK : 1];
@@ -71,291 +248,75 @@ __global__ __launch_bounds__(256, 2) void mqa_bf16_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int lc = lane & 15, lg = lane >> 4;
-
-  int64_t t, qr;  // query position, query row
-  int split = 0;
-  if constexpr (DEC) {
-    qr = blockIdx.y;
-    split = blockIdx.x;
-  } else {
-    // XCD-aware order: the 8 dies each take a contiguous range of tokens, so a
-    // die's L2 keeps the window rows its consecutive tokens share.
-    const int64_t per = (n + 7) >> 3;
-    qr = (int64_t)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
-    if (qr >= n) return;
-  }
-
-  // lane (lg, lc) holds Q[head][32g + 8lg .. +8] for g = 0..C/32-1: the B
-  // operand of S^T = K Q^T.  Loaded straight from global memory, first, so
-  // that the first candidate tile can stream into LDS at the same time.
   const int head = wave * 16 + lc;
+  const int64_t per = (n + 7) >> 3;
+  const int64_t t = (int64_t)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (t >= n) return;
+
+  // q rows first, so that the first tile's gather overlaps their load
   uint4 qraw[NKG];
   {
-    const uint16_t* qh = q + (qr * nh + (head < nh ? head : 0)) * C + lg * 8;
+    const uint16_t* qh = q + (t * nh + (head < nh ? head : 0)) * C + lg * 8;
 #pragma unroll
     for (int g = 0; g < NKG; ++g) qraw[g] = *(const uint4*)(qh + g * 32);
   }
-
-  t = DEC ? posv[qr] : qr;
-  const int nwin = DEC ? (int)max64(0, min64(n_win, t + 1)) : (int)min64(n_win, t + 1);
-  const int64_t ncomp = SPARSE ? (int64_t)k
-                               : (DEC ? max64(0, min64((t + 1) / m, n_entries))
-                                      : min64((t + 1) / m, n_entries));
-  const int64_t ncand = nwin + ncomp;
-  int64_t cbeg = 0, cend = ncand;
-  if constexpr (DEC) {
-    cbeg = (int64_t)split * spl;
-    cend = min64(cbeg + spl, ncand);
-    if (cbeg >= cend) return;  // nothing in this chunk; the combine skips it
-  }
-  const int ntiles = (int)((cend - cbeg + kT - 1) / kT);
-  const int32_t* irow = SPARSE ? idx + qr * (int64_t)k : nullptr;
-  const uint16_t* wbase = DEC ? win + qr * (int64_t)n_win * C : win;
-  const uint16_t* cbase = DEC ? comp + qr * n_entries * C : comp;
-  const int64_t s0 = DEC ? max64(cbeg - nwin, 0) : 0;  // first index slot staged
-  // decode: ring slot of the oldest window position (candidate j at w0 + j mod n_win)
-  const int w0 = (DEC && nwin > 0) ? (int)((t - nwin + 1) % n_win) : 0;
-
-  // ------------------------------------------------ candidate tile loader
-  // Wave w fills bursts w, w+4, ... of the tile.  Lane L < 8 resolves the
-  // wave's L-th row (address and validity flag); each burst's DMA takes its
-  // row address from that lane.
+  const int nwin = (int)min64(n_win, t + 1);
+  const int64_t ncand = nwin + (SPARSE ? (int64_t)k : min64((t + 1) / m, n_entries));
+  const int ntiles = (int)((ncand + kT - 1) / kT);
   auto issue_tile = [&](int ti, int buf) {
-    uint8_t* base = smem + buf * G::TILE;
-    constexpr int BPW = kT / G::RPI / 4;  // bursts (1 KiB each) per wave
-    constexpr int LPR = 64 / G::RPI;      // lanes per row within a burst
-    const uint16_t* rp = wbase;           // a valid row for masked candidates
-    if (lane < BPW * G::RPI) {
-      const int row = (wave + 4 * (lane / G::RPI)) * G::RPI + lane % G::RPI;
-      const int64_t j = cbeg + (int64_t)ti * kT + row;
-      bool ok = false;
-      if (j < cend) {
-        if (j < nwin) {
-          if constexpr (DEC) {
-            int slot = w0 + (int)j;
-            if (slot >= n_win) slot -= n_win;
-            rp = wbase + (int64_t)slot * C;
-          } else {
-            rp = wbase + (t - nwin + 1 + j) * C;
-          }
-          ok = true;
-        } else {
-          const int64_t e = SPARSE ? (int64_t)sidx[j - nwin - s0] : j - nwin;
-          if (e >= 0 && e < n_entries) { rp = cbase + e * C; ok = true; }
-        }
-      }
-      valid[buf][row] = ok;
-    }
-    const uint32_t ra_lo = (uint32_t)(size_t)rp, ra_hi = (uint32_t)((size_t)rp >> 32);
-#pragma unroll
-    for (int u = 0; u < BPW; ++u) {
-      uint32_t lo, hi;
-      if constexpr (G::RPI == 1) {
-        lo = __builtin_amdgcn_readlane(ra_lo, u);
-        hi = __builtin_amdgcn_readlane(ra_hi, u);
-      } else {
-        const int src = u * G::RPI + lane / LPR;
-        lo = __shfl((int)ra_lo, src, 64);
-        hi = __shfl((int)ra_hi, src, 64);
-      }
-      const uint8_t* g = (const uint8_t*)(size_t)(((uint64_t)hi << 32) | lo) + (lane % LPR) * 16;
-      lds_dma16(g, base + (wave + 4 * u) * G::BURST);
-    }
+    issue_tile_rows<C>(smem + buf * G::TILE, valid[buf], lane, wave, (int64_t)ti * kT,
+                       [&](int64_t j, bool& ok) -> const uint16_t* {
+                         ok = false;
+                         if (j >= ncand) return win;  // a valid row for masked candidates
+                         if (j < nwin) { ok = true; return win + (t - nwin + 1 + j) * C; }
+                         const int64_t e = SPARSE ? (int64_t)sidx[j - nwin] : j - nwin;
+                         if (e < 0 || e >= n_entries) return win;
+                         ok = true;
+                         return comp + e * C;
+                       });
   };
-
-  // The first tile holds only window rows whenever the window covers it; its
-  // gather then need not wait for the index row.
-  const bool early0 = ntiles > 0 && cbeg + kT <= nwin;
+  const bool early0 = nwin >= kT;  // tile 0 is window rows only
   if (early0) issue_tile(0, 0);
-
-  // ------------------------------- index row slice and RoPE angles -> LDS
-  if (SPARSE) {
-    if constexpr (DEC) {
-      for (int64_t j = s0 + tid; j < cend - nwin; j += 256) sidx[j - s0] = irow[j];
-    } else {
-      for (int j = tid; j < k; j += 256) sidx[j] = irow[j];
-    }
-  }
-  if (tid < r / 2) {  // one angle per RoPE pair, shared by prologue and epilogue
+  if (SPARSE)
+    for (int j = tid; j < k; j += 256) sidx[j] = idx[t * k + j];
+  for (int p = tid; p < r / 2; p += 256) {
     float cs, sn;
-    rope_cs(t, tid, r, theta, &cs, &sn);
-    rope_tab[tid] = make_float2(cs, sn);
+    rope_cs(t, p, r, theta, &cs, &sn);
+    rope_tab[p] = make_float2(cs, sn);
   }
   __syncthreads();  // sidx and rope_tab are visible
-  if (ntiles > 0 && !early0) issue_tile(0, 0);
+  if (!early0) issue_tile(0, 0);
 
-
-  // --------------------------------- q prologue: RMSNorm, RoPE, bf16 regs
   bf16x8_t qf[NKG];
-  {
-    float ss = 0.f;
-#pragma unroll
-    for (int g = 0; g < NKG; ++g) {
-      float v[8];
-      chunk_to_f32<BF16>(qraw[g], v);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
-    }
-    ss += __shfl_xor(ss, 16, 64);
-    ss += __shfl_xor(ss, 32, 64);
-    const float inv = qk_norm ? rsqrtf(ss / (float)C + eps) : 1.f;
-#pragma unroll
-    for (int g = 0; g < NKG; ++g) {
-      float v[8];
-      chunk_to_f32<BF16>(qraw[g], v);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] *= inv;
-      if (r > 0) {
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const int ch = g * 32 + lg * 8 + e;
-          if (ch >= C - r) {
-            const float2 cs = rope_tab[(ch - (C - r)) >> 1];
-            const float x0 = v[e], x1 = v[e + 1];
-            v[e] = x0 * cs.x - x1 * cs.y;
-            v[e + 1] = x0 * cs.y + x1 * cs.x;
-          }
-        }
-      }
-      qf[g] = __builtin_bit_cast(bf16x8_t, f32_to_chunk<BF16>(v));
-    }
-  }
-
-  // ----------------------------------------------------- softmax state
+  q_prologue<C>(qraw, qf, rope_tab, qk_norm, eps, r, lg);
   constexpr float LOG2E = 1.4426950408889634f;
-  const float sl2 = scale * LOG2E;
-  float run_m = (head < nh ? sink[head] : 0.f) * LOG2E;  // log2 units
-  float run_l = DEC ? 0.f : 1.f;  // decode partials leave the sink to the combine
-
-  // O accumulators in two halves of at most 16 blocks: the compiler keeps
-  // fully unrolled 16-entry arrays in registers, not 32-entry ones.
-  constexpr int NLO = NCB > 16 ? 16 : NCB;
-  constexpr int NHI = NCB > 16 ? NCB - 16 : 1;
-  f32x4_t o_lo[NLO], o_hi[NHI];
+  float run_m = (head < nh ? sink[head] : 0.f) * LOG2E, run_l = 1.f;
+  A o;
 #pragma unroll
-  for (int cb = 0; cb < NLO; ++cb) o_lo[cb] = f32x4_t{};
+  for (int cb = 0; cb < A::NLO; ++cb) o.lo[cb] = f32x4_t{};
 #pragma unroll
-  for (int cb = 0; cb < NHI; ++cb) o_hi[cb] = f32x4_t{};
-
+  for (int cb = 0; cb < A::NHI; ++cb) o.hi[cb] = f32x4_t{};
+  const int koff0 = G::off(slot_pi(lc >> 2, 0, lc & 3)) + lg * 16;
+  const int koff1 = G::off(slot_pi(lc >> 2, 1, lc & 3)) + lg * 16;
+  const int troff0 = G::off(slot_pi(lg, 0, lc >> 2)) + 8 * (lc & 3);
+  const int troff1 = G::off(slot_pi(lg, 1, lc >> 2)) + 8 * (lc & 3);
   wait_vmem();  // tile 0 (and q) have landed
   __syncthreads();
-
-  // Candidate slot permutation.  Lane group lg (lanes 16*lg..16*lg+15) holds,
-  // after the logits, the 8 tile rows pi(lg, h, i) = 16*(lg/2) + 8*h + 4*(lg%2) + i
-  // (h = 0, 1; i = 0..3); those rows are also its PV reduction slots 8*lg+4*h+i.
-  // With 1056-byte LDS rows (8 banks apart) both the 16-byte K reads (rows
-  // pi(lc/4, b, lc%4) for lanes lc) and the transpose reads (4 consecutive
-  // rows per 16-lane group) touch distinct banks.
-  auto pi = [](int g, int h, int i) { return 16 * (g >> 1) + 8 * h + 4 * (g & 1) + i; };
-  const int koff0 = G::off(pi(lc >> 2, 0, lc & 3)) + lg * 16;
-  const int koff1 = G::off(pi(lc >> 2, 1, lc & 3)) + lg * 16;
-  const int troff0 = G::off(pi(lg, 0, lc >> 2)) + 8 * (lc & 3);
-  const int troff1 = G::off(pi(lg, 1, lc >> 2)) + 8 * (lc & 3);
-
   for (int ti = 0; ti < ntiles; ++ti) {
     const int buf = ti & 1;
     if (ti + 1 < ntiles) issue_tile(ti + 1, buf ^ 1);
-    const uint8_t* kv = smem + buf * G::TILE;
-
-    // S^T = K Q^T for the tile: block b's A rows are K rows pi(lc/4, b, lc%4)
-    // (fragments of k-group g+1 are read while g's products issue, so the LDS
-    // latency overlaps the matrix cores)
-    f32x4_t s[2] = {f32x4_t{}, f32x4_t{}};
-    bf16x8_t a0[2], a1[2];
-    a0[0] = *(const bf16x8_t*)(kv + koff0);
-    a1[0] = *(const bf16x8_t*)(kv + koff1);
-#pragma unroll
-    for (int g = 0; g < NKG; ++g) {
-      if (g + 1 < NKG) {
-        a0[(g + 1) & 1] = *(const bf16x8_t*)(kv + koff0 + (g + 1) * 64);
-        a1[(g + 1) & 1] = *(const bf16x8_t*)(kv + koff1 + (g + 1) * 64);
-      }
-      s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[g & 1], qf[g], s[0], 0, 0, 0);
-      s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[g & 1], qf[g], s[1], 0, 0, 0);
-    }
-    // online softmax for head `head` (this lane's column) in log2 units
-    float z[8];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int4 vf = *(const int4*)&valid[buf][pi(lg, b, 0)];  // rows pi(lg, b, 0..3)
-      const int vfl[4] = {vf.x, vf.y, vf.z, vf.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float zz = vfl[i] ? s[b][i] * sl2 : -INFINITY;
-        z[4 * b + i] = zz;
-        mx = fmaxf(mx, zz);
-      }
-    }
-    mx = xlane_max(mx);
-    const bool need = mx > run_m + 8.f;
-    if (__any(need)) {  // wave-uniform rescale of O
-      const float nm = fmaxf(run_m, mx);
-      const float alpha = __builtin_amdgcn_exp2f(run_m - nm);
-      run_l *= alpha;
-      run_m = nm;
-#pragma unroll
-      for (int cb = 0; cb < NLO; ++cb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o_lo[cb][i] *= alpha;
-      if constexpr (NCB > 16) {
-#pragma unroll
-        for (int cb = 0; cb < NHI; ++cb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) o_hi[cb][i] *= alpha;
-      }
-    }
-    f32x8_t p;
-    float ps = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      p[j] = __builtin_amdgcn_exp2f(z[j] - run_m);
-      ps += p[j];
-    }
-    ps = xlane_sum(ps);
-    run_l += ps;
-    const bf16x8_t pb = __builtin_convertvector(p, bf16x8_t);  // B operand, slots 8*lg+j
-
-    // O^T += V^T P^T over the 16-channel blocks; V^T fragments by transpose read:
-    // lane (lg, lc) reads row pi(lg, h, lc/4), channels cb*16 + 4*(lc%4) .. +3,
-    // and receives V[pi(lg, h, j)][cb*16 + lc] for j = 0..3.
-    auto pv = [&](int cb, f32x4_t& acc) {
-      const bf16x4_t x0 =
-          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((CSA_LDS bf16x4_t*)(kv + troff0 + cb * 32));
-      const bf16x4_t x1 =
-          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((CSA_LDS bf16x4_t*)(kv + troff1 + cb * 32));
-      const bf16x8_t a = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, acc, 0, 0, 0);
-    };
-#pragma unroll
-    for (int cb = 0; cb < NLO; ++cb) pv(cb, o_lo[cb]);
-    if constexpr (NCB > 16) {
-#pragma unroll
-      for (int cb = 0; cb < NHI; ++cb) pv(NLO + cb, o_hi[cb]);
-    }
+    mqa_tile<C>(smem + buf * G::TILE, valid[buf], qf, o, run_m, run_l, scale * LOG2E, koff0,
+                koff1, troff0, troff1, lg);
     wait_vmem();
     __syncthreads();
   }
 
-  // ------------------------------------------------------------ epilogue
-  // O^T lane layout: block cb, element i = O[head][cb*16 + 4*lg + i]
-  if constexpr (DEC) {
-    if (head < nh) {
-      const int64_t row = (qr * nsplit + split) * nh + head;
-      float* po = ws_o + row * C + 4 * lg;
-#pragma unroll
-      for (int cb = 0; cb < NLO; ++cb) *(f32x4_t*)(po + cb * 16) = o_lo[cb];
-      if constexpr (NCB > 16) {
-#pragma unroll
-        for (int cb = 0; cb < NHI; ++cb) *(f32x4_t*)(po + (NLO + cb) * 16) = o_hi[cb];
-      }
-      if (lg == 0) ws_ml[row] = make_float2(run_m, run_l);
-    }
-    return;
-  }
+  // epilogue: O^T lane layout: block cb, element i = O[head][cb*16 + 4*lg + i]
   const float inv = 1.f / run_l;
-  uint8_t* ostage = smem;  // [head][C] bf16, padded like q
-  auto emit = [&](int cb, const f32x4_t& acc) {
+  uint8_t* ostage = smem;  // [head][C] bf16, padded like the tiles
+#pragma unroll
+  for (int cb = 0; cb < A::NCB; ++cb) {
+    const f32x4_t acc = cb < A::NLO ? o.lo[cb] : o.hi[cb - A::NLO];
     float v[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = acc[i] * inv;
@@ -365,22 +326,16 @@ __global__ __launch_bounds__(256, 2) void mqa_bf16_kernel(
       for (int i = 0; i < 4; i += 2) {
         const float2 cs = rope_tab[(ch0 + i - (C - r)) >> 1];
         const float x0 = v[i], x1 = v[i + 1];
-        v[i] = x0 * cs.x + x1 * cs.y;      // rotate by -t
+        v[i] = x0 * cs.x + x1 * cs.y;  // rotate by -t
         v[i + 1] = -x0 * cs.y + x1 * cs.x;
       }
     }
     const uint32_t w0 = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
     const uint32_t w1 = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
     *(uint2*)(ostage + G::off(head) + ch0 * 2) = make_uint2(w0, w1);
-  };
-#pragma unroll
-  for (int cb = 0; cb < NLO; ++cb) emit(cb, o_lo[cb]);
-  if constexpr (NCB > 16) {
-#pragma unroll
-    for (int cb = 0; cb < NHI; ++cb) emit(NLO + cb, o_hi[cb]);
   }
   __syncthreads();
-  uint16_t* orow = out + qr * (int64_t)nh * C;
+  uint16_t* orow = out + t * (int64_t)nh * C;
   const int chunks = nh * C / 8;  // 16-byte chunks of this token's output
   for (int ci = tid; ci < chunks; ci += 256) {
     const int h = ci / (C / 8), cc = ci % (C / 8);
@@ -395,20 +350,137 @@ hipError_t launch_mqa_prefill_bf16(const csa_attn_desc& d, int mode, const void*
 #define CSA_FAST(CC)                                                                          \
   if (d.c == CC) {                                                                           \
     if (mode == ATTN_SPARSE)                                                                 \
-      mqa_bf16_kernel<CC, true, false><<<grid, 256, 0, st>>>(                               \
+      mqa_prefill_bf16_kernel<CC, true><<<grid, 256, 0, st>>>(                              \
           (const uint16_t*)q, (const uint16_t*)win, (const uint16_t*)comp, idx, sink,         \
           (uint16_t*)out, d.n, d.n_heads, d.k, d.m, d.n_win, d.scale, d.qk_norm, d.eps,       \
-          d.rope_dims, d.rope_theta, d.n_entries, nullptr, nullptr, nullptr, 0, 0);           \
+          d.rope_dims, d.rope_theta, d.n_entries);                                            \
     else                                                                                     \
-      mqa_bf16_kernel<CC, false, false><<<grid, 256, 0, st>>>(                              \
+      mqa_prefill_bf16_kernel<CC, false><<<grid, 256, 0, st>>>(                             \
           (const uint16_t*)q, (const uint16_t*)win, (const uint16_t*)comp, idx, sink,         \
           (uint16_t*)out, d.n, d.n_heads, d.k, d.m, d.n_win, d.scale, d.qk_norm, d.eps,       \
-          d.rope_dims, d.rope_theta, d.n_entries, nullptr, nullptr, nullptr, 0, 0);           \
+          d.rope_dims, d.rope_theta, d.n_entries);                                            \
     return hipGetLastError();                                                                \
   }
   CSA_FAST(128) CSA_FAST(256) CSA_FAST(512)
 #undef CSA_FAST
   return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// Decode split-K: one workgroup per (candidate chunk `spl` wide, sequence);
+// the query of sequence b sits at position posv[b], window rows come from the
+// ring (position p in slot p % n_win), and the workgroup writes its
+// unnormalised partial O with (running max in log2 units, running sum), the
+// sink left to the combine.
+// ---------------------------------------------------------------------------
+template <int C, bool SPARSE>
+__global__ __launch_bounds__(256, 2) void mqa_decode_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ ring,
+    const uint16_t* __restrict__ cache, const int32_t* __restrict__ idx,
+    const float* __restrict__ sink, int nh, int k, int m, int n_win, float scale, int qk_norm,
+    float eps, int r, float theta, int64_t n_entries, const int64_t* __restrict__ posv,
+    float* __restrict__ ws_o, float2* __restrict__ ws_ml, int nsplit, int spl) {
+  typedef Geo<C> G;
+  typedef OAcc<C> A;
+  constexpr int NKG = C / 32;
+  __shared__ __align__(16) uint8_t smem[2 * G::TILE];
+  __shared__ __align__(16) int valid[2][kT];
+  __shared__ int sidx[SPARSE ? kMaxK : 1];
+  __shared__ float2 rope_tab[C / 2];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lc = lane & 15, lg = lane >> 4;
+  const int head = wave * 16 + lc;
+  const int64_t b = blockIdx.y;
+  const int split = blockIdx.x;
+
+  // q first: its address does not depend on the position
+  uint4 qraw[NKG];
+  {
+    const uint16_t* qh = q + (b * nh + (head < nh ? head : 0)) * C + lg * 8;
+#pragma unroll
+    for (int g = 0; g < NKG; ++g) qraw[g] = *(const uint4*)(qh + g * 32);
+  }
+  const int64_t t = posv[b];
+  const int nwin = (int)max64(0, min64(n_win, t + 1));
+  const int64_t ncomp = SPARSE ? (int64_t)k : max64(0, min64((t + 1) / m, n_entries));
+  const int64_t ncand = nwin + ncomp;
+  const int64_t cbeg = (int64_t)split * spl;
+  const int64_t cend = min64(cbeg + spl, ncand);
+  if (cbeg >= cend) return;  // nothing in this chunk; the combine skips it
+  const int ntiles = (int)((cend - cbeg + kT - 1) / kT);
+  const uint16_t* wbase = ring + b * (int64_t)n_win * C;
+  const uint16_t* cbase = cache + b * n_entries * C;
+  const int64_t s0 = max64(cbeg - nwin, 0);  // first index slot staged
+  // ring slot of the oldest window position (candidate j at w0 + j mod n_win)
+  const int w0 = nwin > 0 ? (int)((t - nwin + 1) % n_win) : 0;
+
+  auto issue_tile = [&](int ti, int buf) {
+    issue_tile_rows<C>(smem + buf * G::TILE, valid[buf], lane, wave, cbeg + (int64_t)ti * kT,
+                       [&](int64_t j, bool& ok) -> const uint16_t* {
+                         ok = false;
+                         if (j >= cend) return wbase;  // a valid row for masked candidates
+                         if (j < nwin) {
+                           int slot = w0 + (int)j;
+                           if (slot >= n_win) slot -= n_win;
+                           ok = true;
+                           return wbase + (int64_t)slot * C;
+                         }
+                         const int64_t e = SPARSE ? (int64_t)sidx[j - nwin - s0] : j - nwin;
+                         if (e < 0 || e >= n_entries) return wbase;
+                         ok = true;
+                         return cbase + e * C;
+                       });
+  };
+  const bool early0 = cbeg + kT <= nwin;  // tile 0 is window rows only
+  if (early0) issue_tile(0, 0);
+  if (SPARSE)
+    for (int64_t j = s0 + tid; j < cend - nwin; j += 256) sidx[j - s0] = idx[b * k + j];
+  for (int p = tid; p < r / 2; p += 256) {
+    float cs, sn;
+    rope_cs(t, p, r, theta, &cs, &sn);
+    rope_tab[p] = make_float2(cs, sn);
+  }
+  __syncthreads();
+  if (!early0) issue_tile(0, 0);
+
+  bf16x8_t qf[NKG];
+  q_prologue<C>(qraw, qf, rope_tab, qk_norm, eps, r, lg);
+  constexpr float LOG2E = 1.4426950408889634f;
+  float run_m = (head < nh ? sink[head] : 0.f) * LOG2E;  // a finite start, log2 units
+  float run_l = 0.f;                                     // the sink is the combine's
+  A o;
+#pragma unroll
+  for (int cb = 0; cb < A::NLO; ++cb) o.lo[cb] = f32x4_t{};
+#pragma unroll
+  for (int cb = 0; cb < A::NHI; ++cb) o.hi[cb] = f32x4_t{};
+  const int koff0 = G::off(slot_pi(lc >> 2, 0, lc & 3)) + lg * 16;
+  const int koff1 = G::off(slot_pi(lc >> 2, 1, lc & 3)) + lg * 16;
+  const int troff0 = G::off(slot_pi(lg, 0, lc >> 2)) + 8 * (lc & 3);
+  const int troff1 = G::off(slot_pi(lg, 1, lc >> 2)) + 8 * (lc & 3);
+  wait_vmem();
+  __syncthreads();
+  for (int ti = 0; ti < ntiles; ++ti) {
+    const int buf = ti & 1;
+    if (ti + 1 < ntiles) issue_tile(ti + 1, buf ^ 1);
+    mqa_tile<C>(smem + buf * G::TILE, valid[buf], qf, o, run_m, run_l, scale * LOG2E, koff0,
+                koff1, troff0, troff1, lg);
+    wait_vmem();
+    __syncthreads();
+  }
+  // partial O^T: block cb, element i = O[head][cb*16 + 4*lg + i]
+  if (head < nh) {
+    const int64_t row = (b * nsplit + split) * nh + head;
+    float* po = ws_o + row * C + 4 * lg;
+#pragma unroll
+    for (int cb = 0; cb < A::NLO; ++cb) *(f32x4_t*)(po + cb * 16) = o.lo[cb];
+    if constexpr (A::NCB > 16) {
+#pragma unroll
+      for (int cb = 0; cb < A::NHI; ++cb) *(f32x4_t*)(po + (A::NLO + cb) * 16) = o.hi[cb];
+    }
+    if (lg == 0) ws_ml[row] = make_float2(run_m, run_l);
+  }
 }
 
 // Fixed-order merge of the chunk partials of one sequence with the sink, then
@@ -508,15 +580,15 @@ hipError_t launch_mqa_decode_bf16(const csa_attn_desc& d, int mode, const void* 
 #define CSA_DEC(CC)                                                                            \
   if (d.c == CC) {                                                                            \
     if (mode == ATTN_SPARSE)                                                                  \
-      mqa_bf16_kernel<CC, true, true><<<grid, 256, 0, st>>>(                                  \
-          (const uint16_t*)q, (const uint16_t*)ring, (const uint16_t*)cache, idx, sink, nullptr, \
-          d.batch, d.n_heads, d.k, d.m, d.n_win, d.scale, d.qk_norm, d.eps, d.rope_dims,         \
-          d.rope_theta, d.n_entries, pos, ws_o, ws_ml, nsplit, spl);                           \
+      mqa_decode_bf16_kernel<CC, true><<<grid, 256, 0, st>>>(                                 \
+          (const uint16_t*)q, (const uint16_t*)ring, (const uint16_t*)cache, idx, sink,          \
+          d.n_heads, d.k, d.m, d.n_win, d.scale, d.qk_norm, d.eps, d.rope_dims, d.rope_theta,    \
+          d.n_entries, pos, ws_o, ws_ml, nsplit, spl);                                         \
     else                                                                                      \
-      mqa_bf16_kernel<CC, false, true><<<grid, 256, 0, st>>>(                                 \
-          (const uint16_t*)q, (const uint16_t*)ring, (const uint16_t*)cache, idx, sink, nullptr, \
-          d.batch, d.n_heads, d.k, d.m, d.n_win, d.scale, d.qk_norm, d.eps, d.rope_dims,         \
-          d.rope_theta, d.n_entries, pos, ws_o, ws_ml, nsplit, spl);                           \
+      mqa_decode_bf16_kernel<CC, false><<<grid, 256, 0, st>>>(                                \
+          (const uint16_t*)q, (const uint16_t*)ring, (const uint16_t*)cache, idx, sink,          \
+          d.n_heads, d.k, d.m, d.n_win, d.scale, d.qk_norm, d.eps, d.rope_dims, d.rope_theta,    \
+          d.n_entries, pos, ws_o, ws_ml, nsplit, spl);                                         \
     hipError_t e = hipGetLastError();                                                         \
     if (e != hipSuccess) return e;                                                            \
     mqa_decode_combine_kernel<CC><<<cgrid, 256, 0, st>>>(                                     \
