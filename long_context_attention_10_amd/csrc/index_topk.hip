@@ -520,32 +520,44 @@ __global__ __launch_bounds__(256) void dec_score_kernel(
   }
   __syncthreads();
   const S* kb = KI + (int64_t)b * n_entries * CI;
-  // each wave: 16 keys per step, 4 steps unrolled
-  for (int64_t s0 = c0 + wave * 64; s0 < c1; s0 += 256) {
-    uint4 kv[4][NG];
+  // Each wave scores a contiguous quarter of the chunk, 64 keys (4 steps of
+  // 16) at a time; the next 64 keys load while the current ones are scored.
+  const int64_t w0 = c0 + (int64_t)wave * (kDecChunk / 4);
+  const int64_t w1 = min64(w0 + kDecChunk / 4, c1);
+  auto load64 = [&](int64_t s0, uint4 (&dst)[4][NG]) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int64_t s = s0 + u * 16 + (lane & 15);
+      const int64_t s = min64(s0 + u * 16 + (lane & 15), c1 - 1);  // past c1: not stored
 #pragma unroll
-      for (int g = 0; g < NG; ++g)
-        kv[u][g] = s < c1 ? *(const uint4*)(kb + s * CI + g * KGE + lg * E) : make_uint4(0, 0, 0, 0);
+      for (int g = 0; g < NG; ++g) dst[u][g] = *(const uint4*)(kb + s * CI + g * KGE + lg * E);
     }
+  };
+  auto score64 = [&](int64_t s0, const uint4 (&src)[4][NG]) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       f32x4_t acc = f32x4_t{};
 #pragma unroll
-      for (int g = 0; g < NG; ++g) mma16<T>(acc, qa[g], kv[u][g]);
+      for (int g = 0; g < NG; ++g) mma16<T>(acc, qa[g], src[u][g]);
       float p = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) p += wv[i] * fmaxf(acc[i], 0.f);
-      p += __shfl_xor(p, 16, 64);
-      p += __shfl_xor(p, 32, 64);
+      p = xlane_sum(p);
       const int64_t s = s0 + u * 16 + (lane & 15);
-      if (lg == 0 && s < c1) {
+      if (lg == 0 && s < w1) {
         scores[(int64_t)b * n_entries + s] = p;
         atomicAdd(&lh[float_key(p) >> 21], 1);
       }
     }
+  };
+  // two register buffers, used alternately (static indices keep them in VGPRs)
+  uint4 ka[4][NG], kc[4][NG];
+  if (w0 < w1) load64(w0, ka);
+  for (int64_t s0 = w0; s0 < w1; s0 += 128) {
+    if (s0 + 64 < w1) load64(s0 + 64, kc);
+    score64(s0, ka);
+    if (s0 + 64 >= w1) break;
+    if (s0 + 128 < w1) load64(s0 + 128, ka);
+    score64(s0 + 64, kc);
   }
   __syncthreads();
   for (int i = tid; i < kCoarseBins; i += 256)
