@@ -65,32 +65,33 @@ struct OAcc {
 // rows per 16-lane group) touch distinct banks.
 CSA_DEV int slot_pi(int g, int h, int i) { return 16 * (g >> 1) + 8 * h + 4 * (g & 1) + i; }
 
-// One 32-candidate tile for this wave's 16 heads: S^T = K Q^T, the online
-// softmax update (log2 units), O^T += V^T P^T.
+// Logits of one 32-candidate tile for this wave's 16 heads, S^T = K Q^T, in
+// log2 units; z[4b+i] is tile row pi(lg, b, i) for head lc, -inf where the
+// row is masked.  Returns the per-head maximum over the tile.
 template <int C>
-CSA_DEV void mqa_tile(const uint8_t* kv, const int* vflags, const bf16x8_t* qf, OAcc<C>& o,
-                      float& run_m, float& run_l, float sl2, int koff0, int koff1, int troff0,
-                      int troff1, int lg) {
+CSA_DEV float tile_logits(const uint8_t* kv, const int* vflags, const bf16x8_t* qf, float sl2,
+                          int koff0, int koff1, int lg, float (&z)[8]) {
   constexpr int NKG = C / 32;
-  typedef OAcc<C> A;
-  // S^T for the tile: block b's A rows are K rows pi(lc/4, b, lc%4).  The
-  // fragments of k-group g+1 are read while g's products issue, so the LDS
+  // block b's A rows are K rows pi(lc/4, b, lc%4).  The fragments of the
+  // next D-1 k-groups are read while a k-group's products issue, so the LDS
   // latency overlaps the matrix cores.
+  constexpr int D = 3;  // k-groups of fragments in flight
   f32x4_t s[2] = {f32x4_t{}, f32x4_t{}};
-  bf16x8_t a0[2], a1[2];
-  a0[0] = *(const bf16x8_t*)(kv + koff0);
-  a1[0] = *(const bf16x8_t*)(kv + koff1);
+  bf16x8_t a0[D], a1[D];
+#pragma unroll
+  for (int g = 0; g < D - 1; ++g) {
+    a0[g] = *(const bf16x8_t*)(kv + koff0 + g * 64);
+    a1[g] = *(const bf16x8_t*)(kv + koff1 + g * 64);
+  }
 #pragma unroll
   for (int g = 0; g < NKG; ++g) {
-    if (g + 1 < NKG) {
-      a0[(g + 1) & 1] = *(const bf16x8_t*)(kv + koff0 + (g + 1) * 64);
-      a1[(g + 1) & 1] = *(const bf16x8_t*)(kv + koff1 + (g + 1) * 64);
+    if (g + D - 1 < NKG) {
+      a0[(g + D - 1) % D] = *(const bf16x8_t*)(kv + koff0 + (g + D - 1) * 64);
+      a1[(g + D - 1) % D] = *(const bf16x8_t*)(kv + koff1 + (g + D - 1) * 64);
     }
-    s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[g & 1], qf[g], s[0], 0, 0, 0);
-    s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[g & 1], qf[g], s[1], 0, 0, 0);
+    s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[g % D], qf[g], s[0], 0, 0, 0);
+    s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[g % D], qf[g], s[1], 0, 0, 0);
   }
-  // online softmax for head `head` (this lane's column) in log2 units
-  float z[8];
   float mx = -INFINITY;
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
@@ -103,7 +104,18 @@ CSA_DEV void mqa_tile(const uint8_t* kv, const int* vflags, const bf16x8_t* qf, 
       mx = fmaxf(mx, zz);
     }
   }
-  mx = xlane_max(mx);
+  return xlane_max(mx);
+}
+
+// One 32-candidate tile for this wave's 16 heads over the full head dim: the
+// logits, the online softmax update (log2 units), O^T += V^T P^T.
+template <int C>
+CSA_DEV void mqa_tile(const uint8_t* kv, const int* vflags, const bf16x8_t* qf, OAcc<C>& o,
+                      float& run_m, float& run_l, float sl2, int koff0, int koff1, int troff0,
+                      int troff1, int lg) {
+  typedef OAcc<C> A;
+  float z[8];
+  const float mx = tile_logits<C>(kv, vflags, qf, sl2, koff0, koff1, lg, z);
   if (__any(mx > run_m + 8.f)) {  // wave-uniform rescale of O
     const float nm = fmaxf(run_m, mx);
     const float alpha = __builtin_amdgcn_exp2f(run_m - nm);
@@ -146,6 +158,94 @@ CSA_DEV void mqa_tile(const uint8_t* kv, const int* vflags, const bf16x8_t* qf, 
   if constexpr (A::NCB > 16) {
 #pragma unroll
     for (int cb = 0; cb < A::NHI; ++cb) pv(A::NLO + cb, o.hi[cb]);
+  }
+}
+
+// Channel-split variant for one query's 64 heads in a workgroup.  Wave w
+// still forms the logits and the softmax of heads 16w..16w+15, but the PV
+// product of the tile is split by channels: wave w accumulates O^T for its
+// C/4 channels and all 64 heads.  Every wave's P^T operand (and, when a
+// wave raised its running max, the rescale factors of its heads) goes
+// through LDS, so each wave transposes a quarter of the tile instead of all
+// of it; the logits still read each K row once per wave.
+struct Xchg {
+  bf16x8_t p[4][64];  // P^T B operands, [wave][lane]
+  float alpha[64];    // O rescale factor per head, valid where flag is set
+  int flag[4];        // wave w raised the running max of its heads
+  float l[64];        // running sums at the end
+};
+
+template <int C>
+struct OSplit {
+  static constexpr int NCB = C / 64;  // 16-channel blocks per wave
+  f32x4_t h[4][NCB];                  // [head block][channel block]
+};
+
+template <int C>
+CSA_DEV void mqa_tile_split(const uint8_t* kv, const int* vflags, const bf16x8_t* qf,
+                            OSplit<C>& o, float& run_m, float& run_l, float sl2, int koff0,
+                            int koff1, int troff0, int troff1, int lane, int lg, int wave,
+                            Xchg& xc) {
+  typedef OSplit<C> A;
+  float z[8];
+  const float mx = tile_logits<C>(kv, vflags, qf, sl2, koff0, koff1, lg, z);
+  const bool resc = __any(mx > run_m + 8.f);
+  if (resc) {  // wave-uniform
+    const float nm = fmaxf(run_m, mx);
+    const float alpha = __builtin_amdgcn_exp2f(run_m - nm);
+    run_l *= alpha;
+    run_m = nm;
+    if (lg == 0) xc.alpha[wave * 16 + lane] = alpha;
+  }
+  if (lane == 0) xc.flag[wave] = resc;
+  f32x8_t p;
+  float ps = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    p[j] = __builtin_amdgcn_exp2f(z[j] - run_m);
+    ps += p[j];
+  }
+  run_l += xlane_sum(ps);
+  xc.p[wave][lane] = __builtin_convertvector(p, bf16x8_t);
+  __syncthreads();  // P^T operands and rescale factors of all heads
+
+  const int4 fl = *(const int4*)xc.flag;
+  const int fla[4] = {fl.x, fl.y, fl.z, fl.w};
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) {
+    if (__builtin_amdgcn_readfirstlane(fla[hb])) {
+      const float a = xc.alpha[hb * 16 + (lane & 15)];
+#pragma unroll
+      for (int cb = 0; cb < A::NCB; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o.h[hb][cb][i] *= a;
+    }
+  }
+  bf16x8_t pb[4];
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) pb[hb] = xc.p[hb][lane];
+  // O^T += V^T P^T over this wave's channel blocks (transpose reads as in
+  // mqa_tile, offset to the wave's channels); one V^T fragment serves the
+  // four head blocks, and the next DV-1 fragments are in flight meanwhile.
+  const int cofs = wave * A::NCB * 32;
+  constexpr int DV = 3;
+  bf16x8_t va[DV];
+  auto vread = [&](int cb) {
+    const bf16x4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (CSA_LDS bf16x4_t*)(kv + troff0 + cofs + cb * 32));
+    const bf16x4_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (CSA_LDS bf16x4_t*)(kv + troff1 + cofs + cb * 32));
+    return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+#pragma unroll
+  for (int cb = 0; cb < DV - 1 && cb < A::NCB; ++cb) va[cb] = vread(cb);
+#pragma unroll
+  for (int cb = 0; cb < A::NCB; ++cb) {
+    if (cb + DV - 1 < A::NCB) va[(cb + DV - 1) % DV] = vread(cb + DV - 1);
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb)
+      o.h[hb][cb] =
+          __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[cb % DV], pb[hb], o.h[hb][cb], 0, 0, 0);
   }
 }
 
@@ -238,9 +338,10 @@ __global__ __launch_bounds__(256, 2) void mqa_prefill_bf16_kernel(
     const float* __restrict__ sink, uint16_t* __restrict__ out, int64_t n, int nh, int k, int m,
     int n_win, float scale, int qk_norm, float eps, int r, float theta, int64_t n_entries) {
   typedef Geo<C> G;
-  typedef OAcc<C> A;
+  typedef OSplit<C> A;
   constexpr int NKG = C / 32;
   __shared__ __align__(16) uint8_t smem[G::BUF];
+  __shared__ __align__(16) Xchg xc;
   __shared__ __align__(16) int valid[2][kT];
   __shared__ int sidx[SPARSE ? kMaxK : 1];
   __shared__ float2 rope_tab[C / 2];  // (cos, sin) of this token's RoPE pairs
@@ -293,9 +394,9 @@ __global__ __launch_bounds__(256, 2) void mqa_prefill_bf16_kernel(
   float run_m = (head < nh ? sink[head] : 0.f) * LOG2E, run_l = 1.f;
   A o;
 #pragma unroll
-  for (int cb = 0; cb < A::NLO; ++cb) o.lo[cb] = f32x4_t{};
+  for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
-  for (int cb = 0; cb < A::NHI; ++cb) o.hi[cb] = f32x4_t{};
+    for (int cb = 0; cb < A::NCB; ++cb) o.h[hb][cb] = f32x4_t{};
   const int koff0 = G::off(slot_pi(lc >> 2, 0, lc & 3)) + lg * 16;
   const int koff1 = G::off(slot_pi(lc >> 2, 1, lc & 3)) + lg * 16;
   const int troff0 = G::off(slot_pi(lg, 0, lc >> 2)) + 8 * (lc & 3);
@@ -305,34 +406,38 @@ __global__ __launch_bounds__(256, 2) void mqa_prefill_bf16_kernel(
   for (int ti = 0; ti < ntiles; ++ti) {
     const int buf = ti & 1;
     if (ti + 1 < ntiles) issue_tile(ti + 1, buf ^ 1);
-    mqa_tile<C>(smem + buf * G::TILE, valid[buf], qf, o, run_m, run_l, scale * LOG2E, koff0,
-                koff1, troff0, troff1, lg);
+    mqa_tile_split<C>(smem + buf * G::TILE, valid[buf], qf, o, run_m, run_l, scale * LOG2E,
+                      koff0, koff1, troff0, troff1, lane, lg, wave, xc);
     wait_vmem();
     __syncthreads();
   }
 
-  // epilogue: O^T lane layout: block cb, element i = O[head][cb*16 + 4*lg + i]
-  const float inv = 1.f / run_l;
+  // epilogue: block (hb, cb), element i = O[16*hb + lc][wave*C/4 + cb*16 + 4*lg + i]
+  if (lg == 0) xc.l[head] = run_l;
+  __syncthreads();
   uint8_t* ostage = smem;  // [head][C] bf16, padded like the tiles
 #pragma unroll
-  for (int cb = 0; cb < A::NCB; ++cb) {
-    const f32x4_t acc = cb < A::NLO ? o.lo[cb] : o.hi[cb - A::NLO];
-    float v[4];
+  for (int hb = 0; hb < 4; ++hb) {
+    const float inv = 1.f / xc.l[hb * 16 + lc];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = acc[i] * inv;
-    const int ch0 = cb * 16 + 4 * lg;
-    if (r > 0 && ch0 >= C - r) {
+    for (int cb = 0; cb < A::NCB; ++cb) {
+      float v[4];
 #pragma unroll
-      for (int i = 0; i < 4; i += 2) {
-        const float2 cs = rope_tab[(ch0 + i - (C - r)) >> 1];
-        const float x0 = v[i], x1 = v[i + 1];
-        v[i] = x0 * cs.x + x1 * cs.y;  // rotate by -t
-        v[i + 1] = -x0 * cs.y + x1 * cs.x;
+      for (int i = 0; i < 4; ++i) v[i] = o.h[hb][cb][i] * inv;
+      const int ch0 = wave * (C / 4) + cb * 16 + 4 * lg;
+      if (r > 0 && ch0 >= C - r) {
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          const float2 cs = rope_tab[(ch0 + i - (C - r)) >> 1];
+          const float x0 = v[i], x1 = v[i + 1];
+          v[i] = x0 * cs.x + x1 * cs.y;  // rotate by -t
+          v[i + 1] = -x0 * cs.y + x1 * cs.x;
+        }
       }
+      const uint32_t w0 = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+      const uint32_t w1 = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+      *(uint2*)(ostage + G::off(hb * 16 + lc) + ch0 * 2) = make_uint2(w0, w1);
     }
-    const uint32_t w0 = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-    const uint32_t w1 = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-    *(uint2*)(ostage + G::off(head) + ch0 * 2) = make_uint2(w0, w1);
   }
   __syncthreads();
   uint16_t* orow = out + t * (int64_t)nh * C;
