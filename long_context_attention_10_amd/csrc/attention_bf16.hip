@@ -181,12 +181,13 @@ struct OSplit {
   f32x4_t h[4][NCB];                  // [head block][channel block]
 };
 
+// Logit side of a channel-split tile: this wave's logits and online softmax
+// (heads 16*sw..16*sw+15), published to `xc` as the P^T operand, with the
+// rescale factors when the running max was raised.
 template <int C>
-CSA_DEV void mqa_tile_split(const uint8_t* kv, const int* vflags, const bf16x8_t* qf,
-                            OSplit<C>& o, float& run_m, float& run_l, float sl2, int koff0,
-                            int koff1, int troff0, int troff1, int lane, int lg, int wave,
-                            Xchg& xc) {
-  typedef OSplit<C> A;
+CSA_DEV void publish_p(const uint8_t* kv, const int* vflags, const bf16x8_t* qf, float& run_m,
+                       float& run_l, float sl2, int koff0, int koff1, int lane, int lg, int sw,
+                       Xchg& xc) {
   float z[8];
   const float mx = tile_logits<C>(kv, vflags, qf, sl2, koff0, koff1, lg, z);
   const bool resc = __any(mx > run_m + 8.f);
@@ -195,9 +196,9 @@ CSA_DEV void mqa_tile_split(const uint8_t* kv, const int* vflags, const bf16x8_t
     const float alpha = __builtin_amdgcn_exp2f(run_m - nm);
     run_l *= alpha;
     run_m = nm;
-    if (lg == 0) xc.alpha[wave * 16 + lane] = alpha;
+    if (lg == 0) xc.alpha[sw * 16 + lane] = alpha;
   }
-  if (lane == 0) xc.flag[wave] = resc;
+  if (lane == 0) xc.flag[sw] = resc;
   f32x8_t p;
   float ps = 0.f;
 #pragma unroll
@@ -206,9 +207,17 @@ CSA_DEV void mqa_tile_split(const uint8_t* kv, const int* vflags, const bf16x8_t
     ps += p[j];
   }
   run_l += xlane_sum(ps);
-  xc.p[wave][lane] = __builtin_convertvector(p, bf16x8_t);
-  __syncthreads();  // P^T operands and rescale factors of all heads
+  xc.p[sw][lane] = __builtin_convertvector(p, bf16x8_t);
+}
 
+// PV side of a channel-split tile: rescale where a logit wave raised its
+// max, then O^T += V^T P^T over channel quarter cq for all 64 heads
+// (transpose reads as in mqa_tile, offset to the quarter); one V^T fragment
+// serves the four head blocks, and the next DV-1 fragments are in flight.
+template <int C>
+CSA_DEV void pv_quarter(const uint8_t* kv, const Xchg& xc, OSplit<C>& o, int troff0, int troff1,
+                        int lane, int cq) {
+  typedef OSplit<C> A;
   const int4 fl = *(const int4*)xc.flag;
   const int fla[4] = {fl.x, fl.y, fl.z, fl.w};
 #pragma unroll
@@ -224,10 +233,7 @@ CSA_DEV void mqa_tile_split(const uint8_t* kv, const int* vflags, const bf16x8_t
   bf16x8_t pb[4];
 #pragma unroll
   for (int hb = 0; hb < 4; ++hb) pb[hb] = xc.p[hb][lane];
-  // O^T += V^T P^T over this wave's channel blocks (transpose reads as in
-  // mqa_tile, offset to the wave's channels); one V^T fragment serves the
-  // four head blocks, and the next DV-1 fragments are in flight meanwhile.
-  const int cofs = wave * A::NCB * 32;
+  const int cofs = cq * A::NCB * 32;
   constexpr int DV = 3;
   bf16x8_t va[DV];
   auto vread = [&](int cb) {
@@ -247,6 +253,16 @@ CSA_DEV void mqa_tile_split(const uint8_t* kv, const int* vflags, const bf16x8_t
       o.h[hb][cb] =
           __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[cb % DV], pb[hb], o.h[hb][cb], 0, 0, 0);
   }
+}
+
+template <int C>
+CSA_DEV void mqa_tile_split(const uint8_t* kv, const int* vflags, const bf16x8_t* qf,
+                            OSplit<C>& o, float& run_m, float& run_l, float sl2, int koff0,
+                            int koff1, int troff0, int troff1, int lane, int lg, int wave,
+                            Xchg& xc) {
+  publish_p<C>(kv, vflags, qf, run_m, run_l, sl2, koff0, koff1, lane, lg, wave, xc);
+  __syncthreads();  // P^T operands and rescale factors of all heads
+  pv_quarter<C>(kv, xc, o, troff0, troff1, lane, wave);
 }
 
 // q prologue: per-head RMSNorm over the row held by the 4 lane groups, RoPE

@@ -135,6 +135,42 @@ def test_sparse_mqa_prefill(lib, dtype, n, nh, c, k, m, n_win, r):
     assert_out_close(out, ref, dtype, "sparse mqa out")
 
 
+@pytest.mark.parametrize("n,c,k,r", [
+    (2304, 512, 512, 64),   # the 64K layer's head shapes
+    (2053, 512, 100, 64),   # ragged tail, k not a tile multiple
+    (2100, 256, 64, 32),
+    (2080, 128, 96, 0),
+])
+def test_sparse_mqa_prefill_2k_tokens(lib, n, c, k, r):
+    """64 heads over two thousand tokens and more: sampled rows, including
+    the early short windows, the 8-way die split of the token range and
+    the last tokens."""
+    nh, m, n_win = 64, 4, 128
+    _say("sparse_mqa_prefill 2k", n, c, k, r)
+    key = ("sparse-2k", n, c, k)
+    ne = n // m
+    q = I.normal((n, nh, c), key + ("q",), dtype="bf16", device=DEV)
+    win = I.normal((n, c), key + ("win",), dtype="bf16", device=DEV)
+    comp = I.normal((ne, c), key + ("comp",), dtype="bf16", device=DEV)
+    sink = I.normal((nh,), key + ("sink",), device=DEV)
+    idx_np = _rand_idx(n, k, m, ne, key)
+    out = lib.csa_sparse_mqa_prefill(q, win, comp, torch.from_numpy(idx_np).to(DEV), sink,
+                                     n_win=n_win, rope_dims=r)
+    torch.cuda.synchronize()
+    per = -(-n // 8)
+    rows = set(range(0, 12)) | {126, 127, 128, 129, n // 2, n - 2, n - 1}
+    for b in range(1, 8):
+        rows |= {b * per - 1, b * per}
+    rows = sorted(x for x in rows | set(range(5, n, n // 24)) if 0 <= x < n)
+    qh, wh, ch, sh = f64(q), f64(win), f64(comp), f64(sink)
+    for t in rows:
+        sel = idx_np[t][idx_np[t] >= 0]
+        lo = max(0, t - n_win + 1)
+        ref = O.attend_decode_row(qh[t], t, wh[lo:t + 1], ch[sel], sh, c ** -0.5, rope_dims=r,
+                                  store="bf16")
+        assert_out_close(out[t], ref, "bf16", f"token {t}")
+
+
 @pytest.mark.parametrize("dtype,n,nh,c,m,n_win,r", [
     ("bf16", 1100, 64, 128, 128, 128, 0),
     ("f32", 300, 8, 128, 4, 128, 0),
