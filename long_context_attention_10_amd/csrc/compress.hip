@@ -17,10 +17,11 @@ constexpr int kMaxKSplit = 8;
 
 // ===========================================================================
 // Projection GEMM:  out[M, 0:N] (fp32) = A[M, K] . [W0; W1; W2]^T
-// 128x128 output tile per 256-thread workgroup (2x2 waves of 64x64), K staged
-// through LDS in 128-byte slices, double buffered.  Both operands are K-major
-// in memory (A rows = tokens, W rows = output channels), so every lane feeds
-// the matrix cores with one 16-byte LDS read per operand and k-group.
+// fp32 operands: 128x128 output tile per 256-thread workgroup (2x2 waves of
+// 64x64), K staged through LDS in 128-byte slices, double buffered.  Both
+// operands are K-major in memory (A rows = tokens, W rows = output channels),
+// so every lane feeds the matrix cores with one 16-byte LDS read per operand
+// and k-group.  (bf16 operands take proj_gemm_bf16_kernel below.)
 // ===========================================================================
 template <class T>
 __global__ __launch_bounds__(256, 2) void proj_gemm_kernel(
@@ -117,6 +118,151 @@ __global__ __launch_bounds__(256, 2) void proj_gemm_kernel(
       for (int i = 0; i < 16; ++i) {
         const int64_t row = m0 + wm * 64 + mb * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
         if (row < M && col < ntot) out[row * ldo + col] = acc[mb][nb][i];
+      }
+    }
+}
+
+// ===========================================================================
+// bf16 projection GEMM: 256x256 output tile per 512-thread workgroup, 4x2
+// waves of 64x128 (2x4 blocks of 32x32x16 MFMA, 128 accumulators; two waves
+// per SIMD).  A and W panels stream into a ring of four LDS stages (32-wide
+// K slices) by direct global->LDS loads issued three slices ahead, so a
+// slice's loads have three slices of products to land in; the next k-group's
+// fragments are read while a k-group's products run.  In LDS, 16-byte
+// granule g of tile row r (64 bytes per row) sits at column g ^ ((r >> 2) & 3),
+// so every 16 consecutive rows of a fragment read cover all banks.  Tile
+// order: die x (workgroup id mod 8) takes M blocks x, x+8, ... in groups that
+// its workgroups run side by side, so the A and W slices they stream are
+// shared in the die's L2.
+// ===========================================================================
+constexpr int kGM = 256, kGN = 256;  // output tile
+constexpr int kGKB = 64;             // bytes of K per slice (32 bf16)
+constexpr int kGS = 4;               // LDS stages
+constexpr int kGAhead = kGS - 1;     // slices in flight ahead of the one in use
+
+__global__ __launch_bounds__(512, 1) void proj_gemm_bf16_kernel(
+    const uint16_t* __restrict__ A, int64_t M, int K, const uint16_t* __restrict__ W0, int r0,
+    const uint16_t* __restrict__ W1, int r1, const uint16_t* __restrict__ W2, int r2,
+    float* __restrict__ out, int64_t ldo, int mblocks, int ntiles) {
+  __shared__ __align__(16) uint8_t sA[kGS][kGM * kGKB];
+  __shared__ __align__(16) uint8_t sB[kGS][kGN * kGKB];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;  // 64-row band, 128-column band
+  // die x owns M blocks x, x+8, ...; it walks them in groups of 8, and
+  // within a group over 8 x 4 tiles (8 M blocks, 4 N tiles) at a time, so the
+  // 32 workgroups a die runs together share every A and W slice they load
+  const int xcd = blockIdx.x & 7, seq = blockIdx.x >> 3;
+  const int mg = seq / (8 * ntiles), rg = seq % (8 * ntiles);
+  const int nfull = ntiles / 4;
+  int mi, nt;
+  if (rg < nfull * 32) {
+    mi = (rg % 32) / 4;
+    nt = 4 * (rg / 32) + rg % 4;
+  } else {
+    const int gs = ntiles - 4 * nfull, rr = rg - nfull * 32;
+    mi = rr / gs;
+    nt = 4 * nfull + rr % gs;
+  }
+  const int mbk = 8 * (8 * mg + mi) + xcd;
+  if (mbk >= mblocks) return;
+  const int64_t m0 = (int64_t)mbk * kGM;
+  const int n0 = nt * kGN;
+  const int ntot = r0 + r1 + r2;
+
+  // Loads: wave w fills 1 KiB chunks w and w+8 (16 rows each) of both
+  // panels; lane i of chunk c carries row 16c + i/4 into LDS column i%4,
+  // which holds global granule (i%4) ^ ((row >> 2) & 3).
+  const uint8_t* pa[2];
+  const uint8_t* pb[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int row = 16 * (wave + 8 * u) + (lane >> 2);
+    const int gran = (lane & 3) ^ ((row >> 2) & 3);
+    const int64_t ar = min64(m0 + row, M - 1);  // rows past M read a valid row
+    pa[u] = (const uint8_t*)(A + ar * K) + gran * 16;
+    int n = n0 + row;
+    const uint16_t* wp = W0;
+    if (n >= ntot) n = 0;  // masked columns read a valid row
+    else if (n >= r0 + r1) { wp = W2; n -= r0 + r1; }
+    else if (n >= r0) { wp = W1; n -= r0; }
+    pb[u] = (const uint8_t*)(wp + (int64_t)n * K) + gran * 16;
+  }
+  constexpr int LPS = 4;  // loads per wave and slice
+  // load q (0..3) of slice kt: A chunk, W chunk, A chunk, W chunk
+  auto issue1 = [&](int kt, int q) {
+    const int s = kt % kGS, u = q >> 1, chunk = wave + 8 * u;
+    if (q & 1) lds_dma16(pb[u] + (int64_t)kt * kGKB, sB[s] + chunk * 1024);
+    else lds_dma16(pa[u] + (int64_t)kt * kGKB, sA[s] + chunk * 1024);
+  };
+  auto issue = [&](int kt) {
+#pragma unroll
+    for (int q = 0; q < LPS; ++q) issue1(kt, q);
+  };
+
+  f32x16_t acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
+  // fragment rows (l & 31) of 32-row blocks, granule 2*kg + l/32
+  const int frow = lane & 31, fhalf = lane >> 5, fsw = (frow >> 2) & 3;
+  const int aoff = (wm * 64 + frow) * kGKB;
+  const int boff = (wn * 128 + frow) * kGKB;
+  bf16x8_t fa[2][2], fb[2][4];
+  auto frags = [&](int s, int kg, int slot) {
+    const int col = ((2 * kg + fhalf) ^ fsw) * 16;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      fa[slot][i] = *(const bf16x8_t*)(sA[s] + aoff + i * 32 * kGKB + col);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      fb[slot][j] = *(const bf16x8_t*)(sB[s] + boff + j * 32 * kGKB + col);
+  };
+
+  const int nk = K / 32;  // K is a multiple of 64, so nk >= 2
+#pragma unroll
+  for (int kt = 0; kt < kGAhead; ++kt)
+    if (kt < nk) issue(kt);
+  // slice 0 has landed once at most the later slices' loads are outstanding
+  if (nk >= 3) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPS));
+  else __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPS));
+  __syncthreads();
+  frags(0, 0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int s = kt % kGS;
+    const bool ahead = kt + kGAhead < nk;
+    frags(s, 1, 1);
+    // the loads of slice kt+3 go out one per four products, so the
+    // load pipe and the matrix cores work side by side
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kg][i], fb[kg][j], acc[i][j],
+                                                              0, 0, 0);
+        if (ahead) issue1(kt + kGAhead, 2 * kg + i);
+      }
+    // slice kt+1 must have landed; the loads of kt+2 and kt+3 may still run
+    const int later = min(nk - 1, kt + kGAhead) - (kt + 1);
+    if (later >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPS));
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPS));
+    else wait_vmem();
+    __syncthreads();
+    if (kt + 1 < nk) frags((kt + 1) % kGS, 0, 0);
+  }
+
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + wn * 128 + j * 32 + frow;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t row = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * fhalf + (e & 3);
+        if (row < M && col < ntot) out[row * ldo + col] = acc[i][j][e];
       }
     }
 }
@@ -470,10 +616,12 @@ hipError_t launch_proj_gemm(int dtype, const void* A, int64_t M, int K, const We
   const int N = w.total();
   dim3 grid((N + 127) / 128, (unsigned)((M + 127) / 128));
   if (dtype == CSA_BF16) {
-    typedef BF16::S S;
-    proj_gemm_kernel<BF16><<<grid, 256, 0, st>>>((const S*)A, M, K, (const S*)w.w[0], w.rows[0],
-                                                  (const S*)w.w[1], w.rows[1], (const S*)w.w[2],
-                                                  w.rows[2], out, ldo);
+    const int mblocks = (int)((M + kGM - 1) / kGM), ntiles = (N + kGN - 1) / kGN;
+    const int mgroups = ((mblocks + 7) / 8 + 7) / 8;  // groups of 8 M blocks per die
+    const unsigned g = (unsigned)(8 * mgroups * 8 * ntiles);
+    proj_gemm_bf16_kernel<<<g, 512, 0, st>>>(
+        (const uint16_t*)A, M, K, (const uint16_t*)w.w[0], w.rows[0], (const uint16_t*)w.w[1],
+        w.rows[1], (const uint16_t*)w.w[2], w.rows[2], out, ldo, mblocks, ntiles);
   } else {
     proj_gemm_kernel<F32><<<grid, 256, 0, st>>>((const float*)A, M, K, (const float*)w.w[0],
                                                  w.rows[0], (const float*)w.w[1], w.rows[1],

@@ -173,6 +173,11 @@ CSA_DEV void lds_dma16(const void* g, const void* lds_dst) {
 // Wait for every outstanding memory operation of the wave.
 CSA_DEV void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
 
+// s_waitcnt immediate that waits until at most n (< 64) vector-memory
+// operations of the wave are outstanding; the other counters are left alone
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 CSA_DEV int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
 CSA_DEV int64_t max64(int64_t a, int64_t b) { return a > b ? a : b; }
 
