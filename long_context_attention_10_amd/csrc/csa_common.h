@@ -178,6 +178,12 @@ CSA_DEV void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
 // (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
+// max(x, 0) in one integer instruction: a float with the sign bit set is a
+// negative int32, so a signed max with 0 zeroes exactly the negatives (and
+// -0); fmaxf would first canonicalise x, since matrix-core results are not
+// known to be canonical.
+CSA_DEV float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 CSA_DEV int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
 CSA_DEV int64_t max64(int64_t a, int64_t b) { return a > b ? a : b; }
 

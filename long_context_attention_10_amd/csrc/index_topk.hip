@@ -128,7 +128,7 @@ __global__ __launch_bounds__(256) void index_scores_prefill_kernel(
         for (int gq = 0; gq < 4; ++gq) {
           float p = 0.f;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) p += wv[rb][gq * 4 + r] * fmaxf(acc[rb][gq * 4 + r], 0.f);
+          for (int r = 0; r < 4; ++r) p += wv[rb][gq * 4 + r] * relu(acc[rb][gq * 4 + r]);
           part[gq] = p;
         }
         const int64_t tb = q0 + (wave * (RB * 32) + rb * 32) / HI;  // first query of this block
@@ -255,13 +255,14 @@ CSA_DEV void coarse_threshold(const int* __restrict__ h, int nb, int need, int* 
 // (key << 32 | ~index): higher score first, ties to the smaller index.
 //   1. keys are binned linearly by score VALUE between the row minimum and
 //      maximum (1024 bins; the map is monotone, so each bin is a key
-//      interval, whose smallest key is recorded) and the bin T holding the
-//      k-th largest is found from the histogram -- raw float bits would pile
-//      most of a row into the few bins of its common exponent;
-//   2. T is resolved exactly: its composites are ranked directly when at
-//      most 256, else selected by an 8-bit radix over the composites of T;
-//   3. the winners are marked in an LDS bitmap over the row, which is
-//      emitted in ascending index order.
+//      interval) and the bin T holding the k-th largest is found from the
+//      histogram -- raw float bits would pile most of a row into the few
+//      bins of its common exponent;
+//   2. in one more pass over the keys, entries of bins above T are marked
+//      as winners in an LDS bitmap over the row and the composites of T are
+//      gathered and ranked (at most 256; else T's need-th largest composite
+//      is found by an 8-bit radix and a last pass marks T's winners);
+//   3. the bitmap is emitted in ascending index order.
 // ===========================================================================
 constexpr int kSelBins = 1024;
 constexpr int kRankMax = 256;
@@ -280,10 +281,8 @@ __global__ __launch_bounds__(256) void topk_rows_prefill_kernel(const float* __r
                                                                 int32_t* __restrict__ idx_out) {
   constexpr int NQ = MAXIT / 4;  // 4-entry groups per thread
   __shared__ int hist[kSelBins];
-  __shared__ uint32_t bmin[kSelBins];
   __shared__ uint32_t bits[MAXIT * 256 / 32];
   __shared__ uint64_t cand[kRankMax];
-  __shared__ uint64_t cthr;
   __shared__ int tmp[8];
   __shared__ int res[2];
   __shared__ uint32_t red[8];
@@ -318,7 +317,7 @@ __global__ __launch_bounds__(256) void topk_rows_prefill_kernel(const float* __r
     }
   }
   auto idx_of = [&](int i) { return 4 * (tid + 256 * (i >> 2)) + (i & 3); };
-  for (int i = tid; i < kSelBins; i += 256) { hist[i] = 0; bmin[i] = 0xffffffffu; }
+  for (int i = tid; i < kSelBins; i += 256) hist[i] = 0;
   for (int w = tid; w < MAXIT * 256 / 32; w += 256) bits[w] = 0u;
   if (tid == 0) ncand = 0;
   uint32_t lo = 0xffffffffu, hi = 0u;
@@ -337,51 +336,47 @@ __global__ __launch_bounds__(256) void topk_rows_prefill_kernel(const float* __r
   const float fmin = key_float(lo), fmax = key_float(hi);
   float scale = (float)kSelBins / (fmax - fmin);
   if (!(scale < INFINITY)) scale = 0.f;  // equal or non-finite range: one bin
-  auto vbin = [&](uint32_t key) {
-    const float f = (key_float(key) - fmin) * scale;
+  // bin of a real key (>= 1): monotone in the key, so bins are key intervals
+  // and membership is recomputed exactly wherever it is needed
+  auto vbin_with = [&](uint32_t key, float f0, float sc) {
+    const float f = (key_float(key) - f0) * sc;
     return f >= (float)(kSelBins - 1) ? kSelBins - 1 : (f > 0.f ? (int)f : 0);
   };
+  auto vbin = [&](uint32_t key) { return vbin_with(key, fmin, scale); };
+  auto mark = [&](int e) { atomicOr(&bits[e >> 5], 1u << (e & 31)); };
 
-  // 1. value histogram with each bin's smallest key; threshold bin T
+  // 1. value histogram; threshold bin T
 #pragma unroll
   for (int i = 0; i < MAXIT; ++i)
-    if (u[i]) {
-      const int b = vbin(u[i]);
-      atomicAdd(&hist[b], 1);
-      atomicMin(&bmin[b], u[i]);
-    }
+    if (u[i]) atomicAdd(&hist[vbin(u[i])], 1);
   __syncthreads();
   bin_threshold<kSelBins>(hist, kt, tmp, res);
   const int T = res[0];
   int need = kt - res[1];  // to take from bin T (>= 1)
   const int nT = hist[T];
-  // bin T = keys in [tlo, thi): thi = smallest key of the next non-empty bin
-  const uint32_t tlo = bmin[T];
-  uint32_t nx = 0xffffffffu;
-  for (int b = T + 1 + tid; b < kSelBins; b += 256) nx = min(nx, bmin[b]);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) nx = min(nx, (uint32_t)__shfl_xor((int)nx, o, 64));
-  if (lane == 0) red[wave] = nx;
-  __syncthreads();
-  const uint64_t thi = T == kSelBins - 1 ? (uint64_t)hi + 1
-                                          : (uint64_t)min(min(red[0], red[1]), min(red[2], red[3]));
-  auto in_t = [&](uint32_t key) { return key >= tlo && (uint64_t)key < thi; };
 
-  // 2. the need-th largest composite of bin T
-  uint64_t thr;
+  // 2. bins above T win outright; bin T's composites (key << 32 | ~index) are
+  //    ranked when few (the winners of T are the need largest), else their
+  //    need-th largest is found by an 8-bit radix.  The bins are recomputed
+  //    (from copies the compiler cannot see through), not kept from pass 1:
+  //    keeping 64 of them would cost as many registers.
+  float fmin2 = fmin, scale2 = scale;
+  asm volatile("" : "+v"(fmin2), "+v"(scale2));
   if (nT <= kRankMax) {
 #pragma unroll
     for (int i = 0; i < MAXIT; ++i)
-      if (u[i] && in_t(u[i])) cand[atomicAdd(&ncand, 1)] = composite(u[i], idx_of(i));
+      if (u[i]) {
+        const int b = vbin_with(u[i], fmin2, scale2);
+        if (b > T) mark(idx_of(i));
+        else if (b == T) cand[atomicAdd(&ncand, 1)] = composite(u[i], idx_of(i));
+      }
     __syncthreads();
     if (tid < nT) {
       const uint64_t c = cand[tid];
       int rank = 0;
       for (int j = 0; j < nT; ++j) rank += cand[j] > c;
-      if (rank == need - 1) cthr = c;  // composites are distinct
+      if (rank < need) mark((int)~(uint32_t)c);  // composites are distinct
     }
-    __syncthreads();
-    thr = cthr;
   } else {
     uint64_t prefix = 0, pmask = 0;
     for (int pass = 0; pass < 8; ++pass) {
@@ -392,7 +387,8 @@ __global__ __launch_bounds__(256) void topk_rows_prefill_kernel(const float* __r
 #pragma unroll
       for (int i = 0; i < MAXIT; ++i) {
         const uint64_t c = composite(u[i], idx_of(i));
-        if (u[i] && in_t(u[i]) && (c & pmask) == prefix) atomicAdd(&hist[(c >> shift) & 255], 1);
+        if (u[i] && vbin_with(u[i], fmin2, scale2) == T && (c & pmask) == prefix)
+          atomicAdd(&hist[(c >> shift) & 255], 1);
       }
       __syncthreads();
       bin_threshold<256>(hist, need, tmp, res);
@@ -400,16 +396,19 @@ __global__ __launch_bounds__(256) void topk_rows_prefill_kernel(const float* __r
       prefix |= (uint64_t)res[0] << shift;
       pmask |= (uint64_t)0xff << shift;
     }
-    thr = prefix;
+    const uint64_t thr = prefix;  // the need-th largest composite of bin T
+#pragma unroll
+    for (int i = 0; i < MAXIT; ++i) {
+      uint32_t ui = u[i];
+      asm volatile("" : "+v"(ui));  // recomputed here, not held from the passes above
+      if (ui) {
+        const int b = vbin_with(ui, fmin2, scale2);
+        if (b > T || (b == T && composite(ui, idx_of(i)) >= thr)) mark(idx_of(i));
+      }
+    }
   }
 
-  // 3. winners -> bitmap -> ascending indices
-#pragma unroll
-  for (int i = 0; i < MAXIT; ++i)
-    if (u[i] && composite(u[i], idx_of(i)) >= thr) {
-      const int e = idx_of(i);
-      atomicOr(&bits[e >> 5], 1u << (e & 31));
-    }
+  // 3. bitmap -> ascending indices
   __syncthreads();
   const int W = (v + 31) / 32;
   const int WPT = (W + 255) / 256;
@@ -540,7 +539,7 @@ __global__ __launch_bounds__(256) void dec_score_kernel(
       for (int g = 0; g < NG; ++g) mma16<T>(acc, qa[g], src[u][g]);
       float p = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p += wv[i] * fmaxf(acc[i], 0.f);
+      for (int i = 0; i < 4; ++i) p += wv[i] * relu(acc[i]);
       p = xlane_sum(p);
       const int64_t s = s0 + u * 16 + (lane & 15);
       if (lg == 0 && s < w1) {

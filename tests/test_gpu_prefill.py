@@ -99,6 +99,33 @@ def test_index_topk_exact_ties_break_to_smaller_index(lib):
         assert sorted(got[t, :kt].tolist()) == sorted(ref[t, :kt].tolist()), f"row {t}"
 
 
+def test_index_topk_wide_tie_bin(lib):
+    """Rows whose threshold bin holds more than 256 equal scores (two score
+    levels, the lower one shared by two thirds of the entries): the bin is
+    resolved by the radix path and ties must go to the smaller index."""
+    _say("index wide tie bin")
+    n, hI, cI, m, k = 2048, 4, 64, 4, 300
+    g = torch.Generator(device="cpu").manual_seed(11)
+    qI = torch.randint(0, 2, (n, hI, cI), generator=g).float()
+    ne = n // m
+    KI = torch.zeros(ne, cI)
+    KI[::3] = 1.0  # every third entry scores sum_h w_h * (q_h . 1), the rest 0
+    wI = torch.rand(n, hI, generator=g)
+    idx = lib.csa_index_topk_prefill(qI.to(DEV), wI.to(DEV), KI.to(DEV), m, k)
+    torch.cuda.synchronize()
+    sc = O.index_scores(qI.double().numpy(), wI.double().numpy(), KI.double().numpy(), m)
+    ref = O.topk(sc, k, m)
+    got = idx.cpu().numpy()
+    wide = 0
+    for t in range(n):
+        kt = min(k, (t + 1) // m)
+        assert sorted(got[t, :kt].tolist()) == sorted(ref[t, :kt].tolist()), f"row {t}"
+        assert (got[t, kt:] == -1).all()
+        v = (t + 1) // m
+        wide += v > k and (v - (v + 2) // 3) > 256
+    assert wide > 100  # rows that take the radix path
+
+
 # --------------------------------------------------------------- attention
 def _rand_idx(n, k, m, ne, key, pad_frac=0.1):
     """Random distinct visible entries per row (k_t = min(k, visible)), then -1."""
