@@ -215,6 +215,7 @@ class HybridDecode:
         self.sti = torch.empty(L.csa_state_bytes(dsi) // 4, dtype=torch.float32, device=device)
         self.sth = torch.empty(L.csa_state_bytes(dsh) // 4, dtype=torch.float32, device=device)
         self.idx = torch.empty((B, cfg["k"]), dtype=torch.int32, device=device)
+        self.side = None  # side streams of the decode step, made on first use
         self.out_c = torch.empty((B, nh, c), dtype=dt, device=device)
         self.out_h = torch.empty((B, nh, c), dtype=dt, device=device)
         # build the caches: prefill of tokens [0, t) for every sequence
@@ -242,21 +243,43 @@ class HybridDecode:
             L._WS.pop(key)
         torch.cuda.empty_cache()
 
-    def step(self):
+    def step(self, streams=True):
+        """One decode step.  Its three chains are independent until the sparse
+        attention: (CSA compressor), (indexer compressor -> top-k) and (HCA
+        compressor -> dense attention); with `streams` they run on the current
+        stream and two forked side streams (default priority), joined back
+        before the step ends, so their small launches overlap on the GPU.
+        Each chain has its own workspaces."""
         c, g = self.cfg, self.g
         m, ov, r = c["m"], c["overlap"], c["rope_dims"]
+        main = torch.cuda.current_stream()
+        if streams:
+            if self.side is None:
+                self.side = (torch.cuda.Stream(), torch.cuda.Stream())
+            sb, sc = self.side
+            sb.wait_stream(main)
+            sc.wait_stream(main)
+        else:
+            sb = sc = main
+        with torch.cuda.stream(sb):
+            L.csa_compress_decode(self.h, self.pos, g["WI_kv"], g["WI_z"], g["apeI"], m, ov, self.sti,
+                                  self.kcache, ws_slot="decode_proj_idx")
+            L.csa_index_topk_decode(g["qI"], g["wI"], self.kcache, self.pos, m, c["k"], out=self.idx)
+        with torch.cuda.stream(sc):
+            L.csa_compress_decode(self.h, self.pos, g["hca_Wkv"], g["hca_Wz"], g["hca_ape"],
+                                  c["m_hca"], 0, self.sth, self.hcache, W_win=g["hca_Wwin"],
+                                  win_ring=self.hring, rope_dims=r, ws_slot="decode_proj_hca")
+            L.hca_dense_mqa_decode(g["hca_q"], self.hring, self.hcache, self.pos, g["hca_sink"],
+                                   c["m_hca"], rope_dims=r, out=self.out_h)
         L.csa_compress_decode(self.h, self.pos, g["csa_Wkv"], g["csa_Wz"], g["csa_ape"], m, ov,
-                              self.st, self.cache, W_win=g["csa_Wwin"], win_ring=self.ring, rope_dims=r)
-        L.csa_compress_decode(self.h, self.pos, g["WI_kv"], g["WI_z"], g["apeI"], m, ov, self.sti,
-                              self.kcache)
-        L.csa_compress_decode(self.h, self.pos, g["hca_Wkv"], g["hca_Wz"], g["hca_ape"], c["m_hca"], 0,
-                              self.sth, self.hcache, W_win=g["hca_Wwin"], win_ring=self.hring,
-                              rope_dims=r)
-        L.csa_index_topk_decode(g["qI"], g["wI"], self.kcache, self.pos, m, c["k"], out=self.idx)
+                              self.st, self.cache, W_win=g["csa_Wwin"], win_ring=self.ring, rope_dims=r,
+                              ws_slot="decode_proj_csa")
+        if streams:
+            main.wait_stream(sb)
         L.csa_sparse_mqa_decode(g["csa_q"], self.ring, self.cache, self.idx, self.pos, g["csa_sink"],
                                 rope_dims=r, out=self.out_c)
-        L.hca_dense_mqa_decode(g["hca_q"], self.hring, self.hcache, self.pos, g["hca_sink"], c["m_hca"],
-                               rope_dims=r, out=self.out_h)
+        if streams:
+            main.wait_stream(sc)
 
     def algorithmic_bytes(self):
         """Bytes a decode step must move at least once (bf16 = 2 B)."""

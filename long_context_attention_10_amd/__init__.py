@@ -199,9 +199,12 @@ def csa_compress_prefill(H, W_kv, W_z, ape, m, overlap, W_win=None, qk_norm=True
 
 
 def csa_compress_decode(h, pos, W_kv, W_z, ape, m, overlap, state, cache, W_win=None,
-                        win_ring=None, qk_norm=True, eps=1e-6, rope_dims=0, rope_theta=10000.0):
+                        win_ring=None, qk_norm=True, eps=1e-6, rope_dims=0, rope_theta=10000.0,
+                        ws_slot="decode_proj"):
     """One new token per sequence: h [B, d], pos [B] int64; updates state,
-    cache [B, max_entries, c] (on emission) and win_ring [B, n_win, c]."""
+    cache [B, max_entries, c] (on emission) and win_ring [B, n_win, c].
+    Calls that may run at the same time on different streams need distinct
+    `ws_slot` names (each names its own cached workspace)."""
     lib = load()
     B, d = h.shape
     w = W_kv.shape[0]
@@ -214,7 +217,7 @@ def csa_compress_decode(h, pos, W_kv, W_z, ape, m, overlap, state, cache, W_win=
                          max_entries=cache.shape[1])
     if state.numel() * 4 < csa_state_bytes(desc):
         raise CsaError("state too small")
-    ws, wsb = workspace(workspace_bytes("compress_decode", desc), h.device, "decode_proj")
+    ws, wsb = workspace(workspace_bytes("compress_decode", desc), h.device, ws_slot)
     st = lib.csa_compress_decode(ctypes.byref(desc), _ptr(h), _ptr(pos), _ptr(W_kv), _ptr(W_z),
                                  _ptr(ape), _ptr(W_win), _ptr(state), _ptr(cache), _ptr(win_ring),
                                  _ptr(ws), wsb, _stream(h.device))
