@@ -165,9 +165,11 @@ def csa_state_init(desc, state: torch.Tensor):
 def csa_compress_prefill(H, W_kv, W_z, ape, m, overlap, W_win=None, qk_norm=True, eps=1e-6,
                          rope_dims=0, rope_theta=10000.0, n_win=128, want_win=True,
                          want_ring=False, want_state=False, out_comp=None, out_win=None,
-                         win_ring=None, state=None):
+                         win_ring=None, state=None, ws_slot="default"):
     """Compressed entries (and window rows / ring / decode state) of one
-    sequence H [n, d].  Weights are output-major [(1+ov)c, d]."""
+    sequence H [n, d].  Weights are output-major [(1+ov)c, d].  Calls that
+    may run at the same time on different streams need distinct `ws_slot`
+    names (each names its own cached workspace)."""
     lib = load()
     n, d = H.shape
     w = W_kv.shape[0]
@@ -189,7 +191,7 @@ def csa_compress_prefill(H, W_kv, W_z, ape, m, overlap, W_win=None, qk_norm=True
             win_ring = torch.empty((n_win, c), dtype=H.dtype, device=dev)
     if want_state and state is None:
         state = torch.empty(csa_state_bytes(desc) // 4, dtype=torch.float32, device=dev)
-    ws, wsb = workspace(workspace_bytes("compress_prefill", desc), dev)
+    ws, wsb = workspace(workspace_bytes("compress_prefill", desc), dev, ws_slot)
     st = lib.csa_compress_prefill(ctypes.byref(desc), _ptr(H), _ptr(W_kv), _ptr(W_z), _ptr(ape),
                                   _ptr(W_win), _ptr(out_comp) if out_comp.numel() else None,
                                   _ptr(out_win), _ptr(win_ring), _ptr(state), _ptr(ws), wsb,
