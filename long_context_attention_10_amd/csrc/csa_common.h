@@ -145,6 +145,14 @@ CSA_DEV float swap32_add(float v) {
   return __uint_as_float(a[0]) + __uint_as_float(a[1]);
 }
 
+// Two half-wave sums in one swap: lanes 0-31 get a + a[lane + 32], lanes
+// 32-63 get b[lane - 32] + b (v_permlane32_swap exchanges the upper half of
+// its first operand with the lower half of its second).
+CSA_DEV float swap32_pair_add(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Order-preserving map fp32 -> uint32 (larger float -> larger key).
 CSA_DEV uint32_t float_key(float f) {
   uint32_t u = __float_as_uint(f);

@@ -88,18 +88,21 @@ __global__ __launch_bounds__(256) void index_scores_prefill_kernel(
   }
   // per stored query: its visible-entry count (0 past the last token), so the
   // causal test in the loop is one compare
-  int64_t vis[RB][4];
+  int vis[RB][4];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int64_t tb = q0 + (wave * (RB * 32) + rb * 32) / HI;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int64_t t = HI == 4 ? tb + 2 * j + hl : HI == 8 ? tb + 2 * hl + (j & 1) : tb + hl;
-      vis[rb][j] = t < n ? (t + 1) / m : 0;
+      vis[rb][j] = t < n ? (int)((t + 1) / m) : 0;
     }
   }
   wait_vmem();
   __syncthreads();
+  // rows of this workgroup's queries: one uniform base, 32-bit offsets
+  float* srow0 = scores + q0 * ld;
+  const int ld32 = (int)ld;
 
   const int nblk = (int)((kend - kbeg + KB - 1) / KB);
   for (int bi = 0; bi < nblk; ++bi) {
@@ -119,8 +122,8 @@ __global__ __launch_bounds__(256) void index_scores_prefill_kernel(
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) mma32<T>(acc[rb], qa[rb][g], kb);
       }
-      const int64_t s = kb0 + kk;
-      const bool sok = s < kend;
+      const int si = (int)(kb0 + kk);  // entry index (< 2^31)
+      const bool sok = si < kend;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         float part[4];
@@ -131,27 +134,21 @@ __global__ __launch_bounds__(256) void index_scores_prefill_kernel(
           for (int r = 0; r < 4; ++r) p += wv[rb][gq * 4 + r] * relu(acc[rb][gq * 4 + r]);
           part[gq] = p;
         }
-        const int64_t tb = q0 + (wave * (RB * 32) + rb * 32) / HI;  // first query of this block
+        // rows of this block's first query relative to the workgroup's first
+        const int tr = (wave * (RB * 32) + rb * 32) / HI;
+        auto put = [&](int tq, int vq, float v) {  // query q0 + tq, visible count vq
+          if (sok && si < vq) srow0[(uint32_t)(tq * ld32 + si)] = v;
+        };
         if (HI == 4) {  // each group of 4 rows is one whole query
 #pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const int64_t t = tb + 2 * gq + hl;
-            if (sok && s < vis[rb][gq]) scores[t * ld + s] = part[gq];
-          }
-        } else if (HI == 8) {
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq) part[gq] = swap32_add(part[gq]);
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int gq = 2 * hl + u;
-            const int64_t t = tb + gq;
-            const float v = gq == 0 ? part[0] : gq == 1 ? part[1] : gq == 2 ? part[2] : part[3];
-            if (sok && s < vis[rb][u]) scores[t * ld + s] = v;
-          }
-        } else {  // HI == 16: rows 0-15 query 0, rows 16-31 query 1
-          const float p0 = swap32_add(part[0] + part[1]), p1 = swap32_add(part[2] + part[3]);
-          const int64_t t = tb + hl;
-          if (sok && s < vis[rb][0]) scores[t * ld + s] = hl ? p1 : p0;
+          for (int gq = 0; gq < 4; ++gq) put(tr + 2 * gq + hl, vis[rb][gq], part[gq]);
+        } else if (HI == 8) {  // rows 8q..8q+7 are query q; lanes < 32 keep 0, 1, the rest 2, 3
+          const float v0 = swap32_pair_add(part[0], part[2]);
+          const float v1 = swap32_pair_add(part[1], part[3]);
+          put(tr + 2 * hl, vis[rb][0], v0);
+          put(tr + 2 * hl + 1, vis[rb][1], v1);
+        } else {  // HI == 16: rows 0-15 query 0 (lanes < 32), rows 16-31 query 1
+          put(tr + hl, vis[rb][0], swap32_pair_add(part[0] + part[1], part[2] + part[3]));
         }
       }
     }
@@ -812,6 +809,8 @@ hipError_t launch_index_scores_prefill(const csa_index_desc& d, const void* qI, 
   if (nvis == 0) return hipSuccess;
   CSA_INDEX_DISPATCH(d.n_heads, d.head_dim, {
     constexpr int TQ = 256 / HI;
+    // the kernel addresses a workgroup's TQ score rows with 32-bit offsets
+    if ((int64_t)TQ * ld >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     dim3 grid((unsigned)((d.n + TQ - 1) / TQ), (unsigned)((nvis + key_chunk - 1) / key_chunk));
     if (d.dtype == CSA_BF16)
       index_scores_prefill_kernel<BF16, HI, CI><<<grid, 256, 0, st>>>(
