@@ -275,7 +275,8 @@ template <int MAXIT>
 __global__ __launch_bounds__(256) void topk_rows_prefill_kernel(const float* __restrict__ scores,
                                                                 int64_t ld, int64_t n,
                                                                 int64_t n_entries, int m, int k,
-                                                                int32_t* __restrict__ idx_out) {
+                                                                int32_t* __restrict__ idx_out,
+                                                                int64_t row0) {
   constexpr int NQ = MAXIT / 4;  // 4-entry groups per thread
   __shared__ int hist[kSelBins];
   __shared__ uint32_t bits[MAXIT * 256 / 32];
@@ -284,7 +285,7 @@ __global__ __launch_bounds__(256) void topk_rows_prefill_kernel(const float* __r
   __shared__ int res[2];
   __shared__ uint32_t red[8];
   __shared__ int ncand;
-  const int t = (int)blockIdx.x;
+  const int t = (int)(row0 + blockIdx.x);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int v = (int)min64((int64_t)(t + 1) / m, n_entries);
   const int kt = min(k, v);
@@ -824,10 +825,30 @@ hipError_t launch_index_scores_prefill(const csa_index_desc& d, const void* qI, 
   return hipGetLastError();
 }
 
+// Rows are launched in bands by their visible-entry count (it grows with t):
+// each band's kernel holds 16, 32, 48 or 64 entries per thread, so short rows do
+// not pay for the longest one's registers and loops.
 hipError_t launch_topk_rows_prefill(const csa_index_desc& d, const float* scores, int64_t ld,
                                     int32_t* idx_out, hipStream_t st) {
-  topk_rows_prefill_kernel<64><<<(unsigned)d.n, 256, 0, st>>>(scores, ld, d.n, d.n_entries, d.m,
-                                                               d.k, idx_out);
+  // first row whose visible count exceeds `cap` entries
+  auto band_end = [&](int64_t cap) {
+    if (d.n_entries <= cap) return d.n;
+    const int64_t e = (cap + 1) * d.m - 1;
+    return e < d.n ? e : d.n;
+  };
+  const int64_t e16 = band_end(16 * 256), e32 = band_end(32 * 256), e48 = band_end(48 * 256);
+  if (e16 > 0)
+    topk_rows_prefill_kernel<16><<<(unsigned)e16, 256, 0, st>>>(scores, ld, d.n, d.n_entries,
+                                                                 d.m, d.k, idx_out, 0);
+  if (e32 > e16)
+    topk_rows_prefill_kernel<32><<<(unsigned)(e32 - e16), 256, 0, st>>>(
+        scores, ld, d.n, d.n_entries, d.m, d.k, idx_out, e16);
+  if (e48 > e32)
+    topk_rows_prefill_kernel<48><<<(unsigned)(e48 - e32), 256, 0, st>>>(
+        scores, ld, d.n, d.n_entries, d.m, d.k, idx_out, e32);
+  if (d.n > e48)
+    topk_rows_prefill_kernel<64><<<(unsigned)(d.n - e48), 256, 0, st>>>(
+        scores, ld, d.n, d.n_entries, d.m, d.k, idx_out, e48);
   return hipGetLastError();
 }
 
