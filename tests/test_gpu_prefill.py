@@ -33,6 +33,7 @@ def _say(*a):
     ("bf16", 1030, 256, 512, 4, 1, 64),    # overlapped CSA with partial RoPE
     ("bf16", 300, 192, 256, 8, 1, 32),
     ("bf16", 3, 128, 128, 4, 1, 0),        # fewer tokens than one block
+    ("bf16", 520, 64, 128, 4, 1, 32),      # d = 64: the GEMM's two-slice K loop
 ])
 def test_compress_prefill(lib, dtype, n, d, c, m, ov, r):
     _say("compress_prefill", dtype, n, d, c, m, ov, r)
@@ -78,6 +79,25 @@ def test_index_topk_prefill(lib, dtype, n, hI, cI, m, k):
     sc = O.index_scores(f64(qI), f64(wI), f64(KI), m)
     ties = check_topk_sets(idx.cpu().numpy(), sc, k, m)
     assert ties <= max(2, n // 100)
+
+
+def test_index_topk_row_bands(lib):
+    """Rows on both sides of the top-k launch's row-band edges (visible
+    counts 4096, 8192, 12288; m = 1 so that the token index is the count),
+    on sampled rows against the oracle."""
+    n, hI, cI, m, k = 12400, 16, 64, 1, 512
+    _say("index row bands", n)
+    key = ("index-bands", n)
+    qI = I.normal((n, hI, cI), key + ("q",), dtype="bf16", device=DEV)
+    wI = I.uniform((n, hI), key + ("w",), dtype="bf16", device=DEV)
+    KI = I.normal((n, cI), key + ("K",), dtype="bf16", device=DEV)
+    idx = lib.csa_index_topk_prefill(qI, wI, KI, m, k).cpu().numpy()
+    torch.cuda.synchronize()
+    rows = [0, 510, 511, 512, 4094, 4095, 4096, 8190, 8191, 8192, 12286, 12287, 12288, n - 1]
+    KIh = f64(KI)
+    for t in rows:
+        sc = O.index_scores(f64(qI[t])[None], f64(wI[t])[None], KIh[: (t + 1) // m], m, t0=t)
+        check_topk_sets(idx[t][None], sc, k, m, t0=t)
 
 
 def test_index_topk_exact_ties_break_to_smaller_index(lib):
