@@ -209,13 +209,12 @@ CSA_DEV void find_digit(const int* hist, int need, int* out) {
 // res = (T, #items above T).  `h` holds NB bins (global memory or LDS), `sh`
 // is LDS scratch of 4 ints; 256 threads.
 template <int NB>
-CSA_DEV void bin_threshold(const int* __restrict__ h, int need, int* sh, int* res) {
+CSA_DEV void bin_threshold_vals(const int (&loc)[NB / 256], int need, int* sh, int* res) {
   constexpr int PER = NB / 256;  // consecutive bins per thread
   const int tid = threadIdx.x;
-  int loc[PER];
   int cs = 0;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) { loc[i] = h[tid * PER + i]; cs += loc[i]; }
+  for (int i = 0; i < PER; ++i) cs += loc[i];
   // inclusive suffix sum over threads
   const int lane = tid & 63, wave = tid >> 6;
   int suf = cs;
@@ -241,9 +240,14 @@ CSA_DEV void bin_threshold(const int* __restrict__ h, int need, int* sh, int* re
   __syncthreads();
 }
 
-CSA_DEV void coarse_threshold(const int* __restrict__ h, int nb, int need, int* sh, int* res) {
-  bin_threshold<2048>(h, need, sh, res);
+template <int NB>
+CSA_DEV void bin_threshold(const int* __restrict__ h, int need, int* sh, int* res) {
+  int loc[NB / 256];
+#pragma unroll
+  for (int i = 0; i < NB / 256; ++i) loc[i] = h[threadIdx.x * (NB / 256) + i];
+  bin_threshold_vals<NB>(loc, need, sh, res);
 }
+
 
 // ===========================================================================
 // Prefill row selection: one workgroup per query row over its v <= 16384
@@ -427,67 +431,80 @@ __global__ __launch_bounds__(256) void topk_rows_prefill_kernel(const float* __r
 
 // ===========================================================================
 // Decode: one query per sequence over up to ~10^6 cached keys.
-//   D0 clear histograms/counters;
+//   D0 clear the histograms;
 //   D1 score chunks of keys (16x16 matrix-core tiles, keys streamed straight
 //      from memory -- this pass moves the step's dominant bytes) and build a
-//      2048-bin histogram of the keys' top 11 bits;
-//   D2 per chunk: find the coarse threshold bin T and histogram the next 11
-//      bits of the keys in T;
-//   D3 per chunk: with the 22-bit threshold prefix P known, append entries
-//      above P to the "sure" list and entries equal to P to the tie list;
-//   D4 per sequence: resolve the tie list exactly on (score, -index), merge,
-//      emit ascending indices through a bitmap.
-// Counts use integer atomics (order-independent), and the final ordering
-// makes the output independent of the order in which lists were filled.
+//      2048-bin histogram of the keys' top 11 bits, added into one of R
+//      copies per sequence (chunk mod R, R = chunks / 32 clamped to [1, 8]):
+//      atomics on one cache line are serialised, so at most ~32 workgroups
+//      add into the same lines;
+//   D2 per chunk: find the coarse threshold bin T of the k-th key from the
+//      summed copies (scanning down from the top bin), then store the
+//      chunk's entries of bins above T (the "sure" entries) at the front of
+//      the chunk's own slice of the list buffer and those of T (the ties) at
+//      its back, with the two counts per chunk -- no atomics;
+//   D3 per sequence: gather the chunks' lists, resolve the ties exactly on
+//      (score, -index) from their fine histogram (a radix select over the
+//      whole tie list when the fine bin is crowded), and merge the two
+//      ascending lists into the output row.
+// Nothing depends on the order in which workgroups run.
 // ===========================================================================
 constexpr int kDecChunk = 1024;    // keys per scoring workgroup
 constexpr int kCoarseBins = 2048;  // top 11 bits
-constexpr int kFineBins = 2048;    // next 11 bits
-constexpr int kBitmapEntries = 262144;  // index spaces sorted through an LDS bitmap
+constexpr int kHistCopies = 8;     // most histogram copies per sequence
+constexpr int kChunkLds = 1024;    // chunk counts staged in LDS by the finalize
+constexpr int kTieLds = 6144;      // tie candidates resolved in LDS
 
 struct DecWs {  // carve-up of the decode workspace
-  float* scores;      // [B][n_entries]
-  int* hist;          // [B][kCoarseBins]
-  int* fine;          // [B][kFineBins]
-  int* cnt;           // [B][4]: sure count, tie count, unused x2
-  int32_t* sure;      // [B][k]
-  uint2* ties;        // [B][n_entries] (key, index)
+  float* scores;  // [B][n_entries]
+  int* hist;      // [B][copies][kCoarseBins], then fine [B][kCoarseBins] (tie bits 20..10)
+  int* fine;
+  int2* ccnt;     // [B][chunks]: (sure, tie) counts per chunk
+  uint2* lists;   // [B][n_entries] (key, index): chunk slices, sure first, ties last
+  uint2* flat;    // [B][n_entries]: tie lists too long for LDS, contiguous
 };
 
 static size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
+static int64_t dec_chunks(const csa_index_desc& d) {
+  return (d.n_entries + kDecChunk - 1) / kDecChunk;
+}
+
+static int dec_hist_copies(int64_t nchunks) {
+  return nchunks >= 32 * kHistCopies ? kHistCopies : nchunks >= 64 ? (int)(nchunks / 32) : 1;
+}
+
 static DecWs carve(void* ws, const csa_index_desc& d) {
   uint8_t* p = (uint8_t*)ws;
   DecWs w;
-  const size_t B = d.batch, ne = d.n_entries;
+  const size_t B = d.batch, ne = d.n_entries, nc = dec_chunks(d);
   w.scores = (float*)p; p += align_up(B * ne * 4);
-  w.hist = (int*)p; p += align_up(B * kCoarseBins * 4);
-  w.fine = (int*)p; p += align_up(B * kFineBins * 4);
-  w.cnt = (int*)p; p += align_up(B * 4 * 4);
-  w.sure = (int32_t*)p; p += align_up(B * (size_t)d.k * 4);
-  w.ties = (uint2*)p; p += align_up(B * ne * 8);
+  w.hist = (int*)p;
+  w.fine = w.hist + B * dec_hist_copies(nc) * kCoarseBins;
+  p += align_up(B * (dec_hist_copies(nc) + 1) * kCoarseBins * 4);
+  w.ccnt = (int2*)p; p += align_up(B * nc * 8);
+  w.lists = (uint2*)p; p += align_up(B * ne * 8);
+  w.flat = (uint2*)p; p += align_up(B * ne * 8);
   return w;
 }
 
 size_t index_decode_ws_bytes(const csa_index_desc& d) {
-  const size_t B = d.batch, ne = d.n_entries;
-  return align_up(B * ne * 4) + align_up(B * kCoarseBins * 4) + align_up(B * kFineBins * 4) +
-         align_up(B * 16) + align_up(B * (size_t)d.k * 4) + align_up(B * ne * 8);
+  const size_t B = d.batch, ne = d.n_entries, nc = dec_chunks(d);
+  return align_up(B * ne * 4) + align_up(B * (dec_hist_copies(nc) + 1) * kCoarseBins * 4) +
+         align_up(B * nc * 8) + 2 * align_up(B * ne * 8);
 }
 
-__global__ void dec_clear_kernel(int* hist, int* fine, int* cnt, int B) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < B * kCoarseBins; i += gridDim.x * blockDim.x) {
-    hist[i] = 0;
-    fine[i] = 0;
-  }
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < B * 4; i += gridDim.x * blockDim.x) cnt[i] = 0;
+__global__ void dec_clear_kernel(int4* __restrict__ hist, int64_t n4) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4;
+       i += (int64_t)gridDim.x * blockDim.x)
+    hist[i] = make_int4(0, 0, 0, 0);
 }
 
 template <class T, int HI, int CI>
 __global__ __launch_bounds__(256) void dec_score_kernel(
     const typename T::S* __restrict__ qI, const typename T::S* __restrict__ wI,
     const typename T::S* __restrict__ KI, const int64_t* __restrict__ posv, int64_t n_entries,
-    int m, int k, float* __restrict__ scores, int* __restrict__ hist) {
+    int m, int k, float* __restrict__ scores, int* __restrict__ hist, int ncopies) {
   typedef typename T::S S;
   constexpr int E = 16 / (int)sizeof(S);
   constexpr int KGE = 4 * E;      // elements per 16x16 k-group
@@ -557,55 +574,60 @@ __global__ __launch_bounds__(256) void dec_score_kernel(
     score64(s0 + 64, kc);
   }
   __syncthreads();
+  int* gh = hist + ((int64_t)b * ncopies + blockIdx.x % ncopies) * kCoarseBins;
   for (int i = tid; i < kCoarseBins; i += 256)
-    if (lh[i]) atomicAdd(&hist[(int64_t)b * kCoarseBins + i], lh[i]);
+    if (lh[i]) atomicAdd(&gh[i], lh[i]);
 }
 
-
-// Second histogram level: entries in the coarse threshold bin T are counted by
-// the next 11 bits of their key.
-__global__ __launch_bounds__(256) void dec_refine_kernel(const int64_t* __restrict__ posv,
-                                                         int64_t n_entries, int m, int k,
-                                                         const float* __restrict__ scores,
-                                                         const int* __restrict__ hist,
-                                                         int* __restrict__ fine) {
-  __shared__ int sh[8];
-  __shared__ int res[2];
-  __shared__ int lf[kFineBins];
-  const int b = blockIdx.y;
-  const int64_t vis = min64((posv[b] + 1) / m, n_entries);
-  if (vis <= k) return;
-  const int64_t c0 = (int64_t)blockIdx.x * kDecChunk;
-  if (c0 >= vis) return;
-  const int64_t c1 = min64(c0 + kDecChunk, vis);
-  const int tid = threadIdx.x;
-  for (int i = tid; i < kFineBins; i += 256) lf[i] = 0;
-  coarse_threshold(hist + (int64_t)b * kCoarseBins, kCoarseBins, k, sh, res);
-  const uint32_t T = (uint32_t)res[0];
-  const float* sc = scores + (int64_t)b * n_entries;
-  for (int64_t s = c0 + tid; s < c1; s += 256) {
-    const uint32_t key = float_key(sc[s]);
-    if ((key >> 21) == T) atomicAdd(&lf[(key >> 10) & (kFineBins - 1)], 1);
+// The coarse threshold bin T of the `need`-th largest key from a sequence's
+// histogram copies: blocks of 256 bins are summed over the copies from the
+// top bin down until they hold `need` keys.  Every thread gets res = (T,
+// #keys in bins above T).  Requires at least `need` keys in the histogram.
+CSA_DEV void dec_threshold(const int* __restrict__ h, int ncopies, int need, int* sh, int* res) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int above = 0;
+  for (int blk = kCoarseBins / 256 - 1; blk >= 0; --blk) {
+    const int bin = blk * 256 + tid;
+    int v[kHistCopies];
+#pragma unroll
+    for (int r = 0; r < kHistCopies; ++r) v[r] = r < ncopies ? h[r * kCoarseBins + bin] : 0;
+    int c = 0;
+#pragma unroll
+    for (int r = 0; r < kHistCopies; ++r) c += v[r];
+    int suf = c;  // inclusive suffix sum over the wave's lanes
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_down(suf, o, 64);
+      if (lane + o < 64) suf += y;
+    }
+    __syncthreads();
+    if (lane == 0) sh[wave] = suf;
+    __syncthreads();
+    for (int w = wave + 1; w < 4; ++w) suf += sh[w];
+    const int tot = sh[0] + sh[1] + sh[2] + sh[3];
+    if (above + suf >= need && above + suf - c < need) {
+      res[0] = bin;
+      res[1] = above + suf - c;
+    }
+    if (above + tot >= need) break;  // uniform
+    above += tot;
   }
   __syncthreads();
-  for (int i = tid; i < kFineBins; i += 256)
-    if (lf[i]) atomicAdd(&fine[(int64_t)b * kFineBins + i], lf[i]);
 }
 
-// With the 22-bit threshold prefix P of the k-th key known from both
-// histogram levels, every entry whose prefix is above P is in the top k (the
-// "sure" list) and those equal to P are the final candidates (the tie list).
-// Each thread classifies a contiguous run of entries; one block-wide prefix
-// sum per list turns its counts into positions, so a workgroup makes a single
-// atomic reservation per list.
+// D2: classify a chunk against T.  Thread j owns entries c0 + PER*j + u; one
+// block-wide prefix sum per list gives each entry its slot in the chunk's
+// slice of `lists` (sure from the front, ties from the back, both in index
+// order).  Ties are also counted by their next 11 key bits (the fine
+// histogram; few per chunk, spread over the bins).
 __global__ __launch_bounds__(256) void dec_collect_kernel(const int64_t* __restrict__ posv,
                                                           int64_t n_entries, int m, int k,
                                                           const float* __restrict__ scores,
                                                           const int* __restrict__ hist,
-                                                          const int* __restrict__ fine,
-                                                          int* __restrict__ cnt,
-                                                          int32_t* __restrict__ sure,
-                                                          uint2* __restrict__ ties) {
+                                                          int* __restrict__ fine,
+                                                          int2* __restrict__ ccnt,
+                                                          uint2* __restrict__ lists,
+                                                          int64_t nchunks, int ncopies) {
   __shared__ int sh[8];
   __shared__ int res[2];
   const int b = blockIdx.y;
@@ -615,40 +637,44 @@ __global__ __launch_bounds__(256) void dec_collect_kernel(const int64_t* __restr
   if (c0 >= vis) return;
   const int64_t c1 = min64(c0 + kDecChunk, vis);
   const int tid = threadIdx.x;
-  coarse_threshold(hist + (int64_t)b * kCoarseBins, kCoarseBins, k, sh, res);
-  const uint32_t T = (uint32_t)res[0];
-  const int above = res[1];
-  coarse_threshold(fine + (int64_t)b * kFineBins, kFineBins, k - above, sh, res);
-  const uint32_t P = (T << 11) | (uint32_t)res[0];
-  const float* sc = scores + (int64_t)b * n_entries;
   constexpr int PER = kDecChunk / 256;
+  const float* sc = scores + (int64_t)b * n_entries;
+  float v[PER];  // loads in flight during the threshold search
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int64_t s = c0 + tid * PER + u;
+    v[u] = s < c1 ? sc[s] : 0.f;
+  }
+  dec_threshold(hist + (int64_t)b * ncopies * kCoarseBins, ncopies, k, sh, res);
+  const uint32_t T = (uint32_t)res[0];
   uint32_t key[PER];
   int ns = 0, nt = 0;
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     const int64_t s = c0 + tid * PER + u;
-    key[u] = s < c1 ? float_key(sc[s]) : 0u;
-    const uint32_t pre = key[u] >> 10;
-    ns += (s < c1 && pre > P);
-    nt += (s < c1 && pre == P);
+    key[u] = float_key(v[u]);
+    const uint32_t bin = key[u] >> 21;
+    ns += (s < c1 && bin > T);
+    nt += (s < c1 && bin == T);
   }
   int totS, totT;
-  const int ps = block_excl_scan(ns, sh, &totS);
-  const int pt = block_excl_scan(nt, sh + 4, &totT);
-  if (tid == 0) {
-    res[0] = totS ? atomicAdd(&cnt[b * 4 + 0], totS) : 0;
-    res[1] = totT ? atomicAdd(&cnt[b * 4 + 1], totT) : 0;
-  }
-  __syncthreads();
-  int os = res[0] + ps, ot = res[1] + pt;
+  int os = block_excl_scan(ns, sh, &totS);
+  int ot = block_excl_scan(nt, sh + 4, &totT);
+  const int cap = (int)(c1 - c0);
+  uint2* L = lists + (int64_t)b * n_entries + c0;
+  ot += cap - totT;
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     const int64_t s = c0 + tid * PER + u;
     if (s >= c1) continue;
-    const uint32_t pre = key[u] >> 10;
-    if (pre > P) sure[(int64_t)b * k + os++] = (int32_t)s;
-    else if (pre == P) ties[(int64_t)b * n_entries + ot++] = make_uint2(key[u], (uint32_t)s);
+    const uint32_t bin = key[u] >> 21;
+    if (bin > T) L[os++] = make_uint2(key[u], (uint32_t)s);
+    else if (bin == T) {
+      L[ot++] = make_uint2(key[u], (uint32_t)s);
+      atomicAdd(&fine[(int64_t)b * kCoarseBins + ((key[u] >> 10) & (kCoarseBins - 1))], 1);
+    }
   }
+  if (tid == 0) ccnt[(int64_t)b * nchunks + blockIdx.x] = make_int2(totS, totT);
 }
 
 // Radix selection over a list in global memory of `cnt` (key, index) pairs,
@@ -680,114 +706,228 @@ CSA_DEV void list_select(const uint2* __restrict__ L, int cnt, int need, int* hi
   *thr_lo = (uint32_t)prefix;
 }
 
+// The same selection over n <= kTieLds pairs held in LDS whose keys share
+// their top 11 bits (composite bits 63..53): digits of 8 bits from composite
+// bit 52 down (the last one 5 bits wide), stopping at the first digit whose
+// bucket is taken whole.
+CSA_DEV uint64_t lds_list_select(const uint2* L, int n, int need, int* hist, int* res) {
+  const int tid = threadIdx.x;
+  uint64_t pmask = ~0ull << 53;
+  uint64_t prefix = composite(L[0].x, L[0].y) & pmask;
+  for (int shift = 45;; shift = shift > 5 ? shift - 8 : 0) {
+    const uint32_t dmask = shift ? 255u : 31u;
+    hist[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += 256) {
+      const uint64_t ck = composite(L[i].x, L[i].y);
+      if ((ck & pmask) == prefix) atomicAdd(&hist[(ck >> shift) & dmask], 1);
+    }
+    __syncthreads();
+    find_digit(hist, need, res);
+    __syncthreads();
+    const int d = res[0];
+    need -= res[1];
+    prefix |= (uint64_t)d << shift;
+    pmask |= (uint64_t)dmask << shift;
+    const bool whole = hist[d] == need;  // uniform: LDS values after the barrier
+    __syncthreads();
+    if (whole || shift == 0) break;
+  }
+  return prefix;
+}
+
+// Position of v in the ascending list a[0, n): how many elements are below it.
+CSA_DEV int lower_rank(const int32_t* a, int n, int32_t v) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] < v) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+// Output positions of a contiguous run a[j0, j1) of one ascending list merged
+// with the ascending list o[0, no) (disjoint values): one binary search for the
+// first element, then a walk, since the ranks grow along the run.
+CSA_DEV void merge_run(const int32_t* a, int j0, int j1, const int32_t* o, int no,
+                       int32_t* __restrict__ out) {
+  if (j0 >= j1) return;
+  int r = lower_rank(o, no, a[j0]);
+  for (int j = j0; j < j1; ++j) {
+    const int32_t x = a[j];
+    while (r < no && o[r] < x) ++r;
+    out[j + r] = x;
+  }
+}
+
+// D3: one workgroup per sequence.  The chunks' sure entries and ties are
+// gathered in chunk order, so both lists are in ascending index order.  The
+// ties' fine histogram (bits 20..10 of the key, counted by D2) gives the fine
+// bin F holding the last winner: ties above F are taken, those in F are
+// ranked exactly (or, past 256 of them, the whole tie list is radix-selected);
+// the winners are compacted in order and merged with the sure list.
 __global__ __launch_bounds__(256) void dec_finalize_kernel(
     const int64_t* __restrict__ posv, int64_t n_entries, int m, int k,
-    const int* __restrict__ hist, const int* __restrict__ fine, const int* __restrict__ cnt,
-    const int32_t* __restrict__ sure, const uint2* __restrict__ ties,
-    int32_t* __restrict__ idx_out) {
+    const int* __restrict__ fine, const int2* __restrict__ ccnt, const uint2* __restrict__ lists,
+    uint2* __restrict__ flat, int64_t nchunks, int32_t* __restrict__ idx_out) {
   __shared__ int sh[8];
   __shared__ int res[2];
   __shared__ int h256[256];
-  __shared__ int32_t outv[2048];
-  __shared__ int ocount;
+  __shared__ int32_t surev[2048];
+  __shared__ int32_t tsel[2048];
+  __shared__ int ncand, ncand_f;
   __shared__ uint64_t fk[256];
   __shared__ uint64_t fk64_thr;
-  __shared__ uint32_t bm[kBitmapEntries / 32];
+  __shared__ uint2 tls[kTieLds];
+  __shared__ int2 ccs[kChunkLds];
+  __shared__ int slotS[2048];
+  __shared__ int slotT[kTieLds];
   const int b = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t vis = min64((posv[b] + 1) / m, n_entries);
   int32_t* orow = idx_out + (int64_t)b * k;
   if (vis <= k) {
     for (int j = tid; j < k; j += 256) orow[j] = j < vis ? j : -1;
     return;
   }
-  const int ns = cnt[b * 4 + 0];  // sure entries: k - need of them
-  const int nt = cnt[b * 4 + 1];  // final candidates sharing the threshold prefix
-  const int need = k - ns;        // >= 1 by the threshold construction
-  for (int j = tid; j < ns; j += 256) outv[j] = sure[(int64_t)b * k + j];
-  const uint2* tl = ties + (int64_t)b * n_entries;
+  // the ties' fine histogram, loaded now so that its latency overlaps the
+  // gather (thread j holds bins 8j .. 8j+7)
+  int fl[kCoarseBins / 256];
+  {
+    const int4* f4 = (const int4*)(fine + (int64_t)b * kCoarseBins) + 2 * tid;
+    const int4 x = f4[0], y = f4[1];
+    fl[0] = x.x; fl[1] = x.y; fl[2] = x.z; fl[3] = x.w;
+    fl[4] = y.x; fl[5] = y.y; fl[6] = y.z; fl[7] = y.w;
+  }
+  // gather: thread j takes a contiguous run of chunks and writes the slice
+  // slot of each of their entries into per-list slot tables in LDS (list
+  // position -> slot), then every thread fetches a share of the entries, so
+  // that the loads of many entries are in flight together
+  const int nch = (int)((vis + kDecChunk - 1) / kDecChunk);
+  const int CPT = (nch + 255) / 256;
+  const int ch0 = min(tid * CPT, nch), ch1 = min(ch0 + CPT, nch);
+  const int2* cg = ccnt + (int64_t)b * nchunks;
+  for (int c = tid; c < nch && c < kChunkLds; c += 256) ccs[c] = cg[c];
+  if (tid == 0) ncand = 0;
+  __syncthreads();
+  const int2* cc = nch <= kChunkLds ? ccs : cg;
+  int my_s = 0, my_t = 0;
+  for (int c = ch0; c < ch1; ++c) {
+    const int2 v = cc[c];
+    my_s += v.x;
+    my_t += v.y;
+  }
+  int ns, nt;
+  int ps = block_excl_scan(my_s, sh, &ns);
+  int pt = block_excl_scan(my_t, sh + 4, &nt);
+  const int need = k - ns;  // >= 1 by the threshold construction
+  const bool in_lds = nt <= kTieLds;
+  uint2* tdst = in_lds ? tls : flat + (int64_t)b * n_entries;
+  const uint2* lb = lists + (int64_t)b * n_entries;
+  for (int c = ch0; c < ch1; ++c) {
+    const int2 v = cc[c];
+    const int base = c * kDecChunk;
+    const int tb = base + (int)min64(kDecChunk, vis - base) - v.y;  // the chunk's ties
+    for (int i = 0; i < v.x; ++i) slotS[ps++] = base + i;
+    if (in_lds)
+      for (int i = 0; i < v.y; ++i) slotT[pt++] = tb + i;
+    else
+      for (int i = 0; i < v.y; ++i) tdst[pt++] = lb[tb + i];  // long lists: slow path
+  }
+  __syncthreads();
+  constexpr int U = 8;
+  for (int p0 = 0; p0 < ns; p0 += 256 * U) {
+    uint32_t e[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int p = p0 + u * 256 + tid;
+      e[u] = p < ns ? lb[slotS[p]].y : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int p = p0 + u * 256 + tid;
+      if (p < ns) surev[p] = (int32_t)e[u];
+    }
+  }
+  if (in_lds) {
+    for (int p0 = 0; p0 < nt; p0 += 256 * U) {
+      uint2 e[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int p = p0 + u * 256 + tid;
+        e[u] = p < nt ? lb[slotT[p]] : make_uint2(0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int p = p0 + u * 256 + tid;
+        if (p < nt) tls[p] = e[u];
+      }
+    }
+  }
+  // fine threshold bin F of the ties (the histogram holds exactly the nt ties)
+  bin_threshold_vals<kCoarseBins>(fl, need, sh, res);
+  const uint32_t F = (uint32_t)res[0];
+  const int need2 = need - res[1];  // winners among the ties of fine bin F (>= 1)
+  if (tid == (int)(F >> 3)) {
+    int v = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v = (int)(F & 7) == i ? fl[i] : v;
+    ncand_f = v;
+  }
+  __syncthreads();
+  const int nF = ncand_f;  // ties in fine bin F
+  const uint2* tl = tdst;
   // composite key (score key << 32 | ~index): larger is better, all distinct;
-  // thr = the need-th largest among the candidates (0 takes all of them)
-  uint64_t thr = 0;
-  if (nt > need && nt <= 256) {  // small set: rank every candidate directly
-    uint64_t ck = 0;
-    if (tid < nt) {
-      const uint2 e = tl[tid];
-      ck = ((uint64_t)e.x << 32) | (uint64_t)(~e.y);
-      fk[tid] = ck;
+  // thr = the need-th largest composite among the ties
+  uint64_t thr;
+  if (nF == need2) {  // fine bin F is taken whole
+    const uint32_t kf = (tl[0].x & ~0x1fffffu) | (F << 10);
+    thr = (uint64_t)kf << 32;
+  } else if (nF <= 256) {  // rank the ties of F directly
+    for (int i = tid; i < nt; i += 256) {
+      const uint2 e = tl[i];
+      if (((e.x >> 10) & (kCoarseBins - 1)) == F) fk[atomicAdd(&ncand, 1)] = composite(e.x, e.y);
     }
     __syncthreads();
+    uint64_t ck = 0;
     int rank = 0;
-    if (tid < nt)
-      for (int j = 0; j < nt; ++j) rank += fk[j] > ck;
-    if (tid < nt && rank == need - 1) fk64_thr = ck;
+    if (tid < nF) {
+      ck = fk[tid];
+      for (int j = 0; j < nF; ++j) rank += fk[j] > ck;
+    }
+    if (tid < nF && rank == need2 - 1) fk64_thr = ck;
     __syncthreads();
     thr = fk64_thr;
-  } else if (nt > need) {
+  } else if (in_lds) {
+    thr = lds_list_select(tls, nt, need, h256, res);
+  } else {
     uint32_t thi = 0, tlo = 0;
     list_select(tl, nt, need, h256, res, &thi, &tlo);
     thr = ((uint64_t)thi << 32) | tlo;
   }
-  if (tid == 0) ocount = 0;
-  __syncthreads();
-  for (int i0 = 0; i0 < nt; i0 += 256) {
-    const int i = i0 + tid;
-    bool take = false;
-    uint2 e = make_uint2(0, 0);
-    if (i < nt) {
-      e = tl[i];
-      take = (((uint64_t)e.x << 32) | (uint64_t)(~e.y)) >= thr;
-    }
-    const uint64_t mt = __ballot(take);
-    int bt = 0;
-    if (lane == 0 && mt) bt = atomicAdd(&ocount, __popcll(mt));
-    bt = __shfl(bt, 0, 64);
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    if (take) outv[ns + bt + __popcll(mt & below)] = (int32_t)e.y;
-  }
-  __syncthreads();
-  if (vis <= kBitmapEntries) {
-    // ascending order from a bitmap of the chosen entries: per-thread runs of
-    // words, popcounts, one block-wide prefix sum, then in-order emission
-    const int W = (int)((vis + 31) >> 5);
-    for (int w = tid; w < W; w += 256) bm[w] = 0u;
-    __syncthreads();
-    for (int j = tid; j < k; j += 256) atomicOr(&bm[outv[j] >> 5], 1u << (outv[j] & 31));
-    __syncthreads();
-    const int WPT = (W + 255) / 256;
-    const int w0 = tid * WPT, w1 = min(w0 + WPT, W);
-    int c = 0;
-    for (int w = w0; w < w1; ++w) c += __popc(bm[w]);
+  // winners in list (= index) order: each thread takes a contiguous run of the
+  // ties, and one prefix sum over the threads' counts places them
+  {
+    const int TPT = (nt + 255) / 256;
+    const int i0 = min(tid * TPT, nt), i1 = min(i0 + TPT, nt);
+    int cnt = 0;
+    for (int i = i0; i < i1; ++i) cnt += composite(tl[i].x, tl[i].y) >= thr;
     int tot;
-    int p = block_excl_scan(c, sh, &tot);
-    for (int w = w0; w < w1; ++w) {
-      uint32_t bits = bm[w];
-      while (bits) {
-        const int bit = __ffs(bits) - 1;
-        orow[p++] = w * 32 + bit;
-        bits &= bits - 1;
-      }
+    int off = block_excl_scan(cnt, sh, &tot);
+    for (int i = i0; i < i1; ++i) {
+      const uint2 e = tl[i];
+      if (composite(e.x, e.y) >= thr) tsel[off++] = (int32_t)e.y;
     }
-    return;
   }
-  // larger index spaces: bitonic sort of the k chosen indices (ascending)
-  int P = 1;
-  while (P < k) P <<= 1;
-  for (int j = k + tid; j < P; j += 256) outv[j] = 0x7fffffff;
   __syncthreads();
-  for (int size = 2; size <= P; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < P / 2; i += 256) {
-        const int lo = 2 * i - (i & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = ((lo & size) == 0);
-        const int a = outv[lo], c = outv[hi];
-        if ((a > c) == up) { outv[lo] = c; outv[hi] = a; }
-      }
-      __syncthreads();
-    }
+  // merge the two ascending lists (disjoint index sets): an element's output
+  // position is its own rank plus its rank in the other list; each thread
+  // places a contiguous run of each list
+  {
+    const int RS = (ns + 255) / 256, RT = (need + 255) / 256;
+    merge_run(surev, min(tid * RS, ns), min(tid * RS + RS, ns), tsel, need, orow);
+    merge_run(tsel, min(tid * RT, need), min(tid * RT + RT, need), surev, ns, orow);
   }
-  for (int j = tid; j < k; j += 256) orow[j] = outv[j];
 }
 
 // ===========================================================================
@@ -857,24 +997,25 @@ hipError_t launch_index_topk_decode(const csa_index_desc& d, const void* qI, con
                                     void* wsp, hipStream_t st) {
   DecWs w = carve(wsp, d);
   const int B = d.batch;
-  dec_clear_kernel<<<(B * kCoarseBins + 255) / 256, 256, 0, st>>>(w.hist, w.fine, w.cnt, B);
-  const unsigned chunks = (unsigned)((d.n_entries + kDecChunk - 1) / kDecChunk);
+  const int64_t nch = dec_chunks(d);
+  const int ncopies = dec_hist_copies(nch);
+  const int64_t n4 = (int64_t)B * (ncopies + 1) * kCoarseBins / 4;  // copies + fine
+  dec_clear_kernel<<<(unsigned)((n4 + 255) / 256), 256, 0, st>>>((int4*)w.hist, n4);
+  const dim3 grid((unsigned)nch, (unsigned)B);
   CSA_INDEX_DISPATCH(d.n_heads, d.head_dim, {
     if (d.dtype == CSA_BF16)
-      dec_score_kernel<BF16, HI, CI><<<dim3(chunks, B), 256, 0, st>>>(
+      dec_score_kernel<BF16, HI, CI><<<grid, 256, 0, st>>>(
           (const BF16::S*)qI, (const BF16::S*)wI, (const BF16::S*)KI, pos, d.n_entries, d.m, d.k,
-          w.scores, w.hist);
+          w.scores, w.hist, ncopies);
     else
-      dec_score_kernel<F32, HI, CI><<<dim3(chunks, B), 256, 0, st>>>(
+      dec_score_kernel<F32, HI, CI><<<grid, 256, 0, st>>>(
           (const float*)qI, (const float*)wI, (const float*)KI, pos, d.n_entries, d.m, d.k,
-          w.scores, w.hist);
+          w.scores, w.hist, ncopies);
   });
-  dec_refine_kernel<<<dim3(chunks, B), 256, 0, st>>>(pos, d.n_entries, d.m, d.k, w.scores, w.hist,
-                                                     w.fine);
-  dec_collect_kernel<<<dim3(chunks, B), 256, 0, st>>>(pos, d.n_entries, d.m, d.k, w.scores, w.hist,
-                                                      w.fine, w.cnt, w.sure, w.ties);
-  dec_finalize_kernel<<<B, 256, 0, st>>>(pos, d.n_entries, d.m, d.k, w.hist, w.fine, w.cnt, w.sure,
-                                         w.ties, idx_out);
+  dec_collect_kernel<<<grid, 256, 0, st>>>(pos, d.n_entries, d.m, d.k, w.scores, w.hist, w.fine,
+                                           w.ccnt, w.lists, nch, ncopies);
+  dec_finalize_kernel<<<B, 256, 0, st>>>(pos, d.n_entries, d.m, d.k, w.fine, w.ccnt, w.lists,
+                                         w.flat, nch, idx_out);
   return hipGetLastError();
 }
 

@@ -80,6 +80,8 @@ def test_state_init_equals_prefill_of_nothing(lib):
     ("f32", 4, 64, 4, 64, 3000, [11999, 5, 300]),
     ("bf16", 8, 128, 2, 33, 5000, [9999, 64, 65, 66]),
     ("bf16", 16, 64, 4, 1024, 262144, [1048575, 600000]),
+    ("bf16", 16, 64, 4, 1024, 100000, [399999, 250001, 5000]),  # 3 histogram copies
+    ("bf16", 4, 64, 4, 64, 1100000, [4399999]),  # > 1024 chunks, several per gather run
 ])
 def test_index_topk_decode(lib, dtype, hI, cI, m, k, ne, pos):
     _say("index_topk_decode", dtype, hI, cI, m, k, ne, pos)
@@ -116,6 +118,34 @@ def test_index_topk_decode_exact_ties(lib):
                             KI[b, :vis].double().numpy(), m, t0=p)
         ref = O.topk(sc, k, m, t0=p)[0]
         assert sorted(got[b].tolist()) == sorted(ref.tolist())
+
+
+@pytest.mark.parametrize("dtype,ne", [("f32", 3000), ("f32", 20000), ("bf16", 20000)])
+def test_index_topk_decode_one_coarse_bin(lib, dtype, ne):
+    """Every score in [1, 1.1): all visible entries share the top 11 key bits,
+    so the whole row is the tie list (held in LDS up to 6144 entries, scanned
+    in place beyond); in bf16 the keys also collapse to a few exact values."""
+    _say("index decode one coarse bin", dtype, ne)
+    B, hI, cI, m, k = 2, 4, 64, 4, 300
+    g = torch.Generator(device="cpu").manual_seed(11)
+    qI = torch.zeros(B, hI, cI)
+    qI[:, 0, 0] = 1.0
+    KI = torch.zeros(B, ne, cI)
+    KI[:, :, 0] = 1.0 + 0.1 * torch.rand(B, ne, generator=g)
+    KI[:, :, 1:] = torch.randn(B, ne, cI - 1, generator=g)  # weight-0 channels
+    wI = torch.zeros(B, hI)
+    wI[:, 0] = 1.0
+    td = I.TORCH_DTYPES[dtype]
+    qI, KI, wI = qI.to(td), KI.to(td), wI.to(td)
+    pos = [4 * ne - 1, 4 * (ne // 2) + 1]
+    idx = lib.csa_index_topk_decode(qI.to(DEV), wI.to(DEV), KI.to(DEV),
+                                    torch.tensor(pos, device=DEV), m, k)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    for b, p in enumerate(pos):
+        vis = min(ne, (p + 1) // m)
+        sc = O.index_scores(f64(qI[b])[None], f64(wI[b])[None], f64(KI[b, :vis]), m, t0=p)
+        check_topk_sets(got[b][None], sc, k, m, t0=p)
 
 
 # --------------------------------------------------------------- attention
