@@ -605,10 +605,13 @@ __global__ __launch_bounds__(256, 2) void mqa_decode_bf16_kernel(
 }
 
 // Fixed-order merge of the chunk partials of one sequence with the sink, then
-// normalisation and the inverse RoPE at the query position.  One wave per
-// (sequence, head); lane l owns channels [CPL*l, CPL*l + CPL).  Chunks are
-// read eight at a time and folded in index order with a running max.
-template <int C>
+// normalisation and the inverse RoPE at the query position.  WPH waves per
+// (sequence, head), 4 / WPH heads per workgroup: wave j of a head folds chunks
+// j, j+WPH, ... in index order (eight loads in flight, a running max), lane l
+// owning channels [CPL*l, CPL*l + CPL); the head's wave states are then
+// merged in wave order through LDS, the sink entering once.  Few chunks take
+// one wave per head; many take four, so that their loads overlap.
+template <int C, int WPH>
 __global__ __launch_bounds__(256) void mqa_decode_combine_kernel(
     const float* __restrict__ ws_o, const float2* __restrict__ ws_ml,
     const int64_t* __restrict__ posv, const float* __restrict__ sink, uint16_t* __restrict__ out,
@@ -617,27 +620,32 @@ __global__ __launch_bounds__(256) void mqa_decode_combine_kernel(
   constexpr int CPL = C / 64;
   constexpr int U = 8;
   constexpr float LOG2E = 1.4426950408889634f;
-  const int lane = threadIdx.x & 63;
-  const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
+  __shared__ float sacc[4][C];
+  __shared__ float2 smd[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = wave % WPH;
+  const int h0 = blockIdx.y * (4 / WPH) + wave / WPH;
+  const bool live = h0 < nh;  // uniform per wave; every wave reaches the barrier
+  const int h = live ? h0 : 0;
   const int64_t b = blockIdx.x;
-  if (h >= nh) return;  // whole wave
   const int64_t pos = posv[b];
   const int64_t nwin = max64(0, min64(n_win, pos + 1));
   const int64_t ncomp = sparse ? (int64_t)k : max64(0, min64((pos + 1) / m, n_entries));
-  const int ns = (int)((nwin + ncomp + spl - 1) / spl);  // chunks that hold candidates
+  const int ns = live ? (int)((nwin + ncomp + spl - 1) / spl) : 0;  // chunks with candidates
   const float2* ml = ws_ml + (int64_t)b * nsplit * nh + h;
   const float* po = ws_o + ((int64_t)b * nsplit * nh + h) * C + lane * CPL;
-  float M = sink[h] * LOG2E;
-  float den = 1.f;  // exp2(sink - M)
+  const float sl2 = sink[h] * LOG2E;
+  float M = sl2;    // a finite start; the sink itself is added in the merge
+  float den = 0.f;
   float acc[CPL];
 #pragma unroll
   for (int i = 0; i < CPL; ++i) acc[i] = 0.f;
-  for (int s0 = 0; s0 < ns; s0 += U) {
+  for (int s0 = sub; s0 < ns; s0 += WPH * U) {
     float2 mv[U];
     float ov[U][CPL];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int s = s0 + u;
+      const int s = s0 + WPH * u;
       mv[u] = make_float2(-INFINITY, 0.f);
 #pragma unroll
       for (int i = 0; i < CPL; ++i) ov[u][i] = 0.f;
@@ -668,10 +676,37 @@ __global__ __launch_bounds__(256) void mqa_decode_combine_kernel(
       for (int i = 0; i < CPL; ++i) acc[i] += f * ov[u][i];
     }
   }
-  const float inv = 1.f / den;
   float v[CPL];
+  if constexpr (WPH == 1) {  // the wave's own state is the head's (M >= the sink's logit)
+    if (!live) return;
+    const float inv = 1.f / (den + __builtin_amdgcn_exp2f(sl2 - M));
 #pragma unroll
-  for (int i = 0; i < CPL; ++i) v[i] = acc[i] * inv;
+    for (int i = 0; i < CPL; ++i) v[i] = acc[i] * inv;
+  } else {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) sacc[wave][lane * CPL + i] = acc[i];
+    if (lane == 0) smd[wave] = make_float2(M, den);
+    __syncthreads();
+    if (sub != 0 || !live) return;
+    float Mt = sl2;
+#pragma unroll
+    for (int w = 0; w < WPH; ++w) Mt = fmaxf(Mt, smd[wave + w].x);
+    float sc[WPH];
+    float dt = __builtin_amdgcn_exp2f(sl2 - Mt);  // the sink's term
+#pragma unroll
+    for (int w = 0; w < WPH; ++w) {
+      sc[w] = __builtin_amdgcn_exp2f(smd[wave + w].x - Mt);
+      dt += sc[w] * smd[wave + w].y;
+    }
+    const float inv = 1.f / dt;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      float x = 0.f;
+#pragma unroll
+      for (int w = 0; w < WPH; ++w) x += sc[w] * sacc[wave + w][lane * CPL + i];
+      v[i] = x * inv;
+    }
+  }
   const int ch0 = lane * CPL;
   if (r > 0 && ch0 >= C - r) {
 #pragma unroll
@@ -697,7 +732,8 @@ hipError_t launch_mqa_decode_bf16(const csa_attn_desc& d, int mode, const void* 
                                   float2* ws_ml, int nsplit, hipStream_t st) {
   const int spl = mqa_decode_bf16_split(mode);
   const dim3 grid((unsigned)nsplit, (unsigned)d.batch);
-  const dim3 cgrid((unsigned)d.batch, (unsigned)((d.n_heads + 3) / 4));
+  const bool wide = nsplit > 8;  // more chunks than one wave's loads in flight
+  const dim3 cgrid((unsigned)d.batch, (unsigned)(wide ? d.n_heads : (d.n_heads + 3) / 4));
 #define CSA_DEC(CC)                                                                            \
   if (d.c == CC) {                                                                            \
     if (mode == ATTN_SPARSE)                                                                  \
@@ -712,9 +748,14 @@ hipError_t launch_mqa_decode_bf16(const csa_attn_desc& d, int mode, const void* 
           d.n_entries, pos, ws_o, ws_ml, nsplit, spl);                                         \
     hipError_t e = hipGetLastError();                                                         \
     if (e != hipSuccess) return e;                                                            \
-    mqa_decode_combine_kernel<CC><<<cgrid, 256, 0, st>>>(                                     \
-        ws_o, ws_ml, pos, sink, (uint16_t*)out, d.n_heads, nsplit, spl, mode == ATTN_SPARSE,    \
-        d.k, d.m, d.n_win, d.n_entries, d.rope_dims, d.rope_theta);                            \
+    if (wide)                                                                                 \
+      mqa_decode_combine_kernel<CC, 4><<<cgrid, 256, 0, st>>>(                                \
+          ws_o, ws_ml, pos, sink, (uint16_t*)out, d.n_heads, nsplit, spl, mode == ATTN_SPARSE,  \
+          d.k, d.m, d.n_win, d.n_entries, d.rope_dims, d.rope_theta);                          \
+    else                                                                                      \
+      mqa_decode_combine_kernel<CC, 1><<<cgrid, 256, 0, st>>>(                                \
+          ws_o, ws_ml, pos, sink, (uint16_t*)out, d.n_heads, nsplit, spl, mode == ATTN_SPARSE,  \
+          d.k, d.m, d.n_win, d.n_entries, d.rope_dims, d.rope_theta);                          \
     return hipGetLastError();                                                                 \
   }
   CSA_DEC(128) CSA_DEC(256) CSA_DEC(512)
