@@ -245,10 +245,10 @@ class HybridDecode:
 
     def step(self, streams=True):
         """One decode step.  Its three chains are independent until the sparse
-        attention: (CSA compressor), (indexer compressor -> top-k) and (HCA
-        compressor -> dense attention); with `streams` they run on the current
-        stream and two forked side streams (default priority), joined back
-        before the step ends, so their small launches overlap on the GPU.
+        attention: (indexer compressor -> top-k), (CSA compressor) and (HCA
+        compressor -> dense attention); with `streams` the first two run on
+        two forked side streams (default priority) and the HCA chain on the
+        current stream, which then joins both and runs the sparse attention.
         Each chain has its own workspaces."""
         c, g = self.cfg, self.g
         m, ov, r = c["m"], c["overlap"], c["rope_dims"]
@@ -266,20 +266,19 @@ class HybridDecode:
                                   self.kcache, ws_slot="decode_proj_idx")
             L.csa_index_topk_decode(g["qI"], g["wI"], self.kcache, self.pos, m, c["k"], out=self.idx)
         with torch.cuda.stream(sc):
-            L.csa_compress_decode(self.h, self.pos, g["hca_Wkv"], g["hca_Wz"], g["hca_ape"],
-                                  c["m_hca"], 0, self.sth, self.hcache, W_win=g["hca_Wwin"],
-                                  win_ring=self.hring, rope_dims=r, ws_slot="decode_proj_hca")
-            L.hca_dense_mqa_decode(g["hca_q"], self.hring, self.hcache, self.pos, g["hca_sink"],
-                                   c["m_hca"], rope_dims=r, out=self.out_h)
-        L.csa_compress_decode(self.h, self.pos, g["csa_Wkv"], g["csa_Wz"], g["csa_ape"], m, ov,
-                              self.st, self.cache, W_win=g["csa_Wwin"], win_ring=self.ring, rope_dims=r,
-                              ws_slot="decode_proj_csa")
+            L.csa_compress_decode(self.h, self.pos, g["csa_Wkv"], g["csa_Wz"], g["csa_ape"], m, ov,
+                                  self.st, self.cache, W_win=g["csa_Wwin"], win_ring=self.ring,
+                                  rope_dims=r, ws_slot="decode_proj_csa")
+        L.csa_compress_decode(self.h, self.pos, g["hca_Wkv"], g["hca_Wz"], g["hca_ape"],
+                              c["m_hca"], 0, self.sth, self.hcache, W_win=g["hca_Wwin"],
+                              win_ring=self.hring, rope_dims=r, ws_slot="decode_proj_hca")
+        L.hca_dense_mqa_decode(g["hca_q"], self.hring, self.hcache, self.pos, g["hca_sink"],
+                               c["m_hca"], rope_dims=r, out=self.out_h)
         if streams:
             main.wait_stream(sb)
+            main.wait_stream(sc)
         L.csa_sparse_mqa_decode(g["csa_q"], self.ring, self.cache, self.idx, self.pos, g["csa_sink"],
                                 rope_dims=r, out=self.out_c)
-        if streams:
-            main.wait_stream(sc)
 
     def algorithmic_bytes(self):
         """Bytes a decode step must move at least once (bf16 = 2 B)."""
