@@ -27,7 +27,12 @@
  *    [c, 2c) the block itself ([A] Compressor).
  *  - All work is enqueued on `stream` (a hipStream_t; NULL = default stream)
  *    and is asynchronous.  `ws` is caller-owned scratch of at least
- *    csa_workspace_bytes(...) bytes (may be NULL when that is 0).
+ *    csa_workspace_bytes(...) bytes (may be NULL when that is 0).  Its
+ *    leading csa_workspace_zero_bytes(...) bytes must be zero when a call
+ *    starts; every call leaves them zero again, so they need clearing only
+ *    when the buffer is new, after the caller wrote to it, after a failed
+ *    call, or before a call whose zero-byte count exceeds the previous one's
+ *    on that buffer (only csa_index_topk_decode has such bytes).
  *  - Return value: CSA_OK or a negative csa_status.  All argument checks run
  *    on the host before anything is enqueued, so a failing call has no side
  *    effect.  A fault inside a kernel surfaces at the caller's next stream
@@ -49,7 +54,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 1
+#define CSA_ABI_VERSION 2
 
 typedef enum csa_status {
   CSA_OK = 0,
@@ -208,6 +213,8 @@ int csa_index_topk_prefill(const csa_index_desc* desc, const void* qI, const voi
  *   KI_cache [B, n_entries, cI]        dtype
  *   pos      [B]                       int64 (device)
  *   idx_out  [B, k]                    int32, ascending, -1 padded
+ *   ws       leading csa_workspace_zero_bytes(CSA_ENTRY_INDEX_TOPK_DECODE,
+ *            desc) bytes zero on entry (left zero on return)
  */
 int csa_index_topk_decode(const csa_index_desc* desc, const void* qI, const void* wI,
                           const void* KI_cache, const int64_t* pos, int32_t* idx_out, void* ws,
@@ -286,6 +293,12 @@ typedef enum csa_entry {
 /* Workspace bytes needed by `entry` for the descriptor `desc` (a pointer to
  * the csa_*_desc type that entry takes).  Returns 0 on a null descriptor. */
 size_t csa_workspace_bytes(int entry, const void* desc);
+
+/* Leading workspace bytes that must be zero when `entry` starts (its
+ * counters; each call returns them to zero), 0 for entries without any.
+ * csa_index_topk_decode keeps its score histograms there, so that no
+ * clearing launch precedes the scoring. */
+size_t csa_workspace_zero_bytes(int entry, const void* desc);
 
 /* Static text for a csa_status value. */
 const char* csa_status_string(int status);

@@ -25,7 +25,8 @@ ENTRY = dict(compress_prefill=0, compress_decode=1, index_topk_prefill=2, index_
 EXPORTED = ["csa_compress_prefill", "csa_compress_decode", "csa_state_bytes", "csa_state_init",
             "csa_index_topk_prefill", "csa_index_topk_decode", "csa_sparse_mqa_prefill",
             "csa_sparse_mqa_decode", "hca_dense_mqa_prefill", "hca_dense_mqa_decode",
-            "csa_workspace_bytes", "csa_status_string", "csa_abi_version"]
+            "csa_workspace_bytes", "csa_workspace_zero_bytes", "csa_status_string",
+            "csa_abi_version"]
 
 
 class CompressDesc(ctypes.Structure):
@@ -72,6 +73,8 @@ def load(path: str = LIB_PATH):
     lib.csa_status_string.argtypes = [I]
     lib.csa_workspace_bytes.restype = S
     lib.csa_workspace_bytes.argtypes = [I, P]
+    lib.csa_workspace_zero_bytes.restype = S
+    lib.csa_workspace_zero_bytes.argtypes = [I, P]
     lib.csa_state_bytes.restype = S
     lib.csa_state_bytes.argtypes = [P]
     lib.csa_state_init.argtypes = [P, P, P]
@@ -84,7 +87,8 @@ def load(path: str = LIB_PATH):
     lib.hca_dense_mqa_prefill.argtypes = [P] * 7 + [S, P]
     lib.hca_dense_mqa_decode.argtypes = [P] * 8 + [S, P]
     for f in EXPORTED:
-        if f not in ("csa_abi_version", "csa_status_string", "csa_workspace_bytes", "csa_state_bytes"):
+        if f not in ("csa_abi_version", "csa_status_string", "csa_workspace_bytes",
+                     "csa_workspace_zero_bytes", "csa_state_bytes"):
             getattr(lib, f).restype = I
     _lib = lib
     return lib
@@ -129,10 +133,14 @@ def _expect(t, shape, dtype, name):
 
 
 _WS = {}
+_WS_ZERO = {}  # (device, slot) -> leading bytes the last call left zero
 
 
-def workspace(nbytes: int, device, slot: str = "default"):
-    """A cached device workspace of at least nbytes (torch-owned memory)."""
+def workspace(nbytes: int, device, slot: str = "default", zero_bytes: int = 0):
+    """A cached device workspace of at least nbytes (torch-owned memory) whose
+    first zero_bytes are zero: they are cleared (a fill kernel on the current
+    stream) when the buffer is new or the previous call on it left fewer of
+    them zero; a call that returns them to zero keeps that state."""
     if nbytes == 0:
         return None, 0
     key = (str(device), slot)
@@ -140,11 +148,22 @@ def workspace(nbytes: int, device, slot: str = "default"):
     if t is None or t.numel() < nbytes:
         t = torch.empty(nbytes, dtype=torch.uint8, device=device)
         _WS[key] = t
+        _WS_ZERO.pop(key, None)
+    if zero_bytes:
+        if _WS_ZERO.get(key, 0) < zero_bytes:
+            t[:zero_bytes].zero_()
+        _WS_ZERO[key] = zero_bytes
+    else:
+        _WS_ZERO.pop(key, None)
     return t, t.numel()
 
 
 def workspace_bytes(entry: str, desc) -> int:
     return load().csa_workspace_bytes(ENTRY[entry], ctypes.byref(desc))
+
+
+def workspace_zero_bytes(entry: str, desc) -> int:
+    return load().csa_workspace_zero_bytes(ENTRY[entry], ctypes.byref(desc))
 
 
 # -------------------------------------------------------------- compressor
@@ -254,9 +273,12 @@ def csa_index_topk_decode(qI, wI, KI_cache, pos, m, k, out=None):
     desc = IndexDesc(0, B, hI, cI, m, k, _dt(qI), ne)
     if out is None:
         out = torch.empty((B, k), dtype=torch.int32, device=qI.device)
-    ws, wsb = workspace(workspace_bytes("index_topk_decode", desc), qI.device, "index_dec")
+    ws, wsb = workspace(workspace_bytes("index_topk_decode", desc), qI.device, "index_dec",
+                        zero_bytes=workspace_zero_bytes("index_topk_decode", desc))
     st = lib.csa_index_topk_decode(ctypes.byref(desc), _ptr(qI), _ptr(wI), _ptr(KI_cache),
                                    _ptr(pos), _ptr(out), _ptr(ws), wsb, _stream(qI.device))
+    if st != 0:
+        _WS_ZERO.pop((str(qI.device), "index_dec"), None)
     _check(st, "csa_index_topk_decode")
     return out
 

@@ -113,6 +113,13 @@ size_t csa_state_bytes(const csa_compress_desc* d) {
   return (size_t)b * (d->overlap ? 3 : 1) * 3 * d->c * 4;
 }
 
+size_t csa_workspace_zero_bytes(int entry, const void* desc) {
+  if (!desc || entry != CSA_ENTRY_INDEX_TOPK_DECODE) return 0;
+  const csa_index_desc* d = (const csa_index_desc*)desc;
+  if (d->batch <= 0) return 0;
+  return index_decode_zero_bytes(*d);
+}
+
 size_t csa_workspace_bytes(int entry, const void* desc) {
   if (!desc) return 0;
   switch (entry) {

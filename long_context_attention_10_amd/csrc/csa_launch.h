@@ -59,6 +59,7 @@ hipError_t launch_topk_rows_prefill(const csa_index_desc& d, const float* scores
                                     int32_t* idx_out, hipStream_t st);
 
 size_t index_decode_ws_bytes(const csa_index_desc& d);
+size_t index_decode_zero_bytes(const csa_index_desc& d);
 hipError_t launch_index_topk_decode(const csa_index_desc& d, const void* qI, const void* wI,
                                     const void* KI, const int64_t* pos, int32_t* idx_out,
                                     void* ws, hipStream_t st);

@@ -431,7 +431,6 @@ __global__ __launch_bounds__(256) void topk_rows_prefill_kernel(const float* __r
 
 // ===========================================================================
 // Decode: one query per sequence over up to ~10^6 cached keys.
-//   D0 clear the histograms;
 //   D1 score chunks of keys (16x16 matrix-core tiles, keys streamed straight
 //      from memory -- this pass moves the step's dominant bytes) and build a
 //      2048-bin histogram of the keys' top 11 bits, added into one of R
@@ -446,8 +445,12 @@ __global__ __launch_bounds__(256) void topk_rows_prefill_kernel(const float* __r
 //   D3 per sequence: gather the chunks' lists, resolve the ties exactly on
 //      (score, -index) from their fine histogram (a radix select over the
 //      whole tie list when the fine bin is crowded), and merge the two
-//      ascending lists into the output row.
-// Nothing depends on the order in which workgroups run.
+//      ascending lists into the output row, and zero the sequence's
+//      histograms for the next call.
+// The histograms lead the workspace: they must be zero when a call starts
+// (the caller clears them once) and every call leaves them zero, so no
+// clearing launch precedes the scoring.  Nothing depends on the order in
+// which workgroups run.
 // ===========================================================================
 constexpr int kDecChunk = 1024;    // keys per scoring workgroup
 constexpr int kCoarseBins = 2048;  // top 11 bits
@@ -456,9 +459,9 @@ constexpr int kChunkLds = 1024;    // chunk counts staged in LDS by the finalize
 constexpr int kTieLds = 6144;      // tie candidates resolved in LDS
 
 struct DecWs {  // carve-up of the decode workspace
-  float* scores;  // [B][n_entries]
   int* hist;      // [B][copies][kCoarseBins], then fine [B][kCoarseBins] (tie bits 20..10)
   int* fine;
+  float* scores;  // [B][n_entries]
   int2* ccnt;     // [B][chunks]: (sure, tie) counts per chunk
   uint2* lists;   // [B][n_entries] (key, index): chunk slices, sure first, ties last
   uint2* flat;    // [B][n_entries]: tie lists too long for LDS, contiguous
@@ -478,26 +481,24 @@ static DecWs carve(void* ws, const csa_index_desc& d) {
   uint8_t* p = (uint8_t*)ws;
   DecWs w;
   const size_t B = d.batch, ne = d.n_entries, nc = dec_chunks(d);
-  w.scores = (float*)p; p += align_up(B * ne * 4);
   w.hist = (int*)p;
   w.fine = w.hist + B * dec_hist_copies(nc) * kCoarseBins;
   p += align_up(B * (dec_hist_copies(nc) + 1) * kCoarseBins * 4);
+  w.scores = (float*)p; p += align_up(B * ne * 4);
   w.ccnt = (int2*)p; p += align_up(B * nc * 8);
   w.lists = (uint2*)p; p += align_up(B * ne * 8);
   w.flat = (uint2*)p; p += align_up(B * ne * 8);
   return w;
 }
 
+size_t index_decode_zero_bytes(const csa_index_desc& d) {
+  return align_up((size_t)d.batch * (dec_hist_copies(dec_chunks(d)) + 1) * kCoarseBins * 4);
+}
+
 size_t index_decode_ws_bytes(const csa_index_desc& d) {
   const size_t B = d.batch, ne = d.n_entries, nc = dec_chunks(d);
   return align_up(B * ne * 4) + align_up(B * (dec_hist_copies(nc) + 1) * kCoarseBins * 4) +
          align_up(B * nc * 8) + 2 * align_up(B * ne * 8);
-}
-
-__global__ void dec_clear_kernel(int4* __restrict__ hist, int64_t n4) {
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4;
-       i += (int64_t)gridDim.x * blockDim.x)
-    hist[i] = make_int4(0, 0, 0, 0);
 }
 
 template <class T, int HI, int CI>
@@ -768,8 +769,9 @@ CSA_DEV void merge_run(const int32_t* a, int j0, int j1, const int32_t* o, int n
 // the winners are compacted in order and merged with the sure list.
 __global__ __launch_bounds__(256) void dec_finalize_kernel(
     const int64_t* __restrict__ posv, int64_t n_entries, int m, int k,
-    const int* __restrict__ fine, const int2* __restrict__ ccnt, const uint2* __restrict__ lists,
-    uint2* __restrict__ flat, int64_t nchunks, int32_t* __restrict__ idx_out) {
+    int* __restrict__ hist, int ncopies, int* __restrict__ fine, const int2* __restrict__ ccnt,
+    const uint2* __restrict__ lists, uint2* __restrict__ flat, int64_t nchunks,
+    int32_t* __restrict__ idx_out) {
   __shared__ int sh[8];
   __shared__ int res[2];
   __shared__ int h256[256];
@@ -794,10 +796,16 @@ __global__ __launch_bounds__(256) void dec_finalize_kernel(
   // gather (thread j holds bins 8j .. 8j+7)
   int fl[kCoarseBins / 256];
   {
-    const int4* f4 = (const int4*)(fine + (int64_t)b * kCoarseBins) + 2 * tid;
+    int4* f4 = (int4*)(fine + (int64_t)b * kCoarseBins) + 2 * tid;
     const int4 x = f4[0], y = f4[1];
     fl[0] = x.x; fl[1] = x.y; fl[2] = x.z; fl[3] = x.w;
     fl[4] = y.x; fl[5] = y.y; fl[6] = y.z; fl[7] = y.w;
+    f4[0] = make_int4(0, 0, 0, 0);  // after this thread's own loads of them
+    f4[1] = make_int4(0, 0, 0, 0);
+  }
+  {  // the coarse copies were read by the collect pass, which has finished
+    int4* h4 = (int4*)(hist + (int64_t)b * ncopies * kCoarseBins);
+    for (int i = tid; i < ncopies * kCoarseBins / 4; i += 256) h4[i] = make_int4(0, 0, 0, 0);
   }
   // gather: thread j takes a contiguous run of chunks and writes the slice
   // slot of each of their entries into per-list slot tables in LDS (list
@@ -999,8 +1007,6 @@ hipError_t launch_index_topk_decode(const csa_index_desc& d, const void* qI, con
   const int B = d.batch;
   const int64_t nch = dec_chunks(d);
   const int ncopies = dec_hist_copies(nch);
-  const int64_t n4 = (int64_t)B * (ncopies + 1) * kCoarseBins / 4;  // copies + fine
-  dec_clear_kernel<<<(unsigned)((n4 + 255) / 256), 256, 0, st>>>((int4*)w.hist, n4);
   const dim3 grid((unsigned)nch, (unsigned)B);
   CSA_INDEX_DISPATCH(d.n_heads, d.head_dim, {
     if (d.dtype == CSA_BF16)
@@ -1014,8 +1020,8 @@ hipError_t launch_index_topk_decode(const csa_index_desc& d, const void* qI, con
   });
   dec_collect_kernel<<<grid, 256, 0, st>>>(pos, d.n_entries, d.m, d.k, w.scores, w.hist, w.fine,
                                            w.ccnt, w.lists, nch, ncopies);
-  dec_finalize_kernel<<<B, 256, 0, st>>>(pos, d.n_entries, d.m, d.k, w.fine, w.ccnt, w.lists,
-                                         w.flat, nch, idx_out);
+  dec_finalize_kernel<<<B, 256, 0, st>>>(pos, d.n_entries, d.m, d.k, w.hist, ncopies, w.fine,
+                                         w.ccnt, w.lists, w.flat, nch, idx_out);
   return hipGetLastError();
 }
 

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.csa_abi_version() == 1
+    assert lib.csa_abi_version() == 2
     for code in (0, -1, -2, -3, -4):
         assert len(lib.csa_status_string(code)) > 0
     assert lib.csa_status_string(-99) == b"unknown status"
@@ -69,6 +69,14 @@ def test_workspace_and_state_sizes(lib):
     ad = L.attn_desc(batch=4, nh=64, c=512, k=1024, n_entries=262144, dtype=L.CSA_BF16)
     assert L.workspace_bytes("sparse_mqa_decode", ad) > 0
     assert lib.csa_workspace_bytes(0, None) == 0
+    # the decode top-k's histograms lead its workspace; no other entry has zero bytes
+    dd = L.IndexDesc(0, 4, 16, 64, 4, 1024, L.CSA_BF16, 262144)
+    z = L.workspace_zero_bytes("index_topk_decode", dd)
+    assert 0 < z < L.workspace_bytes("index_topk_decode", dd)
+    assert z == 4 * (8 + 1) * 2048 * 4  # 8 coarse copies + the fine histogram per sequence
+    assert L.workspace_zero_bytes("index_topk_prefill", idx) == 0
+    assert L.workspace_zero_bytes("sparse_mqa_decode", ad) == 0
+    assert lib.csa_workspace_zero_bytes(3, None) == 0
 
 
 def _p(v=1):

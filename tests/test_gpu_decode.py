@@ -1,6 +1,8 @@
 """GPU parity: decode entry points against the CPU fp64 oracle, plus the
 prefill -> decode hand-off (prefill(n) followed by s decode steps must equal
 prefill(n+s)) and batch invariance."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -143,6 +145,38 @@ def test_index_topk_decode_one_coarse_bin(lib, dtype, ne):
     torch.cuda.synchronize()
     got = idx.cpu().numpy()
     for b, p in enumerate(pos):
+        vis = min(ne, (p + 1) // m)
+        sc = O.index_scores(f64(qI[b])[None], f64(wI[b])[None], f64(KI[b, :vis]), m, t0=p)
+        check_topk_sets(got[b][None], sc, k, m, t0=p)
+
+
+def test_index_topk_decode_leaves_its_counters_zero(lib):
+    """The histograms lead the workspace, must be zero when a call starts and
+    are zero again after it: a second call on the same workspace (no clearing
+    in between) selects the same sets, and the region reads zero after each."""
+    _say("index decode zero region")
+    B, hI, cI, m, k, ne = 3, 16, 64, 4, 512, 100000
+    key = ("izero", B, ne)
+    qI = I.normal((B, hI, cI), key + ("q",), dtype="bf16", device=DEV)
+    wI = I.uniform((B, hI), key + ("w",), dtype="bf16", device=DEV)
+    KI = I.normal((B, ne, cI), key + ("K",), dtype="bf16", device=DEV)
+    pos_t = torch.tensor([4 * ne - 1, 1000, 200001], dtype=torch.int64, device=DEV)
+    desc = lib.IndexDesc(0, B, hI, cI, m, k, lib.CSA_BF16, ne)
+    z = lib.workspace_zero_bytes("index_topk_decode", desc)
+    ws = torch.zeros(lib.workspace_bytes("index_topk_decode", desc), dtype=torch.uint8, device=DEV)
+    outs = []
+    for _ in range(2):
+        out = torch.empty((B, k), dtype=torch.int32, device=DEV)
+        st = lib.load().csa_index_topk_decode(
+            ctypes.byref(desc), lib._ptr(qI), lib._ptr(wI), lib._ptr(KI), lib._ptr(pos_t),
+            lib._ptr(out), lib._ptr(ws), ws.numel(), lib._stream(qI.device))
+        assert st == 0
+        torch.cuda.synchronize()
+        assert int(torch.count_nonzero(ws[:z])) == 0
+        outs.append(out.cpu())
+    assert torch.equal(outs[0], outs[1])
+    got = outs[0].numpy()
+    for b, p in enumerate(pos_t.tolist()):
         vis = min(ne, (p + 1) // m)
         sc = O.index_scores(f64(qI[b])[None], f64(wI[b])[None], f64(KI[b, :vis]), m, t0=p)
         check_topk_sets(got[b][None], sc, k, m, t0=p)
