@@ -523,11 +523,16 @@ __global__ __launch_bounds__(256, 2) void mqa_decode_bf16_kernel(
 #pragma unroll
     for (int g = 0; g < NKG; ++g) qraw[g] = *(const uint4*)(qh + g * 32);
   }
+  // This chunk's first index slots, loaded before the position is known on
+  // the guess that the window is full (t + 1 >= n_win); used if it is.
+  const int64_t cbeg = (int64_t)split * spl;
+  const int64_t js = max64(cbeg - n_win, 0) + tid;
+  const bool pre_ok = SPARSE && js < cbeg + spl - n_win && js < k;
+  const int32_t pre = pre_ok ? idx[b * k + js] : -1;
   const int64_t t = posv[b];
   const int nwin = (int)max64(0, min64(n_win, t + 1));
   const int64_t ncomp = SPARSE ? (int64_t)k : max64(0, min64((t + 1) / m, n_entries));
   const int64_t ncand = nwin + ncomp;
-  const int64_t cbeg = (int64_t)split * spl;
   const int64_t cend = min64(cbeg + spl, ncand);
   if (cbeg >= cend) return;  // nothing in this chunk; the combine skips it
   const int ntiles = (int)((cend - cbeg + kT - 1) / kT);
@@ -556,8 +561,14 @@ __global__ __launch_bounds__(256, 2) void mqa_decode_bf16_kernel(
   };
   const bool early0 = cbeg + kT <= nwin;  // tile 0 is window rows only
   if (early0) issue_tile(0, 0);
-  if (SPARSE)
-    for (int64_t j = s0 + tid; j < cend - nwin; j += 256) sidx[j - s0] = idx[b * k + j];
+  if (SPARSE) {
+    int64_t j = s0 + tid;
+    if (nwin == n_win) {  // the guess held: js == j
+      if (j < cend - nwin) sidx[j - s0] = pre;
+      j += 256;
+    }
+    for (; j < cend - nwin; j += 256) sidx[j - s0] = idx[b * k + j];
+  }
   for (int p = tid; p < r / 2; p += 256) {
     float cs, sn;
     rope_cs(t, p, r, theta, &cs, &sn);

@@ -524,14 +524,12 @@ __global__ __launch_bounds__(256) void decode_update_kernel(
   const int b = blockIdx.x;
   const int j = threadIdx.x;  // channel pair (2j, 2j+1)
   const bool live = j < G;
+  // the partials and the state do not depend on the position: their loads
+  // are issued with the position's
   const int64_t pos = posv[b];
-  if (pos < 0) return;  // uniform per block: no token for this sequence
   const int w = (1 + ov) * c;
   const int ns = ov ? 3 : 1;
   float* st = state + (int64_t)b * ns * 3 * c;
-  const int rr = (int)(pos % m);
-  const bool emit = (rr == m - 1);
-  const int64_t blk = pos / m;
 
   // Sum of the K-slice partials of columns (col, col+1), slices in order.  All
   // columns this thread needs are summed up front so that their loads are in
@@ -562,22 +560,31 @@ __global__ __launch_bounds__(256) void decode_update_kernel(
     }
     if (has_win) wn = colsum2(2 * w + 2 * j);
   }
+  float2 sv[9];  // state rows of channels (2j, 2j+1): 3 per series
+#pragma unroll
+  for (int i = 0; i < 9; ++i)
+    sv[i] = (live && i < 3 * ns) ? *(const float2*)(st + i * c + 2 * j) : make_float2(0.f, 0.f);
+  if (pos < 0) return;  // uniform per block: no token for this sequence
+  const int rr = (int)(pos % m);
+  const bool emit = (rr == m - 1);
+  const int64_t blk = pos / m;
 
   float e0 = 0.f, e1 = 0.f;
   if (live) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int ch = 2 * j + q;
-      float mx = st[0 * c + ch], sm = st[1 * c + ch], ac = st[2 * c + ch];
+      auto sg = [&](int i) { return q ? sv[i].y : sv[i].x; };
+      float mx = sg(0), sm = sg(1), ac = sg(2);
       osm_push(mx, sm, ac, (q ? za.y : za.x) + ape[(int64_t)rr * w + ca + ch], q ? kva.y : kva.x);
       float mb = -INFINITY, sb = 0.f, ab = 0.f;
       if (ov) {
-        mb = st[3 * c + ch]; sb = st[4 * c + ch]; ab = st[5 * c + ch];
+        mb = sg(3); sb = sg(4); ab = sg(5);
         osm_push(mb, sb, ab, (q ? zb.y : zb.x) + ape[(int64_t)rr * w + ch], q ? kvb.y : kvb.x);
       }
       if (emit) {
         float em = mx, es = sm, ea = ac;
-        if (ov) osm_merge(em, es, ea, st[6 * c + ch], st[7 * c + ch], st[8 * c + ch]);
+        if (ov) osm_merge(em, es, ea, sg(6), sg(7), sg(8));
         const float v = ea / es;
         if (q == 0) e0 = v; else e1 = v;
         // the block is finished: its b-series becomes "previous", the rest resets

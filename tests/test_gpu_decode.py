@@ -122,11 +122,13 @@ def test_index_topk_decode_exact_ties(lib):
         assert sorted(got[b].tolist()) == sorted(ref.tolist())
 
 
-@pytest.mark.parametrize("dtype,ne", [("f32", 3000), ("f32", 20000), ("bf16", 20000)])
+@pytest.mark.parametrize("dtype,ne", [("f32", 3000), ("f32", 20000), ("bf16", 20000),
+                                      ("bf16", 5000)])
 def test_index_topk_decode_one_coarse_bin(lib, dtype, ne):
     """Every score in [1, 1.1): all visible entries share the top 11 key bits,
     so the whole row is the tie list (held in LDS up to 6144 entries, scanned
-    in place beyond); in bf16 the keys also collapse to a few exact values."""
+    in place beyond); in bf16 the keys also collapse to a few exact values, so
+    hundreds share the last winner's fine bin (radix select over the list)."""
     _say("index decode one coarse bin", dtype, ne)
     B, hI, cI, m, k = 2, 4, 64, 4, 300
     g = torch.Generator(device="cpu").manual_seed(11)
