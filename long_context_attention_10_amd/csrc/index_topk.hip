@@ -275,7 +275,7 @@ CSA_DEV uint64_t composite(uint32_t key, uint32_t idx) {
   return ((uint64_t)key << 32) | (uint32_t)~idx;
 }
 
-template <int MAXIT>
+template <int MAXIT, int Q>
 __global__ __launch_bounds__(256) void topk_rows_prefill_kernel(const float* __restrict__ scores,
                                                                 int64_t ld, int64_t n,
                                                                 int64_t n_entries, int m, int k,
@@ -322,19 +322,60 @@ __global__ __launch_bounds__(256) void topk_rows_prefill_kernel(const float* __r
   for (int i = tid; i < kSelBins; i += 256) hist[i] = 0;
   for (int w = tid; w < MAXIT * 256 / 32; w += 256) bits[w] = 0u;
   if (tid == 0) ncand = 0;
+  // Lower bound of the kt-th key: every thread holding at least Q real keys
+  // offers its Q-th largest; when those threads' top-Q sets hold >= kt keys,
+  // the smallest offer is <= the kt-th largest key of the row, and keys below
+  // it can never be selected -- they skip the histogram and the marking.
+  // (Q = 0: no bound; the bins span the row's minimum to its maximum.)
   uint32_t lo = 0xffffffffu, hi = 0u;
+  int offers = 0;
+  if constexpr (Q > 0) {
+    uint32_t a[Q];
 #pragma unroll
-  for (int i = 0; i < MAXIT; ++i)
-    if (u[i]) { lo = min(lo, u[i]); hi = max(hi, u[i]); }
+    for (int j = 0; j < Q; ++j) a[j] = 0u;
+#pragma unroll
+    for (int i = 0; i < MAXIT; ++i) {
+      uint32_t x = u[i];
+#pragma unroll
+      for (int j = 0; j < Q; ++j) {  // insertion into the descending top-Q
+        const uint32_t y = max(a[j], x);
+        x = min(a[j], x);
+        a[j] = y;
+      }
+    }
+    hi = a[0];
+    if (a[Q - 1]) { lo = a[Q - 1]; offers = Q; }
+  } else {
+#pragma unroll
+    for (int i = 0; i < MAXIT; ++i)
+      if (u[i]) { lo = min(lo, u[i]); hi = max(hi, u[i]); }
+  }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     lo = min(lo, (uint32_t)__shfl_xor((int)lo, o, 64));
     hi = max(hi, (uint32_t)__shfl_xor((int)hi, o, 64));
+    if constexpr (Q > 0) offers += __shfl_xor(offers, o, 64);
   }
-  if (lane == 0) { red[wave] = lo; red[4 + wave] = hi; }
+  if (lane == 0) { red[wave] = lo; red[4 + wave] = hi; if (Q > 0) tmp[wave] = offers; }
   __syncthreads();
   lo = min(min(red[0], red[1]), min(red[2], red[3]));
   hi = max(max(red[4], red[5]), max(red[6], red[7]));
+  uint32_t lk = 1u;  // keys >= lk take part (real keys are >= 1)
+  if constexpr (Q > 0) {
+    if (tmp[0] + tmp[1] + tmp[2] + tmp[3] >= kt) lk = lo;
+    else {  // too few offers: bins over the whole row
+      lo = 0xffffffffu;
+#pragma unroll
+      for (int i = 0; i < MAXIT; ++i)
+        if (u[i]) lo = min(lo, u[i]);
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) lo = min(lo, (uint32_t)__shfl_xor((int)lo, o, 64));
+      __syncthreads();
+      if (lane == 0) red[wave] = lo;
+      __syncthreads();
+      lo = min(min(red[0], red[1]), min(red[2], red[3]));
+    }
+  }
   const float fmin = key_float(lo), fmax = key_float(hi);
   float scale = (float)kSelBins / (fmax - fmin);
   if (!(scale < INFINITY)) scale = 0.f;  // equal or non-finite range: one bin
@@ -350,7 +391,7 @@ __global__ __launch_bounds__(256) void topk_rows_prefill_kernel(const float* __r
   // 1. value histogram; threshold bin T
 #pragma unroll
   for (int i = 0; i < MAXIT; ++i)
-    if (u[i]) atomicAdd(&hist[vbin(u[i])], 1);
+    if (u[i] >= lk) atomicAdd(&hist[vbin(u[i])], 1);
   __syncthreads();
   bin_threshold<kSelBins>(hist, kt, tmp, res);
   const int T = res[0];
@@ -367,7 +408,7 @@ __global__ __launch_bounds__(256) void topk_rows_prefill_kernel(const float* __r
   if (nT <= kRankMax) {
 #pragma unroll
     for (int i = 0; i < MAXIT; ++i)
-      if (u[i]) {
+      if (u[i] >= lk) {
         const int b = vbin_with(u[i], fmin2, scale2);
         if (b > T) mark(idx_of(i));
         else if (b == T) cand[atomicAdd(&ncand, 1)] = composite(u[i], idx_of(i));
@@ -389,7 +430,7 @@ __global__ __launch_bounds__(256) void topk_rows_prefill_kernel(const float* __r
 #pragma unroll
       for (int i = 0; i < MAXIT; ++i) {
         const uint64_t c = composite(u[i], idx_of(i));
-        if (u[i] && vbin_with(u[i], fmin2, scale2) == T && (c & pmask) == prefix)
+        if (u[i] >= lk && vbin_with(u[i], fmin2, scale2) == T && (c & pmask) == prefix)
           atomicAdd(&hist[(c >> shift) & 255], 1);
       }
       __syncthreads();
@@ -403,7 +444,7 @@ __global__ __launch_bounds__(256) void topk_rows_prefill_kernel(const float* __r
     for (int i = 0; i < MAXIT; ++i) {
       uint32_t ui = u[i];
       asm volatile("" : "+v"(ui));  // recomputed here, not held from the passes above
-      if (ui) {
+      if (ui >= lk) {
         const int b = vbin_with(ui, fmin2, scale2);
         if (b > T || (b == T && composite(ui, idx_of(i)) >= thr)) mark(idx_of(i));
       }
@@ -985,18 +1026,26 @@ hipError_t launch_topk_rows_prefill(const csa_index_desc& d, const float* scores
     return e < d.n ? e : d.n;
   };
   const int64_t e16 = band_end(16 * 256), e32 = band_end(32 * 256), e48 = band_end(48 * 256);
-  if (e16 > 0)
-    topk_rows_prefill_kernel<16><<<(unsigned)e16, 256, 0, st>>>(scores, ld, d.n, d.n_entries,
-                                                                 d.m, d.k, idx_out, 0);
-  if (e32 > e16)
-    topk_rows_prefill_kernel<32><<<(unsigned)(e32 - e16), 256, 0, st>>>(
-        scores, ld, d.n, d.n_entries, d.m, d.k, idx_out, e16);
-  if (e48 > e32)
-    topk_rows_prefill_kernel<48><<<(unsigned)(e48 - e32), 256, 0, st>>>(
-        scores, ld, d.n, d.n_entries, d.m, d.k, idx_out, e32);
-  if (d.n > e48)
-    topk_rows_prefill_kernel<64><<<(unsigned)(d.n - e48), 256, 0, st>>>(
-        scores, ld, d.n, d.n_entries, d.m, d.k, idx_out, e48);
+  // Q: keys per thread offered for the lower bound, 256 * Q >= k
+  const int q = d.k <= 512 ? 2 : d.k <= 1024 ? 4 : 0;
+  auto band = [&](auto maxit, int64_t r0, int64_t r1) {
+    constexpr int MI = decltype(maxit)::value;
+    if (r1 <= r0) return;
+    const unsigned g = (unsigned)(r1 - r0);
+    if (q == 2)
+      topk_rows_prefill_kernel<MI, 2><<<g, 256, 0, st>>>(scores, ld, d.n, d.n_entries, d.m, d.k,
+                                                         idx_out, r0);
+    else if (q == 4)
+      topk_rows_prefill_kernel<MI, 4><<<g, 256, 0, st>>>(scores, ld, d.n, d.n_entries, d.m, d.k,
+                                                         idx_out, r0);
+    else
+      topk_rows_prefill_kernel<MI, 0><<<g, 256, 0, st>>>(scores, ld, d.n, d.n_entries, d.m, d.k,
+                                                         idx_out, r0);
+  };
+  band(std::integral_constant<int, 16>(), 0, e16);
+  band(std::integral_constant<int, 32>(), e16, e32);
+  band(std::integral_constant<int, 48>(), e32, e48);
+  band(std::integral_constant<int, 64>(), e48, d.n);
   return hipGetLastError();
 }
 

@@ -100,6 +100,24 @@ def test_index_topk_row_bands(lib):
         check_topk_sets(idx[t][None], sc, k, m, t0=t)
 
 
+@pytest.mark.parametrize("k", [1024, 1500])
+def test_index_topk_prefill_large_k(lib, k):
+    """k above 512: the lower bound of the k-th key comes from four keys per
+    thread (k <= 1024) or is not used (k > 1024); sampled rows, m = 1."""
+    n, hI, cI, m = 5000, 16, 64, 1
+    _say("index large k", n, k)
+    key = ("index-large-k", n, k)
+    qI = I.normal((n, hI, cI), key + ("q",), dtype="bf16", device=DEV)
+    wI = I.uniform((n, hI), key + ("w",), dtype="bf16", device=DEV)
+    KI = I.normal((n, cI), key + ("K",), dtype="bf16", device=DEV)
+    idx = lib.csa_index_topk_prefill(qI, wI, KI, m, k).cpu().numpy()
+    torch.cuda.synchronize()
+    KIh = f64(KI)
+    for t in [k - 1, k, k + 1, k + 300, 2 * k, 4095, 4096, n - 1]:
+        sc = O.index_scores(f64(qI[t])[None], f64(wI[t])[None], KIh[: (t + 1) // m], m, t0=t)
+        check_topk_sets(idx[t][None], sc, k, m, t0=t)
+
+
 def test_index_topk_exact_ties_break_to_smaller_index(lib):
     """Integer-valued inputs give exact fp32 scores with many equal values;
     the chosen set must then be exactly the oracle's (smaller index wins)."""
