@@ -254,11 +254,15 @@ CSA_DEV void bin_threshold(const int* __restrict__ h, int need, int* sh, int* re
 // visible scores, held in registers as order-preserving uint32 keys (thread
 // j owns entries 4(j + 256 i) + 0..3).  Entries are ordered by the composite
 // (key << 32 | ~index): higher score first, ties to the smaller index.
-//   1. keys are binned linearly by score VALUE between the row minimum and
-//      maximum (1024 bins; the map is monotone, so each bin is a key
-//      interval) and the bin T holding the k-th largest is found from the
-//      histogram -- raw float bits would pile most of a row into the few
-//      bins of its common exponent;
+//   0. a lower bound of the k-th largest key: each thread offers its Q-th
+//      largest key (256 Q >= k); when the offering threads' top-Q sets hold
+//      at least k keys, the smallest offer is such a bound, and keys below it
+//      take no further part (else the bound is the row minimum);
+//   1. keys from the bound up are binned linearly by score VALUE between
+//      the bound and the row maximum (1024 bins; the map is monotone, so each
+//      bin is a key interval) and the bin T holding the k-th largest is found
+//      from the histogram -- raw float bits would pile most of a row into the
+//      few bins of its common exponent;
 //   2. in one more pass over the keys, entries of bins above T are marked
 //      as winners in an LDS bitmap over the row and the composites of T are
 //      gathered and ranked (at most 256; else T's need-th largest composite

@@ -132,3 +132,31 @@ def test_index_and_attention_reject(lib):
     assert lib.csa_sparse_mqa_prefill(ctypes.byref(a), _p(), _p(), _p(), _p(), _p(), _p(), None, 0, None) == -1
     a = L.attn_desc(batch=2, nh=8, c=128, m=4, n_entries=64)
     assert lib.hca_dense_mqa_decode(ctypes.byref(a), _p(), _p(), _p(), _p(), _p(), _p(), _p(), 8, None) == -3
+
+
+def test_binding_keeps_the_zero_region(lib):
+    """The binding clears a workspace's leading zero bytes only when the buffer
+    is new or the region grew past what the last call left zero (host-side
+    logic, exercised on CPU tensors)."""
+    import torch
+    slot = "zero-region-test"
+    key = ("cpu", slot)
+    L._WS.pop(key, None)
+    L._WS_ZERO.pop(key, None)
+    t, n = L.workspace(4096, "cpu", slot, zero_bytes=1024)
+    assert n == 4096 and int(torch.count_nonzero(t[:1024])) == 0
+    t[1024:2048] = 7           # the call's other regions: scores, lists, ...
+    t2, _ = L.workspace(4096, "cpu", slot, zero_bytes=1024)
+    assert t2.data_ptr() == t.data_ptr() and int(t2[1500]) == 7  # nothing cleared
+    t2[:16] = 3                # (a call never leaves this; shows no clearing happens)
+    L.workspace(4096, "cpu", slot, zero_bytes=512)  # smaller region: no clearing
+    assert int(t2[0]) == 3
+    t2[:16] = 0
+    t3, _ = L.workspace(4096, "cpu", slot, zero_bytes=2048)  # grew past 512: cleared
+    assert int(torch.count_nonzero(t3[:2048])) == 0
+    L.workspace(4096, "cpu", slot)  # an entry without zero bytes forgets the state
+    assert key not in L._WS_ZERO
+    t4, _ = L.workspace(8192, "cpu", slot, zero_bytes=1024)  # new buffer: cleared
+    assert t4.numel() == 8192 and int(torch.count_nonzero(t4[:1024])) == 0
+    L._WS.pop(key, None)
+    L._WS_ZERO.pop(key, None)
