@@ -405,15 +405,20 @@ def main():
             print(f"[bench] building decode state for {wname}", file=sys.stderr, flush=True)
             hd = HybridDecode(dc, dev)
             print(f"[bench] timing {wname}", file=sys.stderr, flush=True)
-            tt = time_region(hd.step, max(3, a.steps), 2, flush=flush)
-            tw = time_region(hd.step, max(3, a.steps), 1)
+            nd = max(20, a.steps)  # decode steps are short: at least 20 timed
+            tt = time_region(hd.step, nd, 3, flush=flush)
+            tw = time_region(hd.step, nd, 3)
             g = graph_of(hd.step)  # the same step, launched as one HIP graph
-            tg = time_region(g.replay, max(3, a.steps), 2, flush=flush)
-            tgw = time_region(g.replay, max(3, a.steps), 1)
+            tg = time_region(g.replay, nd, 3, flush=flush)
+            tgw = time_region(g.replay, nd, 3)
             us = float(np.median(tt)) * 1e3
             ug = float(np.median(tg)) * 1e3
             byts = hd.algorithmic_bytes()
             dec[wname] = {"us_per_step": us, "us_per_token": us / dc["batch"],
+                          "us_per_step_p10_p90": [float(np.percentile(tt, 10)) * 1e3,
+                                                  float(np.percentile(tt, 90)) * 1e3],
+                          "graph_us_per_step_p10_p90": [float(np.percentile(tg, 10)) * 1e3,
+                                                        float(np.percentile(tg, 90)) * 1e3],
                           "us_per_step_warm_cache": float(np.mean(tw)) * 1e3,
                           "graph_us_per_step": ug, "graph_us_per_token": ug / dc["batch"],
                           "graph_us_per_step_warm_cache": float(np.mean(tgw)) * 1e3,
