@@ -366,3 +366,40 @@ def attend_decode_row(q_row, pos, win_rows, entries, sink, scale, qk_norm=True,
     kv = np.concatenate([np.asarray(win_rows, F64), np.asarray(entries, F64)], axis=0)
     o = attend(qh, kv, sink, scale)
     return round_to(output_epilogue(o[None], [pos], rope_dims, theta, "f64")[0], store)
+
+
+# ---------------------------------------------------------------------------
+# O8: the layer around the four calls -- query path and grouped output
+# projection ([R] eq 13-15 and 18, section 2.3.1 (d); [A] "Q, K, V 映射与位置
+# 编码注入" excerpt (wq_a -> q_norm -> wq_b) and "输出投影" excerpt)
+# ---------------------------------------------------------------------------
+def query_proj(H, W_DQ, g_q, W_w, W_UQ, W_IUQ, eps, store):
+    """c^Q = q_norm(H . W_DQ) (RMSNorm over the latent, weight g_q; None =
+    unit), stored; q = c^Q . W_UQ and q^I = c^Q . W_IUQ, stored; w^I = H . W_w,
+    stored.  Weights in the pages' orientation [in, out].  The per-head query
+    RMSNorm and RoPE belong to the attention call, not here.  Returns
+    (c^Q, q, q^I, w^I) as [n, width] arrays."""
+    lat = rms_norm(project(H, W_DQ), eps)
+    if g_q is not None:
+        lat = lat * np.asarray(g_q, F64)
+    cq = store(lat)
+    q = store(project(cq, W_UQ))
+    qI = store(project(cq, W_IUQ))
+    wI = store(project(H, W_w))
+    return cq, q, qI, wI
+
+
+def output_proj(o, wo_a, wo_b, store):
+    """Grouped low-rank output projection.  o [n, n_h*c] (the attention
+    output, already rotated back) is split into g consecutive groups of
+    n_h*c/g channels; group j is projected by wo_a[j] [d_g, n_h*c/g] to d_g
+    channels (stored); the g*d_g concatenation is projected by wo_b [d, g*d_g]
+    to d (stored).  wo_a and wo_b are linear-layer weights [out, in]."""
+    o = np.asarray(o, F64)
+    n, g = o.shape[0], wo_a.shape[0]
+    kg = o.shape[1] // g
+    mid = np.empty((n, g, wo_a.shape[1]))
+    for j in range(g):
+        mid[:, j, :] = o[:, j * kg:(j + 1) * kg] @ np.asarray(wo_a[j], F64).T
+    mid = store(mid.reshape(n, -1))
+    return store(mid @ np.asarray(wo_b, F64).T)

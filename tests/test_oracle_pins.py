@@ -381,3 +381,61 @@ def test_causality_perturbation():
     pert = layer(H2)
     np.testing.assert_array_equal(pert[:j], base[:j])
     assert np.max(np.abs(pert[j:] - base[j:])) > 1e-6
+
+
+# ------------------------------------------------- query path / output (O8)
+def test_query_proj_worked_example():
+    """h = (3, 4), W_DQ = I: the latent (3, 4) has mean square 12.5, so with
+    eps = 0 its RMSNorm is (3, 4)/sqrt(12.5); a weight scales it per channel."""
+    H = np.array([[3.0, 4.0]])
+    I2 = np.eye(2)
+    cq, q, qI, wI = O.query_proj(H, I2, np.array([2.0, 0.5]), np.array([[1.0], [-1.0]]), I2,
+                                 np.array([[1.0], [1.0]]), 0.0, lambda x: x)
+    s = 1 / math.sqrt(12.5)
+    np.testing.assert_allclose(cq, [[6 * s, 2 * s]], rtol=1e-15)
+    np.testing.assert_allclose(q, cq, rtol=1e-15)               # W_UQ = I
+    np.testing.assert_allclose(qI, [[8 * s]], rtol=1e-15)      # (6s + 2s)
+    np.testing.assert_allclose(wI, [[-1.0]], rtol=1e-15)       # 3 - 4
+
+
+def test_query_proj_latent_norm_and_scale_invariance():
+    """Without a weight, every latent row has mean square ms/(ms+eps); the
+    latent, q and q^I do not change when h is scaled (eps = 0)."""
+    n, d, dc = 7, 12, 8
+    H = RNG.normal(size=(n, d))
+    W = RNG.normal(size=(d, dc))
+    Wu, Wi, Ww = RNG.normal(size=(dc, 6)), RNG.normal(size=(dc, 4)), RNG.normal(size=(d, 3))
+    eps = 1e-3
+    cq = O.query_proj(H, W, None, Ww, Wu, Wi, eps, lambda x: x)[0]
+    lat = H @ W
+    ms = np.mean(lat * lat, axis=1)
+    np.testing.assert_allclose(np.mean(cq * cq, axis=1), ms / (ms + eps), rtol=1e-12)
+    a = O.query_proj(H, W, None, Ww, Wu, Wi, 0.0, lambda x: x)
+    b = O.query_proj(5.0 * H, W, None, Ww, Wu, Wi, 0.0, lambda x: x)
+    for x, y in zip(a[:3], b[:3]):
+        np.testing.assert_allclose(x, y, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(b[3], 5.0 * a[3], rtol=1e-12)   # w^I is linear in h
+
+
+def test_output_proj_equals_block_diagonal_product():
+    """The grouped projection is the dense product with the block-diagonal
+    matrix of the group weights, followed by wo_b."""
+    import scipy.linalg
+    n, g, kg, dg, d = 5, 3, 4, 2, 7
+    o = RNG.normal(size=(n, g * kg))
+    wo_a = RNG.normal(size=(g, dg, kg))
+    wo_b = RNG.normal(size=(d, g * dg))
+    bd = scipy.linalg.block_diag(*[wo_a[j] for j in range(g)])  # [g*dg, g*kg]
+    ref = o @ bd.T @ wo_b.T
+    np.testing.assert_allclose(O.output_proj(o, wo_a, wo_b, lambda x: x), ref, rtol=1e-12)
+
+
+def test_output_proj_single_group_identity():
+    """g = 1 with wo_a = I leaves o . wo_b^T; storing rounds once per stage."""
+    n, k, d = 4, 6, 3
+    o = RNG.normal(size=(n, k))
+    wo_b = RNG.normal(size=(d, k))
+    out = O.output_proj(o, np.eye(k)[None], wo_b, lambda x: x)
+    np.testing.assert_allclose(out, o @ wo_b.T, rtol=1e-13)
+    outb = O.output_proj(o, np.eye(k)[None], wo_b, O.round_bf16)
+    np.testing.assert_array_equal(outb, O.round_bf16(O.round_bf16(o) @ wo_b.T))
