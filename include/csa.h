@@ -287,8 +287,74 @@ typedef enum csa_entry {
   CSA_ENTRY_SPARSE_MQA_PREFILL = 4,
   CSA_ENTRY_SPARSE_MQA_DECODE = 5,
   CSA_ENTRY_DENSE_MQA_PREFILL = 6,
-  CSA_ENTRY_DENSE_MQA_DECODE = 7
+  CSA_ENTRY_DENSE_MQA_DECODE = 7,
+  CSA_ENTRY_QUERY_PROJ = 8,
+  CSA_ENTRY_OUTPUT_PROJ = 9
 } csa_entry;
+
+/* ------------------------------------------------------------------------
+ * The layer around the four calls: query path and grouped output projection
+ * ---------------------------------------------------------------------- */
+
+typedef struct {
+  int64_t n;          /* rows: tokens (prefill) or sequences (one token each) */
+  int32_t d;          /* hidden size, multiple of 64                          */
+  int32_t d_c;        /* query latent width, multiple of 64                   */
+  int32_t n_heads;    /* attention query heads                                */
+  int32_t c;          /* attention head dim                                   */
+  int32_t n_heads_i;  /* indexer heads                                        */
+  int32_t c_i;        /* indexer head dim                                     */
+  int32_t dtype;      /* CSA_BF16 (the only one these calls take)             */
+  float eps;          /* latent RMSNorm epsilon                               */
+} csa_query_desc;
+
+/* csa_query_proj -- [R] eq 13-15 and 18; [A] "Q, K, V 映射与位置编码注入"
+ * excerpt (wq_a -> q_norm -> wq_b) and the Indexer's wq_b / weights_proj.
+ *
+ *   c^Q = RMSNorm(h . W_DQ^T) * g_q   (over the d_c latent channels; rounded
+ *                                      to bf16, the operand of both up
+ *                                      projections)
+ *   q   = c^Q . W_UQ^T,  q^I = c^Q . W_IUQ^T,  w^I = h . W_w^T
+ *
+ *   H      [n, d]            bf16
+ *   W_DQ   [d_c, d]          bf16 (output-major, as all weights here)
+ *   g_q    [d_c]             fp32, or NULL for unit weight
+ *   W_w    [n_heads_i, d]    bf16
+ *   W_UQ   [n_heads*c, d_c]  bf16
+ *   W_IUQ  [n_heads_i*c_i, d_c] bf16
+ *   q_out  [n, n_heads, c]   bf16  (the attention calls' q: their per-head
+ *                                   RMSNorm and RoPE are applied there)
+ *   qI_out [n, n_heads_i, c_i] bf16
+ *   wI_out [n, n_heads_i]    bf16
+ * Matrix products accumulate in fp32 with one rounding at store.  The
+ * workspace holds the fp32 [n, d_c + n_heads_i] first product. */
+int csa_query_proj(const csa_query_desc* desc, const void* H, const void* W_DQ, const float* g_q,
+                   const void* W_w, const void* W_UQ, const void* W_IUQ, void* q_out,
+                   void* qI_out, void* wI_out, void* ws, size_t ws_bytes, void* stream);
+
+typedef struct {
+  int64_t n;          /* rows (tokens)                                         */
+  int32_t n_heads;    /* heads of the attention output                         */
+  int32_t c;          /* head dim                                              */
+  int32_t groups;     /* g: n_heads*c/g must be a multiple of 64               */
+  int32_t d_g;        /* per-group intermediate width; g*d_g a multiple of 64  */
+  int32_t d;          /* output width (hidden size)                            */
+  int32_t dtype;      /* CSA_BF16                                              */
+} csa_oproj_desc;
+
+/* csa_output_proj -- [R] section 2.3.1 (d) grouped output projection; [A]
+ * "输出投影" excerpt (wo_a per group, then wo_b).
+ *
+ *   o     [n, n_heads, c]           bf16 (an attention call's output, already
+ *                                        rotated back)
+ *   wo_a  [groups, d_g, n_heads*c/groups] bf16: group j of o (channels
+ *                                        [j*n_heads*c/g, (j+1)*n_heads*c/g)
+ *                                        of a row) -> d_g channels
+ *   wo_b  [d, groups*d_g]           bf16
+ *   out   [n, d]                    bf16 = concat_j(o_j . wo_a[j]^T) . wo_b^T
+ * The [n, groups*d_g] intermediate is rounded to bf16 in the workspace. */
+int csa_output_proj(const csa_oproj_desc* desc, const void* o, const void* wo_a, const void* wo_b,
+                    void* out, void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes needed by `entry` for the descriptor `desc` (a pointer to
  * the csa_*_desc type that entry takes).  Returns 0 on a null descriptor. */

@@ -21,12 +21,13 @@ LIB_PATH = os.path.join(_HERE, "libcsa.so")
 
 CSA_F32, CSA_BF16 = 0, 1
 ENTRY = dict(compress_prefill=0, compress_decode=1, index_topk_prefill=2, index_topk_decode=3,
-             sparse_mqa_prefill=4, sparse_mqa_decode=5, dense_mqa_prefill=6, dense_mqa_decode=7)
+             sparse_mqa_prefill=4, sparse_mqa_decode=5, dense_mqa_prefill=6, dense_mqa_decode=7,
+             query_proj=8, output_proj=9)
 EXPORTED = ["csa_compress_prefill", "csa_compress_decode", "csa_state_bytes", "csa_state_init",
             "csa_index_topk_prefill", "csa_index_topk_decode", "csa_sparse_mqa_prefill",
             "csa_sparse_mqa_decode", "hca_dense_mqa_prefill", "hca_dense_mqa_decode",
-            "csa_workspace_bytes", "csa_workspace_zero_bytes", "csa_status_string",
-            "csa_abi_version"]
+            "csa_query_proj", "csa_output_proj", "csa_workspace_bytes",
+            "csa_workspace_zero_bytes", "csa_status_string", "csa_abi_version"]
 
 
 class CompressDesc(ctypes.Structure):
@@ -41,6 +42,18 @@ class IndexDesc(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int64), ("batch", ctypes.c_int32), ("n_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("m", ctypes.c_int32), ("k", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("n_entries", ctypes.c_int64)]
+
+
+class QueryDesc(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("d", ctypes.c_int32), ("d_c", ctypes.c_int32),
+                ("n_heads", ctypes.c_int32), ("c", ctypes.c_int32), ("n_heads_i", ctypes.c_int32),
+                ("c_i", ctypes.c_int32), ("dtype", ctypes.c_int32), ("eps", ctypes.c_float)]
+
+
+class OprojDesc(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("n_heads", ctypes.c_int32), ("c", ctypes.c_int32),
+                ("groups", ctypes.c_int32), ("d_g", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
 
 
 class AttnDesc(ctypes.Structure):
@@ -86,6 +99,8 @@ def load(path: str = LIB_PATH):
     lib.csa_sparse_mqa_decode.argtypes = [P] * 9 + [S, P]
     lib.hca_dense_mqa_prefill.argtypes = [P] * 7 + [S, P]
     lib.hca_dense_mqa_decode.argtypes = [P] * 8 + [S, P]
+    lib.csa_query_proj.argtypes = [P] * 11 + [S, P]
+    lib.csa_output_proj.argtypes = [P] * 6 + [S, P]
     for f in EXPORTED:
         if f not in ("csa_abi_version", "csa_status_string", "csa_workspace_bytes",
                      "csa_workspace_zero_bytes", "csa_state_bytes"):
@@ -368,4 +383,57 @@ def hca_dense_mqa_decode(q, win_ring, comp_cache, pos, sink, m, scale=None, qk_n
     st = lib.hca_dense_mqa_decode(ctypes.byref(desc), _ptr(q), _ptr(win_ring), _ptr(comp_cache),
                                   _ptr(pos), _ptr(sink), _ptr(out), _ptr(ws), wsb, _stream(q.device))
     _check(st, "hca_dense_mqa_decode")
+    return out
+
+
+# ------------------------------------------------- query path / output proj
+def csa_query_proj(H, W_DQ, W_UQ, n_heads, W_IUQ=None, W_w=None, n_heads_i=0, g_q=None, eps=1e-6,
+                   ws_slot="query"):
+    """Low-rank query path of n rows of H [n, d] (bf16): returns q [n, n_heads,
+    c], and, with the indexer weights, q^I [n, n_heads_i, c_i] and w^I [n,
+    n_heads_i].  Weights are output-major: W_DQ [d_c, d], W_UQ [n_heads*c,
+    d_c], W_IUQ [n_heads_i*c_i, d_c], W_w [n_heads_i, d]; g_q [d_c] fp32 or
+    None (unit latent-norm weight)."""
+    lib = load()
+    n, d = H.shape
+    dc = W_DQ.shape[0]
+    c = W_UQ.shape[0] // n_heads
+    ci = W_IUQ.shape[0] // n_heads_i if n_heads_i else 0
+    _expect(W_DQ, (dc, d), H.dtype, "W_DQ")
+    _expect(W_UQ, (n_heads * c, dc), H.dtype, "W_UQ")
+    if n_heads_i:
+        _expect(W_IUQ, (n_heads_i * ci, dc), H.dtype, "W_IUQ")
+        _expect(W_w, (n_heads_i, d), H.dtype, "W_w")
+    if g_q is not None:
+        _expect(g_q, (dc,), torch.float32, "g_q")
+    desc = QueryDesc(n, d, dc, n_heads, c, n_heads_i, ci, _dt(H), eps)
+    q = torch.empty((n, n_heads, c), dtype=H.dtype, device=H.device)
+    qI = torch.empty((n, n_heads_i, ci), dtype=H.dtype, device=H.device) if n_heads_i else None
+    wI = torch.empty((n, n_heads_i), dtype=H.dtype, device=H.device) if n_heads_i else None
+    ws, wsb = workspace(workspace_bytes("query_proj", desc), H.device, ws_slot)
+    st = lib.csa_query_proj(ctypes.byref(desc), _ptr(H), _ptr(W_DQ), _ptr(g_q), _ptr(W_w),
+                            _ptr(W_UQ), _ptr(W_IUQ), _ptr(q), _ptr(qI), _ptr(wI), _ptr(ws), wsb,
+                            _stream(H.device))
+    _check(st, "csa_query_proj")
+    return q, qI, wI
+
+
+def csa_output_proj(o, wo_a, wo_b, out=None, ws_slot="oproj"):
+    """Grouped output projection of an attention output o [n, n_heads, c]
+    (bf16): wo_a [groups, d_g, n_heads*c/groups], wo_b [d, groups*d_g];
+    returns out [n, d]."""
+    lib = load()
+    n, nh, c = o.shape
+    g, dg, kg = wo_a.shape
+    d = wo_b.shape[0]
+    if g * kg != nh * c:
+        raise CsaError(f"wo_a: {g} groups of {kg} channels do not cover {nh}x{c}")
+    _expect(wo_b, (d, g * dg), o.dtype, "wo_b")
+    desc = OprojDesc(n, nh, c, g, dg, d, _dt(o))
+    if out is None:
+        out = torch.empty((n, d), dtype=o.dtype, device=o.device)
+    ws, wsb = workspace(workspace_bytes("output_proj", desc), o.device, ws_slot)
+    st = lib.csa_output_proj(ctypes.byref(desc), _ptr(o), _ptr(wo_a), _ptr(wo_b), _ptr(out),
+                             _ptr(ws), wsb, _stream(o.device))
+    _check(st, "csa_output_proj")
     return out

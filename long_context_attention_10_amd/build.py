@@ -12,7 +12,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libcsa.so")
-SOURCES = ["capi.hip", "compress.hip", "index_topk.hip", "attention.hip", "attention_bf16.hip"]
+SOURCES = ["capi.hip", "compress.hip", "index_topk.hip", "attention.hip", "attention_bf16.hip",
+           "layer.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -88,6 +88,31 @@ int check_attn(const csa_attn_desc* d, bool decode, bool sparse) {
   return CSA_OK;
 }
 
+// ------------------------------------------------------- layer projections
+int check_query(const csa_query_desc* d) {
+  if (!d) return CSA_ERR_INVALID_ARG;
+  if (d->dtype != CSA_BF16) return CSA_ERR_UNSUPPORTED;
+  if (d->n < 0 || d->d <= 0 || d->d_c <= 0 || d->n_heads <= 0 || d->c <= 0 ||
+      d->n_heads_i < 0 || d->c_i < 0 || !(d->eps >= 0.f))
+    return CSA_ERR_INVALID_ARG;
+  if (d->d % 64 || d->d_c % 64) return CSA_ERR_UNSUPPORTED;  // K of the two products
+  if ((int64_t)d->n_heads * d->c + (int64_t)d->n_heads_i * d->c_i > (1 << 30))
+    return CSA_ERR_UNSUPPORTED;
+  return CSA_OK;
+}
+
+int check_oproj(const csa_oproj_desc* d) {
+  if (!d) return CSA_ERR_INVALID_ARG;
+  if (d->dtype != CSA_BF16) return CSA_ERR_UNSUPPORTED;
+  if (d->n < 0 || d->n_heads <= 0 || d->c <= 0 || d->groups <= 0 || d->d_g <= 0 || d->d <= 0)
+    return CSA_ERR_INVALID_ARG;
+  const int64_t width = (int64_t)d->n_heads * d->c;
+  if (width % d->groups) return CSA_ERR_INVALID_ARG;
+  if ((width / d->groups) % 64 || ((int64_t)d->groups * d->d_g) % 64) return CSA_ERR_UNSUPPORTED;
+  if (d->groups > 65535) return CSA_ERR_UNSUPPORTED;
+  return CSA_OK;
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? CSA_OK : CSA_ERR_HIP; }
 
 }  // namespace
@@ -145,6 +170,16 @@ size_t csa_workspace_bytes(int entry, const void* desc) {
     }
     case CSA_ENTRY_SPARSE_MQA_PREFILL:
     case CSA_ENTRY_DENSE_MQA_PREFILL: return 0;
+    case CSA_ENTRY_QUERY_PROJ: {
+      const csa_query_desc* d = (const csa_query_desc*)desc;
+      if (d->n <= 0 || d->d_c <= 0) return 0;
+      return query_proj_ws_bytes(*d);
+    }
+    case CSA_ENTRY_OUTPUT_PROJ: {
+      const csa_oproj_desc* d = (const csa_oproj_desc*)desc;
+      if (d->n <= 0 || d->groups <= 0 || d->d_g <= 0) return 0;
+      return output_proj_ws_bytes(*d);
+    }
     case CSA_ENTRY_SPARSE_MQA_DECODE:
     case CSA_ENTRY_DENSE_MQA_DECODE: {
       const csa_attn_desc* d = (const csa_attn_desc*)desc;
@@ -251,6 +286,31 @@ int csa_index_topk_decode(const csa_index_desc* d, const void* qI, const void* w
   if (!ws || ws_bytes < need) return CSA_ERR_WORKSPACE;
   return hip_status(launch_index_topk_decode(*d, qI, wI, KI_cache, pos, idx_out, ws,
                                              (hipStream_t)stream));
+}
+
+int csa_query_proj(const csa_query_desc* d, const void* H, const void* W_DQ, const float* g_q,
+                   const void* W_w, const void* W_UQ, const void* W_IUQ, void* q_out,
+                   void* qI_out, void* wI_out, void* ws, size_t ws_bytes, void* stream) {
+  int s = check_query(d);
+  if (s) return s;
+  const bool idx = d->n_heads_i > 0 && d->c_i > 0;
+  if (!H || !W_DQ || !W_UQ || !q_out) return CSA_ERR_INVALID_ARG;
+  if (d->n_heads_i > 0 && (!W_w || !wI_out)) return CSA_ERR_INVALID_ARG;
+  if (idx && (!W_IUQ || !qI_out)) return CSA_ERR_INVALID_ARG;
+  if (d->n == 0) return CSA_OK;
+  if (!ws || ws_bytes < query_proj_ws_bytes(*d)) return CSA_ERR_WORKSPACE;
+  return hip_status(launch_query_proj(*d, H, W_DQ, g_q, W_w, W_UQ, W_IUQ, q_out, qI_out, wI_out,
+                                      ws, (hipStream_t)stream));
+}
+
+int csa_output_proj(const csa_oproj_desc* d, const void* o, const void* wo_a, const void* wo_b,
+                    void* out, void* ws, size_t ws_bytes, void* stream) {
+  int s = check_oproj(d);
+  if (s) return s;
+  if (!o || !wo_a || !wo_b || !out) return CSA_ERR_INVALID_ARG;
+  if (d->n == 0) return CSA_OK;
+  if (!ws || ws_bytes < output_proj_ws_bytes(*d)) return CSA_ERR_WORKSPACE;
+  return hip_status(launch_output_proj(*d, o, wo_a, wo_b, out, ws, (hipStream_t)stream));
 }
 
 int csa_sparse_mqa_prefill(const csa_attn_desc* d, const void* q, const void* win_kv,

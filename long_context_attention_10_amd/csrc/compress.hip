@@ -133,17 +133,21 @@ __global__ __launch_bounds__(256, 2) void proj_gemm_kernel(
 // so every 16 consecutive rows of a fragment read cover all banks.  Tile
 // order: die x (workgroup id mod 8) takes M blocks x, x+8, ... in groups that
 // its workgroups run side by side, so the A and W slices they stream are
-// shared in the die's L2.
+// shared in the die's L2.  Each stacked weight matrix writes its columns to
+// its own output (fp32 or bf16, rounded once); blockIdx.y selects a group of
+// a grouped product (A, W0 and output 0 offset per group).
 // ===========================================================================
 constexpr int kGM = 256, kGN = 256;  // output tile
 constexpr int kGKB = 64;             // bytes of K per slice (32 bf16)
 constexpr int kGS = 4;               // LDS stages
 constexpr int kGAhead = kGS - 1;     // slices in flight ahead of the one in use
 
+template <class OUT>
 __global__ __launch_bounds__(512, 1) void proj_gemm_bf16_kernel(
-    const uint16_t* __restrict__ A, int64_t M, int K, const uint16_t* __restrict__ W0, int r0,
-    const uint16_t* __restrict__ W1, int r1, const uint16_t* __restrict__ W2, int r2,
-    float* __restrict__ out, int64_t ldo, int mblocks, int ntiles) {
+    const uint16_t* __restrict__ A, int64_t lda, int64_t M, int K,
+    const uint16_t* __restrict__ W0, int r0, const uint16_t* __restrict__ W1, int r1,
+    const uint16_t* __restrict__ W2, int r2, GemmOuts outs, int mblocks, int ntiles,
+    int64_t a_zoff, int64_t w_zoff, int64_t o_zoff) {
   __shared__ __align__(16) uint8_t sA[kGS][kGM * kGKB];
   __shared__ __align__(16) uint8_t sB[kGS][kGN * kGKB];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -169,6 +173,8 @@ __global__ __launch_bounds__(512, 1) void proj_gemm_bf16_kernel(
   const int64_t m0 = (int64_t)mbk * kGM;
   const int n0 = nt * kGN;
   const int ntot = r0 + r1 + r2;
+  A += blockIdx.y * a_zoff;
+  W0 += blockIdx.y * w_zoff;
 
   // Loads: wave w fills 1 KiB chunks w and w+8 (16 rows each) of both
   // panels; lane i of chunk c carries row 16c + i/4 into LDS column i%4,
@@ -180,7 +186,7 @@ __global__ __launch_bounds__(512, 1) void proj_gemm_bf16_kernel(
     const int row = 16 * (wave + 8 * u) + (lane >> 2);
     const int gran = (lane & 3) ^ ((row >> 2) & 3);
     const int64_t ar = min64(m0 + row, M - 1);  // rows past M read a valid row
-    pa[u] = (const uint8_t*)(A + ar * K) + gran * 16;
+    pa[u] = (const uint8_t*)(A + ar * lda) + gran * 16;
     int n = n0 + row;
     const uint16_t* wp = W0;
     if (n >= ntot) n = 0;  // masked columns read a valid row
@@ -255,16 +261,24 @@ __global__ __launch_bounds__(512, 1) void proj_gemm_bf16_kernel(
   }
 
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int j = 0; j < 4; ++j) {
+    const int col = n0 + wn * 128 + j * 32 + frow;
+    int cm = col;  // column within its weight matrix
+    OUT* op = (OUT*)outs.p[0] + blockIdx.y * o_zoff;
+    int64_t ld = outs.ld[0];
+    if (cm >= r0 + r1) { cm -= r0 + r1; op = (OUT*)outs.p[2]; ld = outs.ld[2]; }
+    else if (cm >= r0) { cm -= r0; op = (OUT*)outs.p[1]; ld = outs.ld[1]; }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = n0 + wn * 128 + j * 32 + frow;
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int64_t row = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * fhalf + (e & 3);
-        if (row < M && col < ntot) out[row * ldo + col] = acc[i][j][e];
+        if (row < M && col < ntot) {
+          if constexpr (sizeof(OUT) == 2) op[row * ld + cm] = f32_to_bf16(acc[i][j][e]);
+          else op[row * ld + cm] = acc[i][j][e];
+        }
       }
-    }
+  }
 }
 
 // ===========================================================================
@@ -618,17 +632,38 @@ __global__ __launch_bounds__(256) void decode_update_kernel(
 // ===========================================================================
 // Host launchers
 // ===========================================================================
+hipError_t launch_gemm_bf16(const void* A, int64_t lda, int64_t M, int K, const WeightStack& w,
+                            const GemmOuts& outs, bool bf16_out, int groups, int64_t a_zoff,
+                            int64_t w_zoff, int64_t o_zoff, hipStream_t st) {
+  const int N = w.total();
+  if (M == 0 || N == 0 || groups == 0) return hipSuccess;
+  const int mblocks = (int)((M + kGM - 1) / kGM), ntiles = (N + kGN - 1) / kGN;
+  const int mgroups = ((mblocks + 7) / 8 + 7) / 8;  // groups of 8 M blocks per die
+  const dim3 g((unsigned)(8 * mgroups * 8 * ntiles), (unsigned)groups);
+  if (bf16_out)
+    proj_gemm_bf16_kernel<uint16_t><<<g, 512, 0, st>>>(
+        (const uint16_t*)A, lda, M, K, (const uint16_t*)w.w[0], w.rows[0],
+        (const uint16_t*)w.w[1], w.rows[1], (const uint16_t*)w.w[2], w.rows[2], outs, mblocks,
+        ntiles, a_zoff, w_zoff, o_zoff);
+  else
+    proj_gemm_bf16_kernel<float><<<g, 512, 0, st>>>(
+        (const uint16_t*)A, lda, M, K, (const uint16_t*)w.w[0], w.rows[0],
+        (const uint16_t*)w.w[1], w.rows[1], (const uint16_t*)w.w[2], w.rows[2], outs, mblocks,
+        ntiles, a_zoff, w_zoff, o_zoff);
+  return hipGetLastError();
+}
+
 hipError_t launch_proj_gemm(int dtype, const void* A, int64_t M, int K, const WeightStack& w,
                             float* out, int64_t ldo, hipStream_t st) {
   const int N = w.total();
   dim3 grid((N + 127) / 128, (unsigned)((M + 127) / 128));
   if (dtype == CSA_BF16) {
-    const int mblocks = (int)((M + kGM - 1) / kGM), ntiles = (N + kGN - 1) / kGN;
-    const int mgroups = ((mblocks + 7) / 8 + 7) / 8;  // groups of 8 M blocks per die
-    const unsigned g = (unsigned)(8 * mgroups * 8 * ntiles);
-    proj_gemm_bf16_kernel<<<g, 512, 0, st>>>(
-        (const uint16_t*)A, M, K, (const uint16_t*)w.w[0], w.rows[0], (const uint16_t*)w.w[1],
-        w.rows[1], (const uint16_t*)w.w[2], w.rows[2], out, ldo, mblocks, ntiles);
+    GemmOuts o;
+    o.p[0] = out;
+    o.p[1] = out + w.rows[0];
+    o.p[2] = out + w.rows[0] + w.rows[1];
+    o.ld[0] = o.ld[1] = o.ld[2] = ldo;
+    return launch_gemm_bf16(A, K, M, K, w, o, false, 1, 0, 0, 0, st);
   } else {
     proj_gemm_kernel<F32><<<grid, 256, 0, st>>>((const float*)A, M, K, (const float*)w.w[0],
                                                  w.rows[0], (const float*)w.w[1], w.rows[1],

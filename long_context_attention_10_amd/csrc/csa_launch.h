@@ -17,6 +17,20 @@ struct WeightStack {
   int total() const { return rows[0] + rows[1] + rows[2]; }
 };
 
+// Outputs of a stacked product: matrix i writes its columns to p[i] with row
+// stride ld[i] (elements of the output type).
+struct GemmOuts {
+  void* p[3];
+  int64_t ld[3];
+};
+
+// bf16 operands: for each group z < groups, out_i = A_z[M, K] . W_i^T where
+// A_z = A + z * a_zoff (row stride lda), W_0 is offset by z * w_zoff and
+// output 0 by z * o_zoff; fp32 or bf16 (rounded once) outputs.  K % 64 == 0.
+hipError_t launch_gemm_bf16(const void* A, int64_t lda, int64_t M, int K, const WeightStack& w,
+                            const GemmOuts& outs, bool bf16_out, int groups, int64_t a_zoff,
+                            int64_t w_zoff, int64_t o_zoff, hipStream_t st);
+
 // out[M, ldo] (fp32, columns [0, stack.total())) = A[M, K] . stack^T
 hipError_t launch_proj_gemm(int dtype, const void* A, int64_t M, int K, const WeightStack& ws,
                             float* out, int64_t ldo, hipStream_t st);
@@ -85,5 +99,15 @@ hipError_t launch_mqa_decode_bf16(const csa_attn_desc& d, int mode, const void* 
 hipError_t launch_mqa_decode(const csa_attn_desc& d, int mode, const void* q, const void* ring,
                              const void* cache, const int32_t* idx, const int64_t* pos,
                              const float* sink, void* out, void* ws, hipStream_t st);
+
+// The layer around the attention calls (layer.hip).
+size_t query_proj_ws_bytes(const csa_query_desc& d);
+hipError_t launch_query_proj(const csa_query_desc& d, const void* H, const void* W_DQ,
+                             const float* g_q, const void* W_w, const void* W_UQ,
+                             const void* W_IUQ, void* q_out, void* qI_out, void* wI_out,
+                             void* ws, hipStream_t st);
+size_t output_proj_ws_bytes(const csa_oproj_desc& d);
+hipError_t launch_output_proj(const csa_oproj_desc& d, const void* o, const void* wo_a,
+                              const void* wo_b, void* out, void* ws, hipStream_t st);
 
 }  // namespace csa

@@ -160,3 +160,25 @@ def test_binding_keeps_the_zero_region(lib):
     assert t4.numel() == 8192 and int(torch.count_nonzero(t4[:1024])) == 0
     L._WS.pop(key, None)
     L._WS_ZERO.pop(key, None)
+
+
+def test_layer_projection_calls_reject(lib):
+    q = L.QueryDesc(64, 256, 128, 8, 128, 4, 64, L.CSA_BF16, 1e-6)
+    args = [_p()] * 10 + [1 << 40, None]
+    bad = L.QueryDesc(64, 256, 128, 8, 128, 4, 64, L.CSA_F32, 1e-6)
+    assert lib.csa_query_proj(ctypes.byref(bad), *args) == -2      # bf16 only
+    bad = L.QueryDesc(64, 100, 128, 8, 128, 4, 64, L.CSA_BF16, 1e-6)
+    assert lib.csa_query_proj(ctypes.byref(bad), *args) == -2      # d not a multiple of 64
+    assert lib.csa_query_proj(None, *args) == -1
+    assert lib.csa_query_proj(ctypes.byref(q), None, *([_p()] * 9), 1 << 40, None) == -1  # H
+    assert lib.csa_query_proj(ctypes.byref(q), *([_p()] * 9), None, 0, None) == -3  # no ws
+    o = L.OprojDesc(64, 8, 128, 2, 64, 256, L.CSA_BF16)
+    oargs = [_p()] * 5 + [1 << 40, None]
+    bad = L.OprojDesc(64, 8, 128, 3, 64, 256, L.CSA_BF16)
+    assert lib.csa_output_proj(ctypes.byref(bad), *oargs) == -1   # groups must divide 8*128
+    bad = L.OprojDesc(64, 8, 128, 32, 64, 256, L.CSA_BF16)
+    assert lib.csa_output_proj(ctypes.byref(bad), *oargs) == -2   # 32-channel groups
+    assert lib.csa_output_proj(ctypes.byref(o), None, _p(), _p(), _p(), _p(), 1 << 40, None) == -1
+    assert lib.csa_output_proj(ctypes.byref(o), _p(), _p(), _p(), _p(), None, 0, None) == -3
+    assert L.workspace_bytes("output_proj", o) == 64 * 2 * 64 * 2
+    assert L.workspace_bytes("query_proj", q) >= 64 * (128 + 4) * 4 + 64 * 128 * 2
