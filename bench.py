@@ -172,6 +172,61 @@ def pmc_probe():
 # --------------------------------------------------------------------------
 # decode (CSA layer + HCA layer, one token per sequence)
 # --------------------------------------------------------------------------
+class CsaLayer:
+    """The whole CSA layer forward of one prefill workload: the query path
+    (latent RMSNorm, q, q^I, w^I), the four calls, and the grouped output
+    projection.  Shares the prefill's compressed-entry buffers; its own q, q^I
+    and w^I come from H."""
+
+    def __init__(self, pf, device="cuda", seed=0):
+        self.pf = pf
+        c = pf.cfg
+        n, d, nh, cc, hI, cI = c["n"], c["d"], c["nh"], c["c"], c["hI"], c["cI"]
+        dc, g, dg = c["d_c"], c["groups"], c["d_g"]
+        name, kw = c["name"], dict(dtype=c["dtype"], device=device)
+        dt = I.TORCH_DTYPES[c["dtype"]]
+        kg = nh * cc // g
+        self.w = dict(
+            W_DQ=I.normal((dc, d), (seed, name, "W_DQ"), std=d ** -0.5, **kw),
+            g_q=1.0 + 0.1 * I.normal((dc,), (seed, name, "g_q"), device=device),
+            W_UQ=I.normal((nh * cc, dc), (seed, name, "W_UQ"), std=dc ** -0.5, **kw),
+            W_IUQ=I.normal((hI * cI, dc), (seed, name, "W_IUQ"), std=dc ** -0.5, **kw),
+            W_w=I.normal((hI, d), (seed, name, "W_w"), std=d ** -0.5, **kw),
+            wo_a=I.normal((g, dg, kg), (seed, name, "wo_a"), std=kg ** -0.5, **kw),
+            wo_b=I.normal((d, g * dg), (seed, name, "wo_b"), std=(g * dg) ** -0.5, **kw))
+        self.q = torch.empty((n, nh, cc), dtype=dt, device=device)
+        self.qI = torch.empty((n, hI, cI), dtype=dt, device=device)
+        self.wI = torch.empty((n, hI), dtype=dt, device=device)
+        self.y = torch.empty((n, d), dtype=dt, device=device)
+
+    def qproj(self):
+        c, w = self.pf.cfg, self.w
+        L.csa_query_proj(self.pf.t["H"], w["W_DQ"], w["W_UQ"], c["nh"], W_IUQ=w["W_IUQ"],
+                         W_w=w["W_w"], n_heads_i=c["hI"], g_q=w["g_q"], eps=c["eps"],
+                         out=(self.q, self.qI, self.wI))
+
+    def oproj(self):
+        L.csa_output_proj(self.pf.out, self.w["wo_a"], self.w["wo_b"], out=self.y)
+
+    def step(self):
+        pf, c = self.pf, self.pf.cfg
+        self.qproj()
+        pf.compress()
+        L.csa_index_topk_prefill(self.qI, self.wI, pf.kI, c["m"], c["k"], out=pf.idx)
+        L.csa_sparse_mqa_prefill(self.q, pf.win, pf.comp, pf.idx, pf.t["sink"], n_win=c["n_win"],
+                                 rope_dims=c["rope_dims"], out=pf.out)
+        self.oproj()
+
+    def proj_flops(self):
+        """(query path, output projection) matrix FLOPs: 2 per multiply-add."""
+        c = self.pf.cfg
+        n, d, dc, hI, cI = c["n"], c["d"], c["d_c"], c["hI"], c["cI"]
+        width = c["nh"] * c["c"]
+        qf = 2.0 * n * d * (dc + hI) + 2.0 * n * dc * (width + hI * cI)
+        of = 2.0 * n * width * c["d_g"] + 2.0 * n * c["groups"] * c["d_g"] * d
+        return qf, of
+
+
 class HybridDecode:
     """State for B sequences at position t = ctx-1 (caches hold [0, t))."""
 
@@ -393,6 +448,25 @@ def main():
                                     f"{pairs} (token, candidate) pairs"},
     }
     del att_t
+    # the whole layer around the four calls (query path and output projection
+    # added), on the same workload
+    print("[bench] timing the full CSA layer", file=sys.stderr, flush=True)
+    lay = CsaLayer(pf, dev)
+    lay_ms = float(np.mean(time_region(lay.step, a.steps, a.warmup)))
+    qp_ms = float(np.mean(time_region(lay.qproj, max(3, a.steps), 1)))
+    op_ms = float(np.mean(time_region(lay.oproj, max(3, a.steps), 1)))
+    qf, of = lay.proj_flops()
+    rec["layer"] = {
+        "workload": cfg["name"] + " + query path + grouped output projection",
+        "widths": {"d_c": cfg["d_c"], "groups": cfg["groups"], "d_g": cfg["d_g"]},
+        "ms_per_step": lay_ms, "tokens_per_s": n / (lay_ms * 1e-3),
+        "stages_ms": {"query_proj": qp_ms, "output_proj": op_ms},
+        "query_proj_tflops": qf / (qp_ms * 1e-3) / 1e12,
+        "output_proj_tflops": of / (op_ms * 1e-3) / 1e12,
+        "output_proj_frac": of / (op_ms * 1e-3) / PEAK_BF16,
+        "algorithmic": f"query path {qf:.4g} FLOP, output projection {of:.4g} FLOP per step"}
+    del lay
+    torch.cuda.empty_cache()
     if not a.no_decode:
         dec = {}
         flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)

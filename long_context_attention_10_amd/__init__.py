@@ -388,12 +388,12 @@ def hca_dense_mqa_decode(q, win_ring, comp_cache, pos, sink, m, scale=None, qk_n
 
 # ------------------------------------------------- query path / output proj
 def csa_query_proj(H, W_DQ, W_UQ, n_heads, W_IUQ=None, W_w=None, n_heads_i=0, g_q=None, eps=1e-6,
-                   ws_slot="query"):
+                   out=None, ws_slot="query"):
     """Low-rank query path of n rows of H [n, d] (bf16): returns q [n, n_heads,
     c], and, with the indexer weights, q^I [n, n_heads_i, c_i] and w^I [n,
     n_heads_i].  Weights are output-major: W_DQ [d_c, d], W_UQ [n_heads*c,
     d_c], W_IUQ [n_heads_i*c_i, d_c], W_w [n_heads_i, d]; g_q [d_c] fp32 or
-    None (unit latent-norm weight)."""
+    None (unit latent-norm weight).  `out` may give the (q, q^I, w^I) buffers."""
     lib = load()
     n, d = H.shape
     dc = W_DQ.shape[0]
@@ -407,9 +407,16 @@ def csa_query_proj(H, W_DQ, W_UQ, n_heads, W_IUQ=None, W_w=None, n_heads_i=0, g_
     if g_q is not None:
         _expect(g_q, (dc,), torch.float32, "g_q")
     desc = QueryDesc(n, d, dc, n_heads, c, n_heads_i, ci, _dt(H), eps)
-    q = torch.empty((n, n_heads, c), dtype=H.dtype, device=H.device)
-    qI = torch.empty((n, n_heads_i, ci), dtype=H.dtype, device=H.device) if n_heads_i else None
-    wI = torch.empty((n, n_heads_i), dtype=H.dtype, device=H.device) if n_heads_i else None
+    if out is not None:
+        q, qI, wI = out
+        _expect(q, (n, n_heads, c), H.dtype, "q out")
+        if n_heads_i:
+            _expect(qI, (n, n_heads_i, ci), H.dtype, "qI out")
+            _expect(wI, (n, n_heads_i), H.dtype, "wI out")
+    else:
+        q = torch.empty((n, n_heads, c), dtype=H.dtype, device=H.device)
+        qI = torch.empty((n, n_heads_i, ci), dtype=H.dtype, device=H.device) if n_heads_i else None
+        wI = torch.empty((n, n_heads_i), dtype=H.dtype, device=H.device) if n_heads_i else None
     ws, wsb = workspace(workspace_bytes("query_proj", desc), H.device, ws_slot)
     st = lib.csa_query_proj(ctypes.byref(desc), _ptr(H), _ptr(W_DQ), _ptr(g_q), _ptr(W_w),
                             _ptr(W_UQ), _ptr(W_IUQ), _ptr(q), _ptr(qI), _ptr(wI), _ptr(ws), wsb,

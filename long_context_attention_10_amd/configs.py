@@ -17,7 +17,10 @@ WORKLOADS = {
         hI=0, cI=0, k=0, nh=64, rope_dims=0),
     "csa_prefill_64k_bf16": dict(
         COMMON, kind="csa_prefill", dtype="bf16", n=65536, d=4096, c=512, m=4, overlap=1,
-        hI=16, cI=64, k=512, nh=64, rope_dims=64),
+        hI=16, cI=64, k=512, nh=64, rope_dims=64,
+        # the layer around the calls: query latent width, output groups and
+        # their width (the pages' V4-Flash values)
+        d_c=1024, groups=8, d_g=1024),
     "decode_b32_128k_bf16": dict(
         COMMON, kind="decode", dtype="bf16", batch=32, ctx=131072, d=4096, c=512, m=4,
         overlap=1, m_hca=128, hI=16, cI=64, k=512, nh=64, rope_dims=0),
