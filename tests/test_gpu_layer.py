@@ -10,7 +10,7 @@ import torch
 
 from oracle import csa_oracle as O
 from long_context_attention_10_amd import inputs as I
-from parity_util import f64
+from parity_util import assert_out_close, check_topk_sets, f64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -107,3 +107,86 @@ def test_layer_projections_full_width_sampled(lib):
     _close(wI[rows], rwI, "wI")
     ref = O.output_proj(f64(q[rows]).reshape(len(rows), -1), f64(wo_a), f64(wo_b), O.round_bf16)
     _close(out[rows], ref, "out")
+
+
+def _chain_inputs(key, n, d, c, m, ov, hI, cI, nh, dc, g, dg):
+    sd = d ** -0.5
+    w = (1 + ov) * c
+    t = dict(
+        H=I.normal((n, d), key + ("H",), dtype="bf16", device=DEV),
+        W_kv=I.normal((w, d), key + ("W_kv",), std=sd, dtype="bf16", device=DEV),
+        W_z=I.normal((w, d), key + ("W_z",), std=sd, dtype="bf16", device=DEV),
+        ape=I.normal((m, w), key + ("ape",), device=DEV),
+        W_win=I.normal((c, d), key + ("W_win",), std=sd, dtype="bf16", device=DEV),
+        sink=I.normal((nh,), key + ("sink",), device=DEV),
+        wo_a=I.normal((g, dg, nh * c // g), key + ("wo_a",), std=(nh * c // g) ** -0.5,
+                      dtype="bf16", device=DEV),
+        wo_b=I.normal((d, g * dg), key + ("wo_b",), std=(g * dg) ** -0.5, dtype="bf16",
+                      device=DEV))
+    if hI:
+        wi = (1 + ov) * cI
+        t.update(WI_kv=I.normal((wi, d), key + ("WI_kv",), std=sd, dtype="bf16", device=DEV),
+                 WI_z=I.normal((wi, d), key + ("WI_z",), std=sd, dtype="bf16", device=DEV),
+                 apeI=I.normal((m, wi), key + ("apeI",), device=DEV))
+    t.update(_weights(key, d, dc, nh, c, max(hI, 1), max(cI, 64), True))
+    return t
+
+
+def test_csa_layer_forward_chained(lib):
+    """A whole bf16 CSA layer through the binding: query path -> compressors ->
+    indexer top-k -> sparse MQA -> grouped output projection.  Each stage is
+    checked against the oracle on the inputs the GPU stage received (so a
+    near-tie in the selection cannot make later stages disagree)."""
+    n, d, c, m, ov, hI, cI, nh, k, r = 512, 256, 128, 4, 1, 4, 64, 8, 32, 32
+    dc, g, dg = 128, 2, 128
+    _say("csa layer chained", n)
+    t = _chain_inputs(("layer-chain", n), n, d, c, m, ov, hI, cI, nh, dc, g, dg)
+    q, qI, wI = lib.csa_query_proj(t["H"], t["W_DQ"], t["W_UQ"], nh, W_IUQ=t["W_IUQ"],
+                                   W_w=t["W_w"], n_heads_i=hI, g_q=t["g_q"])
+    main = lib.csa_compress_prefill(t["H"], t["W_kv"], t["W_z"], t["ape"], m, ov, W_win=t["W_win"],
+                                    rope_dims=r)
+    kidx = lib.csa_compress_prefill(t["H"], t["WI_kv"], t["WI_z"], t["apeI"], m, ov)
+    idx = lib.csa_index_topk_prefill(qI, wI, kidx["comp"], m, k)
+    att = lib.csa_sparse_mqa_prefill(q, main["win"], main["comp"], idx, t["sink"], rope_dims=r)
+    y = lib.csa_output_proj(att, t["wo_a"], t["wo_b"])
+    torch.cuda.synchronize()
+    _, rq, rqI, rwI = _oracle_q(t["H"], t, 1e-6)
+    _close(q.reshape(n, -1), rq, "q")
+    _close(qI.reshape(n, -1), rqI, "qI")
+    _close(wI, rwI, "wI")
+    H = f64(t["H"])
+    KI = O.compress_prefill(H, f64(t["WI_kv"]).T, f64(t["WI_z"]).T, f64(t["apeI"]), m, ov,
+                            store="bf16")
+    sc = O.index_scores(f64(qI), f64(wI), f64(kidx["comp"]), m)
+    check_topk_sets(idx.cpu().numpy(), sc, k, m)
+    _close(kidx["comp"], KI, "indexer keys")
+    ref_att = O.sparse_mqa_prefill(f64(q), f64(main["win"]), f64(main["comp"]), idx.cpu().numpy(),
+                                   f64(t["sink"]), 128, c ** -0.5, rope_dims=r, store="bf16")
+    assert_out_close(att, ref_att, "bf16", "attention")
+    ref_y = O.output_proj(f64(att).reshape(n, -1), f64(t["wo_a"]), f64(t["wo_b"]), O.round_bf16)
+    _close(y, ref_y, "layer output")
+
+
+def test_hca_layer_forward_chained(lib):
+    """The HCA layer: query path without an indexer -> compressor -> dense MQA
+    -> grouped output projection, chained as above."""
+    n, d, c, m, nh, r = 640, 256, 128, 128, 8, 0
+    dc, g, dg = 128, 4, 64
+    _say("hca layer chained", n)
+    t = _chain_inputs(("hca-layer-chain", n), n, d, c, m, 0, 0, 0, nh, dc, g, dg)
+    q, qI, wI = lib.csa_query_proj(t["H"], t["W_DQ"], t["W_UQ"], nh, g_q=t["g_q"])
+    assert qI is None and wI is None
+    main = lib.csa_compress_prefill(t["H"], t["W_kv"], t["W_z"], t["ape"], m, 0, W_win=t["W_win"])
+    att = lib.hca_dense_mqa_prefill(q, main["win"], main["comp"], t["sink"], m)
+    y = lib.csa_output_proj(att, t["wo_a"], t["wo_b"])
+    torch.cuda.synchronize()
+    H = f64(t["H"])
+    g_ = f64(t["g_q"])
+    cq = O.rms_norm(H @ f64(t["W_DQ"]).T, 1e-6) * g_
+    rq = O.round_bf16(O.round_bf16(cq) @ f64(t["W_UQ"]).T)
+    _close(q.reshape(n, -1), rq, "q")
+    ref_att = O.dense_mqa_prefill(f64(q), f64(main["win"]), f64(main["comp"]), f64(t["sink"]), m,
+                                  128, c ** -0.5, store="bf16")
+    assert_out_close(att, ref_att, "bf16", "attention")
+    ref_y = O.output_proj(f64(att).reshape(n, -1), f64(t["wo_a"]), f64(t["wo_b"]), O.round_bf16)
+    _close(y, ref_y, "layer output")
