@@ -448,6 +448,21 @@ def main():
                                     f"{pairs} (token, candidate) pairs"},
     }
     del att_t
+    # selection on bf16-rounded index scores ([R] section 4.4): its time and
+    # its recall of the fp32-score selection, row by row (-1 slots excluded)
+    idx32 = pf.idx.clone()
+    idx16 = torch.empty_like(idx32)
+
+    def index_bf16():
+        L.csa_index_topk_prefill(pf.t["qI"], pf.t["wI"], pf.kI, cfg["m"], cfg["k"], out=idx16,
+                                 scores="bf16")
+    ib_ms = float(np.mean(time_region(index_bf16, max(3, a.steps), 1)))
+    pos = torch.searchsorted(idx16, idx32).clamp_(max=idx16.shape[1] - 1)
+    hit = (idx16.gather(1, pos) == idx32) & (idx32 >= 0)
+    rec["index_bf16_scores"] = {
+        "index_topk_ms": ib_ms, "index_topk_fp32_ms": idx_ms, "speedup": idx_ms / ib_ms,
+        "recall_of_fp32_selection": float(hit.sum().item()) / float((idx32 >= 0).sum().item())}
+    del idx32, idx16, pos, hit
     # the whole layer around the four calls (query path and output projection
     # added), on the same workload
     print("[bench] timing the full CSA layer", file=sys.stderr, flush=True)

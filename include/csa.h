@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 2
+#define CSA_ABI_VERSION 3
 
 typedef enum csa_status {
   CSA_OK = 0,
@@ -97,6 +97,10 @@ typedef struct csa_index_desc {
   int32_t k;           /* top-k, 1..2048                                     */
   int32_t dtype;       /* csa_dtype of qI, wI and the keys                  */
   int64_t n_entries;   /* prefill: rows of KI; decode: cache rows per seq   */
+  int32_t score_dtype; /* prefill: CSA_F32, or CSA_BF16 to select on index
+                          scores rounded to bf16 ([R] section 4.4: bf16
+                          index scores for a faster selector); decode:
+                          CSA_F32                                           */
 } csa_index_desc;
 
 /* Shared-KV multi-query core attention with window and sink ([R] eq 18-19,

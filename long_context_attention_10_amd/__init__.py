@@ -41,7 +41,8 @@ class CompressDesc(ctypes.Structure):
 class IndexDesc(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int64), ("batch", ctypes.c_int32), ("n_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("m", ctypes.c_int32), ("k", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("n_entries", ctypes.c_int64)]
+                ("dtype", ctypes.c_int32), ("n_entries", ctypes.c_int64),
+                ("score_dtype", ctypes.c_int32)]
 
 
 class QueryDesc(ctypes.Structure):
@@ -261,14 +262,16 @@ def csa_compress_decode(h, pos, W_kv, W_z, ape, m, overlap, state, cache, W_win=
 
 
 # ----------------------------------------------------------------- indexer
-def csa_index_topk_prefill(qI, wI, KI, m, k, out=None):
-    """idx [n, k] int32: per token, the top-k visible entries (ascending), -1 padded."""
+def csa_index_topk_prefill(qI, wI, KI, m, k, out=None, scores="f32"):
+    """idx [n, k] int32: per token, the top-k visible entries (ascending), -1
+    padded.  scores="bf16" selects on index scores rounded to bf16."""
     lib = load()
     n, hI, cI = qI.shape
     _expect(wI, (n, hI), qI.dtype, "wI")
     ne = KI.shape[0]
     _expect(KI, (ne, cI), qI.dtype, "KI")
-    desc = IndexDesc(n, 1, hI, cI, m, k, _dt(qI), ne)
+    sdt = {"f32": CSA_F32, "bf16": CSA_BF16}[scores]
+    desc = IndexDesc(n, 1, hI, cI, m, k, _dt(qI), ne, sdt)
     if out is None:
         out = torch.empty((n, k), dtype=torch.int32, device=qI.device)
     ws, wsb = workspace(workspace_bytes("index_topk_prefill", desc), qI.device, "index")

@@ -56,7 +56,9 @@ int check_index(const csa_index_desc* d, bool decode) {
   if (!(d->n_heads == 4 || d->n_heads == 8 || d->n_heads == 16)) return CSA_ERR_UNSUPPORTED;
   if (!(d->head_dim == 64 || d->head_dim == 128)) return CSA_ERR_UNSUPPORTED;
   if (d->k > 2048) return CSA_ERR_UNSUPPORTED;
+  if (d->score_dtype != CSA_F32 && d->score_dtype != CSA_BF16) return CSA_ERR_UNSUPPORTED;
   if (decode) {
+    if (d->score_dtype != CSA_F32) return CSA_ERR_UNSUPPORTED;
     if (d->batch <= 0) return CSA_ERR_INVALID_ARG;
     if (d->n_entries >= (int64_t)1 << 31) return CSA_ERR_UNSUPPORTED;
   } else {
@@ -161,7 +163,7 @@ size_t csa_workspace_bytes(int entry, const void* desc) {
     case CSA_ENTRY_INDEX_TOPK_PREFILL: {
       const csa_index_desc* d = (const csa_index_desc*)desc;
       if (d->m <= 0 || d->n <= 0) return 0;
-      return al((size_t)d->n * index_prefill_ld(d) * 4);
+      return al((size_t)d->n * index_prefill_ld(d) * (d->score_dtype == CSA_BF16 ? 2 : 4));
     }
     case CSA_ENTRY_INDEX_TOPK_DECODE: {
       const csa_index_desc* d = (const csa_index_desc*)desc;
@@ -267,13 +269,13 @@ int csa_index_topk_prefill(const csa_index_desc* d, const void* qI, const void* 
   if (d->n == 0) return CSA_OK;
   if (!qI || !wI || !idx_out || (d->n_entries > 0 && !KI)) return CSA_ERR_INVALID_ARG;
   const int64_t ld = index_prefill_ld(d);
-  const size_t need = al((size_t)d->n * ld * 4);
+  const size_t need = al((size_t)d->n * ld * (d->score_dtype == CSA_BF16 ? 2 : 4));
   if (ld > 0 && (!ws || ws_bytes < need)) return CSA_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = hipSuccess;
-  if (ld > 0) e = launch_index_scores_prefill(*d, qI, wI, KI, (float*)ws, ld, st);
+  if (ld > 0) e = launch_index_scores_prefill(*d, qI, wI, KI, ws, ld, st);
   if (e != hipSuccess) return CSA_ERR_HIP;
-  return hip_status(launch_topk_rows_prefill(*d, (const float*)ws, ld, idx_out, st));
+  return hip_status(launch_topk_rows_prefill(*d, ws, ld, idx_out, st));
 }
 
 int csa_index_topk_decode(const csa_index_desc* d, const void* qI, const void* wI,

@@ -66,10 +66,11 @@ hipError_t launch_decode_update(int dtype, const float* part, int ksplit, int B,
 int decode_proj_ksplit(int N, int K, int dtype);
 
 // ------------------------------------------------------------- indexer
+// scores: [n, ld] of d.score_dtype (fp32, or bf16 rounded once)
 hipError_t launch_index_scores_prefill(const csa_index_desc& d, const void* qI, const void* wI,
-                                       const void* KI, float* scores, int64_t ld,
+                                       const void* KI, void* scores, int64_t ld,
                                        hipStream_t st);
-hipError_t launch_topk_rows_prefill(const csa_index_desc& d, const float* scores, int64_t ld,
+hipError_t launch_topk_rows_prefill(const csa_index_desc& d, const void* scores, int64_t ld,
                                     int32_t* idx_out, hipStream_t st);
 
 size_t index_decode_ws_bytes(const csa_index_desc& d);

@@ -24,11 +24,11 @@ namespace csa {
 // the 16 lanes of a B-fragment read (16 keys, one granule each) hit distinct
 // banks.  The head reduction with the ReLU and weights happens in registers.
 // ===========================================================================
-template <class T, int HI, int CI>
+template <class T, int HI, int CI, class SC>
 __global__ __launch_bounds__(256) void index_scores_prefill_kernel(
     const typename T::S* __restrict__ qI, const typename T::S* __restrict__ wI,
     const typename T::S* __restrict__ KI, int64_t n, int64_t n_entries, int m, int key_chunk,
-    float* __restrict__ scores, int64_t ld) {
+    SC* __restrict__ scores, int64_t ld) {
   typedef typename T::S S;
   constexpr int E = 16 / (int)sizeof(S);
   constexpr int KGE = 2 * E;        // elements per 32x32 k-group
@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256) void index_scores_prefill_kernel(
   wait_vmem();
   __syncthreads();
   // rows of this workgroup's queries: one uniform base, 32-bit offsets
-  float* srow0 = scores + q0 * ld;
+  SC* srow0 = scores + q0 * ld;
   const int ld32 = (int)ld;
 
   const int nblk = (int)((kend - kbeg + KB - 1) / KB);
@@ -137,7 +137,10 @@ __global__ __launch_bounds__(256) void index_scores_prefill_kernel(
         // rows of this block's first query relative to the workgroup's first
         const int tr = (wave * (RB * 32) + rb * 32) / HI;
         auto put = [&](int tq, int vq, float v) {  // query q0 + tq, visible count vq
-          if (sok && si < vq) srow0[(uint32_t)(tq * ld32 + si)] = v;
+          if (sok && si < vq) {
+            if constexpr (sizeof(SC) == 2) srow0[(uint32_t)(tq * ld32 + si)] = f32_to_bf16(v);
+            else srow0[(uint32_t)(tq * ld32 + si)] = v;
+          }
         };
         if (HI == 4) {  // each group of 4 rows is one whole query
 #pragma unroll
@@ -279,8 +282,8 @@ CSA_DEV uint64_t composite(uint32_t key, uint32_t idx) {
   return ((uint64_t)key << 32) | (uint32_t)~idx;
 }
 
-template <int MAXIT, int Q>
-__global__ __launch_bounds__(256) void topk_rows_prefill_kernel(const float* __restrict__ scores,
+template <int MAXIT, int Q, class SC>
+__global__ __launch_bounds__(256) void topk_rows_prefill_kernel(const SC* __restrict__ scores,
                                                                 int64_t ld, int64_t n,
                                                                 int64_t n_entries, int m, int k,
                                                                 int32_t* __restrict__ idx_out,
@@ -305,9 +308,9 @@ __global__ __launch_bounds__(256) void topk_rows_prefill_kernel(const float* __r
   // keys (coalesced 16-byte loads, all in flight together; the row start is
   // 16-byte aligned and ld % 4 == 0).  Entries past v get key 0, below every
   // real key.
-  const float* srow = scores + (int64_t)t * ld;
+  const SC* srow = scores + (int64_t)t * ld;
   uint32_t u[MAXIT];
-  {
+  if constexpr (sizeof(SC) == 4) {
     float4 xs[NQ];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
@@ -320,6 +323,21 @@ __global__ __launch_bounds__(256) void topk_rows_prefill_kernel(const float* __r
       const float x4[4] = {xs[q].x, xs[q].y, xs[q].z, xs[q].w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) u[4 * q + j] = e + j < v ? float_key(x4[j]) : 0u;
+    }
+  } else {  // bf16 scores: 8-byte loads of 4 entries, widened exactly to fp32
+    uint2 xs[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int e = 4 * (tid + 256 * q);
+      if (e < v) xs[q] = *(const uint2*)(srow + e);
+    }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int e = 4 * (tid + 256 * q);
+      const uint32_t b4[4] = {xs[q].x << 16, xs[q].x & 0xffff0000u, xs[q].y << 16,
+                              xs[q].y & 0xffff0000u};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) u[4 * q + j] = e + j < v ? float_key(__uint_as_float(b4[j])) : 0u;
     }
   }
   auto idx_of = [&](int i) { return 4 * (tid + 256 * (i >> 2)) + (i & 3); };
@@ -996,7 +1014,7 @@ __global__ __launch_bounds__(256) void dec_finalize_kernel(
   else return hipErrorInvalidValue;
 
 hipError_t launch_index_scores_prefill(const csa_index_desc& d, const void* qI, const void* wI,
-                                       const void* KI, float* scores, int64_t ld,
+                                       const void* KI, void* scores, int64_t ld,
                                        hipStream_t st) {
   const int key_chunk = 2048;
   const int64_t nvis = d.n / d.m < d.n_entries ? d.n / d.m : d.n_entries;
@@ -1006,14 +1024,23 @@ hipError_t launch_index_scores_prefill(const csa_index_desc& d, const void* qI, 
     // the kernel addresses a workgroup's TQ score rows with 32-bit offsets
     if ((int64_t)TQ * ld >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     dim3 grid((unsigned)((d.n + TQ - 1) / TQ), (unsigned)((nvis + key_chunk - 1) / key_chunk));
-    if (d.dtype == CSA_BF16)
-      index_scores_prefill_kernel<BF16, HI, CI><<<grid, 256, 0, st>>>(
+    const bool sb = d.score_dtype == CSA_BF16;
+    if (d.dtype == CSA_BF16 && sb)
+      index_scores_prefill_kernel<BF16, HI, CI, uint16_t><<<grid, 256, 0, st>>>(
           (const BF16::S*)qI, (const BF16::S*)wI, (const BF16::S*)KI, d.n, d.n_entries, d.m,
-          key_chunk, scores, ld);
-    else
-      index_scores_prefill_kernel<F32, HI, CI><<<grid, 256, 0, st>>>(
+          key_chunk, (uint16_t*)scores, ld);
+    else if (d.dtype == CSA_BF16)
+      index_scores_prefill_kernel<BF16, HI, CI, float><<<grid, 256, 0, st>>>(
+          (const BF16::S*)qI, (const BF16::S*)wI, (const BF16::S*)KI, d.n, d.n_entries, d.m,
+          key_chunk, (float*)scores, ld);
+    else if (sb)
+      index_scores_prefill_kernel<F32, HI, CI, uint16_t><<<grid, 256, 0, st>>>(
           (const float*)qI, (const float*)wI, (const float*)KI, d.n, d.n_entries, d.m, key_chunk,
-          scores, ld);
+          (uint16_t*)scores, ld);
+    else
+      index_scores_prefill_kernel<F32, HI, CI, float><<<grid, 256, 0, st>>>(
+          (const float*)qI, (const float*)wI, (const float*)KI, d.n, d.n_entries, d.m, key_chunk,
+          (float*)scores, ld);
   });
   return hipGetLastError();
 }
@@ -1021,7 +1048,7 @@ hipError_t launch_index_scores_prefill(const csa_index_desc& d, const void* qI, 
 // Rows are launched in bands by their visible-entry count (it grows with t):
 // each band's kernel holds 16, 32, 48 or 64 entries per thread, so short rows do
 // not pay for the longest one's registers and loops.
-hipError_t launch_topk_rows_prefill(const csa_index_desc& d, const float* scores, int64_t ld,
+hipError_t launch_topk_rows_prefill(const csa_index_desc& d, const void* scores, int64_t ld,
                                     int32_t* idx_out, hipStream_t st) {
   // first row whose visible count exceeds `cap` entries
   auto band_end = [&](int64_t cap) {
@@ -1032,19 +1059,25 @@ hipError_t launch_topk_rows_prefill(const csa_index_desc& d, const float* scores
   const int64_t e16 = band_end(16 * 256), e32 = band_end(32 * 256), e48 = band_end(48 * 256);
   // Q: keys per thread offered for the lower bound, 256 * Q >= k
   const int q = d.k <= 512 ? 2 : d.k <= 1024 ? 4 : 0;
-  auto band = [&](auto maxit, int64_t r0, int64_t r1) {
+  auto band_t = [&](auto maxit, auto sc, int64_t r0, int64_t r1) {
     constexpr int MI = decltype(maxit)::value;
+    typedef decltype(sc) SC;
+    const SC* sp = (const SC*)scores;
     if (r1 <= r0) return;
     const unsigned g = (unsigned)(r1 - r0);
     if (q == 2)
-      topk_rows_prefill_kernel<MI, 2><<<g, 256, 0, st>>>(scores, ld, d.n, d.n_entries, d.m, d.k,
-                                                         idx_out, r0);
+      topk_rows_prefill_kernel<MI, 2, SC><<<g, 256, 0, st>>>(sp, ld, d.n, d.n_entries, d.m, d.k,
+                                                             idx_out, r0);
     else if (q == 4)
-      topk_rows_prefill_kernel<MI, 4><<<g, 256, 0, st>>>(scores, ld, d.n, d.n_entries, d.m, d.k,
-                                                         idx_out, r0);
+      topk_rows_prefill_kernel<MI, 4, SC><<<g, 256, 0, st>>>(sp, ld, d.n, d.n_entries, d.m, d.k,
+                                                             idx_out, r0);
     else
-      topk_rows_prefill_kernel<MI, 0><<<g, 256, 0, st>>>(scores, ld, d.n, d.n_entries, d.m, d.k,
-                                                         idx_out, r0);
+      topk_rows_prefill_kernel<MI, 0, SC><<<g, 256, 0, st>>>(sp, ld, d.n, d.n_entries, d.m, d.k,
+                                                             idx_out, r0);
+  };
+  auto band = [&](auto maxit, int64_t r0, int64_t r1) {
+    if (d.score_dtype == CSA_BF16) band_t(maxit, uint16_t(), r0, r1);
+    else band_t(maxit, float(), r0, r1);
   };
   band(std::integral_constant<int, 16>(), 0, e16);
   band(std::integral_constant<int, 32>(), e16, e32);

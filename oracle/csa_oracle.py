@@ -236,6 +236,14 @@ def topk(scores, k, m, t0=0):
 # ---------------------------------------------------------------------------
 # O7 - O10: shared-KV MQA with window and sink  ([R] eq 18-19, 27; 2.3.3)
 # ---------------------------------------------------------------------------
+def topk_bf16_scores(scores, k, m, t0=0):
+    """The selector on index scores quantised from fp32 to bf16 ([R] section
+    4.4, the indexer QK path under quantisation-aware training: bf16 scores
+    for a faster top-k): the top-k of the scores rounded to bf16, ties still
+    broken toward the smaller entry index."""
+    return topk(round_bf16(scores), k, m, t0=t0)
+
+
 def query_prologue(q, pos, qk_norm, eps, rope_dims, theta):
     """Per-head RMSNorm, then RoPE of the last r dims at the query position.
     q [rows, nh, c]; pos [rows]."""

@@ -45,16 +45,39 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.csa_abi_version() == 2
+    assert lib.csa_abi_version() == 3
     for code in (0, -1, -2, -3, -4):
         assert len(lib.csa_status_string(code)) > 0
     assert lib.csa_status_string(-99) == b"unknown status"
 
 
-def test_struct_sizes_match_c_layout():
-    assert ctypes.sizeof(L.CompressDesc) == 64
-    assert ctypes.sizeof(L.IndexDesc) == 40
-    assert ctypes.sizeof(L.AttnDesc) == 64
+def test_struct_sizes_match_c_layout(tmp_path):
+    """The binding's ctypes descriptors have the C compiler's size and field
+    offsets for every descriptor in include/csa.h."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    pairs = [("csa_compress_desc", L.CompressDesc), ("csa_index_desc", L.IndexDesc),
+             ("csa_attn_desc", L.AttnDesc), ("csa_query_desc", L.QueryDesc),
+             ("csa_oproj_desc", L.OprojDesc)]
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "csa.h"', "int main(void) {"]
+    for cname, py in pairs:
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'  printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines.append("  return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = dict(l.rsplit(" ", 1) for l in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                        check=True).stdout.splitlines())
+    for cname, py in pairs:
+        assert int(got[f"{cname} size"]) == ctypes.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert int(got[f"{cname} {f}"]) == getattr(py, f).offset, (cname, f)
 
 
 def test_workspace_and_state_sizes(lib):
@@ -182,3 +205,16 @@ def test_layer_projection_calls_reject(lib):
     assert lib.csa_output_proj(ctypes.byref(o), _p(), _p(), _p(), _p(), None, 0, None) == -3
     assert L.workspace_bytes("output_proj", o) == 64 * 2 * 64 * 2
     assert L.workspace_bytes("query_proj", q) >= 64 * (128 + 4) * 4 + 64 * 128 * 2
+
+
+def test_index_score_dtype(lib):
+    """Prefill selects on fp32 or bf16 scores (half the workspace); decode only
+    on fp32; anything else is rejected before a launch."""
+    d32 = L.IndexDesc(4096, 1, 16, 64, 4, 512, L.CSA_BF16, 1024, L.CSA_F32)
+    d16 = L.IndexDesc(4096, 1, 16, 64, 4, 512, L.CSA_BF16, 1024, L.CSA_BF16)
+    assert L.workspace_bytes("index_topk_prefill", d16) * 2 == L.workspace_bytes("index_topk_prefill", d32)
+    bad = L.IndexDesc(4096, 1, 16, 64, 4, 512, L.CSA_BF16, 1024, 7)
+    assert lib.csa_index_topk_prefill(ctypes.byref(bad), _p(), _p(), _p(), _p(), _p(), 1 << 40, None) == -2
+    dec = L.IndexDesc(0, 2, 16, 64, 4, 512, L.CSA_BF16, 1024, L.CSA_BF16)
+    assert lib.csa_index_topk_decode(ctypes.byref(dec), _p(), _p(), _p(), _p(), _p(), _p(), 1 << 40,
+                                     None) == -2

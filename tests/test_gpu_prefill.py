@@ -11,7 +11,7 @@ import torch
 
 from oracle import csa_oracle as O
 from long_context_attention_10_amd import inputs as I
-from parity_util import assert_out_close, assert_stored_close, check_topk_sets, f64
+from parity_util import bf16_ulp, assert_out_close, assert_stored_close, check_topk_sets, f64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -116,6 +116,68 @@ def test_index_topk_prefill_large_k(lib, k):
     for t in [k - 1, k, k + 1, k + 300, 2 * k, 4095, 4096, n - 1]:
         sc = O.index_scores(f64(qI[t])[None], f64(wI[t])[None], KIh[: (t + 1) // m], m, t0=t)
         check_topk_sets(idx[t][None], sc, k, m, t0=t)
+
+
+def _check_bf16_selection(got, sc, k, m, t0=0):
+    """GPU rows selected on bf16 scores against the oracle's selection on the
+    fp64 scores rounded to bf16.  The GPU rounds fp32 scores, so an entry
+    whose score sits within one bf16 step of the k-th rounded score may round
+    the other way; only such entries may differ.  Returns the rows that
+    differ."""
+    ref = O.topk_bf16_scores(sc, k, m, t0=t0)
+    rb = O.round_bf16(sc)
+    nd = 0
+    for r in range(got.shape[0]):
+        vis = int(min(sc.shape[1], (t0 + r + 1) // m))
+        kt = min(k, vis)
+        g = got[r]
+        assert np.all(g[kt:] == -1) and np.all(np.diff(g[:kt]) > 0), f"row {r}: layout"
+        diff = set(g[:kt].tolist()) ^ set(ref[r, :kt].tolist())
+        if diff:
+            kth = np.sort(rb[r, :vis])[::-1][kt - 1]
+            band = 1.01 * float(bf16_ulp(kth)) + 1e-6
+            for s_ in diff:
+                assert abs(sc[r, s_] - kth) <= band, f"row {r}: entry {s_} off the bf16 tie band"
+            nd += 1
+    return nd
+
+
+def test_index_topk_prefill_bf16_scores(lib):
+    """Selection on bf16-rounded scores ([R] section 4.4) over 4096 tokens with
+    the 64K workload's indexer shape."""
+    n, hI, cI, m, k = 4096, 16, 64, 4, 512
+    _say("index bf16 scores", n)
+    key = ("index-bf16-scores", n)
+    qI = I.normal((n, hI, cI), key + ("q",), dtype="bf16", device=DEV)
+    wI = I.uniform((n, hI), key + ("w",), dtype="bf16", device=DEV)
+    KI = I.normal((n // m, cI), key + ("K",), dtype="bf16", device=DEV)
+    idx = lib.csa_index_topk_prefill(qI, wI, KI, m, k, scores="bf16").cpu().numpy()
+    torch.cuda.synchronize()
+    sc = O.index_scores(f64(qI), f64(wI), f64(KI), m)
+    nd = _check_bf16_selection(idx, sc, k, m)
+    assert nd <= n // 20
+
+
+def test_index_topk_bf16_scores_exact_ties(lib):
+    """Integer-valued inputs: every score is a small integer, exact in bf16 on
+    both sides, so the selection must equal the oracle's exactly (ties to the
+    smaller index)."""
+    _say("index bf16 scores ties")
+    n, hI, cI, m, k = 2048, 4, 64, 4, 40
+    g = torch.Generator(device="cpu").manual_seed(21)
+    qI = torch.randint(-1, 2, (n, hI, cI), generator=g).to(torch.bfloat16)
+    KI = torch.randint(0, 2, (n // m, cI), generator=g).to(torch.bfloat16)
+    wI = torch.ones(n, hI, dtype=torch.bfloat16)
+    idx = lib.csa_index_topk_prefill(qI.to(DEV), wI.to(DEV), KI.to(DEV), m, k, scores="bf16")
+    torch.cuda.synchronize()
+    sc = O.index_scores(f64(qI), f64(wI), f64(KI), m)
+    fin = sc[np.isfinite(sc)]  # (invisible entries are -inf)
+    assert np.all(np.abs(fin) <= 256) and np.all(fin == np.round(fin))  # exact in bf16
+    ref = O.topk_bf16_scores(sc, k, m)
+    got = idx.cpu().numpy()
+    for t in range(n):
+        kt = min(k, (t + 1) // m)
+        assert sorted(got[t, :kt].tolist()) == sorted(ref[t, :kt].tolist()), f"row {t}"
 
 
 def test_index_topk_exact_ties_break_to_smaller_index(lib):

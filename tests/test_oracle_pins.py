@@ -439,3 +439,15 @@ def test_output_proj_single_group_identity():
     np.testing.assert_allclose(out, o @ wo_b.T, rtol=1e-13)
     outb = O.output_proj(o, np.eye(k)[None], wo_b, O.round_bf16)
     np.testing.assert_array_equal(outb, O.round_bf16(O.round_bf16(o) @ wo_b.T))
+
+
+def test_topk_on_bf16_scores_worked_example():
+    """Scores 1.0, 1.001, 0.5, 1.003: in bf16 (8 significant bits, step 2^-7
+    at 1) the first, second and fourth all become exactly 1.0, so with k = 2
+    the two smallest indices of that tie win (0 and 1), while on the exact
+    scores the two largest (3 and 1) would."""
+    sc = np.array([[1.0, 1.001, 0.5, 1.003]])
+    np.testing.assert_array_equal(O.round_bf16(sc), [[1.0, 1.0, 0.5, 1.0]])
+    got = O.topk_bf16_scores(sc, 2, 1, t0=3)
+    assert sorted(got[0].tolist()) == [0, 1]
+    assert sorted(O.topk(sc, 2, 1, t0=3)[0].tolist()) == [1, 3]
