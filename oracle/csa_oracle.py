@@ -35,6 +35,8 @@ Parity pins for every function live in tests/test_oracle_pins.py.
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 F64 = np.float64
@@ -411,3 +413,69 @@ def output_proj(o, wo_a, wo_b, store):
         mid[:, j, :] = o[:, j * kg:(j + 1) * kg] @ np.asarray(wo_a[j], F64).T
     mid = store(mid.reshape(n, -1))
     return store(mid @ np.asarray(wo_b, F64).T)
+
+
+# ---------------------------------------------------------------------------
+# O9: the indexer's quantised QK path ([A] Compressor with rotate=True and the
+# Indexer forward: rotate_activation, then fp4_act_quant of q^I and of the
+# stored keys; [R] section 4.4: the indexer QK path cached, loaded and
+# multiplied in FP4)
+# ---------------------------------------------------------------------------
+FP4_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])  # E2M1 magnitudes
+FP4_BLOCK = 32
+
+
+def hadamard(x):
+    """rotate_activation: the normalised Walsh-Hadamard transform over the last
+    axis (length a power of two), x . H_n / sqrt(n) with H_n the Sylvester
+    matrix (H_1 = [1], H_2k = [[H_k, H_k], [H_k, -H_k]])."""
+    x = np.asarray(x, F64)
+    n = x.shape[-1]
+    h = np.ones((1, 1))
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    assert h.shape[0] == n, "length must be a power of two"
+    return x @ h / math.sqrt(n)
+
+
+def fp4_quant(x):
+    """fp4_act_quant, read as the MX-style format: every block of 32
+    consecutive values along the last axis shares a power-of-two scale 2^e,
+    e = ceil(log2(amax / 6)) (e = 0 for an all-zero block), so that every
+    |x| / 2^e <= 6; each x / 2^e is then rounded to the nearest E2M1 value,
+    ties to the even mantissa (0, 1, 2, 4).  Returns (codes, exps): codes in
+    0..15, bit 3 the sign (set only for a nonzero magnitude), bits 0-2 the
+    index into FP4_GRID; exps the block exponents e."""
+    x = np.asarray(x, F64)
+    nb = x.shape[-1] // FP4_BLOCK
+    xb = x.reshape(x.shape[:-1] + (nb, FP4_BLOCK))
+    amax = np.max(np.abs(xb), axis=-1)
+    f, k = np.frexp(amax / 6.0)                 # amax/6 = f * 2^k, 0.5 <= f < 1
+    e = np.where(amax > 0, np.where(f == 0.5, k - 1, k), 0).astype(np.int64)
+    a = np.abs(xb) / np.ldexp(1.0, e)[..., None]
+    idx = np.searchsorted(FP4_GRID, a, side="right") - 1   # largest grid value <= a
+    idx = np.clip(idx, 0, 7)
+    up = np.minimum(idx + 1, 7)
+    dlo, dhi = a - FP4_GRID[idx], FP4_GRID[up] - a
+    pick_up = (dhi < dlo) | ((dhi == dlo) & (idx % 2 == 1))
+    mag = np.where(pick_up, up, idx)
+    sign = (xb < 0) & (mag > 0)
+    codes = (mag + 8 * sign).reshape(x.shape)
+    return codes.astype(np.int64), e
+
+
+def fp4_dequant(codes, exps):
+    """Values of fp4_quant's output: sign * FP4_GRID[code & 7] * 2^e."""
+    codes = np.asarray(codes)
+    nb = codes.shape[-1] // FP4_BLOCK
+    cb = codes.reshape(codes.shape[:-1] + (nb, FP4_BLOCK))
+    v = np.where(cb >= 8, -1.0, 1.0) * FP4_GRID[cb & 7] * np.ldexp(1.0, np.asarray(exps))[..., None]
+    return v.reshape(codes.shape)
+
+
+def index_scores_fp4(qI, wI, KI, m, t0=0):
+    """Index scores of the quantised path: q^I and the keys rotated and
+    FP4-quantised, then eq 16 on the dequantised values."""
+    qc, qe = fp4_quant(hadamard(qI))
+    kc, ke = fp4_quant(hadamard(KI))
+    return index_scores(fp4_dequant(qc, qe), wI, fp4_dequant(kc, ke), m, t0=t0)

@@ -451,3 +451,55 @@ def test_topk_on_bf16_scores_worked_example():
     got = O.topk_bf16_scores(sc, 2, 1, t0=3)
     assert sorted(got[0].tolist()) == [0, 1]
     assert sorted(O.topk(sc, 2, 1, t0=3)[0].tolist()) == [1, 3]
+
+
+# ------------------------------------------- quantised indexer path (O9)
+def test_hadamard_worked_example_and_orthogonality():
+    """H_2 / sqrt(2) maps (1, 0) to (1, 1)/sqrt(2); the normalised transform is
+    its own inverse and keeps dot products, so the scores of rotated q and k
+    equal the unrotated ones."""
+    np.testing.assert_allclose(O.hadamard(np.array([1.0, 0.0])), [2 ** -0.5, 2 ** -0.5], rtol=1e-15)
+    np.testing.assert_allclose(O.hadamard(np.array([1.0, 2.0, 3.0, 4.0])), [5.0, -1.0, -2.0, 0.0],
+                               rtol=1e-15, atol=1e-15)  # (10, -2, -4, 0) / 2
+    x = RNG.normal(size=(5, 64))
+    np.testing.assert_allclose(O.hadamard(O.hadamard(x)), x, rtol=1e-12, atol=1e-12)
+    q, K = RNG.normal(size=(3, 4, 64)), RNG.normal(size=(9, 64))
+    w = RNG.uniform(size=(3, 4))
+    np.testing.assert_allclose(O.index_scores(O.hadamard(q), w, O.hadamard(K), 1, t0=8),
+                               O.index_scores(q, w, K, 1, t0=8), rtol=1e-12, atol=1e-12)
+
+
+def test_fp4_quant_worked_examples():
+    """A block with amax 12 takes 2^e = 2 (12/6 = 2 exactly); 3.0 -> 1.5 is on
+    the grid; 2.5 -> 1.25 is a tie between 1 and 1.5 and goes to the even 1;
+    -7.0 -> -3.5, a tie between 3 and 4, goes to 4; 0.4 -> 0.2 rounds to 0 and
+    keeps no sign; 12 -> 6 is the largest code."""
+    x = np.zeros(32)
+    x[:6] = [12.0, 3.0, 2.5, -7.0, -0.4, 0.9]
+    codes, exps = O.fp4_quant(x)
+    assert exps.tolist() == [1]
+    assert codes[:6].tolist() == [7, 3, 2, 8 + 6, 0, 1]  # 0.9/2 = 0.45 -> 0.5 (index 1)
+    np.testing.assert_array_equal(O.fp4_dequant(codes, exps)[:6], [12.0, 3.0, 2.0, -8.0, 0.0, 1.0])
+    z, ez = O.fp4_quant(np.zeros((2, 64)))
+    assert (z == 0).all() and (ez == 0).all()
+
+
+def test_fp4_quant_round_trip_and_error_bound():
+    """Grid values times the block scale come back exactly; any value is off
+    by at most half of the widest grid gap (1 at the top, times 2^e), and
+    each block's largest magnitude stays within 6 * 2^e."""
+    e = -3
+    vals = np.zeros(32)
+    vals[:8], vals[8:15], vals[15:23] = O.FP4_GRID, -O.FP4_GRID[1:], O.FP4_GRID
+    vals *= 2.0 ** e
+    vals[0] = 6 * 2.0 ** e  # pin the block amax so that e is -3
+    c, ex = O.fp4_quant(vals)
+    assert ex.tolist() == [e]
+    np.testing.assert_array_equal(O.fp4_dequant(c, ex), vals)
+    x = RNG.normal(size=(50, 128)) * np.exp(RNG.normal(size=(50, 1)))
+    c, ex = O.fp4_quant(x)
+    dq = O.fp4_dequant(c, ex)
+    scale = np.repeat(np.ldexp(1.0, ex), 32, axis=-1)
+    assert np.all(np.abs(dq - x) <= scale * 1.0 + 1e-15)
+    assert np.all(np.abs(x) <= 6 * scale * (1 + 1e-12))
+    assert np.all(np.abs(x).reshape(50, 4, 32).max(-1) > 3 * np.ldexp(1.0, ex) * (1 - 1e-12))
