@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 3
+#define CSA_ABI_VERSION 4
 
 typedef enum csa_status {
   CSA_OK = 0,
@@ -225,6 +225,49 @@ int csa_index_topk_decode(const csa_index_desc* desc, const void* qI, const void
                           size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * The quantised indexer path: rotation + FP4 ([A] Compressor with rotate =
+ * True and the Indexer forward: rotate_activation, fp4_act_quant; [R]
+ * section 4.4: the indexer QK path cached, loaded and multiplied in FP4)
+ * ---------------------------------------------------------------------- */
+
+typedef struct {
+  int64_t rows;       /* rows to quantise                                      */
+  int32_t width;      /* row width: 64 or 128                                  */
+  int32_t dtype;      /* csa_dtype of the input                                */
+} csa_fp4_desc;
+
+/* csa_indexer_fp4_quant -- each row x[r] (width W) is rotated by the
+ * normalised Walsh-Hadamard transform (x . H_W / sqrt(W), H_W the Sylvester
+ * matrix) and stored in FP4: every block of 32 consecutive rotated values
+ * has a scale 2^e, e the smallest integer with max|x| <= 6 * 2^e (0 for an
+ * all-zero block), and each value is rounded to the nearest E2M1 value
+ * (0, 0.5, 1, 1.5, 2, 3, 4, 6 times the scale, with sign), ties to the even
+ * mantissa; a zero keeps no sign.
+ *
+ *   x      [rows, W]     dtype
+ *   codes  [rows, W/2]   uint8: element 2j in the low nibble, 2j+1 in the
+ *                        high one; nibble = sign << 3 | E2M1 index
+ *   exps   [rows, W/32]  uint8: e + 127 per block
+ * Used for the indexer keys (after their compressor) and for q^I. */
+int csa_indexer_fp4_quant(const csa_fp4_desc* desc, const void* x, uint8_t* codes, uint8_t* exps,
+                          void* stream);
+
+/* csa_index_topk_decode_fp4 -- csa_index_topk_decode on the quantised path:
+ * q^I and the cached keys in the format csa_indexer_fp4_quant writes (the
+ * scores are eq 16 on the dequantised values, in fp32), wI as before in
+ * desc->dtype (CSA_BF16 only).  Same descriptor (head_dim = W), same
+ * workspace and zero bytes as csa_index_topk_decode
+ * (CSA_ENTRY_INDEX_TOPK_DECODE_FP4 gives them).
+ *
+ *   qI_codes [B, hI, cI/2], qI_exps [B, hI, cI/32]
+ *   K_codes  [B, n_entries, cI/2], K_exps [B, n_entries, cI/32]
+ *   wI [B, hI], pos [B], idx_out [B, k] as in csa_index_topk_decode */
+int csa_index_topk_decode_fp4(const csa_index_desc* desc, const uint8_t* qI_codes,
+                              const uint8_t* qI_exps, const void* wI, const uint8_t* K_codes,
+                              const uint8_t* K_exps, const int64_t* pos, int32_t* idx_out,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Core attention
  * ---------------------------------------------------------------------- */
 
@@ -293,7 +336,8 @@ typedef enum csa_entry {
   CSA_ENTRY_DENSE_MQA_PREFILL = 6,
   CSA_ENTRY_DENSE_MQA_DECODE = 7,
   CSA_ENTRY_QUERY_PROJ = 8,
-  CSA_ENTRY_OUTPUT_PROJ = 9
+  CSA_ENTRY_OUTPUT_PROJ = 9,
+  CSA_ENTRY_INDEX_TOPK_DECODE_FP4 = 10
 } csa_entry;
 
 /* ------------------------------------------------------------------------

@@ -22,11 +22,12 @@ LIB_PATH = os.path.join(_HERE, "libcsa.so")
 CSA_F32, CSA_BF16 = 0, 1
 ENTRY = dict(compress_prefill=0, compress_decode=1, index_topk_prefill=2, index_topk_decode=3,
              sparse_mqa_prefill=4, sparse_mqa_decode=5, dense_mqa_prefill=6, dense_mqa_decode=7,
-             query_proj=8, output_proj=9)
+             query_proj=8, output_proj=9, index_topk_decode_fp4=10)
 EXPORTED = ["csa_compress_prefill", "csa_compress_decode", "csa_state_bytes", "csa_state_init",
             "csa_index_topk_prefill", "csa_index_topk_decode", "csa_sparse_mqa_prefill",
             "csa_sparse_mqa_decode", "hca_dense_mqa_prefill", "hca_dense_mqa_decode",
-            "csa_query_proj", "csa_output_proj", "csa_workspace_bytes",
+            "csa_query_proj", "csa_output_proj", "csa_indexer_fp4_quant",
+            "csa_index_topk_decode_fp4", "csa_workspace_bytes",
             "csa_workspace_zero_bytes", "csa_status_string", "csa_abi_version"]
 
 
@@ -43,6 +44,10 @@ class IndexDesc(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("m", ctypes.c_int32), ("k", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("n_entries", ctypes.c_int64),
                 ("score_dtype", ctypes.c_int32)]
+
+
+class Fp4Desc(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("width", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
 class QueryDesc(ctypes.Structure):
@@ -102,6 +107,8 @@ def load(path: str = LIB_PATH):
     lib.hca_dense_mqa_decode.argtypes = [P] * 8 + [S, P]
     lib.csa_query_proj.argtypes = [P] * 11 + [S, P]
     lib.csa_output_proj.argtypes = [P] * 6 + [S, P]
+    lib.csa_indexer_fp4_quant.argtypes = [P] * 5
+    lib.csa_index_topk_decode_fp4.argtypes = [P] * 9 + [S, P]
     for f in EXPORTED:
         if f not in ("csa_abi_version", "csa_status_string", "csa_workspace_bytes",
                      "csa_workspace_zero_bytes", "csa_state_bytes"):
@@ -446,4 +453,47 @@ def csa_output_proj(o, wo_a, wo_b, out=None, ws_slot="oproj"):
     st = lib.csa_output_proj(ctypes.byref(desc), _ptr(o), _ptr(wo_a), _ptr(wo_b), _ptr(out),
                              _ptr(ws), wsb, _stream(o.device))
     _check(st, "csa_output_proj")
+    return out
+
+
+# ------------------------------------------------------ quantised indexer
+def csa_indexer_fp4_quant(x):
+    """Rotation + FP4 of the rows of x [..., W] (W = 64 or 128): returns
+    (codes uint8 [..., W/2], exps uint8 [..., W/32])."""
+    lib = load()
+    W = x.shape[-1]
+    rows = x.numel() // W if W else 0
+    codes = torch.empty(x.shape[:-1] + (W // 2,), dtype=torch.uint8, device=x.device)
+    exps = torch.empty(x.shape[:-1] + (W // 32,), dtype=torch.uint8, device=x.device)
+    desc = Fp4Desc(rows, W, _dt(x))
+    st = lib.csa_indexer_fp4_quant(ctypes.byref(desc), _ptr(x), _ptr(codes), _ptr(exps),
+                                   _stream(x.device))
+    _check(st, "csa_indexer_fp4_quant")
+    return codes, exps
+
+
+def csa_index_topk_decode_fp4(q_codes, q_exps, wI, k_codes, k_exps, pos, m, k, out=None):
+    """csa_index_topk_decode on FP4 q^I [B, hI, cI/2] (+ exps [B, hI, cI/32])
+    and FP4 keys [B, n_entries, cI/2] (+ exps); wI [B, hI] bf16."""
+    lib = load()
+    B, hI, half = q_codes.shape
+    cI = 2 * half
+    ne = k_codes.shape[1]
+    _expect(q_exps, (B, hI, cI // 32), torch.uint8, "q_exps")
+    _expect(k_codes, (B, ne, half), torch.uint8, "k_codes")
+    _expect(k_exps, (B, ne, cI // 32), torch.uint8, "k_exps")
+    _expect(wI, (B, hI), None, "wI")
+    _expect(pos, (B,), torch.int64, "pos")
+    desc = IndexDesc(0, B, hI, cI, m, k, _dt(wI), ne)
+    if out is None:
+        out = torch.empty((B, k), dtype=torch.int32, device=q_codes.device)
+    ws, wsb = workspace(workspace_bytes("index_topk_decode_fp4", desc), q_codes.device,
+                        "index_dec_fp4",
+                        zero_bytes=workspace_zero_bytes("index_topk_decode_fp4", desc))
+    st = lib.csa_index_topk_decode_fp4(ctypes.byref(desc), _ptr(q_codes), _ptr(q_exps), _ptr(wI),
+                                       _ptr(k_codes), _ptr(k_exps), _ptr(pos), _ptr(out),
+                                       _ptr(ws), wsb, _stream(q_codes.device))
+    if st != 0:
+        _WS_ZERO.pop((str(q_codes.device), "index_dec_fp4"), None)
+    _check(st, "csa_index_topk_decode_fp4")
     return out

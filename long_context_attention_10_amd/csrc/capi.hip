@@ -141,7 +141,8 @@ size_t csa_state_bytes(const csa_compress_desc* d) {
 }
 
 size_t csa_workspace_zero_bytes(int entry, const void* desc) {
-  if (!desc || entry != CSA_ENTRY_INDEX_TOPK_DECODE) return 0;
+  if (!desc || (entry != CSA_ENTRY_INDEX_TOPK_DECODE && entry != CSA_ENTRY_INDEX_TOPK_DECODE_FP4))
+    return 0;
   const csa_index_desc* d = (const csa_index_desc*)desc;
   if (d->batch <= 0) return 0;
   return index_decode_zero_bytes(*d);
@@ -165,7 +166,8 @@ size_t csa_workspace_bytes(int entry, const void* desc) {
       if (d->m <= 0 || d->n <= 0) return 0;
       return al((size_t)d->n * index_prefill_ld(d) * (d->score_dtype == CSA_BF16 ? 2 : 4));
     }
-    case CSA_ENTRY_INDEX_TOPK_DECODE: {
+    case CSA_ENTRY_INDEX_TOPK_DECODE:
+    case CSA_ENTRY_INDEX_TOPK_DECODE_FP4: {
       const csa_index_desc* d = (const csa_index_desc*)desc;
       if (d->batch <= 0) return 0;
       return index_decode_ws_bytes(*d);
@@ -313,6 +315,32 @@ int csa_output_proj(const csa_oproj_desc* d, const void* o, const void* wo_a, co
   if (d->n == 0) return CSA_OK;
   if (!ws || ws_bytes < output_proj_ws_bytes(*d)) return CSA_ERR_WORKSPACE;
   return hip_status(launch_output_proj(*d, o, wo_a, wo_b, out, ws, (hipStream_t)stream));
+}
+
+int csa_indexer_fp4_quant(const csa_fp4_desc* d, const void* x, uint8_t* codes, uint8_t* exps,
+                          void* stream) {
+  if (!d) return CSA_ERR_INVALID_ARG;
+  if (!dtype_ok(d->dtype)) return CSA_ERR_UNSUPPORTED;
+  if (d->rows < 0) return CSA_ERR_INVALID_ARG;
+  if (d->width != 64 && d->width != 128) return CSA_ERR_UNSUPPORTED;
+  if (d->rows == 0) return CSA_OK;
+  if (!x || !codes || !exps) return CSA_ERR_INVALID_ARG;
+  return hip_status(
+      launch_fp4_rotate_quant(d->dtype, x, d->rows, d->width, codes, exps, (hipStream_t)stream));
+}
+
+int csa_index_topk_decode_fp4(const csa_index_desc* d, const uint8_t* qI_codes,
+                              const uint8_t* qI_exps, const void* wI, const uint8_t* K_codes,
+                              const uint8_t* K_exps, const int64_t* pos, int32_t* idx_out,
+                              void* ws, size_t ws_bytes, void* stream) {
+  int s = check_index(d, true);
+  if (s) return s;
+  if (d->dtype != CSA_BF16) return CSA_ERR_UNSUPPORTED;
+  if (!qI_codes || !qI_exps || !wI || !K_codes || !K_exps || !pos || !idx_out)
+    return CSA_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < index_decode_ws_bytes(*d)) return CSA_ERR_WORKSPACE;
+  return hip_status(launch_index_topk_decode_fp4(*d, qI_codes, qI_exps, wI, K_codes, K_exps, pos,
+                                                 idx_out, ws, (hipStream_t)stream));
 }
 
 int csa_sparse_mqa_prefill(const csa_attn_desc* d, const void* q, const void* win_kv,

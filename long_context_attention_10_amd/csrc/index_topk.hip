@@ -643,6 +643,170 @@ __global__ __launch_bounds__(256) void dec_score_kernel(
     if (lh[i]) atomicAdd(&gh[i], lh[i]);
 }
 
+// ---------------------------------------------------------------------------
+// The quantised indexer path ([A] Compressor with rotate=True and the Indexer
+// forward: rotate_activation then fp4_act_quant; [R] section 4.4: the QK path
+// cached, loaded and multiplied in FP4).  A row of width CI is rotated by the
+// normalised Walsh-Hadamard transform and stored as E2M1 codes (two per byte,
+// the even element in the low nibble) with one power-of-two scale per block
+// of 32 values (its exponent e as the byte e + 127), the smallest e with
+// max |x| <= 6 * 2^e; values round to the nearest E2M1 value, ties to the
+// even mantissa.
+// ---------------------------------------------------------------------------
+CSA_DEV uint32_t e2m1_code(float x, float inv_scale) {
+  const float a = fabsf(x) * inv_scale;  // in [0, 6]
+  const uint32_t i = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
+                     (a >= 3.5f) + (a > 5.0f);
+  return i | ((x < 0.f && i) ? 8u : 0u);
+}
+
+CSA_DEV int e2m1_block_exp(float amax) {
+  if (!(amax > 0.f)) return 0;
+  int k;
+  const float f = frexpf(amax, &k);  // amax = f * 2^k, 0.5 <= f < 1
+  return f <= 0.75f ? k - 3 : k - 2;
+}
+
+// One wave per row: lane l holds elements l (and l + 64); butterflies over
+// the strides 64 (in the lane), 32 .. 1 (across lanes), then 1/sqrt(CI).
+template <class T, int CI>
+__global__ __launch_bounds__(256) void fp4_rotate_quant_kernel(const typename T::S* __restrict__ x,
+                                                               int64_t rows,
+                                                               uint8_t* __restrict__ codes,
+                                                               uint8_t* __restrict__ exps) {
+  constexpr int NV = CI / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;  // whole wave
+  float v[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) v[j] = T::ld(x, r * CI + j * 64 + lane);
+  if constexpr (NV == 2) {
+    const float a = v[0], b = v[1];
+    v[0] = a + b;
+    v[1] = a - b;
+  }
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1)
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const float p = __shfl_xor(v[j], s, 64);
+      v[j] = (lane & s) ? p - v[j] : v[j] + p;
+    }
+  const float norm = CI == 64 ? 0.125f : 0.0883883476483184406f;  // 1/sqrt(CI)
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const float y = v[j] * norm;
+    float am = fabsf(y);
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 64));  // 32-value block
+    const int e = e2m1_block_exp(am);
+    const uint32_t c = e2m1_code(y, ldexpf(1.f, -e));
+    const uint32_t c1 = __shfl_xor(c, 1, 64);
+    const int elem = j * 64 + lane;
+    if (!(lane & 1)) codes[r * (CI / 2) + elem / 2] = (uint8_t)(c | (c1 << 4));
+    if ((lane & 31) == 0) exps[r * (CI / 32) + elem / 32] = (uint8_t)(e + 127);
+  }
+}
+
+// 8 consecutive E2M1 values (4 code bytes) with the block scale 2^(eb - 127)
+// as one bf16 matrix-core fragment.
+CSA_DEV uint4 fp4x8_to_bf16(uint32_t cw, uint32_t eb) {
+  const float sc = __uint_as_float(eb << 23);  // 2^(eb - 127)
+  uint4 r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 0));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 1));
+  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 2));
+  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 3));
+  return r;
+}
+
+// D1 over FP4 keys: dec_score_kernel with q^I and the keys read as E2M1 codes
+// and block exponents (a quarter of the bf16 bytes) and widened to bf16
+// fragments in registers; the products, head sum and histogram are the same.
+template <int HI, int CI>
+__global__ __launch_bounds__(256) void dec_score_fp4_kernel(
+    const uint8_t* __restrict__ qc, const uint8_t* __restrict__ qe, const uint16_t* __restrict__ wI,
+    const uint8_t* __restrict__ kc, const uint8_t* __restrict__ ke,
+    const int64_t* __restrict__ posv, int64_t n_entries, int m, int k, float* __restrict__ scores,
+    int* __restrict__ hist, int ncopies) {
+  constexpr int NG = CI / 32;  // 32-value k-groups (= scale blocks) per row
+  constexpr int RB = CI / 2;   // code bytes per row
+  __shared__ int lh[kCoarseBins];
+  const int b = blockIdx.y;
+  const int64_t vis = min64((posv[b] + 1) / m, n_entries);
+  if (vis <= k) return;  // everything visible is selected
+  const int64_t c0 = (int64_t)blockIdx.x * kDecChunk;
+  if (c0 >= vis) return;
+  const int64_t c1 = min64(c0 + kDecChunk, vis);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lg = lane >> 4;
+  for (int i = tid; i < kCoarseBins; i += 256) lh[i] = 0;
+
+  uint4 qa[NG];
+  float wv[4];
+  const int hrow = lane & 15;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int64_t row = (int64_t)b * HI + hrow;
+    qa[g] = hrow < HI ? fp4x8_to_bf16(*(const uint32_t*)(qc + row * RB + g * 16 + lg * 4),
+                                      qe[row * NG + g])
+                      : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * lg + i;
+    wv[i] = h < HI ? BF16::ld(wI, (int64_t)b * HI + h) : 0.f;
+  }
+  __syncthreads();
+  const uint8_t* kcb = kc + (int64_t)b * n_entries * RB;
+  const uint8_t* keb = ke + (int64_t)b * n_entries * NG;
+  const int64_t w0 = c0 + (int64_t)wave * (kDecChunk / 4);
+  const int64_t w1 = min64(w0 + kDecChunk / 4, c1);
+  // 64 keys per step: each lane loads 4 code bytes and the scale byte per
+  // k-group for its 4 keys (16 keys per MFMA, 4 MFMA steps)
+  auto load64 = [&](int64_t s0, uint32_t (&dc)[4][NG], uint32_t (&de)[4][NG]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t s = min64(s0 + u * 16 + (lane & 15), c1 - 1);  // past c1: not stored
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        dc[u][g] = *(const uint32_t*)(kcb + s * RB + g * 16 + lg * 4);
+        de[u][g] = keb[s * NG + g];
+      }
+    }
+  };
+  auto score64 = [&](int64_t s0, const uint32_t (&dc)[4][NG], const uint32_t (&de)[4][NG]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      f32x4_t acc = f32x4_t{};
+#pragma unroll
+      for (int g = 0; g < NG; ++g) mma16<BF16>(acc, qa[g], fp4x8_to_bf16(dc[u][g], de[u][g]));
+      float p = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p += wv[i] * relu(acc[i]);
+      p = xlane_sum(p);
+      const int64_t s = s0 + u * 16 + (lane & 15);
+      if (lg == 0 && s < w1) {
+        scores[(int64_t)b * n_entries + s] = p;
+        atomicAdd(&lh[float_key(p) >> 21], 1);
+      }
+    }
+  };
+  uint32_t ka[4][NG], kae[4][NG], kb[4][NG], kbe[4][NG];
+  if (w0 < w1) load64(w0, ka, kae);
+  for (int64_t s0 = w0; s0 < w1; s0 += 128) {
+    if (s0 + 64 < w1) load64(s0 + 64, kb, kbe);
+    score64(s0, ka, kae);
+    if (s0 + 64 >= w1) break;
+    if (s0 + 128 < w1) load64(s0 + 128, ka, kae);
+    score64(s0 + 64, kb, kbe);
+  }
+  __syncthreads();
+  int* gh = hist + ((int64_t)b * ncopies + blockIdx.x % ncopies) * kCoarseBins;
+  for (int i = tid; i < kCoarseBins; i += 256)
+    if (lh[i]) atomicAdd(&gh[i], lh[i]);
+}
+
 // The coarse threshold bin T of the `need`-th largest key from a sequence's
 // histogram copies: blocks of 256 bins are summed over the copies from the
 // top bin down until they hold `need` keys.  Every thread gets res = (T,
@@ -1086,6 +1250,17 @@ hipError_t launch_topk_rows_prefill(const csa_index_desc& d, const void* scores,
   return hipGetLastError();
 }
 
+// D2 and D3 after the scores and histograms of a decode call are in place.
+static hipError_t dec_select(const csa_index_desc& d, const DecWs& w, int64_t nch, int ncopies,
+                             const int64_t* pos, int32_t* idx_out, hipStream_t st) {
+  const dim3 grid((unsigned)nch, (unsigned)d.batch);
+  dec_collect_kernel<<<grid, 256, 0, st>>>(pos, d.n_entries, d.m, d.k, w.scores, w.hist, w.fine,
+                                           w.ccnt, w.lists, nch, ncopies);
+  dec_finalize_kernel<<<d.batch, 256, 0, st>>>(pos, d.n_entries, d.m, d.k, w.hist, ncopies, w.fine,
+                                               w.ccnt, w.lists, w.flat, nch, idx_out);
+  return hipGetLastError();
+}
+
 hipError_t launch_index_topk_decode(const csa_index_desc& d, const void* qI, const void* wI,
                                     const void* KI, const int64_t* pos, int32_t* idx_out,
                                     void* wsp, hipStream_t st) {
@@ -1104,10 +1279,44 @@ hipError_t launch_index_topk_decode(const csa_index_desc& d, const void* qI, con
           (const float*)qI, (const float*)wI, (const float*)KI, pos, d.n_entries, d.m, d.k,
           w.scores, w.hist, ncopies);
   });
-  dec_collect_kernel<<<grid, 256, 0, st>>>(pos, d.n_entries, d.m, d.k, w.scores, w.hist, w.fine,
-                                           w.ccnt, w.lists, nch, ncopies);
-  dec_finalize_kernel<<<B, 256, 0, st>>>(pos, d.n_entries, d.m, d.k, w.hist, ncopies, w.fine,
-                                         w.ccnt, w.lists, w.flat, nch, idx_out);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return dec_select(d, w, nch, ncopies, pos, idx_out, st);
+}
+
+hipError_t launch_index_topk_decode_fp4(const csa_index_desc& d, const uint8_t* qc,
+                                        const uint8_t* qe, const void* wI, const uint8_t* kc,
+                                        const uint8_t* ke, const int64_t* pos, int32_t* idx_out,
+                                        void* wsp, hipStream_t st) {
+  DecWs w = carve(wsp, d);
+  const int64_t nch = dec_chunks(d);
+  const int ncopies = dec_hist_copies(nch);
+  const dim3 grid((unsigned)nch, (unsigned)d.batch);
+  CSA_INDEX_DISPATCH(d.n_heads, d.head_dim, {
+    dec_score_fp4_kernel<HI, CI><<<grid, 256, 0, st>>>(qc, qe, (const uint16_t*)wI, kc, ke, pos,
+                                                        d.n_entries, d.m, d.k, w.scores, w.hist,
+                                                        ncopies);
+  });
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return dec_select(d, w, nch, ncopies, pos, idx_out, st);
+}
+
+hipError_t launch_fp4_rotate_quant(int dtype, const void* x, int64_t rows, int width,
+                                   uint8_t* codes, uint8_t* exps, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  const unsigned g = (unsigned)((rows + 3) / 4);
+  if (width == 64) {
+    if (dtype == CSA_BF16)
+      fp4_rotate_quant_kernel<BF16, 64><<<g, 256, 0, st>>>((const uint16_t*)x, rows, codes, exps);
+    else
+      fp4_rotate_quant_kernel<F32, 64><<<g, 256, 0, st>>>((const float*)x, rows, codes, exps);
+  } else {
+    if (dtype == CSA_BF16)
+      fp4_rotate_quant_kernel<BF16, 128><<<g, 256, 0, st>>>((const uint16_t*)x, rows, codes, exps);
+    else
+      fp4_rotate_quant_kernel<F32, 128><<<g, 256, 0, st>>>((const float*)x, rows, codes, exps);
+  }
   return hipGetLastError();
 }
 

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.csa_abi_version() == 3
+    assert lib.csa_abi_version() == 4
     for code in (0, -1, -2, -3, -4):
         assert len(lib.csa_status_string(code)) > 0
     assert lib.csa_status_string(-99) == b"unknown status"
@@ -61,7 +61,7 @@ def test_struct_sizes_match_c_layout(tmp_path):
         pytest.skip("no C compiler")
     pairs = [("csa_compress_desc", L.CompressDesc), ("csa_index_desc", L.IndexDesc),
              ("csa_attn_desc", L.AttnDesc), ("csa_query_desc", L.QueryDesc),
-             ("csa_oproj_desc", L.OprojDesc)]
+             ("csa_oproj_desc", L.OprojDesc), ("csa_fp4_desc", L.Fp4Desc)]
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "csa.h"', "int main(void) {"]
     for cname, py in pairs:
         lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
@@ -218,3 +218,20 @@ def test_index_score_dtype(lib):
     dec = L.IndexDesc(0, 2, 16, 64, 4, 512, L.CSA_BF16, 1024, L.CSA_BF16)
     assert lib.csa_index_topk_decode(ctypes.byref(dec), _p(), _p(), _p(), _p(), _p(), _p(), 1 << 40,
                                      None) == -2
+
+
+def test_fp4_calls_reject(lib):
+    d = L.Fp4Desc(16, 96, L.CSA_BF16)
+    assert lib.csa_indexer_fp4_quant(ctypes.byref(d), _p(), _p(), _p(), None) == -2  # width
+    d = L.Fp4Desc(16, 64, 9)
+    assert lib.csa_indexer_fp4_quant(ctypes.byref(d), _p(), _p(), _p(), None) == -2  # dtype
+    d = L.Fp4Desc(16, 64, L.CSA_BF16)
+    assert lib.csa_indexer_fp4_quant(ctypes.byref(d), None, _p(), _p(), None) == -1
+    assert lib.csa_indexer_fp4_quant(None, _p(), _p(), _p(), None) == -1
+    dec = L.IndexDesc(0, 2, 16, 64, 4, 512, L.CSA_F32, 1024)
+    assert lib.csa_index_topk_decode_fp4(ctypes.byref(dec), *([_p()] * 8), 1 << 40, None) == -2
+    dec = L.IndexDesc(0, 2, 16, 64, 4, 512, L.CSA_BF16, 1024)
+    assert lib.csa_index_topk_decode_fp4(ctypes.byref(dec), *([_p()] * 7), None, 0, None) == -3
+    assert lib.csa_index_topk_decode_fp4(ctypes.byref(dec), None, *([_p()] * 7), 1 << 40, None) == -1
+    assert L.workspace_bytes("index_topk_decode_fp4", dec) == L.workspace_bytes("index_topk_decode", dec)
+    assert L.workspace_zero_bytes("index_topk_decode_fp4", dec) > 0
