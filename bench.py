@@ -335,6 +335,47 @@ class HybridDecode:
         L.csa_sparse_mqa_decode(g["csa_q"], self.ring, self.cache, self.idx, self.pos, g["csa_sink"],
                                 rope_dims=r, out=self.out_c)
 
+    def step_fp4(self, streams=True):
+        """The same step with the FP4 indexer path: q^I is rotated and
+        quantised, the indexer compressor's new entry is quantised into the
+        FP4 key cache, and the top-k reads FP4 keys (the attention and the
+        other chains are unchanged)."""
+        c, g = self.cfg, self.g
+        m, ov, r = c["m"], c["overlap"], c["rope_dims"]
+        if getattr(self, "kc", None) is None:  # the FP4 key cache, made once
+            self.kc, self.ke = L.csa_indexer_fp4_quant(self.kcache)
+            self.qc, self.qe = L.csa_indexer_fp4_quant(g["qI"])
+        main = torch.cuda.current_stream()
+        if streams:
+            if self.side is None:
+                self.side = (torch.cuda.Stream(), torch.cuda.Stream())
+            sb, sc = self.side
+            sb.wait_stream(main)
+            sc.wait_stream(main)
+        else:
+            sb = sc = main
+        with torch.cuda.stream(sb):
+            L.csa_indexer_fp4_quant(g["qI"], out=(self.qc, self.qe))
+            L.csa_compress_decode(self.h, self.pos, g["WI_kv"], g["WI_z"], g["apeI"], m, ov, self.sti,
+                                  self.kcache, ws_slot="decode_proj_idx")
+            L.csa_indexer_fp4_quant_decode(self.kcache, self.pos, m, self.kc, self.ke)
+            L.csa_index_topk_decode_fp4(self.qc, self.qe, g["wI"], self.kc, self.ke, self.pos, m,
+                                        c["k"], out=self.idx)
+        with torch.cuda.stream(sc):
+            L.csa_compress_decode(self.h, self.pos, g["csa_Wkv"], g["csa_Wz"], g["csa_ape"], m, ov,
+                                  self.st, self.cache, W_win=g["csa_Wwin"], win_ring=self.ring,
+                                  rope_dims=r, ws_slot="decode_proj_csa")
+        L.csa_compress_decode(self.h, self.pos, g["hca_Wkv"], g["hca_Wz"], g["hca_ape"],
+                              c["m_hca"], 0, self.sth, self.hcache, W_win=g["hca_Wwin"],
+                              win_ring=self.hring, rope_dims=r, ws_slot="decode_proj_hca")
+        L.hca_dense_mqa_decode(g["hca_q"], self.hring, self.hcache, self.pos, g["hca_sink"],
+                               c["m_hca"], rope_dims=r, out=self.out_h)
+        if streams:
+            main.wait_stream(sb)
+            main.wait_stream(sc)
+        L.csa_sparse_mqa_decode(g["csa_q"], self.ring, self.cache, self.idx, self.pos, g["csa_sink"],
+                                rope_dims=r, out=self.out_c)
+
     def algorithmic_bytes(self):
         """Bytes a decode step must move at least once (bf16 = 2 B)."""
         c = self.cfg
@@ -516,6 +557,38 @@ def main():
                           "hbm_frac": byts / (us * 1e-6) / PEAK_HBM,
                           "graph_hbm_frac": byts / (ug * 1e-6) / PEAK_HBM}
             del g
+            # the FP4 indexer path (rotation + E2M1 keys and q^I): the top-k
+            # over FP4 keys against the same call over bf16 keys, and how much
+            # of the bf16-key selection it recalls
+            c_, g_ = hd.cfg, hd.g
+            kc, ke = L.csa_indexer_fp4_quant(hd.kcache)
+            qc, qe = L.csa_indexer_fp4_quant(g_["qI"])
+            idx4 = torch.empty_like(hd.idx)
+
+            def topk_bf16():
+                L.csa_index_topk_decode(g_["qI"], g_["wI"], hd.kcache, hd.pos, c_["m"], c_["k"],
+                                        out=hd.idx)
+
+            def topk_fp4():
+                L.csa_index_topk_decode_fp4(qc, qe, g_["wI"], kc, ke, hd.pos, c_["m"], c_["k"],
+                                            out=idx4)
+            t16 = float(np.median(time_region(graph_of(topk_bf16).replay, nd, 3, flush=flush))) * 1e3
+            t4 = float(np.median(time_region(graph_of(topk_fp4).replay, nd, 3, flush=flush))) * 1e3
+            topk_bf16()
+            topk_fp4()
+            pos_ = torch.searchsorted(idx4, hd.idx).clamp_(max=idx4.shape[1] - 1)
+            hit = (idx4.gather(1, pos_) == hd.idx) & (hd.idx >= 0)
+            tstep = time_region(hd.step_fp4, nd, 3, flush=flush)
+            gf = graph_of(hd.step_fp4)
+            tgs = time_region(gf.replay, nd, 3, flush=flush)
+            del gf
+            dec[wname]["fp4_indexer"] = {
+                "us_per_step": float(np.median(tstep)) * 1e3,
+                "graph_us_per_step": float(np.median(tgs)) * 1e3,
+                "topk_us_fp4_keys": t4, "topk_us_bf16_keys": t16,
+                "key_bytes_per_entry": [kc.shape[-1] + ke.shape[-1], 2 * hd.kcache.shape[-1]],
+                "recall_of_bf16_selection": float(hit.sum().item()) / float((hd.idx >= 0).sum().item())}
+            del kc, ke, qc, qe, idx4, pos_, hit
             del hd
             torch.cuda.empty_cache()
         rec["decode"] = dec

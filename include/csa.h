@@ -252,6 +252,16 @@ typedef struct {
 int csa_indexer_fp4_quant(const csa_fp4_desc* desc, const void* x, uint8_t* codes, uint8_t* exps,
                           void* stream);
 
+/* csa_indexer_fp4_quant_decode -- the same rotation and FP4 for the entry a
+ * decode step has just emitted into a bf16/fp32 key cache: for each of the
+ * desc->rows sequences b with (pos[b] + 1) % m == 0, row pos[b] / m of
+ * cache[b] ([B, n_entries, W], the csa_compress_decode output) is written to
+ * row pos[b] / m of codes [B, n_entries, W/2] and exps [B, n_entries, W/32];
+ * other rows are left as they are. */
+int csa_indexer_fp4_quant_decode(const csa_fp4_desc* desc, const void* cache, int64_t n_entries,
+                                 const int64_t* pos, int m, uint8_t* codes, uint8_t* exps,
+                                 void* stream);
+
 /* csa_index_topk_decode_fp4 -- csa_index_topk_decode on the quantised path:
  * q^I and the cached keys in the format csa_indexer_fp4_quant writes (the
  * scores are eq 16 on the dequantised values, in fp32), wI as before in

@@ -27,7 +27,7 @@ EXPORTED = ["csa_compress_prefill", "csa_compress_decode", "csa_state_bytes", "c
             "csa_index_topk_prefill", "csa_index_topk_decode", "csa_sparse_mqa_prefill",
             "csa_sparse_mqa_decode", "hca_dense_mqa_prefill", "hca_dense_mqa_decode",
             "csa_query_proj", "csa_output_proj", "csa_indexer_fp4_quant",
-            "csa_index_topk_decode_fp4", "csa_workspace_bytes",
+            "csa_index_topk_decode_fp4", "csa_indexer_fp4_quant_decode", "csa_workspace_bytes",
             "csa_workspace_zero_bytes", "csa_status_string", "csa_abi_version"]
 
 
@@ -109,6 +109,7 @@ def load(path: str = LIB_PATH):
     lib.csa_output_proj.argtypes = [P] * 6 + [S, P]
     lib.csa_indexer_fp4_quant.argtypes = [P] * 5
     lib.csa_index_topk_decode_fp4.argtypes = [P] * 9 + [S, P]
+    lib.csa_indexer_fp4_quant_decode.argtypes = [P, P, ctypes.c_int64, P, I, P, P, P]
     for f in EXPORTED:
         if f not in ("csa_abi_version", "csa_status_string", "csa_workspace_bytes",
                      "csa_workspace_zero_bytes", "csa_state_bytes"):
@@ -457,14 +458,19 @@ def csa_output_proj(o, wo_a, wo_b, out=None, ws_slot="oproj"):
 
 
 # ------------------------------------------------------ quantised indexer
-def csa_indexer_fp4_quant(x):
+def csa_indexer_fp4_quant(x, out=None):
     """Rotation + FP4 of the rows of x [..., W] (W = 64 or 128): returns
-    (codes uint8 [..., W/2], exps uint8 [..., W/32])."""
+    (codes uint8 [..., W/2], exps uint8 [..., W/32]); `out` may give them."""
     lib = load()
     W = x.shape[-1]
     rows = x.numel() // W if W else 0
-    codes = torch.empty(x.shape[:-1] + (W // 2,), dtype=torch.uint8, device=x.device)
-    exps = torch.empty(x.shape[:-1] + (W // 32,), dtype=torch.uint8, device=x.device)
+    if out is not None:
+        codes, exps = out
+        _expect(codes, tuple(x.shape[:-1]) + (W // 2,), torch.uint8, "codes")
+        _expect(exps, tuple(x.shape[:-1]) + (W // 32,), torch.uint8, "exps")
+    else:
+        codes = torch.empty(x.shape[:-1] + (W // 2,), dtype=torch.uint8, device=x.device)
+        exps = torch.empty(x.shape[:-1] + (W // 32,), dtype=torch.uint8, device=x.device)
     desc = Fp4Desc(rows, W, _dt(x))
     st = lib.csa_indexer_fp4_quant(ctypes.byref(desc), _ptr(x), _ptr(codes), _ptr(exps),
                                    _stream(x.device))
@@ -497,3 +503,18 @@ def csa_index_topk_decode_fp4(q_codes, q_exps, wI, k_codes, k_exps, pos, m, k, o
         _WS_ZERO.pop((str(q_codes.device), "index_dec_fp4"), None)
     _check(st, "csa_index_topk_decode_fp4")
     return out
+
+
+def csa_indexer_fp4_quant_decode(cache, pos, m, codes, exps):
+    """Quantise, into the FP4 cache (codes [B, n_entries, W/2], exps [B,
+    n_entries, W/32]), the entry each sequence's decode step has just emitted
+    into the key cache [B, n_entries, W]."""
+    lib = load()
+    B, ne, W = cache.shape
+    _expect(pos, (B,), torch.int64, "pos")
+    _expect(codes, (B, ne, W // 2), torch.uint8, "codes")
+    _expect(exps, (B, ne, W // 32), torch.uint8, "exps")
+    desc = Fp4Desc(B, W, _dt(cache))
+    st = lib.csa_indexer_fp4_quant_decode(ctypes.byref(desc), _ptr(cache), ne, _ptr(pos), m,
+                                          _ptr(codes), _ptr(exps), _stream(cache.device))
+    _check(st, "csa_indexer_fp4_quant_decode")

@@ -325,8 +325,21 @@ int csa_indexer_fp4_quant(const csa_fp4_desc* d, const void* x, uint8_t* codes, 
   if (d->width != 64 && d->width != 128) return CSA_ERR_UNSUPPORTED;
   if (d->rows == 0) return CSA_OK;
   if (!x || !codes || !exps) return CSA_ERR_INVALID_ARG;
-  return hip_status(
-      launch_fp4_rotate_quant(d->dtype, x, d->rows, d->width, codes, exps, (hipStream_t)stream));
+  return hip_status(launch_fp4_rotate_quant(d->dtype, x, d->rows, d->width, codes, exps, nullptr,
+                                            0, 1, (hipStream_t)stream));
+}
+
+int csa_indexer_fp4_quant_decode(const csa_fp4_desc* d, const void* cache, int64_t n_entries,
+                                 const int64_t* pos, int m, uint8_t* codes, uint8_t* exps,
+                                 void* stream) {
+  if (!d) return CSA_ERR_INVALID_ARG;
+  if (!dtype_ok(d->dtype)) return CSA_ERR_UNSUPPORTED;
+  if (d->rows < 0 || n_entries < 0 || m <= 0) return CSA_ERR_INVALID_ARG;
+  if (d->width != 64 && d->width != 128) return CSA_ERR_UNSUPPORTED;
+  if (d->rows == 0 || n_entries == 0) return CSA_OK;
+  if (!cache || !pos || !codes || !exps) return CSA_ERR_INVALID_ARG;
+  return hip_status(launch_fp4_rotate_quant(d->dtype, cache, d->rows, d->width, codes, exps, pos,
+                                            n_entries, m, (hipStream_t)stream));
 }
 
 int csa_index_topk_decode_fp4(const csa_index_desc* d, const uint8_t* qI_codes,

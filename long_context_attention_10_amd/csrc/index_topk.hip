@@ -669,15 +669,24 @@ CSA_DEV int e2m1_block_exp(float amax) {
 
 // One wave per row: lane l holds elements l (and l + 64); butterflies over
 // the strides 64 (in the lane), 32 .. 1 (across lanes), then 1/sqrt(CI).
+// With posv (decode): wave b quantises row b * n_entries + pos[b] / m of
+// the cache, the entry the step has just emitted, when (pos[b] + 1) % m == 0.
 template <class T, int CI>
 __global__ __launch_bounds__(256) void fp4_rotate_quant_kernel(const typename T::S* __restrict__ x,
                                                                int64_t rows,
                                                                uint8_t* __restrict__ codes,
-                                                               uint8_t* __restrict__ exps) {
+                                                               uint8_t* __restrict__ exps,
+                                                               const int64_t* __restrict__ posv,
+                                                               int64_t n_entries, int m) {
   constexpr int NV = CI / 64;
   const int lane = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;  // whole wave
+  if (posv) {
+    const int64_t p = posv[r];
+    if (p < 0 || (p + 1) % m != 0 || p / m >= n_entries) return;
+    r = r * n_entries + p / m;
+  }
   float v[NV];
 #pragma unroll
   for (int j = 0; j < NV; ++j) v[j] = T::ld(x, r * CI + j * 64 + lane);
@@ -1303,20 +1312,21 @@ hipError_t launch_index_topk_decode_fp4(const csa_index_desc& d, const uint8_t* 
 }
 
 hipError_t launch_fp4_rotate_quant(int dtype, const void* x, int64_t rows, int width,
-                                   uint8_t* codes, uint8_t* exps, hipStream_t st) {
+                                   uint8_t* codes, uint8_t* exps, const int64_t* pos,
+                                   int64_t n_entries, int m, hipStream_t st) {
   if (rows == 0) return hipSuccess;
   const unsigned g = (unsigned)((rows + 3) / 4);
+#define CSA_FP4Q(TT, WW)                                                                      \
+  fp4_rotate_quant_kernel<TT, WW><<<g, 256, 0, st>>>((const TT::S*)x, rows, codes, exps, pos, \
+                                                     n_entries, m)
   if (width == 64) {
-    if (dtype == CSA_BF16)
-      fp4_rotate_quant_kernel<BF16, 64><<<g, 256, 0, st>>>((const uint16_t*)x, rows, codes, exps);
-    else
-      fp4_rotate_quant_kernel<F32, 64><<<g, 256, 0, st>>>((const float*)x, rows, codes, exps);
+    if (dtype == CSA_BF16) CSA_FP4Q(BF16, 64);
+    else CSA_FP4Q(F32, 64);
   } else {
-    if (dtype == CSA_BF16)
-      fp4_rotate_quant_kernel<BF16, 128><<<g, 256, 0, st>>>((const uint16_t*)x, rows, codes, exps);
-    else
-      fp4_rotate_quant_kernel<F32, 128><<<g, 256, 0, st>>>((const float*)x, rows, codes, exps);
+    if (dtype == CSA_BF16) CSA_FP4Q(BF16, 128);
+    else CSA_FP4Q(F32, 128);
   }
+#undef CSA_FP4Q
   return hipGetLastError();
 }
 

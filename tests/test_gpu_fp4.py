@@ -89,3 +89,49 @@ def test_index_topk_decode_fp4(lib, hI, cI, m, k, ne, pos):
         check_topk_sets(got[b][None], sc, k, m, t0=p)
     # and the quantiser's, on a sample of the keys
     _check_quant(KI[0, :2048], kc[0, :2048], ke[0, :2048])
+
+
+def test_fp4_quant_decode_writes_only_emitted_rows(lib):
+    """The decode variant quantises row pos/m of each sequence whose step
+    emits an entry ((pos+1) % m == 0) and leaves every other row alone; the
+    written rows equal the plain quantiser's output for them."""
+    _say("fp4 quant decode")
+    B, ne, W, m = 5, 300, 64, 4
+    cache = I.normal((B, ne, W), ("fp4qd", "cache"), dtype="bf16", device=DEV)
+    pl = [7, 8, 1199, 402, -1]  # (p + 1) % 4 == 0 for b = 0 and 2 only
+    pos = torch.tensor(pl, dtype=torch.int64, device=DEV)
+    codes = torch.full((B, ne, W // 2), 0xAA, dtype=torch.uint8, device=DEV)
+    exps = torch.full((B, ne, W // 32), 0x55, dtype=torch.uint8, device=DEV)
+    lib.csa_indexer_fp4_quant_decode(cache, pos, m, codes, exps)
+    rc, re_ = lib.csa_indexer_fp4_quant(cache)
+    torch.cuda.synchronize()
+    written = {(b, p // m) for b, p in enumerate(pl) if p >= 0 and (p + 1) % m == 0}
+    assert written == {(0, 1), (2, 299)}
+    for b in range(B):
+        for r in range(ne):
+            if (b, r) in written:
+                assert torch.equal(codes[b, r], rc[b, r]) and torch.equal(exps[b, r], re_[b, r])
+    mask = torch.ones((B, ne), dtype=torch.bool)
+    for b, r in written:
+        mask[b, r] = False
+    assert (codes.cpu()[mask] == 0xAA).all() and (exps.cpu()[mask] == 0x55).all()
+
+
+def test_decode_step_with_fp4_indexer_keeps_the_fp4_cache(lib):
+    """The benchmark's decode step on the FP4 indexer path: after a step that
+    emits an entry, its FP4 key cache equals a fresh quantisation of the bf16
+    key cache, and its selection equals the FP4 top-k over that cache."""
+    import bench
+    print("[fp4] decode step B=3 ctx=4100 d=512", flush=True)
+    cfg = dict(name="fp4-step-check", kind="decode", dtype="bf16", batch=3, ctx=4100, d=512,
+               c=512, m=4, overlap=1, m_hca=128, hI=16, cI=64, k=256, nh=64, n_win=128,
+               rope_dims=64, qk_norm=1, eps=1e-6, theta=10000.0)
+    hd = bench.HybridDecode(cfg, DEV)
+    hd.step_fp4(streams=True)
+    torch.cuda.synchronize()
+    kc, ke = lib.csa_indexer_fp4_quant(hd.kcache)
+    assert torch.equal(kc, hd.kc) and torch.equal(ke, hd.ke)
+    qc, qe = lib.csa_indexer_fp4_quant(hd.g["qI"])
+    idx = lib.csa_index_topk_decode_fp4(qc, qe, hd.g["wI"], kc, ke, hd.pos, cfg["m"], cfg["k"])
+    torch.cuda.synchronize()
+    assert torch.equal(idx, hd.idx)
