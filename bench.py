@@ -376,6 +376,68 @@ class HybridDecode:
         L.csa_sparse_mqa_decode(g["csa_q"], self.ring, self.cache, self.idx, self.pos, g["csa_sink"],
                                 rope_dims=r, out=self.out_c)
 
+    def paginate(self, page_tokens=128, seed=0):
+        """Copies of the three entry caches as shuffled pools of pages of
+        `page_tokens` raw tokens (page_tokens / m entries each) with their
+        page tables, for step_paged."""
+        dev = self.cache.device
+        gen = torch.Generator(device="cpu").manual_seed(seed)
+        self.pg = {}
+        for name, cache, m in (("cache", self.cache, self.cfg["m"]),
+                               ("kcache", self.kcache, self.cfg["m"]),
+                               ("hcache", self.hcache, self.cfg["m_hca"])):
+            B, ne, w = cache.shape
+            pe = max(1, page_tokens // m)
+            npg = -(-ne // pe)
+            table = torch.randperm(B * npg, generator=gen).to(torch.int32).reshape(B, npg)
+            e = torch.arange(ne)
+            rows = (table[:, e // pe].long() * pe + (e % pe)[None]).reshape(-1).to(dev)
+            pool = torch.empty((B * npg * pe, w), dtype=cache.dtype, device=dev)
+            pool[rows] = cache.reshape(B * ne, w)
+            self.pg[name] = (pool, table.to(dev), pe)
+        torch.cuda.synchronize()
+
+    def step_paged(self, streams=True):
+        """The decode step over the paged caches of paginate(): the same calls
+        as step() through their _paged entry points."""
+        c, g = self.cfg, self.g
+        m, ov, r = c["m"], c["overlap"], c["rope_dims"]
+        (cp, ct, ce), (kp, kt, ke), (hp, ht, he) = (self.pg["cache"], self.pg["kcache"],
+                                                    self.pg["hcache"])
+        main = torch.cuda.current_stream()
+        if streams:
+            if self.side is None:
+                self.side = (torch.cuda.Stream(), torch.cuda.Stream())
+            sb, sc = self.side
+            sb.wait_stream(main)
+            sc.wait_stream(main)
+        else:
+            sb = sc = main
+        with torch.cuda.stream(sb):
+            L.csa_compress_decode_paged(self.h, self.pos, g["WI_kv"], g["WI_z"], g["apeI"], m, ov,
+                                        self.sti, kp, kt, ke, n_entries=self.kcache.shape[1],
+                                        ws_slot="decode_proj_idx")
+            L.csa_index_topk_decode_paged(g["qI"], g["wI"], kp, kt, ke, self.pos, m, c["k"],
+                                          n_entries=self.kcache.shape[1], out=self.idx)
+        with torch.cuda.stream(sc):
+            L.csa_compress_decode_paged(self.h, self.pos, g["csa_Wkv"], g["csa_Wz"], g["csa_ape"],
+                                        m, ov, self.st, cp, ct, ce, W_win=g["csa_Wwin"],
+                                        win_ring=self.ring, n_entries=self.cache.shape[1],
+                                        rope_dims=r, ws_slot="decode_proj_csa")
+        L.csa_compress_decode_paged(self.h, self.pos, g["hca_Wkv"], g["hca_Wz"], g["hca_ape"],
+                                    c["m_hca"], 0, self.sth, hp, ht, he, W_win=g["hca_Wwin"],
+                                    win_ring=self.hring, n_entries=self.hcache.shape[1],
+                                    rope_dims=r, ws_slot="decode_proj_hca")
+        L.hca_dense_mqa_decode_paged(g["hca_q"], self.hring, hp, ht, he, self.pos, g["hca_sink"],
+                                     c["m_hca"], n_entries=self.hcache.shape[1], rope_dims=r,
+                                     out=self.out_h)
+        if streams:
+            main.wait_stream(sb)
+            main.wait_stream(sc)
+        L.csa_sparse_mqa_decode_paged(g["csa_q"], self.ring, cp, ct, ce, self.idx, self.pos,
+                                      g["csa_sink"], n_entries=self.cache.shape[1], rope_dims=r,
+                                      out=self.out_c)
+
     def algorithmic_bytes(self):
         """Bytes a decode step must move at least once (bf16 = 2 B)."""
         c = self.cfg
@@ -589,6 +651,18 @@ def main():
                 "key_bytes_per_entry": [kc.shape[-1] + ke.shape[-1], 2 * hd.kcache.shape[-1]],
                 "recall_of_bf16_selection": float(hit.sum().item()) / float((hd.idx >= 0).sum().item())}
             del kc, ke, qc, qe, idx4, pos_, hit
+            # the same step over caches in shuffled pages of 128 raw tokens
+            hd.paginate(128)
+            gp = graph_of(hd.step_paged)
+            tgp = time_region(gp.replay, nd, 3, flush=flush)
+            tgpw = time_region(gp.replay, nd, 3)
+            del gp
+            dec[wname]["paged"] = {
+                "page_tokens": 128,
+                "page_entries": {"csa": hd.pg["cache"][2], "indexer": hd.pg["kcache"][2],
+                                 "hca": hd.pg["hcache"][2]},
+                "graph_us_per_step": float(np.median(tgp)) * 1e3,
+                "graph_us_per_step_warm_cache": float(np.mean(tgpw)) * 1e3}
             del hd
             torch.cuda.empty_cache()
         rec["decode"] = dec

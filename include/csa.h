@@ -4,7 +4,8 @@
  *
  * Citation keys (page title, then where on the page):
  *   [R] "DeepSeek-V4 技术解读报告" (juejin.cn/post/7631898635937497134),
- *       section 2.3 (equations 9-23, 27) and section 4.3 (determinism).
+ *       section 2.3 (equations 9-23, 27), section 4.3 (determinism) and
+ *       section 4.6 (inference framework: the heterogeneous KV cache).
  *   [A] "DeepSeek-V4：算法架构" (1zeryu.github.io/p/deepseek-v4/), code
  *       excerpts: attention Q/KV path, Sparse Attention candidate assembly,
  *       Compressor, Indexer, HCA selection rule, output projection.
@@ -54,7 +55,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 4
+#define CSA_ABI_VERSION 5
 
 typedef enum csa_status {
   CSA_OK = 0,
@@ -331,6 +332,57 @@ int hca_dense_mqa_prefill(const csa_attn_desc* desc, const void* q, const void* 
 int hca_dense_mqa_decode(const csa_attn_desc* desc, const void* q, const void* win_ring,
                          const void* comp_cache, const int64_t* pos, const float* sink,
                          void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Decode over paged entry caches -- [R] section 4.6: the compressed
+ * ("classical") caches are handed out in pages of a fixed number of raw
+ * tokens, while the window ring and the compressor state (the "state cache")
+ * stay preallocated per sequence.
+ *
+ * Each _paged call computes exactly what its contiguous form computes (the
+ * results are bit-identical) with the per-sequence cache [B, N, width]
+ * replaced by a shared pool of pages:
+ *   pool        [P * page_entries, width]  entry rows of all sequences
+ *   page_table  [B, max_pages]  int32 (device), max_pages =
+ *               ceil(N / page_entries) with N = desc->max_entries (compressor)
+ *               or desc->n_entries (indexer, attention)
+ *   page_entries  entries per page (>= 1); a page of 128 raw tokens holds
+ *               128 / m entries (32 for m = 4, 1 for m = 128)
+ * Entry e of sequence b lives in pool row
+ *   page_table[b * max_pages + e / page_entries] * page_entries
+ *     + e % page_entries.
+ * Only the table slots of the pages holding entries that the call reads
+ * (e < min(floor((pos[b]+1)/m), N)) or writes (the emitted entry
+ * pos[b] / m) are read; each must name a page of the pool (0 <= id < P).
+ * The library cannot check ids against P: an id outside the pool reads or
+ * writes outside it.  Two sequences may share a page only for entries that
+ * no call writes (a shared prefix).  Errors: NULL page_table or
+ * page_entries < 1 -> CSA_ERR_INVALID_ARG; the attention calls support
+ * dtype CSA_BF16 only (CSA_ERR_UNSUPPORTED otherwise).  Workspaces are those
+ * of the contiguous entry (CSA_ENTRY_COMPRESS_DECODE, _INDEX_TOPK_DECODE,
+ * _SPARSE_MQA_DECODE, _DENSE_MQA_DECODE), zero bytes included.
+ * ---------------------------------------------------------------------- */
+int csa_compress_decode_paged(const csa_compress_desc* desc, const void* h, const int64_t* pos,
+                              const void* W_kv, const void* W_z, const float* ape,
+                              const void* W_win, float* state, void* cache_pool,
+                              const int32_t* page_table, int32_t page_entries, void* win_ring,
+                              void* ws, size_t ws_bytes, void* stream);
+
+int csa_index_topk_decode_paged(const csa_index_desc* desc, const void* qI, const void* wI,
+                                const void* KI_pool, const int32_t* page_table,
+                                int32_t page_entries, const int64_t* pos, int32_t* idx_out,
+                                void* ws, size_t ws_bytes, void* stream);
+
+int csa_sparse_mqa_decode_paged(const csa_attn_desc* desc, const void* q, const void* win_ring,
+                                const void* comp_pool, const int32_t* page_table,
+                                int32_t page_entries, const int32_t* idx, const int64_t* pos,
+                                const float* sink, void* out, void* ws, size_t ws_bytes,
+                                void* stream);
+
+int hca_dense_mqa_decode_paged(const csa_attn_desc* desc, const void* q, const void* win_ring,
+                               const void* comp_pool, const int32_t* page_table,
+                               int32_t page_entries, const int64_t* pos, const float* sink,
+                               void* out, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Helpers

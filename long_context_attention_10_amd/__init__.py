@@ -28,7 +28,9 @@ EXPORTED = ["csa_compress_prefill", "csa_compress_decode", "csa_state_bytes", "c
             "csa_sparse_mqa_decode", "hca_dense_mqa_prefill", "hca_dense_mqa_decode",
             "csa_query_proj", "csa_output_proj", "csa_indexer_fp4_quant",
             "csa_index_topk_decode_fp4", "csa_indexer_fp4_quant_decode", "csa_workspace_bytes",
-            "csa_workspace_zero_bytes", "csa_status_string", "csa_abi_version"]
+            "csa_workspace_zero_bytes", "csa_status_string", "csa_abi_version",
+            "csa_compress_decode_paged", "csa_index_topk_decode_paged",
+            "csa_sparse_mqa_decode_paged", "hca_dense_mqa_decode_paged"]
 
 
 class CompressDesc(ctypes.Structure):
@@ -110,6 +112,11 @@ def load(path: str = LIB_PATH):
     lib.csa_indexer_fp4_quant.argtypes = [P] * 5
     lib.csa_index_topk_decode_fp4.argtypes = [P] * 9 + [S, P]
     lib.csa_indexer_fp4_quant_decode.argtypes = [P, P, ctypes.c_int64, P, I, P, P, P]
+    I32 = ctypes.c_int32
+    lib.csa_compress_decode_paged.argtypes = [P] * 10 + [I32] + [P] * 2 + [S, P]
+    lib.csa_index_topk_decode_paged.argtypes = [P] * 5 + [I32] + [P] * 3 + [S, P]
+    lib.csa_sparse_mqa_decode_paged.argtypes = [P] * 5 + [I32] + [P] * 5 + [S, P]
+    lib.hca_dense_mqa_decode_paged.argtypes = [P] * 5 + [I32] + [P] * 4 + [S, P]
     for f in EXPORTED:
         if f not in ("csa_abi_version", "csa_status_string", "csa_workspace_bytes",
                      "csa_workspace_zero_bytes", "csa_state_bytes"):
@@ -267,6 +274,119 @@ def csa_compress_decode(h, pos, W_kv, W_z, ape, m, overlap, state, cache, W_win=
                                  _ptr(ape), _ptr(W_win), _ptr(state), _ptr(cache), _ptr(win_ring),
                                  _ptr(ws), wsb, _stream(h.device))
     _check(st, "csa_compress_decode")
+
+
+# -------------------------------------------------------- paged entry caches
+def _paged(pool, page_table, page_entries, B, width, dtype, n_entries, name):
+    """Checks a page pool [P * page_entries, width] and its table [B,
+    ceil(n_entries / page_entries)] int32; returns n_entries (default: the
+    table's capacity).  Page ids are not checked (that would synchronise)."""
+    if page_entries < 1:
+        raise CsaError("page_entries must be >= 1")
+    if n_entries is None:
+        n_entries = page_table.shape[1] * page_entries
+    _expect(page_table, (B, -(-n_entries // page_entries)), torch.int32, "page_table")
+    if pool.dim() != 2 or pool.shape[1] != width or pool.shape[0] % page_entries:
+        raise CsaError(f"{name}: expected [pages * {page_entries}, {width}], got "
+                       f"{tuple(pool.shape)}")
+    if pool.dtype != dtype:
+        raise CsaError(f"{name}: expected {dtype}, got {pool.dtype}")
+    return n_entries
+
+
+def csa_compress_decode_paged(h, pos, W_kv, W_z, ape, m, overlap, state, cache_pool, page_table,
+                              page_entries, W_win=None, win_ring=None, n_entries=None,
+                              qk_norm=True, eps=1e-6, rope_dims=0, rope_theta=10000.0,
+                              ws_slot="decode_proj"):
+    """csa_compress_decode with the entry cache in pages: entry e of sequence
+    b is row page_table[b, e // page_entries] * page_entries + e %
+    page_entries of cache_pool."""
+    lib = load()
+    B, d = h.shape
+    w = W_kv.shape[0]
+    c = w // (2 if overlap else 1)
+    _expect(pos, (B,), torch.int64, "pos")
+    ne = _paged(cache_pool, page_table, page_entries, B, c, h.dtype, n_entries, "cache_pool")
+    n_win = win_ring.shape[1] if win_ring is not None else 0
+    desc = compress_desc(batch=B, d=d, c=c, m=m, overlap=overlap, dtype=_dt(h), qk_norm=qk_norm,
+                         eps=eps, rope_dims=rope_dims, rope_theta=rope_theta, n_win=n_win,
+                         max_entries=ne)
+    if state.numel() * 4 < csa_state_bytes(desc):
+        raise CsaError("state too small")
+    ws, wsb = workspace(workspace_bytes("compress_decode", desc), h.device, ws_slot)
+    st = lib.csa_compress_decode_paged(ctypes.byref(desc), _ptr(h), _ptr(pos), _ptr(W_kv),
+                                       _ptr(W_z), _ptr(ape), _ptr(W_win), _ptr(state),
+                                       _ptr(cache_pool), _ptr(page_table), page_entries,
+                                       _ptr(win_ring), _ptr(ws), wsb, _stream(h.device))
+    _check(st, "csa_compress_decode_paged")
+
+
+def csa_index_topk_decode_paged(qI, wI, KI_pool, page_table, page_entries, pos, m, k,
+                                n_entries=None, out=None):
+    lib = load()
+    B, hI, cI = qI.shape
+    ne = _paged(KI_pool, page_table, page_entries, B, cI, qI.dtype, n_entries, "KI_pool")
+    _expect(pos, (B,), torch.int64, "pos")
+    desc = IndexDesc(0, B, hI, cI, m, k, _dt(qI), ne)
+    if out is None:
+        out = torch.empty((B, k), dtype=torch.int32, device=qI.device)
+    ws, wsb = workspace(workspace_bytes("index_topk_decode", desc), qI.device, "index_dec",
+                        zero_bytes=workspace_zero_bytes("index_topk_decode", desc))
+    st = lib.csa_index_topk_decode_paged(ctypes.byref(desc), _ptr(qI), _ptr(wI), _ptr(KI_pool),
+                                         _ptr(page_table), page_entries, _ptr(pos), _ptr(out),
+                                         _ptr(ws), wsb, _stream(qI.device))
+    if st != 0:
+        _WS_ZERO.pop((str(qI.device), "index_dec"), None)
+    _check(st, "csa_index_topk_decode_paged")
+    return out
+
+
+def csa_sparse_mqa_decode_paged(q, win_ring, comp_pool, page_table, page_entries, idx, pos, sink,
+                                n_entries=None, scale=None, qk_norm=True, eps=1e-6, rope_dims=0,
+                                rope_theta=10000.0, out=None):
+    lib = load()
+    B, nh, c = q.shape
+    n_win = win_ring.shape[1]
+    k = idx.shape[1]
+    _expect(win_ring, (B, n_win, c), q.dtype, "win_ring")
+    ne = _paged(comp_pool, page_table, page_entries, B, c, q.dtype, n_entries, "comp_pool")
+    _expect(idx, (B, k), torch.int32, "idx")
+    _expect(pos, (B,), torch.int64, "pos")
+    desc = attn_desc(batch=B, nh=nh, c=c, k=k, n_win=n_win, dtype=_dt(q), scale=scale,
+                     qk_norm=qk_norm, eps=eps, rope_dims=rope_dims, rope_theta=rope_theta,
+                     n_entries=ne)
+    if out is None:
+        out = torch.empty_like(q)
+    ws, wsb = workspace(workspace_bytes("sparse_mqa_decode", desc), q.device, "attn_dec_s")
+    st = lib.csa_sparse_mqa_decode_paged(ctypes.byref(desc), _ptr(q), _ptr(win_ring),
+                                         _ptr(comp_pool), _ptr(page_table), page_entries,
+                                         _ptr(idx), _ptr(pos), _ptr(sink), _ptr(out), _ptr(ws),
+                                         wsb, _stream(q.device))
+    _check(st, "csa_sparse_mqa_decode_paged")
+    return out
+
+
+def hca_dense_mqa_decode_paged(q, win_ring, comp_pool, page_table, page_entries, pos, sink, m,
+                               n_entries=None, scale=None, qk_norm=True, eps=1e-6, rope_dims=0,
+                               rope_theta=10000.0, out=None):
+    lib = load()
+    B, nh, c = q.shape
+    n_win = win_ring.shape[1]
+    _expect(win_ring, (B, n_win, c), q.dtype, "win_ring")
+    ne = _paged(comp_pool, page_table, page_entries, B, c, q.dtype, n_entries, "comp_pool")
+    _expect(pos, (B,), torch.int64, "pos")
+    desc = attn_desc(batch=B, nh=nh, c=c, m=m, n_win=n_win, dtype=_dt(q), scale=scale,
+                     qk_norm=qk_norm, eps=eps, rope_dims=rope_dims, rope_theta=rope_theta,
+                     n_entries=ne)
+    if out is None:
+        out = torch.empty_like(q)
+    ws, wsb = workspace(workspace_bytes("dense_mqa_decode", desc), q.device, "attn_dec_d")
+    st = lib.hca_dense_mqa_decode_paged(ctypes.byref(desc), _ptr(q), _ptr(win_ring),
+                                        _ptr(comp_pool), _ptr(page_table), page_entries,
+                                        _ptr(pos), _ptr(sink), _ptr(out), _ptr(ws), wsb,
+                                        _stream(q.device))
+    _check(st, "hca_dense_mqa_decode_paged")
+    return out
 
 
 # ----------------------------------------------------------------- indexer

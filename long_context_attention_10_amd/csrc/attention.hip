@@ -491,7 +491,8 @@ static hipError_t dispatch_decode(const csa_attn_desc& d, const void* q, const v
 
 hipError_t launch_mqa_decode(const csa_attn_desc& d, int mode, const void* q, const void* ring,
                              const void* cache, const int32_t* idx, const int64_t* pos,
-                             const float* sink, void* out, void* ws, hipStream_t st) {
+                             const float* sink, void* out, void* ws, hipStream_t st,
+                             EntryMap em) {
   if (d.batch == 0) return hipSuccess;
   if (d.dtype == CSA_BF16) {
     const int S_ = decode_nsplit(d, mode);
@@ -499,7 +500,7 @@ hipError_t launch_mqa_decode(const csa_attn_desc& d, int mode, const void* q, co
     float* ws_o = (float*)ws;
     float2* ws_ml = (float2*)((uint8_t*)ws + ((rows * d.c * 4 + 255) & ~(size_t)255));
     return launch_mqa_decode_bf16(d, mode, q, ring, cache, idx, pos, sink, out, ws_o, ws_ml, S_,
-                                  st);
+                                  st, em);
   }
   if (d.dtype == CSA_BF16)
     return mode == ATTN_SPARSE

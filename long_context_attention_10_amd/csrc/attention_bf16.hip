@@ -500,7 +500,7 @@ __global__ __launch_bounds__(256, 2) void mqa_decode_bf16_kernel(
     const uint16_t* __restrict__ cache, const int32_t* __restrict__ idx,
     const float* __restrict__ sink, int nh, int k, int m, int n_win, float scale, int qk_norm,
     float eps, int r, float theta, int64_t n_entries, const int64_t* __restrict__ posv,
-    float* __restrict__ ws_o, float2* __restrict__ ws_ml, int nsplit, int spl) {
+    float* __restrict__ ws_o, float2* __restrict__ ws_ml, int nsplit, int spl, EntryMap em) {
   typedef Geo<C> G;
   typedef OAcc<C> A;
   constexpr int NKG = C / 32;
@@ -537,7 +537,6 @@ __global__ __launch_bounds__(256, 2) void mqa_decode_bf16_kernel(
   if (cbeg >= cend) return;  // nothing in this chunk; the combine skips it
   const int ntiles = (int)((cend - cbeg + kT - 1) / kT);
   const uint16_t* wbase = ring + b * (int64_t)n_win * C;
-  const uint16_t* cbase = cache + b * n_entries * C;
   const int64_t s0 = max64(cbeg - nwin, 0);  // first index slot staged
   // ring slot of the oldest window position (candidate j at w0 + j mod n_win)
   const int w0 = nwin > 0 ? (int)((t - nwin + 1) % n_win) : 0;
@@ -556,7 +555,7 @@ __global__ __launch_bounds__(256, 2) void mqa_decode_bf16_kernel(
                          const int64_t e = SPARSE ? (int64_t)sidx[j - nwin - s0] : j - nwin;
                          if (e < 0 || e >= n_entries) return wbase;
                          ok = true;
-                         return cbase + e * C;
+                         return cache + em.row(b, e, n_entries) * C;
                        });
   };
   const bool early0 = cbeg + kT <= nwin;  // tile 0 is window rows only
@@ -740,7 +739,7 @@ int mqa_decode_bf16_split(int mode) { return mode == ATTN_SPARSE ? 128 : 256; }
 hipError_t launch_mqa_decode_bf16(const csa_attn_desc& d, int mode, const void* q,
                                   const void* ring, const void* cache, const int32_t* idx,
                                   const int64_t* pos, const float* sink, void* out, float* ws_o,
-                                  float2* ws_ml, int nsplit, hipStream_t st) {
+                                  float2* ws_ml, int nsplit, hipStream_t st, EntryMap em) {
   const int spl = mqa_decode_bf16_split(mode);
   const dim3 grid((unsigned)nsplit, (unsigned)d.batch);
   const bool wide = nsplit > 8;  // more chunks than one wave's loads in flight
@@ -751,12 +750,12 @@ hipError_t launch_mqa_decode_bf16(const csa_attn_desc& d, int mode, const void* 
       mqa_decode_bf16_kernel<CC, true><<<grid, 256, 0, st>>>(                                 \
           (const uint16_t*)q, (const uint16_t*)ring, (const uint16_t*)cache, idx, sink,          \
           d.n_heads, d.k, d.m, d.n_win, d.scale, d.qk_norm, d.eps, d.rope_dims, d.rope_theta,    \
-          d.n_entries, pos, ws_o, ws_ml, nsplit, spl);                                         \
+          d.n_entries, pos, ws_o, ws_ml, nsplit, spl, em);                                     \
     else                                                                                      \
       mqa_decode_bf16_kernel<CC, false><<<grid, 256, 0, st>>>(                                \
           (const uint16_t*)q, (const uint16_t*)ring, (const uint16_t*)cache, idx, sink,          \
           d.n_heads, d.k, d.m, d.n_win, d.scale, d.qk_norm, d.eps, d.rope_dims, d.rope_theta,    \
-          d.n_entries, pos, ws_o, ws_ml, nsplit, spl);                                         \
+          d.n_entries, pos, ws_o, ws_ml, nsplit, spl, em);                                     \
     hipError_t e = hipGetLastError();                                                         \
     if (e != hipSuccess) return e;                                                            \
     if (wide)                                                                                 \

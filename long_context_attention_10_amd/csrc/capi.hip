@@ -117,6 +117,71 @@ int check_oproj(const csa_oproj_desc* d) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? CSA_OK : CSA_ERR_HIP; }
 
+// A paged cache: entry e of sequence b is pool row
+// page_table[b * max_pages + e / page] * page + e % page, with max_pages the
+// pages that `capacity` entries per sequence need.
+int entry_map(const int32_t* table, int32_t page, int64_t capacity, EntryMap* em) {
+  if (!table || page <= 0 || capacity < 0) return CSA_ERR_INVALID_ARG;
+  const int64_t np = (capacity + page - 1) / page;
+  if (np > INT32_MAX) return CSA_ERR_UNSUPPORTED;
+  em->table = table;
+  em->page = page;
+  em->max_pages = (int32_t)np;
+  return CSA_OK;
+}
+
+int compress_decode(const csa_compress_desc* d, const void* h, const int64_t* pos,
+                    const void* W_kv, const void* W_z, const float* ape, const void* W_win,
+                    float* state, void* cache, void* win_ring, void* ws, size_t ws_bytes,
+                    void* stream, EntryMap em) {
+  int s = check_compress(d, true);
+  if (s) return s;
+  if (!h || !pos || !W_kv || !W_z || !ape || !state || !cache) return CSA_ERR_INVALID_ARG;
+  const bool has_win = W_win != nullptr;
+  if (has_win != (win_ring != nullptr)) return CSA_ERR_INVALID_ARG;
+  if (has_win && d->n_win <= 0) return CSA_ERR_INVALID_ARG;
+  const size_t need = ws_compress_decode(d, has_win);
+  if (!ws || ws_bytes < need) return CSA_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const int w = (1 + d->overlap) * d->c;
+  const int N = 2 * w + (has_win ? d->c : 0);
+  const int ks = decode_proj_ksplit(N, d->d, d->dtype);
+  WeightStack stack = {{W_kv, W_z, W_win}, {w, w, has_win ? d->c : 0}};
+  hipError_t e = launch_decode_proj(d->dtype, h, d->batch, d->d, stack, (float*)ws, ks, st);
+  if (e != hipSuccess) return CSA_ERR_HIP;
+  e = launch_decode_update(d->dtype, (const float*)ws, ks, d->batch, N, d->c, d->m, d->overlap,
+                           has_win, ape, pos, state, cache, d->max_entries, win_ring, d->n_win,
+                           d->qk_norm, d->eps, d->rope_dims, d->rope_theta, st, em);
+  return hip_status(e);
+}
+
+int index_topk_decode(const csa_index_desc* d, const void* qI, const void* wI,
+                      const void* KI_cache, const int64_t* pos, int32_t* idx_out, void* ws,
+                      size_t ws_bytes, void* stream, EntryMap em) {
+  int s = check_index(d, true);
+  if (s) return s;
+  if (!qI || !wI || !KI_cache || !pos || !idx_out) return CSA_ERR_INVALID_ARG;
+  const size_t need = index_decode_ws_bytes(*d);
+  if (!ws || ws_bytes < need) return CSA_ERR_WORKSPACE;
+  return hip_status(launch_index_topk_decode(*d, qI, wI, KI_cache, pos, idx_out, ws,
+                                             (hipStream_t)stream, em));
+}
+
+int mqa_decode(const csa_attn_desc* d, int mode, const void* q, const void* win_ring,
+               const void* comp_cache, const int32_t* idx, const int64_t* pos, const float* sink,
+               void* out, void* ws, size_t ws_bytes, void* stream, EntryMap em) {
+  const bool sparse = mode == ATTN_SPARSE;
+  int s = check_attn(d, true, sparse);
+  if (s) return s;
+  if (!q || !win_ring || !comp_cache || (sparse && !idx) || !pos || !sink || !out)
+    return CSA_ERR_INVALID_ARG;
+  if (em.table && d->dtype != CSA_BF16) return CSA_ERR_UNSUPPORTED;
+  const size_t need = mqa_decode_ws_bytes(*d, mode);
+  if (!ws || ws_bytes < need) return CSA_ERR_WORKSPACE;
+  return hip_status(launch_mqa_decode(*d, mode, q, win_ring, comp_cache, sparse ? idx : nullptr,
+                                      pos, sink, out, ws, (hipStream_t)stream, em));
+}
+
 }  // namespace
 
 extern "C" {
@@ -242,25 +307,21 @@ int csa_compress_decode(const csa_compress_desc* d, const void* h, const int64_t
                         const void* W_kv, const void* W_z, const float* ape, const void* W_win,
                         float* state, void* cache, void* win_ring, void* ws, size_t ws_bytes,
                         void* stream) {
-  int s = check_compress(d, true);
+  return compress_decode(d, h, pos, W_kv, W_z, ape, W_win, state, cache, win_ring, ws, ws_bytes,
+                         stream, EntryMap());
+}
+
+int csa_compress_decode_paged(const csa_compress_desc* d, const void* h, const int64_t* pos,
+                              const void* W_kv, const void* W_z, const float* ape,
+                              const void* W_win, float* state, void* cache_pool,
+                              const int32_t* page_table, int32_t page_entries, void* win_ring,
+                              void* ws, size_t ws_bytes, void* stream) {
+  if (!d) return CSA_ERR_INVALID_ARG;
+  EntryMap em;
+  int s = entry_map(page_table, page_entries, d->max_entries, &em);
   if (s) return s;
-  if (!h || !pos || !W_kv || !W_z || !ape || !state || !cache) return CSA_ERR_INVALID_ARG;
-  const bool has_win = W_win != nullptr;
-  if (has_win != (win_ring != nullptr)) return CSA_ERR_INVALID_ARG;
-  if (has_win && d->n_win <= 0) return CSA_ERR_INVALID_ARG;
-  const size_t need = ws_compress_decode(d, has_win);
-  if (!ws || ws_bytes < need) return CSA_ERR_WORKSPACE;
-  hipStream_t st = (hipStream_t)stream;
-  const int w = (1 + d->overlap) * d->c;
-  const int N = 2 * w + (has_win ? d->c : 0);
-  const int ks = decode_proj_ksplit(N, d->d, d->dtype);
-  WeightStack stack = {{W_kv, W_z, W_win}, {w, w, has_win ? d->c : 0}};
-  hipError_t e = launch_decode_proj(d->dtype, h, d->batch, d->d, stack, (float*)ws, ks, st);
-  if (e != hipSuccess) return CSA_ERR_HIP;
-  e = launch_decode_update(d->dtype, (const float*)ws, ks, d->batch, N, d->c, d->m, d->overlap,
-                           has_win, ape, pos, state, cache, d->max_entries, win_ring, d->n_win,
-                           d->qk_norm, d->eps, d->rope_dims, d->rope_theta, st);
-  return hip_status(e);
+  return compress_decode(d, h, pos, W_kv, W_z, ape, W_win, state, cache_pool, win_ring, ws,
+                         ws_bytes, stream, em);
 }
 
 int csa_index_topk_prefill(const csa_index_desc* d, const void* qI, const void* wI,
@@ -283,13 +344,18 @@ int csa_index_topk_prefill(const csa_index_desc* d, const void* qI, const void* 
 int csa_index_topk_decode(const csa_index_desc* d, const void* qI, const void* wI,
                           const void* KI_cache, const int64_t* pos, int32_t* idx_out, void* ws,
                           size_t ws_bytes, void* stream) {
-  int s = check_index(d, true);
+  return index_topk_decode(d, qI, wI, KI_cache, pos, idx_out, ws, ws_bytes, stream, EntryMap());
+}
+
+int csa_index_topk_decode_paged(const csa_index_desc* d, const void* qI, const void* wI,
+                                const void* KI_pool, const int32_t* page_table,
+                                int32_t page_entries, const int64_t* pos, int32_t* idx_out,
+                                void* ws, size_t ws_bytes, void* stream) {
+  if (!d) return CSA_ERR_INVALID_ARG;
+  EntryMap em;
+  int s = entry_map(page_table, page_entries, d->n_entries, &em);
   if (s) return s;
-  if (!qI || !wI || !KI_cache || !pos || !idx_out) return CSA_ERR_INVALID_ARG;
-  const size_t need = index_decode_ws_bytes(*d);
-  if (!ws || ws_bytes < need) return CSA_ERR_WORKSPACE;
-  return hip_status(launch_index_topk_decode(*d, qI, wI, KI_cache, pos, idx_out, ws,
-                                             (hipStream_t)stream));
+  return index_topk_decode(d, qI, wI, KI_pool, pos, idx_out, ws, ws_bytes, stream, em);
 }
 
 int csa_query_proj(const csa_query_desc* d, const void* H, const void* W_DQ, const float* g_q,
@@ -372,13 +438,21 @@ int csa_sparse_mqa_prefill(const csa_attn_desc* d, const void* q, const void* wi
 int csa_sparse_mqa_decode(const csa_attn_desc* d, const void* q, const void* win_ring,
                           const void* comp_cache, const int32_t* idx, const int64_t* pos,
                           const float* sink, void* out, void* ws, size_t ws_bytes, void* stream) {
-  int s = check_attn(d, true, true);
+  return mqa_decode(d, ATTN_SPARSE, q, win_ring, comp_cache, idx, pos, sink, out, ws, ws_bytes,
+                    stream, EntryMap());
+}
+
+int csa_sparse_mqa_decode_paged(const csa_attn_desc* d, const void* q, const void* win_ring,
+                                const void* comp_pool, const int32_t* page_table,
+                                int32_t page_entries, const int32_t* idx, const int64_t* pos,
+                                const float* sink, void* out, void* ws, size_t ws_bytes,
+                                void* stream) {
+  if (!d) return CSA_ERR_INVALID_ARG;
+  EntryMap em;
+  int s = entry_map(page_table, page_entries, d->n_entries, &em);
   if (s) return s;
-  if (!q || !win_ring || !comp_cache || !idx || !pos || !sink || !out) return CSA_ERR_INVALID_ARG;
-  const size_t need = mqa_decode_ws_bytes(*d, ATTN_SPARSE);
-  if (!ws || ws_bytes < need) return CSA_ERR_WORKSPACE;
-  return hip_status(launch_mqa_decode(*d, ATTN_SPARSE, q, win_ring, comp_cache, idx, pos, sink,
-                                      out, ws, (hipStream_t)stream));
+  return mqa_decode(d, ATTN_SPARSE, q, win_ring, comp_pool, idx, pos, sink, out, ws, ws_bytes,
+                    stream, em);
 }
 
 int hca_dense_mqa_prefill(const csa_attn_desc* d, const void* q, const void* win_kv,
@@ -396,13 +470,20 @@ int hca_dense_mqa_prefill(const csa_attn_desc* d, const void* q, const void* win
 int hca_dense_mqa_decode(const csa_attn_desc* d, const void* q, const void* win_ring,
                          const void* comp_cache, const int64_t* pos, const float* sink, void* out,
                          void* ws, size_t ws_bytes, void* stream) {
-  int s = check_attn(d, true, false);
+  return mqa_decode(d, ATTN_DENSE, q, win_ring, comp_cache, nullptr, pos, sink, out, ws, ws_bytes,
+                    stream, EntryMap());
+}
+
+int hca_dense_mqa_decode_paged(const csa_attn_desc* d, const void* q, const void* win_ring,
+                               const void* comp_pool, const int32_t* page_table,
+                               int32_t page_entries, const int64_t* pos, const float* sink,
+                               void* out, void* ws, size_t ws_bytes, void* stream) {
+  if (!d) return CSA_ERR_INVALID_ARG;
+  EntryMap em;
+  int s = entry_map(page_table, page_entries, d->n_entries, &em);
   if (s) return s;
-  if (!q || !win_ring || !comp_cache || !pos || !sink || !out) return CSA_ERR_INVALID_ARG;
-  const size_t need = mqa_decode_ws_bytes(*d, ATTN_DENSE);
-  if (!ws || ws_bytes < need) return CSA_ERR_WORKSPACE;
-  return hip_status(launch_mqa_decode(*d, ATTN_DENSE, q, win_ring, comp_cache, nullptr, pos, sink,
-                                      out, ws, (hipStream_t)stream));
+  return mqa_decode(d, ATTN_DENSE, q, win_ring, comp_pool, nullptr, pos, sink, out, ws, ws_bytes,
+                    stream, em);
 }
 
 }  // extern "C"

@@ -533,7 +533,7 @@ __global__ __launch_bounds__(256) void decode_update_kernel(
     const float* __restrict__ part, int ksplit, int B, int N, int c, int m, int ov, int has_win,
     const float* __restrict__ ape, const int64_t* __restrict__ posv, float* __restrict__ state,
     typename T::S* __restrict__ cache, int64_t max_entries, typename T::S* __restrict__ ring,
-    int n_win, int qk_norm, float eps, int r, float theta) {
+    int n_win, int qk_norm, float eps, int r, float theta, EntryMap em) {
   __shared__ float red[4];
   const int b = blockIdx.x;
   const int j = threadIdx.x;  // channel pair (2j, 2j+1)
@@ -613,7 +613,7 @@ __global__ __launch_bounds__(256) void decode_update_kernel(
   if (emit) {  // uniform across the block
     row_finish<G>(e0, e1, j, c, (int64_t)m * blk, qk_norm, eps, r, theta, red);
     if (live && blk < max_entries) {
-      typename T::S* dst = cache + ((int64_t)b * max_entries + blk) * c;
+      typename T::S* dst = cache + em.row(b, blk, max_entries) * c;
       T::st(dst, 2 * j, e0);
       T::st(dst, 2 * j + 1, e1);
     }
@@ -759,17 +759,17 @@ hipError_t launch_decode_update(int dtype, const float* part, int ksplit, int B,
                                 int m, int ov, int has_win, const float* ape, const int64_t* pos,
                                 float* state, void* cache, int64_t max_entries, void* ring,
                                 int n_win, int qk_norm, float eps, int r, float theta,
-                                hipStream_t st) {
+                                hipStream_t st, EntryMap em) {
   CSA_DISPATCH_G(c, {
     const int threads = G < 64 ? 64 : G;
     if (dtype == CSA_BF16)
       decode_update_kernel<BF16, G><<<B, threads, 0, st>>>(
           part, ksplit, B, N, c, m, ov, has_win, ape, pos, state, (BF16::S*)cache, max_entries,
-          (BF16::S*)ring, n_win, qk_norm, eps, r, theta);
+          (BF16::S*)ring, n_win, qk_norm, eps, r, theta, em);
     else
       decode_update_kernel<F32, G><<<B, threads, 0, st>>>(
           part, ksplit, B, N, c, m, ov, has_win, ape, pos, state, (float*)cache, max_entries,
-          (float*)ring, n_win, qk_norm, eps, r, theta);
+          (float*)ring, n_win, qk_norm, eps, r, theta, em);
   });
   return hipGetLastError();
 }

@@ -154,6 +154,19 @@ CSA_DEV float swap32_pair_add(float a, float b) {
 }
 
 // Order-preserving map fp32 -> uint32 (larger float -> larger key).
+// Where entry e of sequence b sits in a decode cache: row b * n_entries + e
+// of a contiguous [B, n_entries] cache when table is null, else row
+// table[b * max_pages + e / page] * page + e % page of a page pool.
+struct EntryMap {
+  const int32_t* table = nullptr;
+  int32_t page = 1;
+  int32_t max_pages = 0;
+  CSA_DEV int64_t row(int64_t b, int64_t e, int64_t n_entries) const {
+    if (!table) return b * n_entries + e;
+    return (int64_t)table[b * max_pages + e / page] * page + e % page;
+  }
+};
+
 CSA_DEV uint32_t float_key(float f) {
   uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);

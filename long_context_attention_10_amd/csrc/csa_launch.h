@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "../../include/csa.h"
+#include "csa_common.h"  // EntryMap
 
 namespace csa {
 
@@ -61,7 +62,7 @@ hipError_t launch_decode_update(int dtype, const float* part, int ksplit, int B,
                                 int m, int ov, int has_win, const float* ape, const int64_t* pos,
                                 float* state, void* cache, int64_t max_entries, void* ring,
                                 int n_win, int qk_norm, float eps, int rope_dims, float theta,
-                                hipStream_t st);
+                                hipStream_t st, EntryMap em = EntryMap());
 
 int decode_proj_ksplit(int N, int K, int dtype);
 
@@ -86,7 +87,7 @@ hipError_t launch_fp4_rotate_quant(int dtype, const void* x, int64_t rows, int w
                                    int64_t n_entries, int m, hipStream_t st);
 hipError_t launch_index_topk_decode(const csa_index_desc& d, const void* qI, const void* wI,
                                     const void* KI, const int64_t* pos, int32_t* idx_out,
-                                    void* ws, hipStream_t st);
+                                    void* ws, hipStream_t st, EntryMap em = EntryMap());
 
 // ------------------------------------------------------------- attention
 enum AttnMode { ATTN_SPARSE = 0, ATTN_DENSE = 1 };
@@ -105,10 +106,12 @@ int mqa_decode_bf16_split(int mode);
 hipError_t launch_mqa_decode_bf16(const csa_attn_desc& d, int mode, const void* q,
                                   const void* ring, const void* cache, const int32_t* idx,
                                   const int64_t* pos, const float* sink, void* out, float* ws_o,
-                                  float2* ws_ml, int nsplit, hipStream_t st);
+                                  float2* ws_ml, int nsplit, hipStream_t st,
+                                  EntryMap em = EntryMap());
 hipError_t launch_mqa_decode(const csa_attn_desc& d, int mode, const void* q, const void* ring,
                              const void* cache, const int32_t* idx, const int64_t* pos,
-                             const float* sink, void* out, void* ws, hipStream_t st);
+                             const float* sink, void* out, void* ws, hipStream_t st,
+                             EntryMap em = EntryMap());
 
 // The layer around the attention calls (layer.hip).
 size_t query_proj_ws_bytes(const csa_query_desc& d);

@@ -568,7 +568,7 @@ template <class T, int HI, int CI>
 __global__ __launch_bounds__(256) void dec_score_kernel(
     const typename T::S* __restrict__ qI, const typename T::S* __restrict__ wI,
     const typename T::S* __restrict__ KI, const int64_t* __restrict__ posv, int64_t n_entries,
-    int m, int k, float* __restrict__ scores, int* __restrict__ hist, int ncopies) {
+    int m, int k, float* __restrict__ scores, int* __restrict__ hist, int ncopies, EntryMap em) {
   typedef typename T::S S;
   constexpr int E = 16 / (int)sizeof(S);
   constexpr int KGE = 4 * E;      // elements per 16x16 k-group
@@ -597,7 +597,6 @@ __global__ __launch_bounds__(256) void dec_score_kernel(
     wv[i] = h < HI ? T::ld(wI, (int64_t)b * HI + h) : 0.f;
   }
   __syncthreads();
-  const S* kb = KI + (int64_t)b * n_entries * CI;
   // Each wave scores a contiguous quarter of the chunk, 64 keys (4 steps of
   // 16) at a time; the next 64 keys load while the current ones are scored.
   const int64_t w0 = c0 + (int64_t)wave * (kDecChunk / 4);
@@ -606,8 +605,9 @@ __global__ __launch_bounds__(256) void dec_score_kernel(
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int64_t s = min64(s0 + u * 16 + (lane & 15), c1 - 1);  // past c1: not stored
+      const S* krow = KI + em.row(b, s, n_entries) * CI;
 #pragma unroll
-      for (int g = 0; g < NG; ++g) dst[u][g] = *(const uint4*)(kb + s * CI + g * KGE + lg * E);
+      for (int g = 0; g < NG; ++g) dst[u][g] = *(const uint4*)(krow + g * KGE + lg * E);
     }
   };
   auto score64 = [&](int64_t s0, const uint4 (&src)[4][NG]) {
@@ -1272,7 +1272,7 @@ static hipError_t dec_select(const csa_index_desc& d, const DecWs& w, int64_t nc
 
 hipError_t launch_index_topk_decode(const csa_index_desc& d, const void* qI, const void* wI,
                                     const void* KI, const int64_t* pos, int32_t* idx_out,
-                                    void* wsp, hipStream_t st) {
+                                    void* wsp, hipStream_t st, EntryMap em) {
   DecWs w = carve(wsp, d);
   const int B = d.batch;
   const int64_t nch = dec_chunks(d);
@@ -1282,11 +1282,11 @@ hipError_t launch_index_topk_decode(const csa_index_desc& d, const void* qI, con
     if (d.dtype == CSA_BF16)
       dec_score_kernel<BF16, HI, CI><<<grid, 256, 0, st>>>(
           (const BF16::S*)qI, (const BF16::S*)wI, (const BF16::S*)KI, pos, d.n_entries, d.m, d.k,
-          w.scores, w.hist, ncopies);
+          w.scores, w.hist, ncopies, em);
     else
       dec_score_kernel<F32, HI, CI><<<grid, 256, 0, st>>>(
           (const float*)qI, (const float*)wI, (const float*)KI, pos, d.n_entries, d.m, d.k,
-          w.scores, w.hist, ncopies);
+          w.scores, w.hist, ncopies, em);
   });
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -450,8 +450,10 @@ def fp4_quant(x):
     nb = x.shape[-1] // FP4_BLOCK
     xb = x.reshape(x.shape[:-1] + (nb, FP4_BLOCK))
     amax = np.max(np.abs(xb), axis=-1)
-    f, k = np.frexp(amax / 6.0)                 # amax/6 = f * 2^k, 0.5 <= f < 1
-    e = np.where(amax > 0, np.where(f == 0.5, k - 1, k), 0).astype(np.int64)
+    # the smallest e with amax <= 6 * 2^e, without a rounded division:
+    # amax = f * 2^k (0.5 <= f < 1) gives e = k - 3 when f <= 0.75, else k - 2
+    f, k = np.frexp(amax)
+    e = np.where(amax > 0, np.where(f <= 0.75, k - 3, k - 2), 0).astype(np.int64)
     a = np.abs(xb) / np.ldexp(1.0, e)[..., None]
     idx = np.searchsorted(FP4_GRID, a, side="right") - 1   # largest grid value <= a
     idx = np.clip(idx, 0, 7)

@@ -41,11 +41,11 @@ def test_library_exports_every_declared_symbol(lib):
     assert len(names) >= 12
     for f in names:
         assert hasattr(lib, f), f"libcsa.so does not export {f}"
-    assert set(names) <= set(L.EXPORTED) | set(names)
+    assert set(names) == set(L.EXPORTED)
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.csa_abi_version() == 4
+    assert lib.csa_abi_version() == 5
     for code in (0, -1, -2, -3, -4):
         assert len(lib.csa_status_string(code)) > 0
     assert lib.csa_status_string(-99) == b"unknown status"
@@ -235,3 +235,31 @@ def test_fp4_calls_reject(lib):
     assert lib.csa_index_topk_decode_fp4(ctypes.byref(dec), None, *([_p()] * 7), 1 << 40, None) == -1
     assert L.workspace_bytes("index_topk_decode_fp4", dec) == L.workspace_bytes("index_topk_decode", dec)
     assert L.workspace_zero_bytes("index_topk_decode_fp4", dec) > 0
+
+
+def test_paged_calls_reject(lib):
+    """The paged decode calls reject a missing page table, a page size below
+    one, and fp32 attention, before anything is enqueued."""
+    d = L.compress_desc(batch=2, d=128, c=128, m=4, max_entries=64)
+    args = [_p()] * 7  # h, pos, W_kv, W_z, ape, W_win, state
+    assert lib.csa_compress_decode_paged(ctypes.byref(d), *args, _p(), None, 32, _p(), _p(),
+                                         1 << 40, None) == -1
+    assert lib.csa_compress_decode_paged(ctypes.byref(d), *args, _p(), _p(), 0, _p(), _p(),
+                                         1 << 40, None) == -1
+    assert lib.csa_compress_decode_paged(None, *args, _p(), _p(), 32, _p(), _p(), 1 << 40,
+                                         None) == -1
+    dd = L.IndexDesc(0, 2, 16, 64, 4, 8, L.CSA_BF16, 100)
+    assert lib.csa_index_topk_decode_paged(ctypes.byref(dd), _p(), _p(), _p(), None, 32, _p(),
+                                           _p(), _p(), 1 << 40, None) == -1
+    assert lib.csa_index_topk_decode_paged(ctypes.byref(dd), _p(), _p(), _p(), _p(), -4, _p(),
+                                           _p(), _p(), 1 << 40, None) == -1
+    assert lib.csa_index_topk_decode_paged(ctypes.byref(dd), _p(), _p(), _p(), _p(), 32, _p(),
+                                           _p(), _p(), 8, None) == -3
+    a = L.attn_desc(batch=2, nh=8, c=128, k=4, n_entries=64, dtype=L.CSA_F32)
+    assert lib.csa_sparse_mqa_decode_paged(ctypes.byref(a), _p(), _p(), _p(), _p(), 32, _p(),
+                                           _p(), _p(), _p(), _p(), 1 << 40, None) == -2
+    a = L.attn_desc(batch=2, nh=8, c=128, m=4, n_entries=64, dtype=L.CSA_BF16)
+    assert lib.hca_dense_mqa_decode_paged(ctypes.byref(a), _p(), _p(), _p(), None, 1, _p(), _p(),
+                                          _p(), _p(), 1 << 40, None) == -1
+    assert lib.hca_dense_mqa_decode_paged(ctypes.byref(a), _p(), _p(), _p(), _p(), 1, _p(), _p(),
+                                          _p(), _p(), 8, None) == -3
