@@ -351,14 +351,17 @@ int hca_dense_mqa_decode(const csa_attn_desc* desc, const void* q, const void* w
  * Entry e of sequence b lives in pool row
  *   page_table[b * max_pages + e / page_entries] * page_entries
  *     + e % page_entries.
- * Only the table slots of the pages holding entries that the call reads
- * (e < min(floor((pos[b]+1)/m), N)) or writes (the emitted entry
- * pos[b] / m) are read; each must name a page of the pool (0 <= id < P).
- * The library cannot check ids against P: an id outside the pool reads or
- * writes outside it.  Two sequences may share a page only for entries that
- * no call writes (a shared prefix).  Errors: NULL page_table or
- * page_entries < 1 -> CSA_ERR_INVALID_ARG; the attention calls support
- * dtype CSA_BF16 only (CSA_ERR_UNSUPPORTED otherwise).  Workspaces are those
+ * The whole table must be readable device memory, but only the values of
+ * the slots of pages holding entries that the call reads (the visible
+ * entries e < min(floor((pos[b]+1)/m), N) for the indexer and dense
+ * attention, the entries idx names for sparse attention) or writes (the
+ * emitted entry pos[b] / m) are used; each of those must name a page of the
+ * pool (0 <= id < P), the other slots may hold anything.  The library cannot
+ * check ids against P: an id outside the pool reads or writes outside it.
+ * Two sequences may share a page only for entries that no call writes (a
+ * shared prefix).  Errors: NULL page_table or page_entries < 1 ->
+ * CSA_ERR_INVALID_ARG; N > 2^31 - 1 -> CSA_ERR_UNSUPPORTED; the attention
+ * calls support dtype CSA_BF16 only (CSA_ERR_UNSUPPORTED otherwise).  Workspaces are those
  * of the contiguous entry (CSA_ENTRY_COMPRESS_DECODE, _INDEX_TOPK_DECODE,
  * _SPARSE_MQA_DECODE, _DENSE_MQA_DECODE), zero bytes included.
  * ---------------------------------------------------------------------- */

@@ -492,9 +492,13 @@ hipError_t launch_mqa_prefill_bf16(const csa_attn_desc& d, int mode, const void*
 // the query of sequence b sits at position posv[b], window rows come from the
 // ring (position p in slot p % n_win), and the workgroup writes its
 // unnormalised partial O with (running max in log2 units, running sum), the
-// sink left to the combine.
+// sink left to the combine.  PAGED: the entry cache is a page pool; each
+// chunk looks its entries' pool rows up once, into LDS, before its first
+// tile, so no tile load waits on a page-table read.
 // ---------------------------------------------------------------------------
-template <int C, bool SPARSE>
+constexpr int kDecSplitMax = 256;  // candidates per chunk, at most
+
+template <int C, bool SPARSE, bool PAGED>
 __global__ __launch_bounds__(256, 2) void mqa_decode_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ ring,
     const uint16_t* __restrict__ cache, const int32_t* __restrict__ idx,
@@ -507,6 +511,7 @@ __global__ __launch_bounds__(256, 2) void mqa_decode_bf16_kernel(
   __shared__ __align__(16) uint8_t smem[2 * G::TILE];
   __shared__ __align__(16) int valid[2][kT];
   __shared__ int sidx[SPARSE ? kMaxK : 1];
+  __shared__ int64_t srow[PAGED ? kDecSplitMax : 1];  // pool row per staged entry slot
   __shared__ float2 rope_tab[C / 2];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -555,18 +560,31 @@ __global__ __launch_bounds__(256, 2) void mqa_decode_bf16_kernel(
                          const int64_t e = SPARSE ? (int64_t)sidx[j - nwin - s0] : j - nwin;
                          if (e < 0 || e >= n_entries) return wbase;
                          ok = true;
-                         return cache + em.row(b, e, n_entries) * C;
+                         return cache + (PAGED ? srow[j - nwin - s0] : b * n_entries + e) * C;
                        });
   };
   const bool early0 = cbeg + kT <= nwin;  // tile 0 is window rows only
   if (early0) issue_tile(0, 0);
+  // entry slot j (index slot j of idx, or entry j) of this chunk -> pool row
+  auto stage_row = [&](int64_t j, int64_t e) {
+    if (PAGED) srow[j - s0] = e >= 0 && e < n_entries ? em.row(b, e, n_entries) : 0;
+  };
   if (SPARSE) {
     int64_t j = s0 + tid;
     if (nwin == n_win) {  // the guess held: js == j
-      if (j < cend - nwin) sidx[j - s0] = pre;
+      if (j < cend - nwin) {
+        sidx[j - s0] = pre;
+        stage_row(j, pre);
+      }
       j += 256;
     }
-    for (; j < cend - nwin; j += 256) sidx[j - s0] = idx[b * k + j];
+    for (; j < cend - nwin; j += 256) {
+      const int32_t e = idx[b * k + j];
+      sidx[j - s0] = e;
+      stage_row(j, e);
+    }
+  } else if (PAGED) {
+    for (int64_t j = s0 + tid; j < cend - nwin; j += 256) stage_row(j, j);
   }
   for (int p = tid; p < r / 2; p += 256) {
     float cs, sn;
@@ -741,21 +759,25 @@ hipError_t launch_mqa_decode_bf16(const csa_attn_desc& d, int mode, const void* 
                                   const int64_t* pos, const float* sink, void* out, float* ws_o,
                                   float2* ws_ml, int nsplit, hipStream_t st, EntryMap em) {
   const int spl = mqa_decode_bf16_split(mode);
+  if (spl > kDecSplitMax) return hipErrorInvalidValue;  // the LDS row table's size
   const dim3 grid((unsigned)nsplit, (unsigned)d.batch);
   const bool wide = nsplit > 8;  // more chunks than one wave's loads in flight
   const dim3 cgrid((unsigned)d.batch, (unsigned)(wide ? d.n_heads : (d.n_heads + 3) / 4));
+#define CSA_DEC_K(CC, SP, PG)                                                                  \
+  mqa_decode_bf16_kernel<CC, SP, PG><<<grid, 256, 0, st>>>(                                    \
+      (const uint16_t*)q, (const uint16_t*)ring, (const uint16_t*)cache, idx, sink, d.n_heads,   \
+      d.k, d.m, d.n_win, d.scale, d.qk_norm, d.eps, d.rope_dims, d.rope_theta, d.n_entries, pos, \
+      ws_o, ws_ml, nsplit, spl, em);
 #define CSA_DEC(CC)                                                                            \
   if (d.c == CC) {                                                                            \
-    if (mode == ATTN_SPARSE)                                                                  \
-      mqa_decode_bf16_kernel<CC, true><<<grid, 256, 0, st>>>(                                 \
-          (const uint16_t*)q, (const uint16_t*)ring, (const uint16_t*)cache, idx, sink,          \
-          d.n_heads, d.k, d.m, d.n_win, d.scale, d.qk_norm, d.eps, d.rope_dims, d.rope_theta,    \
-          d.n_entries, pos, ws_o, ws_ml, nsplit, spl, em);                                     \
+    if (mode == ATTN_SPARSE && em.table)                                                      \
+      CSA_DEC_K(CC, true, true)                                                               \
+    else if (mode == ATTN_SPARSE)                                                             \
+      CSA_DEC_K(CC, true, false)                                                              \
+    else if (em.table)                                                                        \
+      CSA_DEC_K(CC, false, true)                                                              \
     else                                                                                      \
-      mqa_decode_bf16_kernel<CC, false><<<grid, 256, 0, st>>>(                                \
-          (const uint16_t*)q, (const uint16_t*)ring, (const uint16_t*)cache, idx, sink,          \
-          d.n_heads, d.k, d.m, d.n_win, d.scale, d.qk_norm, d.eps, d.rope_dims, d.rope_theta,    \
-          d.n_entries, pos, ws_o, ws_ml, nsplit, spl, em);                                     \
+      CSA_DEC_K(CC, false, false)                                                             \
     hipError_t e = hipGetLastError();                                                         \
     if (e != hipSuccess) return e;                                                            \
     if (wide)                                                                                 \
@@ -770,6 +792,7 @@ hipError_t launch_mqa_decode_bf16(const csa_attn_desc& d, int mode, const void* 
   }
   CSA_DEC(128) CSA_DEC(256) CSA_DEC(512)
 #undef CSA_DEC
+#undef CSA_DEC_K
   return hipErrorInvalidValue;
 }
 

@@ -122,8 +122,8 @@ int hip_status(hipError_t e) { return e == hipSuccess ? CSA_OK : CSA_ERR_HIP; }
 // pages that `capacity` entries per sequence need.
 int entry_map(const int32_t* table, int32_t page, int64_t capacity, EntryMap* em) {
   if (!table || page <= 0 || capacity < 0) return CSA_ERR_INVALID_ARG;
+  if (capacity > INT32_MAX) return CSA_ERR_UNSUPPORTED;  // entry numbers stay 32-bit
   const int64_t np = (capacity + page - 1) / page;
-  if (np > INT32_MAX) return CSA_ERR_UNSUPPORTED;
   em->table = table;
   em->page = page;
   em->max_pages = (int32_t)np;

@@ -153,7 +153,6 @@ CSA_DEV float swap32_pair_add(float a, float b) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Order-preserving map fp32 -> uint32 (larger float -> larger key).
 // Where entry e of sequence b sits in a decode cache: row b * n_entries + e
 // of a contiguous [B, n_entries] cache when table is null, else row
 // table[b * max_pages + e / page] * page + e % page of a page pool.
@@ -163,10 +162,12 @@ struct EntryMap {
   int32_t max_pages = 0;
   CSA_DEV int64_t row(int64_t b, int64_t e, int64_t n_entries) const {
     if (!table) return b * n_entries + e;
-    return (int64_t)table[b * max_pages + e / page] * page + e % page;
+    const uint32_t u = (uint32_t)e;  // entries per sequence are < 2^31 when paged
+    return (int64_t)table[b * max_pages + u / (uint32_t)page] * page + u % (uint32_t)page;
   }
 };
 
+// Order-preserving map fp32 -> uint32 (larger float -> larger key).
 CSA_DEV uint32_t float_key(float f) {
   uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);

@@ -564,7 +564,11 @@ size_t index_decode_ws_bytes(const csa_index_desc& d) {
          align_up(B * nc * 8) + 2 * align_up(B * ne * 8);
 }
 
-template <class T, int HI, int CI>
+// PAGED: KI is a page pool.  The page-table slots of the chunk's entries are
+// read first, before the position (they lie in the table whether or not the
+// entries are visible; only the visible ones' values are used), and turned
+// into pool rows in LDS, so no key load waits on a table read.
+template <class T, int HI, int CI, bool PAGED>
 __global__ __launch_bounds__(256) void dec_score_kernel(
     const typename T::S* __restrict__ qI, const typename T::S* __restrict__ wI,
     const typename T::S* __restrict__ KI, const int64_t* __restrict__ posv, int64_t n_entries,
@@ -574,14 +578,32 @@ __global__ __launch_bounds__(256) void dec_score_kernel(
   constexpr int KGE = 4 * E;      // elements per 16x16 k-group
   constexpr int NG = CI / KGE;
   __shared__ int lh[kCoarseBins];
+  __shared__ int64_t srow[PAGED ? kDecChunk : 1];
   const int b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lg = lane >> 4;
+  const int64_t c0 = (int64_t)blockIdx.x * kDecChunk;
+  constexpr int NS = kDecChunk / 256;  // entries per thread in the row table
+  int32_t tslot[PAGED ? NS : 1];
+  if (PAGED) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int64_t s = c0 + tid + 256 * i;
+      tslot[i] = s < n_entries ? em.table[(int64_t)b * em.max_pages + (uint32_t)s / (uint32_t)em.page]
+                               : 0;
+    }
+  }
   const int64_t vis = min64((posv[b] + 1) / m, n_entries);
   if (vis <= k) return;  // everything visible is selected
-  const int64_t c0 = (int64_t)blockIdx.x * kDecChunk;
   if (c0 >= vis) return;
   const int64_t c1 = min64(c0 + kDecChunk, vis);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lg = lane >> 4;
   for (int i = tid; i < kCoarseBins; i += 256) lh[i] = 0;
+  if (PAGED) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int64_t s = c0 + tid + 256 * i;
+      if (s < c1) srow[s - c0] = (int64_t)tslot[i] * em.page + (uint32_t)s % (uint32_t)em.page;
+    }
+  }
 
   // A = indexer queries: row = head (lane % 16), padded with zero rows
   uint4 qa[NG];
@@ -605,7 +627,7 @@ __global__ __launch_bounds__(256) void dec_score_kernel(
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int64_t s = min64(s0 + u * 16 + (lane & 15), c1 - 1);  // past c1: not stored
-      const S* krow = KI + em.row(b, s, n_entries) * CI;
+      const S* krow = KI + (PAGED ? srow[s - c0] : (int64_t)b * n_entries + s) * CI;
 #pragma unroll
       for (int g = 0; g < NG; ++g) dst[u][g] = *(const uint4*)(krow + g * KGE + lg * E);
     }
@@ -1278,16 +1300,20 @@ hipError_t launch_index_topk_decode(const csa_index_desc& d, const void* qI, con
   const int64_t nch = dec_chunks(d);
   const int ncopies = dec_hist_copies(nch);
   const dim3 grid((unsigned)nch, (unsigned)B);
+#define CSA_DSCORE(TT, PG)                                                                    \
+  dec_score_kernel<TT, HI, CI, PG><<<grid, 256, 0, st>>>(                                     \
+      (const TT::S*)qI, (const TT::S*)wI, (const TT::S*)KI, pos, d.n_entries, d.m, d.k,        \
+      w.scores, w.hist, ncopies, em)
   CSA_INDEX_DISPATCH(d.n_heads, d.head_dim, {
-    if (d.dtype == CSA_BF16)
-      dec_score_kernel<BF16, HI, CI><<<grid, 256, 0, st>>>(
-          (const BF16::S*)qI, (const BF16::S*)wI, (const BF16::S*)KI, pos, d.n_entries, d.m, d.k,
-          w.scores, w.hist, ncopies, em);
-    else
-      dec_score_kernel<F32, HI, CI><<<grid, 256, 0, st>>>(
-          (const float*)qI, (const float*)wI, (const float*)KI, pos, d.n_entries, d.m, d.k,
-          w.scores, w.hist, ncopies, em);
+    if (d.dtype == CSA_BF16) {
+      if (em.table) CSA_DSCORE(BF16, true);
+      else CSA_DSCORE(BF16, false);
+    } else {
+      if (em.table) CSA_DSCORE(F32, true);
+      else CSA_DSCORE(F32, false);
+    }
   });
+#undef CSA_DSCORE
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return dec_select(d, w, nch, ncopies, pos, idx_out, st);
