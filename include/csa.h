@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 5
+#define CSA_ABI_VERSION 6
 
 typedef enum csa_status {
   CSA_OK = 0,
@@ -86,6 +86,9 @@ typedef struct csa_compress_desc {
   float rope_theta;    /* RoPE base                                          */
   int32_t n_win;       /* window ring length (slots)                         */
   int64_t max_entries; /* decode: rows per sequence in the entry cache      */
+  int64_t pos0;        /* prefill: position of the first new token, a
+                          multiple of m (0 = from the start; > 0 = one chunk
+                          of a chunked prefill, see csa_compress_prefill)   */
 } csa_compress_desc;
 
 /* Lightning indexer + top-k ([R] eq 16-17). */
@@ -102,6 +105,8 @@ typedef struct csa_index_desc {
                           scores rounded to bf16 ([R] section 4.4: bf16
                           index scores for a faster selector); decode:
                           CSA_F32                                           */
+  int64_t t0;          /* prefill: position of query row 0 (chunked prefill;
+                          0 = from the start)                               */
 } csa_index_desc;
 
 /* Shared-KV multi-query core attention with window and sink ([R] eq 18-19,
@@ -121,6 +126,9 @@ typedef struct csa_attn_desc {
   int32_t rope_dims;   /* r: query RoPE at t, inverse RoPE of the output    */
   float rope_theta;
   int64_t n_entries;   /* prefill: rows of comp; decode: cache rows per seq */
+  int64_t t0;          /* prefill: position of query row 0 (chunked prefill;
+                          0 = from the start); win_kv row 0 is then position
+                          max(0, t0 - n_win + 1)                            */
 } csa_attn_desc;
 
 /* ------------------------------------------------------------------------
@@ -141,7 +149,17 @@ typedef struct csa_attn_desc {
  *   state (optional): the decode state after token n-1 (see
  *     csa_compress_decode), so decoding can continue at position n.
  *
- *   H        [n, d]            dtype
+ * Chunked prefill ([R] section 4.6, prefix reuse: entries are kept up to the
+ * last complete block and only the rest is recomputed): with pos0 > 0 the n
+ * new tokens sit at positions pos0 .. pos0+n-1 (pos0 % m == 0, else
+ * CSA_ERR_UNSUPPORTED).  Entries, window rows, ring slots and the state are
+ * those of a prefill from position 0 restricted to the new tokens: out_comp
+ * row i is entry pos0/m + i, out_win row t is position pos0 + t, and the
+ * state continues at pos0 + n.  Under overlap, entry pos0/m pools block
+ * pos0/m - 1's b-series as well, so H then has n + m rows: the m tokens at
+ * positions pos0-m .. pos0-1 (the halo) first, then the new ones.
+ *
+ *   H        [n, d]            dtype  ([n + m, d] under overlap with pos0 > 0)
  *   W_kv     [(1+ov)c, d]      dtype
  *   W_z      [(1+ov)c, d]      dtype
  *   ape      [m, (1+ov)c]      fp32   learned position bias B (B_b | B_a)
@@ -205,6 +223,9 @@ int csa_state_init(const csa_compress_desc* desc, float* state, void* stream);
  *   KI      [n_entries, cI] dtype   (n_entries >= floor(n/m) is not required;
  *                                    entries beyond n_entries are invisible)
  *   idx_out [n, k]       int32
+ * With t0 > 0 (a chunk of a chunked prefill) row t is the token at position
+ * t0 + t and sees s < floor((t0+t+1)/m).  Rows hold at most 16384 visible
+ * entries (CSA_ERR_UNSUPPORTED beyond).
  */
 int csa_index_topk_prefill(const csa_index_desc* desc, const void* qI, const void* wI,
                            const void* KI, int32_t* idx_out, void* ws, size_t ws_bytes,
@@ -298,6 +319,10 @@ int csa_index_topk_decode_fp4(const csa_index_desc* desc, const uint8_t* qI_code
  *   idx    [n, k]       int32  (entries must be < n_entries or -1)
  *   sink   [nh]         fp32
  *   out    [n, nh, c]   dtype
+ * With t0 > 0 (a chunk of a chunked prefill) row t is the token at position
+ * t0 + t: RoPE, the window and the visible entries follow that position, and
+ * win_kv holds the window rows of positions max(0, t0-n_win+1) .. t0+n-1
+ * (the previous chunk's last n_win-1 rows, then the chunk's own).
  */
 int csa_sparse_mqa_prefill(const csa_attn_desc* desc, const void* q, const void* win_kv,
                            const void* comp, const int32_t* idx, const float* sink, void* out,

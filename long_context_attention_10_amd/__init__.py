@@ -38,14 +38,15 @@ class CompressDesc(ctypes.Structure):
                 ("c", ctypes.c_int32), ("m", ctypes.c_int32), ("overlap", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("qk_norm", ctypes.c_int32), ("eps", ctypes.c_float),
                 ("rope_dims", ctypes.c_int32), ("rope_theta", ctypes.c_float),
-                ("n_win", ctypes.c_int32), ("max_entries", ctypes.c_int64)]
+                ("n_win", ctypes.c_int32), ("max_entries", ctypes.c_int64),
+                ("pos0", ctypes.c_int64)]
 
 
 class IndexDesc(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int64), ("batch", ctypes.c_int32), ("n_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("m", ctypes.c_int32), ("k", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("n_entries", ctypes.c_int64),
-                ("score_dtype", ctypes.c_int32)]
+                ("score_dtype", ctypes.c_int32), ("t0", ctypes.c_int64)]
 
 
 class Fp4Desc(ctypes.Structure):
@@ -70,7 +71,7 @@ class AttnDesc(ctypes.Structure):
                 ("n_win", ctypes.c_int32), ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("qk_norm", ctypes.c_int32), ("eps", ctypes.c_float),
                 ("rope_dims", ctypes.c_int32), ("rope_theta", ctypes.c_float),
-                ("n_entries", ctypes.c_int64)]
+                ("n_entries", ctypes.c_int64), ("t0", ctypes.c_int64)]
 
 
 _lib = None
@@ -199,9 +200,9 @@ def workspace_zero_bytes(entry: str, desc) -> int:
 
 # -------------------------------------------------------------- compressor
 def compress_desc(n=0, batch=1, d=0, c=0, m=1, overlap=0, dtype=CSA_F32, qk_norm=True, eps=1e-6,
-                  rope_dims=0, rope_theta=10000.0, n_win=128, max_entries=0):
+                  rope_dims=0, rope_theta=10000.0, n_win=128, max_entries=0, pos0=0):
     return CompressDesc(n, batch, d, c, m, int(overlap), dtype, int(qk_norm), eps, rope_dims,
-                        rope_theta, n_win, max_entries)
+                        rope_theta, n_win, max_entries, pos0)
 
 
 def csa_state_bytes(desc) -> int:
@@ -215,13 +216,17 @@ def csa_state_init(desc, state: torch.Tensor):
 def csa_compress_prefill(H, W_kv, W_z, ape, m, overlap, W_win=None, qk_norm=True, eps=1e-6,
                          rope_dims=0, rope_theta=10000.0, n_win=128, want_win=True,
                          want_ring=False, want_state=False, out_comp=None, out_win=None,
-                         win_ring=None, state=None, ws_slot="default"):
+                         win_ring=None, state=None, ws_slot="default", pos0=0):
     """Compressed entries (and window rows / ring / decode state) of one
     sequence H [n, d].  Weights are output-major [(1+ov)c, d].  Calls that
     may run at the same time on different streams need distinct `ws_slot`
-    names (each names its own cached workspace)."""
+    names (each names its own cached workspace).  pos0 > 0 (a multiple of
+    m): a chunk of new tokens at positions pos0.., whose H under overlap
+    starts with the m tokens before pos0 (the halo)."""
     lib = load()
     n, d = H.shape
+    if overlap and pos0 > 0:
+        n -= m  # the halo rows are not new tokens
     w = W_kv.shape[0]
     c = w // (2 if overlap else 1)
     dt = _dt(H)
@@ -229,7 +234,7 @@ def csa_compress_prefill(H, W_kv, W_z, ape, m, overlap, W_win=None, qk_norm=True
     _expect(W_z, (w, d), H.dtype, "W_z")
     _expect(ape, (m, w), torch.float32, "ape")
     desc = compress_desc(n=n, d=d, c=c, m=m, overlap=overlap, dtype=dt, qk_norm=qk_norm, eps=eps,
-                         rope_dims=rope_dims, rope_theta=rope_theta, n_win=n_win)
+                         rope_dims=rope_dims, rope_theta=rope_theta, n_win=n_win, pos0=pos0)
     dev = H.device
     if out_comp is None:
         out_comp = torch.empty((n // m, c), dtype=H.dtype, device=dev)
@@ -390,16 +395,17 @@ def hca_dense_mqa_decode_paged(q, win_ring, comp_pool, page_table, page_entries,
 
 
 # ----------------------------------------------------------------- indexer
-def csa_index_topk_prefill(qI, wI, KI, m, k, out=None, scores="f32"):
+def csa_index_topk_prefill(qI, wI, KI, m, k, out=None, scores="f32", t0=0):
     """idx [n, k] int32: per token, the top-k visible entries (ascending), -1
-    padded.  scores="bf16" selects on index scores rounded to bf16."""
+    padded.  scores="bf16" selects on index scores rounded to bf16.  t0:
+    position of row 0 (a chunk of a chunked prefill)."""
     lib = load()
     n, hI, cI = qI.shape
     _expect(wI, (n, hI), qI.dtype, "wI")
     ne = KI.shape[0]
     _expect(KI, (ne, cI), qI.dtype, "KI")
     sdt = {"f32": CSA_F32, "bf16": CSA_BF16}[scores]
-    desc = IndexDesc(n, 1, hI, cI, m, k, _dt(qI), ne, sdt)
+    desc = IndexDesc(n, 1, hI, cI, m, k, _dt(qI), ne, sdt, t0)
     if out is None:
         out = torch.empty((n, k), dtype=torch.int32, device=qI.device)
     ws, wsb = workspace(workspace_bytes("index_topk_prefill", desc), qI.device, "index")
@@ -431,23 +437,32 @@ def csa_index_topk_decode(qI, wI, KI_cache, pos, m, k, out=None):
 
 # --------------------------------------------------------------- attention
 def attn_desc(n=0, batch=1, nh=1, c=0, k=0, m=1, n_win=128, dtype=CSA_F32, scale=None,
-              qk_norm=True, eps=1e-6, rope_dims=0, rope_theta=10000.0, n_entries=0):
+              qk_norm=True, eps=1e-6, rope_dims=0, rope_theta=10000.0, n_entries=0, t0=0):
     if scale is None:
         scale = c ** -0.5
     return AttnDesc(n, batch, nh, c, k, m, n_win, dtype, scale, int(qk_norm), eps, rope_dims,
-                    rope_theta, n_entries)
+                    rope_theta, n_entries, t0)
+
+
+def _win_rows(n, n_win, t0):
+    """Window rows a prefill chunk at t0 takes: positions max(0, t0-n_win+1)
+    .. t0+n-1."""
+    return t0 + n - max(0, t0 - n_win + 1)
 
 
 def csa_sparse_mqa_prefill(q, win_kv, comp, idx, sink, n_win=128, scale=None, qk_norm=True,
-                           eps=1e-6, rope_dims=0, rope_theta=10000.0, out=None):
+                           eps=1e-6, rope_dims=0, rope_theta=10000.0, out=None, t0=0):
+    """t0: position of row 0 (a chunk of a chunked prefill); win_kv then holds
+    the window rows of positions max(0, t0-n_win+1) .. t0+n-1."""
     lib = load()
     n, nh, c = q.shape
     k = idx.shape[1]
-    _expect(win_kv, (n, c), q.dtype, "win_kv")
+    _expect(win_kv, (_win_rows(n, n_win, t0), c), q.dtype, "win_kv")
     _expect(idx, (n, k), torch.int32, "idx")
     _expect(sink, (nh,), torch.float32, "sink")
     desc = attn_desc(n=n, nh=nh, c=c, k=k, n_win=n_win, dtype=_dt(q), scale=scale, qk_norm=qk_norm,
-                     eps=eps, rope_dims=rope_dims, rope_theta=rope_theta, n_entries=comp.shape[0])
+                     eps=eps, rope_dims=rope_dims, rope_theta=rope_theta, n_entries=comp.shape[0],
+                     t0=t0)
     if out is None:
         out = torch.empty_like(q)
     st = lib.csa_sparse_mqa_prefill(ctypes.byref(desc), _ptr(q), _ptr(win_kv),
@@ -458,13 +473,14 @@ def csa_sparse_mqa_prefill(q, win_kv, comp, idx, sink, n_win=128, scale=None, qk
 
 
 def hca_dense_mqa_prefill(q, win_kv, comp, sink, m, n_win=128, scale=None, qk_norm=True, eps=1e-6,
-                          rope_dims=0, rope_theta=10000.0, out=None):
+                          rope_dims=0, rope_theta=10000.0, out=None, t0=0):
     lib = load()
     n, nh, c = q.shape
-    _expect(win_kv, (n, c), q.dtype, "win_kv")
+    _expect(win_kv, (_win_rows(n, n_win, t0), c), q.dtype, "win_kv")
     _expect(sink, (nh,), torch.float32, "sink")
     desc = attn_desc(n=n, nh=nh, c=c, m=m, n_win=n_win, dtype=_dt(q), scale=scale, qk_norm=qk_norm,
-                     eps=eps, rope_dims=rope_dims, rope_theta=rope_theta, n_entries=comp.shape[0])
+                     eps=eps, rope_dims=rope_dims, rope_theta=rope_theta, n_entries=comp.shape[0],
+                     t0=t0)
     if out is None:
         out = torch.empty_like(q)
     st = lib.hca_dense_mqa_prefill(ctypes.byref(desc), _ptr(q), _ptr(win_kv),

@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void mqa_kernel(
     const int64_t* __restrict__ posv, const float* __restrict__ sink, typename T::S* __restrict__ out,
     float* __restrict__ ws_o, float* __restrict__ ws_ml, int64_t n, int nh, int k, int m,
     int n_win, float scale, int qk_norm, float eps, int r, float theta, int64_t n_entries,
-    int nsplit) {
+    int nsplit, int64_t t0) {
   typedef typename T::S S;
   typedef MqaSmem<T, C, MB> Sm;
   constexpr int E = 16 / (int)sizeof(S);
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) void mqa_kernel(
   int h0 = 0, split = 0;
   if (!DECODE) {
     t = blockIdx.x;
-    pos = t;
+    pos = t0 + t;  // win row 0 is position max(t0 - n_win + 1, 0)
   } else {
     b = blockIdx.y;
     h0 = blockIdx.z * 16;
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(256) void mqa_kernel(
     if (j < cend) {
       if (j < nwin) {
         const int64_t p = pos - nwin + 1 + j;
-        src = DECODE ? wbase + (p % n_win) * C : wbase + p * C;
+        src = DECODE ? wbase + (p % n_win) * C : wbase + (p - max64(t0 - n_win + 1, 0)) * C;
       } else {
         const int64_t jj = j - nwin;
         int64_t e;
@@ -425,7 +425,7 @@ static hipError_t dispatch_prefill(const csa_attn_desc& d, const void* q, const 
     mqa_kernel<T, CC, MBB, MODE><<<(unsigned)d.n, 256, 0, st>>>(                               \
         (const S*)q, (const S*)win, (const S*)comp, idx, nullptr, sink, (S*)out, nullptr,       \
         nullptr, d.n, d.n_heads, d.k, d.m, d.n_win, d.scale, d.qk_norm, d.eps, d.rope_dims,     \
-        d.rope_theta, d.n_entries, 1);                                                          \
+        d.rope_theta, d.n_entries, 1, d.t0);                                                    \
     return hipGetLastError();                                                                   \
   }
   CSA_MQA_P(128, 1) CSA_MQA_P(128, 2) CSA_MQA_P(128, 4)
@@ -478,7 +478,7 @@ static hipError_t dispatch_decode(const csa_attn_desc& d, const void* q, const v
     mqa_kernel<T, CC, 1, MODE><<<grid, 256, 0, st>>>(                                          \
         (const S*)q, (const S*)ring, (const S*)cache, idx, pos, sink, nullptr, ws_o, ws_ml, 0,  \
         d.n_heads, d.k, d.m, d.n_win, d.scale, d.qk_norm, d.eps, d.rope_dims, d.rope_theta,     \
-        d.n_entries, S_);                                                                       \
+        d.n_entries, S_, (int64_t)0);                                                           \
   } else
   CSA_MQA_D(128) CSA_MQA_D(256) CSA_MQA_D(512) { return hipErrorInvalidValue; }
 #undef CSA_MQA_D

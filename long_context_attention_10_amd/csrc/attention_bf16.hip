@@ -352,7 +352,8 @@ __global__ __launch_bounds__(256, 2) void mqa_prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ win,
     const uint16_t* __restrict__ comp, const int32_t* __restrict__ idx,
     const float* __restrict__ sink, uint16_t* __restrict__ out, int64_t n, int nh, int k, int m,
-    int n_win, float scale, int qk_norm, float eps, int r, float theta, int64_t n_entries) {
+    int n_win, float scale, int qk_norm, float eps, int r, float theta, int64_t n_entries,
+    int64_t t0) {
   typedef Geo<C> G;
   typedef OSplit<C> A;
   constexpr int NKG = C / 32;
@@ -377,15 +378,17 @@ __global__ __launch_bounds__(256, 2) void mqa_prefill_bf16_kernel(
 #pragma unroll
     for (int g = 0; g < NKG; ++g) qraw[g] = *(const uint4*)(qh + g * 32);
   }
-  const int nwin = (int)min64(n_win, t + 1);
-  const int64_t ncand = nwin + (SPARSE ? (int64_t)k : min64((t + 1) / m, n_entries));
+  // row t is the token at position pt = t0 + t; win row 0 is position w0
+  const int64_t pt = t0 + t, w0 = max64(t0 - n_win + 1, 0);
+  const int nwin = (int)min64(n_win, pt + 1);
+  const int64_t ncand = nwin + (SPARSE ? (int64_t)k : min64((pt + 1) / m, n_entries));
   const int ntiles = (int)((ncand + kT - 1) / kT);
   auto issue_tile = [&](int ti, int buf) {
     issue_tile_rows<C>(smem + buf * G::TILE, valid[buf], lane, wave, (int64_t)ti * kT,
                        [&](int64_t j, bool& ok) -> const uint16_t* {
                          ok = false;
                          if (j >= ncand) return win;  // a valid row for masked candidates
-                         if (j < nwin) { ok = true; return win + (t - nwin + 1 + j) * C; }
+                         if (j < nwin) { ok = true; return win + (pt - nwin + 1 + j - w0) * C; }
                          const int64_t e = SPARSE ? (int64_t)sidx[j - nwin] : j - nwin;
                          if (e < 0 || e >= n_entries) return win;
                          ok = true;
@@ -398,7 +401,7 @@ __global__ __launch_bounds__(256, 2) void mqa_prefill_bf16_kernel(
     for (int j = tid; j < k; j += 256) sidx[j] = idx[t * k + j];
   for (int p = tid; p < r / 2; p += 256) {
     float cs, sn;
-    rope_cs(t, p, r, theta, &cs, &sn);
+    rope_cs(pt, p, r, theta, &cs, &sn);
     rope_tab[p] = make_float2(cs, sn);
   }
   __syncthreads();  // sidx and rope_tab are visible
@@ -474,12 +477,12 @@ hipError_t launch_mqa_prefill_bf16(const csa_attn_desc& d, int mode, const void*
       mqa_prefill_bf16_kernel<CC, true><<<grid, 256, 0, st>>>(                              \
           (const uint16_t*)q, (const uint16_t*)win, (const uint16_t*)comp, idx, sink,         \
           (uint16_t*)out, d.n, d.n_heads, d.k, d.m, d.n_win, d.scale, d.qk_norm, d.eps,       \
-          d.rope_dims, d.rope_theta, d.n_entries);                                            \
+          d.rope_dims, d.rope_theta, d.n_entries, d.t0);                                      \
     else                                                                                     \
       mqa_prefill_bf16_kernel<CC, false><<<grid, 256, 0, st>>>(                             \
           (const uint16_t*)q, (const uint16_t*)win, (const uint16_t*)comp, idx, sink,         \
           (uint16_t*)out, d.n, d.n_heads, d.k, d.m, d.n_win, d.scale, d.qk_norm, d.eps,       \
-          d.rope_dims, d.rope_theta, d.n_entries);                                            \
+          d.rope_dims, d.rope_theta, d.n_entries, d.t0);                                      \
     return hipGetLastError();                                                                \
   }
   CSA_FAST(128) CSA_FAST(256) CSA_FAST(512)

@@ -31,14 +31,19 @@ int check_compress(const csa_compress_desc* d, bool decode) {
   if (decode) {
     if (d->batch <= 0 || d->max_entries < 0) return CSA_ERR_INVALID_ARG;
   } else {
-    if (d->n < 0) return CSA_ERR_INVALID_ARG;
+    if (d->n < 0 || d->pos0 < 0) return CSA_ERR_INVALID_ARG;
+    if (d->pos0 % d->m) return CSA_ERR_UNSUPPORTED;  // chunks start at a block boundary
   }
   return CSA_OK;
 }
 
+// Rows of H a prefill projects: under overlap a chunk (pos0 > 0) also
+// projects the previous block (the halo) for its b-series.
+int64_t prefill_halo(const csa_compress_desc* d) { return d->overlap && d->pos0 > 0 ? d->m : 0; }
+
 size_t ws_compress_prefill(const csa_compress_desc* d, bool has_win) {
   const int w = (1 + d->overlap) * d->c;
-  return al((size_t)d->n * (size_t)(2 * w + (has_win ? d->c : 0)) * 4);
+  return al((size_t)(d->n + prefill_halo(d)) * (size_t)(2 * w + (has_win ? d->c : 0)) * 4);
 }
 
 size_t ws_compress_decode(const csa_compress_desc* d, bool has_win) {
@@ -62,8 +67,9 @@ int check_index(const csa_index_desc* d, bool decode) {
     if (d->batch <= 0) return CSA_ERR_INVALID_ARG;
     if (d->n_entries >= (int64_t)1 << 31) return CSA_ERR_UNSUPPORTED;
   } else {
-    if (d->n < 0) return CSA_ERR_INVALID_ARG;
-    const int64_t vis = d->n / d->m < d->n_entries ? d->n / d->m : d->n_entries;
+    if (d->n < 0 || d->t0 < 0) return CSA_ERR_INVALID_ARG;
+    const int64_t last = (d->t0 + d->n) / d->m;  // visible entries of the last row
+    const int64_t vis = last < d->n_entries ? last : d->n_entries;
     if (vis > 256 * 64) return CSA_ERR_UNSUPPORTED;  // row held in registers
   }
   return CSA_OK;
@@ -71,7 +77,8 @@ int check_index(const csa_index_desc* d, bool decode) {
 
 // Row stride of the prefill score workspace (a multiple of 4 floats).
 int64_t index_prefill_ld(const csa_index_desc* d) {
-  const int64_t vis = d->n / d->m < d->n_entries ? d->n / d->m : d->n_entries;
+  const int64_t last = (d->t0 + d->n) / d->m;
+  const int64_t vis = last < d->n_entries ? last : d->n_entries;
   return (vis + 3) & ~(int64_t)3;
 }
 
@@ -86,7 +93,7 @@ int check_attn(const csa_attn_desc* d, bool decode, bool sparse) {
   if (!sparse && d->m <= 0) return CSA_ERR_INVALID_ARG;
   if (d->rope_dims < 0 || d->rope_dims > d->c || (d->rope_dims % 8)) return CSA_ERR_UNSUPPORTED;
   if (d->rope_dims > 0 && !(d->rope_theta > 0.f)) return CSA_ERR_INVALID_ARG;
-  if (decode ? d->batch <= 0 : d->n < 0) return CSA_ERR_INVALID_ARG;
+  if (decode ? d->batch <= 0 : d->n < 0 || d->t0 < 0) return CSA_ERR_INVALID_ARG;
   return CSA_OK;
 }
 
@@ -218,7 +225,7 @@ size_t csa_workspace_bytes(int entry, const void* desc) {
   switch (entry) {
     case CSA_ENTRY_COMPRESS_PREFILL: {
       const csa_compress_desc* d = (const csa_compress_desc*)desc;
-      if (d->n <= 0 || d->c <= 0) return 0;
+      if (d->n + prefill_halo(d) <= 0 || d->c <= 0) return 0;
       return ws_compress_prefill(d, true);
     }
     case CSA_ENTRY_COMPRESS_DECODE: {
@@ -275,29 +282,33 @@ int csa_compress_prefill(const csa_compress_desc* d, const void* H, const void* 
   if ((out_win || win_ring) && !has_win) return CSA_ERR_INVALID_ARG;
   if (win_ring && d->n_win <= 0) return CSA_ERR_INVALID_ARG;
   const int64_t nc = d->n / d->m;
-  if (d->n > 0 && (!H || !W_kv || !W_z || !ape)) return CSA_ERR_INVALID_ARG;
+  const int64_t halo = prefill_halo(d), rows = d->n + halo;
+  if (rows > 0 && (!H || !W_kv || !W_z || !ape)) return CSA_ERR_INVALID_ARG;
   if (nc > 0 && !out_comp) return CSA_ERR_INVALID_ARG;
-  const size_t need = d->n > 0 ? ws_compress_prefill(d, has_win) : 0;
+  const size_t need = rows > 0 ? ws_compress_prefill(d, has_win) : 0;
   if (need > 0 && (!ws || ws_bytes < need)) return CSA_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   const int w = (1 + d->overlap) * d->c;
   const int64_t ld = 2 * w + (has_win ? d->c : 0);
   float* P = (float*)ws;
-  if (d->n > 0) {
+  float* Pn = P + halo * ld;  // the new tokens' rows
+  if (rows > 0) {
     WeightStack stack = {{W_kv, W_z, W_win}, {w, w, has_win ? d->c : 0}};
-    hipError_t e = launch_proj_gemm(d->dtype, H, d->n, d->d, stack, P, ld, st);
+    hipError_t e = launch_proj_gemm(d->dtype, H, rows, d->d, stack, P, ld, st);
     if (e != hipSuccess) return CSA_ERR_HIP;
-    e = launch_pool_entries(d->dtype, P, ld, d->n, d->c, d->m, d->overlap, ape, d->qk_norm, d->eps,
-                            d->rope_dims, d->rope_theta, out_comp, 0, st);
+    e = launch_pool_entries(d->dtype, Pn, ld, d->n, d->c, d->m, d->overlap, ape, d->qk_norm,
+                            d->eps, d->rope_dims, d->rope_theta, out_comp, d->pos0, st,
+                            halo > 0);
     if (e != hipSuccess) return CSA_ERR_HIP;
     if (has_win && (out_win || win_ring)) {
-      e = launch_window_rows(d->dtype, P, ld, 2 * w, d->n, d->c, d->qk_norm, d->eps, d->rope_dims,
-                             d->rope_theta, out_win, win_ring, d->n_win, 0, st);
+      e = launch_window_rows(d->dtype, Pn, ld, 2 * w, d->n, d->c, d->qk_norm, d->eps,
+                             d->rope_dims, d->rope_theta, out_win, win_ring, d->n_win, d->pos0,
+                             st);
       if (e != hipSuccess) return CSA_ERR_HIP;
     }
   }
-  if (state) {
-    hipError_t e = launch_stash_state(P, ld, d->n, d->c, d->m, d->overlap, ape, state, st);
+  if (state) {  // block-aligned from P's first row, so the halo is one more block
+    hipError_t e = launch_stash_state(P, ld, rows, d->c, d->m, d->overlap, ape, state, st);
     if (e != hipSuccess) return CSA_ERR_HIP;
   }
   return CSA_OK;

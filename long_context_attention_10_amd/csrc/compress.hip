@@ -349,7 +349,9 @@ template <class T, int G>
 __global__ __launch_bounds__(256) void pool_entries_kernel(
     const float* __restrict__ P, int64_t ld, int64_t n_entries, int c, int m, int ov,
     const float* __restrict__ ape, int qk_norm, float eps, int r, float theta,
-    typename T::S* __restrict__ out, int64_t pos0) {
+    typename T::S* __restrict__ out, int64_t pos0, int prev0) {
+  // prev0: the m rows before P hold block -1 (a chunk's halo), whose
+  // b-series joins entry 0 under overlap
   __shared__ float red[4];
   constexpr int GPW = 256 / G;
   const int g = threadIdx.x / G, j = threadIdx.x % G;
@@ -368,7 +370,7 @@ __global__ __launch_bounds__(256) void pool_entries_kernel(
       osm_push(mx0, s0, a0, zv.x + bv.x, cv.x);
       osm_push(mx1, s1, a1, zv.y + bv.y, cv.y);
     }
-    if (ov && i > 0) {  // block i-1's b-series joins the same softmax
+    if (ov && (i > 0 || prev0)) {  // block i-1's b-series joins the same softmax
       for (int rr = 0; rr < m; ++rr) {
         const float* row = P + ((i - 1) * m + rr) * ld;
         const float2 cv = *(const float2*)(row + 2 * j);
@@ -684,17 +686,17 @@ hipError_t launch_proj_gemm(int dtype, const void* A, int64_t M, int K, const We
 
 hipError_t launch_pool_entries(int dtype, const float* P, int64_t ld, int64_t n, int c, int m,
                                int ov, const float* ape, int qk_norm, float eps, int r,
-                               float theta, void* out, int64_t pos0, hipStream_t st) {
+                               float theta, void* out, int64_t pos0, hipStream_t st, int prev0) {
   const int64_t ne = n / m;
   if (ne == 0) return hipSuccess;
   CSA_DISPATCH_G(c, {
     dim3 grid((unsigned)((ne + 256 / G - 1) / (256 / G)));
     if (dtype == CSA_BF16)
       pool_entries_kernel<BF16, G><<<grid, 256, 0, st>>>(P, ld, ne, c, m, ov, ape, qk_norm, eps, r,
-                                                         theta, (BF16::S*)out, pos0);
+                                                         theta, (BF16::S*)out, pos0, prev0);
     else
       pool_entries_kernel<F32, G><<<grid, 256, 0, st>>>(P, ld, ne, c, m, ov, ape, qk_norm, eps, r,
-                                                        theta, (float*)out, pos0);
+                                                        theta, (float*)out, pos0, prev0);
   });
   return hipGetLastError();
 }

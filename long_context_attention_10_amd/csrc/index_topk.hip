@@ -28,7 +28,7 @@ template <class T, int HI, int CI, class SC>
 __global__ __launch_bounds__(256) void index_scores_prefill_kernel(
     const typename T::S* __restrict__ qI, const typename T::S* __restrict__ wI,
     const typename T::S* __restrict__ KI, int64_t n, int64_t n_entries, int m, int key_chunk,
-    SC* __restrict__ scores, int64_t ld) {
+    SC* __restrict__ scores, int64_t ld, int64_t t0) {
   typedef typename T::S S;
   constexpr int E = 16 / (int)sizeof(S);
   constexpr int KGE = 2 * E;        // elements per 32x32 k-group
@@ -49,7 +49,9 @@ __global__ __launch_bounds__(256) void index_scores_prefill_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t q0 = (int64_t)blockIdx.x * TQ;
   const int64_t tlast = min64(q0 + TQ, n) - 1;
-  const int64_t kend = min64(min64((tlast + 1) / m, n_entries), (int64_t)(blockIdx.y + 1) * key_chunk);
+  // query row t is the token at position t0 + t
+  const int64_t kend =
+      min64(min64((t0 + tlast + 1) / m, n_entries), (int64_t)(blockIdx.y + 1) * key_chunk);
   const int64_t kbeg = (int64_t)blockIdx.y * key_chunk;
   if (kbeg >= kend) return;
 
@@ -95,7 +97,7 @@ __global__ __launch_bounds__(256) void index_scores_prefill_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int64_t t = HI == 4 ? tb + 2 * j + hl : HI == 8 ? tb + 2 * hl + (j & 1) : tb + hl;
-      vis[rb][j] = t < n ? (int)((t + 1) / m) : 0;
+      vis[rb][j] = t < n ? (int)min64((t0 + t + 1) / m, n_entries) : 0;
     }
   }
   wait_vmem();
@@ -287,7 +289,7 @@ __global__ __launch_bounds__(256) void topk_rows_prefill_kernel(const SC* __rest
                                                                 int64_t ld, int64_t n,
                                                                 int64_t n_entries, int m, int k,
                                                                 int32_t* __restrict__ idx_out,
-                                                                int64_t row0) {
+                                                                int64_t row0, int64_t t0) {
   constexpr int NQ = MAXIT / 4;  // 4-entry groups per thread
   __shared__ int hist[kSelBins];
   __shared__ uint32_t bits[MAXIT * 256 / 32];
@@ -298,7 +300,7 @@ __global__ __launch_bounds__(256) void topk_rows_prefill_kernel(const SC* __rest
   __shared__ int ncand;
   const int t = (int)(row0 + blockIdx.x);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int v = (int)min64((int64_t)(t + 1) / m, n_entries);
+  const int v = (int)min64((t0 + t + 1) / m, n_entries);  // row t: position t0 + t
   const int kt = min(k, v);
   int32_t* orow = idx_out + (int64_t)t * k;
   if (v <= k) {
@@ -1212,7 +1214,7 @@ hipError_t launch_index_scores_prefill(const csa_index_desc& d, const void* qI, 
                                        const void* KI, void* scores, int64_t ld,
                                        hipStream_t st) {
   const int key_chunk = 2048;
-  const int64_t nvis = d.n / d.m < d.n_entries ? d.n / d.m : d.n_entries;
+  const int64_t nvis = (d.t0 + d.n) / d.m < d.n_entries ? (d.t0 + d.n) / d.m : d.n_entries;
   if (nvis == 0) return hipSuccess;
   CSA_INDEX_DISPATCH(d.n_heads, d.head_dim, {
     constexpr int TQ = 256 / HI;
@@ -1223,19 +1225,19 @@ hipError_t launch_index_scores_prefill(const csa_index_desc& d, const void* qI, 
     if (d.dtype == CSA_BF16 && sb)
       index_scores_prefill_kernel<BF16, HI, CI, uint16_t><<<grid, 256, 0, st>>>(
           (const BF16::S*)qI, (const BF16::S*)wI, (const BF16::S*)KI, d.n, d.n_entries, d.m,
-          key_chunk, (uint16_t*)scores, ld);
+          key_chunk, (uint16_t*)scores, ld, d.t0);
     else if (d.dtype == CSA_BF16)
       index_scores_prefill_kernel<BF16, HI, CI, float><<<grid, 256, 0, st>>>(
           (const BF16::S*)qI, (const BF16::S*)wI, (const BF16::S*)KI, d.n, d.n_entries, d.m,
-          key_chunk, (float*)scores, ld);
+          key_chunk, (float*)scores, ld, d.t0);
     else if (sb)
       index_scores_prefill_kernel<F32, HI, CI, uint16_t><<<grid, 256, 0, st>>>(
           (const float*)qI, (const float*)wI, (const float*)KI, d.n, d.n_entries, d.m, key_chunk,
-          (uint16_t*)scores, ld);
+          (uint16_t*)scores, ld, d.t0);
     else
       index_scores_prefill_kernel<F32, HI, CI, float><<<grid, 256, 0, st>>>(
           (const float*)qI, (const float*)wI, (const float*)KI, d.n, d.n_entries, d.m, key_chunk,
-          (float*)scores, ld);
+          (float*)scores, ld, d.t0);
   });
   return hipGetLastError();
 }
@@ -1248,8 +1250,8 @@ hipError_t launch_topk_rows_prefill(const csa_index_desc& d, const void* scores,
   // first row whose visible count exceeds `cap` entries
   auto band_end = [&](int64_t cap) {
     if (d.n_entries <= cap) return d.n;
-    const int64_t e = (cap + 1) * d.m - 1;
-    return e < d.n ? e : d.n;
+    const int64_t e = (cap + 1) * d.m - 1 - d.t0;  // row of position (cap + 1) m - 1
+    return e < 0 ? (int64_t)0 : e < d.n ? e : d.n;
   };
   const int64_t e16 = band_end(16 * 256), e32 = band_end(32 * 256), e48 = band_end(48 * 256);
   // Q: keys per thread offered for the lower bound, 256 * Q >= k
@@ -1262,13 +1264,13 @@ hipError_t launch_topk_rows_prefill(const csa_index_desc& d, const void* scores,
     const unsigned g = (unsigned)(r1 - r0);
     if (q == 2)
       topk_rows_prefill_kernel<MI, 2, SC><<<g, 256, 0, st>>>(sp, ld, d.n, d.n_entries, d.m, d.k,
-                                                             idx_out, r0);
+                                                             idx_out, r0, d.t0);
     else if (q == 4)
       topk_rows_prefill_kernel<MI, 4, SC><<<g, 256, 0, st>>>(sp, ld, d.n, d.n_entries, d.m, d.k,
-                                                             idx_out, r0);
+                                                             idx_out, r0, d.t0);
     else
       topk_rows_prefill_kernel<MI, 0, SC><<<g, 256, 0, st>>>(sp, ld, d.n, d.n_entries, d.m, d.k,
-                                                             idx_out, r0);
+                                                             idx_out, r0, d.t0);
   };
   auto band = [&](auto maxit, int64_t r0, int64_t r1) {
     if (d.score_dtype == CSA_BF16) band_t(maxit, uint16_t(), r0, r1);

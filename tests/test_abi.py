@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.csa_abi_version() == 5
+    assert lib.csa_abi_version() == 6
     for code in (0, -1, -2, -3, -4):
         assert len(lib.csa_status_string(code)) > 0
     assert lib.csa_status_string(-99) == b"unknown status"
@@ -263,3 +263,22 @@ def test_paged_calls_reject(lib):
                                           _p(), _p(), 1 << 40, None) == -1
     assert lib.hca_dense_mqa_decode_paged(ctypes.byref(a), _p(), _p(), _p(), _p(), 1, _p(), _p(),
                                           _p(), _p(), 8, None) == -3
+
+
+def test_chunked_prefill_rejects(lib):
+    """A chunk must start at a block boundary and at a position >= 0."""
+    d = L.compress_desc(n=64, d=128, c=128, m=4, pos0=6)
+    assert lib.csa_compress_prefill(ctypes.byref(d), *([_p()] * 10), 1 << 40, None) == -2
+    d = L.compress_desc(n=64, d=128, c=128, m=4, pos0=-4)
+    assert lib.csa_compress_prefill(ctypes.byref(d), *([_p()] * 10), 1 << 40, None) == -1
+    # under overlap a chunk projects the halo block too
+    d0 = L.compress_desc(n=64, d=128, c=128, m=4, overlap=1)
+    d1 = L.compress_desc(n=64, d=128, c=128, m=4, overlap=1, pos0=8)
+    assert L.workspace_bytes("compress_prefill", d1) > L.workspace_bytes("compress_prefill", d0)
+    di = L.IndexDesc(16, 1, 16, 64, 4, 8, L.CSA_BF16, 4, 0, -1)
+    assert lib.csa_index_topk_prefill(ctypes.byref(di), *([_p()] * 5), 1 << 30, None) == -1
+    # the last row's visible count decides the register limit
+    di = L.IndexDesc(16, 1, 16, 64, 4, 512, L.CSA_BF16, 1 << 20, 0, 4 * 16384)
+    assert lib.csa_index_topk_prefill(ctypes.byref(di), *([_p()] * 5), 1 << 40, None) == -2
+    a = L.attn_desc(n=8, nh=8, c=128, k=4, t0=-1)
+    assert lib.csa_sparse_mqa_prefill(ctypes.byref(a), *([_p()] * 6), None, 0, None) == -1
