@@ -83,6 +83,29 @@ class CsaPrefill:
         self.index()
         self.attend()
 
+    def step_chunked(self, chunk=8192):
+        """The same prefill in block-aligned chunks of `chunk` tokens: each
+        chunk compresses its tokens (with the block before it under overlap)
+        into the shared entry buffers, then selects and attends for its own
+        rows over the entries so far and the window rows before it."""
+        c, t = self.cfg, self.t
+        n, m, ov, nw, r = c["n"], c["m"], c["overlap"], c["n_win"], c["rope_dims"]
+        for p0 in range(0, n, chunk):
+            p1 = min(n, p0 + chunk)
+            h0 = p0 - m if ov and p0 > 0 else p0
+            e0, e1 = p0 // m, p1 // m
+            L.csa_compress_prefill(t["H"][h0:p1], t["W_kv"], t["W_z"], t["ape"], m, ov,
+                                   W_win=t["W_win"], rope_dims=r, out_comp=self.comp[e0:e1],
+                                   out_win=self.win[p0:p1], pos0=p0)
+            L.csa_compress_prefill(t["H"][h0:p1], t["WI_kv"], t["WI_z"], t["apeI"], m, ov,
+                                   out_comp=self.kI[e0:e1], pos0=p0)
+            L.csa_index_topk_prefill(t["qI"][p0:p1], t["wI"][p0:p1], self.kI[:e1], m, c["k"],
+                                     out=self.idx[p0:p1], t0=p0)
+            w0 = max(0, p0 - nw + 1)
+            L.csa_sparse_mqa_prefill(t["q"][p0:p1], self.win[w0:p1], self.comp[:e1],
+                                     self.idx[p0:p1], t["sink"], n_win=nw, rope_dims=r,
+                                     out=self.out[p0:p1], t0=p0)
+
     def attn_flops(self):
         """Algorithmic FLOPs of the sparse MQA: 2 matmuls x 2 FLOP per
         multiply-add x heads x width, per (token, candidate) pair."""
@@ -544,13 +567,26 @@ def main():
                    "k": cfg["k"], "nh": cfg["nh"], "n_win": cfg["n_win"],
                    "rope_dims": cfg["rope_dims"], "parallelism": "none (1 GPU)"},
         "stages_ms": {"compress": comp_ms, "index_topk": idx_ms, "sparse_mqa": att_ms},
-        "roofline": {"kernel": "mqa_kernel (csa_sparse_mqa_prefill)", "bound": "mfma",
+        "roofline": {"kernel": "mqa_prefill_bf16_kernel (csa_sparse_mqa_prefill)", "bound": "mfma",
                      "achieved": achieved / 1e12, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16, "traffic": measured_traffic(),
                      "algorithmic": f"{flops:.4g} FLOP per launch = 4 x 64 heads x 512 x "
                                     f"{pairs} (token, candidate) pairs"},
     }
     del att_t
+    # the same prefill in 8 chunks of 8192 tokens (chunked prefill): its time,
+    # and whether its outputs equal the one-shot prefill's bit for bit
+    pf.step()
+    one_shot = [x.clone() for x in (pf.comp, pf.kI, pf.idx, pf.out)]
+    pf.step_chunked(8192)
+    same = all(torch.equal(a_.view(torch.int16) if a_.dtype == torch.bfloat16 else a_,
+                           b_.view(torch.int16) if b_.dtype == torch.bfloat16 else b_)
+               for a_, b_ in zip(one_shot, (pf.comp, pf.kI, pf.idx, pf.out)))
+    ch_ms = float(np.mean(time_region(lambda: pf.step_chunked(8192), a.steps, 1)))
+    rec["chunked_prefill"] = {"chunk_tokens": 8192, "chunks": -(-n // 8192), "ms_per_step": ch_ms,
+                              "tokens_per_s": n / (ch_ms * 1e-3),
+                              "outputs_equal_one_shot": bool(same)}
+    del one_shot
     # selection on bf16-rounded index scores ([R] section 4.4): its time and
     # its recall of the fp32-score selection, row by row (-1 slots excluded)
     idx32 = pf.idx.clone()
