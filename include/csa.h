@@ -33,7 +33,8 @@
  *    starts; every call leaves them zero again, so they need clearing only
  *    when the buffer is new, after the caller wrote to it, after a failed
  *    call, or before a call whose zero-byte count exceeds the previous one's
- *    on that buffer (only csa_index_topk_decode has such bytes).
+ *    on that buffer (only the decode top-k calls, and csa_index_topk_prefill
+ *    on rows of more than 16384 visible entries, have such bytes).
  *  - Return value: CSA_OK or a negative csa_status.  All argument checks run
  *    on the host before anything is enqueued, so a failing call has no side
  *    effect.  A fault inside a kernel surfaces at the caller's next stream
@@ -224,8 +225,11 @@ int csa_state_init(const csa_compress_desc* desc, float* state, void* stream);
  *                                    entries beyond n_entries are invisible)
  *   idx_out [n, k]       int32
  * With t0 > 0 (a chunk of a chunked prefill) row t is the token at position
- * t0 + t and sees s < floor((t0+t+1)/m).  Rows hold at most 16384 visible
- * entries (CSA_ERR_UNSUPPORTED beyond).
+ * t0 + t and sees s < floor((t0+t+1)/m).  When the last row sees more than
+ * 16384 entries the rows are selected by the decode top-k, in batches of
+ * rows sharing KI (same result definition; fp32 scores only, else
+ * CSA_ERR_UNSUPPORTED); the workspace then has leading zero bytes
+ * (csa_workspace_zero_bytes(CSA_ENTRY_INDEX_TOPK_PREFILL, desc)).
  */
 int csa_index_topk_prefill(const csa_index_desc* desc, const void* qI, const void* wI,
                            const void* KI, int32_t* idx_out, void* ws, size_t ws_bytes,

@@ -408,10 +408,13 @@ def csa_index_topk_prefill(qI, wI, KI, m, k, out=None, scores="f32", t0=0):
     desc = IndexDesc(n, 1, hI, cI, m, k, _dt(qI), ne, sdt, t0)
     if out is None:
         out = torch.empty((n, k), dtype=torch.int32, device=qI.device)
-    ws, wsb = workspace(workspace_bytes("index_topk_prefill", desc), qI.device, "index")
+    ws, wsb = workspace(workspace_bytes("index_topk_prefill", desc), qI.device, "index",
+                        zero_bytes=workspace_zero_bytes("index_topk_prefill", desc))
     st = lib.csa_index_topk_prefill(ctypes.byref(desc), _ptr(qI), _ptr(wI),
                                     _ptr(KI) if ne else None, _ptr(out), _ptr(ws), wsb,
                                     _stream(qI.device))
+    if st != 0:
+        _WS_ZERO.pop((str(qI.device), "index"), None)
     _check(st, "csa_index_topk_prefill")
     return out
 

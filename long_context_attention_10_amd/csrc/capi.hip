@@ -54,6 +54,8 @@ size_t ws_compress_decode(const csa_compress_desc* d, bool has_win) {
 }
 
 // ---------------------------------------------------------------- indexer
+constexpr int64_t kRegRowMax = 256 * 64;  // visible entries a prefill row holds in registers
+
 int check_index(const csa_index_desc* d, bool decode) {
   if (!d) return CSA_ERR_INVALID_ARG;
   if (!dtype_ok(d->dtype)) return CSA_ERR_UNSUPPORTED;
@@ -70,9 +72,18 @@ int check_index(const csa_index_desc* d, bool decode) {
     if (d->n < 0 || d->t0 < 0) return CSA_ERR_INVALID_ARG;
     const int64_t last = (d->t0 + d->n) / d->m;  // visible entries of the last row
     const int64_t vis = last < d->n_entries ? last : d->n_entries;
-    if (vis > 256 * 64) return CSA_ERR_UNSUPPORTED;  // row held in registers
+    // rows past the register selector take the decode top-k (fp32 scores only)
+    if (vis > kRegRowMax && (d->score_dtype != CSA_F32 || vis >= (int64_t)1 << 31))
+      return CSA_ERR_UNSUPPORTED;
   }
   return CSA_OK;
+}
+
+// A prefill call whose last row sees more entries than the register selector
+// holds: it runs the decode top-k over batches of rows.
+bool index_prefill_long(const csa_index_desc* d) {
+  const int64_t last = (d->t0 + d->n) / d->m;
+  return (last < d->n_entries ? last : d->n_entries) > kRegRowMax;
 }
 
 // Row stride of the prefill score workspace (a multiple of 4 floats).
@@ -213,6 +224,11 @@ size_t csa_state_bytes(const csa_compress_desc* d) {
 }
 
 size_t csa_workspace_zero_bytes(int entry, const void* desc) {
+  if (desc && entry == CSA_ENTRY_INDEX_TOPK_PREFILL) {
+    const csa_index_desc* d = (const csa_index_desc*)desc;
+    if (d->m <= 0 || d->n <= 0 || !index_prefill_long(d)) return 0;
+    return index_prefill_long_zero_bytes(*d);
+  }
   if (!desc || (entry != CSA_ENTRY_INDEX_TOPK_DECODE && entry != CSA_ENTRY_INDEX_TOPK_DECODE_FP4))
     return 0;
   const csa_index_desc* d = (const csa_index_desc*)desc;
@@ -236,6 +252,7 @@ size_t csa_workspace_bytes(int entry, const void* desc) {
     case CSA_ENTRY_INDEX_TOPK_PREFILL: {
       const csa_index_desc* d = (const csa_index_desc*)desc;
       if (d->m <= 0 || d->n <= 0) return 0;
+      if (index_prefill_long(d)) return index_prefill_long_ws_bytes(*d);
       return al((size_t)d->n * index_prefill_ld(d) * (d->score_dtype == CSA_BF16 ? 2 : 4));
     }
     case CSA_ENTRY_INDEX_TOPK_DECODE:
@@ -342,6 +359,11 @@ int csa_index_topk_prefill(const csa_index_desc* d, const void* qI, const void* 
   if (s) return s;
   if (d->n == 0) return CSA_OK;
   if (!qI || !wI || !idx_out || (d->n_entries > 0 && !KI)) return CSA_ERR_INVALID_ARG;
+  if (index_prefill_long(d)) {
+    if (!ws || ws_bytes < index_prefill_long_ws_bytes(*d)) return CSA_ERR_WORKSPACE;
+    return hip_status(
+        launch_index_topk_prefill_long(*d, qI, wI, KI, idx_out, ws, (hipStream_t)stream));
+  }
   const int64_t ld = index_prefill_ld(d);
   const size_t need = al((size_t)d->n * ld * (d->score_dtype == CSA_BF16 ? 2 : 4));
   if (ld > 0 && (!ws || ws_bytes < need)) return CSA_ERR_WORKSPACE;

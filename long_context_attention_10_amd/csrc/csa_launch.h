@@ -77,6 +77,12 @@ hipError_t launch_topk_rows_prefill(const csa_index_desc& d, const void* scores,
                                     int32_t* idx_out, hipStream_t st);
 
 size_t index_decode_ws_bytes(const csa_index_desc& d);
+// prefill rows beyond the register selector (decode top-k over row batches)
+size_t index_prefill_long_ws_bytes(const csa_index_desc& d);
+size_t index_prefill_long_zero_bytes(const csa_index_desc& d);
+hipError_t launch_index_topk_prefill_long(const csa_index_desc& d, const void* qI,
+                                          const void* wI, const void* KI, int32_t* idx_out,
+                                          void* ws, hipStream_t st);
 size_t index_decode_zero_bytes(const csa_index_desc& d);
 hipError_t launch_index_topk_decode_fp4(const csa_index_desc& d, const uint8_t* qc,
                                         const uint8_t* qe, const void* wI, const uint8_t* kc,

@@ -1321,6 +1321,66 @@ hipError_t launch_index_topk_decode(const csa_index_desc& d, const void* qI, con
   return dec_select(d, w, nch, ncopies, pos, idx_out, st);
 }
 
+// ---------------------------------------------------------------------------
+// Prefill rows with more visible entries than the register selector holds
+// (long chunks of a chunked prefill): sub-batches of rows run the decode
+// top-k, each row a "sequence" at position t0 + row, all rows sharing the
+// one key table through an entry map of a single page (max_pages = 0, so
+// every row reads slot 0, which holds page 0).
+// ---------------------------------------------------------------------------
+__global__ void long_rows_prep_kernel(int64_t* __restrict__ pos, int64_t first, int rows,
+                                      int32_t* __restrict__ table) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < rows) pos[i] = first + i;
+  if (i == 0) table[0] = 0;
+}
+
+static csa_index_desc long_rows_desc(const csa_index_desc& d) {
+  csa_index_desc dd = d;
+  const int64_t last = (d.t0 + d.n) / d.m;  // visible entries of the last row
+  dd.n_entries = last < d.n_entries ? last : d.n_entries;
+  // rows per sub-batch: about 2 GiB of decode workspace (20 B per entry and row)
+  const int64_t r = ((int64_t)1 << 31) / (20 * (dd.n_entries > 0 ? dd.n_entries : 1));
+  dd.batch = (int32_t)(r < 1 ? 1 : r > 1024 ? 1024 : r);
+  if (dd.batch > d.n) dd.batch = (int32_t)(d.n > 0 ? d.n : 1);
+  return dd;
+}
+
+size_t index_prefill_long_zero_bytes(const csa_index_desc& d) {
+  return index_decode_zero_bytes(long_rows_desc(d));
+}
+
+size_t index_prefill_long_ws_bytes(const csa_index_desc& d) {
+  const csa_index_desc dd = long_rows_desc(d);
+  return index_decode_ws_bytes(dd) + align_up((size_t)dd.batch * 8) + 256;
+}
+
+hipError_t launch_index_topk_prefill_long(const csa_index_desc& d, const void* qI,
+                                          const void* wI, const void* KI, int32_t* idx_out,
+                                          void* ws, hipStream_t st) {
+  const csa_index_desc dd = long_rows_desc(d);
+  uint8_t* extra = (uint8_t*)ws + index_decode_ws_bytes(dd);
+  int64_t* pos = (int64_t*)extra;
+  int32_t* table = (int32_t*)(extra + align_up((size_t)dd.batch * 8));
+  EntryMap em;
+  em.table = table;
+  em.page = (int32_t)(dd.n_entries > 0 ? dd.n_entries : 1);
+  em.max_pages = 0;
+  const size_t es = d.dtype == CSA_BF16 ? 2 : 4;
+  for (int64_t r0 = 0; r0 < d.n; r0 += dd.batch) {
+    csa_index_desc db = dd;
+    db.batch = (int32_t)(d.n - r0 < dd.batch ? d.n - r0 : dd.batch);
+    long_rows_prep_kernel<<<(db.batch + 255) / 256, 256, 0, st>>>(pos, d.t0 + r0, db.batch, table);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_index_topk_decode(db, (const uint8_t*)qI + r0 * d.n_heads * d.head_dim * es,
+                                 (const uint8_t*)wI + r0 * d.n_heads * es, KI, pos,
+                                 idx_out + r0 * d.k, ws, st, em);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_index_topk_decode_fp4(const csa_index_desc& d, const uint8_t* qc,
                                         const uint8_t* qe, const void* wI, const uint8_t* kc,
                                         const uint8_t* ke, const int64_t* pos, int32_t* idx_out,

@@ -143,8 +143,14 @@ def test_index_and_attention_reject(lib):
     assert lib.csa_index_topk_prefill(ctypes.byref(bad), _p(), _p(), _p(), _p(), _p(), 1 << 30, None) == -2
     big_k = L.IndexDesc(16, 1, 16, 64, 4, 4096, L.CSA_BF16, 4)
     assert lib.csa_index_topk_prefill(ctypes.byref(big_k), _p(), _p(), _p(), _p(), _p(), 1 << 30, None) == -2
-    too_many = L.IndexDesc(1 << 20, 1, 16, 64, 4, 512, L.CSA_BF16, 1 << 18)  # row beyond register select
+    # rows beyond the register selector take the decode top-k: fp32 scores only
+    too_many = L.IndexDesc(1 << 20, 1, 16, 64, 4, 512, L.CSA_BF16, 1 << 18, L.CSA_BF16)
     assert lib.csa_index_topk_prefill(ctypes.byref(too_many), _p(), _p(), _p(), _p(), _p(), 1 << 40, None) == -2
+    long_rows = L.IndexDesc(1 << 20, 1, 16, 64, 4, 512, L.CSA_BF16, 1 << 18)
+    assert lib.csa_index_topk_prefill(ctypes.byref(long_rows), _p(), _p(), _p(), _p(), _p(), 8, None) == -3
+    assert L.workspace_zero_bytes("index_topk_prefill", long_rows) > 0
+    short_rows = L.IndexDesc(1 << 14, 1, 16, 64, 4, 512, L.CSA_BF16, 1 << 12)
+    assert L.workspace_zero_bytes("index_topk_prefill", short_rows) == 0
     dd = L.IndexDesc(0, 2, 16, 64, 4, 8, L.CSA_BF16, 100)
     assert lib.csa_index_topk_decode(ctypes.byref(dd), _p(), _p(), _p(), _p(), _p(), _p(), 8, None) == -3
     a = L.attn_desc(n=8, nh=65, c=128, k=4)
@@ -277,8 +283,12 @@ def test_chunked_prefill_rejects(lib):
     assert L.workspace_bytes("compress_prefill", d1) > L.workspace_bytes("compress_prefill", d0)
     di = L.IndexDesc(16, 1, 16, 64, 4, 8, L.CSA_BF16, 4, 0, -1)
     assert lib.csa_index_topk_prefill(ctypes.byref(di), *([_p()] * 5), 1 << 30, None) == -1
-    # the last row's visible count decides the register limit
-    di = L.IndexDesc(16, 1, 16, 64, 4, 512, L.CSA_BF16, 1 << 20, 0, 4 * 16384)
+    # the last row's visible count decides which selector runs
+    di = L.IndexDesc(16, 1, 16, 64, 4, 512, L.CSA_BF16, 1 << 20, L.CSA_BF16, 4 * 16384)
     assert lib.csa_index_topk_prefill(ctypes.byref(di), *([_p()] * 5), 1 << 40, None) == -2
+    di = L.IndexDesc(16, 1, 16, 64, 4, 512, L.CSA_BF16, 1 << 20, L.CSA_F32, 4 * 16384)
+    assert L.workspace_zero_bytes("index_topk_prefill", di) > 0
+    di.t0 = 0
+    assert L.workspace_zero_bytes("index_topk_prefill", di) == 0
     a = L.attn_desc(n=8, nh=8, c=128, k=4, t0=-1)
     assert lib.csa_sparse_mqa_prefill(ctypes.byref(a), *([_p()] * 6), None, 0, None) == -1

@@ -137,3 +137,32 @@ def test_mqa_prefill_chunked(lib, sparse, dtype, nh, c, k, m, N, n_win, r, cuts)
     ref = O.attend_decode_row(f64(q[t]), t, f64(win[t - nw + 1:t + 1]), f64(comp)[sel], f64(sink),
                               c ** -0.5, rope_dims=r, store=dtype)
     assert_out_close(parts[1][0], ref, dtype, f"row {t}")
+
+
+@pytest.mark.parametrize("k,ne,t0,n", [
+    (512, 200000, 800000, 700),   # two row batches, every row past the register selector
+    (1024, 20000, 65000, 700),    # the chunk crosses the selector's 16384-entry limit
+])
+def test_index_topk_prefill_long_rows(lib, k, ne, t0, n):
+    """Rows that see more than 16384 entries run the decode top-k over
+    batches of rows; each row must match the decode call at its position
+    bit for bit, and sampled rows the oracle."""
+    _say("index_topk_prefill_long_rows", k, ne, t0, n)
+    hI, cI, m = 16, 64, 4
+    key = ("chunk_long", k, ne, t0, n)
+    qI = I.normal((n, hI, cI), key + ("q",), dtype="bf16", device=DEV)
+    wI = I.uniform((n, hI), key + ("w",), dtype="bf16", device=DEV)
+    KI = I.normal((ne, cI), key + ("K",), dtype="bf16", device=DEV)
+    idx = lib.csa_index_topk_prefill(qI, wI, KI, m, k, t0=t0)
+    rows = [0, 1, n // 2, 537, n - 1]
+    pos = torch.tensor([t0 + r for r in rows], dtype=torch.int64, device=DEV)
+    for i, r in enumerate(rows):
+        d = lib.csa_index_topk_decode(qI[r:r + 1].contiguous(), wI[r:r + 1].contiguous(), KI[None],
+                                      pos[i:i + 1].contiguous(), m, k)
+        torch.cuda.synchronize()
+        assert torch.equal(d[0], idx[r]), f"row {r}"
+    got = idx.cpu().numpy()
+    for r in (0, 537, n - 1):
+        t = t0 + r
+        sc = O.index_scores(f64(qI[r])[None], f64(wI[r])[None], f64(KI), m, t0=t)
+        check_topk_sets(got[r:r + 1], sc, k, m, t0=t)
