@@ -115,6 +115,47 @@ class CsaPrefill:
         return 4.0 * c["nh"] * c["c"] * float(pairs.sum()), int(pairs.sum())
 
 
+def chunk_at_context(pf, ctx, chunk, steps, device="cuda"):
+    """One prefill chunk of `chunk` tokens ending a `ctx`-token context, with
+    the earlier entries, indexer keys and window rows synthetic N(0, 1)
+    stand-ins (the 64K workload's weights and per-token inputs): compress
+    (main + indexer, with the halo block), select over up to ctx/m entries,
+    attend.  Returns the stage times in ms."""
+    c, t = pf.cfg, pf.t
+    m, ov, nw, r, k = c["m"], c["overlap"], c["n_win"], c["rope_dims"], c["k"]
+    p0 = ctx - chunk
+    name = ("chunk_at", ctx)
+    kw = dict(dtype=c["dtype"], device=device)
+    H = I.normal((chunk + m, c["d"]), name + ("H",), **kw)
+    comp = I.normal((ctx // m, c["c"]), name + ("comp",), **kw)
+    kI = I.normal((ctx // m, c["cI"]), name + ("kI",), **kw)
+    w0 = p0 - nw + 1
+    win = I.normal((ctx - w0, c["c"]), name + ("win",), **kw)
+    q, qI, wI = t["q"][:chunk], t["qI"][:chunk], t["wI"][:chunk]
+    idx = torch.empty((chunk, k), dtype=torch.int32, device=device)
+    out = torch.empty_like(q)
+    e0, e1 = p0 // m, ctx // m
+
+    def compress():
+        L.csa_compress_prefill(H, t["W_kv"], t["W_z"], t["ape"], m, ov, W_win=t["W_win"],
+                               rope_dims=r, out_comp=comp[e0:e1], out_win=win[p0 - w0:], pos0=p0)
+        L.csa_compress_prefill(H, t["WI_kv"], t["WI_z"], t["apeI"], m, ov, out_comp=kI[e0:e1],
+                               pos0=p0)
+
+    def index():
+        L.csa_index_topk_prefill(qI, wI, kI, m, k, out=idx, t0=p0)
+
+    def attend():
+        L.csa_sparse_mqa_prefill(q, win, comp, idx, t["sink"], n_win=nw, rope_dims=r, out=out,
+                                 t0=p0)
+    res = {}
+    for nm, fn in (("compress", compress), ("index_topk", index), ("sparse_mqa", attend)):
+        res[nm] = float(np.mean(time_region(fn, steps, 1)))
+    del H, comp, kI, win, idx, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def time_region(fn, steps, warmup, flush=None):
     """Per-step event times (ms) on the current stream."""
     for _ in range(warmup):
@@ -587,6 +628,12 @@ def main():
                               "tokens_per_s": n / (ch_ms * 1e-3),
                               "outputs_equal_one_shot": bool(same)}
     del one_shot
+    # one 8192-token chunk ending a 1M-token context: its rows see up to
+    # 262144 entries, so the selection runs the decode top-k over row batches
+    st1m = chunk_at_context(pf, 1 << 20, 8192, max(3, a.steps), dev)
+    rec["chunked_prefill"]["chunk_ending_1m_context"] = {
+        "stages_ms": st1m, "ms": sum(st1m.values()),
+        "tokens_per_s": 8192 / (sum(st1m.values()) * 1e-3)}
     # selection on bf16-rounded index scores ([R] section 4.4): its time and
     # its recall of the fp32-score selection, row by row (-1 slots excluded)
     idx32 = pf.idx.clone()
