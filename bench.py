@@ -62,12 +62,19 @@ class CsaPrefill:
         self.out = torch.empty((n, nh, c), dtype=dt, device=device)
 
     def compress(self):
+        self.compress_main()
+        self.compress_indexer()
+
+    def compress_main(self):
         c, t = self.cfg, self.t
         L.csa_compress_prefill(t["H"], t["W_kv"], t["W_z"], t["ape"], c["m"], c["overlap"],
                                W_win=t["W_win"], rope_dims=c["rope_dims"], out_comp=self.comp,
                                out_win=self.win)
+
+    def compress_indexer(self):
+        c, t = self.cfg, self.t
         L.csa_compress_prefill(t["H"], t["WI_kv"], t["WI_z"], t["apeI"], c["m"], c["overlap"],
-                               out_comp=self.kI)
+                               out_comp=self.kI, ws_slot="prefill_indexer")
 
     def index(self):
         c, t = self.cfg, self.t
@@ -78,9 +85,27 @@ class CsaPrefill:
         L.csa_sparse_mqa_prefill(t["q"], self.win, self.comp, self.idx, t["sink"],
                                  n_win=c["n_win"], rope_dims=c["rope_dims"], out=self.out)
 
-    def step(self):
-        self.compress()
-        self.index()
+    def step(self, streams=False):
+        """One prefill pass.  The indexer chain (its compressor, then the
+        top-k) and the main compressor are independent until the attention:
+        with `streams` the indexer chain runs on a forked side stream
+        (default priority) while the main compressor runs on the current
+        stream, which joins it before the attention.  Off by default: at 64K
+        both chains fill the chip, and the overlap measured no faster."""
+        if not streams:
+            self.compress()
+            self.index()
+            self.attend()
+            return
+        main = torch.cuda.current_stream()
+        if getattr(self, "side", None) is None:
+            self.side = torch.cuda.Stream()
+        self.side.wait_stream(main)
+        with torch.cuda.stream(self.side):
+            self.compress_indexer()
+            self.index()
+        self.compress_main()
+        main.wait_stream(self.side)
         self.attend()
 
     def step_chunked(self, chunk=8192):

@@ -50,3 +50,25 @@ def test_decode_step_streams_match_one_stream(lib):
         print(f"[streams] graph replay {rep}", flush=True)
         for n, a, b in zip(names, outs, ref):
             assert torch.equal(a, b), f"graph replay {rep}: {n} differs from the one-stream step"
+
+
+def test_prefill_step_streams_match_one_stream(lib):
+    """The benchmark's prefill step with the indexer chain on a forked stream
+    gives bitwise the one-stream results."""
+    from long_context_attention_10_amd import configs
+    print("[streams] prefill step n=4096", flush=True)
+    cfg = dict(configs.get("csa_prefill_64k_bf16", n=4096))
+    cfg["name"] = "streams-check-prefill"
+    pf = bench.CsaPrefill(cfg, "cuda")
+    outs = [pf.comp, pf.win, pf.kI, pf.idx, pf.out]
+    names = ["comp", "win", "kI", "idx", "out"]
+    pf.step(streams=False)
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in outs]
+    for x in outs:
+        x.zero_()
+    for _ in range(2):
+        pf.step(streams=True)
+        torch.cuda.synchronize()
+        for n, a, b in zip(names, outs, ref):
+            assert torch.equal(a, b), f"streams: {n} differs from the one-stream step"
