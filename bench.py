@@ -140,6 +140,41 @@ class CsaPrefill:
         return 4.0 * c["nh"] * c["c"] * float(pairs.sum()), int(pairs.sum())
 
 
+class HcaPrefill:
+    """One HCA layer prefill (compressor with window rows, then dense MQA over
+    every visible entry) on the workload's synthetic inputs."""
+
+    def __init__(self, cfg, device="cuda"):
+        self.cfg = cfg
+        self.t = I.csa_prefill_inputs(cfg, device=device, with_indexer=False)
+        n, c, m, nh = cfg["n"], cfg["c"], cfg["m"], cfg["nh"]
+        dt = I.TORCH_DTYPES[cfg["dtype"]]
+        self.comp = torch.empty((n // m, c), dtype=dt, device=device)
+        self.win = torch.empty((n, c), dtype=dt, device=device)
+        self.out = torch.empty((n, nh, c), dtype=dt, device=device)
+
+    def compress(self):
+        c, t = self.cfg, self.t
+        L.csa_compress_prefill(t["H"], t["W_kv"], t["W_z"], t["ape"], c["m"], 0,
+                               W_win=t["W_win"], rope_dims=c.get("rope_dims", 0),
+                               out_comp=self.comp, out_win=self.win)
+
+    def attend(self):
+        c, t = self.cfg, self.t
+        L.hca_dense_mqa_prefill(t["q"], self.win, self.comp, t["sink"], c["m"], n_win=c["n_win"],
+                                rope_dims=c.get("rope_dims", 0), out=self.out)
+
+    def step(self):
+        self.compress()
+        self.attend()
+
+    def attn_flops(self):
+        c = self.cfg
+        t = np.arange(c["n"], dtype=np.int64)
+        pairs = np.minimum(c["n_win"], t + 1) + (t + 1) // c["m"]
+        return 4.0 * c["nh"] * c["c"] * float(pairs.sum())
+
+
 def chunk_at_context(pf, ctx, chunk, steps, device="cuda"):
     """One prefill chunk of `chunk` tokens ending a `ctx`-token context, with
     the earlier entries, indexer keys and window rows synthetic N(0, 1)
@@ -659,6 +694,24 @@ def main():
     rec["chunked_prefill"]["chunk_ending_1m_context"] = {
         "stages_ms": st1m, "ms": sum(st1m.values()),
         "tokens_per_s": 8192 / (sum(st1m.values()) * 1e-3)}
+    # the HCA layer's prefill at its own workload (16K) and at 64K tokens
+    rec["hca_prefill"] = {}
+    for n_h in (16384, 65536):
+        hcfg = dict(configs.get("hca_prefill_16k_bf16", n=n_h))
+        hp = HcaPrefill(hcfg, dev)
+        h_ms = float(np.mean(time_region(hp.step, a.steps, a.warmup)))
+        ha_ms = float(np.mean(time_region(hp.attend, max(3, a.steps), 1)))
+        hf = hp.attn_flops()
+        rec["hca_prefill"][f"n{n_h}"] = {
+            "ms_per_step": h_ms, "tokens_per_s": n_h / (h_ms * 1e-3),
+            "stages_ms": {"compress": h_ms - ha_ms, "dense_mqa": ha_ms},
+            "dense_mqa_tflops": hf / (ha_ms * 1e-3) / 1e12,
+            "dense_mqa_frac": hf / (ha_ms * 1e-3) / PEAK_BF16,
+            # q and out, window rows and entries, each once (bf16)
+            "dense_mqa_hbm_frac": 2.0 * hcfg["c"] * (2 * n_h * hcfg["nh"] + n_h + n_h // hcfg["m"])
+                                  / (ha_ms * 1e-3) / PEAK_HBM}
+        del hp
+        torch.cuda.empty_cache()
     # selection on bf16-rounded index scores ([R] section 4.4): its time and
     # its recall of the fp32-score selection, row by row (-1 slots excluded)
     idx32 = pf.idx.clone()
