@@ -635,7 +635,7 @@ def main():
                     help="only the copy reference and the MQA prefill, for counter passes")
     a = ap.parse_args()
     if a.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {a.gpus}).",
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus {a.gpus}).",
               file=sys.stderr)
         sys.exit(2)
     L.load()
