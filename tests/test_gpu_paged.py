@@ -185,3 +185,58 @@ def test_mqa_decode_paged(lib, sparse, nh, c, k, m, ne, page, r, pos, share):
     ref = O.attend_decode_row(f64(q[b]), pos[b], _ring_rows(f64(ring[b]), pos[b], n_win),
                               f64(cache[b])[sel], f64(sink), c ** -0.5, rope_dims=r, store="bf16")
     assert_out_close(out_p[b], ref, "bf16", f"seq {b}")
+
+
+def test_chunked_prefill_then_paged_decode(lib):
+    """The paged-cache flow end to end: a prefill in block-aligned chunks, its
+    entries copied into a shuffled page pool, then decode steps over the
+    pool, against a one-shot prefill and contiguous decode, bit for bit
+    (entries, ring, state and the dense attention output of every step)."""
+    _say("chunked prefill -> paged decode")
+    d, c, m, ov, r, page, n_win, nh = 256, 512, 4, 1, 64, 32, 128, 64
+    N, cuts, steps = 700, [256, 512], 9
+    w = (1 + ov) * c
+    key = ("flow", d, c, m)
+    H = I.normal((N + steps, d), key + ("H",), dtype="bf16", device=DEV)
+    Wkv = I.normal((w, d), key + ("Wkv",), std=d ** -0.5, dtype="bf16", device=DEV)
+    Wz = I.normal((w, d), key + ("Wz",), std=d ** -0.5, dtype="bf16", device=DEV)
+    Ww = I.normal((c, d), key + ("Ww",), std=d ** -0.5, dtype="bf16", device=DEV)
+    ape = I.normal((m, w), key + ("ape",), device=DEV)
+    q = I.normal((steps, 1, nh, c), key + ("q",), dtype="bf16", device=DEV)
+    sink = I.normal((nh,), key + ("sink",), device=DEV)
+    max_e = (N + steps) // m + 1
+    # one-shot prefill, contiguous cache
+    full = lib.csa_compress_prefill(H[:N].contiguous(), Wkv, Wz, ape, m, ov, W_win=Ww, rope_dims=r,
+                                    n_win=n_win, want_ring=True, want_state=True)
+    cache = torch.zeros((1, max_e, c), dtype=H.dtype, device=DEV)
+    cache[0, :N // m] = full["comp"]
+    ring, state = full["ring"][None].contiguous(), full["state"]
+    # chunked prefill, entries copied into a page pool
+    ring_p = torch.zeros((1, n_win, c), dtype=H.dtype, device=DEV)
+    comps, state_p = [], None
+    bounds = [0] + cuts + [N]
+    for p0, p1 in zip(bounds[:-1], bounds[1:]):
+        h0 = p0 - m if p0 > 0 else 0
+        res = lib.csa_compress_prefill(H[h0:p1].contiguous(), Wkv, Wz, ape, m, ov, W_win=Ww,
+                                       rope_dims=r, n_win=n_win, win_ring=ring_p[0],
+                                       want_state=True, pos0=p0)
+        comps.append(res["comp"])
+        state_p = res["state"]
+    staged = torch.zeros((1, max_e, c), dtype=H.dtype, device=DEV)
+    staged[0, :N // m] = torch.cat(comps)
+    pool, table = _paginate(staged, page, key)
+    for s in range(steps):
+        pos = torch.tensor([N + s], dtype=torch.int64, device=DEV)
+        h = H[N + s][None].contiguous()
+        lib.csa_compress_decode(h, pos, Wkv, Wz, ape, m, ov, state, cache, W_win=Ww,
+                                win_ring=ring, rope_dims=r)
+        lib.csa_compress_decode_paged(h, pos, Wkv, Wz, ape, m, ov, state_p, pool, table, page,
+                                      W_win=Ww, win_ring=ring_p, n_entries=max_e, rope_dims=r)
+        o = lib.hca_dense_mqa_decode(q[s], ring, cache, pos, sink, m, rope_dims=r)
+        o_p = lib.hca_dense_mqa_decode_paged(q[s], ring_p, pool, table, page, pos, sink, m,
+                                             n_entries=max_e, rope_dims=r)
+        torch.cuda.synchronize()
+        assert _same_bits(o_p, o), f"step {s}"
+    assert _same_bits(_gather(pool, table, page, max_e), cache)
+    assert _same_bits(ring_p, ring)
+    assert _same_bits(state_p, state)
