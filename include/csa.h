@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 6
+#define CSA_ABI_VERSION 7
 
 typedef enum csa_status {
   CSA_OK = 0,
@@ -415,6 +415,24 @@ int hca_dense_mqa_decode_paged(const csa_attn_desc* desc, const void* q, const v
                                const void* comp_pool, const int32_t* page_table,
                                int32_t page_entries, const int64_t* pos, const float* sink,
                                void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* The FP4 indexer over paged caches: the key pool [P*page_entries, cI] and
+ * the FP4 pools (codes [P*page_entries, cI/2], exps [P*page_entries, cI/32])
+ * share one page table, so an entry has the same row in all three.  As
+ * csa_indexer_fp4_quant_decode and csa_index_topk_decode_fp4, with rows
+ * mapped as above (N = n_entries, resp. desc->n_entries). */
+int csa_indexer_fp4_quant_decode_paged(const csa_fp4_desc* desc, const void* cache_pool,
+                                       int64_t n_entries, const int64_t* pos, int m,
+                                       uint8_t* codes_pool, uint8_t* exps_pool,
+                                       const int32_t* page_table, int32_t page_entries,
+                                       void* stream);
+
+int csa_index_topk_decode_fp4_paged(const csa_index_desc* desc, const uint8_t* qI_codes,
+                                    const uint8_t* qI_exps, const void* wI,
+                                    const uint8_t* K_codes_pool, const uint8_t* K_exps_pool,
+                                    const int32_t* page_table, int32_t page_entries,
+                                    const int64_t* pos, int32_t* idx_out, void* ws,
+                                    size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Helpers

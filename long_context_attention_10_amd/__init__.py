@@ -30,7 +30,8 @@ EXPORTED = ["csa_compress_prefill", "csa_compress_decode", "csa_state_bytes", "c
             "csa_index_topk_decode_fp4", "csa_indexer_fp4_quant_decode", "csa_workspace_bytes",
             "csa_workspace_zero_bytes", "csa_status_string", "csa_abi_version",
             "csa_compress_decode_paged", "csa_index_topk_decode_paged",
-            "csa_sparse_mqa_decode_paged", "hca_dense_mqa_decode_paged"]
+            "csa_sparse_mqa_decode_paged", "hca_dense_mqa_decode_paged",
+            "csa_indexer_fp4_quant_decode_paged", "csa_index_topk_decode_fp4_paged"]
 
 
 class CompressDesc(ctypes.Structure):
@@ -118,6 +119,8 @@ def load(path: str = LIB_PATH):
     lib.csa_index_topk_decode_paged.argtypes = [P] * 5 + [I32] + [P] * 3 + [S, P]
     lib.csa_sparse_mqa_decode_paged.argtypes = [P] * 5 + [I32] + [P] * 5 + [S, P]
     lib.hca_dense_mqa_decode_paged.argtypes = [P] * 5 + [I32] + [P] * 4 + [S, P]
+    lib.csa_indexer_fp4_quant_decode_paged.argtypes = [P, P, ctypes.c_int64, P, I, P, P, P, I32, P]
+    lib.csa_index_topk_decode_fp4_paged.argtypes = [P] * 7 + [I32] + [P] * 3 + [S, P]
     for f in EXPORTED:
         if f not in ("csa_abi_version", "csa_status_string", "csa_workspace_bytes",
                      "csa_workspace_zero_bytes", "csa_state_bytes"):
@@ -657,3 +660,50 @@ def csa_indexer_fp4_quant_decode(cache, pos, m, codes, exps):
     st = lib.csa_indexer_fp4_quant_decode(ctypes.byref(desc), _ptr(cache), ne, _ptr(pos), m,
                                           _ptr(codes), _ptr(exps), _stream(cache.device))
     _check(st, "csa_indexer_fp4_quant_decode")
+
+
+def csa_indexer_fp4_quant_decode_paged(cache_pool, pos, m, codes_pool, exps_pool, page_table,
+                                       page_entries, n_entries=None):
+    """csa_indexer_fp4_quant_decode over paged caches: the key pool [P * page,
+    W] and the FP4 pools (codes [P * page, W/2], exps [P * page, W/32]) share
+    page_table [B, ceil(n_entries / page)]."""
+    lib = load()
+    B = pos.shape[0]
+    W = cache_pool.shape[1]
+    ne = _paged(cache_pool, page_table, page_entries, B, W, cache_pool.dtype, n_entries,
+                "cache_pool")
+    _expect(codes_pool, (cache_pool.shape[0], W // 2), torch.uint8, "codes_pool")
+    _expect(exps_pool, (cache_pool.shape[0], W // 32), torch.uint8, "exps_pool")
+    desc = Fp4Desc(B, W, _dt(cache_pool))
+    st = lib.csa_indexer_fp4_quant_decode_paged(ctypes.byref(desc), _ptr(cache_pool), ne, _ptr(pos),
+                                                m, _ptr(codes_pool), _ptr(exps_pool),
+                                                _ptr(page_table), page_entries,
+                                                _stream(cache_pool.device))
+    _check(st, "csa_indexer_fp4_quant_decode_paged")
+
+
+def csa_index_topk_decode_fp4_paged(q_codes, q_exps, wI, k_codes_pool, k_exps_pool, page_table,
+                                    page_entries, pos, m, k, n_entries=None, out=None):
+    lib = load()
+    B, hI, half = q_codes.shape
+    cI = 2 * half
+    _expect(q_exps, (B, hI, cI // 32), torch.uint8, "q_exps")
+    ne = _paged(k_codes_pool, page_table, page_entries, B, half, torch.uint8, n_entries,
+                "k_codes_pool")
+    _expect(k_exps_pool, (k_codes_pool.shape[0], cI // 32), torch.uint8, "k_exps_pool")
+    _expect(wI, (B, hI), None, "wI")
+    _expect(pos, (B,), torch.int64, "pos")
+    desc = IndexDesc(0, B, hI, cI, m, k, _dt(wI), ne)
+    if out is None:
+        out = torch.empty((B, k), dtype=torch.int32, device=q_codes.device)
+    ws, wsb = workspace(workspace_bytes("index_topk_decode_fp4", desc), q_codes.device,
+                        "index_dec_fp4",
+                        zero_bytes=workspace_zero_bytes("index_topk_decode_fp4", desc))
+    st = lib.csa_index_topk_decode_fp4_paged(ctypes.byref(desc), _ptr(q_codes), _ptr(q_exps),
+                                             _ptr(wI), _ptr(k_codes_pool), _ptr(k_exps_pool),
+                                             _ptr(page_table), page_entries, _ptr(pos), _ptr(out),
+                                             _ptr(ws), wsb, _stream(q_codes.device))
+    if st != 0:
+        _WS_ZERO.pop((str(q_codes.device), "index_dec_fp4"), None)
+    _check(st, "csa_index_topk_decode_fp4_paged")
+    return out

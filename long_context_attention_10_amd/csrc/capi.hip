@@ -441,6 +441,45 @@ int csa_indexer_fp4_quant_decode(const csa_fp4_desc* d, const void* cache, int64
                                             n_entries, m, (hipStream_t)stream));
 }
 
+int csa_indexer_fp4_quant_decode_paged(const csa_fp4_desc* d, const void* cache_pool,
+                                       int64_t n_entries, const int64_t* pos, int m,
+                                       uint8_t* codes_pool, uint8_t* exps_pool,
+                                       const int32_t* page_table, int32_t page_entries,
+                                       void* stream) {
+  if (!d) return CSA_ERR_INVALID_ARG;
+  if (!dtype_ok(d->dtype)) return CSA_ERR_UNSUPPORTED;
+  if (d->rows < 0 || n_entries < 0 || m <= 0) return CSA_ERR_INVALID_ARG;
+  if (d->width != 64 && d->width != 128) return CSA_ERR_UNSUPPORTED;
+  EntryMap em;
+  int s = entry_map(page_table, page_entries, n_entries, &em);
+  if (s) return s;
+  if (d->rows == 0 || n_entries == 0) return CSA_OK;
+  if (!cache_pool || !pos || !codes_pool || !exps_pool) return CSA_ERR_INVALID_ARG;
+  return hip_status(launch_fp4_rotate_quant(d->dtype, cache_pool, d->rows, d->width, codes_pool,
+                                            exps_pool, pos, n_entries, m, (hipStream_t)stream,
+                                            em));
+}
+
+int csa_index_topk_decode_fp4_paged(const csa_index_desc* d, const uint8_t* qI_codes,
+                                    const uint8_t* qI_exps, const void* wI,
+                                    const uint8_t* K_codes_pool, const uint8_t* K_exps_pool,
+                                    const int32_t* page_table, int32_t page_entries,
+                                    const int64_t* pos, int32_t* idx_out, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  int s = check_index(d, true);
+  if (s) return s;
+  if (d->dtype != CSA_BF16) return CSA_ERR_UNSUPPORTED;
+  EntryMap em;
+  s = entry_map(page_table, page_entries, d->n_entries, &em);
+  if (s) return s;
+  if (!qI_codes || !qI_exps || !wI || !K_codes_pool || !K_exps_pool || !pos || !idx_out)
+    return CSA_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < index_decode_ws_bytes(*d)) return CSA_ERR_WORKSPACE;
+  return hip_status(launch_index_topk_decode_fp4(*d, qI_codes, qI_exps, wI, K_codes_pool,
+                                                 K_exps_pool, pos, idx_out, ws,
+                                                 (hipStream_t)stream, em));
+}
+
 int csa_index_topk_decode_fp4(const csa_index_desc* d, const uint8_t* qI_codes,
                               const uint8_t* qI_exps, const void* wI, const uint8_t* K_codes,
                               const uint8_t* K_exps, const int64_t* pos, int32_t* idx_out,

@@ -87,12 +87,13 @@ size_t index_decode_zero_bytes(const csa_index_desc& d);
 hipError_t launch_index_topk_decode_fp4(const csa_index_desc& d, const uint8_t* qc,
                                         const uint8_t* qe, const void* wI, const uint8_t* kc,
                                         const uint8_t* ke, const int64_t* pos, int32_t* idx_out,
-                                        void* wsp, hipStream_t st);
+                                        void* wsp, hipStream_t st, EntryMap em = EntryMap());
 // pos == nullptr: rows 0..rows-1; else row b * n_entries + pos[b] / m of each
 // of `rows` sequences, when (pos[b] + 1) % m == 0.
 hipError_t launch_fp4_rotate_quant(int dtype, const void* x, int64_t rows, int width,
                                    uint8_t* codes, uint8_t* exps, const int64_t* pos,
-                                   int64_t n_entries, int m, hipStream_t st);
+                                   int64_t n_entries, int m, hipStream_t st,
+                                   EntryMap em = EntryMap());
 hipError_t launch_index_topk_decode(const csa_index_desc& d, const void* qI, const void* wI,
                                     const void* KI, const int64_t* pos, int32_t* idx_out,
                                     void* ws, hipStream_t st, EntryMap em = EntryMap());

@@ -701,7 +701,8 @@ __global__ __launch_bounds__(256) void fp4_rotate_quant_kernel(const typename T:
                                                                uint8_t* __restrict__ codes,
                                                                uint8_t* __restrict__ exps,
                                                                const int64_t* __restrict__ posv,
-                                                               int64_t n_entries, int m) {
+                                                               int64_t n_entries, int m,
+                                                               EntryMap em) {
   constexpr int NV = CI / 64;
   const int lane = threadIdx.x & 63;
   int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -709,7 +710,7 @@ __global__ __launch_bounds__(256) void fp4_rotate_quant_kernel(const typename T:
   if (posv) {
     const int64_t p = posv[r];
     if (p < 0 || (p + 1) % m != 0 || p / m >= n_entries) return;
-    r = r * n_entries + p / m;
+    r = em.row(r, p / m, n_entries);  // the same row of the key cache and the FP4 caches
   }
   float v[NV];
 #pragma unroll
@@ -757,23 +758,41 @@ CSA_DEV uint4 fp4x8_to_bf16(uint32_t cw, uint32_t eb) {
 // D1 over FP4 keys: dec_score_kernel with q^I and the keys read as E2M1 codes
 // and block exponents (a quarter of the bf16 bytes) and widened to bf16
 // fragments in registers; the products, head sum and histogram are the same.
-template <int HI, int CI>
+template <int HI, int CI, bool PAGED>
 __global__ __launch_bounds__(256) void dec_score_fp4_kernel(
     const uint8_t* __restrict__ qc, const uint8_t* __restrict__ qe, const uint16_t* __restrict__ wI,
     const uint8_t* __restrict__ kc, const uint8_t* __restrict__ ke,
     const int64_t* __restrict__ posv, int64_t n_entries, int m, int k, float* __restrict__ scores,
-    int* __restrict__ hist, int ncopies) {
+    int* __restrict__ hist, int ncopies, EntryMap em) {
   constexpr int NG = CI / 32;  // 32-value k-groups (= scale blocks) per row
   constexpr int RB = CI / 2;   // code bytes per row
   __shared__ int lh[kCoarseBins];
+  __shared__ int64_t srow[PAGED ? kDecChunk : 1];  // pool rows (as in dec_score_kernel)
   const int b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lg = lane >> 4;
+  const int64_t c0 = (int64_t)blockIdx.x * kDecChunk;
+  constexpr int NS = kDecChunk / 256;
+  int32_t tslot[PAGED ? NS : 1];
+  if (PAGED) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int64_t s = c0 + tid + 256 * i;
+      tslot[i] = s < n_entries ? em.table[(int64_t)b * em.max_pages + (uint32_t)s / (uint32_t)em.page]
+                               : 0;
+    }
+  }
   const int64_t vis = min64((posv[b] + 1) / m, n_entries);
   if (vis <= k) return;  // everything visible is selected
-  const int64_t c0 = (int64_t)blockIdx.x * kDecChunk;
   if (c0 >= vis) return;
   const int64_t c1 = min64(c0 + kDecChunk, vis);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lg = lane >> 4;
   for (int i = tid; i < kCoarseBins; i += 256) lh[i] = 0;
+  if (PAGED) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int64_t s = c0 + tid + 256 * i;
+      if (s < c1) srow[s - c0] = (int64_t)tslot[i] * em.page + (uint32_t)s % (uint32_t)em.page;
+    }
+  }
 
   uint4 qa[NG];
   float wv[4];
@@ -791,8 +810,7 @@ __global__ __launch_bounds__(256) void dec_score_fp4_kernel(
     wv[i] = h < HI ? BF16::ld(wI, (int64_t)b * HI + h) : 0.f;
   }
   __syncthreads();
-  const uint8_t* kcb = kc + (int64_t)b * n_entries * RB;
-  const uint8_t* keb = ke + (int64_t)b * n_entries * NG;
+  const int64_t rb0 = PAGED ? 0 : (int64_t)b * n_entries;  // row of entry 0 (contiguous)
   const int64_t w0 = c0 + (int64_t)wave * (kDecChunk / 4);
   const int64_t w1 = min64(w0 + kDecChunk / 4, c1);
   // 64 keys per step: each lane loads 4 code bytes and the scale byte per
@@ -801,10 +819,11 @@ __global__ __launch_bounds__(256) void dec_score_fp4_kernel(
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int64_t s = min64(s0 + u * 16 + (lane & 15), c1 - 1);  // past c1: not stored
+      const int64_t row = PAGED ? srow[s - c0] : rb0 + s;
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
-        dc[u][g] = *(const uint32_t*)(kcb + s * RB + g * 16 + lg * 4);
-        de[u][g] = keb[s * NG + g];
+        dc[u][g] = *(const uint32_t*)(kc + row * RB + g * 16 + lg * 4);
+        de[u][g] = ke[row * NG + g];
       }
     }
   };
@@ -1384,15 +1403,20 @@ hipError_t launch_index_topk_prefill_long(const csa_index_desc& d, const void* q
 hipError_t launch_index_topk_decode_fp4(const csa_index_desc& d, const uint8_t* qc,
                                         const uint8_t* qe, const void* wI, const uint8_t* kc,
                                         const uint8_t* ke, const int64_t* pos, int32_t* idx_out,
-                                        void* wsp, hipStream_t st) {
+                                        void* wsp, hipStream_t st, EntryMap em) {
   DecWs w = carve(wsp, d);
   const int64_t nch = dec_chunks(d);
   const int ncopies = dec_hist_copies(nch);
   const dim3 grid((unsigned)nch, (unsigned)d.batch);
   CSA_INDEX_DISPATCH(d.n_heads, d.head_dim, {
-    dec_score_fp4_kernel<HI, CI><<<grid, 256, 0, st>>>(qc, qe, (const uint16_t*)wI, kc, ke, pos,
-                                                        d.n_entries, d.m, d.k, w.scores, w.hist,
-                                                        ncopies);
+    if (em.table)
+      dec_score_fp4_kernel<HI, CI, true><<<grid, 256, 0, st>>>(
+          qc, qe, (const uint16_t*)wI, kc, ke, pos, d.n_entries, d.m, d.k, w.scores, w.hist,
+          ncopies, em);
+    else
+      dec_score_fp4_kernel<HI, CI, false><<<grid, 256, 0, st>>>(
+          qc, qe, (const uint16_t*)wI, kc, ke, pos, d.n_entries, d.m, d.k, w.scores, w.hist,
+          ncopies, em);
   });
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1401,12 +1425,12 @@ hipError_t launch_index_topk_decode_fp4(const csa_index_desc& d, const uint8_t* 
 
 hipError_t launch_fp4_rotate_quant(int dtype, const void* x, int64_t rows, int width,
                                    uint8_t* codes, uint8_t* exps, const int64_t* pos,
-                                   int64_t n_entries, int m, hipStream_t st) {
+                                   int64_t n_entries, int m, hipStream_t st, EntryMap em) {
   if (rows == 0) return hipSuccess;
   const unsigned g = (unsigned)((rows + 3) / 4);
 #define CSA_FP4Q(TT, WW)                                                                      \
   fp4_rotate_quant_kernel<TT, WW><<<g, 256, 0, st>>>((const TT::S*)x, rows, codes, exps, pos, \
-                                                     n_entries, m)
+                                                     n_entries, m, em)
   if (width == 64) {
     if (dtype == CSA_BF16) CSA_FP4Q(BF16, 64);
     else CSA_FP4Q(F32, 64);

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.csa_abi_version() == 6
+    assert lib.csa_abi_version() == 7
     for code in (0, -1, -2, -3, -4):
         assert len(lib.csa_status_string(code)) > 0
     assert lib.csa_status_string(-99) == b"unknown status"

@@ -240,3 +240,50 @@ def test_chunked_prefill_then_paged_decode(lib):
     assert _same_bits(_gather(pool, table, page, max_e), cache)
     assert _same_bits(ring_p, ring)
     assert _same_bits(state_p, state)
+
+
+def _scatter(x, table, page, P):
+    """Rows of x [B, ne, w] placed in a pool of P pages by an existing page
+    table."""
+    B, ne, w = x.shape
+    pool = torch.zeros((P * page, w), dtype=x.dtype, device=x.device)
+    e = torch.arange(ne, device=x.device)
+    rows = table.long()[:, e // page] * page + (e % page)[None]
+    pool[rows.reshape(-1)] = x.reshape(B * ne, w)
+    return pool
+
+
+def test_fp4_indexer_paged(lib):
+    """The FP4 top-k and the FP4 quantisation of emitted entries over paged
+    caches (the key pool and the FP4 pools sharing one page table) are
+    bit-identical to the contiguous calls."""
+    _say("fp4 indexer paged")
+    B, hI, cI, m, k, ne, page = 3, 16, 64, 4, 512, 40007, 32
+    key = ("pfp4", B, ne)
+    qI = I.normal((B, hI, cI), key + ("q",), dtype="bf16", device=DEV)
+    wI = I.uniform((B, hI), key + ("w",), dtype="bf16", device=DEV)
+    KI = I.normal((B, ne, cI), key + ("K",), dtype="bf16", device=DEV)
+    qc, qe = lib.csa_indexer_fp4_quant(qI)
+    kc, ke = lib.csa_indexer_fp4_quant(KI)
+    kpool, table = _paginate(KI, page, key)
+    P = kpool.shape[0] // page
+    cpool, epool = _scatter(kc, table, page, P), _scatter(ke, table, page, P)
+    pos = torch.tensor([4 * ne - 1, 100003, 7999], dtype=torch.int64, device=DEV)
+    idx = lib.csa_index_topk_decode_fp4(qc, qe, wI, kc, ke, pos, m, k)
+    idx_p = lib.csa_index_topk_decode_fp4_paged(qc, qe, wI, cpool, epool, table, page, pos, m, k,
+                                                n_entries=ne)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_p, idx)
+    # new emitted entries (positions with (p+1) % m == 0), written to both caches
+    pos2 = torch.tensor([403, 8, 1199], dtype=torch.int64, device=DEV)
+    fresh = I.normal((B, cI), key + ("fresh",), dtype="bf16", device=DEV)
+    e = (pos2 // m).tolist()
+    for b in range(B):
+        KI[b, e[b]] = fresh[b]
+        r = int(table[b, e[b] // page]) * page + e[b] % page
+        kpool[r] = fresh[b]
+    lib.csa_indexer_fp4_quant_decode(KI, pos2, m, kc, ke)
+    lib.csa_indexer_fp4_quant_decode_paged(kpool, pos2, m, cpool, epool, table, page, n_entries=ne)
+    torch.cuda.synchronize()
+    assert torch.equal(_gather(cpool, table, page, ne), kc)
+    assert torch.equal(_gather(epool, table, page, ne), ke)
