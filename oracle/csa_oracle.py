@@ -28,8 +28,12 @@ design notes of the repository):
   * RoPE: adjacent pairs (2p, 2p+1) of the last r dims, angle pos*theta^(-2p/r);
     entry i sits at position m*i; the output is rotated back by -t;
   * QK-RMSNorm has unit weight; core-attention scale is passed in (c^-1/2);
-  * rounding (bf16 configs): pooling / norm / RoPE in high precision, one
-    round-to-nearest-even at store; attention output rounded once.
+  * rounding (bf16 configs): a pooled entry, and a window row's projection,
+    is rounded to the storage type before its RMSNorm ([A] Compressor casts
+    the pooled value to the model dtype before its norm; the attention's wkv
+    is a model-dtype linear layer); norm and RoPE then run in high precision
+    with one more round-to-nearest-even at store; attention output rounded
+    once.
 
 Parity pins for every function live in tests/test_oracle_pins.py.
 """
@@ -170,8 +174,11 @@ def rope(x, pos, rope_dims: int, theta: float, inverse: bool = False):
 
 
 def entry_epilogue(x, positions, qk_norm, eps, rope_dims, theta, store):
-    """Normalise, rotate at the entry's position, round once to storage."""
-    y = rms_norm(x, eps) if qk_norm else np.asarray(x, F64)
+    """Round the pooled (or projected) row to the storage type, as [A]
+    Compressor's cast to the model dtype before its RMSNorm does; normalise;
+    rotate at the entry's position; round to storage again."""
+    y = round_to(x, store)
+    y = rms_norm(y, eps) if qk_norm else y
     y = rope(y, positions, rope_dims, theta)
     return round_to(y, store)
 

@@ -335,6 +335,125 @@ def test_output_inverse_rope_makes_output_relative():
     np.testing.assert_allclose(run(0.0), run(37.0), atol=1e-10)
 
 
+def _positions_case():
+    """The worked example's inputs, built through the oracle's own entry and
+    window-row functions (identity projections, no QK-RMSNorm), so that each
+    position the oracle assigns is exercised."""
+    g = GOLD["attention_positions"]
+    c, r, th, m, t = g["c"], g["rope_dims"], g["theta"], g["m"], g["t"]
+    n = t + 1
+    H = np.zeros((n, c))
+    H[t] = g["raw_window_row_at_t"]
+    win = O.window_rows(H, np.eye(c), qk_norm=False, rope_dims=r, theta=th, store="f64")
+    # entries: m = 2 identical token rows per block, so pooling returns the row
+    Hc = np.zeros((n, c))
+    Hc[0:2] = g["raw_entry_0"]
+    Hc[2:4] = g["raw_entry_1"]
+    comp = O.compress_prefill(Hc, np.eye(c), np.zeros((c, c)), np.zeros((m, c)), m, False,
+                              qk_norm=False, rope_dims=r, theta=th, store="f64")
+    q = np.zeros((n, 1, c))
+    q[t, 0] = g["raw_q_at_t"]
+    return g, q, win, comp
+
+
+def test_attention_positions_worked_example_sparse():
+    """Query rotated by +t, window row j at j, entry i at m*i, output rotated
+    back by -t: the contribution of each candidate depends only on its
+    distance to the query, and the values match the hand derivation."""
+    g, q, win, comp = _positions_case()
+    t = g["t"]
+    idx = np.full((t + 1, 1), -1)
+    idx[t, 0] = 1
+    out = O.sparse_mqa_prefill(q, win, comp, idx, np.array(g["sink"]), g["n_win"], g["scale"],
+                               qk_norm=False, rope_dims=g["rope_dims"], theta=g["theta"],
+                               store="f64", rows=[t])
+    np.testing.assert_allclose(out[0, 0], g["expected_sparse"], rtol=0, atol=1e-15)
+
+
+def test_attention_positions_worked_example_dense():
+    g, q, win, comp = _positions_case()
+    t = g["t"]
+    out = O.dense_mqa_prefill(q, win, comp, np.array(g["sink"]), g["m"], g["n_win"], g["scale"],
+                              qk_norm=False, rope_dims=g["rope_dims"], theta=g["theta"],
+                              store="f64", rows=[t])
+    np.testing.assert_allclose(out[0, 0], g["expected_dense"], rtol=0, atol=1e-15)
+
+
+def test_attention_positions_single_window_row_is_relative():
+    """One token, n_win = 1, no entries, r = c: the query and its own window
+    row carry the same rotation, so the logit is the unrotated q.v and the
+    output rotated back is p_self * v with p_self = e^z / (e^z + e^z')."""
+    c, r, t = 4, 4, 9
+    rng = np.random.default_rng(5)
+    raw_v = rng.normal(size=c)
+    qraw = rng.normal(size=c)
+    sink = np.array([0.25])
+    H = np.zeros((t + 1, c))
+    H[t] = raw_v
+    win = O.window_rows(H, np.eye(c), qk_norm=False, rope_dims=r, theta=100.0, store="f64")
+    q = np.zeros((t + 1, 1, c))
+    q[t, 0] = qraw
+    idx = np.full((t + 1, 1), -1)
+    out = O.sparse_mqa_prefill(q, win, np.zeros((0, c)), idx, sink, 1, 0.5, qk_norm=False,
+                               rope_dims=r, theta=100.0, store="f64", rows=[t])
+    z = 0.5 * float(qraw @ raw_v)
+    p_self = math.exp(z) / (math.exp(z) + math.exp(0.25))
+    np.testing.assert_allclose(out[0, 0], p_self * raw_v, rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("r", [0, 8])
+def test_attend_decode_row_equals_prefill_rows(r):
+    """One decode query at t over its window rows and the entries a prefill
+    row would attend to gives that prefill row, for the sparse (selected
+    entries) and the dense (all visible entries) modes."""
+    rng = np.random.default_rng(11 + r)
+    n, c, nh, m, n_win, k = 29, 16, 3, 4, 5, 3
+    q = rng.normal(size=(n, nh, c))
+    win = O.rope(rng.normal(size=(n, c)), np.arange(n, dtype=float), r, 1000.0)
+    comp = O.rope(rng.normal(size=(n // m, c)), m * np.arange(n // m, dtype=float), r, 1000.0)
+    sink = rng.normal(size=nh)
+    idx = np.full((n, k), -1)
+    for t in range(n):
+        v = (t + 1) // m
+        sel = rng.permutation(v)[:k]
+        idx[t, :len(sel)] = sel
+    kw = dict(qk_norm=True, eps=1e-6, rope_dims=r, theta=1000.0, store="f64")
+    sp = O.sparse_mqa_prefill(q, win, comp, idx, sink, n_win, 0.3, **kw)
+    de = O.dense_mqa_prefill(q, win, comp, sink, m, n_win, 0.3, **kw)
+    for t in (0, 3, 4, 17, n - 1):
+        wr = win[O.window_range(t, n_win)]
+        sel = [s for s in idx[t] if s >= 0]
+        a = O.attend_decode_row(q[t], t, wr, comp[sel], sink, 0.3, **kw)
+        np.testing.assert_allclose(a, sp[t], rtol=0, atol=1e-13)
+        b = O.attend_decode_row(q[t], t, wr, comp[: (t + 1) // m], sink, 0.3, **kw)
+        np.testing.assert_allclose(b, de[t], rtol=0, atol=1e-13)
+
+
+def test_prenorm_rounding_worked_example():
+    """A17: the pooled value is rounded to the storage type before its
+    RMSNorm; in this example the cast changes the stored bf16 value."""
+    g = GOLD["prenorm_rounding"]
+    x = np.array([g["x"]])
+    got = O.entry_epilogue(x, [0.0], True, g["eps"], 0, 10000.0, g["store"])
+    np.testing.assert_array_equal(got[0], g["expected"])
+    no_cast = O.round_bf16(O.rms_norm(x, g["eps"]))
+    np.testing.assert_array_equal(no_cast[0], g["expected_without_prenorm_rounding"])
+
+
+def test_prenorm_rounding_reaches_entries_and_window_rows():
+    """Entries and window rows both pass through the pre-norm rounding: with
+    identity projections they equal the epilogue of the bf16-rounded input,
+    which differs from the single-rounding result on these inputs."""
+    x = np.array([[1.00390625, 0.0], [1.01171875, 0.2], [0.75, -1.0]])
+    win = O.window_rows(x, np.eye(2), eps=1.0, store="bf16")
+    ref = O.round_bf16(O.rms_norm(O.round_bf16(x), 1.0))
+    np.testing.assert_array_equal(win, ref)
+    assert np.any(win != O.round_bf16(O.rms_norm(x, 1.0)))
+    comp = O.compress_prefill(x, np.eye(2), np.zeros((2, 2)), np.zeros((1, 2)), 1, False,
+                              eps=1.0, store="bf16")
+    np.testing.assert_array_equal(comp, ref)
+
+
 # --------------------------------------------------------- decode (OD)
 @pytest.mark.parametrize("overlap,m", [(False, 4), (True, 4), (False, 8), (True, 3)])
 def test_stateful_decode_equals_prefill(overlap, m):
