@@ -284,14 +284,20 @@ __global__ __launch_bounds__(512, 1) void proj_gemm_bf16_kernel(
 // ===========================================================================
 // Row epilogue shared by entries, window rows and decode emission: a group of
 // G = c/2 threads owns one row of width c, thread j the channel pair
-// (2j, 2j+1).  RMSNorm (unit weight) over the row, then RoPE of the last r
-// channels at `pos` ([R] 2.3.3; pairs are adjacent channels).
+// (2j, 2j+1).  The pooled (or projected) values are first rounded to the
+// storage type T, as [A] Compressor casts the pooled entry to the model dtype
+// before its norm (and the attention's wkv is a model-dtype linear layer);
+// then RMSNorm (unit weight) over the row, then RoPE of the last r channels
+// at `pos` ([R] 2.3.3; pairs are adjacent channels).  The caller rounds the
+// result to T once more at store.
 // `red` is LDS scratch of at least (blockDim / 64) floats, used when G > 64.
 // Every thread of the block must call this (it may synchronise).
 // ===========================================================================
-template <int G>
+template <class T, int G>
 CSA_DEV void row_finish(float& v0, float& v1, int j, int c, int64_t pos, int qk_norm, float eps,
                         int r, float theta, float* red) {
+  v0 = T::f(T::cvt(v0));
+  v1 = T::f(T::cvt(v1));
   if (qk_norm) {
     float s = v0 * v0 + v1 * v1;
     if (G <= 64) {
@@ -383,7 +389,7 @@ __global__ __launch_bounds__(256) void pool_entries_kernel(
     v0 = a0 / s0;
     v1 = a1 / s1;
   }
-  row_finish<G>(v0, v1, j, c, (int64_t)m * (pos0 / m + i), qk_norm, eps, r, theta, red);
+  row_finish<T, G>(v0, v1, j, c, (int64_t)m * (pos0 / m + i), qk_norm, eps, r, theta, red);
   if (live) {
     T::st(out, i * c + 2 * j, v0);
     T::st(out, i * c + 2 * j + 1, v1);
@@ -407,7 +413,7 @@ __global__ __launch_bounds__(256) void window_rows_kernel(
     v0 = v.x;
     v1 = v.y;
   }
-  row_finish<G>(v0, v1, j, c, pos0 + t, qk_norm, eps, r, theta, red);
+  row_finish<T, G>(v0, v1, j, c, pos0 + t, qk_norm, eps, r, theta, red);
   if (live) {
     if (out) {
       T::st(out, t * c + 2 * j, v0);
@@ -613,7 +619,7 @@ __global__ __launch_bounds__(256) void decode_update_kernel(
     }
   }
   if (emit) {  // uniform across the block
-    row_finish<G>(e0, e1, j, c, (int64_t)m * blk, qk_norm, eps, r, theta, red);
+    row_finish<T, G>(e0, e1, j, c, (int64_t)m * blk, qk_norm, eps, r, theta, red);
     if (live && blk < max_entries) {
       typename T::S* dst = cache + em.row(b, blk, max_entries) * c;
       T::st(dst, 2 * j, e0);
@@ -622,7 +628,7 @@ __global__ __launch_bounds__(256) void decode_update_kernel(
   }
   if (has_win) {
     float v0 = wn.x, v1 = wn.y;
-    row_finish<G>(v0, v1, j, c, pos, qk_norm, eps, r, theta, red);
+    row_finish<T, G>(v0, v1, j, c, pos, qk_norm, eps, r, theta, red);
     if (live) {
       typename T::S* dst = ring + ((int64_t)b * n_win + pos % n_win) * c;
       T::st(dst, 2 * j, v0);

@@ -19,26 +19,82 @@ def bf16_ulp(x):
 BF16_ABS_SLACK = 1e-5
 
 
-def assert_stored_close(gpu, ref, dtype, what, atol_f32=3e-5, unrounded=None):
-    """Stored entries/rows (unit-RMS after QK-RMSNorm): fp32 within atol_f32;
-    bf16 within one bf16 ulp of the oracle value (itself rounded to bf16) plus
-    BF16_ABS_SLACK.  The slack covers fp32 accumulation error before the
+def bf16_midpoint_dist(x):
+    """Distance from x to the nearest point halfway between two adjacent
+    bfloat16 values (where round-to-nearest changes its decision)."""
+    x = np.abs(np.asarray(x, np.float64))
+    u = bf16_ulp(x)
+    frac = np.mod(x / u, 1.0)
+    return np.abs(frac - 0.5) * u
+
+
+def _pair_max(a, rope_dims):
+    """For the last rope_dims channels (adjacent pairs rotated together),
+    the larger of each pair's two values; other channels unchanged."""
+    a = np.array(a, np.float64, copy=True)
+    if rope_dims:
+        c = a.shape[-1]
+        t = a[..., c - rope_dims:].reshape(a.shape[:-1] + (rope_dims // 2, 2))
+        t[:] = t.max(axis=-1, keepdims=True)
+        a[..., c - rope_dims:] = t.reshape(a.shape[:-1] + (rope_dims,))
+    return a
+
+
+def assert_stored_close(gpu, ref, dtype, what, atol_f32=3e-5, unrounded=None, prenorm=None,
+                        rope_dims=0):
+    """Stored entries / window rows (unit-RMS after QK-RMSNorm).
+
+    fp32: within atol_f32 (fp32 accumulation of the projection and pooling).
+
+    bf16: within one bf16 ulp of the oracle value (itself rounded to bf16)
+    plus BF16_ABS_SLACK.  The slack covers fp32 accumulation error before the
     rounding: a value that nearly cancels (|x| ~ 1e-5) carries the same
-    ~2e-6 absolute fp32 error as any other, which is many bf16 ulps of x."""
+    ~2e-6 absolute fp32 error as any other, which is many bf16 ulps of x.
+
+    The row is rounded twice, before its RMSNorm and at store.  Where the
+    GPU's fp32 pre-norm value and the oracle's fp64 one straddle a bf16
+    rounding midpoint, the first rounding differs by one pre-norm ulp, i.e.
+    by at most 2^-7 |y| after the norm (y the stored value), and the store
+    rounding adds at most one ulp of y: such elements may differ by up to
+    ulp(y) + 2^-7 |y|.  In the last rope_dims channels RoPE mixes each
+    adjacent pair, so a flip in either member moves both by up to 2^-7 times
+    the pair's norm.  These elements are allowed only as the rare event this
+    is (at most 1 % of the elements, plus 8), and, when the oracle's pre-norm
+    values are given, only where that value (or, in a rotated pair, either
+    member's) lies within 1e-4 * max(1, |x|) of a midpoint (the fp32
+    accumulation error of the pre-norm value)."""
     g, r = f64(gpu) if isinstance(gpu, torch.Tensor) else gpu, ref
     assert g.shape == r.shape, (what, g.shape, r.shape)
     err = np.abs(g - r)
     if dtype == "f32":
         bad = err > atol_f32
     else:
-        bad = err > bf16_ulp(r) * 1.0001 + BF16_ABS_SLACK
+        tight = bf16_ulp(r) * 1.0001 + BF16_ABS_SLACK
+        mag = np.abs(r)
+        if rope_dims:
+            c = r.shape[-1]
+            pr = r[..., c - rope_dims:].reshape(r.shape[:-1] + (rope_dims // 2, 2))
+            pn_ = np.repeat(np.sqrt((pr * pr).sum(-1)), 2, axis=-1)
+            mag = mag.copy()
+            mag[..., c - rope_dims:] = pn_
+        wide = bf16_ulp(r) * 1.0001 + 2.0 ** -7 * mag * 1.01 + BF16_ABS_SLACK
+        flip = (err > tight) & (err <= wide)
+        if prenorm is not None:
+            pn = np.asarray(prenorm, np.float64).reshape(r.shape)
+            near = (bf16_midpoint_dist(pn) <= 1e-4 * np.maximum(1.0, np.abs(pn))).astype(np.float64)
+            flip &= _pair_max(near, rope_dims) > 0
+        nflip = int(flip.sum())
+        assert nflip <= 0.01 * r.size + 8, (
+            f"{what}: {nflip} of {r.size} elements need the pre-norm rounding allowance")
+        bad = (err > tight) & ~flip
     if bad.any():
         where = np.argwhere(bad)[:5]
         detail = []
         for w in where:
             w = tuple(w)
             u = "" if unrounded is None else f" unrounded {unrounded[w]!r}"
-            detail.append(f"at {w}: gpu {g[w]!r} oracle {r[w]!r}{u}")
+            pn = "" if prenorm is None else f" pre-norm {np.asarray(prenorm).reshape(r.shape)[w]!r}"
+            detail.append(f"at {w}: gpu {g[w]!r} oracle {r[w]!r}{u}{pn}")
         raise AssertionError(f"{what}: {bad.sum()} of {bad.size} elements off, max err "
                              f"{err.max():.3g}; " + "; ".join(detail))
     return float(err.max())

@@ -271,6 +271,40 @@ def test_paged_calls_reject(lib):
                                           _p(), _p(), 8, None) == -3
 
 
+def test_fp4_paged_calls_reject(lib):
+    """The two FP4 paged calls reject a missing page table, a page size below
+    one, a capacity past 32-bit entry numbers and missing pools, before
+    anything is enqueued."""
+    f = L.Fp4Desc(2, 64, L.CSA_BF16)
+    q = lib.csa_indexer_fp4_quant_decode_paged
+    assert q(ctypes.byref(f), _p(), 64, _p(), 4, _p(), _p(), None, 32, None) == -1
+    assert q(ctypes.byref(f), _p(), 64, _p(), 4, _p(), _p(), _p(), 0, None) == -1
+    assert q(ctypes.byref(f), _p(), 64, _p(), 4, _p(), _p(), _p(), -2, None) == -1
+    assert q(ctypes.byref(f), _p(), 1 << 31, _p(), 4, _p(), _p(), _p(), 32, None) == -2
+    assert q(ctypes.byref(f), None, 64, _p(), 4, _p(), _p(), _p(), 32, None) == -1
+    assert q(ctypes.byref(f), _p(), 64, _p(), 4, None, _p(), _p(), 32, None) == -1
+    assert q(ctypes.byref(f), _p(), 64, _p(), 4, _p(), None, _p(), 32, None) == -1
+    assert q(None, _p(), 64, _p(), 4, _p(), _p(), _p(), 32, None) == -1
+    t = lib.csa_index_topk_decode_fp4_paged
+    dd = L.IndexDesc(0, 2, 16, 64, 4, 8, L.CSA_BF16, 100)
+    assert t(ctypes.byref(dd), _p(), _p(), _p(), _p(), _p(), None, 32, _p(), _p(), _p(),
+             1 << 40, None) == -1
+    assert t(ctypes.byref(dd), _p(), _p(), _p(), _p(), _p(), _p(), 0, _p(), _p(), _p(),
+             1 << 40, None) == -1
+    assert t(ctypes.byref(dd), _p(), _p(), _p(), None, _p(), _p(), 32, _p(), _p(), _p(),
+             1 << 40, None) == -1
+    assert t(ctypes.byref(dd), _p(), _p(), _p(), _p(), None, _p(), 32, _p(), _p(), _p(),
+             1 << 40, None) == -1
+    assert t(ctypes.byref(dd), _p(), _p(), _p(), _p(), _p(), _p(), 32, _p(), _p(), _p(),
+             8, None) == -3
+    big = L.IndexDesc(0, 2, 16, 64, 4, 8, L.CSA_BF16, 1 << 31)
+    assert t(ctypes.byref(big), _p(), _p(), _p(), _p(), _p(), _p(), 32, _p(), _p(), _p(),
+             1 << 40, None) == -2
+    f32 = L.IndexDesc(0, 2, 16, 64, 4, 8, L.CSA_F32, 100)
+    assert t(ctypes.byref(f32), _p(), _p(), _p(), _p(), _p(), _p(), 32, _p(), _p(), _p(),
+             1 << 40, None) == -2
+
+
 def test_chunked_prefill_rejects(lib):
     """A chunk must start at a block boundary and at a position >= 0."""
     d = L.compress_desc(n=64, d=128, c=128, m=4, pos0=6)

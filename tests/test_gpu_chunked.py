@@ -64,7 +64,7 @@ def test_compress_prefill_chunked(lib, dtype, d, c, m, ov, r, N, cuts):
     if (N - p0) >= m:
         ref = O.compress_prefill(f64(H[:p0 + m]), f64(Wkv).T, f64(Wz).T, f64(ape), m, ov,
                                  rope_dims=r, store=dtype)
-        assert_stored_close(comps[-1][:1], ref[p0 // m:p0 // m + 1], dtype, "chunk entry")
+        assert_stored_close(comps[-1][:1], ref[p0 // m:p0 // m + 1], dtype, "chunk entry", rope_dims=r)
 
 
 # ----------------------------------------------------------------- indexer

@@ -61,10 +61,14 @@ def test_compress_decode_continues_prefill(lib, dtype, d, c, m, ov, r, lens, ste
         Hb = f64(H[b, :N])
         ref = O.compress_prefill(Hb, f64(Wkv).T, f64(Wz).T, f64(ape), m, ov, rope_dims=r, store=dtype)
         if N // m:
-            assert_stored_close(cache[b, : N // m], ref, dtype, f"seq {b} entries")
+            pre = O.pool(O.project(Hb, f64(Wkv).T), O.project(Hb, f64(Wz).T), f64(ape), m, ov)
+            assert_stored_close(cache[b, : N // m], ref, dtype, f"seq {b} entries", prenorm=pre,
+                                rope_dims=r)
         wref = O.window_rows(Hb, f64(Ww).T, rope_dims=r, store=dtype)
+        wpre = O.project(Hb, f64(Ww).T)
         for p in range(max(0, N - n_win), N):
-            assert_stored_close(ring[b, p % n_win][None], wref[p][None], dtype, f"seq {b} ring {p}")
+            assert_stored_close(ring[b, p % n_win][None], wref[p][None], dtype, f"seq {b} ring {p}",
+                                prenorm=wpre[p][None], rope_dims=r)
 
 
 def test_state_init_equals_prefill_of_nothing(lib):

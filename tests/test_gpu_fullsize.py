@@ -55,13 +55,13 @@ def test_csa_prefill_64k_sampled(lib):
         a, b = _block_rows(m, ov, i)
         Hs = f64(t["H"][a:b])
         ref = _oracle_entry(Hs, Wkv, Wz, ape, m, ov, i, r, "bf16")
-        assert_stored_close(pf.comp[i:i + 1], ref[None], "bf16", f"entry {i}")
+        assert_stored_close(pf.comp[i:i + 1], ref[None], "bf16", f"entry {i}", rope_dims=r)
         refI = _oracle_entry(Hs, WIk, WIz, apeI, m, ov, i, 0, "bf16")
         assert_stored_close(pf.kI[i:i + 1], refI[None], "bf16", f"indexer key {i}")
     rows = sorted(set([0, 1, 127, 128, 4095, n // 2, n - 2, n - 1] + list(range(333, n, n // 40))))
     win_ref = np.stack([O.window_rows(f64(t["H"][j:j + 1]), Ww, rope_dims=r, store="bf16", pos0=j)[0]
                         for j in rows])
-    assert_stored_close(pf.win[rows], win_ref, "bf16", "window rows")
+    assert_stored_close(pf.win[rows], win_ref, "bf16", "window rows", rope_dims=r)
     KI = f64(pf.kI)
     idx = pf.idx.cpu().numpy()
     qI, wI = f64(t["qI"][rows]), f64(t["wI"][rows])
@@ -134,17 +134,18 @@ def test_decode_step_sampled(lib, wname, seqs):
         i = vis - 1  # the entry this step emitted
         ref = _oracle_entry(rows_of(*_block_rows(m, ov, i)), f64(g["csa_Wkv"]).T, f64(g["csa_Wz"]).T,
                             f64(g["csa_ape"]), m, ov, i, r, "bf16")
-        assert_stored_close(hd.cache[b, i:i + 1], ref[None], "bf16", f"seq {b} emitted entry")
+        assert_stored_close(hd.cache[b, i:i + 1], ref[None], "bf16", f"seq {b} emitted entry", rope_dims=r)
         refI = _oracle_entry(rows_of(*_block_rows(m, ov, i)), f64(g["WI_kv"]).T, f64(g["WI_z"]).T,
                              f64(g["apeI"]), m, ov, i, 0, "bf16")
         assert_stored_close(hd.kcache[b, i:i + 1], refI[None], "bf16", f"seq {b} emitted key")
         ih = vis_h - 1
         refH = _oracle_entry(rows_of(*_block_rows(mh, 0, ih)), f64(g["hca_Wkv"]).T, f64(g["hca_Wz"]).T,
                              f64(g["hca_ape"]), mh, 0, ih, r, "bf16")
-        assert_stored_close(hd.hcache[b, ih:ih + 1], refH[None], "bf16", f"seq {b} emitted HCA entry")
+        assert_stored_close(hd.hcache[b, ih:ih + 1], refH[None], "bf16", f"seq {b} emitted HCA entry",
+                            rope_dims=r)
         wref = O.window_rows(rows_of(tpos, tpos + 1), f64(g["csa_Wwin"]).T, rope_dims=r, store="bf16",
                              pos0=tpos)
-        assert_stored_close(hd.ring[b, tpos % nw][None], wref, "bf16", f"seq {b} window row")
+        assert_stored_close(hd.ring[b, tpos % nw][None], wref, "bf16", f"seq {b} window row", rope_dims=r)
         # indexer top-k over the whole cache
         sc = O.index_scores(f64(g["qI"][b])[None], f64(g["wI"][b])[None], f64(hd.kcache[b, :vis]), m,
                             t0=tpos)

@@ -108,7 +108,7 @@ def test_compress_decode_paged(lib, d, c, m, ov, r, page, lens, steps):
     ref = O.compress_prefill(f64(H[b, :N]), f64(Wkv).T, f64(Wz).T, f64(ape), m, ov, rope_dims=r,
                              store="bf16")
     got = _gather(pool, table, page, max_e)[b, : N // m]
-    assert_stored_close(got, ref, "bf16", "paged entries")
+    assert_stored_close(got, ref, "bf16", "paged entries", rope_dims=r)
 
 
 # ----------------------------------------------------------------- indexer

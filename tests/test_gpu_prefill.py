@@ -51,10 +51,12 @@ def test_compress_prefill(lib, dtype, n, d, c, m, ov, r):
     ref = O.compress_prefill(Hh, Wkvh, Wzh, apeh, m, ov, rope_dims=r, store=dtype)
     assert res["comp"].shape == (n // m, c)
     if n // m:
-        assert_stored_close(res["comp"], ref, dtype, "entries")
+        pre = O.pool(O.project(Hh, Wkvh), O.project(Hh, Wzh), apeh, m, ov)
+        assert_stored_close(res["comp"], ref, dtype, "entries", prenorm=pre, rope_dims=r)
     win_ref = O.window_rows(Hh, Wwh, rope_dims=r, store=dtype)
     assert_stored_close(res["win"], win_ref, dtype, "window rows",
-                        unrounded=O.window_rows(Hh, Wwh, rope_dims=r, store="f64"))
+                        unrounded=O.window_rows(Hh, Wwh, rope_dims=r, store="f64"),
+                        prenorm=O.project(Hh, Wwh), rope_dims=r)
     ring = f64(res["ring"])
     for t in range(max(0, n - 128), n):
         np.testing.assert_array_equal(ring[t % 128], f64(res["win"])[t])
