@@ -14,7 +14,8 @@
  * ----------------------------------------
  *  - Every tensor argument is a DEVICE pointer to a row-major, contiguous
  *    buffer that the caller allocates and frees.  The library allocates and
- *    frees nothing, never synchronises, and keeps no mutable global state.
+ *    frees nothing, never synchronises, and keeps no mutable global state
+ *    (beyond the per-device scratch of csa_index_topk_decode_noalloc).
  *  - Element types: `dtype` (CSA_F32 or CSA_BF16) applies to hidden states,
  *    weights, queries, indexer queries/weights, caches and outputs.  The
  *    position biases `ape`, the sink logits and the compressor decode state
@@ -249,6 +250,30 @@ int csa_index_topk_prefill(const csa_index_desc* desc, const void* qI, const voi
 int csa_index_topk_decode(const csa_index_desc* desc, const void* qI, const void* wI,
                           const void* KI_cache, const int64_t* pos, int32_t* idx_out, void* ws,
                           size_t ws_bytes, void* stream);
+
+/* csa_index_topk_decode_noalloc -- csa_index_topk_decode for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments and result, with
+ * no workspace: the scratch is a library-owned static device array of
+ * csa_noalloc_scratch_bytes() (32 MiB) bytes, one per GPU, held until the
+ * process ends.  A descriptor whose csa_workspace_bytes(
+ * CSA_ENTRY_INDEX_TOPK_DECODE, desc) exceeds that is rejected with
+ * CSA_ERR_WORKSPACE before anything is enqueued (32 sequences of 32768
+ * entries, or 4 of 262144, need 22.4 MiB).  The array's device address is
+ * looked up on the first call on each device (CSA_ERR_HIP if that fails).
+ * Its leading histogram bytes must be zero when a call starts: each call
+ * leaves them zero, and a call that needs more of them than the previous
+ * call on that GPU left zero clears them first with a fill kernel on
+ * `stream` (no memset, so the call can be captured).  Every call on a GPU
+ * shares the array, so calls that overlap on one GPU (unordered streams, or
+ * host threads racing on different streams) race; calls ordered on one
+ * stream do not.  The library allocates nothing and calls no allocator. */
+int csa_index_topk_decode_noalloc(const csa_index_desc* desc, const void* qI, const void* wI,
+                                  const void* KI_cache, const int64_t* pos, int32_t* idx_out,
+                                  void* stream);
+
+/* Bytes of the per-device scratch csa_index_topk_decode_noalloc runs in. */
+size_t csa_noalloc_scratch_bytes(void);
 
 /* ------------------------------------------------------------------------
  * The quantised indexer path: rotation + FP4 ([A] Compressor with rotate =

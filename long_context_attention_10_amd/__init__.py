@@ -31,7 +31,8 @@ EXPORTED = ["csa_compress_prefill", "csa_compress_decode", "csa_state_bytes", "c
             "csa_workspace_zero_bytes", "csa_status_string", "csa_abi_version",
             "csa_compress_decode_paged", "csa_index_topk_decode_paged",
             "csa_sparse_mqa_decode_paged", "hca_dense_mqa_decode_paged",
-            "csa_indexer_fp4_quant_decode_paged", "csa_index_topk_decode_fp4_paged"]
+            "csa_indexer_fp4_quant_decode_paged", "csa_index_topk_decode_fp4_paged",
+            "csa_index_topk_decode_noalloc", "csa_noalloc_scratch_bytes"]
 
 
 class CompressDesc(ctypes.Structure):
@@ -121,9 +122,12 @@ def load(path: str = LIB_PATH):
     lib.hca_dense_mqa_decode_paged.argtypes = [P] * 5 + [I32] + [P] * 4 + [S, P]
     lib.csa_indexer_fp4_quant_decode_paged.argtypes = [P, P, ctypes.c_int64, P, I, P, P, P, I32, P]
     lib.csa_index_topk_decode_fp4_paged.argtypes = [P] * 7 + [I32] + [P] * 3 + [S, P]
+    lib.csa_index_topk_decode_noalloc.argtypes = [P] * 7
+    lib.csa_noalloc_scratch_bytes.restype = S
+    lib.csa_noalloc_scratch_bytes.argtypes = []
     for f in EXPORTED:
         if f not in ("csa_abi_version", "csa_status_string", "csa_workspace_bytes",
-                     "csa_workspace_zero_bytes", "csa_state_bytes"):
+                     "csa_workspace_zero_bytes", "csa_state_bytes", "csa_noalloc_scratch_bytes"):
             getattr(lib, f).restype = I
     _lib = lib
     return lib
@@ -438,6 +442,24 @@ def csa_index_topk_decode(qI, wI, KI_cache, pos, m, k, out=None):
     if st != 0:
         _WS_ZERO.pop((str(qI.device), "index_dec"), None)
     _check(st, "csa_index_topk_decode")
+    return out
+
+
+def csa_index_topk_decode_noalloc(qI, wI, KI_cache, pos, m, k, out=None):
+    """csa_index_topk_decode on the library's own per-device scratch (no
+    workspace; `out` may be preallocated so that the call allocates nothing)."""
+    lib = load()
+    B, hI, cI = qI.shape
+    ne = KI_cache.shape[1]
+    _expect(KI_cache, (B, ne, cI), qI.dtype, "KI_cache")
+    _expect(pos, (B,), torch.int64, "pos")
+    desc = IndexDesc(0, B, hI, cI, m, k, _dt(qI), ne)
+    if out is None:
+        out = torch.empty((B, k), dtype=torch.int32, device=qI.device)
+    st = lib.csa_index_topk_decode_noalloc(ctypes.byref(desc), _ptr(qI), _ptr(wI),
+                                           _ptr(KI_cache), _ptr(pos), _ptr(out),
+                                           _stream(qI.device))
+    _check(st, "csa_index_topk_decode_noalloc")
     return out
 
 

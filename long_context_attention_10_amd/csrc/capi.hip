@@ -380,6 +380,18 @@ int csa_index_topk_decode(const csa_index_desc* d, const void* qI, const void* w
   return index_topk_decode(d, qI, wI, KI_cache, pos, idx_out, ws, ws_bytes, stream, EntryMap());
 }
 
+int csa_index_topk_decode_noalloc(const csa_index_desc* d, const void* qI, const void* wI,
+                                  const void* KI_cache, const int64_t* pos, int32_t* idx_out,
+                                  void* stream) {
+  int s = check_index(d, true);
+  if (s) return s;
+  if (index_decode_ws_bytes(*d) > noalloc_scratch_bytes()) return CSA_ERR_WORKSPACE;
+  if (!qI || !wI || !KI_cache || !pos || !idx_out) return CSA_ERR_INVALID_ARG;
+  return index_topk_decode_noalloc(*d, qI, wI, KI_cache, pos, idx_out, (hipStream_t)stream);
+}
+
+size_t csa_noalloc_scratch_bytes(void) { return noalloc_scratch_bytes(); }
+
 int csa_index_topk_decode_paged(const csa_index_desc* d, const void* qI, const void* wI,
                                 const void* KI_pool, const int32_t* page_table,
                                 int32_t page_entries, const int64_t* pos, int32_t* idx_out,

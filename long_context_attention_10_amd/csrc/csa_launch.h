@@ -98,6 +98,13 @@ hipError_t launch_index_topk_decode(const csa_index_desc& d, const void* qI, con
                                     const void* KI, const int64_t* pos, int32_t* idx_out,
                                     void* ws, hipStream_t st, EntryMap em = EntryMap());
 
+// The no-allocation variant (noalloc.hip): the same launches on a
+// library-owned static scratch of noalloc_scratch_bytes() per device.
+size_t noalloc_scratch_bytes();
+int index_topk_decode_noalloc(const csa_index_desc& d, const void* qI, const void* wI,
+                              const void* KI, const int64_t* pos, int32_t* idx_out,
+                              hipStream_t st);
+
 // ------------------------------------------------------------- attention
 enum AttnMode { ATTN_SPARSE = 0, ATTN_DENSE = 1 };
 

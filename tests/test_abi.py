@@ -326,3 +326,20 @@ def test_chunked_prefill_rejects(lib):
     assert L.workspace_zero_bytes("index_topk_prefill", di) == 0
     a = L.attn_desc(n=8, nh=8, c=128, k=4, t0=-1)
     assert lib.csa_sparse_mqa_prefill(ctypes.byref(a), *([_p()] * 6), None, 0, None) == -1
+
+
+def test_noalloc_topk_rejects(lib):
+    """The no-allocation top-k rejects descriptors whose scratch exceeds the
+    library's static array, and null pointers, before touching the GPU."""
+    assert lib.csa_noalloc_scratch_bytes() == 32 << 20
+    ok = L.IndexDesc(0, 32, 16, 64, 4, 512, L.CSA_BF16, 32768)
+    assert L.workspace_bytes("index_topk_decode", ok) <= lib.csa_noalloc_scratch_bytes()
+    big = L.IndexDesc(0, 64, 16, 64, 4, 512, L.CSA_BF16, 32768)
+    assert L.workspace_bytes("index_topk_decode", big) > lib.csa_noalloc_scratch_bytes()
+    f = lib.csa_index_topk_decode_noalloc
+    assert f(ctypes.byref(big), _p(), _p(), _p(), _p(), _p(), None) == -3
+    assert f(ctypes.byref(ok), None, _p(), _p(), _p(), _p(), None) == -1
+    assert f(ctypes.byref(ok), _p(), _p(), _p(), None, _p(), None) == -1
+    assert f(None, _p(), _p(), _p(), _p(), _p(), None) == -1
+    bad = L.IndexDesc(0, 2, 16, 64, 4, 0, L.CSA_BF16, 100)
+    assert f(ctypes.byref(bad), _p(), _p(), _p(), _p(), _p(), None) in (-1, -2)
