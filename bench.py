@@ -241,6 +241,56 @@ def time_region(fn, steps, warmup, flush=None):
     return times
 
 
+def time_ahead(fn, steps, warmup, pre):
+    """Per-step GPU times (ms) of fn, each step enqueued after pre() on the
+    current stream.  The host enqueues every iteration before it reads any
+    event, so no step waits for the host to launch its kernels; pre() (a
+    cache flush, or a GPU sleep for warm steps) gives the host the time to
+    run ahead."""
+    for _ in range(warmup):
+        pre()
+        fn()
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(steps):
+        pre()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        ev.append((s, e))
+    torch.cuda.synchronize()
+    return [s.elapsed_time(e) for s, e in ev]
+
+
+class CacheFlush:
+    """Evicts the step's data from the caches before a cold step.
+
+    clean(): write 1 GiB, then read 512 MiB of another buffer, so that the
+    256 MiB last-level cache holds clean lines of neither buffer and the
+    write-back of the flush's own dirty lines happens before the step, not
+    inside it.  dirty(): the write alone (the step then also pays that
+    write-back).  warm(): evicts nothing.  Each ends with a GPU sleep of
+    about 0.5 ms, which touches no memory and gives the host the time to
+    enqueue the next step before the GPU reaches it."""
+
+    def __init__(self, dev):
+        self.w = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        self.r = torch.ones(1 << 27, dtype=torch.float32, device=dev)
+
+    def clean(self):
+        self.w.random_(0, 255)
+        self.r.sum()
+        torch.cuda._sleep(1000000)
+
+    def dirty(self):
+        self.w.random_(0, 255)
+        torch.cuda._sleep(1000000)
+
+    def warm(self):
+        torch.cuda._sleep(1000000)
+
+
 def graph_of(fn):
     """Capture fn (after a warm call that sizes every workspace) in a HIP graph."""
     fn()
@@ -423,27 +473,32 @@ class HybridDecode:
         torch.cuda.empty_cache()
 
     def step(self, streams=True):
-        """One decode step.  Its three chains are independent until the sparse
-        attention: (indexer compressor -> top-k), (CSA compressor) and (HCA
-        compressor -> dense attention); with `streams` the first two run on
-        two forked side streams (default priority) and the HCA chain on the
-        current stream, which then joins both and runs the sparse attention.
-        Each chain has its own workspaces."""
+        """One decode step.  Its chains are independent until the sparse
+        attention: (indexer compressor -> selection), (scoring of the cached
+        indexer keys -> selection), (CSA compressor) and (HCA compressor ->
+        dense attention).  The scoring reads only keys that precede this
+        step, so it starts with the step, beside the compressors.  With
+        `streams` each compressor has a forked stream (the HCA chain runs on
+        the current one); the scoring's stream then waits for the indexer
+        compressor's, selects, waits for the CSA compressor's and runs the
+        sparse attention; the current stream joins the others at the end.
+        The compressors are enqueued first, so that their projections start
+        with the step.  Each chain has its own workspaces."""
         c, g = self.cfg, self.g
         m, ov, r = c["m"], c["overlap"], c["rope_dims"]
         main = torch.cuda.current_stream()
         if streams:
-            if self.side is None:
-                self.side = (torch.cuda.Stream(), torch.cuda.Stream())
-            sb, sc = self.side
+            if self.side is None or len(self.side) < 3:
+                self.side = (torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream())
+            sb, sc, sd = self.side
             sb.wait_stream(main)
             sc.wait_stream(main)
+            sd.wait_stream(main)
         else:
-            sb = sc = main
+            sb = sc = sd = main
         with torch.cuda.stream(sb):
             L.csa_compress_decode(self.h, self.pos, g["WI_kv"], g["WI_z"], g["apeI"], m, ov, self.sti,
                                   self.kcache, ws_slot="decode_proj_idx")
-            L.csa_index_topk_decode(g["qI"], g["wI"], self.kcache, self.pos, m, c["k"], out=self.idx)
         with torch.cuda.stream(sc):
             L.csa_compress_decode(self.h, self.pos, g["csa_Wkv"], g["csa_Wz"], g["csa_ape"], m, ov,
                                   self.st, self.cache, W_win=g["csa_Wwin"], win_ring=self.ring,
@@ -451,13 +506,22 @@ class HybridDecode:
         L.csa_compress_decode(self.h, self.pos, g["hca_Wkv"], g["hca_Wz"], g["hca_ape"],
                               c["m_hca"], 0, self.sth, self.hcache, W_win=g["hca_Wwin"],
                               win_ring=self.hring, rope_dims=r, ws_slot="decode_proj_hca")
+        with torch.cuda.stream(sd):
+            L.csa_index_topk_decode_score(g["qI"], g["wI"], self.kcache, self.pos, m, c["k"])
+            if streams:
+                sd.wait_stream(sb)
+            L.csa_index_topk_decode_select(g["qI"], g["wI"], self.kcache, self.pos, m, c["k"],
+                                           out=self.idx)
+            if streams:
+                sd.wait_stream(sc)
+            L.csa_sparse_mqa_decode(g["csa_q"], self.ring, self.cache, self.idx, self.pos,
+                                    g["csa_sink"], rope_dims=r, out=self.out_c)
         L.hca_dense_mqa_decode(g["hca_q"], self.hring, self.hcache, self.pos, g["hca_sink"],
                                c["m_hca"], rope_dims=r, out=self.out_h)
         if streams:
             main.wait_stream(sb)
             main.wait_stream(sc)
-        L.csa_sparse_mqa_decode(g["csa_q"], self.ring, self.cache, self.idx, self.pos, g["csa_sink"],
-                                rope_dims=r, out=self.out_c)
+            main.wait_stream(sd)
 
     def step_fp4(self, streams=True):
         """The same step with the FP4 indexer path: q^I is rotated and
@@ -472,8 +536,8 @@ class HybridDecode:
         main = torch.cuda.current_stream()
         if streams:
             if self.side is None:
-                self.side = (torch.cuda.Stream(), torch.cuda.Stream())
-            sb, sc = self.side
+                self.side = (torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream())
+            sb, sc = self.side[:2]
             sb.wait_stream(main)
             sc.wait_stream(main)
         else:
@@ -531,8 +595,8 @@ class HybridDecode:
         main = torch.cuda.current_stream()
         if streams:
             if self.side is None:
-                self.side = (torch.cuda.Stream(), torch.cuda.Stream())
-            sb, sc = self.side
+                self.side = (torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream())
+            sb, sc = self.side[:2]
             sb.wait_stream(main)
             sc.wait_stream(main)
         else:
@@ -748,10 +812,11 @@ def main():
     torch.cuda.empty_cache()
     if not a.no_decode:
         dec = {}
-        flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        cf = CacheFlush(dev)
+        flush = cf.clean
 
-        def flush():
-            flush_buf.random_(0, 255)  # overwrites the 256 MiB last-level cache
+        def med_us(ts):
+            return float(np.median(ts)) * 1e3
 
         for wname in ("decode_b32_128k_bf16", "decode_b4_1m_bf16"):
             dc = configs.get(wname)
@@ -759,22 +824,23 @@ def main():
             hd = HybridDecode(dc, dev)
             print(f"[bench] timing {wname}", file=sys.stderr, flush=True)
             nd = max(20, a.steps)  # decode steps are short: at least 20 timed
-            tt = time_region(hd.step, nd, 3, flush=flush)
-            tw = time_region(hd.step, nd, 3)
+            tt = time_ahead(hd.step, nd, 3, cf.clean)
+            tw = time_ahead(hd.step, nd, 3, cf.warm)
+            td = time_ahead(hd.step, nd, 3, cf.dirty)
             g = graph_of(hd.step)  # the same step, launched as one HIP graph
-            tg = time_region(g.replay, nd, 3, flush=flush)
-            tgw = time_region(g.replay, nd, 3)
-            us = float(np.median(tt)) * 1e3
-            ug = float(np.median(tg)) * 1e3
+            tg = time_ahead(g.replay, nd, 3, cf.clean)
+            tgw = time_ahead(g.replay, nd, 3, cf.warm)
+            us, ug = med_us(tt), med_us(tg)
             byts = hd.algorithmic_bytes()
             dec[wname] = {"us_per_step": us, "us_per_token": us / dc["batch"],
                           "us_per_step_p10_p90": [float(np.percentile(tt, 10)) * 1e3,
                                                   float(np.percentile(tt, 90)) * 1e3],
                           "graph_us_per_step_p10_p90": [float(np.percentile(tg, 10)) * 1e3,
                                                         float(np.percentile(tg, 90)) * 1e3],
-                          "us_per_step_warm_cache": float(np.mean(tw)) * 1e3,
+                          "us_per_step_warm_cache": med_us(tw),
+                          "us_per_step_dirty_flush": med_us(td),
                           "graph_us_per_step": ug, "graph_us_per_token": ug / dc["batch"],
-                          "graph_us_per_step_warm_cache": float(np.mean(tgw)) * 1e3,
+                          "graph_us_per_step_warm_cache": med_us(tgw),
                           "batch": dc["batch"], "ctx": dc["ctx"], "k": dc["k"],
                           "hbm_bytes_algorithmic": byts,
                           "hbm_frac": byts / (us * 1e-6) / PEAK_HBM,
@@ -795,15 +861,15 @@ def main():
             def topk_fp4():
                 L.csa_index_topk_decode_fp4(qc, qe, g_["wI"], kc, ke, hd.pos, c_["m"], c_["k"],
                                             out=idx4)
-            t16 = float(np.median(time_region(graph_of(topk_bf16).replay, nd, 3, flush=flush))) * 1e3
-            t4 = float(np.median(time_region(graph_of(topk_fp4).replay, nd, 3, flush=flush))) * 1e3
+            t16 = med_us(time_ahead(graph_of(topk_bf16).replay, nd, 3, flush))
+            t4 = med_us(time_ahead(graph_of(topk_fp4).replay, nd, 3, flush))
             topk_bf16()
             topk_fp4()
             pos_ = torch.searchsorted(idx4, hd.idx).clamp_(max=idx4.shape[1] - 1)
             hit = (idx4.gather(1, pos_) == hd.idx) & (hd.idx >= 0)
-            tstep = time_region(hd.step_fp4, nd, 3, flush=flush)
+            tstep = time_ahead(hd.step_fp4, nd, 3, flush)
             gf = graph_of(hd.step_fp4)
-            tgs = time_region(gf.replay, nd, 3, flush=flush)
+            tgs = time_ahead(gf.replay, nd, 3, flush)
             del gf
             dec[wname]["fp4_indexer"] = {
                 "us_per_step": float(np.median(tstep)) * 1e3,
@@ -815,15 +881,15 @@ def main():
             # the same step over caches in shuffled pages of 128 raw tokens
             hd.paginate(128)
             gp = graph_of(hd.step_paged)
-            tgp = time_region(gp.replay, nd, 3, flush=flush)
-            tgpw = time_region(gp.replay, nd, 3)
+            tgp = time_ahead(gp.replay, nd, 3, flush)
+            tgpw = time_ahead(gp.replay, nd, 3, cf.warm)
             del gp
             dec[wname]["paged"] = {
                 "page_tokens": 128,
                 "page_entries": {"csa": hd.pg["cache"][2], "indexer": hd.pg["kcache"][2],
                                  "hca": hd.pg["hcache"][2]},
                 "graph_us_per_step": float(np.median(tgp)) * 1e3,
-                "graph_us_per_step_warm_cache": float(np.mean(tgpw)) * 1e3}
+                "graph_us_per_step_warm_cache": med_us(tgpw)}
             del hd
             torch.cuda.empty_cache()
         rec["decode"] = dec

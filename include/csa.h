@@ -29,13 +29,10 @@
  *    [c, 2c) the block itself ([A] Compressor).
  *  - All work is enqueued on `stream` (a hipStream_t; NULL = default stream)
  *    and is asynchronous.  `ws` is caller-owned scratch of at least
- *    csa_workspace_bytes(...) bytes (may be NULL when that is 0).  Its
- *    leading csa_workspace_zero_bytes(...) bytes must be zero when a call
- *    starts; every call leaves them zero again, so they need clearing only
- *    when the buffer is new, after the caller wrote to it, after a failed
- *    call, or before a call whose zero-byte count exceeds the previous one's
- *    on that buffer (only the decode top-k calls, and csa_index_topk_prefill
- *    on rows of more than 16384 visible entries, have such bytes).
+ *    csa_workspace_bytes(...) bytes (may be NULL when that is 0).  No entry
+ *    point carries state between calls in its workspace, so it needs no
+ *    clearing (csa_workspace_zero_bytes returns 0 for every entry and is
+ *    kept for callers written against earlier versions of this header).
  *  - Return value: CSA_OK or a negative csa_status.  All argument checks run
  *    on the host before anything is enqueued, so a failing call has no side
  *    effect.  A fault inside a kernel surfaces at the caller's next stream
@@ -229,8 +226,7 @@ int csa_state_init(const csa_compress_desc* desc, float* state, void* stream);
  * t0 + t and sees s < floor((t0+t+1)/m).  When the last row sees more than
  * 16384 entries the rows are selected by the decode top-k, in batches of
  * rows sharing KI (same result definition; fp32 scores only, else
- * CSA_ERR_UNSUPPORTED); the workspace then has leading zero bytes
- * (csa_workspace_zero_bytes(CSA_ENTRY_INDEX_TOPK_PREFILL, desc)).
+ * CSA_ERR_UNSUPPORTED).
  */
 int csa_index_topk_prefill(const csa_index_desc* desc, const void* qI, const void* wI,
                            const void* KI, int32_t* idx_out, void* ws, size_t ws_bytes,
@@ -244,12 +240,35 @@ int csa_index_topk_prefill(const csa_index_desc* desc, const void* qI, const voi
  *   KI_cache [B, n_entries, cI]        dtype
  *   pos      [B]                       int64 (device)
  *   idx_out  [B, k]                    int32, ascending, -1 padded
- *   ws       leading csa_workspace_zero_bytes(CSA_ENTRY_INDEX_TOPK_DECODE,
- *            desc) bytes zero on entry (left zero on return)
  */
 int csa_index_topk_decode(const csa_index_desc* desc, const void* qI, const void* wI,
                           const void* KI_cache, const int64_t* pos, int32_t* idx_out, void* ws,
                           size_t ws_bytes, void* stream);
+
+/* csa_index_topk_decode_score + csa_index_topk_decode_select -- the same
+ * selection as csa_index_topk_decode in two calls, so that scoring the cached
+ * keys can overlap the step's compressor ([R] eq 16-17; the pages' decode
+ * step emits the new entry before the indexer scores, [A] Indexer forward).
+ *
+ *   _score  scores the keys of the entries that exist before each sequence's
+ *           position step, KI_cache[b][0 .. floor(pos[b]/m)); it reads no row
+ *           that step's csa_compress_decode writes, so it may run while that
+ *           call runs on another stream.
+ *   _select then, after the compressor has written the step's entry (row
+ *           floor(pos/m) when (pos+1) % m == 0), scores that entry and selects
+ *           over all floor((pos+1)/m) visible entries into idx_out.
+ *
+ * Both take the same desc, qI, wI, KI_cache, pos and workspace (sized as
+ * for csa_index_topk_decode); between the two the workspace is in use and no
+ * other call may touch it.
+ * csa_index_topk_decode runs exactly these two steps, so the two ways give
+ * bitwise the same idx_out. */
+int csa_index_topk_decode_score(const csa_index_desc* desc, const void* qI, const void* wI,
+                                const void* KI_cache, const int64_t* pos, void* ws,
+                                size_t ws_bytes, void* stream);
+int csa_index_topk_decode_select(const csa_index_desc* desc, const void* qI, const void* wI,
+                                 const void* KI_cache, const int64_t* pos, int32_t* idx_out,
+                                 void* ws, size_t ws_bytes, void* stream);
 
 /* csa_index_topk_decode_noalloc -- csa_index_topk_decode for callers that
  * cannot allocate device memory (code under HIP graph capture, tight serving
@@ -259,15 +278,12 @@ int csa_index_topk_decode(const csa_index_desc* desc, const void* qI, const void
  * process ends.  A descriptor whose csa_workspace_bytes(
  * CSA_ENTRY_INDEX_TOPK_DECODE, desc) exceeds that is rejected with
  * CSA_ERR_WORKSPACE before anything is enqueued (32 sequences of 32768
- * entries, or 4 of 262144, need 22.4 MiB).  The array's device address is
- * looked up on the first call on each device (CSA_ERR_HIP if that fails).
- * Its leading histogram bytes must be zero when a call starts: each call
- * leaves them zero, and a call that needs more of them than the previous
- * call on that GPU left zero clears them first with a fill kernel on
- * `stream` (no memset, so the call can be captured).  Every call on a GPU
- * shares the array, so calls that overlap on one GPU (unordered streams, or
- * host threads racing on different streams) race; calls ordered on one
- * stream do not.  The library allocates nothing and calls no allocator. */
+ * entries need 4.4 MiB, 4 of 262144 need 4.2 MiB: about 4 B per entry).
+ * The array's device address is looked up on the first call on each device
+ * (CSA_ERR_HIP if that fails).  Every call on a GPU shares the array, so
+ * calls that overlap on one GPU (unordered streams, or host threads racing
+ * on different streams) race; calls ordered on one stream do not.  The
+ * library allocates nothing and calls no allocator. */
 int csa_index_topk_decode_noalloc(const csa_index_desc* desc, const void* qI, const void* wI,
                                   const void* KI_cache, const int64_t* pos, int32_t* idx_out,
                                   void* stream);
@@ -317,8 +333,8 @@ int csa_indexer_fp4_quant_decode(const csa_fp4_desc* desc, const void* cache, in
  * q^I and the cached keys in the format csa_indexer_fp4_quant writes (the
  * scores are eq 16 on the dequantised values, in fp32), wI as before in
  * desc->dtype (CSA_BF16 only).  Same descriptor (head_dim = W), same
- * workspace and zero bytes as csa_index_topk_decode
- * (CSA_ENTRY_INDEX_TOPK_DECODE_FP4 gives them).
+ * workspace as csa_index_topk_decode (CSA_ENTRY_INDEX_TOPK_DECODE_FP4
+ * gives its size).
  *
  *   qI_codes [B, hI, cI/2], qI_exps [B, hI, cI/32]
  *   K_codes  [B, n_entries, cI/2], K_exps [B, n_entries, cI/32]
@@ -417,7 +433,7 @@ int hca_dense_mqa_decode(const csa_attn_desc* desc, const void* q, const void* w
  * CSA_ERR_INVALID_ARG; N > 2^31 - 1 -> CSA_ERR_UNSUPPORTED; the attention
  * calls support dtype CSA_BF16 only (CSA_ERR_UNSUPPORTED otherwise).  Workspaces are those
  * of the contiguous entry (CSA_ENTRY_COMPRESS_DECODE, _INDEX_TOPK_DECODE,
- * _SPARSE_MQA_DECODE, _DENSE_MQA_DECODE), zero bytes included.
+ * _SPARSE_MQA_DECODE, _DENSE_MQA_DECODE).
  * ---------------------------------------------------------------------- */
 int csa_compress_decode_paged(const csa_compress_desc* desc, const void* h, const int64_t* pos,
                               const void* W_kv, const void* W_z, const float* ape,
@@ -545,10 +561,8 @@ int csa_output_proj(const csa_oproj_desc* desc, const void* o, const void* wo_a,
  * the csa_*_desc type that entry takes).  Returns 0 on a null descriptor. */
 size_t csa_workspace_bytes(int entry, const void* desc);
 
-/* Leading workspace bytes that must be zero when `entry` starts (its
- * counters; each call returns them to zero), 0 for entries without any.
- * csa_index_topk_decode keeps its score histograms there, so that no
- * clearing launch precedes the scoring. */
+/* Leading workspace bytes that must be zero when `entry` starts: 0 for
+ * every entry of this version (no entry keeps counters in its workspace). */
 size_t csa_workspace_zero_bytes(int entry, const void* desc);
 
 /* Static text for a csa_status value. */

@@ -32,7 +32,8 @@ EXPORTED = ["csa_compress_prefill", "csa_compress_decode", "csa_state_bytes", "c
             "csa_compress_decode_paged", "csa_index_topk_decode_paged",
             "csa_sparse_mqa_decode_paged", "hca_dense_mqa_decode_paged",
             "csa_indexer_fp4_quant_decode_paged", "csa_index_topk_decode_fp4_paged",
-            "csa_index_topk_decode_noalloc", "csa_noalloc_scratch_bytes"]
+            "csa_index_topk_decode_noalloc", "csa_noalloc_scratch_bytes",
+            "csa_index_topk_decode_score", "csa_index_topk_decode_select"]
 
 
 class CompressDesc(ctypes.Structure):
@@ -123,6 +124,8 @@ def load(path: str = LIB_PATH):
     lib.csa_indexer_fp4_quant_decode_paged.argtypes = [P, P, ctypes.c_int64, P, I, P, P, P, I32, P]
     lib.csa_index_topk_decode_fp4_paged.argtypes = [P] * 7 + [I32] + [P] * 3 + [S, P]
     lib.csa_index_topk_decode_noalloc.argtypes = [P] * 7
+    lib.csa_index_topk_decode_score.argtypes = [P] * 6 + [S, P]
+    lib.csa_index_topk_decode_select.argtypes = [P] * 7 + [S, P]
     lib.csa_noalloc_scratch_bytes.restype = S
     lib.csa_noalloc_scratch_bytes.argtypes = []
     for f in EXPORTED:
@@ -442,6 +445,45 @@ def csa_index_topk_decode(qI, wI, KI_cache, pos, m, k, out=None):
     if st != 0:
         _WS_ZERO.pop((str(qI.device), "index_dec"), None)
     _check(st, "csa_index_topk_decode")
+    return out
+
+
+def csa_index_topk_decode_score(qI, wI, KI_cache, pos, m, k, ws_slot="index_dec"):
+    """First half of csa_index_topk_decode: scores the cached keys that precede
+    each sequence's step; csa_index_topk_decode_select with the same
+    arguments and ws_slot must follow."""
+    lib = load()
+    B, hI, cI = qI.shape
+    ne = KI_cache.shape[1]
+    _expect(KI_cache, (B, ne, cI), qI.dtype, "KI_cache")
+    _expect(pos, (B,), torch.int64, "pos")
+    desc = IndexDesc(0, B, hI, cI, m, k, _dt(qI), ne)
+    ws, wsb = workspace(workspace_bytes("index_topk_decode", desc), qI.device, ws_slot,
+                        zero_bytes=workspace_zero_bytes("index_topk_decode", desc))
+    # the histograms stay in use until the select call returns them to zero
+    _WS_ZERO.pop((str(qI.device), ws_slot), None)
+    st = lib.csa_index_topk_decode_score(ctypes.byref(desc), _ptr(qI), _ptr(wI), _ptr(KI_cache),
+                                         _ptr(pos), _ptr(ws), wsb, _stream(qI.device))
+    _check(st, "csa_index_topk_decode_score")
+
+
+def csa_index_topk_decode_select(qI, wI, KI_cache, pos, m, k, out=None, ws_slot="index_dec"):
+    """Second half: scores the step's new entries and selects."""
+    lib = load()
+    B, hI, cI = qI.shape
+    ne = KI_cache.shape[1]
+    desc = IndexDesc(0, B, hI, cI, m, k, _dt(qI), ne)
+    if out is None:
+        out = torch.empty((B, k), dtype=torch.int32, device=qI.device)
+    ws = _WS.get((str(qI.device), ws_slot))
+    need = workspace_bytes("index_topk_decode", desc)
+    if ws is None or ws.numel() < need:
+        raise CsaError("csa_index_topk_decode_select: no matching _score call on this workspace")
+    st = lib.csa_index_topk_decode_select(ctypes.byref(desc), _ptr(qI), _ptr(wI), _ptr(KI_cache),
+                                          _ptr(pos), _ptr(out), _ptr(ws), ws.numel(),
+                                          _stream(qI.device))
+    _check(st, "csa_index_topk_decode_select")
+    _WS_ZERO[(str(qI.device), ws_slot)] = workspace_zero_bytes("index_topk_decode", desc)
     return out
 
 

@@ -380,6 +380,28 @@ int csa_index_topk_decode(const csa_index_desc* d, const void* qI, const void* w
   return index_topk_decode(d, qI, wI, KI_cache, pos, idx_out, ws, ws_bytes, stream, EntryMap());
 }
 
+int csa_index_topk_decode_score(const csa_index_desc* d, const void* qI, const void* wI,
+                                const void* KI_cache, const int64_t* pos, void* ws,
+                                size_t ws_bytes, void* stream) {
+  int s = check_index(d, true);
+  if (s) return s;
+  if (!qI || !wI || !KI_cache || !pos) return CSA_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < index_decode_ws_bytes(*d)) return CSA_ERR_WORKSPACE;
+  return hip_status(launch_index_topk_decode_score(*d, qI, wI, KI_cache, pos, ws,
+                                                   (hipStream_t)stream, EntryMap()));
+}
+
+int csa_index_topk_decode_select(const csa_index_desc* d, const void* qI, const void* wI,
+                                 const void* KI_cache, const int64_t* pos, int32_t* idx_out,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  int s = check_index(d, true);
+  if (s) return s;
+  if (!qI || !wI || !KI_cache || !pos || !idx_out) return CSA_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < index_decode_ws_bytes(*d)) return CSA_ERR_WORKSPACE;
+  return hip_status(launch_index_topk_decode_select(*d, qI, wI, KI_cache, pos, idx_out, ws,
+                                                    (hipStream_t)stream, EntryMap()));
+}
+
 int csa_index_topk_decode_noalloc(const csa_index_desc* d, const void* qI, const void* wI,
                                   const void* KI_cache, const int64_t* pos, int32_t* idx_out,
                                   void* stream) {

@@ -97,6 +97,16 @@ hipError_t launch_fp4_rotate_quant(int dtype, const void* x, int64_t rows, int w
 hipError_t launch_index_topk_decode(const csa_index_desc& d, const void* qI, const void* wI,
                                     const void* KI, const int64_t* pos, int32_t* idx_out,
                                     void* ws, hipStream_t st, EntryMap em = EntryMap());
+// The same in two parts: scoring of the entries that precede each position's
+// step (may run while that step's compressor emits its entry), then the
+// selection, which scores the emitted entry itself.
+hipError_t launch_index_topk_decode_score(const csa_index_desc& d, const void* qI,
+                                          const void* wI, const void* KI, const int64_t* pos,
+                                          void* ws, hipStream_t st, EntryMap em = EntryMap());
+hipError_t launch_index_topk_decode_select(const csa_index_desc& d, const void* qI,
+                                           const void* wI, const void* KI, const int64_t* pos,
+                                           int32_t* idx_out, void* ws, hipStream_t st,
+                                           EntryMap em = EntryMap());
 
 // The no-allocation variant (noalloc.hip): the same launches on a
 // library-owned static scratch of noalloc_scratch_bytes() per device.

@@ -496,40 +496,30 @@ __global__ __launch_bounds__(256) void topk_rows_prefill_kernel(const SC* __rest
 
 // ===========================================================================
 // Decode: one query per sequence over up to ~10^6 cached keys.
-//   D1 score chunks of keys (16x16 matrix-core tiles, keys streamed straight
-//      from memory -- this pass moves the step's dominant bytes) and build a
-//      2048-bin histogram of the keys' top 11 bits, added into one of R
-//      copies per sequence (chunk mod R, R = chunks / 32 clamped to [1, 8]):
-//      atomics on one cache line are serialised, so at most ~32 workgroups
-//      add into the same lines;
-//   D2 per chunk: find the coarse threshold bin T of the k-th key from the
-//      summed copies (scanning down from the top bin), then store the
-//      chunk's entries of bins above T (the "sure" entries) at the front of
-//      the chunk's own slice of the list buffer and those of T (the ties) at
-//      its back, with the two counts per chunk -- no atomics;
-//   D3 per sequence: gather the chunks' lists, resolve the ties exactly on
-//      (score, -index) from their fine histogram (a radix select over the
-//      whole tie list when the fine bin is crowded), and merge the two
-//      ascending lists into the output row, and zero the sequence's
-//      histograms for the next call.
-// The histograms lead the workspace: they must be zero when a call starts
-// (the caller clears them once) and every call leaves them zero, so no
-// clearing launch precedes the scoring.  Nothing depends on the order in
-// which workgroups run.
+//   D1 one workgroup per chunk of 1024 keys scores them (16x16 matrix-core
+//      tiles, keys streamed straight from memory -- this pass moves the
+//      step's dominant bytes), stores the scores, and keeps the chunk's L
+//      best entries as its candidates, in index order, with the L-th best.
+//      Entries are ranked by the composite (key << 32 | ~index): higher score
+//      first, ties to the smaller index, all distinct.
+//   D2 one workgroup per sequence gathers every chunk's candidates into LDS
+//      (adding the step's own new entry when D1 left it out), finds the k-th
+//      best composite by a radix selection in LDS and emits the winners in
+//      index order.  A chunk that offered L candidates and whose L-th best
+//      still beats that threshold may hold more winners than it offered;
+//      then the workgroup selects exactly over all the row's stored scores
+//      instead (slow, and rare: L is twice a chunk's expected share of the k,
+//      plus 16).
+// No state carries from one call to the next: the workspace needs no
+// clearing, and nothing depends on the order in which workgroups run.
 // ===========================================================================
-constexpr int kDecChunk = 1024;    // keys per scoring workgroup
-constexpr int kCoarseBins = 2048;  // top 11 bits
-constexpr int kHistCopies = 8;     // most histogram copies per sequence
-constexpr int kChunkLds = 1024;    // chunk counts staged in LDS by the finalize
-constexpr int kTieLds = 6144;      // tie candidates resolved in LDS
+constexpr int kDecChunk = 1024;  // keys per scoring workgroup
+constexpr int kCandLds = 8192;   // candidates D2 holds in LDS (64 KiB)
 
 struct DecWs {  // carve-up of the decode workspace
-  int* hist;      // [B][copies][kCoarseBins], then fine [B][kCoarseBins] (tie bits 20..10)
-  int* fine;
   float* scores;  // [B][n_entries]
-  int2* ccnt;     // [B][chunks]: (sure, tie) counts per chunk
-  uint2* lists;   // [B][n_entries] (key, index): chunk slices, sure first, ties last
-  uint2* flat;    // [B][n_entries]: tie lists too long for LDS, contiguous
+  uint2* cand;    // [B][chunks][L] (key, index), index order
+  uint4* cmeta;   // [B][chunks]: (count, full, L-th key, L-th index)
 };
 
 static size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -538,32 +528,134 @@ static int64_t dec_chunks(const csa_index_desc& d) {
   return (d.n_entries + kDecChunk - 1) / kDecChunk;
 }
 
-static int dec_hist_copies(int64_t nchunks) {
-  return nchunks >= 32 * kHistCopies ? kHistCopies : nchunks >= 64 ? (int)(nchunks / 32) : 1;
+// Candidates per chunk: twice a chunk's expected share of the k winners,
+// plus 16, within what D2 holds in LDS (one slot kept for the new entry).
+static int dec_cand_per_chunk(const csa_index_desc& d) {
+  const int64_t nch = dec_chunks(d) > 0 ? dec_chunks(d) : 1;
+  int64_t L = 2 * (int64_t)d.k / nch + 16;
+  L = (L + 7) & ~(int64_t)7;
+  if (L > kDecChunk) L = kDecChunk;
+  const int64_t cap = (kCandLds - 1) / nch;
+  if (L > cap) L = cap;  // D2 then falls back for rows with more chunks
+  return (int)(L < 1 ? 1 : L);
 }
 
 static DecWs carve(void* ws, const csa_index_desc& d) {
   uint8_t* p = (uint8_t*)ws;
   DecWs w;
-  const size_t B = d.batch, ne = d.n_entries, nc = dec_chunks(d);
-  w.hist = (int*)p;
-  w.fine = w.hist + B * dec_hist_copies(nc) * kCoarseBins;
-  p += align_up(B * (dec_hist_copies(nc) + 1) * kCoarseBins * 4);
+  const size_t B = d.batch, ne = d.n_entries, nc = dec_chunks(d), L = dec_cand_per_chunk(d);
   w.scores = (float*)p; p += align_up(B * ne * 4);
-  w.ccnt = (int2*)p; p += align_up(B * nc * 8);
-  w.lists = (uint2*)p; p += align_up(B * ne * 8);
-  w.flat = (uint2*)p; p += align_up(B * ne * 8);
+  w.cand = (uint2*)p; p += align_up(B * nc * L * 8);
+  w.cmeta = (uint4*)p;
   return w;
 }
 
-size_t index_decode_zero_bytes(const csa_index_desc& d) {
-  return align_up((size_t)d.batch * (dec_hist_copies(dec_chunks(d)) + 1) * kCoarseBins * 4);
-}
+size_t index_decode_zero_bytes(const csa_index_desc&) { return 0; }
 
 size_t index_decode_ws_bytes(const csa_index_desc& d) {
-  const size_t B = d.batch, ne = d.n_entries, nc = dec_chunks(d);
-  return align_up(B * ne * 4) + align_up(B * (dec_hist_copies(nc) + 1) * kCoarseBins * 4) +
-         align_up(B * nc * 8) + 2 * align_up(B * ne * 8);
+  const size_t B = d.batch, ne = d.n_entries, nc = dec_chunks(d), L = dec_cand_per_chunk(d);
+  return align_up(B * ne * 4) + align_up(B * nc * L * 8) + align_up(B * nc * 16);
+}
+
+// Block-wide max / min of a uint32 over 256 threads (sh: 8 ints of LDS).
+CSA_DEV uint32_t block_max_u32(uint32_t v, int* sh) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = (int)v;
+  __syncthreads();
+  return max(max((uint32_t)sh[0], (uint32_t)sh[1]), max((uint32_t)sh[2], (uint32_t)sh[3]));
+}
+CSA_DEV uint32_t block_min_u32(uint32_t v, int* sh) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[4 + (threadIdx.x >> 6)] = (int)v;
+  __syncthreads();
+  return min(min((uint32_t)sh[4], (uint32_t)sh[5]), min((uint32_t)sh[6], (uint32_t)sh[7]));
+}
+
+// D1's chunk-local selection.  ls[0, c) holds the chunk's keys in index order
+// (entry c0 + i at i); thread j owns entries 4j .. 4j+3.  Keeps the L best
+// by composite (all of them when c <= L) in cand, in index order, and
+// records (count, full, L-th best key, its index) in *meta.  hist: 256 ints
+// of LDS.
+CSA_DEV void chunk_candidates(const uint32_t* ls, int c, int L, int64_t c0, int* hist, int* sh,
+                              int* res, uint2* __restrict__ cand, uint4* __restrict__ meta) {
+  const int tid = threadIdx.x;
+  uint32_t key[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) key[u] = 4 * tid + u < c ? ls[4 * tid + u] : 0u;
+  uint32_t V = 0;  // the L-th largest key
+  int take = 0;    // how many entries of key V are kept (the smallest indices)
+  if (c > L) {
+    // the bits above the highest one where the keys differ are common: the
+    // radix starts below them, so that its first digit spreads the keys
+    uint32_t kmax = 0, kmin = 0xffffffffu;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (4 * tid + u < c) { kmax = max(kmax, key[u]); kmin = min(kmin, key[u]); }
+    kmax = block_max_u32(kmax, sh);
+    kmin = block_min_u32(kmin, sh);
+    int hi = kmax == kmin ? -1 : 31 - __builtin_clz(kmax ^ kmin);  // highest undecided bit
+    uint32_t mask = hi >= 31 ? 0u : ~((2u << hi) - 1u);
+    uint32_t prefix = kmax & mask;
+    int need = L;
+    while (hi >= 0) {
+      const int lo = hi >= 7 ? hi - 7 : 0;
+      const uint32_t dm = (2u << (hi - lo)) - 1u;
+      hist[tid] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (4 * tid + u < c && (key[u] & mask) == prefix) atomicAdd(&hist[(key[u] >> lo) & dm], 1);
+      __syncthreads();
+      find_digit(hist, need, res);
+      __syncthreads();
+      const int d = res[0];
+      need -= res[1];
+      prefix |= (uint32_t)d << lo;
+      mask |= dm << lo;
+      __syncthreads();
+      hi = lo - 1;
+    }
+    V = prefix;  // the L-th largest key itself (every bit decided)
+    take = need;
+  }
+  // tie ranks in index order, then output slots in index order
+  int nt = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) nt += (c > L && 4 * tid + u < c && key[u] == V);
+  int tot;
+  int tr = block_excl_scan(nt, sh, &tot);
+  bool keep[4];
+  int nk = 0;
+  int lth = -1;  // the L-th best entry, if this thread holds it (tie rank take - 1)
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = 4 * tid + u;
+    bool kp = i < c;
+    if (c > L && kp) {
+      if (key[u] == V) {
+        kp = tr < take;
+        if (tr == take - 1) lth = i;
+        ++tr;
+      } else {
+        kp = key[u] > V;
+      }
+    }
+    keep[u] = kp;
+    nk += kp;
+  }
+  int off = block_excl_scan(nk, sh + 4, &tot);
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if (keep[u]) cand[off++] = make_uint2(key[u], (uint32_t)(c0 + 4 * tid + u));
+  if (c <= L) {
+    if (tid == 0) *meta = make_uint4((uint32_t)c, 0u, 0u, 0u);
+  } else if (lth >= 0) {
+    *meta = make_uint4((uint32_t)L, 1u, V, (uint32_t)(c0 + lth));
+  }
 }
 
 // PAGED: KI is a page pool.  The page-table slots of the chunk's entries are
@@ -574,12 +666,16 @@ template <class T, int HI, int CI, bool PAGED>
 __global__ __launch_bounds__(256) void dec_score_kernel(
     const typename T::S* __restrict__ qI, const typename T::S* __restrict__ wI,
     const typename T::S* __restrict__ KI, const int64_t* __restrict__ posv, int64_t n_entries,
-    int m, int k, float* __restrict__ scores, int* __restrict__ hist, int ncopies, EntryMap em) {
+    int m, int k, float* __restrict__ scores, uint2* __restrict__ cand, uint4* __restrict__ cmeta,
+    int L, int64_t nch, EntryMap em) {
   typedef typename T::S S;
   constexpr int E = 16 / (int)sizeof(S);
   constexpr int KGE = 4 * E;      // elements per 16x16 k-group
   constexpr int NG = CI / KGE;
-  __shared__ int lh[kCoarseBins];
+  __shared__ uint32_t ls[kDecChunk];  // the chunk's keys, in index order
+  __shared__ int hist[256];
+  __shared__ int sh[8];
+  __shared__ int res[2];
   __shared__ int64_t srow[PAGED ? kDecChunk : 1];
   const int b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lg = lane >> 4;
@@ -594,11 +690,15 @@ __global__ __launch_bounds__(256) void dec_score_kernel(
                                : 0;
     }
   }
-  const int64_t vis = min64((posv[b] + 1) / m, n_entries);
+  const int64_t tpos = posv[b];
+  const int64_t vis = min64((tpos + 1) / m, n_entries);
   if (vis <= k) return;  // everything visible is selected
-  if (c0 >= vis) return;
-  const int64_t c1 = min64(c0 + kDecChunk, vis);
-  for (int i = tid; i < kCoarseBins; i += 256) lh[i] = 0;
+  // Only the entries that exist before position tpos's own step: the one
+  // that step emits (when (tpos + 1) % m == 0) is scored by the selection
+  // pass, so this kernel may run while the compressor writes it.
+  const int64_t vpre = min64(tpos / m, n_entries);
+  if (c0 >= vpre) return;
+  const int64_t c1 = min64(c0 + kDecChunk, vpre);
   if (PAGED) {
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
@@ -647,7 +747,7 @@ __global__ __launch_bounds__(256) void dec_score_kernel(
       const int64_t s = s0 + u * 16 + (lane & 15);
       if (lg == 0 && s < w1) {
         scores[(int64_t)b * n_entries + s] = p;
-        atomicAdd(&lh[float_key(p) >> 21], 1);
+        ls[s - c0] = float_key(p);
       }
     }
   };
@@ -662,9 +762,8 @@ __global__ __launch_bounds__(256) void dec_score_kernel(
     score64(s0 + 64, kc);
   }
   __syncthreads();
-  int* gh = hist + ((int64_t)b * ncopies + blockIdx.x % ncopies) * kCoarseBins;
-  for (int i = tid; i < kCoarseBins; i += 256)
-    if (lh[i]) atomicAdd(&gh[i], lh[i]);
+  const int64_t slot = (int64_t)b * nch + blockIdx.x;
+  chunk_candidates(ls, (int)(c1 - c0), L, c0, hist, sh, res, cand + slot * L, cmeta + slot);
 }
 
 // ---------------------------------------------------------------------------
@@ -763,10 +862,13 @@ __global__ __launch_bounds__(256) void dec_score_fp4_kernel(
     const uint8_t* __restrict__ qc, const uint8_t* __restrict__ qe, const uint16_t* __restrict__ wI,
     const uint8_t* __restrict__ kc, const uint8_t* __restrict__ ke,
     const int64_t* __restrict__ posv, int64_t n_entries, int m, int k, float* __restrict__ scores,
-    int* __restrict__ hist, int ncopies, EntryMap em) {
+    uint2* __restrict__ cand, uint4* __restrict__ cmeta, int L, int64_t nch, EntryMap em) {
   constexpr int NG = CI / 32;  // 32-value k-groups (= scale blocks) per row
   constexpr int RB = CI / 2;   // code bytes per row
-  __shared__ int lh[kCoarseBins];
+  __shared__ uint32_t ls[kDecChunk];
+  __shared__ int hist[256];
+  __shared__ int sh[8];
+  __shared__ int res[2];
   __shared__ int64_t srow[PAGED ? kDecChunk : 1];  // pool rows (as in dec_score_kernel)
   const int b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lg = lane >> 4;
@@ -785,7 +887,6 @@ __global__ __launch_bounds__(256) void dec_score_fp4_kernel(
   if (vis <= k) return;  // everything visible is selected
   if (c0 >= vis) return;
   const int64_t c1 = min64(c0 + kDecChunk, vis);
-  for (int i = tid; i < kCoarseBins; i += 256) lh[i] = 0;
   if (PAGED) {
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
@@ -840,7 +941,7 @@ __global__ __launch_bounds__(256) void dec_score_fp4_kernel(
       const int64_t s = s0 + u * 16 + (lane & 15);
       if (lg == 0 && s < w1) {
         scores[(int64_t)b * n_entries + s] = p;
-        atomicAdd(&lh[float_key(p) >> 21], 1);
+        ls[s - c0] = float_key(p);
       }
     }
   };
@@ -854,366 +955,220 @@ __global__ __launch_bounds__(256) void dec_score_fp4_kernel(
     score64(s0 + 64, kb, kbe);
   }
   __syncthreads();
-  int* gh = hist + ((int64_t)b * ncopies + blockIdx.x % ncopies) * kCoarseBins;
-  for (int i = tid; i < kCoarseBins; i += 256)
-    if (lh[i]) atomicAdd(&gh[i], lh[i]);
+  const int64_t slot = (int64_t)b * nch + blockIdx.x;
+  chunk_candidates(ls, (int)(c1 - c0), L, c0, hist, sh, res, cand + slot * L, cmeta + slot);
 }
 
-// The coarse threshold bin T of the `need`-th largest key from a sequence's
-// histogram copies: blocks of 256 bins are summed over the copies from the
-// top bin down until they hold `need` keys.  Every thread gets res = (T,
-// #keys in bins above T).  Requires at least `need` keys in the histogram.
-CSA_DEV void dec_threshold(const int* __restrict__ h, int ncopies, int need, int* sh, int* res) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int above = 0;
-  for (int blk = kCoarseBins / 256 - 1; blk >= 0; --blk) {
-    const int bin = blk * 256 + tid;
-    int v[kHistCopies];
+// Index score of one key row (eq 16 for one entry), computed by one wave:
+// lane l takes head l / 4 and a quarter of the key's channels, in a fixed
+// order, so every caller gets the same value bit for bit.
+template <class T, int HI, int CI>
+CSA_DEV float one_entry_score(const typename T::S* __restrict__ q,
+                              const typename T::S* __restrict__ w,
+                              const typename T::S* __restrict__ key, int lane) {
+  constexpr int DPL = CI / 4;
+  const int h = lane >> 2, part = lane & 3;
+  float dot = 0.f;
+  if (h < HI) {
 #pragma unroll
-    for (int r = 0; r < kHistCopies; ++r) v[r] = r < ncopies ? h[r * kCoarseBins + bin] : 0;
-    int c = 0;
-#pragma unroll
-    for (int r = 0; r < kHistCopies; ++r) c += v[r];
-    int suf = c;  // inclusive suffix sum over the wave's lanes
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_down(suf, o, 64);
-      if (lane + o < 64) suf += y;
+    for (int i = 0; i < DPL; ++i) {
+      const int dch = part * DPL + i;
+      dot = fmaf(T::ld(q, h * CI + dch), T::ld(key, dch), dot);
     }
-    __syncthreads();
-    if (lane == 0) sh[wave] = suf;
-    __syncthreads();
-    for (int w = wave + 1; w < 4; ++w) suf += sh[w];
-    const int tot = sh[0] + sh[1] + sh[2] + sh[3];
-    if (above + suf >= need && above + suf - c < need) {
-      res[0] = bin;
-      res[1] = above + suf - c;
-    }
-    if (above + tot >= need) break;  // uniform
-    above += tot;
   }
-  __syncthreads();
+  dot += __shfl_xor(dot, 1, 64);
+  dot += __shfl_xor(dot, 2, 64);
+  const float p = (h < HI && part == 0) ? T::ld(w, h) * relu(dot) : 0.f;
+  return wave_sum(p);
 }
 
-// D2: classify a chunk against T.  Thread j owns entries c0 + PER*j + u; one
-// block-wide prefix sum per list gives each entry its slot in the chunk's
-// slice of `lists` (sure from the front, ties from the back, both in index
-// order).  Ties are also counted by their next 11 key bits (the fine
-// histogram; few per chunk, spread over the bins).
-__global__ __launch_bounds__(256) void dec_collect_kernel(const int64_t* __restrict__ posv,
-                                                          int64_t n_entries, int m, int k,
-                                                          const float* __restrict__ scores,
-                                                          const int* __restrict__ hist,
-                                                          int* __restrict__ fine,
-                                                          int2* __restrict__ ccnt,
-                                                          uint2* __restrict__ lists,
-                                                          int64_t nchunks, int ncopies) {
-  __shared__ int sh[8];
-  __shared__ int res[2];
-  const int b = blockIdx.y;
-  const int64_t vis = min64((posv[b] + 1) / m, n_entries);
-  if (vis <= k) return;
-  const int64_t c0 = (int64_t)blockIdx.x * kDecChunk;
-  if (c0 >= vis) return;
-  const int64_t c1 = min64(c0 + kDecChunk, vis);
+// Radix selection of the k-th best composite: digits of up to 8 bits from
+// composite bit `hi` down (the bits above it are `prefix`, common to every
+// item), stopping at the first digit whose bucket is taken whole (the lower
+// bits are then zero in the result).  Items >= the result are exactly the
+// `need` best.  get(i) gives item i's composite; hist: 256 ints of LDS.
+template <class GET>
+CSA_DEV uint64_t radix_select64(GET get, int64_t n, int need, int hi, uint64_t prefix,
+                                int* hist, int* res) {
   const int tid = threadIdx.x;
-  constexpr int PER = kDecChunk / 256;
-  const float* sc = scores + (int64_t)b * n_entries;
-  float v[PER];  // loads in flight during the threshold search
-#pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int64_t s = c0 + tid * PER + u;
-    v[u] = s < c1 ? sc[s] : 0.f;
-  }
-  dec_threshold(hist + (int64_t)b * ncopies * kCoarseBins, ncopies, k, sh, res);
-  const uint32_t T = (uint32_t)res[0];
-  uint32_t key[PER];
-  int ns = 0, nt = 0;
-#pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int64_t s = c0 + tid * PER + u;
-    key[u] = float_key(v[u]);
-    const uint32_t bin = key[u] >> 21;
-    ns += (s < c1 && bin > T);
-    nt += (s < c1 && bin == T);
-  }
-  int totS, totT;
-  int os = block_excl_scan(ns, sh, &totS);
-  int ot = block_excl_scan(nt, sh + 4, &totT);
-  const int cap = (int)(c1 - c0);
-  uint2* L = lists + (int64_t)b * n_entries + c0;
-  ot += cap - totT;
-#pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int64_t s = c0 + tid * PER + u;
-    if (s >= c1) continue;
-    const uint32_t bin = key[u] >> 21;
-    if (bin > T) L[os++] = make_uint2(key[u], (uint32_t)s);
-    else if (bin == T) {
-      L[ot++] = make_uint2(key[u], (uint32_t)s);
-      atomicAdd(&fine[(int64_t)b * kCoarseBins + ((key[u] >> 10) & (kCoarseBins - 1))], 1);
-    }
-  }
-  if (tid == 0) ccnt[(int64_t)b * nchunks + blockIdx.x] = make_int2(totS, totT);
-}
-
-// Radix selection over a list in global memory of `cnt` (key, index) pairs,
-// ordered by (key desc, index asc): marks how many to take via the composite
-// 64-bit value (key << 32) | ~index.  Returns through res the composite
-// threshold (hi, lo); items >= threshold are the `need` best.
-CSA_DEV void list_select(const uint2* __restrict__ L, int cnt, int need, int* hist, int* res,
-                         uint32_t* thr_hi, uint32_t* thr_lo) {
-  uint64_t prefix = 0, pmask = 0;
-  const int tid = threadIdx.x;
-  for (int pass = 0; pass < 8; ++pass) {
-    const int shift = 56 - 8 * pass;
+  uint64_t pmask = hi >= 63 ? 0ull : ~((2ull << hi) - 1ull);
+  while (hi >= 0) {
+    const int lo = hi >= 7 ? hi - 7 : 0;
+    const uint32_t dm = (2u << (hi - lo)) - 1u;
     hist[tid] = 0;
     __syncthreads();
-    for (int i = tid; i < cnt; i += 256) {
-      const uint2 e = L[i];
-      const uint64_t ck = ((uint64_t)e.x << 32) | (uint64_t)(~e.y);
-      if ((ck & pmask) == prefix) atomicAdd(&hist[(ck >> shift) & 255], 1);
-    }
-    __syncthreads();
-    find_digit(hist, need, res);
-    __syncthreads();
-    need -= res[1];
-    prefix |= (uint64_t)res[0] << shift;
-    pmask |= (uint64_t)0xff << shift;
-    __syncthreads();
-  }
-  *thr_hi = (uint32_t)(prefix >> 32);
-  *thr_lo = (uint32_t)prefix;
-}
-
-// The same selection over n <= kTieLds pairs held in LDS whose keys share
-// their top 11 bits (composite bits 63..53): digits of 8 bits from composite
-// bit 52 down (the last one 5 bits wide), stopping at the first digit whose
-// bucket is taken whole.
-CSA_DEV uint64_t lds_list_select(const uint2* L, int n, int need, int* hist, int* res) {
-  const int tid = threadIdx.x;
-  uint64_t pmask = ~0ull << 53;
-  uint64_t prefix = composite(L[0].x, L[0].y) & pmask;
-  for (int shift = 45;; shift = shift > 5 ? shift - 8 : 0) {
-    const uint32_t dmask = shift ? 255u : 31u;
-    hist[tid] = 0;
-    __syncthreads();
-    for (int i = tid; i < n; i += 256) {
-      const uint64_t ck = composite(L[i].x, L[i].y);
-      if ((ck & pmask) == prefix) atomicAdd(&hist[(ck >> shift) & dmask], 1);
+    for (int64_t i = tid; i < n; i += 256) {
+      const uint64_t ck = get(i);
+      if ((ck & pmask) == prefix) atomicAdd(&hist[(uint32_t)(ck >> lo) & dm], 1);
     }
     __syncthreads();
     find_digit(hist, need, res);
     __syncthreads();
     const int d = res[0];
     need -= res[1];
-    prefix |= (uint64_t)d << shift;
-    pmask |= (uint64_t)dmask << shift;
+    prefix |= (uint64_t)d << lo;
+    pmask |= (uint64_t)dm << lo;
     const bool whole = hist[d] == need;  // uniform: LDS values after the barrier
     __syncthreads();
-    if (whole || shift == 0) break;
+    if (whole) break;
+    hi = lo - 1;
   }
   return prefix;
 }
 
-// Position of v in the ascending list a[0, n): how many elements are below it.
-CSA_DEV int lower_rank(const int32_t* a, int n, int32_t v) {
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (a[mid] < v) lo = mid + 1; else hi = mid;
+// The highest composite bit where items can differ, and the common bits above
+// it, from the block-wide max and min of the items' keys.
+CSA_DEV int common_prefix(uint32_t kmax, uint32_t kmin, uint64_t* prefix) {
+  if (kmax == kmin) {  // every key equal: the indices decide
+    *prefix = (uint64_t)kmax << 32;
+    return 31;
   }
-  return lo;
+  const int hb = 31 - __builtin_clz(kmax ^ kmin);
+  const uint32_t m = hb >= 31 ? 0u : ~((2u << hb) - 1u);
+  *prefix = (uint64_t)(kmax & m) << 32;
+  return 32 + hb;
 }
 
-// Output positions of a contiguous run a[j0, j1) of one ascending list merged
-// with the ascending list o[0, no) (disjoint values): one binary search for the
-// first element, then a walk, since the ranks grow along the run.
-CSA_DEV void merge_run(const int32_t* a, int j0, int j1, const int32_t* o, int no,
-                       int32_t* __restrict__ out) {
-  if (j0 >= j1) return;
-  int r = lower_rank(o, no, a[j0]);
-  for (int j = j0; j < j1; ++j) {
-    const int32_t x = a[j];
-    while (r < no && o[r] < x) ++r;
-    out[j + r] = x;
-  }
-}
-
-// D3: one workgroup per sequence.  The chunks' sure entries and ties are
-// gathered in chunk order, so both lists are in ascending index order.  The
-// ties' fine histogram (bits 20..10 of the key, counted by D2) gives the fine
-// bin F holding the last winner: ties above F are taken, those in F are
-// ranked exactly (or, past 256 of them, the whole tie list is radix-selected);
-// the winners are compacted in order and merged with the sure list.
-__global__ __launch_bounds__(256) void dec_finalize_kernel(
+// D2: one workgroup per sequence (see the section comment).  FOLD: the
+// entry emitted by position t's own step (when (t + 1) % m == 0) was left
+// out of D1; it is scored here and joins the candidates.
+template <class TS, int HI, int CI, bool FOLD>
+__global__ __launch_bounds__(256) void dec_select_kernel(
     const int64_t* __restrict__ posv, int64_t n_entries, int m, int k,
-    int* __restrict__ hist, int ncopies, int* __restrict__ fine, const int2* __restrict__ ccnt,
-    const uint2* __restrict__ lists, uint2* __restrict__ flat, int64_t nchunks,
+    const float* __restrict__ scores, const uint2* __restrict__ cand,
+    const uint4* __restrict__ cmeta, int64_t nchunks, int L, const typename TS::S* __restrict__ qI,
+    const typename TS::S* __restrict__ wI, const typename TS::S* __restrict__ KI, EntryMap em,
     int32_t* __restrict__ idx_out) {
+  __shared__ uint2 cl[kCandLds];
+  __shared__ int coff[kCandLds];  // per chunk: its first slot in cl, or -1 past its count
+  __shared__ int hist[256];
   __shared__ int sh[8];
   __shared__ int res[2];
-  __shared__ int h256[256];
-  __shared__ int32_t surev[2048];
-  __shared__ int32_t tsel[2048];
-  __shared__ int ncand, ncand_f;
-  __shared__ uint64_t fk[256];
-  __shared__ uint64_t fk64_thr;
-  __shared__ uint2 tls[kTieLds];
-  __shared__ int2 ccs[kChunkLds];
-  __shared__ int slotS[2048];
-  __shared__ int slotT[kTieLds];
+  __shared__ float snew;
   const int b = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t vis = min64((posv[b] + 1) / m, n_entries);
+  const int tid = threadIdx.x;
+  const int64_t tpos = posv[b];
+  const int64_t vis = min64((tpos + 1) / m, n_entries);
   int32_t* orow = idx_out + (int64_t)b * k;
   if (vis <= k) {
     for (int j = tid; j < k; j += 256) orow[j] = j < vis ? j : -1;
     return;
   }
-  // the ties' fine histogram, loaded now so that its latency overlaps the
-  // gather (thread j holds bins 8j .. 8j+7)
-  int fl[kCoarseBins / 256];
-  {
-    int4* f4 = (int4*)(fine + (int64_t)b * kCoarseBins) + 2 * tid;
-    const int4 x = f4[0], y = f4[1];
-    fl[0] = x.x; fl[1] = x.y; fl[2] = x.z; fl[3] = x.w;
-    fl[4] = y.x; fl[5] = y.y; fl[6] = y.z; fl[7] = y.w;
-    f4[0] = make_int4(0, 0, 0, 0);  // after this thread's own loads of them
-    f4[1] = make_int4(0, 0, 0, 0);
-  }
-  {  // the coarse copies were read by the collect pass, which has finished
-    int4* h4 = (int4*)(hist + (int64_t)b * ncopies * kCoarseBins);
-    for (int i = tid; i < ncopies * kCoarseBins / 4; i += 256) h4[i] = make_int4(0, 0, 0, 0);
-  }
-  // gather: thread j takes a contiguous run of chunks and writes the slice
-  // slot of each of their entries into per-list slot tables in LDS (list
-  // position -> slot), then every thread fetches a share of the entries, so
-  // that the loads of many entries are in flight together
-  const int nch = (int)((vis + kDecChunk - 1) / kDecChunk);
+  const int64_t e_new = (FOLD && (tpos + 1) % m == 0 && (tpos + 1) / m <= n_entries) ? vis - 1 : -1;
+  const int64_t vsc = e_new >= 0 ? vis - 1 : vis;  // entries D1 scored
+  const int nch = (int)((vsc + kDecChunk - 1) / kDecChunk);
+  const float* sc = scores + (int64_t)b * n_entries;
+  // chunk counts: thread j sums a contiguous run of chunks, one prefix sum
+  // places the runs in chunk (= index) order
   const int CPT = (nch + 255) / 256;
   const int ch0 = min(tid * CPT, nch), ch1 = min(ch0 + CPT, nch);
-  const int2* cg = ccnt + (int64_t)b * nchunks;
-  for (int c = tid; c < nch && c < kChunkLds; c += 256) ccs[c] = cg[c];
-  if (tid == 0) ncand = 0;
-  __syncthreads();
-  const int2* cc = nch <= kChunkLds ? ccs : cg;
-  int my_s = 0, my_t = 0;
-  for (int c = ch0; c < ch1; ++c) {
-    const int2 v = cc[c];
-    my_s += v.x;
-    my_t += v.y;
-  }
-  int ns, nt;
-  int ps = block_excl_scan(my_s, sh, &ns);
-  int pt = block_excl_scan(my_t, sh + 4, &nt);
-  const int need = k - ns;  // >= 1 by the threshold construction
-  const bool in_lds = nt <= kTieLds;
-  uint2* tdst = in_lds ? tls : flat + (int64_t)b * n_entries;
-  const uint2* lb = lists + (int64_t)b * n_entries;
-  for (int c = ch0; c < ch1; ++c) {
-    const int2 v = cc[c];
-    const int base = c * kDecChunk;
-    const int tb = base + (int)min64(kDecChunk, vis - base) - v.y;  // the chunk's ties
-    for (int i = 0; i < v.x; ++i) slotS[ps++] = base + i;
-    if (in_lds)
-      for (int i = 0; i < v.y; ++i) slotT[pt++] = tb + i;
-    else
-      for (int i = 0; i < v.y; ++i) tdst[pt++] = lb[tb + i];  // long lists: slow path
-  }
-  __syncthreads();
-  constexpr int U = 8;
-  for (int p0 = 0; p0 < ns; p0 += 256 * U) {
-    uint32_t e[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int p = p0 + u * 256 + tid;
-      e[u] = p < ns ? lb[slotS[p]].y : 0u;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int p = p0 + u * 256 + tid;
-      if (p < ns) surev[p] = (int32_t)e[u];
+  const uint4* meta = cmeta + (int64_t)b * nchunks;
+  int my = 0;
+  bool full_any = false;  // one of this thread's chunks may hide winners
+  for (int c = ch0; c < ch1; ++c) my += (int)meta[c].x;
+  if (e_new >= 0) {  // uniform: one wave scores the new entry
+    if (tid < 64) {
+      const float p = one_entry_score<TS, HI, CI>(qI + (int64_t)b * HI * CI, wI + (int64_t)b * HI,
+                                                  KI + em.row(b, e_new, n_entries) * CI, tid);
+      if (tid == 0) snew = p;
     }
   }
-  if (in_lds) {
-    for (int p0 = 0; p0 < nt; p0 += 256 * U) {
-      uint2 e[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int p = p0 + u * 256 + tid;
-        e[u] = p < nt ? lb[slotT[p]] : make_uint2(0, 0);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int p = p0 + u * 256 + tid;
-        if (p < nt) tls[p] = e[u];
-      }
-    }
-  }
-  // fine threshold bin F of the ties (the histogram holds exactly the nt ties)
-  bin_threshold_vals<kCoarseBins>(fl, need, sh, res);
-  const uint32_t F = (uint32_t)res[0];
-  const int need2 = need - res[1];  // winners among the ties of fine bin F (>= 1)
-  if (tid == (int)(F >> 3)) {
-    int v = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v = (int)(F & 7) == i ? fl[i] : v;
-    ncand_f = v;
-  }
-  __syncthreads();
-  const int nF = ncand_f;  // ties in fine bin F
-  const uint2* tl = tdst;
-  // composite key (score key << 32 | ~index): larger is better, all distinct;
-  // thr = the need-th largest composite among the ties
-  uint64_t thr;
-  if (nF == need2) {  // fine bin F is taken whole
-    const uint32_t kf = (tl[0].x & ~0x1fffffu) | (F << 10);
-    thr = (uint64_t)kf << 32;
-  } else if (nF <= 256) {  // rank the ties of F directly
-    for (int i = tid; i < nt; i += 256) {
-      const uint2 e = tl[i];
-      if (((e.x >> 10) & (kCoarseBins - 1)) == F) fk[atomicAdd(&ncand, 1)] = composite(e.x, e.y);
+  int tot;
+  int off = block_excl_scan(my, sh, &tot);  // its barriers also publish snew
+  const int ntot = tot + (e_new >= 0);
+  const uint32_t new_key = e_new >= 0 ? float_key(snew) : 0u;
+  bool fallback = ntot > kCandLds || ntot < k;  // (fewer than k: not reached, see L)
+  uint64_t thr = 0;
+  if (!fallback) {
+    // slot p = c * L + i of the candidate buffer goes to cl[coff[c] + i] when
+    // i < count(c): every thread loads independent slots, 8 in flight
+    for (int c = ch0; c < ch1; ++c) {
+      coff[c] = off;
+      off += (int)meta[c].x;
     }
     __syncthreads();
-    uint64_t ck = 0;
-    int rank = 0;
-    if (tid < nF) {
-      ck = fk[tid];
-      for (int j = 0; j < nF; ++j) rank += fk[j] > ck;
+    const uint2* cb = cand + (int64_t)b * nchunks * L;
+    const int nslot = nch * L;
+    for (int p0 = tid; p0 < nslot; p0 += 256 * 8) {
+      uint2 v[8];
+      int dst[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int p = p0 + 256 * u;
+        dst[u] = -1;
+        if (p < nslot) {
+          const int c = p / L, i = p - c * L;
+          const int lim = (c + 1 < nch ? coff[c + 1] : tot) - coff[c];  // count(c)
+          if (i < lim) {
+            dst[u] = coff[c] + i;
+            v[u] = cb[p];
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (dst[u] >= 0) cl[dst[u]] = v[u];
     }
-    if (tid < nF && rank == need2 - 1) fk64_thr = ck;
+    if (e_new >= 0 && tid == 0) cl[tot] = make_uint2(new_key, (uint32_t)e_new);
     __syncthreads();
-    thr = fk64_thr;
-  } else if (in_lds) {
-    thr = lds_list_select(tls, nt, need, h256, res);
-  } else {
-    uint32_t thi = 0, tlo = 0;
-    list_select(tl, nt, need, h256, res, &thi, &tlo);
-    thr = ((uint64_t)thi << 32) | tlo;
+    uint32_t kmax = 0, kmin = 0xffffffffu;
+    for (int i = tid; i < ntot; i += 256) {
+      kmax = max(kmax, cl[i].x);
+      kmin = min(kmin, cl[i].x);
+    }
+    uint64_t pre;
+    const int hi = common_prefix(block_max_u32(kmax, sh), block_min_u32(kmin, sh), &pre);
+    thr = radix_select64([&](int64_t i) { return composite(cl[i].x, cl[i].y); }, ntot, k, hi, pre,
+                         hist, res);
+    // a chunk that kept L entries whose L-th best beats thr may hide winners
+    for (int c = ch0; c < ch1; ++c) {
+      const uint4 mt = meta[c];
+      full_any |= mt.y != 0 && composite(mt.z, mt.w) > thr;
+    }
   }
-  // winners in list (= index) order: each thread takes a contiguous run of the
-  // ties, and one prefix sum over the threads' counts places them
-  {
-    const int TPT = (nt + 255) / 256;
-    const int i0 = min(tid * TPT, nt), i1 = min(i0 + TPT, nt);
+  fallback = __syncthreads_or(fallback || full_any);
+  if (!fallback) {
+    // winners in list (= index) order: contiguous runs, one prefix sum
+    const int TPT = (ntot + 255) / 256;
+    const int i0 = min(tid * TPT, ntot), i1 = min(i0 + TPT, ntot);
     int cnt = 0;
-    for (int i = i0; i < i1; ++i) cnt += composite(tl[i].x, tl[i].y) >= thr;
-    int tot;
-    int off = block_excl_scan(cnt, sh, &tot);
-    for (int i = i0; i < i1; ++i) {
-      const uint2 e = tl[i];
-      if (composite(e.x, e.y) >= thr) tsel[off++] = (int32_t)e.y;
-    }
+    for (int i = i0; i < i1; ++i) cnt += composite(cl[i].x, cl[i].y) >= thr;
+    int o = block_excl_scan(cnt, sh, &tot);
+    for (int i = i0; i < i1; ++i)
+      if (composite(cl[i].x, cl[i].y) >= thr) orow[o++] = (int32_t)cl[i].y;
+    return;
   }
-  __syncthreads();
-  // merge the two ascending lists (disjoint index sets): an element's output
-  // position is its own rank plus its rank in the other list; each thread
-  // places a contiguous run of each list
+  // exact selection over the whole row's scores, then the winners in index
+  // order, tile by tile
+  auto row_key = [&](int64_t i) { return i == e_new ? new_key : float_key(sc[i]); };
   {
-    const int RS = (ns + 255) / 256, RT = (need + 255) / 256;
-    merge_run(surev, min(tid * RS, ns), min(tid * RS + RS, ns), tsel, need, orow);
-    merge_run(tsel, min(tid * RT, need), min(tid * RT + RT, need), surev, ns, orow);
+    uint32_t kmax = 0, kmin = 0xffffffffu;
+    for (int64_t i = tid; i < vis; i += 256) {
+      const uint32_t kk = row_key(i);
+      kmax = max(kmax, kk);
+      kmin = min(kmin, kk);
+    }
+    uint64_t pre;
+    const int hi = common_prefix(block_max_u32(kmax, sh), block_min_u32(kmin, sh), &pre);
+    thr = radix_select64([&](int64_t i) { return composite(row_key(i), (uint32_t)i); }, vis, k,
+                         hi, pre, hist, res);
+  }
+  int base = 0;
+  for (int64_t t0 = 0; t0 < vis; t0 += 1024) {
+    int cnt = 0;
+    bool win[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = t0 + 4 * tid + u;
+      const uint32_t kk = i < vis ? row_key(i) : 0u;
+      win[u] = i < vis && composite(kk, (uint32_t)i) >= thr;
+      cnt += win[u];
+    }
+    int o = block_excl_scan(cnt, sh, &tot);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (win[u]) orow[base + o++] = (int32_t)(t0 + 4 * tid + u);
+    base += tot;
   }
 }
 
@@ -1303,28 +1258,31 @@ hipError_t launch_topk_rows_prefill(const csa_index_desc& d, const void* scores,
 }
 
 // D2 and D3 after the scores and histograms of a decode call are in place.
-static hipError_t dec_select(const csa_index_desc& d, const DecWs& w, int64_t nch, int ncopies,
-                             const int64_t* pos, int32_t* idx_out, hipStream_t st) {
-  const dim3 grid((unsigned)nch, (unsigned)d.batch);
-  dec_collect_kernel<<<grid, 256, 0, st>>>(pos, d.n_entries, d.m, d.k, w.scores, w.hist, w.fine,
-                                           w.ccnt, w.lists, nch, ncopies);
-  dec_finalize_kernel<<<d.batch, 256, 0, st>>>(pos, d.n_entries, d.m, d.k, w.hist, ncopies, w.fine,
-                                               w.ccnt, w.lists, w.flat, nch, idx_out);
+// D2 (FOLD: with the position's own new entry, see dec_select_kernel).
+template <class T, int HI, int CI, bool FOLD>
+static hipError_t dec_select(const csa_index_desc& d, const DecWs& w, int64_t nch, int L,
+                             const int64_t* pos, int32_t* idx_out, const void* qI,
+                             const void* wI, const void* KI, EntryMap em, hipStream_t st) {
+  typedef typename T::S S;
+  dec_select_kernel<T, HI, CI, FOLD><<<d.batch, 256, 0, st>>>(
+      pos, d.n_entries, d.m, d.k, w.scores, w.cand, w.cmeta, nch, L, (const S*)qI, (const S*)wI,
+      (const S*)KI, em, idx_out);
   return hipGetLastError();
 }
 
-hipError_t launch_index_topk_decode(const csa_index_desc& d, const void* qI, const void* wI,
-                                    const void* KI, const int64_t* pos, int32_t* idx_out,
-                                    void* wsp, hipStream_t st, EntryMap em) {
+// D1 over the entries that exist before each sequence's position steps
+// (entries s < floor(pos / m)): it reads no row that step's compressor writes.
+hipError_t launch_index_topk_decode_score(const csa_index_desc& d, const void* qI,
+                                          const void* wI, const void* KI, const int64_t* pos,
+                                          void* wsp, hipStream_t st, EntryMap em) {
   DecWs w = carve(wsp, d);
-  const int B = d.batch;
   const int64_t nch = dec_chunks(d);
-  const int ncopies = dec_hist_copies(nch);
-  const dim3 grid((unsigned)nch, (unsigned)B);
+  const int L = dec_cand_per_chunk(d);
+  const dim3 grid((unsigned)nch, (unsigned)d.batch);
 #define CSA_DSCORE(TT, PG)                                                                    \
   dec_score_kernel<TT, HI, CI, PG><<<grid, 256, 0, st>>>(                                     \
       (const TT::S*)qI, (const TT::S*)wI, (const TT::S*)KI, pos, d.n_entries, d.m, d.k,        \
-      w.scores, w.hist, ncopies, em)
+      w.scores, w.cand, w.cmeta, L, nch, em)
   CSA_INDEX_DISPATCH(d.n_heads, d.head_dim, {
     if (d.dtype == CSA_BF16) {
       if (em.table) CSA_DSCORE(BF16, true);
@@ -1335,9 +1293,32 @@ hipError_t launch_index_topk_decode(const csa_index_desc& d, const void* qI, con
     }
   });
 #undef CSA_DSCORE
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+// D2 after launch_index_topk_decode_score on the same workspace, once the
+// step's new entries are in the cache: the new entry of each sequence is
+// scored here.
+hipError_t launch_index_topk_decode_select(const csa_index_desc& d, const void* qI,
+                                           const void* wI, const void* KI, const int64_t* pos,
+                                           int32_t* idx_out, void* wsp, hipStream_t st,
+                                           EntryMap em) {
+  DecWs w = carve(wsp, d);
+  const int64_t nch = dec_chunks(d);
+  const int L = dec_cand_per_chunk(d);
+  CSA_INDEX_DISPATCH(d.n_heads, d.head_dim, {
+    if (d.dtype == CSA_BF16)
+      return dec_select<BF16, HI, CI, true>(d, w, nch, L, pos, idx_out, qI, wI, KI, em, st);
+    return dec_select<F32, HI, CI, true>(d, w, nch, L, pos, idx_out, qI, wI, KI, em, st);
+  });
+}
+
+hipError_t launch_index_topk_decode(const csa_index_desc& d, const void* qI, const void* wI,
+                                    const void* KI, const int64_t* pos, int32_t* idx_out,
+                                    void* wsp, hipStream_t st, EntryMap em) {
+  hipError_t e = launch_index_topk_decode_score(d, qI, wI, KI, pos, wsp, st, em);
   if (e != hipSuccess) return e;
-  return dec_select(d, w, nch, ncopies, pos, idx_out, st);
+  return launch_index_topk_decode_select(d, qI, wI, KI, pos, idx_out, wsp, st, em);
 }
 
 // ---------------------------------------------------------------------------
@@ -1358,8 +1339,9 @@ static csa_index_desc long_rows_desc(const csa_index_desc& d) {
   csa_index_desc dd = d;
   const int64_t last = (d.t0 + d.n) / d.m;  // visible entries of the last row
   dd.n_entries = last < d.n_entries ? last : d.n_entries;
-  // rows per sub-batch: about 2 GiB of decode workspace (20 B per entry and row)
-  const int64_t r = ((int64_t)1 << 31) / (20 * (dd.n_entries > 0 ? dd.n_entries : 1));
+  // rows per sub-batch: about 2 GiB of decode workspace
+  dd.batch = 1;
+  const int64_t r = ((int64_t)1 << 31) / (int64_t)index_decode_ws_bytes(dd);
   dd.batch = (int32_t)(r < 1 ? 1 : r > 1024 ? 1024 : r);
   if (dd.batch > d.n) dd.batch = (int32_t)(d.n > 0 ? d.n : 1);
   return dd;
@@ -1406,21 +1388,23 @@ hipError_t launch_index_topk_decode_fp4(const csa_index_desc& d, const uint8_t* 
                                         void* wsp, hipStream_t st, EntryMap em) {
   DecWs w = carve(wsp, d);
   const int64_t nch = dec_chunks(d);
-  const int ncopies = dec_hist_copies(nch);
+  const int L = dec_cand_per_chunk(d);
   const dim3 grid((unsigned)nch, (unsigned)d.batch);
   CSA_INDEX_DISPATCH(d.n_heads, d.head_dim, {
     if (em.table)
       dec_score_fp4_kernel<HI, CI, true><<<grid, 256, 0, st>>>(
-          qc, qe, (const uint16_t*)wI, kc, ke, pos, d.n_entries, d.m, d.k, w.scores, w.hist,
-          ncopies, em);
+          qc, qe, (const uint16_t*)wI, kc, ke, pos, d.n_entries, d.m, d.k, w.scores, w.cand,
+          w.cmeta, L, nch, em);
     else
       dec_score_fp4_kernel<HI, CI, false><<<grid, 256, 0, st>>>(
-          qc, qe, (const uint16_t*)wI, kc, ke, pos, d.n_entries, d.m, d.k, w.scores, w.hist,
-          ncopies, em);
+          qc, qe, (const uint16_t*)wI, kc, ke, pos, d.n_entries, d.m, d.k, w.scores, w.cand,
+          w.cmeta, L, nch, em);
   });
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return dec_select(d, w, nch, ncopies, pos, idx_out, st);
+  // the FP4 scorer scores every visible entry, the new one included
+  return dec_select<BF16, 4, 64, false>(d, w, nch, L, pos, idx_out, nullptr, nullptr, nullptr, em,
+                                        st);
 }
 
 hipError_t launch_fp4_rotate_quant(int dtype, const void* x, int64_t rows, int width,

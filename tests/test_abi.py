@@ -92,11 +92,13 @@ def test_workspace_and_state_sizes(lib):
     ad = L.attn_desc(batch=4, nh=64, c=512, k=1024, n_entries=262144, dtype=L.CSA_BF16)
     assert L.workspace_bytes("sparse_mqa_decode", ad) > 0
     assert lib.csa_workspace_bytes(0, None) == 0
-    # the decode top-k's histograms lead its workspace; no other entry has zero bytes
+    # no entry carries state between calls in its workspace: nothing needs clearing
     dd = L.IndexDesc(0, 4, 16, 64, 4, 1024, L.CSA_BF16, 262144)
-    z = L.workspace_zero_bytes("index_topk_decode", dd)
-    assert 0 < z < L.workspace_bytes("index_topk_decode", dd)
-    assert z == 4 * (8 + 1) * 2048 * 4  # 8 coarse copies + the fine histogram per sequence
+    assert L.workspace_zero_bytes("index_topk_decode", dd) == 0
+    # scores (4 B per entry) plus each 1024-entry chunk's candidates (8 B each) and record
+    chunks, per_chunk = 256, 2 * 1024 // 256 + 16
+    assert L.workspace_bytes("index_topk_decode", dd) == (
+        4 * 262144 * 4 + 4 * chunks * per_chunk * 8 + 4 * chunks * 16)
     assert L.workspace_zero_bytes("index_topk_prefill", idx) == 0
     assert L.workspace_zero_bytes("sparse_mqa_decode", ad) == 0
     assert lib.csa_workspace_zero_bytes(3, None) == 0
@@ -148,7 +150,7 @@ def test_index_and_attention_reject(lib):
     assert lib.csa_index_topk_prefill(ctypes.byref(too_many), _p(), _p(), _p(), _p(), _p(), 1 << 40, None) == -2
     long_rows = L.IndexDesc(1 << 20, 1, 16, 64, 4, 512, L.CSA_BF16, 1 << 18)
     assert lib.csa_index_topk_prefill(ctypes.byref(long_rows), _p(), _p(), _p(), _p(), _p(), 8, None) == -3
-    assert L.workspace_zero_bytes("index_topk_prefill", long_rows) > 0
+    assert L.workspace_zero_bytes("index_topk_prefill", long_rows) == 0
     short_rows = L.IndexDesc(1 << 14, 1, 16, 64, 4, 512, L.CSA_BF16, 1 << 12)
     assert L.workspace_zero_bytes("index_topk_prefill", short_rows) == 0
     dd = L.IndexDesc(0, 2, 16, 64, 4, 8, L.CSA_BF16, 100)
@@ -240,7 +242,7 @@ def test_fp4_calls_reject(lib):
     assert lib.csa_index_topk_decode_fp4(ctypes.byref(dec), *([_p()] * 7), None, 0, None) == -3
     assert lib.csa_index_topk_decode_fp4(ctypes.byref(dec), None, *([_p()] * 7), 1 << 40, None) == -1
     assert L.workspace_bytes("index_topk_decode_fp4", dec) == L.workspace_bytes("index_topk_decode", dec)
-    assert L.workspace_zero_bytes("index_topk_decode_fp4", dec) > 0
+    assert L.workspace_zero_bytes("index_topk_decode_fp4", dec) == 0
 
 
 def test_paged_calls_reject(lib):
@@ -321,8 +323,9 @@ def test_chunked_prefill_rejects(lib):
     di = L.IndexDesc(16, 1, 16, 64, 4, 512, L.CSA_BF16, 1 << 20, L.CSA_BF16, 4 * 16384)
     assert lib.csa_index_topk_prefill(ctypes.byref(di), *([_p()] * 5), 1 << 40, None) == -2
     di = L.IndexDesc(16, 1, 16, 64, 4, 512, L.CSA_BF16, 1 << 20, L.CSA_F32, 4 * 16384)
-    assert L.workspace_zero_bytes("index_topk_prefill", di) > 0
+    long_ws = L.workspace_bytes("index_topk_prefill", di)  # the decode selector's workspace
     di.t0 = 0
+    assert L.workspace_bytes("index_topk_prefill", di) != long_ws  # the register selector's
     assert L.workspace_zero_bytes("index_topk_prefill", di) == 0
     a = L.attn_desc(n=8, nh=8, c=128, k=4, t0=-1)
     assert lib.csa_sparse_mqa_prefill(ctypes.byref(a), *([_p()] * 6), None, 0, None) == -1
@@ -334,7 +337,7 @@ def test_noalloc_topk_rejects(lib):
     assert lib.csa_noalloc_scratch_bytes() == 32 << 20
     ok = L.IndexDesc(0, 32, 16, 64, 4, 512, L.CSA_BF16, 32768)
     assert L.workspace_bytes("index_topk_decode", ok) <= lib.csa_noalloc_scratch_bytes()
-    big = L.IndexDesc(0, 64, 16, 64, 4, 512, L.CSA_BF16, 32768)
+    big = L.IndexDesc(0, 128, 16, 64, 4, 512, L.CSA_BF16, 65536)
     assert L.workspace_bytes("index_topk_decode", big) > lib.csa_noalloc_scratch_bytes()
     f = lib.csa_index_topk_decode_noalloc
     assert f(ctypes.byref(big), _p(), _p(), _p(), _p(), _p(), None) == -3
@@ -343,3 +346,17 @@ def test_noalloc_topk_rejects(lib):
     assert f(None, _p(), _p(), _p(), _p(), _p(), None) == -1
     bad = L.IndexDesc(0, 2, 16, 64, 4, 0, L.CSA_BF16, 100)
     assert f(ctypes.byref(bad), _p(), _p(), _p(), _p(), _p(), None) in (-1, -2)
+
+
+def test_split_topk_calls_reject(lib):
+    """The two halves of the decode top-k validate like the single call."""
+    d = L.IndexDesc(0, 2, 16, 64, 4, 8, L.CSA_BF16, 100)
+    need = L.workspace_bytes("index_topk_decode", d)
+    sc, se = lib.csa_index_topk_decode_score, lib.csa_index_topk_decode_select
+    assert sc(ctypes.byref(d), None, _p(), _p(), _p(), _p(), need, None) == -1
+    assert sc(ctypes.byref(d), _p(), _p(), _p(), _p(), _p(), need - 1, None) == -3
+    assert sc(None, _p(), _p(), _p(), _p(), _p(), need, None) == -1
+    assert se(ctypes.byref(d), _p(), _p(), _p(), _p(), None, _p(), need, None) == -1
+    assert se(ctypes.byref(d), _p(), _p(), _p(), _p(), _p(), None, need, None) == -3
+    bad = L.IndexDesc(0, 2, 12, 64, 4, 8, L.CSA_BF16, 100)  # 12 heads: not a kernel shape
+    assert sc(ctypes.byref(bad), _p(), _p(), _p(), _p(), _p(), need, None) in (-1, -2)

@@ -156,6 +156,62 @@ def test_index_topk_decode_one_coarse_bin(lib, dtype, ne):
         check_topk_sets(got[b][None], sc, k, m, t0=p)
 
 
+@pytest.mark.parametrize("ne,pos,k", [
+    (32768, [131071, 131070, 4 * 20000 - 1, 4 * 20000, 2047, 517], 512),  # emitting and not
+    (262144, [1048575, 999999], 1024),
+    (5000, [4 * 129 - 1, 4 * 130 - 1, 4 * 129 + 2], 128),  # visible counts k+1 and k+2 around k
+])
+def test_index_topk_decode_split_calls_equal_one_call(lib, ne, pos, k):
+    """Scoring the cached keys first (csa_index_topk_decode_score) and then
+    selecting with the step's new entry folded in (_select) gives bitwise the
+    single call's indices, which match the oracle's sets."""
+    _say("index decode split", ne, pos, k)
+    B, hI, cI, m = len(pos), 16, 64, 4
+    key = ("isplit", ne, k)
+    qI = I.normal((B, hI, cI), key + ("q",), dtype="bf16", device=DEV)
+    wI = I.uniform((B, hI), key + ("w",), dtype="bf16", device=DEV)
+    KI = I.normal((B, ne, cI), key + ("K",), dtype="bf16", device=DEV)
+    pos_t = torch.tensor(pos, dtype=torch.int64, device=DEV)
+    one = lib.csa_index_topk_decode(qI, wI, KI, pos_t, m, k)
+    for rep in range(2):
+        lib.csa_index_topk_decode_score(qI, wI, KI, pos_t, m, k, ws_slot="split_test")
+        two = lib.csa_index_topk_decode_select(qI, wI, KI, pos_t, m, k, ws_slot="split_test")
+        torch.cuda.synchronize()
+        assert torch.equal(one.cpu(), two.cpu()), f"repeat {rep}"
+    got = one.cpu().numpy()
+    for b, p in enumerate(pos):
+        vis = min(ne, (p + 1) // m)
+        sc = O.index_scores(f64(qI[b])[None], f64(wI[b])[None], f64(KI[b, :vis]), m, t0=p)
+        check_topk_sets(got[b][None], sc, k, m, t0=p)
+
+
+@pytest.mark.parametrize("boost_rows,k", [
+    (slice(3072, 4096), 512),   # every winner in chunk 3: the exact row fallback
+    (slice(5000, 5060), 512),   # 60 boosted keys in chunk 4, more than its 48 candidates
+    (slice(100, 140), 512),     # 40: within what chunk 0 offers
+])
+def test_index_topk_decode_concentrated_winners(lib, boost_rows, k):
+    """When one chunk holds more of the winners than the candidates it keeps,
+    the selection falls back to all of the row's scores; the sets still
+    match the oracle."""
+    _say("index decode concentrated", boost_rows, k)
+    B, hI, cI, m, ne = 2, 16, 64, 4, 32768
+    key = ("iconc", boost_rows.start, boost_rows.stop, k)
+    qI = I.normal((B, hI, cI), key + ("q",), dtype="bf16", device=DEV)
+    wI = I.uniform((B, hI), key + ("w",), dtype="bf16", device=DEV)
+    KI = I.normal((B, ne, cI), key + ("K",), dtype="bf16", device=DEV)
+    KI[:, boost_rows] *= 4.0
+    pos = [4 * ne - 1, 4 * ne - 2]  # one step emits an entry, the other does not
+    pos_t = torch.tensor(pos, dtype=torch.int64, device=DEV)
+    idx = lib.csa_index_topk_decode(qI, wI, KI, pos_t, m, k)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    for b, p in enumerate(pos):
+        vis = min(ne, (p + 1) // m)
+        sc = O.index_scores(f64(qI[b])[None], f64(wI[b])[None], f64(KI[b, :vis]), m, t0=p)
+        check_topk_sets(got[b][None], sc, k, m, t0=p)
+
+
 def test_index_topk_decode_leaves_its_counters_zero(lib):
     """The histograms lead the workspace, must be zero when a call starts and
     are zero again after it: a second call on the same workspace (no clearing

@@ -42,7 +42,7 @@ def test_noalloc_topk_matches_workspace_call(lib):
 
 
 def test_noalloc_topk_rejects_oversized(lib):
-    B, ne = 64, 32768  # 44.8 MiB of scratch > 32 MiB
+    B, ne = 128, 65536  # 34 MiB of scratch > 32 MiB
     qI, wI, KI, p = _case(B, 16, 64, 4, 512, ne, [4 * ne - 1] * B, "big")
     with pytest.raises(Exception):
         lib.csa_index_topk_decode_noalloc(qI, wI, KI, p, 4, 512)
