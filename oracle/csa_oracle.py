@@ -488,3 +488,93 @@ def index_scores_fp4(qI, wI, KI, m, t0=0):
     qc, qe = fp4_quant(hadamard(qI))
     kc, ke = fp4_quant(hadamard(KI))
     return index_scores(fp4_dequant(qc, qe), wI, fp4_dequant(kc, ke), m, t0=t0)
+
+
+# ---------------------------------------------------------------------------
+# O11: backward of the core attention.  [R] section 4.3 asks for a
+# deterministic attention backward (no atomic adds: per-unit accumulation
+# buffers and a deterministic global sum); what it computes is the chain rule
+# through the forward of eq 19 and 27 with the query RMSNorm / RoPE and the
+# output's inverse RoPE of section 2.3.3.  Gradients are taken with respect
+# to the raw queries, the stored window rows and entries (the compressor's
+# own backward is not part of it) and the sink logits, for an upstream
+# gradient dout of the output.
+# ---------------------------------------------------------------------------
+def attention_backward_row(q_row, t, kv, sink, dout_row, scale, qk_norm=True, eps=1e-6,
+                           rope_dims=0, theta=10000.0):
+    """One query token t: q_row [nh, c] (raw), kv [N, c] its candidates (keys
+    and values), dout_row [nh, c] the gradient of its output.  Returns
+    (dq_row [nh, c], dkv [N, c], dsink [nh])."""
+    q = np.asarray(q_row, F64)
+    kv = np.asarray(kv, F64)
+    zs = np.asarray(sink, F64)
+    # forward, keeping what the backward needs
+    if qk_norm:
+        rr = np.sqrt(np.mean(q * q, axis=-1, keepdims=True) + eps)
+        nq = q / rr
+    else:
+        nq = q
+    qh = rope(nq, [t], rope_dims, theta)                         # the rotated query
+    z = scale * (qh @ kv.T)                                      # [nh, N]
+    M = np.maximum(np.max(z, axis=1, initial=-np.inf), zs)
+    e = np.exp(z - M[:, None])
+    es = np.exp(zs - M)
+    den = np.sum(e, axis=1) + es
+    p = e / den[:, None]
+    ps = es / den
+    o_rot = p @ kv                                               # before the inverse RoPE
+    # backward: o = R(-t) o_rot, so the gradient reaching o_rot is R(t) dout
+    do = rope(np.asarray(dout_row, F64), [t], rope_dims, theta)
+    dp = do @ kv.T                                               # [nh, N]
+    dd = np.sum(do * o_rot, axis=-1)                             # sum_j p_j dp_j
+    dz = p * (dp - dd[:, None])                                  # softmax with the sink term
+    dsink = -ps * dd
+    dqh = scale * (dz @ kv)
+    dkv = p.T @ do + scale * (dz.T @ qh)                         # as value, then as key
+    dn = rope(dqh, [t], rope_dims, theta, inverse=True)          # R(t)^T = R(-t)
+    if qk_norm:
+        dq = (dn - nq * np.mean(dn * nq, axis=-1, keepdims=True)) / rr
+    else:
+        dq = dn
+    return dq, dkv, dsink
+
+
+def sparse_mqa_backward(q, win_kv, comp, idx, sink, dout, n_win, scale, qk_norm=True,
+                        eps=1e-6, rope_dims=0, theta=10000.0):
+    """Gradients of sparse_mqa_prefill (unrounded) for upstream gradient dout
+    [n, nh, c]: (dq [n, nh, c], dwin [n, c], dcomp [n_e, c], dsink [nh]).  A
+    row that is a candidate of several queries sums their contributions."""
+    q = np.asarray(q, F64)
+    win_kv = np.asarray(win_kv, F64)
+    comp = np.asarray(comp, F64)
+    n, nh, c = q.shape
+    dq = np.zeros_like(q)
+    dwin = np.zeros_like(win_kv)
+    dcomp = np.zeros_like(comp)
+    dsink = np.zeros(nh)
+    for t in range(n):
+        wr = window_range(t, n_win)
+        sel = [s for s in np.asarray(idx[t]).tolist() if s >= 0]
+        kv = np.concatenate([win_kv[wr], comp[sel]], axis=0)
+        g_q, g_kv, g_s = attention_backward_row(q[t], t, kv, sink, dout[t], scale, qk_norm, eps,
+                                                rope_dims, theta)
+        dq[t] = g_q
+        dwin[wr] += g_kv[: len(wr)]
+        for a, s in enumerate(sel):
+            dcomp[s] += g_kv[len(wr) + a]
+        dsink += g_s
+    return dq, dwin, dcomp, dsink
+
+
+def dense_mqa_backward(q, win_kv, comp, sink, dout, m, n_win, scale, qk_norm=True, eps=1e-6,
+                       rope_dims=0, theta=10000.0):
+    """Gradients of dense_mqa_prefill: every visible entry s < floor((t+1)/m)
+    is a candidate of token t."""
+    n = np.asarray(q).shape[0]
+    ne = np.asarray(comp).shape[0]
+    idx = np.full((n, max(1, ne)), -1)
+    for t in range(n):
+        v = int(min(ne, visible_entries(t, m)))
+        idx[t, :v] = np.arange(v)
+    return sparse_mqa_backward(q, win_kv, comp, idx, sink, dout, n_win, scale, qk_norm, eps,
+                               rope_dims, theta)

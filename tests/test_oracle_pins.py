@@ -622,3 +622,115 @@ def test_fp4_quant_round_trip_and_error_bound():
     assert np.all(np.abs(dq - x) <= scale * 1.0 + 1e-15)
     assert np.all(np.abs(x) <= 6 * scale * (1 + 1e-12))
     assert np.all(np.abs(x).reshape(50, 4, 32).max(-1) > 3 * np.ldexp(1.0, ex) * (1 - 1e-12))
+
+
+# ------------------------------------------------- attention backward (O11)
+def _bwd_case(seed, rope_dims, qk_norm):
+    rng = np.random.default_rng(seed)
+    n, nh, c, m, n_win, k = 9, 2, 6, 2, 3, 2
+    q = rng.normal(size=(n, nh, c))
+    win = rng.normal(size=(n, c))
+    comp = rng.normal(size=(n // m, c))
+    sink = rng.normal(size=nh)
+    dout = rng.normal(size=(n, nh, c))
+    idx = np.full((n, k), -1)
+    for t in range(n):
+        v = (t + 1) // m
+        sel = rng.permutation(v)[:k]
+        idx[t, :len(sel)] = sel
+    kw = dict(qk_norm=qk_norm, eps=1e-3, rope_dims=rope_dims, theta=100.0)
+    return q, win, comp, idx, sink, dout, m, n_win, kw
+
+
+@pytest.mark.parametrize("rope_dims,qk_norm", [(0, False), (2, True), (4, True)])
+def test_attention_backward_matches_finite_differences(rope_dims, qk_norm):
+    """Central differences of L = sum(dout * out) in fp64 (step 1e-6) agree
+    with every gradient of the hand-derived backward, sparse and dense."""
+    q, win, comp, idx, sink, dout, m, n_win, kw = _bwd_case(3 + rope_dims, rope_dims, qk_norm)
+    scale = 0.4
+
+    def loss_sparse(q_, win_, comp_, sink_):
+        return float(np.sum(dout * O.sparse_mqa_prefill(q_, win_, comp_, idx, sink_, n_win, scale,
+                                                        store="f64", **kw)))
+
+    def loss_dense(q_, win_, comp_, sink_):
+        return float(np.sum(dout * O.dense_mqa_prefill(q_, win_, comp_, sink_, m, n_win, scale,
+                                                       store="f64", **kw)))
+
+    for loss, grads in (
+            (loss_sparse, O.sparse_mqa_backward(q, win, comp, idx, sink, dout, n_win, scale, **kw)),
+            (loss_dense, O.dense_mqa_backward(q, win, comp, sink, dout, m, n_win, scale, **kw))):
+        args = [q, win, comp, sink]
+        for a, (x, g) in enumerate(zip(args, grads)):
+            num = np.zeros_like(x)
+            h = 1e-6
+            for pos in np.ndindex(x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[pos] += h
+                xm[pos] -= h
+                ap, am = list(args), list(args)
+                ap[a], am[a] = xp, xm
+                num[pos] = (loss(*ap) - loss(*am)) / (2 * h)
+            np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-7)
+
+
+def test_attention_backward_matches_torch_autograd():
+    """The same gradients from torch's automatic differentiation (fp64, CPU)
+    of the forward written with torch operations."""
+    torch = pytest.importorskip("torch")
+    q, win, comp, idx, sink, dout, m, n_win, kw = _bwd_case(11, 4, True)
+    scale, eps, r, theta = 0.4, kw["eps"], kw["rope_dims"], kw["theta"]
+    T = lambda x: torch.tensor(x, dtype=torch.float64, requires_grad=True)  # noqa: E731
+    tq, tw, tc, ts = T(q), T(win), T(comp), T(sink)
+    n, nh, c = q.shape
+
+    def rot(x, pos, sign):
+        x0, x1 = x[..., c - r::2], x[..., c - r + 1::2]
+        ang = sign * pos * theta ** (-2.0 * torch.arange(r // 2, dtype=torch.float64) / r)
+        y0 = x0 * torch.cos(ang) - x1 * torch.sin(ang)
+        y1 = x0 * torch.sin(ang) + x1 * torch.cos(ang)
+        out = x.clone()
+        out[..., c - r::2] = y0
+        out[..., c - r + 1::2] = y1
+        return out
+
+    outs = []
+    for t in range(n):
+        qn = tq[t] / torch.sqrt((tq[t] ** 2).mean(-1, keepdim=True) + eps)
+        qh = rot(qn, float(t), 1.0)
+        wr = O.window_range(t, n_win).tolist()
+        sel = [s for s in idx[t].tolist() if s >= 0]
+        kv = torch.cat([tw[wr], tc[sel]], 0)
+        z = scale * qh @ kv.T
+        allz = torch.cat([z, ts[:, None]], 1)
+        pz = torch.softmax(allz, 1)[:, :-1]
+        outs.append(rot(pz @ kv, float(t), -1.0))
+    (torch.stack(outs) * torch.tensor(dout)).sum().backward()
+    got = O.sparse_mqa_backward(q, win, comp, idx, sink, dout, n_win, scale, **kw)
+    for g, x in zip(got, (tq, tw, tc, ts)):
+        np.testing.assert_allclose(g, x.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_attention_backward_logit_gradients_sum_to_zero():
+    """Adding one constant to every logit and the sink leaves the output
+    unchanged, so the logit gradients of a row (candidates and sink) sum to
+    zero: checked through a query of all zeros (qk_norm off), where the
+    gradient of the sink equals minus the summed candidate-logit gradients."""
+    rng = np.random.default_rng(7)
+    nh, c, N = 2, 4, 5
+    kv = rng.normal(size=(N, c))
+    sink = rng.normal(size=nh)
+    dout = rng.normal(size=(nh, c))
+    q = rng.normal(size=(nh, c))
+    dq, dkv, dsink = O.attention_backward_row(q, 0, kv, sink, dout, 1.0, qk_norm=False)
+    # d(loss)/d(shift all candidate logits) = sum_j dz_j = -dsink by the identity;
+    # shifting every candidate logit by s is adding s / scale to q . kv_j for all j,
+    # which the direction q -> q + s * v with kv v = 1 would do: use finite differences
+    s = 1e-6
+    def out(sh):
+        z = q @ kv.T + sh
+        M = np.maximum(z.max(1), sink)
+        e, es = np.exp(z - M[:, None]), np.exp(sink - M)
+        return ((e / (e.sum(1) + es)[:, None]) @ kv * dout).sum()
+    dz_sum = (out(s) - out(-s)) / (2 * s)
+    np.testing.assert_allclose(dz_sum, -dsink.sum(), rtol=1e-6)
