@@ -42,6 +42,7 @@ from long_context_attention_10_amd import configs, inputs as I  # noqa: E402
 
 PEAK_BF16 = 2.5e15      # dense bf16 matrix FLOP/s, MI355X
 PEAK_HBM = 8.0e12       # HBM3E bytes/s, MI355X
+PEAK_FP32 = 157.3e12    # fp32 vector FLOP/s, MI355X
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mqa_prefill_bf16_64k_traffic.txt")
 MQA_SOURCE = os.path.join(ROOT, "long_context_attention_10_amd", "csrc", "attention_bf16.hip")
 
@@ -688,6 +689,37 @@ def cpu_baseline(pf, sample_tokens=2048, sample_rows=48):
                       f"attention {t_att * 1e3:.3f} ms per token)"}
 
 
+def backward_record(steps, dev="cuda"):
+    """csa_sparse_mqa_backward and hca_dense_mqa_backward on the 2K-token fp32
+    CSA workload's shapes (8 heads x 128, k = 64, window 128, m = 4; the
+    dense call over the same entries), timed with events; algorithmic work
+    10 nh c FLOP per (query, candidate) pair (logits, dp, dq and both parts
+    of the row gradient), against the fp32 vector peak."""
+    cfg = configs.get("csa_prefill_2k_f32")
+    t = I.csa_prefill_inputs(cfg, device=dev)
+    m, ov, k, nw, c, nh = cfg["m"], cfg["overlap"], cfg["k"], cfg["n_win"], cfg["c"], cfg["nh"]
+    main_ = L.csa_compress_prefill(t["H"], t["W_kv"], t["W_z"], t["ape"], m, ov, W_win=t["W_win"])
+    kI = L.csa_compress_prefill(t["H"], t["WI_kv"], t["WI_z"], t["apeI"], m, ov)
+    idx = L.csa_index_topk_prefill(t["qI"], t["wI"], kI["comp"], m, k)
+    dout = I.normal(tuple(t["q"].shape), (0, cfg["name"], "dout"), device=dev)
+    n = cfg["n"]
+    tt = torch.arange(n, device=dev)
+    win_pairs = int(torch.clamp(tt + 1, max=nw).sum().item())
+    pairs_s = win_pairs + int((idx >= 0).sum().item())
+    pairs_d = win_pairs + int(torch.clamp((tt + 1) // m, max=main_["comp"].shape[0]).sum().item())
+    res = {"workload": cfg["name"] + " attention backward", "n": n, "nh": nh, "c": c, "k": k}
+    for nm, fn, pairs in (
+            ("sparse", lambda: L.csa_sparse_mqa_backward(t["q"], main_["win"], main_["comp"], idx,
+                                                         t["sink"], dout, n_win=nw), pairs_s),
+            ("dense", lambda: L.hca_dense_mqa_backward(t["q"], main_["win"], main_["comp"],
+                                                       t["sink"], dout, m, n_win=nw), pairs_d)):
+        ms = float(np.median(time_region(fn, max(5, steps), 2)))
+        fl = 10.0 * nh * c * pairs
+        res[nm] = {"ms": ms, "pairs": pairs, "tokens_per_s": n / (ms * 1e-3),
+                   "tflops": fl / (ms * 1e-3) / 1e12, "frac_fp32": fl / (ms * 1e-3) / PEAK_FP32}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -776,6 +808,9 @@ def main():
                                   / (ha_ms * 1e-3) / PEAK_HBM}
         del hp
         torch.cuda.empty_cache()
+    # the deterministic attention backward at the 2K fp32 workload: entries,
+    # window rows and the selection from the forward path, dout ~ N(0, 1)
+    rec["backward"] = backward_record(a.steps)
     # selection on bf16-rounded index scores ([R] section 4.4): its time and
     # its recall of the fp32-score selection, row by row (-1 slots excluded)
     idx32 = pf.idx.clone()

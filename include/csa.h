@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 7
+#define CSA_ABI_VERSION 8
 
 typedef enum csa_status {
   CSA_OK = 0,
@@ -490,7 +490,9 @@ typedef enum csa_entry {
   CSA_ENTRY_DENSE_MQA_DECODE = 7,
   CSA_ENTRY_QUERY_PROJ = 8,
   CSA_ENTRY_OUTPUT_PROJ = 9,
-  CSA_ENTRY_INDEX_TOPK_DECODE_FP4 = 10
+  CSA_ENTRY_INDEX_TOPK_DECODE_FP4 = 10,
+  CSA_ENTRY_SPARSE_MQA_BACKWARD = 11,
+  CSA_ENTRY_DENSE_MQA_BACKWARD = 12
 } csa_entry;
 
 /* ------------------------------------------------------------------------
@@ -556,6 +558,38 @@ typedef struct {
  * The [n, groups*d_g] intermediate is rounded to bf16 in the workspace. */
 int csa_output_proj(const csa_oproj_desc* desc, const void* o, const void* wo_a, const void* wo_b,
                     void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Backward of the core attention ([R] section 4.3: deterministic training;
+ * the attention backward accumulates in independent per-unit buffers and
+ * sums them deterministically, with no atomic adds).  The gradients are the
+ * chain rule through the forward of csa_sparse_mqa_prefill /
+ * hca_dense_mqa_prefill (eq 19, 27; the query RMSNorm and RoPE and the
+ * output's inverse RoPE of section 2.3.3), for an upstream gradient dout of
+ * their output, taken with respect to
+ *   dq    [n, nh, c]   the raw queries q,
+ *   dwin  [n, c]       the window rows win_kv (row t is position t),
+ *   dcomp [n_e, c]     the entries comp (rows no query attends to get 0),
+ *   dsink [nh]         the sink logits (fp32).
+ * A row that is a candidate of several queries receives the sum of their
+ * contributions.  Query tokens are split into min(256, n) contiguous blocks,
+ * one workgroup each, that add into their own buffers in token order; a
+ * second kernel sums the buffers in block order, so results are bitwise
+ * repeatable.  The softmax statistics are recomputed (no forward state is
+ * taken).  Supported: dtype CSA_F32 (every tensor fp32), c in {128, 256,
+ * 512}, nh in {4, 8, 16} with 512 <= nh*c <= 2048, t0 = 0; otherwise
+ * CSA_ERR_UNSUPPORTED.  The workspace (CSA_ENTRY_SPARSE_MQA_BACKWARD /
+ * _DENSE_MQA_BACKWARD) holds the per-block buffers: about
+ * min(256, n) * (n_e + n/min(256,n) + n_win) * c * 4 bytes; it is cleared by
+ * the call itself.  q, win_kv, comp, idx, sink as for the forward call. */
+int csa_sparse_mqa_backward(const csa_attn_desc* desc, const void* q, const void* win_kv,
+                            const void* comp, const int32_t* idx, const float* sink,
+                            const void* dout, void* dq, void* dwin, void* dcomp, float* dsink,
+                            void* ws, size_t ws_bytes, void* stream);
+int hca_dense_mqa_backward(const csa_attn_desc* desc, const void* q, const void* win_kv,
+                           const void* comp, const float* sink, const void* dout, void* dq,
+                           void* dwin, void* dcomp, float* dsink, void* ws, size_t ws_bytes,
+                           void* stream);
 
 /* Workspace bytes needed by `entry` for the descriptor `desc` (a pointer to
  * the csa_*_desc type that entry takes).  Returns 0 on a null descriptor. */

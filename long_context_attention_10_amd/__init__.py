@@ -22,7 +22,8 @@ LIB_PATH = os.path.join(_HERE, "libcsa.so")
 CSA_F32, CSA_BF16 = 0, 1
 ENTRY = dict(compress_prefill=0, compress_decode=1, index_topk_prefill=2, index_topk_decode=3,
              sparse_mqa_prefill=4, sparse_mqa_decode=5, dense_mqa_prefill=6, dense_mqa_decode=7,
-             query_proj=8, output_proj=9, index_topk_decode_fp4=10)
+             query_proj=8, output_proj=9, index_topk_decode_fp4=10, sparse_mqa_backward=11,
+             dense_mqa_backward=12)
 EXPORTED = ["csa_compress_prefill", "csa_compress_decode", "csa_state_bytes", "csa_state_init",
             "csa_index_topk_prefill", "csa_index_topk_decode", "csa_sparse_mqa_prefill",
             "csa_sparse_mqa_decode", "hca_dense_mqa_prefill", "hca_dense_mqa_decode",
@@ -33,7 +34,8 @@ EXPORTED = ["csa_compress_prefill", "csa_compress_decode", "csa_state_bytes", "c
             "csa_sparse_mqa_decode_paged", "hca_dense_mqa_decode_paged",
             "csa_indexer_fp4_quant_decode_paged", "csa_index_topk_decode_fp4_paged",
             "csa_index_topk_decode_noalloc", "csa_noalloc_scratch_bytes",
-            "csa_index_topk_decode_score", "csa_index_topk_decode_select"]
+            "csa_index_topk_decode_score", "csa_index_topk_decode_select",
+            "csa_sparse_mqa_backward", "hca_dense_mqa_backward"]
 
 
 class CompressDesc(ctypes.Structure):
@@ -125,6 +127,8 @@ def load(path: str = LIB_PATH):
     lib.csa_index_topk_decode_fp4_paged.argtypes = [P] * 7 + [I32] + [P] * 3 + [S, P]
     lib.csa_index_topk_decode_noalloc.argtypes = [P] * 7
     lib.csa_index_topk_decode_score.argtypes = [P] * 6 + [S, P]
+    lib.csa_sparse_mqa_backward.argtypes = [P] * 12 + [S, P]
+    lib.hca_dense_mqa_backward.argtypes = [P] * 11 + [S, P]
     lib.csa_index_topk_decode_select.argtypes = [P] * 7 + [S, P]
     lib.csa_noalloc_scratch_bytes.restype = S
     lib.csa_noalloc_scratch_bytes.argtypes = []
@@ -512,6 +516,57 @@ def attn_desc(n=0, batch=1, nh=1, c=0, k=0, m=1, n_win=128, dtype=CSA_F32, scale
         scale = c ** -0.5
     return AttnDesc(n, batch, nh, c, k, m, n_win, dtype, scale, int(qk_norm), eps, rope_dims,
                     rope_theta, n_entries, t0)
+
+
+def _mqa_backward(sparse, q, win_kv, comp, idx, sink, dout, m, n_win, scale, qk_norm, eps,
+                  rope_dims, rope_theta):
+    lib = load()
+    n, nh, c = q.shape
+    ne = comp.shape[0]
+    k = idx.shape[1] if sparse else 0
+    _expect(win_kv, (n, c), q.dtype, "win_kv")
+    _expect(dout, (n, nh, c), q.dtype, "dout")
+    _expect(comp, (ne, c), q.dtype, "comp")
+    _expect(sink, (nh,), torch.float32, "sink")
+    if sparse:
+        _expect(idx, (n, k), torch.int32, "idx")
+    desc = attn_desc(n=n, nh=nh, c=c, k=k, m=m, n_win=n_win, dtype=_dt(q), scale=scale,
+                     qk_norm=qk_norm, eps=eps, rope_dims=rope_dims, rope_theta=rope_theta,
+                     n_entries=ne)
+    dq = torch.empty_like(q)
+    dwin = torch.empty_like(win_kv)
+    dcomp = torch.empty_like(comp)
+    dsink = torch.empty(nh, dtype=torch.float32, device=q.device)
+    name = "sparse_mqa_backward" if sparse else "dense_mqa_backward"
+    ws, wsb = workspace(workspace_bytes(name, desc), q.device, "mqa_bwd")
+    if sparse:
+        st = lib.csa_sparse_mqa_backward(ctypes.byref(desc), _ptr(q), _ptr(win_kv), _ptr(comp),
+                                         _ptr(idx), _ptr(sink), _ptr(dout), _ptr(dq), _ptr(dwin),
+                                         _ptr(dcomp), _ptr(dsink), _ptr(ws), wsb,
+                                         _stream(q.device))
+    else:
+        st = lib.hca_dense_mqa_backward(ctypes.byref(desc), _ptr(q), _ptr(win_kv), _ptr(comp),
+                                        _ptr(sink), _ptr(dout), _ptr(dq), _ptr(dwin), _ptr(dcomp),
+                                        _ptr(dsink), _ptr(ws), wsb, _stream(q.device))
+    _check(st, "csa_" + name if sparse else "hca_" + name)
+    return dq, dwin, dcomp, dsink
+
+
+def csa_sparse_mqa_backward(q, win_kv, comp, idx, sink, dout, n_win=128, scale=None,
+                            qk_norm=True, eps=1e-6, rope_dims=0, rope_theta=10000.0):
+    """Gradients (dq, dwin, dcomp, dsink) of csa_sparse_mqa_prefill's output
+    for the upstream gradient dout (fp32 tensors)."""
+    return _mqa_backward(True, q, win_kv, comp, idx, sink, dout, 1, n_win,
+                         scale if scale is not None else q.shape[2] ** -0.5, qk_norm, eps,
+                         rope_dims, rope_theta)
+
+
+def hca_dense_mqa_backward(q, win_kv, comp, sink, dout, m, n_win=128, scale=None, qk_norm=True,
+                           eps=1e-6, rope_dims=0, rope_theta=10000.0):
+    """Gradients (dq, dwin, dcomp, dsink) of hca_dense_mqa_prefill's output."""
+    return _mqa_backward(False, q, win_kv, comp, None, sink, dout, m, n_win,
+                         scale if scale is not None else q.shape[2] ** -0.5, qk_norm, eps,
+                         rope_dims, rope_theta)
 
 
 def _win_rows(n, n_win, t0):

@@ -263,6 +263,13 @@ size_t csa_workspace_bytes(int entry, const void* desc) {
     }
     case CSA_ENTRY_SPARSE_MQA_PREFILL:
     case CSA_ENTRY_DENSE_MQA_PREFILL: return 0;
+    case CSA_ENTRY_SPARSE_MQA_BACKWARD:
+    case CSA_ENTRY_DENSE_MQA_BACKWARD: {
+      const csa_attn_desc* d = (const csa_attn_desc*)desc;
+      if (d->n < 0 || d->c <= 0 || d->n_heads <= 0 || d->n_win <= 0 || d->n_entries < 0)
+        return 0;
+      return mqa_backward_ws_bytes(*d);
+    }
     case CSA_ENTRY_QUERY_PROJ: {
       const csa_query_desc* d = (const csa_query_desc*)desc;
       if (d->n <= 0 || d->d_c <= 0) return 0;
@@ -539,6 +546,40 @@ int csa_sparse_mqa_prefill(const csa_attn_desc* d, const void* q, const void* wi
     return CSA_ERR_INVALID_ARG;
   return hip_status(launch_mqa_prefill(*d, ATTN_SPARSE, q, win_kv, comp, idx, sink, out,
                                        (hipStream_t)stream));
+}
+
+static int mqa_backward(const csa_attn_desc* d, int mode, const void* q, const void* win_kv,
+                        const void* comp, const int32_t* idx, const float* sink,
+                        const void* dout, void* dq, void* dwin, void* dcomp, float* dsink,
+                        void* ws, size_t ws_bytes, void* stream) {
+  const bool sparse = mode == ATTN_SPARSE;
+  int s = check_attn(d, false, sparse);
+  if (s) return s;
+  if (!mqa_backward_supported(*d)) return CSA_ERR_UNSUPPORTED;
+  if (!q || !win_kv || (sparse && !idx) || !sink || !dout || !dq || !dwin || !dsink ||
+      (d->n_entries > 0 && (!comp || !dcomp)))
+    return CSA_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < mqa_backward_ws_bytes(*d)) return CSA_ERR_WORKSPACE;
+  return hip_status(launch_mqa_backward(*d, mode, (const float*)q, (const float*)win_kv,
+                                        (const float*)comp, idx, sink, (const float*)dout,
+                                        (float*)dq, (float*)dwin, (float*)dcomp, dsink, ws,
+                                        (hipStream_t)stream));
+}
+
+int csa_sparse_mqa_backward(const csa_attn_desc* d, const void* q, const void* win_kv,
+                            const void* comp, const int32_t* idx, const float* sink,
+                            const void* dout, void* dq, void* dwin, void* dcomp, float* dsink,
+                            void* ws, size_t ws_bytes, void* stream) {
+  return mqa_backward(d, ATTN_SPARSE, q, win_kv, comp, idx, sink, dout, dq, dwin, dcomp, dsink,
+                      ws, ws_bytes, stream);
+}
+
+int hca_dense_mqa_backward(const csa_attn_desc* d, const void* q, const void* win_kv,
+                           const void* comp, const float* sink, const void* dout, void* dq,
+                           void* dwin, void* dcomp, float* dsink, void* ws, size_t ws_bytes,
+                           void* stream) {
+  return mqa_backward(d, ATTN_DENSE, q, win_kv, comp, nullptr, sink, dout, dq, dwin, dcomp,
+                      dsink, ws, ws_bytes, stream);
 }
 
 int csa_sparse_mqa_decode(const csa_attn_desc* d, const void* q, const void* win_ring,

@@ -139,6 +139,14 @@ hipError_t launch_mqa_decode(const csa_attn_desc& d, int mode, const void* q, co
                              const float* sink, void* out, void* ws, hipStream_t st,
                              EntryMap em = EntryMap());
 
+// Deterministic fp32 attention backward (backward.hip).
+bool mqa_backward_supported(const csa_attn_desc& d);
+size_t mqa_backward_ws_bytes(const csa_attn_desc& d);
+hipError_t launch_mqa_backward(const csa_attn_desc& d, int mode, const float* q, const float* win,
+                               const float* comp, const int32_t* idx, const float* sink,
+                               const float* dout, float* dq, float* dwin, float* dcomp,
+                               float* dsink, void* ws, hipStream_t st);
+
 // The layer around the attention calls (layer.hip).
 size_t query_proj_ws_bytes(const csa_query_desc& d);
 hipError_t launch_query_proj(const csa_query_desc& d, const void* H, const void* W_DQ,

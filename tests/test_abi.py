@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.csa_abi_version() == 7
+    assert lib.csa_abi_version() == 8
     for code in (0, -1, -2, -3, -4):
         assert len(lib.csa_status_string(code)) > 0
     assert lib.csa_status_string(-99) == b"unknown status"
@@ -360,3 +360,24 @@ def test_split_topk_calls_reject(lib):
     assert se(ctypes.byref(d), _p(), _p(), _p(), _p(), _p(), None, need, None) == -3
     bad = L.IndexDesc(0, 2, 12, 64, 4, 8, L.CSA_BF16, 100)  # 12 heads: not a kernel shape
     assert sc(ctypes.byref(bad), _p(), _p(), _p(), _p(), _p(), need, None) in (-1, -2)
+
+
+def test_backward_calls_reject(lib):
+    """The attention backward takes fp32 only, the supported head shapes and
+    a full workspace, checked before anything is enqueued."""
+    d = L.attn_desc(n=64, nh=8, c=128, k=16, n_entries=16, dtype=L.CSA_F32)
+    need = L.workspace_bytes("sparse_mqa_backward", d)
+    assert need > 0 and need == L.workspace_bytes("dense_mqa_backward", d)
+    sb, db = lib.csa_sparse_mqa_backward, lib.hca_dense_mqa_backward
+    assert sb(ctypes.byref(d), *([_p()] * 11), need - 1, None) == -3
+    assert sb(ctypes.byref(d), None, *([_p()] * 10), need, None) == -1
+    assert sb(ctypes.byref(d), _p(), _p(), _p(), None, *([_p()] * 7), need, None) == -1
+    assert db(ctypes.byref(d), *([_p()] * 10), need - 1, None) == -3
+    assert db(ctypes.byref(d), _p(), _p(), _p(), _p(), _p(), _p(), _p(), _p(), None, _p(),
+              need, None) == -1  # dsink missing
+    bf = L.attn_desc(n=64, nh=8, c=128, k=16, n_entries=16, dtype=L.CSA_BF16)
+    assert sb(ctypes.byref(bf), *([_p()] * 11), need, None) == -2
+    wide = L.attn_desc(n=64, nh=64, c=512, k=16, n_entries=16, dtype=L.CSA_F32)
+    assert sb(ctypes.byref(wide), *([_p()] * 11), 1 << 40, None) == -2
+    chunk = L.attn_desc(n=64, nh=8, c=128, k=16, n_entries=16, dtype=L.CSA_F32, t0=128)
+    assert sb(ctypes.byref(chunk), *([_p()] * 11), 1 << 40, None) == -2
