@@ -578,3 +578,77 @@ def dense_mqa_backward(q, win_kv, comp, sink, dout, m, n_win, scale, qk_norm=Tru
         idx[t, :v] = np.arange(v)
     return sparse_mqa_backward(q, win_kv, comp, idx, sink, dout, n_win, scale, qk_norm, eps,
                                rope_dims, theta)
+
+
+# ---------------------------------------------------------------------------
+# O12: FP8 storage of the KV rows ([A] "Q, K, V 映射与位置编码注入" and the
+# Compressor: act_quant of kv[..., :-rd] with block size 64 -- the channels
+# without RoPE are quantised to FP8, the RoPE channels keep their precision;
+# [R] section 2.3.4: the KV cache stores the RoPE dims in BF16 and the rest
+# in FP8).  Read as E4M3 (4 exponent bits, bias 7, 3 mantissa bits, largest
+# finite 448, subnormal step 2^-9) with one power-of-two scale per block of
+# 64 values, the smallest 2^e with max |x| <= 448 * 2^e; each x / 2^e rounds
+# to the nearest E4M3 value, ties to the even mantissa.
+# ---------------------------------------------------------------------------
+FP8_BLOCK = 64
+FP8_MAX = 448.0
+
+
+def fp8_e4m3_values():
+    """Every non-negative finite E4M3 value, indexed by its 7-bit code
+    (exponent field << 3 | mantissa): subnormals m * 2^-9 for field 0, else
+    (1 + m/8) * 2^(field - 7); field 15 with mantissa 7 is not a number."""
+    v = []
+    for ef in range(16):
+        for mt in range(8):
+            if ef == 15 and mt == 7:
+                v.append(np.nan)
+            elif ef == 0:
+                v.append(mt * 2.0 ** -9)
+            else:
+                v.append((1 + mt / 8.0) * 2.0 ** (ef - 7))
+    return np.array(v)
+
+
+def fp8_quant(x):
+    """Returns (codes, exps): codes 0..255 (bit 7 the sign, set only for a
+    nonzero magnitude), exps the block exponents e."""
+    x = np.asarray(x, F64)
+    nb = x.shape[-1] // FP8_BLOCK
+    xb = x.reshape(x.shape[:-1] + (nb, FP8_BLOCK))
+    amax = np.max(np.abs(xb), axis=-1)
+    # smallest e with amax <= 448 * 2^e: amax = f * 2^k, 448 = 0.875 * 2^9
+    f, k = np.frexp(amax)
+    e = np.where(amax > 0, np.where(f <= 0.875, k - 9, k - 8), 0).astype(np.int64)
+    a = np.abs(xb) / np.ldexp(1.0, e)[..., None]
+    grid = fp8_e4m3_values()[:127]                      # finite magnitudes, ascending
+    lo = np.clip(np.searchsorted(grid, a, side="right") - 1, 0, 126)
+    hi = np.minimum(lo + 1, 126)
+    dlo, dhi = a - grid[lo], grid[hi] - a
+    pick_up = (dhi < dlo) | ((dhi == dlo) & (lo % 2 == 1))
+    mag = np.where(pick_up, hi, lo)
+    sign = (xb < 0) & (mag > 0)
+    codes = (mag + 128 * sign).reshape(x.shape)
+    return codes.astype(np.int64), e
+
+
+def fp8_dequant(codes, exps):
+    """sign * E4M3 magnitude * 2^e of fp8_quant's output."""
+    codes = np.asarray(codes)
+    nb = codes.shape[-1] // FP8_BLOCK
+    cb = codes.reshape(codes.shape[:-1] + (nb, FP8_BLOCK))
+    v = np.where(cb >= 128, -1.0, 1.0) * fp8_e4m3_values()[cb & 127]
+    v = v * np.ldexp(1.0, np.asarray(exps))[..., None]
+    return v.reshape(codes.shape)
+
+
+def kv_fp8(rows, rope_dims):
+    """A stored KV row as its FP8 form holds it: the first c - r channels
+    quantised and dequantised, the last r (the RoPE channels) unchanged."""
+    rows = np.asarray(rows, F64)
+    c = rows.shape[-1]
+    out = rows.copy()
+    if c - rope_dims:
+        codes, e = fp8_quant(rows[..., : c - rope_dims])
+        out[..., : c - rope_dims] = fp8_dequant(codes, e)
+    return out

@@ -734,3 +734,52 @@ def test_attention_backward_logit_gradients_sum_to_zero():
         return ((e / (e.sum(1) + es)[:, None]) @ kv * dout).sum()
     dz_sum = (out(s) - out(-s)) / (2 * s)
     np.testing.assert_allclose(dz_sum, -dsink.sum(), rtol=1e-6)
+
+
+# ------------------------------------------------------- FP8 KV rows (O12)
+def test_fp8_quant_worked_examples():
+    g = GOLD["fp8_kv"]
+    for blk in ("a", "b"):
+        x = np.zeros(64)
+        vals = g["block_" + blk]
+        x[:len(vals)] = vals
+        codes, e = O.fp8_quant(x)
+        assert e.tolist() == [g["exp_" + blk]]
+        assert codes[:len(vals)].tolist() == g["codes_" + blk]
+        np.testing.assert_array_equal(O.fp8_dequant(codes, e)[:len(vals)], g["values_" + blk])
+
+
+def test_fp8_grid_round_trip_and_error_bound():
+    """Grid values times the scale come back exactly; otherwise the error is
+    at most half a grid step (2^-4 of the value for normals, 2^-10 of the
+    scale below 2^-6), and the scale is the smallest power of two that holds
+    the block's largest magnitude."""
+    grid = O.fp8_e4m3_values()[:127]
+    x = np.concatenate([grid, -grid[1:65]]) * 2.0 ** 3  # 191 values: three blocks less one
+    x = x[:128].reshape(2, 64)
+    x[:, 0] = 448 * 8.0  # pin e = 3 in both blocks
+    c, e = O.fp8_quant(x)
+    assert e.tolist() == [[3], [3]]
+    np.testing.assert_array_equal(O.fp8_dequant(c, e), x)
+    rng = np.random.default_rng(21)
+    y = rng.normal(size=(40, 256)) * np.exp(rng.normal(size=(40, 1)) * 3)
+    c, e = O.fp8_quant(y)
+    d = O.fp8_dequant(c, e)
+    scale = np.repeat(np.ldexp(1.0, e), 64, axis=-1)
+    normal = np.abs(y) >= 2.0 ** -6 * scale
+    assert np.all(np.abs(d - y)[normal] <= 2.0 ** -4 * np.abs(y)[normal] * (1 + 1e-12))
+    assert np.all(np.abs(d - y)[~normal] <= 2.0 ** -10 * scale[~normal] * (1 + 1e-12))
+    amax = np.abs(y).reshape(40, 4, 64).max(-1)
+    assert np.all(amax <= 448 * np.ldexp(1.0, e)) and np.all(amax > 224 * np.ldexp(1.0, e))
+    z, ez = O.fp8_quant(np.zeros((2, 64)))
+    assert (z == 0).all() and (ez == 0).all()
+
+
+def test_kv_fp8_keeps_rope_channels():
+    rng = np.random.default_rng(4)
+    x = rng.normal(size=(5, 512))
+    y = O.kv_fp8(x, 64)
+    np.testing.assert_array_equal(y[:, 448:], x[:, 448:])
+    c, e = O.fp8_quant(x[:, :448])
+    np.testing.assert_array_equal(y[:, :448], O.fp8_dequant(c, e))
+    np.testing.assert_array_equal(O.kv_fp8(x, 512), x)
