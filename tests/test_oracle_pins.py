@@ -747,6 +747,11 @@ def test_fp8_quant_worked_examples():
         assert e.tolist() == [g["exp_" + blk]]
         assert codes[:len(vals)].tolist() == g["codes_" + blk]
         np.testing.assert_array_equal(O.fp8_dequant(codes, e)[:len(vals)], g["values_" + blk])
+    # a negative value that rounds to zero keeps no sign: -2^-10 is half the
+    # subnormal step below zero (block scale 1, set by a 448 in the block)
+    x = np.zeros(64)
+    x[0], x[1] = 448.0, -2.0 ** -10
+    assert O.fp8_quant(x)[0][1] == 0
 
 
 def test_fp8_grid_round_trip_and_error_bound():
