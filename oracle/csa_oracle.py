@@ -588,10 +588,15 @@ def dense_mqa_backward(q, win_kv, comp, sink, dout, m, n_win, scale, qk_norm=Tru
 # in FP8).  Read as E4M3 (4 exponent bits, bias 7, 3 mantissa bits, largest
 # finite 448, subnormal step 2^-9) with one power-of-two scale per block of
 # 64 values, the smallest 2^e with max |x| <= 448 * 2^e; each x / 2^e rounds
-# to the nearest E4M3 value, ties to the even mantissa.
+# to the nearest E4M3 value, ties to the even mantissa.  The pages leave the
+# scale's range open; it is stored as one byte e + 127, and here e is floored
+# at -117 so that the smallest step of the grid, 2^(e-9), is 2^-126, the
+# smallest normal fp32 number: a block whose largest magnitude is below
+# 448 * 2^-117 is rounded on that fixed grid.
 # ---------------------------------------------------------------------------
 FP8_BLOCK = 64
 FP8_MAX = 448.0
+FP8_E_MIN = -117
 
 
 def fp8_e4m3_values():
@@ -620,6 +625,7 @@ def fp8_quant(x):
     # smallest e with amax <= 448 * 2^e: amax = f * 2^k, 448 = 0.875 * 2^9
     f, k = np.frexp(amax)
     e = np.where(amax > 0, np.where(f <= 0.875, k - 9, k - 8), 0).astype(np.int64)
+    e = np.maximum(e, FP8_E_MIN)
     a = np.abs(xb) / np.ldexp(1.0, e)[..., None]
     grid = fp8_e4m3_values()[:127]                      # finite magnitudes, ascending
     lo = np.clip(np.searchsorted(grid, a, side="right") - 1, 0, 126)

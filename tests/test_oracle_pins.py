@@ -754,6 +754,22 @@ def test_fp8_quant_worked_examples():
     assert O.fp8_quant(x)[0][1] == 0
 
 
+def test_fp8_scale_floor():
+    """The scale exponent stops at -117 (smallest grid step 2^-126, the
+    smallest normal fp32 number).  A block with largest magnitude 2^-110 would
+    take e = -118 (2^-110 = 0.5 * 2^-109); floored, 2^-110 / 2^-117 = 128 =
+    field 14, mantissa 0 (code 112); 3 * 2^-127 / 2^-117 = 1.5 steps of 2^-9,
+    a tie between 1 and 2, even 2 (code 2, value 2^-125); 2^-130 is 1/16 of a
+    step and rounds to 0."""
+    x = np.zeros(64)
+    x[0], x[1], x[2], x[3] = 2.0 ** -110, 3 * 2.0 ** -127, 2.0 ** -130, -(2.0 ** -110)
+    c, e = O.fp8_quant(x)
+    assert e.tolist() == [-117]
+    assert c[:4].tolist() == [112, 2, 0, 128 + 112]
+    np.testing.assert_array_equal(O.fp8_dequant(c, e)[:4],
+                                  [2.0 ** -110, 2.0 ** -125, 0.0, -(2.0 ** -110)])
+
+
 def test_fp8_grid_round_trip_and_error_bound():
     """Grid values times the scale come back exactly; otherwise the error is
     at most half a grid step (2^-4 of the value for normals, 2^-10 of the
