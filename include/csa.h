@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 8
+#define CSA_ABI_VERSION 9
 
 typedef enum csa_status {
   CSA_OK = 0,
@@ -558,6 +558,62 @@ typedef struct {
  * The [n, groups*d_g] intermediate is rounded to bf16 in the workspace. */
 int csa_output_proj(const csa_oproj_desc* desc, const void* o, const void* wo_a, const void* wo_b,
                     void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * FP8 KV rows ([A] "Q, K, V 映射与位置编码注入" and the Compressor: act_quant of
+ * kv[..., :-rd] with block size 64 -- the channels without RoPE in FP8, the
+ * RoPE channels at their precision; [R] section 2.3.4: the KV cache keeps the
+ * RoPE dims in BF16 and the rest in FP8).  A row of c = 512 channels whose
+ * last r (a multiple of 64, r < c) carry RoPE is stored as
+ *   bytes [0, c-r)           E4M3 codes of channels 0 .. c-r-1 (bit 7 sign,
+ *                            bits 6..3 exponent with bias 7, bits 2..0
+ *                            mantissa; exponent 0 holds m * 2^-9),
+ *   bytes [c-r, c+r)         channels c-r .. c-1 as bf16,
+ *   bytes [c+r, c+r+(c-r)/64) one byte e + 127 per 64-channel block: its
+ *                            values are code * 2^e, with e the smallest
+ *                            integer >= -117 such that max |x| <= 448 * 2^e
+ *                            (the floor keeps the grid step 2^(e-9) an fp32
+ *                            normal; the pages leave the range open),
+ * padded with zeros to csa_kv_fp8_row_bytes(c, r) (592 for c = 512, r = 64;
+ * 528 for r = 0).  Codes round x / 2^e to the nearest E4M3 value, ties to
+ * the even mantissa; a value that rounds to zero keeps no sign.  Source
+ * values must be finite and below 2^127 in magnitude (a block scale of 2^120
+ * could otherwise round a value up to 2^128, which fp32 cannot hold).
+ * ---------------------------------------------------------------------- */
+typedef struct csa_kv8_desc {
+  int64_t rows;        /* rows to convert (decode: sequences B)             */
+  int32_t c;           /* row width: 512                                    */
+  int32_t rope_dims;   /* r: channels kept in bf16 (a multiple of 64, < c)   */
+  int32_t dtype;       /* csa_dtype of the source rows                       */
+} csa_kv8_desc;
+
+/* Bytes of one FP8 row (0 for an unsupported c, r). */
+size_t csa_kv_fp8_row_bytes(int c, int rope_dims);
+
+/* csa_kv_fp8_quant -- src [rows, c] (dtype) -> dst [rows, row_bytes]. */
+int csa_kv_fp8_quant(const csa_kv8_desc* desc, const void* src, uint8_t* dst, void* stream);
+
+/* csa_kv_fp8_quant_decode -- the rows a decode step wrote, one per sequence
+ * b < desc->rows, from src [B, n_rows, c] to dst [B, n_rows, row_bytes]:
+ * ring != 0: the window slot pos[b] % n_rows (every step); ring == 0: the
+ * entry pos[b] / m, only when (pos[b] + 1) % m == 0 (the step emitted it) and
+ * pos[b] / m < n_rows.  Sequences with pos < 0 are skipped. */
+int csa_kv_fp8_quant_decode(const csa_kv8_desc* desc, const void* src, int64_t n_rows,
+                            const int64_t* pos, int m, int ring, uint8_t* dst, void* stream);
+
+/* csa_sparse_mqa_decode_fp8 / hca_dense_mqa_decode_fp8 -- the decode
+ * attention calls over FP8 rows: the window ring [B, n_win, row_bytes] and
+ * the entry cache [B, n_entries, row_bytes] in the format above, decoded
+ * exactly to bf16 as they are gathered; q, sink, out, idx, pos and the
+ * workspace as for the bf16 calls (same descriptor, CSA_BF16, c = 512, and
+ * rope_dims equal to the rows' r). */
+int csa_sparse_mqa_decode_fp8(const csa_attn_desc* desc, const void* q, const void* win_ring8,
+                              const void* cache8, const int32_t* idx, const int64_t* pos,
+                              const float* sink, void* out, void* ws, size_t ws_bytes,
+                              void* stream);
+int hca_dense_mqa_decode_fp8(const csa_attn_desc* desc, const void* q, const void* win_ring8,
+                             const void* cache8, const int64_t* pos, const float* sink, void* out,
+                             void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Backward of the core attention ([R] section 4.3: deterministic training;

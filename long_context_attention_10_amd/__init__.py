@@ -35,7 +35,9 @@ EXPORTED = ["csa_compress_prefill", "csa_compress_decode", "csa_state_bytes", "c
             "csa_indexer_fp4_quant_decode_paged", "csa_index_topk_decode_fp4_paged",
             "csa_index_topk_decode_noalloc", "csa_noalloc_scratch_bytes",
             "csa_index_topk_decode_score", "csa_index_topk_decode_select",
-            "csa_sparse_mqa_backward", "hca_dense_mqa_backward"]
+            "csa_sparse_mqa_backward", "hca_dense_mqa_backward", "csa_kv_fp8_row_bytes",
+            "csa_kv_fp8_quant", "csa_kv_fp8_quant_decode", "csa_sparse_mqa_decode_fp8",
+            "hca_dense_mqa_decode_fp8"]
 
 
 class CompressDesc(ctypes.Structure):
@@ -56,6 +58,11 @@ class IndexDesc(ctypes.Structure):
 
 class Fp4Desc(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_int64), ("width", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class Kv8Desc(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("c", ctypes.c_int32), ("rope_dims", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
 
 
 class QueryDesc(ctypes.Structure):
@@ -130,11 +137,18 @@ def load(path: str = LIB_PATH):
     lib.csa_sparse_mqa_backward.argtypes = [P] * 12 + [S, P]
     lib.hca_dense_mqa_backward.argtypes = [P] * 11 + [S, P]
     lib.csa_index_topk_decode_select.argtypes = [P] * 7 + [S, P]
+    lib.csa_kv_fp8_row_bytes.restype = S
+    lib.csa_kv_fp8_row_bytes.argtypes = [I, I]
+    lib.csa_kv_fp8_quant.argtypes = [P] * 4
+    lib.csa_kv_fp8_quant_decode.argtypes = [P, P, ctypes.c_int64, P, I, I, P, P]
+    lib.csa_sparse_mqa_decode_fp8.argtypes = [P] * 9 + [S, P]
+    lib.hca_dense_mqa_decode_fp8.argtypes = [P] * 8 + [S, P]
     lib.csa_noalloc_scratch_bytes.restype = S
     lib.csa_noalloc_scratch_bytes.argtypes = []
     for f in EXPORTED:
         if f not in ("csa_abi_version", "csa_status_string", "csa_workspace_bytes",
-                     "csa_workspace_zero_bytes", "csa_state_bytes", "csa_noalloc_scratch_bytes"):
+                     "csa_workspace_zero_bytes", "csa_state_bytes", "csa_noalloc_scratch_bytes",
+                     "csa_kv_fp8_row_bytes"):
             getattr(lib, f).restype = I
     _lib = lib
     return lib
@@ -655,6 +669,98 @@ def hca_dense_mqa_decode(q, win_ring, comp_cache, pos, sink, m, scale=None, qk_n
     st = lib.hca_dense_mqa_decode(ctypes.byref(desc), _ptr(q), _ptr(win_ring), _ptr(comp_cache),
                                   _ptr(pos), _ptr(sink), _ptr(out), _ptr(ws), wsb, _stream(q.device))
     _check(st, "hca_dense_mqa_decode")
+    return out
+
+
+# ------------------------------------------------------------ FP8 KV rows
+def kv_fp8_row_bytes(c, rope_dims):
+    """Bytes of one FP8 KV row of c channels whose last rope_dims stay bf16."""
+    n = load().csa_kv_fp8_row_bytes(c, rope_dims)
+    if n == 0:
+        raise CsaError(f"no FP8 row format for c={c}, rope_dims={rope_dims}")
+    return n
+
+
+def csa_kv_fp8_quant(rows, rope_dims, out=None):
+    """rows [..., c] (bf16 or fp32) -> their FP8 rows, uint8 [..., row_bytes]."""
+    lib = load()
+    c = rows.shape[-1]
+    rb = kv_fp8_row_bytes(c, rope_dims)
+    shape = tuple(rows.shape[:-1]) + (rb,)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.uint8, device=rows.device)
+    _expect(out, shape, torch.uint8, "out")
+    desc = Kv8Desc(rows.numel() // c if c else 0, c, rope_dims, _dt(rows))
+    _check(lib.csa_kv_fp8_quant(ctypes.byref(desc), _ptr(rows), _ptr(out), _stream(rows.device)),
+           "csa_kv_fp8_quant")
+    return out
+
+
+def csa_kv_fp8_quant_decode(src, pos, dst, rope_dims, m=1, ring=False):
+    """The rows one decode step wrote into src [B, n_rows, c] (a window ring
+    when `ring`, else an entry cache of ratio m), converted in place into
+    their FP8 copy dst [B, n_rows, row_bytes]."""
+    lib = load()
+    B, n_rows, c = src.shape
+    rb = kv_fp8_row_bytes(c, rope_dims)
+    _expect(dst, (B, n_rows, rb), torch.uint8, "dst")
+    _expect(pos, (B,), torch.int64, "pos")
+    desc = Kv8Desc(B, c, rope_dims, _dt(src))
+    _check(lib.csa_kv_fp8_quant_decode(ctypes.byref(desc), _ptr(src), n_rows, _ptr(pos), m,
+                                       1 if ring else 0, _ptr(dst), _stream(src.device)),
+           "csa_kv_fp8_quant_decode")
+    return dst
+
+
+def _fp8_rows(t, B, rb, name):
+    if t.dtype != torch.uint8 or t.dim() != 3 or t.shape[0] != B or t.shape[2] != rb:
+        raise CsaError(f"{name}: expected uint8 [{B}, n, {rb}], got {t.dtype} {tuple(t.shape)}")
+
+
+def csa_sparse_mqa_decode_fp8(q, win_ring8, cache8, idx, pos, sink, rope_dims, scale=None,
+                              qk_norm=True, eps=1e-6, rope_theta=10000.0, out=None):
+    """csa_sparse_mqa_decode over FP8 rows: win_ring8 [B, n_win, row_bytes],
+    cache8 [B, n_entries, row_bytes] (uint8, csa_kv_fp8_quant's format)."""
+    lib = load()
+    B, nh, c = q.shape
+    rb = kv_fp8_row_bytes(c, rope_dims)
+    _fp8_rows(win_ring8, B, rb, "win_ring8")
+    _fp8_rows(cache8, B, rb, "cache8")
+    k = idx.shape[1]
+    _expect(idx, (B, k), torch.int32, "idx")
+    _expect(pos, (B,), torch.int64, "pos")
+    desc = attn_desc(batch=B, nh=nh, c=c, k=k, n_win=win_ring8.shape[1], dtype=_dt(q),
+                     scale=scale, qk_norm=qk_norm, eps=eps, rope_dims=rope_dims,
+                     rope_theta=rope_theta, n_entries=cache8.shape[1])
+    if out is None:
+        out = torch.empty_like(q)
+    ws, wsb = workspace(workspace_bytes("sparse_mqa_decode", desc), q.device, "attn_dec_s")
+    st = lib.csa_sparse_mqa_decode_fp8(ctypes.byref(desc), _ptr(q), _ptr(win_ring8), _ptr(cache8),
+                                       _ptr(idx), _ptr(pos), _ptr(sink), _ptr(out), _ptr(ws), wsb,
+                                       _stream(q.device))
+    _check(st, "csa_sparse_mqa_decode_fp8")
+    return out
+
+
+def hca_dense_mqa_decode_fp8(q, win_ring8, cache8, pos, sink, m, rope_dims, scale=None,
+                             qk_norm=True, eps=1e-6, rope_theta=10000.0, out=None):
+    """hca_dense_mqa_decode over FP8 rows (formats as csa_sparse_mqa_decode_fp8)."""
+    lib = load()
+    B, nh, c = q.shape
+    rb = kv_fp8_row_bytes(c, rope_dims)
+    _fp8_rows(win_ring8, B, rb, "win_ring8")
+    _fp8_rows(cache8, B, rb, "cache8")
+    _expect(pos, (B,), torch.int64, "pos")
+    desc = attn_desc(batch=B, nh=nh, c=c, m=m, n_win=win_ring8.shape[1], dtype=_dt(q),
+                     scale=scale, qk_norm=qk_norm, eps=eps, rope_dims=rope_dims,
+                     rope_theta=rope_theta, n_entries=cache8.shape[1])
+    if out is None:
+        out = torch.empty_like(q)
+    ws, wsb = workspace(workspace_bytes("dense_mqa_decode", desc), q.device, "attn_dec_d")
+    st = lib.hca_dense_mqa_decode_fp8(ctypes.byref(desc), _ptr(q), _ptr(win_ring8), _ptr(cache8),
+                                      _ptr(pos), _ptr(sink), _ptr(out), _ptr(ws), wsb,
+                                      _stream(q.device))
+    _check(st, "hca_dense_mqa_decode_fp8")
     return out
 
 

@@ -13,7 +13,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libcsa.so")
 SOURCES = ["capi.hip", "compress.hip", "index_topk.hip", "attention.hip", "attention_bf16.hip",
-           "layer.hip", "noalloc.hip", "backward.hip"]
+           "layer.hip", "noalloc.hip", "backward.hip", "kvfp8.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

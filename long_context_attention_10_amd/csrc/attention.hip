@@ -492,7 +492,7 @@ static hipError_t dispatch_decode(const csa_attn_desc& d, const void* q, const v
 hipError_t launch_mqa_decode(const csa_attn_desc& d, int mode, const void* q, const void* ring,
                              const void* cache, const int32_t* idx, const int64_t* pos,
                              const float* sink, void* out, void* ws, hipStream_t st,
-                             EntryMap em) {
+                             EntryMap em, bool kv8) {
   if (d.batch == 0) return hipSuccess;
   if (d.dtype == CSA_BF16) {
     const int S_ = decode_nsplit(d, mode);
@@ -500,8 +500,9 @@ hipError_t launch_mqa_decode(const csa_attn_desc& d, int mode, const void* q, co
     float* ws_o = (float*)ws;
     float2* ws_ml = (float2*)((uint8_t*)ws + ((rows * d.c * 4 + 255) & ~(size_t)255));
     return launch_mqa_decode_bf16(d, mode, q, ring, cache, idx, pos, sink, out, ws_o, ws_ml, S_,
-                                  st, em);
+                                  st, em, kv8);
   }
+  if (kv8) return hipErrorInvalidValue;
   if (d.dtype == CSA_BF16)
     return mode == ATTN_SPARSE
                ? dispatch_decode<BF16, MODE_DECODE_SPARSE>(d, q, ring, cache, idx, pos, sink, out, ws, mode, st)

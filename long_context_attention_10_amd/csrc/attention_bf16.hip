@@ -501,7 +501,10 @@ hipError_t launch_mqa_prefill_bf16(const csa_attn_desc& d, int mode, const void*
 // ---------------------------------------------------------------------------
 constexpr int kDecSplitMax = 256;  // candidates per chunk, at most
 
-template <int C, bool SPARSE, bool PAGED>
+// KV8: the ring and the cache hold FP8 rows (kv8_row_bytes(C, r) bytes each,
+// C = 512): wave w's 8 rows of a tile are loaded into registers while the
+// previous tile is computed, then decoded to bf16 into the same LDS layout.
+template <int C, bool SPARSE, bool PAGED, bool KV8>
 __global__ __launch_bounds__(256, 2) void mqa_decode_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ ring,
     const uint16_t* __restrict__ cache, const int32_t* __restrict__ idx,
@@ -566,7 +569,67 @@ __global__ __launch_bounds__(256, 2) void mqa_decode_bf16_kernel(
                          return cache + (PAGED ? srow[j - nwin - s0] : b * n_entries + e) * C;
                        });
   };
-  const bool early0 = cbeg + kT <= nwin;  // tile 0 is window rows only
+  // ---- FP8 rows: register-staged gather (C = 512, one row per LDS burst)
+  static_assert(!KV8 || C == 512, "FP8 rows are 512 channels wide");
+  const int RB8 = kv8_row_bytes(C, r);
+  const int nf8 = C - r;
+  const uint8_t* ring8 = (const uint8_t*)ring;
+  const uint8_t* cache8 = (const uint8_t*)cache;
+  uint4 st8[kT / 4];  // this lane's raw part of each of the wave's rows:
+                      // 8 codes and the block's scale byte, or 8 bf16 channels
+  auto row8_of = [&](int64_t j, bool& ok) -> const uint8_t* {
+    ok = false;
+    if (j >= cend) return ring8;
+    if (j < nwin) {
+      int slot = w0 + (int)j;
+      if (slot >= n_win) slot -= n_win;
+      ok = true;
+      return ring8 + (b * (int64_t)n_win + slot) * RB8;
+    }
+    const int64_t e = SPARSE ? (int64_t)sidx[j - nwin - s0] : j - nwin;
+    if (e < 0 || e >= n_entries) return ring8;
+    ok = true;
+    return cache8 + (PAGED ? srow[j - nwin - s0] : b * n_entries + e) * RB8;
+  };
+  auto load8 = [&](int ti, int buf) {  // wave w: rows w, w + 4, ..., w + 28
+    const uint8_t* rp = ring8;
+    if (lane < kT / 4) {
+      const int row = wave + 4 * lane;
+      bool ok;
+      rp = row8_of(cbeg + (int64_t)ti * kT + row, ok);
+      valid[buf][row] = ok;
+    }
+    const uint32_t lo_a = (uint32_t)(size_t)rp, hi_a = (uint32_t)((size_t)rp >> 32);
+#pragma unroll
+    for (int u = 0; u < kT / 4; ++u) {
+      // readlane returns int: take both halves as uint32 so that the low
+      // half is not sign-extended into the high one
+      const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane(lo_a, u);
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane(hi_a, u);
+      const uint8_t* g = (const uint8_t*)(size_t)(((uint64_t)hi << 32) | lo);
+      if (8 * lane < nf8) {
+        const uint2 cw = *(const uint2*)(g + 8 * lane);
+        st8[u] = make_uint4(cw.x, cw.y, g[nf8 + 2 * r + lane / 8], 0u);
+      } else {
+        st8[u] = *(const uint4*)(g + nf8 + 16 * (lane - nf8 / 8));
+      }
+    }
+  };
+  auto store8 = [&](int buf) {  // decode to bf16 into the tile's LDS rows
+#pragma unroll
+    for (int u = 0; u < kT / 4; ++u) {
+      uint4 o = st8[u];
+      if (8 * lane < nf8) {
+        float v[8];
+        e4m3x4_to_f32(st8[u].x, (int)st8[u].z - 127, v);
+        e4m3x4_to_f32(st8[u].y, (int)st8[u].z - 127, v + 4);
+        o = f32_to_chunk<BF16>(v);
+      }
+      *(uint4*)(smem + buf * G::TILE + (wave + 4 * u) * G::BURST + 16 * lane) = o;
+    }
+  };
+
+  const bool early0 = !KV8 && cbeg + kT <= nwin;  // tile 0 is window rows only
   if (early0) issue_tile(0, 0);
   // entry slot j (index slot j of idx, or entry j) of this chunk -> pool row
   auto stage_row = [&](int64_t j, int64_t e) {
@@ -595,7 +658,12 @@ __global__ __launch_bounds__(256, 2) void mqa_decode_bf16_kernel(
     rope_tab[p] = make_float2(cs, sn);
   }
   __syncthreads();
-  if (!early0) issue_tile(0, 0);
+  if constexpr (KV8) {
+    load8(0, 0);
+    store8(0);
+  } else if (!early0) {
+    issue_tile(0, 0);
+  }
 
   bf16x8_t qf[NKG];
   q_prologue<C>(qraw, qf, rope_tab, qk_norm, eps, r, lg);
@@ -615,10 +683,18 @@ __global__ __launch_bounds__(256, 2) void mqa_decode_bf16_kernel(
   __syncthreads();
   for (int ti = 0; ti < ntiles; ++ti) {
     const int buf = ti & 1;
-    if (ti + 1 < ntiles) issue_tile(ti + 1, buf ^ 1);
+    if constexpr (KV8) {
+      if (ti + 1 < ntiles) load8(ti + 1, buf ^ 1);
+    } else {
+      if (ti + 1 < ntiles) issue_tile(ti + 1, buf ^ 1);
+    }
     mqa_tile<C>(smem + buf * G::TILE, valid[buf], qf, o, run_m, run_l, scale * LOG2E, koff0,
                 koff1, troff0, troff1, lg);
-    wait_vmem();
+    if constexpr (KV8) {
+      if (ti + 1 < ntiles) store8(buf ^ 1);
+    } else {
+      wait_vmem();
+    }
     __syncthreads();
   }
   // partial O^T: block cb, element i = O[head][cb*16 + 4*lg + i]
@@ -760,27 +836,31 @@ int mqa_decode_bf16_split(int mode) { return mode == ATTN_SPARSE ? 128 : 256; }
 hipError_t launch_mqa_decode_bf16(const csa_attn_desc& d, int mode, const void* q,
                                   const void* ring, const void* cache, const int32_t* idx,
                                   const int64_t* pos, const float* sink, void* out, float* ws_o,
-                                  float2* ws_ml, int nsplit, hipStream_t st, EntryMap em) {
+                                  float2* ws_ml, int nsplit, hipStream_t st, EntryMap em,
+                                  bool kv8) {
   const int spl = mqa_decode_bf16_split(mode);
   if (spl > kDecSplitMax) return hipErrorInvalidValue;  // the LDS row table's size
+  if (kv8 && d.c != 512) return hipErrorInvalidValue;
   const dim3 grid((unsigned)nsplit, (unsigned)d.batch);
   const bool wide = nsplit > 8;  // more chunks than one wave's loads in flight
   const dim3 cgrid((unsigned)d.batch, (unsigned)(wide ? d.n_heads : (d.n_heads + 3) / 4));
-#define CSA_DEC_K(CC, SP, PG)                                                                  \
-  mqa_decode_bf16_kernel<CC, SP, PG><<<grid, 256, 0, st>>>(                                    \
+#define CSA_DEC_K(CC, SP, PG, K8)                                                              \
+  mqa_decode_bf16_kernel<CC, SP, PG, K8><<<grid, 256, 0, st>>>(                                \
       (const uint16_t*)q, (const uint16_t*)ring, (const uint16_t*)cache, idx, sink, d.n_heads,   \
       d.k, d.m, d.n_win, d.scale, d.qk_norm, d.eps, d.rope_dims, d.rope_theta, d.n_entries, pos, \
       ws_o, ws_ml, nsplit, spl, em);
-#define CSA_DEC(CC)                                                                            \
+#define CSA_DEC_MODES(CC, K8)                                                                  \
+  if (mode == ATTN_SPARSE && em.table)                                                        \
+    CSA_DEC_K(CC, true, true, K8)                                                             \
+  else if (mode == ATTN_SPARSE)                                                               \
+    CSA_DEC_K(CC, true, false, K8)                                                            \
+  else if (em.table)                                                                          \
+    CSA_DEC_K(CC, false, true, K8)                                                            \
+  else                                                                                        \
+    CSA_DEC_K(CC, false, false, K8)
+#define CSA_DEC(CC, ...)                                                                       \
   if (d.c == CC) {                                                                            \
-    if (mode == ATTN_SPARSE && em.table)                                                      \
-      CSA_DEC_K(CC, true, true)                                                               \
-    else if (mode == ATTN_SPARSE)                                                             \
-      CSA_DEC_K(CC, true, false)                                                              \
-    else if (em.table)                                                                        \
-      CSA_DEC_K(CC, false, true)                                                              \
-    else                                                                                      \
-      CSA_DEC_K(CC, false, false)                                                             \
+    __VA_ARGS__                                                                               \
     hipError_t e = hipGetLastError();                                                         \
     if (e != hipSuccess) return e;                                                            \
     if (wide)                                                                                 \
@@ -793,8 +873,11 @@ hipError_t launch_mqa_decode_bf16(const csa_attn_desc& d, int mode, const void* 
           d.k, d.m, d.n_win, d.n_entries, d.rope_dims, d.rope_theta);                          \
     return hipGetLastError();                                                                 \
   }
-  CSA_DEC(128) CSA_DEC(256) CSA_DEC(512)
+  CSA_DEC(128, CSA_DEC_MODES(128, false))
+  CSA_DEC(256, CSA_DEC_MODES(256, false))
+  CSA_DEC(512, if (kv8) { CSA_DEC_MODES(512, true) } else { CSA_DEC_MODES(512, false) })
 #undef CSA_DEC
+#undef CSA_DEC_MODES
 #undef CSA_DEC_K
   return hipErrorInvalidValue;
 }

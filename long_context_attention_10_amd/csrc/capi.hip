@@ -548,6 +548,63 @@ int csa_sparse_mqa_prefill(const csa_attn_desc* d, const void* q, const void* wi
                                        (hipStream_t)stream));
 }
 
+static bool kv8_shape_ok(int c, int r) { return c == 512 && r >= 0 && r < c && r % 64 == 0; }
+
+static int mqa_decode_fp8(const csa_attn_desc* d, int mode, const void* q, const void* ring8,
+                          const void* cache8, const int32_t* idx, const int64_t* pos,
+                          const float* sink, void* out, void* ws, size_t ws_bytes,
+                          void* stream) {
+  const bool sparse = mode == ATTN_SPARSE;
+  int s = check_attn(d, true, sparse);
+  if (s) return s;
+  if (d->dtype != CSA_BF16 || !kv8_shape_ok(d->c, d->rope_dims)) return CSA_ERR_UNSUPPORTED;
+  if (!q || !ring8 || !cache8 || (sparse && !idx) || !pos || !sink || !out)
+    return CSA_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < mqa_decode_ws_bytes(*d, mode)) return CSA_ERR_WORKSPACE;
+  return hip_status(launch_mqa_decode(*d, mode, q, ring8, cache8, sparse ? idx : nullptr, pos,
+                                      sink, out, ws, (hipStream_t)stream, EntryMap(), true));
+}
+
+size_t csa_kv_fp8_row_bytes(int c, int rope_dims) {
+  return kv8_shape_ok(c, rope_dims) ? (size_t)kv8_row_bytes(c, rope_dims) : 0;
+}
+
+int csa_kv_fp8_quant(const csa_kv8_desc* d, const void* src, uint8_t* dst, void* stream) {
+  if (!d) return CSA_ERR_INVALID_ARG;
+  if (!dtype_ok(d->dtype) || !kv8_shape_ok(d->c, d->rope_dims)) return CSA_ERR_UNSUPPORTED;
+  if (d->rows < 0) return CSA_ERR_INVALID_ARG;
+  if (d->rows == 0) return CSA_OK;
+  if (!src || !dst) return CSA_ERR_INVALID_ARG;
+  return hip_status(launch_kv_fp8_quant(d->dtype, src, d->rows, d->rope_dims, dst, nullptr, 0,
+                                        1, 0, (hipStream_t)stream));
+}
+
+int csa_kv_fp8_quant_decode(const csa_kv8_desc* d, const void* src, int64_t n_rows,
+                            const int64_t* pos, int m, int ring, uint8_t* dst, void* stream) {
+  if (!d) return CSA_ERR_INVALID_ARG;
+  if (!dtype_ok(d->dtype) || !kv8_shape_ok(d->c, d->rope_dims)) return CSA_ERR_UNSUPPORTED;
+  if (d->rows < 0 || n_rows <= 0 || (!ring && m <= 0)) return CSA_ERR_INVALID_ARG;
+  if (d->rows == 0) return CSA_OK;
+  if (!src || !pos || !dst) return CSA_ERR_INVALID_ARG;
+  return hip_status(launch_kv_fp8_quant(d->dtype, src, d->rows, d->rope_dims, dst, pos, n_rows,
+                                        ring ? 1 : m, ring ? 1 : 0, (hipStream_t)stream));
+}
+
+int csa_sparse_mqa_decode_fp8(const csa_attn_desc* d, const void* q, const void* win_ring8,
+                              const void* cache8, const int32_t* idx, const int64_t* pos,
+                              const float* sink, void* out, void* ws, size_t ws_bytes,
+                              void* stream) {
+  return mqa_decode_fp8(d, ATTN_SPARSE, q, win_ring8, cache8, idx, pos, sink, out, ws, ws_bytes,
+                        stream);
+}
+
+int hca_dense_mqa_decode_fp8(const csa_attn_desc* d, const void* q, const void* win_ring8,
+                             const void* cache8, const int64_t* pos, const float* sink, void* out,
+                             void* ws, size_t ws_bytes, void* stream) {
+  return mqa_decode_fp8(d, ATTN_DENSE, q, win_ring8, cache8, nullptr, pos, sink, out, ws,
+                        ws_bytes, stream);
+}
+
 static int mqa_backward(const csa_attn_desc* d, int mode, const void* q, const void* win_kv,
                         const void* comp, const int32_t* idx, const float* sink,
                         const void* dout, void* dq, void* dwin, void* dcomp, float* dsink,

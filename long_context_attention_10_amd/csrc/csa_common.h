@@ -167,6 +167,31 @@ struct EntryMap {
   }
 };
 
+// ---------------------------------------------------------------- FP8 KV rows
+// A KV row of width c with r RoPE channels stored in FP8 ([A] act_quant of the
+// channels without RoPE, block 64; [R] 2.3.4): the c - r E4M3 codes, then the
+// r RoPE channels as bf16, then one scale byte e + 127 per 64-code block
+// (scale 2^e), padded to a multiple of 16 bytes.
+__host__ __device__ constexpr inline int kv8_row_bytes(int c, int r) {
+  return ((c - r) + 2 * r + (c - r) / 64 + 15) & ~15;
+}
+
+// Four E4M3 codes (bytes of `w`, lowest first) times 2^e as fp32 values.
+// E4M3: sign bit 7, exponent field bits 6..3 (bias 7), mantissa bits 2..0;
+// field 0 holds the subnormals m * 2^-9.  Every value is exact in fp32 (and in
+// bf16: at most 4 significant bits).
+CSA_DEV void e4m3x4_to_f32(uint32_t w, int e, float* v) {
+  const float sub = __uint_as_float((uint32_t)(e - 9 + 127) << 23);  // 2^(e-9)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t c = (w >> (8 * i)) & 0xffu;
+    const uint32_t ef = (c >> 3) & 15u, m = c & 7u;
+    const float a = ef ? __uint_as_float(((ef + (uint32_t)(e - 7 + 127)) << 23) | (m << 20))
+                       : (float)m * sub;
+    v[i] = (c & 0x80u) ? -a : a;
+  }
+}
+
 // Order-preserving map fp32 -> uint32 (larger float -> larger key).
 CSA_DEV uint32_t float_key(float f) {
   uint32_t u = __float_as_uint(f);

@@ -133,11 +133,19 @@ hipError_t launch_mqa_decode_bf16(const csa_attn_desc& d, int mode, const void* 
                                   const void* ring, const void* cache, const int32_t* idx,
                                   const int64_t* pos, const float* sink, void* out, float* ws_o,
                                   float2* ws_ml, int nsplit, hipStream_t st,
-                                  EntryMap em = EntryMap());
+                                  EntryMap em = EntryMap(), bool kv8 = false);
+// kv8: ring and cache hold FP8 rows (kv8_row_bytes; bf16 queries and output)
 hipError_t launch_mqa_decode(const csa_attn_desc& d, int mode, const void* q, const void* ring,
                              const void* cache, const int32_t* idx, const int64_t* pos,
                              const float* sink, void* out, void* ws, hipStream_t st,
-                             EntryMap em = EntryMap());
+                             EntryMap em = EntryMap(), bool kv8 = false);
+// FP8 KV rows (kvfp8.hip): rows of width 512 with r RoPE channels.  pos ==
+// nullptr: rows 0..rows-1; else one row per sequence b < rows: ring != 0 the
+// window slot b * n + pos % n, ring == 0 the entry pos / m of sequence b
+// (through em) when (pos + 1) % m == 0.
+hipError_t launch_kv_fp8_quant(int dtype, const void* src, int64_t rows, int r, uint8_t* dst,
+                               const int64_t* pos, int64_t n, int m, int ring, hipStream_t st,
+                               EntryMap em = EntryMap());
 
 // Deterministic fp32 attention backward (backward.hip).
 bool mqa_backward_supported(const csa_attn_desc& d);

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.csa_abi_version() == 8
+    assert lib.csa_abi_version() == 9
     for code in (0, -1, -2, -3, -4):
         assert len(lib.csa_status_string(code)) > 0
     assert lib.csa_status_string(-99) == b"unknown status"
@@ -61,7 +61,8 @@ def test_struct_sizes_match_c_layout(tmp_path):
         pytest.skip("no C compiler")
     pairs = [("csa_compress_desc", L.CompressDesc), ("csa_index_desc", L.IndexDesc),
              ("csa_attn_desc", L.AttnDesc), ("csa_query_desc", L.QueryDesc),
-             ("csa_oproj_desc", L.OprojDesc), ("csa_fp4_desc", L.Fp4Desc)]
+             ("csa_oproj_desc", L.OprojDesc), ("csa_fp4_desc", L.Fp4Desc),
+             ("csa_kv8_desc", L.Kv8Desc)]
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "csa.h"', "int main(void) {"]
     for cname, py in pairs:
         lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
@@ -381,3 +382,37 @@ def test_backward_calls_reject(lib):
     assert sb(ctypes.byref(wide), *([_p()] * 11), 1 << 40, None) == -2
     chunk = L.attn_desc(n=64, nh=8, c=128, k=16, n_entries=16, dtype=L.CSA_F32, t0=128)
     assert sb(ctypes.byref(chunk), *([_p()] * 11), 1 << 40, None) == -2
+
+
+def test_fp8_calls_reject(lib):
+    """FP8 rows: the row size, and the quantiser and decode attention calls
+    reject unsupported shapes, a fp32 query and missing pointers."""
+    assert lib.csa_kv_fp8_row_bytes(512, 64) == 592
+    assert lib.csa_kv_fp8_row_bytes(512, 0) == 528
+    assert lib.csa_kv_fp8_row_bytes(512, 448) == 976  # 64 codes, 448 bf16, 1 scale byte
+    for c, r in ((512, 32), (512, 512), (256, 64), (512, -64)):
+        assert lib.csa_kv_fp8_row_bytes(c, r) == 0
+    d = L.Kv8Desc(4, 512, 64, L.CSA_BF16)
+    assert lib.csa_kv_fp8_quant(ctypes.byref(d), None, _p(), None) == -1
+    assert lib.csa_kv_fp8_quant(None, _p(), _p(), None) == -1
+    assert lib.csa_kv_fp8_quant(ctypes.byref(L.Kv8Desc(4, 256, 64, L.CSA_BF16)), _p(), _p(),
+                                None) == -2
+    assert lib.csa_kv_fp8_quant(ctypes.byref(L.Kv8Desc(0, 512, 64, L.CSA_BF16)), None, None,
+                                None) == 0  # nothing to do
+    qd = lib.csa_kv_fp8_quant_decode
+    assert qd(ctypes.byref(d), _p(), 8, _p(), 0, 0, _p(), None) == -1  # entries need m > 0
+    assert qd(ctypes.byref(d), _p(), 0, _p(), 4, 0, _p(), None) == -1  # no rows
+    assert qd(ctypes.byref(d), _p(), 8, None, 4, 0, _p(), None) == -1
+    a = L.attn_desc(batch=2, nh=64, c=512, k=64, n_win=128, n_entries=256, dtype=L.CSA_BF16,
+                    rope_dims=64)
+    need = L.workspace_bytes("sparse_mqa_decode", a)
+    sd, dd = lib.csa_sparse_mqa_decode_fp8, lib.hca_dense_mqa_decode_fp8
+    assert sd(ctypes.byref(a), *([_p()] * 8), need - 1, None) == -3
+    assert sd(ctypes.byref(a), _p(), _p(), _p(), None, *([_p()] * 4), need, None) == -1
+    assert dd(ctypes.byref(a), _p(), _p(), None, *([_p()] * 4), 1 << 40, None) == -1
+    for bad in (dict(dtype=L.CSA_F32), dict(c=256), dict(rope_dims=32)):
+        kw = dict(batch=2, nh=64, c=512, k=64, n_win=128, n_entries=256, dtype=L.CSA_BF16,
+                  rope_dims=64)
+        kw.update(bad)
+        b = L.attn_desc(**kw)
+        assert sd(ctypes.byref(b), *([_p()] * 8), 1 << 40, None) == -2, bad
