@@ -473,7 +473,15 @@ class HybridDecode:
             L._WS.pop(key)
         torch.cuda.empty_cache()
 
-    def step(self, streams=True):
+    def make_kv8(self):
+        """FP8 copies of the two window rings and entry caches (the format of
+        csa_kv_fp8_quant), for step(kv8=True)."""
+        r = self.cfg["rope_dims"]
+        self.kv8 = {n: L.csa_kv_fp8_quant(getattr(self, n), r)
+                    for n in ("ring", "cache", "hring", "hcache")}
+        torch.cuda.synchronize()
+
+    def step(self, streams=True, kv8=False):
         """One decode step.  Its chains are independent until the sparse
         attention: (indexer compressor -> selection), (scoring of the cached
         indexer keys -> selection), (CSA compressor) and (HCA compressor ->
@@ -484,7 +492,10 @@ class HybridDecode:
         compressor's, selects, waits for the CSA compressor's and runs the
         sparse attention; the current stream joins the others at the end.
         The compressors are enqueued first, so that their projections start
-        with the step.  Each chain has its own workspaces."""
+        with the step.  Each chain has its own workspaces.  With `kv8` the
+        attention reads FP8 rings and caches (make_kv8): each compressor's new
+        bf16 row (window slot, and the entry when one is emitted) is converted
+        into them by csa_kv_fp8_quant_decode on the compressor's stream."""
         c, g = self.cfg, self.g
         m, ov, r = c["m"], c["overlap"], c["rope_dims"]
         main = torch.cuda.current_stream()
@@ -504,9 +515,15 @@ class HybridDecode:
             L.csa_compress_decode(self.h, self.pos, g["csa_Wkv"], g["csa_Wz"], g["csa_ape"], m, ov,
                                   self.st, self.cache, W_win=g["csa_Wwin"], win_ring=self.ring,
                                   rope_dims=r, ws_slot="decode_proj_csa")
+            if kv8:
+                L.csa_kv_fp8_quant_decode(self.cache, self.pos, self.kv8["cache"], r, m=m)
+                L.csa_kv_fp8_quant_decode(self.ring, self.pos, self.kv8["ring"], r, ring=True)
         L.csa_compress_decode(self.h, self.pos, g["hca_Wkv"], g["hca_Wz"], g["hca_ape"],
                               c["m_hca"], 0, self.sth, self.hcache, W_win=g["hca_Wwin"],
                               win_ring=self.hring, rope_dims=r, ws_slot="decode_proj_hca")
+        if kv8:
+            L.csa_kv_fp8_quant_decode(self.hcache, self.pos, self.kv8["hcache"], r, m=c["m_hca"])
+            L.csa_kv_fp8_quant_decode(self.hring, self.pos, self.kv8["hring"], r, ring=True)
         with torch.cuda.stream(sd):
             L.csa_index_topk_decode_score(g["qI"], g["wI"], self.kcache, self.pos, m, c["k"])
             if streams:
@@ -515,10 +532,18 @@ class HybridDecode:
                                            out=self.idx)
             if streams:
                 sd.wait_stream(sc)
-            L.csa_sparse_mqa_decode(g["csa_q"], self.ring, self.cache, self.idx, self.pos,
-                                    g["csa_sink"], rope_dims=r, out=self.out_c)
-        L.hca_dense_mqa_decode(g["hca_q"], self.hring, self.hcache, self.pos, g["hca_sink"],
-                               c["m_hca"], rope_dims=r, out=self.out_h)
+            if kv8:
+                L.csa_sparse_mqa_decode_fp8(g["csa_q"], self.kv8["ring"], self.kv8["cache"],
+                                            self.idx, self.pos, g["csa_sink"], r, out=self.out_c)
+            else:
+                L.csa_sparse_mqa_decode(g["csa_q"], self.ring, self.cache, self.idx, self.pos,
+                                        g["csa_sink"], rope_dims=r, out=self.out_c)
+        if kv8:
+            L.hca_dense_mqa_decode_fp8(g["hca_q"], self.kv8["hring"], self.kv8["hcache"], self.pos,
+                                       g["hca_sink"], c["m_hca"], r, out=self.out_h)
+        else:
+            L.hca_dense_mqa_decode(g["hca_q"], self.hring, self.hcache, self.pos, g["hca_sink"],
+                                   c["m_hca"], rope_dims=r, out=self.out_h)
         if streams:
             main.wait_stream(sb)
             main.wait_stream(sc)
@@ -627,8 +652,9 @@ class HybridDecode:
                                       g["csa_sink"], n_entries=self.cache.shape[1], rope_dims=r,
                                       out=self.out_c)
 
-    def algorithmic_bytes(self):
-        """Bytes a decode step must move at least once (bf16 = 2 B)."""
+    def algorithmic_bytes(self, kv8=False):
+        """Bytes a decode step must move at least once (bf16 = 2 B; with
+        `kv8` the attention's window rows and entries are FP8 rows)."""
         c = self.cfg
         B, ctx, d, cc, m, ov = c["batch"], c["ctx"], c["d"], c["c"], c["m"], c["overlap"]
         t = ctx - 1
@@ -638,8 +664,9 @@ class HybridDecode:
         w, wI = (1 + ov) * cc, (1 + ov) * c["cI"]
         weights = d * (2 * w + cc + 2 * wI + 2 * cc + cc) * e
         keys = B * vis * c["cI"] * e
-        csa = B * (nw + min(c["k"], vis)) * cc * e
-        hca = B * (nw + vis_h) * cc * e
+        row = L.kv_fp8_row_bytes(cc, c["rope_dims"]) if kv8 else cc * e
+        csa = B * (nw + min(c["k"], vis)) * row
+        hca = B * (nw + vis_h) * row
         qo = 4 * B * c["nh"] * cc * e + B * (c["hI"] * c["cI"] + c["hI"]) * e + B * d * e
         return weights + keys + csa + hca + qo
 
@@ -913,6 +940,44 @@ def main():
                 "key_bytes_per_entry": [kc.shape[-1] + ke.shape[-1], 2 * hd.kcache.shape[-1]],
                 "recall_of_bf16_selection": float(hit.sum().item()) / float((hd.idx >= 0).sum().item())}
             del kc, ke, qc, qe, idx4, pos_, hit
+            # FP8 KV rows (E4M3 codes with block-64 scales, RoPE channels in
+            # bf16): the same step with the attention reading FP8 rings and
+            # caches, and each attention call alone beside its bf16 twin
+            hd.make_kv8()
+            k8 = hd.kv8
+
+            def att(fp8, sparse):
+                if sparse and fp8:
+                    return lambda: L.csa_sparse_mqa_decode_fp8(
+                        g_["csa_q"], k8["ring"], k8["cache"], hd.idx, hd.pos, g_["csa_sink"],
+                        c_["rope_dims"], out=hd.out_c)
+                if sparse:
+                    return lambda: L.csa_sparse_mqa_decode(
+                        g_["csa_q"], hd.ring, hd.cache, hd.idx, hd.pos, g_["csa_sink"],
+                        rope_dims=c_["rope_dims"], out=hd.out_c)
+                if fp8:
+                    return lambda: L.hca_dense_mqa_decode_fp8(
+                        g_["hca_q"], k8["hring"], k8["hcache"], hd.pos, g_["hca_sink"],
+                        c_["m_hca"], c_["rope_dims"], out=hd.out_h)
+                return lambda: L.hca_dense_mqa_decode(
+                    g_["hca_q"], hd.hring, hd.hcache, hd.pos, g_["hca_sink"], c_["m_hca"],
+                    rope_dims=c_["rope_dims"], out=hd.out_h)
+            att_us = {}
+            for nm, fp8, sp in (("sparse_bf16", False, True), ("sparse_fp8", True, True),
+                                ("dense_bf16", False, False), ("dense_fp8", True, False)):
+                att_us[nm] = med_us(time_ahead(graph_of(att(fp8, sp)).replay, nd, 3, flush))
+            s8 = lambda: hd.step(kv8=True)  # noqa: E731
+            t8 = time_ahead(s8, nd, 3, flush)
+            g8 = graph_of(s8)
+            tg8 = time_ahead(g8.replay, nd, 3, flush)
+            del g8
+            b8 = hd.algorithmic_bytes(kv8=True)
+            dec[wname]["fp8_kv"] = {
+                "us_per_step": med_us(t8), "graph_us_per_step": med_us(tg8),
+                "row_bytes": [L.kv_fp8_row_bytes(c_["c"], c_["rope_dims"]), 2 * c_["c"]],
+                "hbm_bytes_algorithmic": b8, "hbm_frac": b8 / (med_us(t8) * 1e-6) / PEAK_HBM,
+                "attention_graph_us_cold": att_us}
+            del hd.kv8, k8
             # the same step over caches in shuffled pages of 128 raw tokens
             hd.paginate(128)
             gp = graph_of(hd.step_paged)

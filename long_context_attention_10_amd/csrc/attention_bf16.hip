@@ -519,6 +519,8 @@ __global__ __launch_bounds__(256, 2) void mqa_decode_bf16_kernel(
   __shared__ int sidx[SPARSE ? kMaxK : 1];
   __shared__ int64_t srow[PAGED ? kDecSplitMax : 1];  // pool row per staged entry slot
   __shared__ float2 rope_tab[C / 2];
+  constexpr int kRaw8 = kv8_row_bytes(512, 448);  // the widest FP8 row (r < 512)
+  __shared__ __align__(16) uint8_t raw8[KV8 ? 2 * kT * kRaw8 : 16];  // tiles ti & 1
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -527,13 +529,14 @@ __global__ __launch_bounds__(256, 2) void mqa_decode_bf16_kernel(
   const int64_t b = blockIdx.y;
   const int split = blockIdx.x;
 
-  // q first: its address does not depend on the position
+  // q and the sink first: their addresses do not depend on the position
   uint4 qraw[NKG];
   {
     const uint16_t* qh = q + (b * nh + (head < nh ? head : 0)) * C + lg * 8;
 #pragma unroll
     for (int g = 0; g < NKG; ++g) qraw[g] = *(const uint4*)(qh + g * 32);
   }
+  const float sink_h = head < nh ? sink[head] : 0.f;
   // This chunk's first index slots, loaded before the position is known on
   // the guess that the window is full (t + 1 >= n_win); used if it is.
   const int64_t cbeg = (int64_t)split * spl;
@@ -569,64 +572,105 @@ __global__ __launch_bounds__(256, 2) void mqa_decode_bf16_kernel(
                          return cache + (PAGED ? srow[j - nwin - s0] : b * n_entries + e) * C;
                        });
   };
-  // ---- FP8 rows: register-staged gather (C = 512, one row per LDS burst)
+  // ---- FP8 rows (C = 512): each wave gathers its own rows w, w + 4, ...,
+  // w + 28 of a tile as raw bytes into LDS with DMA, two tiles ahead of the
+  // one computing (no registers held meanwhile), then decodes them to the
+  // bf16 tile layout.  Every gather is exactly kT / 4 DMA instructions per
+  // wave (a masked row loads a row of this sequence's ring that is then
+  // ignored), so a wait for all but the newest gather is vmcnt(kT / 4).  A
+  // masked row's bf16 row is written as zeros, so that P = 0 never meets a
+  // non-finite V.
   static_assert(!KV8 || C == 512, "FP8 rows are 512 channels wide");
   const int RB8 = kv8_row_bytes(C, r);
   const int nf8 = C - r;
-  const uint8_t* ring8 = (const uint8_t*)ring;
   const uint8_t* cache8 = (const uint8_t*)cache;
-  uint4 st8[kT / 4];  // this lane's raw part of each of the wave's rows:
-                      // 8 codes and the block's scale byte, or 8 bf16 channels
-  auto row8_of = [&](int64_t j, bool& ok) -> const uint8_t* {
-    ok = false;
-    if (j >= cend) return ring8;
+  const uint8_t* wbase8 = (const uint8_t*)ring + b * (int64_t)n_win * RB8;
+  int ok8 = 0;  // lanes 0..7, bit p: row wave + 4 * lane of the tile of parity p is live
+  auto row8_of = [&](int64_t j, int& ok) -> const uint8_t* {
+    ok = 0;
+    if (j >= cend) return wbase8;
     if (j < nwin) {
       int slot = w0 + (int)j;
       if (slot >= n_win) slot -= n_win;
-      ok = true;
-      return ring8 + (b * (int64_t)n_win + slot) * RB8;
+      ok = 1;
+      return wbase8 + (int64_t)slot * RB8;
     }
     const int64_t e = SPARSE ? (int64_t)sidx[j - nwin - s0] : j - nwin;
-    if (e < 0 || e >= n_entries) return ring8;
-    ok = true;
+    if (e < 0 || e >= n_entries) return wbase8;
+    ok = 1;
     return cache8 + (PAGED ? srow[j - nwin - s0] : b * n_entries + e) * RB8;
   };
-  auto load8 = [&](int ti, int buf) {  // wave w: rows w, w + 4, ..., w + 28
-    const uint8_t* rp = ring8;
+  auto dma8 = [&](int ti) {  // raw bytes of this wave's rows of tile ti
+    const int par = ti & 1;
+    const uint8_t* rp = wbase8;
     if (lane < kT / 4) {
-      const int row = wave + 4 * lane;
-      bool ok;
-      rp = row8_of(cbeg + (int64_t)ti * kT + row, ok);
-      valid[buf][row] = ok;
+      int ok;
+      rp = row8_of(cbeg + (int64_t)ti * kT + wave + 4 * lane, ok);
+      ok8 = (ok8 & ~(1 << par)) | (ok << par);
     }
     const uint32_t lo_a = (uint32_t)(size_t)rp, hi_a = (uint32_t)((size_t)rp >> 32);
+    const int nl = RB8 / 16;  // 16-byte pieces per row
+    uint8_t* dst = raw8 + par * (kT * kRaw8);
 #pragma unroll
     for (int u = 0; u < kT / 4; ++u) {
-      // readlane returns int: take both halves as uint32 so that the low
-      // half is not sign-extended into the high one
+      // readlane returns int: both halves as uint32 (no sign extension)
       const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane(lo_a, u);
       const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane(hi_a, u);
       const uint8_t* g = (const uint8_t*)(size_t)(((uint64_t)hi << 32) | lo);
-      if (8 * lane < nf8) {
-        const uint2 cw = *(const uint2*)(g + 8 * lane);
-        st8[u] = make_uint4(cw.x, cw.y, g[nf8 + 2 * r + lane / 8], 0u);
-      } else {
-        st8[u] = *(const uint4*)(g + nf8 + 16 * (lane - nf8 / 8));
+      if (lane < nl) lds_dma16(g + 16 * lane, dst + (wave + 4 * u) * kRaw8);
+    }
+  };
+  auto decode8 = [&](int ti) {  // this wave's raw rows of tile ti -> bf16 tile ti & 1
+    const int par = ti & 1;
+    if (lane < kT / 4) valid[par][wave + 4 * lane] = (ok8 >> par) & 1;
+    // Branch-free, four rows at a time, so that their LDS reads issue back to
+    // back: a code lane (8 * lane < c - r) reads its 8 codes and its block's
+    // scale byte, a RoPE lane its 8 bf16 channels (two 8-byte reads); every
+    // lane converts, and selects keep the right result (zero for a masked row).
+    const bool code_lane = 8 * lane < nf8;
+    const int off0 = code_lane ? 8 * lane : nf8 + 16 * (lane - nf8 / 8);
+    const int offs = code_lane ? nf8 + 2 * r + lane / 8 : 0;
+    const uint8_t* raw0 = raw8 + par * (kT * kRaw8);
+    uint8_t* dst0 = smem + par * G::TILE + 16 * lane;
+#pragma unroll
+    for (int u0 = 0; u0 < kT / 4; u0 += 4) {
+      uint2 w0[4], w1[4];
+      uint32_t sb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint8_t* raw = raw0 + (wave + 4 * (u0 + i)) * kRaw8;
+        w0[i] = *(const uint2*)(raw + off0);
+        w1[i] = *(const uint2*)(raw + off0 + 8);
+        sb[i] = raw[offs];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // the matrix cores' OCP E4M3 conversion times the block's 2^e (byte
+        // e + 127 is the exponent field of 2^e as fp32); every product is
+        // exact in bf16
+        const float sc = __uint_as_float(sb[i] << 23);
+        const uint32_t c0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0[i].x, sc, false));
+        const uint32_t c1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0[i].x, sc, true));
+        const uint32_t c2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0[i].y, sc, false));
+        const uint32_t c3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0[i].y, sc, true));
+        // all-ones when the row is live (a wave-uniform mask, no branch)
+        const uint32_t km = 0u - (uint32_t)((__builtin_amdgcn_readlane(ok8, u0 + i) >> par) & 1);
+        uint4 o;
+        o.x = (code_lane ? c0 : w0[i].x) & km;
+        o.y = (code_lane ? c1 : w0[i].y) & km;
+        o.z = (code_lane ? c2 : w1[i].x) & km;
+        o.w = (code_lane ? c3 : w1[i].y) & km;
+        *(uint4*)(dst0 + (wave + 4 * (u0 + i)) * G::BURST) = o;
       }
     }
   };
-  auto store8 = [&](int buf) {  // decode to bf16 into the tile's LDS rows
-#pragma unroll
-    for (int u = 0; u < kT / 4; ++u) {
-      uint4 o = st8[u];
-      if (8 * lane < nf8) {
-        float v[8];
-        e4m3x4_to_f32(st8[u].x, (int)st8[u].z - 127, v);
-        e4m3x4_to_f32(st8[u].y, (int)st8[u].z - 127, v + 4);
-        o = f32_to_chunk<BF16>(v);
-      }
-      *(uint4*)(smem + buf * G::TILE + (wave + 4 * u) * G::BURST + 16 * lane) = o;
-    }
+  // wait until the gather of tile ti has landed, the next one (issued
+  // later) still in flight when `newer`
+  auto wait8 = [&](bool newer) {
+    if (newer)
+      wait_vmem_fence_n<kT / 4>();
+    else
+      wait_vmem_fence_n<0>();
   };
 
   const bool early0 = !KV8 && cbeg + kT <= nwin;  // tile 0 is window rows only
@@ -659,8 +703,12 @@ __global__ __launch_bounds__(256, 2) void mqa_decode_bf16_kernel(
   }
   __syncthreads();
   if constexpr (KV8) {
-    load8(0, 0);
-    store8(0);
+    // the compiler counts only its own loads: settle them (q, the sink) so
+    // that none of its waits later drains the gathers, which land while the
+    // query prologue runs
+    wait_vmem();
+    dma8(0);
+    if (ntiles > 1) dma8(1);
   } else if (!early0) {
     issue_tile(0, 0);
   }
@@ -668,7 +716,7 @@ __global__ __launch_bounds__(256, 2) void mqa_decode_bf16_kernel(
   bf16x8_t qf[NKG];
   q_prologue<C>(qraw, qf, rope_tab, qk_norm, eps, r, lg);
   constexpr float LOG2E = 1.4426950408889634f;
-  float run_m = (head < nh ? sink[head] : 0.f) * LOG2E;  // a finite start, log2 units
+  float run_m = sink_h * LOG2E;  // a finite start, log2 units
   float run_l = 0.f;                                     // the sink is the combine's
   A o;
 #pragma unroll
@@ -679,19 +727,32 @@ __global__ __launch_bounds__(256, 2) void mqa_decode_bf16_kernel(
   const int koff1 = G::off(slot_pi(lc >> 2, 1, lc & 3)) + lg * 16;
   const int troff0 = G::off(slot_pi(lg, 0, lc >> 2)) + 8 * (lc & 3);
   const int troff1 = G::off(slot_pi(lg, 1, lc >> 2)) + 8 * (lc & 3);
-  wait_vmem();
+  if constexpr (KV8) {
+    wait8(ntiles > 1);
+    decode8(0);
+    if (ntiles > 2) dma8(2);
+  } else {
+    wait_vmem();
+  }
   __syncthreads();
   for (int ti = 0; ti < ntiles; ++ti) {
     const int buf = ti & 1;
     if constexpr (KV8) {
-      if (ti + 1 < ntiles) load8(ti + 1, buf ^ 1);
+      // tile ti+1's rows landed while tile ti-1 computed (tile ti+2's gather
+      // may still run); bf16 buffer buf^1 was last read before the previous
+      // barrier.  The decode is straight-line code ahead of the tile's
+      // matrix work, which the compiler may interleave with it.
+      if (ti + 1 < ntiles) {
+        wait8(ti + 2 < ntiles);
+        decode8(ti + 1);
+      }
     } else {
       if (ti + 1 < ntiles) issue_tile(ti + 1, buf ^ 1);
     }
     mqa_tile<C>(smem + buf * G::TILE, valid[buf], qf, o, run_m, run_l, scale * LOG2E, koff0,
                 koff1, troff0, troff1, lg);
     if constexpr (KV8) {
-      if (ti + 1 < ntiles) store8(buf ^ 1);
+      if (ti + 3 < ntiles) dma8(ti + 3);  // raw buffer (ti+1) & 1 is decoded
     } else {
       wait_vmem();
     }

@@ -176,22 +176,6 @@ __host__ __device__ constexpr inline int kv8_row_bytes(int c, int r) {
   return ((c - r) + 2 * r + (c - r) / 64 + 15) & ~15;
 }
 
-// Four E4M3 codes (bytes of `w`, lowest first) times 2^e as fp32 values.
-// E4M3: sign bit 7, exponent field bits 6..3 (bias 7), mantissa bits 2..0;
-// field 0 holds the subnormals m * 2^-9.  Every value is exact in fp32 (and in
-// bf16: at most 4 significant bits).
-CSA_DEV void e4m3x4_to_f32(uint32_t w, int e, float* v) {
-  const float sub = __uint_as_float((uint32_t)(e - 9 + 127) << 23);  // 2^(e-9)
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t c = (w >> (8 * i)) & 0xffu;
-    const uint32_t ef = (c >> 3) & 15u, m = c & 7u;
-    const float a = ef ? __uint_as_float(((ef + (uint32_t)(e - 7 + 127)) << 23) | (m << 20))
-                       : (float)m * sub;
-    v[i] = (c & 0x80u) ? -a : a;
-  }
-}
-
 // Order-preserving map fp32 -> uint32 (larger float -> larger key).
 CSA_DEV uint32_t float_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -219,6 +203,16 @@ CSA_DEV void lds_dma16(const void* g, const void* lds_dst) {
 
 // Wait for every outstanding memory operation of the wave.
 CSA_DEV void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Wait until at most N vector-memory operations of the wave are outstanding,
+// as a compiler barrier: LDS reads of DMA-filled bytes that follow it in
+// program order are not moved above it.  Loads complete in issue order, so
+// this waits for all but the N newest.
+template <int N>
+CSA_DEV void wait_vmem_fence_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // s_waitcnt immediate that waits until at most n (< 64) vector-memory
 // operations of the wave are outstanding; the other counters are left alone
