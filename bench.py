@@ -671,6 +671,124 @@ class HybridDecode:
         return weights + keys + csa + hca + qo
 
 
+def prefill_flops(cfg):
+    """Algorithmic FLOPs of one CSA prefill step, by stage: the projections
+    (2 d per output column per token: C, Z and window rows of the main
+    compressor, C and Z of the indexer's), the index scores (2 hI cI per
+    visible (token, entry) pair) and the attention (4 nh c per (token,
+    candidate) pair)."""
+    n, d, c, m, ov = cfg["n"], cfg["d"], cfg["c"], cfg["m"], cfg["overlap"]
+    w, wI = (1 + ov) * c, (1 + ov) * cfg["cI"]
+    t = np.arange(n, dtype=np.int64)
+    vis = (t + 1) // m
+    pairs = np.minimum(cfg["n_win"], t + 1) + np.minimum(cfg["k"], vis)
+    return {"projection": 2.0 * n * d * (2 * w + c + 2 * wI),
+            "index": 2.0 * cfg["hI"] * cfg["cI"] * float(vis.sum()),
+            "attention": 4.0 * cfg["nh"] * c * float(pairs.sum())}
+
+
+def c1_record(steps, warmup, dev):
+    """The 2K-token fp32 CSA workload end to end (compressors, index + top-k,
+    sparse attention): step time and its fraction of the fp32 peak."""
+    cfg = configs.get("csa_prefill_2k_f32")
+    pf = CsaPrefill(cfg, dev)
+    ms = float(np.mean(time_region(pf.step, steps, warmup)))
+    st = {nm: float(np.mean(time_region(fn, max(3, steps), 1)))
+          for nm, fn in (("compress", pf.compress), ("index_topk", pf.index),
+                         ("sparse_mqa", pf.attend))}
+    fl = prefill_flops(cfg)
+    tot = sum(fl.values())
+    return {"workload": cfg["name"], "ms_per_step": ms, "tokens_per_s": cfg["n"] / (ms * 1e-3),
+            "stages_ms": st, "gflop": {k_: v / 1e9 for k_, v in fl.items()},
+            "tflops": tot / (ms * 1e-3) / 1e12, "frac_fp32_peak": tot / (ms * 1e-3) / PEAK_FP32}
+
+
+def oracle_times():
+    """The CPU fp64 oracle timed on whole workloads (no GPU): the 2K fp32 CSA
+    prefill and the 16K bf16 HCA prefill in full, and one decode step of one
+    sequence at 128K and at 1M context (the new token's projections by the
+    three compressors with the pooling and epilogue of the block it closes,
+    the index scores over every visible key and the top-k, the sparse and the
+    dense attention rows), scaled by the batch for a whole step."""
+    from oracle import csa_oracle as O
+    cores = len(os.sched_getaffinity(0))
+    f = lambda x: x.detach().to("cpu", torch.float64).numpy()  # noqa: E731
+    out = {"cores": cores}
+    # 2K fp32 CSA prefill, every stage for every token
+    cfg = configs.get("csa_prefill_2k_f32")
+    t = I.csa_prefill_inputs(cfg)
+    n, m, ov, k, c = cfg["n"], cfg["m"], cfg["overlap"], cfg["k"], cfg["c"]
+    H = f(t["H"])
+    t0 = time.perf_counter()
+    comp = O.compress_prefill(H, f(t["W_kv"]).T, f(t["W_z"]).T, f(t["ape"]), m, ov)
+    win = O.window_rows(H, f(t["W_win"]).T)
+    KI = O.compress_prefill(H, f(t["WI_kv"]).T, f(t["WI_z"]).T, f(t["apeI"]), m, ov)
+    t1 = time.perf_counter()
+    idx = O.topk(O.index_scores(f(t["qI"]), f(t["wI"]), KI, m), k, m)
+    t2 = time.perf_counter()
+    O.sparse_mqa_prefill(f(t["q"]), win, comp, idx, f(t["sink"]), cfg["n_win"], c ** -0.5)
+    t3 = time.perf_counter()
+    out[cfg["name"]] = {"s": t3 - t0, "stages_s": {"compress": t1 - t0, "index_topk": t2 - t1,
+                                                    "sparse_mqa": t3 - t2}}
+    # 16K bf16 HCA prefill
+    cfg = configs.get("hca_prefill_16k_bf16")
+    t = I.csa_prefill_inputs(cfg, with_indexer=False)
+    n, m, c = cfg["n"], cfg["m"], cfg["c"]
+    H = f(t["H"])
+    t0 = time.perf_counter()
+    comp = O.compress_prefill(H, f(t["W_kv"]).T, f(t["W_z"]).T, f(t["ape"]), m, 0, store="bf16")
+    win = O.window_rows(H, f(t["W_win"]).T, store="bf16")
+    t1 = time.perf_counter()
+    O.dense_mqa_prefill(f(t["q"]), win, comp, f(t["sink"]), m, cfg["n_win"], c ** -0.5,
+                        store="bf16")
+    t2 = time.perf_counter()
+    out[cfg["name"]] = {"s": t2 - t0, "stages_s": {"compress": t1 - t0, "dense_mqa": t2 - t1}}
+    del H, comp, win
+    # one decode step of one sequence
+    rng = np.random.default_rng(0)
+    for wname in ("decode_b32_128k_bf16", "decode_b4_1m_bf16"):
+        dc = configs.get(wname)
+        d, c, m, mh, ov, r = dc["d"], dc["c"], dc["m"], dc["m_hca"], dc["overlap"], dc["rope_dims"]
+        tpos = dc["ctx"] - 1
+        vis, vis_h, nw = (tpos + 1) // m, (tpos + 1) // mh, min(dc["n_win"], tpos + 1)
+        w, wI = (1 + ov) * c, (1 + ov) * dc["cI"]
+        h = rng.standard_normal((1, d))
+        Wm = rng.standard_normal((d, 2 * w + c)) * d ** -0.5
+        Wi = rng.standard_normal((d, 2 * wI)) * d ** -0.5
+        Wh = rng.standard_normal((d, 3 * c)) * d ** -0.5
+        blk = lambda rows, cols: rng.standard_normal((rows, cols))  # noqa: E731
+        Cm, Zm, Ci, Zi, Ch, Zh = (blk((1 + ov) * m, w), blk((1 + ov) * m, w),
+                                  blk((1 + ov) * m, wI), blk((1 + ov) * m, wI),
+                                  blk(mh, c), blk(mh, c))
+        qI, wIv = blk(dc["hI"], dc["cI"])[None], rng.uniform(size=(1, dc["hI"]))
+        KI = blk(vis, dc["cI"])
+        q = blk(dc["nh"], c)
+        sink = blk(1, dc["nh"])[0]
+        ent = O.rms_norm(blk(dc["k"], c), 1e-6)
+        ent_h = O.rms_norm(blk(vis_h, c), 1e-6)
+        wrows = O.rms_norm(blk(nw, c), 1e-6)
+        t0 = time.perf_counter()
+        O.project(h, Wm), O.project(h, Wi), O.project(h, Wh)
+        for C_, Z_, ape_, mm, ovv in ((Cm, Zm, blk(m, w), m, ov), (Ci, Zi, blk(m, wI), m, ov),
+                                      (Ch, Zh, blk(mh, c), mh, 0)):
+            e_ = O.pool(C_, Z_, ape_, mm, ovv)[-1:]
+            O.entry_epilogue(e_[:, :c] if e_.shape[1] > c else e_, [tpos], True, 1e-6, r,
+                             10000.0, "bf16")
+        t1 = time.perf_counter()
+        sc = O.index_scores(qI, wIv, KI, m, t0=tpos)
+        O.topk(sc, dc["k"], m, t0=tpos)
+        t2 = time.perf_counter()
+        O.attend_decode_row(q, tpos, wrows, ent, sink, c ** -0.5, rope_dims=r, store="bf16")
+        O.attend_decode_row(q, tpos, wrows, ent_h, sink, c ** -0.5, rope_dims=r, store="bf16")
+        t3 = time.perf_counter()
+        out[wname] = {"s_per_sequence": t3 - t0, "s_per_step": (t3 - t0) * dc["batch"],
+                      "batch": dc["batch"],
+                      "stages_s_per_sequence": {"compressors": t1 - t0, "index_topk": t2 - t1,
+                                                "attention": t3 - t2}}
+        del KI
+    return out
+
+
 def cpu_baseline(pf, sample_tokens=2048, sample_rows=48):
     """Time the CPU fp64 oracle on a bounded sample of the prefill workload and
     scale to tokens/s: compressor on the first `sample_tokens` tokens, indexer
@@ -756,7 +874,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="only the copy reference and the MQA prefill, for counter passes")
+    ap.add_argument("--oracle-times", action="store_true",
+                    help="only time the CPU oracle on whole workloads (no GPU) and print that")
     a = ap.parse_args()
+    if a.oracle_times:
+        print(json.dumps({"oracle_times": oracle_times()}), flush=True)
+        return
     if a.gpus != 1:
         print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus {a.gpus}).",
               file=sys.stderr)
@@ -835,6 +958,18 @@ def main():
                                   / (ha_ms * 1e-3) / PEAK_HBM}
         del hp
         torch.cuda.empty_cache()
+    # the 2K-token fp32 workload end to end, against the fp32 peak
+    rec["c1_prefill_2k_f32"] = c1_record(a.steps, a.warmup, dev)
+    # the 64K workload without overlapping compression (ov = 0)
+    pf0 = CsaPrefill(dict(cfg, overlap=0), dev)
+    ms0 = float(np.mean(time_region(pf0.step, a.steps, a.warmup)))
+    rec["ov0_prefill"] = {
+        "overlap": 0, "ms_per_step": ms0, "tokens_per_s": n / (ms0 * 1e-3),
+        "stages_ms": {nm: float(np.mean(time_region(fn, max(3, a.steps), 1)))
+                      for nm, fn in (("compress", pf0.compress), ("index_topk", pf0.index),
+                                     ("sparse_mqa", pf0.attend))}}
+    del pf0
+    torch.cuda.empty_cache()
     # the deterministic attention backward at the 2K fp32 workload: entries,
     # window rows and the selection from the forward path, dout ~ N(0, 1)
     rec["backward"] = backward_record(a.steps)
@@ -907,6 +1042,14 @@ def main():
                           "hbm_bytes_algorithmic": byts,
                           "hbm_frac": byts / (us * 1e-6) / PEAK_HBM,
                           "graph_hbm_frac": byts / (ug * 1e-6) / PEAK_HBM}
+            # the step at t = ctx, which emits no entry (the graph reads the
+            # position from device memory)
+            hd.pos.fill_(dc["ctx"])
+            tne = time_ahead(hd.step, nd, 3, flush)
+            tneg = time_ahead(g.replay, nd, 3, flush)
+            hd.pos.fill_(dc["ctx"] - 1)
+            dec[wname]["no_emission_t_ctx"] = {"us_per_step": med_us(tne),
+                                               "graph_us_per_step": med_us(tneg)}
             del g
             # the FP4 indexer path (rotation + E2M1 keys and q^I): the top-k
             # over FP4 keys against the same call over bf16 keys, and how much
@@ -991,6 +1134,17 @@ def main():
                 "graph_us_per_step": float(np.median(tgp)) * 1e3,
                 "graph_us_per_step_warm_cache": med_us(tgpw)}
             del hd
+            torch.cuda.empty_cache()
+            # the same step without overlapping compression (ov = 0)
+            hd0 = HybridDecode(dict(dc, overlap=0), dev)
+            g0 = graph_of(hd0.step)
+            t0e = time_ahead(hd0.step, nd, 3, flush)
+            t0g = time_ahead(g0.replay, nd, 3, flush)
+            b0 = hd0.algorithmic_bytes()
+            dec[wname]["ov0"] = {"overlap": 0, "us_per_step": med_us(t0e),
+                                 "graph_us_per_step": med_us(t0g), "hbm_bytes_algorithmic": b0,
+                                 "hbm_frac": b0 / (med_us(t0e) * 1e-6) / PEAK_HBM}
+            del g0, hd0
             torch.cuda.empty_cache()
         rec["decode"] = dec
     if not a.no_cpu_baseline:

@@ -107,6 +107,36 @@ def test_hca_prefill_16k_sampled(lib):
     assert_out_close(out[rows], oref, "bf16", "dense attention rows")
 
 
+def test_hca_prefill_16k_end_to_end(lib):
+    """The 16K HCA workload from its raw inputs, every row: the oracle runs
+    its own compressor, window rows and dense attention in fp64 (rounding
+    stored values to bf16 where the path stores them), and all 16384 x 64
+    output rows must be within the bf16 output bound of the GPU's.  The
+    GPU's entries and window rows may differ from the oracle's by one bf16
+    step (A17's flips), which moves an output by far less than the bound."""
+    cfg = configs.get("hca_prefill_16k_bf16")
+    _say("16k HCA prefill end to end", cfg["name"])
+    n, d, c, m, nh = cfg["n"], cfg["d"], cfg["c"], cfg["m"], cfg["nh"]
+    key = (0, cfg["name"])
+    H = I.normal((n, d), key + ("H",), dtype="bf16", device=DEV)
+    Wkv = I.normal((c, d), key + ("Wkv",), std=d ** -0.5, dtype="bf16", device=DEV)
+    Wz = I.normal((c, d), key + ("Wz",), std=d ** -0.5, dtype="bf16", device=DEV)
+    Ww = I.normal((c, d), key + ("Ww",), std=d ** -0.5, dtype="bf16", device=DEV)
+    ape = I.normal((m, c), key + ("ape",), device=DEV)
+    q = I.normal((n, nh, c), key + ("q",), dtype="bf16", device=DEV)
+    sink = I.normal((nh,), key + ("sink",), device=DEV)
+    res = lib.csa_compress_prefill(H, Wkv, Wz, ape, m, 0, W_win=Ww)
+    out = lib.hca_dense_mqa_prefill(q, res["win"], res["comp"], sink, m)
+    torch.cuda.synchronize()
+    Hh = f64(H)
+    comp = O.compress_prefill(Hh, f64(Wkv).T, f64(Wz).T, f64(ape), m, 0, store="bf16")
+    win = O.window_rows(Hh, f64(Ww).T, store="bf16")
+    assert_stored_close(res["win"], win, "bf16", "all window rows")
+    ref = O.dense_mqa_prefill(f64(q), win, comp, f64(sink), m, cfg["n_win"], c ** -0.5,
+                              store="bf16")
+    assert_out_close(out, ref, "bf16", "all 16384 output rows")
+
+
 @pytest.mark.parametrize("wname,seqs", [("decode_b32_128k_bf16", [0, 13, 31]),
                                         ("decode_b4_1m_bf16", [0, 3])])
 def test_decode_step_sampled(lib, wname, seqs):
