@@ -123,36 +123,45 @@ __global__ __launch_bounds__(256, 2) void proj_gemm_kernel(
 }
 
 // ===========================================================================
-// bf16 projection GEMM: 256x256 output tile per 512-thread workgroup, 4x2
-// waves of 64x128 (2x4 blocks of 32x32x16 MFMA, 128 accumulators; two waves
-// per SIMD).  A and W panels stream into a ring of four LDS stages (32-wide
-// K slices) by direct global->LDS loads issued three slices ahead, so a
-// slice's loads have three slices of products to land in; the next k-group's
-// fragments are read while a k-group's products run.  In LDS, 16-byte
-// granule g of tile row r (64 bytes per row) sits at column g ^ ((r >> 2) & 3),
-// so every 16 consecutive rows of a fragment read cover all banks.  Tile
-// order: die x (workgroup id mod 8) takes M blocks x, x+8, ... in groups that
-// its workgroups run side by side, so the A and W slices they stream are
-// shared in the die's L2.  Each stacked weight matrix writes its columns to
-// its own output (fp32 or bf16, rounded once); blockIdx.y selects a group of
-// a grouped product (A, W0 and output 0 offset per group).
+// bf16 projection GEMM: TM x TN output tile per 512-thread workgroup, 4x2
+// waves of (TM/4) x (TN/2) (blocks of 32x32x16 MFMA; the 256x256 tile gives
+// each wave 2x4 blocks, 128 accumulators, two waves per SIMD).  A and W
+// panels stream into a ring of four LDS stages (32-wide K slices) by direct
+// global->LDS loads issued three slices ahead, so a slice's loads have three
+// slices of products to land in; the next k-group's fragments are read while
+// a k-group's products run.  In LDS, 16-byte granule g of tile row r (64
+// bytes per row) sits at column g ^ ((r >> 2) & 3), so every 16 consecutive
+// rows of a fragment read cover all banks.  Tile order: die x (workgroup id
+// mod 8) takes M blocks x, x+8, ... in groups that its workgroups run side
+// by side, so the A and W slices they stream are shared in the die's L2.
+// Each stacked weight matrix writes its columns to its own output (fp32 or
+// bf16, rounded once); blockIdx.y selects a group of a grouped product (A,
+// W0 and output 0 offset per group).  Smaller tiles serve products too
+// narrow to give the 256x256 tile a workgroup per CU.
 // ===========================================================================
-constexpr int kGM = 256, kGN = 256;  // output tile
 constexpr int kGKB = 64;             // bytes of K per slice (32 bf16)
+constexpr int kGemmBigTileMinWorkgroups = 256;  // one 256x256 tile per CU at least
+constexpr int kGemmSmallTM = 256;               // rows of the narrow-product tile
 constexpr int kGS = 4;               // LDS stages
 constexpr int kGAhead = kGS - 1;     // slices in flight ahead of the one in use
 
-template <class OUT>
+template <class OUT, int TM, int TN>
 __global__ __launch_bounds__(512, 1) void proj_gemm_bf16_kernel(
     const uint16_t* __restrict__ A, int64_t lda, int64_t M, int K,
     const uint16_t* __restrict__ W0, int r0, const uint16_t* __restrict__ W1, int r1,
     const uint16_t* __restrict__ W2, int r2, GemmOuts outs, int mblocks, int ntiles,
     int64_t a_zoff, int64_t w_zoff, int64_t o_zoff) {
-  __shared__ __align__(16) uint8_t sA[kGS][kGM * kGKB];
-  __shared__ __align__(16) uint8_t sB[kGS][kGN * kGKB];
+  static_assert(TM % 128 == 0 && TN % 128 == 0, "tiles are multiples of 128");
+  constexpr int WM = TM / 4, WN = TN / 2;     // wave tile
+  constexpr int MB = WM / 32, NB = WN / 32;   // 32x32 blocks per wave
+  constexpr int NA = TM / 128, NW = TN / 128; // 1 KiB load chunks per wave and slice
+  constexpr int LPS = NA + NW;                // loads per wave and slice
+  static_assert(LPS <= 2 * MB + 2, "every load of a slice has a product slot");
+  __shared__ __align__(16) uint8_t sA[kGS][TM * kGKB];
+  __shared__ __align__(16) uint8_t sB[kGS][TN * kGKB];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;  // 64-row band, 128-column band
+  const int wm = wave >> 1, wn = wave & 1;  // row band, column band
   // die x owns M blocks x, x+8, ...; it walks them in groups of 8, and
   // within a group over 8 x 4 tiles (8 M blocks, 4 N tiles) at a time, so the
   // 32 workgroups a die runs together share every A and W slice they load
@@ -170,23 +179,28 @@ __global__ __launch_bounds__(512, 1) void proj_gemm_bf16_kernel(
   }
   const int mbk = 8 * (8 * mg + mi) + xcd;
   if (mbk >= mblocks) return;
-  const int64_t m0 = (int64_t)mbk * kGM;
-  const int n0 = nt * kGN;
+  const int64_t m0 = (int64_t)mbk * TM;
+  const int n0 = nt * TN;
   const int ntot = r0 + r1 + r2;
   A += blockIdx.y * a_zoff;
   W0 += blockIdx.y * w_zoff;
 
-  // Loads: wave w fills 1 KiB chunks w and w+8 (16 rows each) of both
+  // Loads: wave w fills 1 KiB chunks w, w+8, ... (16 rows each) of both
   // panels; lane i of chunk c carries row 16c + i/4 into LDS column i%4,
   // which holds global granule (i%4) ^ ((row >> 2) & 3).
-  const uint8_t* pa[2];
-  const uint8_t* pb[2];
+  const uint8_t* pa[NA];
+  const uint8_t* pb[NW];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < NA; ++u) {
     const int row = 16 * (wave + 8 * u) + (lane >> 2);
     const int gran = (lane & 3) ^ ((row >> 2) & 3);
     const int64_t ar = min64(m0 + row, M - 1);  // rows past M read a valid row
     pa[u] = (const uint8_t*)(A + ar * lda) + gran * 16;
+  }
+#pragma unroll
+  for (int u = 0; u < NW; ++u) {
+    const int row = 16 * (wave + 8 * u) + (lane >> 2);
+    const int gran = (lane & 3) ^ ((row >> 2) & 3);
     int n = n0 + row;
     const uint16_t* wp = W0;
     if (n >= ntot) n = 0;  // masked columns read a valid row
@@ -194,35 +208,34 @@ __global__ __launch_bounds__(512, 1) void proj_gemm_bf16_kernel(
     else if (n >= r0) { wp = W1; n -= r0; }
     pb[u] = (const uint8_t*)(wp + (int64_t)n * K) + gran * 16;
   }
-  constexpr int LPS = 4;  // loads per wave and slice
-  // load q (0..3) of slice kt: A chunk, W chunk, A chunk, W chunk
+  // load q (0 .. LPS-1) of slice kt: the A chunks, then the W chunks
   auto issue1 = [&](int kt, int q) {
-    const int s = kt % kGS, u = q >> 1, chunk = wave + 8 * u;
-    if (q & 1) lds_dma16(pb[u] + (int64_t)kt * kGKB, sB[s] + chunk * 1024);
-    else lds_dma16(pa[u] + (int64_t)kt * kGKB, sA[s] + chunk * 1024);
+    const int s = kt % kGS;
+    if (q < NA) lds_dma16(pa[q] + (int64_t)kt * kGKB, sA[s] + (wave + 8 * q) * 1024);
+    else lds_dma16(pb[q - NA] + (int64_t)kt * kGKB, sB[s] + (wave + 8 * (q - NA)) * 1024);
   };
   auto issue = [&](int kt) {
 #pragma unroll
     for (int q = 0; q < LPS; ++q) issue1(kt, q);
   };
 
-  f32x16_t acc[2][4];
+  f32x16_t acc[MB][NB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
+    for (int j = 0; j < NB; ++j) acc[i][j] = f32x16_t{};
   // fragment rows (l & 31) of 32-row blocks, granule 2*kg + l/32
   const int frow = lane & 31, fhalf = lane >> 5, fsw = (frow >> 2) & 3;
-  const int aoff = (wm * 64 + frow) * kGKB;
-  const int boff = (wn * 128 + frow) * kGKB;
-  bf16x8_t fa[2][2], fb[2][4];
+  const int aoff = (wm * WM + frow) * kGKB;
+  const int boff = (wn * WN + frow) * kGKB;
+  bf16x8_t fa[2][MB], fb[2][NB];
   auto frags = [&](int s, int kg, int slot) {
     const int col = ((2 * kg + fhalf) ^ fsw) * 16;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MB; ++i)
       fa[slot][i] = *(const bf16x8_t*)(sA[s] + aoff + i * 32 * kGKB + col);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NB; ++j)
       fb[slot][j] = *(const bf16x8_t*)(sB[s] + boff + j * 32 * kGKB + col);
   };
 
@@ -239,18 +252,22 @@ __global__ __launch_bounds__(512, 1) void proj_gemm_bf16_kernel(
     const int s = kt % kGS;
     const bool ahead = kt + kGAhead < nk;
     frags(s, 1, 1);
-    // the loads of slice kt+3 go out one per four products, so the
-    // load pipe and the matrix cores work side by side
+    // the loads of slice kt+3 go out between the products, so the load
+    // pipe and the matrix cores work side by side
 #pragma unroll
     for (int kg = 0; kg < 2; ++kg)
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < MB; ++i) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NB; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kg][i], fb[kg][j], acc[i][j],
                                                               0, 0, 0);
-        if (ahead) issue1(kt + kGAhead, 2 * kg + i);
+        if (ahead && kg * MB + i < LPS) issue1(kt + kGAhead, kg * MB + i);
       }
+    if (ahead) {
+#pragma unroll
+      for (int q = 2 * MB; q < LPS; ++q) issue1(kt + kGAhead, q);
+    }
     // slice kt+1 must have landed; the loads of kt+2 and kt+3 may still run
     const int later = min(nk - 1, kt + kGAhead) - (kt + 1);
     if (later >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPS));
@@ -261,18 +278,18 @@ __global__ __launch_bounds__(512, 1) void proj_gemm_bf16_kernel(
   }
 
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int col = n0 + wn * 128 + j * 32 + frow;
+  for (int j = 0; j < NB; ++j) {
+    const int col = n0 + wn * WN + j * 32 + frow;
     int cm = col;  // column within its weight matrix
     OUT* op = (OUT*)outs.p[0] + blockIdx.y * o_zoff;
     int64_t ld = outs.ld[0];
     if (cm >= r0 + r1) { cm -= r0 + r1; op = (OUT*)outs.p[2]; ld = outs.ld[2]; }
     else if (cm >= r0) { cm -= r0; op = (OUT*)outs.p[1]; ld = outs.ld[1]; }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int64_t row = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * fhalf + (e & 3);
+        const int64_t row = m0 + wm * WM + i * 32 + 8 * (e >> 2) + 4 * fhalf + (e & 3);
         if (row < M && col < ntot) {
           if constexpr (sizeof(OUT) == 2) op[row * ld + cm] = f32_to_bf16(acc[i][j][e]);
           else op[row * ld + cm] = acc[i][j][e];
@@ -391,6 +408,59 @@ __global__ __launch_bounds__(256) void pool_entries_kernel(
   }
   row_finish<T, G>(v0, v1, j, c, (int64_t)m * (pos0 / m + i), qk_norm, eps, r, theta, red);
   if (live) {
+    T::st(out, i * c + 2 * j, v0);
+    T::st(out, i * c + 2 * j + 1, v1);
+  }
+}
+
+// The same pooling for long blocks (m >= kPoolSplitM, HCA's m' = 128): one
+// workgroup per entry, its 256 / G thread groups each folding the rows
+// rr = g, g + S, ... of the block (and of block i-1's b-series under
+// overlap) into an online softmax state of their own; the S states are then
+// merged in group order through LDS, so the result does not depend on
+// scheduling.  Few long blocks would otherwise leave most of the chip idle
+// while each thread walked m rows in sequence.
+constexpr int kPoolSplitM = 32;
+
+template <class T, int G>
+__global__ __launch_bounds__(256) void pool_entries_split_kernel(
+    const float* __restrict__ P, int64_t ld, int64_t n_entries, int c, int m, int ov,
+    const float* __restrict__ ape, int qk_norm, float eps, int r, float theta,
+    typename T::S* __restrict__ out, int64_t pos0, int prev0) {
+  constexpr int S = 256 / G;
+  __shared__ float red[4];
+  __shared__ float st[S][6][G];  // (max, sum, acc) of both channels, per group
+  const int g = threadIdx.x / G, j = threadIdx.x % G;
+  const int64_t i = blockIdx.x;  // grid = n_entries
+  const int w = (1 + ov) * c;
+  const int ca = ov ? c : 0;  // a-series column offset
+  float mx0 = -INFINITY, s0 = 0.f, a0 = 0.f, mx1 = -INFINITY, s1 = 0.f, a1 = 0.f;
+  auto fold = [&](int64_t row0, int col) {
+#pragma unroll 4
+    for (int rr = g; rr < m; rr += S) {
+      const float* row = P + (row0 + rr) * ld;
+      const float2 cv = *(const float2*)(row + col + 2 * j);
+      const float2 zv = *(const float2*)(row + w + col + 2 * j);
+      const float2 bv = *(const float2*)(ape + (int64_t)rr * w + col + 2 * j);
+      osm_push(mx0, s0, a0, zv.x + bv.x, cv.x);
+      osm_push(mx1, s1, a1, zv.y + bv.y, cv.y);
+    }
+  };
+  fold(i * m, ca);
+  if (ov && (i > 0 || prev0)) fold((i - 1) * m, 0);  // block i-1's b-series
+  st[g][0][j] = mx0; st[g][1][j] = s0; st[g][2][j] = a0;
+  st[g][3][j] = mx1; st[g][4][j] = s1; st[g][5][j] = a1;
+  __syncthreads();
+  mx0 = st[0][0][j]; s0 = st[0][1][j]; a0 = st[0][2][j];
+  mx1 = st[0][3][j]; s1 = st[0][4][j]; a1 = st[0][5][j];
+#pragma unroll
+  for (int h = 1; h < S; ++h) {
+    osm_merge(mx0, s0, a0, st[h][0][j], st[h][1][j], st[h][2][j]);
+    osm_merge(mx1, s1, a1, st[h][3][j], st[h][4][j], st[h][5][j]);
+  }
+  float v0 = a0 / s0, v1 = a1 / s1;
+  row_finish<T, G>(v0, v1, j, c, (int64_t)m * (pos0 / m + i), qk_norm, eps, r, theta, red);
+  if (g == 0) {
     T::st(out, i * c + 2 * j, v0);
     T::st(out, i * c + 2 * j + 1, v1);
   }
@@ -640,24 +710,40 @@ __global__ __launch_bounds__(256) void decode_update_kernel(
 // ===========================================================================
 // Host launchers
 // ===========================================================================
+template <int TM, int TN>
+static void gemm_bf16_tiles(const void* A, int64_t lda, int64_t M, int K, const WeightStack& w,
+                            const GemmOuts& outs, bool bf16_out, int groups, int64_t a_zoff,
+                            int64_t w_zoff, int64_t o_zoff, hipStream_t st) {
+  const int N = w.total();
+  const int mblocks = (int)((M + TM - 1) / TM), ntiles = (N + TN - 1) / TN;
+  const int mgroups = ((mblocks + 7) / 8 + 7) / 8;  // groups of 8 M blocks per die
+  const dim3 g((unsigned)(8 * mgroups * 8 * ntiles), (unsigned)groups);
+  if (bf16_out)
+    proj_gemm_bf16_kernel<uint16_t, TM, TN><<<g, 512, 0, st>>>(
+        (const uint16_t*)A, lda, M, K, (const uint16_t*)w.w[0], w.rows[0],
+        (const uint16_t*)w.w[1], w.rows[1], (const uint16_t*)w.w[2], w.rows[2], outs, mblocks,
+        ntiles, a_zoff, w_zoff, o_zoff);
+  else
+    proj_gemm_bf16_kernel<float, TM, TN><<<g, 512, 0, st>>>(
+        (const uint16_t*)A, lda, M, K, (const uint16_t*)w.w[0], w.rows[0],
+        (const uint16_t*)w.w[1], w.rows[1], (const uint16_t*)w.w[2], w.rows[2], outs, mblocks,
+        ntiles, a_zoff, w_zoff, o_zoff);
+}
+
+// Tile shape: 256x256 when that gives every CU a workgroup (per group of a
+// grouped product), else the smaller tiles, which give narrow products (few
+// 256-column tiles, a partly empty last one) more workgroups.
 hipError_t launch_gemm_bf16(const void* A, int64_t lda, int64_t M, int K, const WeightStack& w,
                             const GemmOuts& outs, bool bf16_out, int groups, int64_t a_zoff,
                             int64_t w_zoff, int64_t o_zoff, hipStream_t st) {
   const int N = w.total();
   if (M == 0 || N == 0 || groups == 0) return hipSuccess;
-  const int mblocks = (int)((M + kGM - 1) / kGM), ntiles = (N + kGN - 1) / kGN;
-  const int mgroups = ((mblocks + 7) / 8 + 7) / 8;  // groups of 8 M blocks per die
-  const dim3 g((unsigned)(8 * mgroups * 8 * ntiles), (unsigned)groups);
-  if (bf16_out)
-    proj_gemm_bf16_kernel<uint16_t><<<g, 512, 0, st>>>(
-        (const uint16_t*)A, lda, M, K, (const uint16_t*)w.w[0], w.rows[0],
-        (const uint16_t*)w.w[1], w.rows[1], (const uint16_t*)w.w[2], w.rows[2], outs, mblocks,
-        ntiles, a_zoff, w_zoff, o_zoff);
+  const int64_t wg256 = (int64_t)groups * ((M + 255) / 256) * ((N + 255) / 256);
+  if (wg256 >= kGemmBigTileMinWorkgroups)
+    gemm_bf16_tiles<256, 256>(A, lda, M, K, w, outs, bf16_out, groups, a_zoff, w_zoff, o_zoff, st);
   else
-    proj_gemm_bf16_kernel<float><<<g, 512, 0, st>>>(
-        (const uint16_t*)A, lda, M, K, (const uint16_t*)w.w[0], w.rows[0],
-        (const uint16_t*)w.w[1], w.rows[1], (const uint16_t*)w.w[2], w.rows[2], outs, mblocks,
-        ntiles, a_zoff, w_zoff, o_zoff);
+    gemm_bf16_tiles<kGemmSmallTM, 128>(A, lda, M, K, w, outs, bf16_out, groups, a_zoff, w_zoff,
+                                       o_zoff, st);
   return hipGetLastError();
 }
 
@@ -696,13 +782,22 @@ hipError_t launch_pool_entries(int dtype, const float* P, int64_t ld, int64_t n,
   const int64_t ne = n / m;
   if (ne == 0) return hipSuccess;
   CSA_DISPATCH_G(c, {
-    dim3 grid((unsigned)((ne + 256 / G - 1) / (256 / G)));
-    if (dtype == CSA_BF16)
-      pool_entries_kernel<BF16, G><<<grid, 256, 0, st>>>(P, ld, ne, c, m, ov, ape, qk_norm, eps, r,
-                                                         theta, (BF16::S*)out, pos0, prev0);
-    else
-      pool_entries_kernel<F32, G><<<grid, 256, 0, st>>>(P, ld, ne, c, m, ov, ape, qk_norm, eps, r,
-                                                        theta, (float*)out, pos0, prev0);
+    if (m >= kPoolSplitM) {  // a choice by m alone: chunks and one-shot calls agree
+      if (dtype == CSA_BF16)
+        pool_entries_split_kernel<BF16, G><<<(unsigned)ne, 256, 0, st>>>(
+            P, ld, ne, c, m, ov, ape, qk_norm, eps, r, theta, (BF16::S*)out, pos0, prev0);
+      else
+        pool_entries_split_kernel<F32, G><<<(unsigned)ne, 256, 0, st>>>(
+            P, ld, ne, c, m, ov, ape, qk_norm, eps, r, theta, (float*)out, pos0, prev0);
+    } else {
+      dim3 grid((unsigned)((ne + 256 / G - 1) / (256 / G)));
+      if (dtype == CSA_BF16)
+        pool_entries_kernel<BF16, G><<<grid, 256, 0, st>>>(P, ld, ne, c, m, ov, ape, qk_norm, eps,
+                                                           r, theta, (BF16::S*)out, pos0, prev0);
+      else
+        pool_entries_kernel<F32, G><<<grid, 256, 0, st>>>(P, ld, ne, c, m, ov, ape, qk_norm, eps,
+                                                          r, theta, (float*)out, pos0, prev0);
+    }
   });
   return hipGetLastError();
 }
