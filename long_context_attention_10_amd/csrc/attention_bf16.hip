@@ -467,9 +467,314 @@ __global__ __launch_bounds__(256, 2) void mqa_prefill_bf16_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Dense prefill for 128-channel rows and 64 heads (HCA, [R] 2.3.2): one
+// workgroup per block of kDenseTB consecutive tokens, two waves per token,
+// each with 32 of its heads (kDenseHG 16-head groups: their O accumulators,
+// queries and probabilities fit the vector registers, two waves per SIMD).  The block's tokens
+// share nearly all their candidates: their windows differ in a few rows, and
+// the entries visible to the last token include every other token's.  So
+// each 32-row tile is gathered into LDS once, each K and V fragment read from
+// it feeds four head groups, and each wave masks the tile by its own token's
+// window and visible entries.  Tiles are fixed by absolute position: window
+// tile a holds positions 32a .. 32a+31, entry tile e entries 32e .. 32e+31;
+// a block visits the window tiles its tokens' windows touch, then the entry
+// tiles its last token sees.  A token thus meets the same tiles in the same
+// order whatever block or chunk it is computed in (tiles it does not see are
+// all masked: they add exact zeros), so chunked and one-shot calls agree bit
+// for bit.  The per-head softmax is the one-token kernel's: running max from
+// the sink logit, running sum from 1, the O rescale only when a max rises by
+// more than 2^8.  The output goes through LDS so that HBM sees whole-row
+// stores.
+// ---------------------------------------------------------------------------
+constexpr int kDenseTB = 2;  // tokens per workgroup (two workgroups per CU)
+constexpr int kDenseHG = 2;  // 16-head groups per wave: two waves per token
+
+// Its tiles have a layout of their own: 32 rows of 256 bytes back to back, and
+// 16-byte granule g of row r at slot g ^ dense_key(r).  A K read touches one
+// granule of 16 rows, whose keys are distinct; a transposed V read touches two
+// adjacent granules of 8 rows, whose keys differ above bit 0: both read
+// patterns then cover distinct LDS banks.  The gather fetches, for slot s of
+// row r, global granule s ^ dense_key(r).
+CSA_DEV int dense_key(int r) { return ((r & 7) << 1) | ((r >> 4) & 1); }
+
+template <int C>
+__global__ __launch_bounds__(64 * kDenseTB * 4 / kDenseHG, 8 / (kDenseTB * 4 / kDenseHG)) void
+mqa_dense_tokblock_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ win,
+    const uint16_t* __restrict__ comp, const float* __restrict__ sink,
+    uint16_t* __restrict__ out, int64_t n, int m, int n_win, float scale, int qk_norm, float eps,
+    int r, float theta, int64_t n_entries, int64_t t0) {
+  static_assert(C == 128, "the tile layout is that of 256-byte rows");
+  constexpr int NH = 64, HG = kDenseHG;    // heads; 16-head groups per wave
+  constexpr int WPT = 4 / HG;              // waves per token
+  constexpr int NKG = C / 32, NCB = C / 16;
+  constexpr int OST = C * 2 + 16;          // staged output row stride (bytes)
+  constexpr int NBUF = 4, AHEAD = NBUF - 1;  // tile ring; gathers run 3 tiles ahead
+  constexpr int TROW = C * 2, TBYTES = kT * TROW;  // 256 B rows, 8 KiB tiles
+  constexpr int BPW = TBYTES / 1024 / 4;     // 1 KiB DMA bursts per gathering wave and tile
+  __shared__ __align__(16) uint8_t smem[NBUF * TBYTES];
+  __shared__ __align__(16) uint8_t ostage[kDenseTB][NH * OST];
+  __shared__ float2 rope_tab[kDenseTB][C / 2];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tw = wave / WPT, hw = wave % WPT;  // token of the block; head range 16 HG hw ..
+  const int h0 = 16 * HG * hw;
+  const int lc = lane & 15, lg = lane >> 4;
+  // XCD-aware order: die x takes a contiguous range of blocks, whose window
+  // rows and entries its L2 keeps
+  const int64_t nblk = (n + kDenseTB - 1) / kDenseTB;
+  const int64_t per = (nblk + 7) >> 3;
+  const int64_t blk = (int64_t)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (blk >= nblk) return;  // the whole workgroup
+  const int64_t tb = blk * kDenseTB, tl = min64(tb + kDenseTB - 1, n - 1);
+  const bool live = tb + tw < n;
+  const int64_t t = live ? tb + tw : tl;  // a wave past n repeats the last token, unstored
+  const int64_t pt = t0 + t, ptb = t0 + tb, ptl = t0 + tl;
+  const int64_t w0 = max64(t0 - n_win + 1, 0);           // position of win row 0
+  const int64_t wt0 = max64(ptb - n_win + 1, 0) / kT;    // first window tile
+  const int64_t nwr = (ptl / kT - wt0 + 1) * kT;         // window tile rows
+  const int64_t neu = min64((ptl + 1) / m, n_entries);   // entries of the last token
+  const int64_t pw0 = wt0 * kT;                          // position of window tile row 0
+  const int ntiles = (int)(nwr / kT + (neu + kT - 1) / kT);
+  // this token's candidates: window tile rows [wbeg, wend], entries < vis
+  const int64_t wbeg = max64(pt - n_win + 1, 0) - pw0, wend = pt - pw0;
+  const int64_t vis = min64((pt + 1) / m, n_entries);
+
+  uint4 qraw[HG][NKG];
+  {
+    const uint16_t* qt = q + t * (int64_t)NH * C + lg * 8;
+#pragma unroll
+    for (int hg = 0; hg < HG; ++hg)
+#pragma unroll
+      for (int g = 0; g < NKG; ++g)
+        qraw[hg][g] = *(const uint4*)(qt + (h0 + 16 * hg + lc) * C + g * 32);
+  }
+  float sink_h[HG];
+#pragma unroll
+  for (int hg = 0; hg < HG; ++hg) sink_h[hg] = sink[h0 + 16 * hg + lc];
+
+  auto issue_tile = [&](int ti, int buf) {
+    auto row_of = [&](int64_t j, bool& ok) -> const uint16_t* {
+      // rows no token of the block sees load a valid row
+      const uint16_t* dummy = win + (ptl - w0) * C;
+      if (j < nwr) {
+        const int64_t p = pw0 + j;
+        ok = p >= w0 && p <= ptl;
+        return ok ? win + (p - w0) * C : dummy;
+      }
+      ok = j - nwr < neu;
+      return ok ? comp + (j - nwr) * C : dummy;
+    };
+    // lane L < 8 resolves row 4 (wave + 4 (L / 4)) + L % 4; burst u of the
+    // wave (rows 4 (wave + 4u) .. + 3) takes its lanes' rows from lanes
+    // 4u + L / 16
+    const uint16_t* rp = win;
+    if (lane < 8) {
+      bool ok;
+      rp = row_of((int64_t)ti * kT + 4 * (wave + 4 * (lane >> 2)) + (lane & 3), ok);
+    }
+    const uint32_t lo_a = (uint32_t)(size_t)rp, hi_a = (uint32_t)((size_t)rp >> 32);
+#pragma unroll
+    for (int u = 0; u < BPW; ++u) {
+      const int src = 4 * u + (lane >> 4);
+      const uint32_t lo = (uint32_t)__shfl((int)lo_a, src, 64);
+      const uint32_t hi = (uint32_t)__shfl((int)hi_a, src, 64);
+      const int rr = 4 * (wave + 4 * u) + (lane >> 4);
+      const uint8_t* g =
+          (const uint8_t*)(size_t)(((uint64_t)hi << 32) | lo) + ((lane & 15) ^ dense_key(rr)) * 16;
+      lds_dma16(g, smem + buf * TBYTES + (wave + 4 * u) * 1024);
+    }
+  };
+  // the gather: the first four waves (eight 1 KiB bursts of a tile)
+  if (wave < 4) issue_tile(0, 0);  // eight 1 KiB bursts per tile
+  if (hw == 0)
+    for (int p = lane; p < r / 2; p += 64) {
+      float cs, sn;
+      rope_cs(pt, p, r, theta, &cs, &sn);
+      rope_tab[tw][p] = make_float2(cs, sn);
+    }
+  __syncthreads();  // rope_tab is visible
+
+  bf16x8_t qf[HG][NKG];
+#pragma unroll
+  for (int hg = 0; hg < HG; ++hg)
+    q_prologue<C>(qraw[hg], qf[hg], rope_tab[tw], qk_norm, eps, r, lg);
+  constexpr float LOG2E = 1.4426950408889634f;
+  const float sl2 = scale * LOG2E;
+  float run_m[HG], run_l[HG];
+  f32x4_t o[HG][NCB];
+#pragma unroll
+  for (int hg = 0; hg < HG; ++hg) {
+    run_m[hg] = sink_h[hg] * LOG2E;  // the sink enters the sum once, as 1
+    run_l[hg] = 1.f;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) o[hg][cb] = f32x4_t{};
+  }
+  // the next gathers only now: the compiler's waits for q and the sink count
+  // its own loads only, and would drain gathers issued before them
+#pragma unroll
+  for (int a = 1; a < AHEAD; ++a)
+    if (wave < 4 && a < ntiles) issue_tile(a, a);
+  // fragment addresses: K rows pi(lc >> 2, b, lc & 3), granule 4 g + lg;
+  // transposed-read rows pi(lg, h, lc >> 2), granule 2 cb + (lc & 3) / 2,
+  // half lc & 1
+  int kofs[2][NKG], tofs[2][NCB];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int rk = slot_pi(lc >> 2, b, lc & 3), rt = slot_pi(lg, b, lc >> 2);
+#pragma unroll
+    for (int g = 0; g < NKG; ++g) kofs[b][g] = rk * TROW + (((4 * g + lg) ^ dense_key(rk)) << 4);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+      tofs[b][cb] = rt * TROW + (((2 * cb + ((lc & 3) >> 1)) ^ dense_key(rt)) << 4) + 8 * (lc & 1);
+  }
+  int slot[8];  // tile rows pi(lg, b, i) of this lane's logits z[4b + i]
+#pragma unroll
+  for (int e = 0; e < 8; ++e) slot[e] = slot_pi(lg, e >> 2, e & 3);
+  // tile 0 has landed once at most the later prologue gathers are in flight
+  if (min(AHEAD - 1, ntiles - 1) >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * BPW));
+  else if (min(AHEAD - 1, ntiles - 1) == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(BPW));
+  else wait_vmem();
+  __syncthreads();
+  for (int ti = 0; ti < ntiles; ++ti) {
+    const int buf = ti % NBUF;  // buffer (ti + AHEAD) % NBUF held tile ti - 1
+    if (wave < 4 && ti + AHEAD < ntiles) issue_tile(ti + AHEAD, (ti + AHEAD) % NBUF);
+    const uint8_t* kv = smem + buf * TBYTES;
+    // S^T = K Q^T for the wave's head groups; each K fragment read once
+    f32x4_t sc[HG][2];
+#pragma unroll
+    for (int hg = 0; hg < HG; ++hg) sc[hg][0] = sc[hg][1] = f32x4_t{};
+#pragma unroll
+    for (int g = 0; g < NKG; ++g) {
+      const bf16x8_t a0 = *(const bf16x8_t*)(kv + kofs[0][g]);
+      const bf16x8_t a1 = *(const bf16x8_t*)(kv + kofs[1][g]);
+#pragma unroll
+      for (int hg = 0; hg < HG; ++hg) {
+        sc[hg][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[hg][g], sc[hg][0], 0, 0, 0);
+        sc[hg][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[hg][g], sc[hg][1], 0, 0, 0);
+      }
+    }
+    // this token's rows of the tile: [lo, hi] (wave-uniform); a tile it
+    // sees whole needs no mask
+    const int64_t j0 = (int64_t)ti * kT;
+    const int64_t lo64 = j0 < nwr ? wbeg - j0 : 0;
+    const int64_t hi64 = j0 < nwr ? wend - j0 : vis - (j0 - nwr) - 1;
+    const int lo = (int)max64(min64(lo64, kT), 0), hi = (int)max64(min64(hi64, kT - 1), -1);
+    const bool whole = lo == 0 && hi == kT - 1, none = hi < lo;
+    // a bias per row of this lane: 0 where the token sees it, else -inf
+    float bias[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      bias[e] = whole || (!none && (unsigned)(slot[e] - lo) <= (unsigned)(hi - lo)) ? 0.f
+                                                                                  : -INFINITY;
+    bf16x8_t pb[HG];
+#pragma unroll
+    for (int hg = 0; hg < HG; ++hg) {
+      float z[8];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        z[e] = fmaf(sc[hg][e >> 2][e & 3], sl2, bias[e]);
+        mx = fmaxf(mx, z[e]);
+      }
+      mx = xlane_max(mx);
+      if (__any(mx > run_m[hg] + 8.f)) {  // wave-uniform rescale of this group's O
+        const float nm = fmaxf(run_m[hg], mx);
+        const float alpha = __builtin_amdgcn_exp2f(run_m[hg] - nm);
+        run_l[hg] *= alpha;
+        run_m[hg] = nm;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[hg][cb][i] *= alpha;
+      }
+      f32x8_t p;
+      float ps = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = __builtin_amdgcn_exp2f(z[e] - run_m[hg]);
+        ps += p[e];
+      }
+      run_l[hg] += xlane_sum(ps);
+      pb[hg] = __builtin_convertvector(p, bf16x8_t);
+    }
+    // O^T += V^T P^T; each V^T fragment (transpose read) feeds every group
+    bf16x8_t vt[NCB];  // every V^T fragment of the tile, read before the products
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const bf16x4_t x0 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((CSA_LDS bf16x4_t*)(kv + tofs[0][cb]));
+      const bf16x4_t x1 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((CSA_LDS bf16x4_t*)(kv + tofs[1][cb]));
+      vt[cb] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const bf16x8_t a = vt[cb];
+#pragma unroll
+      for (int hg = 0; hg < HG; ++hg)
+        o[hg][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[hg], o[hg][cb], 0, 0, 0);
+    }
+    // tile ti+1 must have landed; the gathers of ti+2 .. ti+AHEAD may run
+    const int later = min(ntiles - 1, ti + AHEAD) - (ti + 1);
+    if (later >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * BPW));
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(BPW));
+    else wait_vmem();
+    __syncthreads();
+  }
+
+  // epilogue: o[hg][cb][i] = O[16 hg + lc][16 cb + 4 lg + i]; normalise,
+  // rotate back by -t, stage this token's [64][C] rows, store them whole
+  uint8_t* st = ostage[tw];
+#pragma unroll
+  for (int hg = 0; hg < HG; ++hg) {
+    const float inv = 1.f / run_l[hg];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = o[hg][cb][i] * inv;
+      const int ch0 = cb * 16 + 4 * lg;
+      if (r > 0 && ch0 >= C - r) {
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          const float2 cs = rope_tab[tw][(ch0 + i - (C - r)) >> 1];
+          const float x0 = v[i], x1 = v[i + 1];
+          v[i] = x0 * cs.x + x1 * cs.y;  // rotate by -t
+          v[i + 1] = -x0 * cs.y + x1 * cs.x;
+        }
+      }
+      const uint32_t u0 = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+      const uint32_t u1 = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+      *(uint2*)(st + (h0 + 16 * hg + lc) * OST + ch0 * 2) = make_uint2(u0, u1);
+    }
+  }
+  __syncthreads();
+  if (live) {
+    uint16_t* orow = out + t * (int64_t)NH * C;
+    constexpr int CH = C / 8;  // 16-byte chunks per head row; this wave's heads
+#pragma unroll 4
+    for (int ci = h0 * CH + lane; ci < (h0 + 16 * HG) * CH; ci += 64) {
+      const int h = ci / CH, cc = ci % CH;
+      *(uint4*)(orow + (int64_t)h * C + cc * 8) = *(const uint4*)(st + h * OST + cc * 16);
+    }
+  }
+}
+
 hipError_t launch_mqa_prefill_bf16(const csa_attn_desc& d, int mode, const void* q, const void* win,
                                    const void* comp, const int32_t* idx, const float* sink,
                                    void* out, hipStream_t st) {
+  if (mode != ATTN_SPARSE && d.c == 128 && d.n_heads == 64) {  // HCA's shape
+    const int64_t nblk = (d.n + kDenseTB - 1) / kDenseTB;
+    mqa_dense_tokblock_kernel<128><<<(unsigned)(((nblk + 7) / 8) * 8), 64 * kDenseTB * 4 / kDenseHG, 0,
+                                     st>>>(
+        (const uint16_t*)q, (const uint16_t*)win, (const uint16_t*)comp, sink, (uint16_t*)out,
+        d.n, d.m, d.n_win, d.scale, d.qk_norm, d.eps, d.rope_dims, d.rope_theta, d.n_entries,
+        d.t0);
+    return hipGetLastError();
+  }
   const unsigned grid = (unsigned)(((d.n + 7) / 8) * 8);
 #define CSA_FAST(CC)                                                                          \
   if (d.c == CC) {                                                                           \
