@@ -20,9 +20,13 @@ when the kernel source no longer matches the one the counters were taken on.
 workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode]
-                       [--no-cpu-baseline] [--pmc-probe]
-  --pmc-probe: run only a 1 GiB device copy (the counter scale reference)
-               and the sparse MQA prefill, for rocprofv3 --pmc passes.
+                       [--no-cpu-baseline] [--pmc-probe [mqa|hca|decode]]
+                       [--oracle-times]
+  --pmc-probe: run only a 1 GiB device copy (the counter scale reference) and
+               one workload's kernels (the 64K sparse MQA prefill by default,
+               the 16K HCA prefill step, or decode step replays), for
+               rocprofv3 --pmc passes.
+  --oracle-times: time the CPU oracle on whole workloads (no GPU).
 """
 import hashlib
 import argparse
@@ -324,9 +328,12 @@ def measured_traffic():
         return None
 
 
-def pmc_probe():
+def pmc_probe(target="mqa"):
     """One 1 GiB device-to-device copy (counter scale reference), then the
-    sparse MQA prefill of the 64K workload twice."""
+    kernels of `target` for counter passes: "mqa" the sparse MQA prefill of
+    the 64K workload twice; "hca" the 16K HCA prefill step (compressor and
+    dense MQA) twice; "decode" four graph replays of each decode workload's
+    step (both after a clean cache flush)."""
     dev = "cuda"
     src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
@@ -334,14 +341,32 @@ def pmc_probe():
     dst.copy_(src)
     torch.cuda.synchronize()
     del src, dst
-    pf = CsaPrefill(configs.get("csa_prefill_64k_bf16"), dev)
-    pf.compress()
-    pf.index()
+    if target == "mqa":
+        pf = CsaPrefill(configs.get("csa_prefill_64k_bf16"), dev)
+        pf.compress()
+        pf.index()
+        torch.cuda.synchronize()
+        for _ in range(2):
+            pf.attend()
+    elif target == "hca":
+        hp = HcaPrefill(configs.get("hca_prefill_16k_bf16"), dev)
+        for _ in range(2):
+            hp.step()
+    elif target == "decode":
+        cf = CacheFlush(dev)
+        for wname in ("decode_b32_128k_bf16", "decode_b4_1m_bf16"):
+            hd = HybridDecode(configs.get(wname), dev)
+            g = graph_of(hd.step)
+            for _ in range(4):
+                cf.clean()
+                g.replay()
+            torch.cuda.synchronize()
+            del g, hd
+            torch.cuda.empty_cache()
+    else:
+        raise SystemExit(f"unknown probe target {target}")
     torch.cuda.synchronize()
-    for _ in range(2):
-        pf.attend()
-    torch.cuda.synchronize()
-    print("[bench] pmc probe done: 1 GiB copy, 2 x sparse MQA prefill", flush=True)
+    print(f"[bench] pmc probe done: 1 GiB copy, then {target}", flush=True)
 
 
 # --------------------------------------------------------------------------
@@ -872,8 +897,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pmc-probe", action="store_true",
-                    help="only the copy reference and the MQA prefill, for counter passes")
+    ap.add_argument("--pmc-probe", nargs="?", const="mqa", default=None,
+                    choices=("mqa", "hca", "decode"),
+                    help="only the copy reference and the kernels of one workload, for "
+                         "counter passes")
     ap.add_argument("--oracle-times", action="store_true",
                     help="only time the CPU oracle on whole workloads (no GPU) and print that")
     a = ap.parse_args()
@@ -886,7 +913,7 @@ def main():
         sys.exit(2)
     L.load()
     if a.pmc_probe:
-        pmc_probe()
+        pmc_probe(a.pmc_probe)
         return
     dev = "cuda"
     cfg = configs.get("csa_prefill_64k_bf16")
