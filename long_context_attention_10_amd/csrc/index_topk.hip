@@ -1029,11 +1029,84 @@ CSA_DEV int common_prefix(uint32_t kmax, uint32_t kmin, uint64_t* prefix) {
   return 32 + hb;
 }
 
+constexpr int kSelThreads = 1024;  // one selection workgroup per sequence
+
+// Block-wide helpers for a workgroup of NT threads (NT / 64 waves): the
+// selection runs wider than the scorer, whose helpers above assume four.
+template <int NT>
+CSA_DEV int block_excl_scan_n(int v, int* tmp, int* total) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  __syncthreads();
+  if (lane == 63) tmp[wave] = x;
+  __syncthreads();
+  int base = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    base += w < wave ? tmp[w] : 0;
+    all += tmp[w];
+  }
+  *total = all;
+  return base + x - v;
+}
+template <int NT, bool MAX>
+CSA_DEV uint32_t block_ext_u32(uint32_t v, int* sh) {
+  constexpr int NW = NT / 64;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint32_t y = (uint32_t)__shfl_xor((int)v, o, 64);
+    v = MAX ? max(v, y) : min(v, y);
+  }
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = (int)v;
+  __syncthreads();
+  uint32_t r = (uint32_t)sh[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) r = MAX ? max(r, (uint32_t)sh[w]) : min(r, (uint32_t)sh[w]);
+  __syncthreads();  // sh is reused by the next call
+  return r;
+}
+// radix_select64 for NT threads (hist: 256 ints of LDS).
+template <int NT, class GET>
+CSA_DEV uint64_t radix_select64_n(GET get, int64_t n, int need, int hi, uint64_t prefix,
+                                  int* hist, int* res) {
+  const int tid = threadIdx.x;
+  uint64_t pmask = hi >= 63 ? 0ull : ~((2ull << hi) - 1ull);
+  while (hi >= 0) {
+    const int lo = hi >= 7 ? hi - 7 : 0;
+    const uint32_t dm = (2u << (hi - lo)) - 1u;
+    for (int i = tid; i < 256; i += NT) hist[i] = 0;
+    __syncthreads();
+    for (int64_t i = tid; i < n; i += NT) {
+      const uint64_t ck = get(i);
+      if ((ck & pmask) == prefix) atomicAdd(&hist[(uint32_t)(ck >> lo) & dm], 1);
+    }
+    __syncthreads();
+    find_digit(hist, need, res);
+    __syncthreads();
+    const int d = res[0];
+    need -= res[1];
+    prefix |= (uint64_t)d << lo;
+    pmask |= (uint64_t)dm << lo;
+    const bool whole = hist[d] == need;  // uniform: LDS values after the barrier
+    __syncthreads();
+    if (whole) break;
+    hi = lo - 1;
+  }
+  return prefix;
+}
+
 // D2: one workgroup per sequence (see the section comment).  FOLD: the
 // entry emitted by position t's own step (when (t + 1) % m == 0) was left
 // out of D1; it is scored here and joins the candidates.
-template <class TS, int HI, int CI, bool FOLD>
-__global__ __launch_bounds__(256) void dec_select_kernel(
+template <class TS, int HI, int CI, bool FOLD, int NT>
+__global__ __launch_bounds__(NT) void dec_select_kernel(
     const int64_t* __restrict__ posv, int64_t n_entries, int m, int k,
     const float* __restrict__ scores, const uint2* __restrict__ cand,
     const uint4* __restrict__ cmeta, int64_t nchunks, int L, const typename TS::S* __restrict__ qI,
@@ -1042,7 +1115,7 @@ __global__ __launch_bounds__(256) void dec_select_kernel(
   __shared__ uint2 cl[kCandLds];
   __shared__ int coff[kCandLds];  // per chunk: its first slot in cl, or -1 past its count
   __shared__ int hist[256];
-  __shared__ int sh[8];
+  __shared__ int sh[NT / 64];
   __shared__ int res[2];
   __shared__ float snew;
   const int b = blockIdx.x;
@@ -1051,7 +1124,7 @@ __global__ __launch_bounds__(256) void dec_select_kernel(
   const int64_t vis = min64((tpos + 1) / m, n_entries);
   int32_t* orow = idx_out + (int64_t)b * k;
   if (vis <= k) {
-    for (int j = tid; j < k; j += 256) orow[j] = j < vis ? j : -1;
+    for (int j = tid; j < k; j += NT) orow[j] = j < vis ? j : -1;
     return;
   }
   const int64_t e_new = (FOLD && (tpos + 1) % m == 0 && (tpos + 1) / m <= n_entries) ? vis - 1 : -1;
@@ -1060,7 +1133,7 @@ __global__ __launch_bounds__(256) void dec_select_kernel(
   const float* sc = scores + (int64_t)b * n_entries;
   // chunk counts: thread j sums a contiguous run of chunks, one prefix sum
   // places the runs in chunk (= index) order
-  const int CPT = (nch + 255) / 256;
+  const int CPT = (nch + NT - 1) / NT;
   const int ch0 = min(tid * CPT, nch), ch1 = min(ch0 + CPT, nch);
   const uint4* meta = cmeta + (int64_t)b * nchunks;
   int my = 0;
@@ -1074,7 +1147,7 @@ __global__ __launch_bounds__(256) void dec_select_kernel(
     }
   }
   int tot;
-  int off = block_excl_scan(my, sh, &tot);  // its barriers also publish snew
+  int off = block_excl_scan_n<NT>(my, sh, &tot);  // its barriers also publish snew
   const int ntot = tot + (e_new >= 0);
   const uint32_t new_key = e_new >= 0 ? float_key(snew) : 0u;
   bool fallback = ntot > kCandLds || ntot < k;  // (fewer than k: not reached, see L)
@@ -1089,12 +1162,12 @@ __global__ __launch_bounds__(256) void dec_select_kernel(
     __syncthreads();
     const uint2* cb = cand + (int64_t)b * nchunks * L;
     const int nslot = nch * L;
-    for (int p0 = tid; p0 < nslot; p0 += 256 * 8) {
+    for (int p0 = tid; p0 < nslot; p0 += NT * 8) {
       uint2 v[8];
       int dst[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int p = p0 + 256 * u;
+        const int p = p0 + NT * u;
         dst[u] = -1;
         if (p < nslot) {
           const int c = p / L, i = p - c * L;
@@ -1112,14 +1185,15 @@ __global__ __launch_bounds__(256) void dec_select_kernel(
     if (e_new >= 0 && tid == 0) cl[tot] = make_uint2(new_key, (uint32_t)e_new);
     __syncthreads();
     uint32_t kmax = 0, kmin = 0xffffffffu;
-    for (int i = tid; i < ntot; i += 256) {
+    for (int i = tid; i < ntot; i += NT) {
       kmax = max(kmax, cl[i].x);
       kmin = min(kmin, cl[i].x);
     }
     uint64_t pre;
-    const int hi = common_prefix(block_max_u32(kmax, sh), block_min_u32(kmin, sh), &pre);
-    thr = radix_select64([&](int64_t i) { return composite(cl[i].x, cl[i].y); }, ntot, k, hi, pre,
-                         hist, res);
+    const uint32_t bmax = block_ext_u32<NT, true>(kmax, sh);
+    const int hi = common_prefix(bmax, block_ext_u32<NT, false>(kmin, sh), &pre);
+    thr = radix_select64_n<NT>([&](int64_t i) { return composite(cl[i].x, cl[i].y); }, ntot, k, hi,
+                               pre, hist, res);
     // a chunk that kept L entries whose L-th best beats thr may hide winners
     for (int c = ch0; c < ch1; ++c) {
       const uint4 mt = meta[c];
@@ -1129,11 +1203,11 @@ __global__ __launch_bounds__(256) void dec_select_kernel(
   fallback = __syncthreads_or(fallback || full_any);
   if (!fallback) {
     // winners in list (= index) order: contiguous runs, one prefix sum
-    const int TPT = (ntot + 255) / 256;
+    const int TPT = (ntot + NT - 1) / NT;
     const int i0 = min(tid * TPT, ntot), i1 = min(i0 + TPT, ntot);
     int cnt = 0;
     for (int i = i0; i < i1; ++i) cnt += composite(cl[i].x, cl[i].y) >= thr;
-    int o = block_excl_scan(cnt, sh, &tot);
+    int o = block_excl_scan_n<NT>(cnt, sh, &tot);
     for (int i = i0; i < i1; ++i)
       if (composite(cl[i].x, cl[i].y) >= thr) orow[o++] = (int32_t)cl[i].y;
     return;
@@ -1143,18 +1217,19 @@ __global__ __launch_bounds__(256) void dec_select_kernel(
   auto row_key = [&](int64_t i) { return i == e_new ? new_key : float_key(sc[i]); };
   {
     uint32_t kmax = 0, kmin = 0xffffffffu;
-    for (int64_t i = tid; i < vis; i += 256) {
+    for (int64_t i = tid; i < vis; i += NT) {
       const uint32_t kk = row_key(i);
       kmax = max(kmax, kk);
       kmin = min(kmin, kk);
     }
     uint64_t pre;
-    const int hi = common_prefix(block_max_u32(kmax, sh), block_min_u32(kmin, sh), &pre);
-    thr = radix_select64([&](int64_t i) { return composite(row_key(i), (uint32_t)i); }, vis, k,
-                         hi, pre, hist, res);
+    const uint32_t bmax = block_ext_u32<NT, true>(kmax, sh);
+    const int hi = common_prefix(bmax, block_ext_u32<NT, false>(kmin, sh), &pre);
+    thr = radix_select64_n<NT>([&](int64_t i) { return composite(row_key(i), (uint32_t)i); }, vis,
+                               k, hi, pre, hist, res);
   }
   int base = 0;
-  for (int64_t t0 = 0; t0 < vis; t0 += 1024) {
+  for (int64_t t0 = 0; t0 < vis; t0 += 4 * NT) {
     int cnt = 0;
     bool win[4];
 #pragma unroll
@@ -1164,7 +1239,7 @@ __global__ __launch_bounds__(256) void dec_select_kernel(
       win[u] = i < vis && composite(kk, (uint32_t)i) >= thr;
       cnt += win[u];
     }
-    int o = block_excl_scan(cnt, sh, &tot);
+    int o = block_excl_scan_n<NT>(cnt, sh, &tot);
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       if (win[u]) orow[base + o++] = (int32_t)(t0 + 4 * tid + u);
@@ -1264,7 +1339,7 @@ static hipError_t dec_select(const csa_index_desc& d, const DecWs& w, int64_t nc
                              const int64_t* pos, int32_t* idx_out, const void* qI,
                              const void* wI, const void* KI, EntryMap em, hipStream_t st) {
   typedef typename T::S S;
-  dec_select_kernel<T, HI, CI, FOLD><<<d.batch, 256, 0, st>>>(
+  dec_select_kernel<T, HI, CI, FOLD, kSelThreads><<<d.batch, kSelThreads, 0, st>>>(
       pos, d.n_entries, d.m, d.k, w.scores, w.cand, w.cmeta, nch, L, (const S*)qI, (const S*)wI,
       (const S*)KI, em, idx_out);
   return hipGetLastError();
