@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 9
+#define CSA_ABI_VERSION 10
 
 typedef enum csa_status {
   CSA_OK = 0,
@@ -338,7 +338,10 @@ int csa_indexer_fp4_quant_decode(const csa_fp4_desc* desc, const void* cache, in
  *
  *   qI_codes [B, hI, cI/2], qI_exps [B, hI, cI/32]
  *   K_codes  [B, n_entries, cI/2], K_exps [B, n_entries, cI/32]
- *   wI [B, hI], pos [B], idx_out [B, k] as in csa_index_topk_decode */
+ *   wI [B, hI], pos [B], idx_out [B, k] as in csa_index_topk_decode
+ * qI_codes and K_codes start on a 16-byte boundary (else
+ * CSA_ERR_INVALID_ARG, checked after the workspace): the scorer loads 16
+ * code bytes at a time. */
 int csa_index_topk_decode_fp4(const csa_index_desc* desc, const uint8_t* qI_codes,
                               const uint8_t* qI_exps, const void* wI, const uint8_t* K_codes,
                               const uint8_t* K_exps, const int64_t* pos, int32_t* idx_out,

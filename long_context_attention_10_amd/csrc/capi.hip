@@ -501,6 +501,12 @@ int csa_indexer_fp4_quant_decode_paged(const csa_fp4_desc* d, const void* cache_
                                             em));
 }
 
+// The FP4 scorer reads 16 code bytes per lane: both code arrays start on a
+// 16-byte boundary (rows are 16-byte multiples, so every row does).
+static bool codes_aligned(const uint8_t* q, const uint8_t* k) {
+  return (((uintptr_t)q | (uintptr_t)k) & 15u) == 0;
+}
+
 int csa_index_topk_decode_fp4_paged(const csa_index_desc* d, const uint8_t* qI_codes,
                                     const uint8_t* qI_exps, const void* wI,
                                     const uint8_t* K_codes_pool, const uint8_t* K_exps_pool,
@@ -516,6 +522,7 @@ int csa_index_topk_decode_fp4_paged(const csa_index_desc* d, const uint8_t* qI_c
   if (!qI_codes || !qI_exps || !wI || !K_codes_pool || !K_exps_pool || !pos || !idx_out)
     return CSA_ERR_INVALID_ARG;
   if (!ws || ws_bytes < index_decode_ws_bytes(*d)) return CSA_ERR_WORKSPACE;
+  if (!codes_aligned(qI_codes, K_codes_pool)) return CSA_ERR_INVALID_ARG;
   return hip_status(launch_index_topk_decode_fp4(*d, qI_codes, qI_exps, wI, K_codes_pool,
                                                  K_exps_pool, pos, idx_out, ws,
                                                  (hipStream_t)stream, em));
@@ -531,6 +538,7 @@ int csa_index_topk_decode_fp4(const csa_index_desc* d, const uint8_t* qI_codes,
   if (!qI_codes || !qI_exps || !wI || !K_codes || !K_exps || !pos || !idx_out)
     return CSA_ERR_INVALID_ARG;
   if (!ws || ws_bytes < index_decode_ws_bytes(*d)) return CSA_ERR_WORKSPACE;
+  if (!codes_aligned(qI_codes, K_codes)) return CSA_ERR_INVALID_ARG;
   return hip_status(launch_index_topk_decode_fp4(*d, qI_codes, qI_exps, wI, K_codes, K_exps, pos,
                                                  idx_out, ws, (hipStream_t)stream));
 }

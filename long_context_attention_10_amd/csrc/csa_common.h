@@ -99,6 +99,19 @@ template <> CSA_DEV void mma32<F32>(f32x16_t& acc, const uint4& a, const uint4& 
   acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
 }
 
+// 32x32 output block of the scaled matrix instruction with E2M1 (FP4) A and
+// B.  Lane l supplies A row (l % 32) and B column (l % 32): 32 consecutive
+// values of the 64-wide k-group, [32*(l/32), 32*(l/32) + 32), as 16 bytes
+// (value 2i in the low nibble of byte i, 2i + 1 in the high one), and that
+// block's power-of-two scale as the biased exponent e + 127 in byte 0 of sa /
+// sb (each lane scales its own 32 values).  acc layout as mma32.
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
+CSA_DEV void mma32_fp4(f32x16_t& acc, const uint4& a, uint32_t sa, const uint4& b, uint32_t sb) {
+  const i32x8_t av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  const i32x8_t bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 4, 4, 0, (int)sa, 0, (int)sb);
+}
+
 // ---------------------------------------------------------------- RoPE
 // cos/sin of pos * theta^(-2p/r) for pair p.  The angle is formed and reduced
 // modulo 2*pi in fp64 so that positions up to 2^20 and beyond keep fp32

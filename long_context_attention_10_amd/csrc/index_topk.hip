@@ -842,36 +842,35 @@ __global__ __launch_bounds__(256) void fp4_rotate_quant_kernel(const typename T:
   }
 }
 
-// 8 consecutive E2M1 values (4 code bytes) with the block scale 2^(eb - 127)
-// as one bf16 matrix-core fragment.
-CSA_DEV uint4 fp4x8_to_bf16(uint32_t cw, uint32_t eb) {
-  const float sc = __uint_as_float(eb << 23);  // 2^(eb - 127)
-  uint4 r;
-  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 0));
-  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 1));
-  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 2));
-  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 3));
-  return r;
-}
-
-// D1 over FP4 keys: dec_score_kernel with q^I and the keys read as E2M1 codes
-// and block exponents (a quarter of the bf16 bytes) and widened to bf16
-// fragments in registers; the products, head sum and histogram are the same.
+// D1 over FP4 keys: q^I and the keys stay E2M1 codes and block exponents
+// (a quarter of the bf16 bytes) and go straight into the scaled FP4 matrix
+// instruction, one per 64 channels for 32 keys: A = q^I (row = head, rows
+// past HI zero), B = 32 keys (column = key); lane l loads 16 code bytes and
+// the scale byte of channel block (l / 32) of its key (l % 32).  Each product
+// of two E2M1 values is exact and a block's 32 of them sum exactly, so a
+// score differs from the dequantised dot product only by the fp32 rounding
+// of the block sums' accumulation.  Head sum and histogram as dec_score_kernel.
 template <int HI, int CI, bool PAGED>
 __global__ __launch_bounds__(256) void dec_score_fp4_kernel(
     const uint8_t* __restrict__ qc, const uint8_t* __restrict__ qe, const uint16_t* __restrict__ wI,
     const uint8_t* __restrict__ kc, const uint8_t* __restrict__ ke,
     const int64_t* __restrict__ posv, int64_t n_entries, int m, int k, float* __restrict__ scores,
     uint2* __restrict__ cand, uint4* __restrict__ cmeta, int L, int64_t nch, EntryMap em) {
-  constexpr int NG = CI / 32;  // 32-value k-groups (= scale blocks) per row
+  constexpr int NG = CI / 32;  // 32-value scale blocks per row
+  constexpr int NH = CI / 64;  // 64-channel k-groups per row: one instruction each
   constexpr int RB = CI / 2;   // code bytes per row
+  constexpr int KW = kDecChunk / 4;  // keys per wave
+  constexpr int NU = KW / 32;        // 32-key groups per wave
+  constexpr int NQ = HI > 8 ? 8 : 4; // accumulators that hold heads < HI
+  static_assert(HI <= 16, "heads 16..31 of the 32-row block are not summed");
   __shared__ uint32_t ls[kDecChunk];
   __shared__ int hist[256];
   __shared__ int sh[8];
   __shared__ int res[2];
   __shared__ int64_t srow[PAGED ? kDecChunk : 1];  // pool rows (as in dec_score_kernel)
   const int b = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lg = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, kg = lane >> 5;
   const int64_t c0 = (int64_t)blockIdx.x * kDecChunk;
   constexpr int NS = kDecChunk / 256;
   int32_t tslot[PAGED ? NS : 1];
@@ -895,64 +894,59 @@ __global__ __launch_bounds__(256) void dec_score_fp4_kernel(
     }
   }
 
-  uint4 qa[NG];
-  float wv[4];
-  const int hrow = lane & 15;
+  // q^I rows as the A operand; a row past HI is zero with scale 1 (a finite
+  // scale keeps its products zero)
+  uint4 qa[NH];
+  uint32_t qs[NH];
 #pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    const int64_t row = (int64_t)b * HI + hrow;
-    qa[g] = hrow < HI ? fp4x8_to_bf16(*(const uint32_t*)(qc + row * RB + g * 16 + lg * 4),
-                                      qe[row * NG + g])
-                      : make_uint4(0, 0, 0, 0);
+  for (int h = 0; h < NH; ++h) {
+    const int64_t row = (int64_t)b * HI + col;
+    const int blk = 2 * h + kg;
+    qa[h] = col < HI ? *(const uint4*)(qc + row * RB + blk * 16) : make_uint4(0, 0, 0, 0);
+    qs[h] = col < HI ? (uint32_t)qe[row * NG + blk] : 127u;
   }
+  // weights of the heads in this lane's accumulators: acc[4j+i] is head 8j + 4*kg + i
+  float wv[NQ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int h = 4 * lg + i;
-    wv[i] = h < HI ? BF16::ld(wI, (int64_t)b * HI + h) : 0.f;
+  for (int q = 0; q < NQ; ++q) {
+    const int h = 8 * (q / 4) + 4 * kg + (q % 4);
+    wv[q] = h < HI ? BF16::ld(wI, (int64_t)b * HI + h) : 0.f;
   }
   __syncthreads();
   const int64_t rb0 = PAGED ? 0 : (int64_t)b * n_entries;  // row of entry 0 (contiguous)
-  const int64_t w0 = c0 + (int64_t)wave * (kDecChunk / 4);
-  const int64_t w1 = min64(w0 + kDecChunk / 4, c1);
-  // 64 keys per step: each lane loads 4 code bytes and the scale byte per
-  // k-group for its 4 keys (16 keys per MFMA, 4 MFMA steps)
-  auto load64 = [&](int64_t s0, uint32_t (&dc)[4][NG], uint32_t (&de)[4][NG]) {
+  const int64_t w0 = c0 + (int64_t)wave * KW;
+  const int64_t w1 = min64(w0 + KW, c1);
+  if (w0 < w1) {
+    // every load of the wave in flight at once; a key past c1 re-reads row
+    // c1 - 1 and is not stored
+    uint4 kw[NU][NH];
+    uint32_t ks[NU][NH];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t s = min64(s0 + u * 16 + (lane & 15), c1 - 1);  // past c1: not stored
+    for (int u = 0; u < NU; ++u) {
+      const int64_t s = min64(w0 + u * 32 + col, c1 - 1);
       const int64_t row = PAGED ? srow[s - c0] : rb0 + s;
 #pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        dc[u][g] = *(const uint32_t*)(kc + row * RB + g * 16 + lg * 4);
-        de[u][g] = ke[row * NG + g];
+      for (int h = 0; h < NH; ++h) {
+        kw[u][h] = *(const uint4*)(kc + row * RB + (2 * h + kg) * 16);
+        ks[u][h] = ke[row * NG + 2 * h + kg];
       }
     }
-  };
-  auto score64 = [&](int64_t s0, const uint32_t (&dc)[4][NG], const uint32_t (&de)[4][NG]) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      f32x4_t acc = f32x4_t{};
+    for (int u = 0; u < NU; ++u) {
+      if (w0 + u * 32 >= w1) break;  // uniform
+      f32x16_t acc = f32x16_t{};
 #pragma unroll
-      for (int g = 0; g < NG; ++g) mma16<BF16>(acc, qa[g], fp4x8_to_bf16(dc[u][g], de[u][g]));
+      for (int h = 0; h < NH; ++h) mma32_fp4(acc, qa[h], qs[h], kw[u][h], ks[u][h]);
       float p = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p += wv[i] * relu(acc[i]);
-      p = xlane_sum(p);
-      const int64_t s = s0 + u * 16 + (lane & 15);
-      if (lg == 0 && s < w1) {
+      for (int q = 0; q < NQ; ++q) p += wv[q] * relu(acc[q]);
+      p += __shfl_xor(p, 32, 64);  // the other half of the heads
+      const int64_t s = w0 + u * 32 + col;
+      if (kg == 0 && s < w1) {
         scores[(int64_t)b * n_entries + s] = p;
         ls[s - c0] = float_key(p);
       }
     }
-  };
-  uint32_t ka[4][NG], kae[4][NG], kb[4][NG], kbe[4][NG];
-  if (w0 < w1) load64(w0, ka, kae);
-  for (int64_t s0 = w0; s0 < w1; s0 += 128) {
-    if (s0 + 64 < w1) load64(s0 + 64, kb, kbe);
-    score64(s0, ka, kae);
-    if (s0 + 64 >= w1) break;
-    if (s0 + 128 < w1) load64(s0 + 128, ka, kae);
-    score64(s0 + 64, kb, kbe);
   }
   __syncthreads();
   const int64_t slot = (int64_t)b * nch + blockIdx.x;

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.csa_abi_version() == 9
+    assert lib.csa_abi_version() == 10
     for code in (0, -1, -2, -3, -4):
         assert len(lib.csa_status_string(code)) > 0
     assert lib.csa_status_string(-99) == b"unknown status"
@@ -242,6 +242,13 @@ def test_fp4_calls_reject(lib):
     dec = L.IndexDesc(0, 2, 16, 64, 4, 512, L.CSA_BF16, 1024)
     assert lib.csa_index_topk_decode_fp4(ctypes.byref(dec), *([_p()] * 7), None, 0, None) == -3
     assert lib.csa_index_topk_decode_fp4(ctypes.byref(dec), None, *([_p()] * 7), 1 << 40, None) == -1
+    # code arrays off a 16-byte boundary (the other pointers aligned, the
+    # workspace large enough): rejected before anything is enqueued
+    a = [_p(4096)] * 8
+    for i in (0, 3):  # qI_codes, K_codes
+        bad = list(a)
+        bad[i] = _p(4096 + 8)
+        assert lib.csa_index_topk_decode_fp4(ctypes.byref(dec), *bad, 1 << 40, None) == -1
     assert L.workspace_bytes("index_topk_decode_fp4", dec) == L.workspace_bytes("index_topk_decode", dec)
     assert L.workspace_zero_bytes("index_topk_decode_fp4", dec) == 0
 
@@ -300,6 +307,11 @@ def test_fp4_paged_calls_reject(lib):
              1 << 40, None) == -1
     assert t(ctypes.byref(dd), _p(), _p(), _p(), _p(), _p(), _p(), 32, _p(), _p(), _p(),
              8, None) == -3
+    for i in (0, 3):  # qI_codes, K_codes_pool off a 16-byte boundary
+        a = [_p(4096)] * 5
+        a[i] = _p(4096 + 4)
+        assert t(ctypes.byref(dd), *a, _p(4096), 32, _p(4096), _p(4096), _p(4096),
+                 1 << 40, None) == -1
     big = L.IndexDesc(0, 2, 16, 64, 4, 8, L.CSA_BF16, 1 << 31)
     assert t(ctypes.byref(big), _p(), _p(), _p(), _p(), _p(), _p(), 32, _p(), _p(), _p(),
              1 << 40, None) == -2
