@@ -1014,7 +1014,30 @@ def main():
     rec["index_bf16_scores"] = {
         "index_topk_ms": ib_ms, "index_topk_fp32_ms": idx_ms, "speedup": idx_ms / ib_ms,
         "recall_of_fp32_selection": float(hit.sum().item()) / float((idx32 >= 0).sum().item())}
-    del idx32, idx16, pos, hit
+    # the FP4 indexer path at prefill ([R] section 4.4): q^I and the keys
+    # rotated and quantised to E2M1, scores from the scaled FP4 matrix
+    # instruction; its time, the quantisation it adds, and its recall of the
+    # fp32-score selection on the same inputs
+    qc, qe = L.csa_indexer_fp4_quant(pf.t["qI"])
+    kc, ke = L.csa_indexer_fp4_quant(pf.kI)
+
+    def quant_fp4():
+        L.csa_indexer_fp4_quant(pf.t["qI"], out=(qc, qe))
+        L.csa_indexer_fp4_quant(pf.kI, out=(kc, ke))
+
+    def index_fp4():
+        L.csa_index_topk_prefill_fp4(qc, qe, pf.t["wI"], kc, ke, cfg["m"], cfg["k"], out=idx16)
+    i4_ms = float(np.mean(time_region(index_fp4, max(3, a.steps), 1)))
+    q4_ms = float(np.mean(time_region(quant_fp4, max(3, a.steps), 1)))
+    index_fp4()
+    pos = torch.searchsorted(idx16, idx32).clamp_(max=idx16.shape[1] - 1)
+    hit = (idx16.gather(1, pos) == idx32) & (idx32 >= 0)
+    rec["index_fp4"] = {
+        "index_topk_ms": i4_ms, "quant_ms": q4_ms, "index_topk_fp32_ms": idx_ms,
+        "speedup_with_quant": idx_ms / (i4_ms + q4_ms),
+        "key_bytes_per_entry": [kc.shape[-1] + ke.shape[-1], 2 * pf.kI.shape[-1]],
+        "recall_of_fp32_selection": float(hit.sum().item()) / float((idx32 >= 0).sum().item())}
+    del idx32, idx16, pos, hit, qc, qe, kc, ke
     # the whole layer around the four calls (query path and output projection
     # added), on the same workload
     print("[bench] timing the full CSA layer", file=sys.stderr, flush=True)

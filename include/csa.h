@@ -347,6 +347,26 @@ int csa_index_topk_decode_fp4(const csa_index_desc* desc, const uint8_t* qI_code
                               const uint8_t* K_exps, const int64_t* pos, int32_t* idx_out,
                               void* ws, size_t ws_bytes, void* stream);
 
+/* csa_index_topk_prefill_fp4 -- csa_index_topk_prefill on the quantised
+ * path ([R] section 4.4: the indexer's QK path in FP4 for prefill as for
+ * decode): q^I and the keys in the format csa_indexer_fp4_quant writes, the
+ * products taken on the scaled E2M1 matrix instruction, the scores eq 16 on
+ * the dequantised values in fp32 (or rounded to bf16 with score_dtype
+ * CSA_BF16), the selection as csa_index_topk_prefill.  wI in desc->dtype
+ * (CSA_BF16 only).  Rows that see more than 16384 entries are not supported
+ * on this path (CSA_ERR_UNSUPPORTED).  Workspace:
+ * CSA_ENTRY_INDEX_TOPK_PREFILL_FP4 (the score rows, no zero bytes).
+ *
+ *   qI_codes [n, hI, cI/2], qI_exps [n, hI, cI/32]
+ *   K_codes  [n_entries, cI/2], K_exps [n_entries, cI/32]
+ *   wI [n, hI], idx_out [n, k] as in csa_index_topk_prefill
+ * qI_codes and K_codes start on a 16-byte boundary (else
+ * CSA_ERR_INVALID_ARG, checked after the workspace). */
+int csa_index_topk_prefill_fp4(const csa_index_desc* desc, const uint8_t* qI_codes,
+                               const uint8_t* qI_exps, const void* wI, const uint8_t* K_codes,
+                               const uint8_t* K_exps, int32_t* idx_out, void* ws,
+                               size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * Core attention
  * ---------------------------------------------------------------------- */
@@ -495,7 +515,8 @@ typedef enum csa_entry {
   CSA_ENTRY_OUTPUT_PROJ = 9,
   CSA_ENTRY_INDEX_TOPK_DECODE_FP4 = 10,
   CSA_ENTRY_SPARSE_MQA_BACKWARD = 11,
-  CSA_ENTRY_DENSE_MQA_BACKWARD = 12
+  CSA_ENTRY_DENSE_MQA_BACKWARD = 12,
+  CSA_ENTRY_INDEX_TOPK_PREFILL_FP4 = 13
 } csa_entry;
 
 /* ------------------------------------------------------------------------

@@ -23,7 +23,7 @@ CSA_F32, CSA_BF16 = 0, 1
 ENTRY = dict(compress_prefill=0, compress_decode=1, index_topk_prefill=2, index_topk_decode=3,
              sparse_mqa_prefill=4, sparse_mqa_decode=5, dense_mqa_prefill=6, dense_mqa_decode=7,
              query_proj=8, output_proj=9, index_topk_decode_fp4=10, sparse_mqa_backward=11,
-             dense_mqa_backward=12)
+             dense_mqa_backward=12, index_topk_prefill_fp4=13)
 EXPORTED = ["csa_compress_prefill", "csa_compress_decode", "csa_state_bytes", "csa_state_init",
             "csa_index_topk_prefill", "csa_index_topk_decode", "csa_sparse_mqa_prefill",
             "csa_sparse_mqa_decode", "hca_dense_mqa_prefill", "hca_dense_mqa_decode",
@@ -37,7 +37,7 @@ EXPORTED = ["csa_compress_prefill", "csa_compress_decode", "csa_state_bytes", "c
             "csa_index_topk_decode_score", "csa_index_topk_decode_select",
             "csa_sparse_mqa_backward", "hca_dense_mqa_backward", "csa_kv_fp8_row_bytes",
             "csa_kv_fp8_quant", "csa_kv_fp8_quant_decode", "csa_sparse_mqa_decode_fp8",
-            "hca_dense_mqa_decode_fp8"]
+            "hca_dense_mqa_decode_fp8", "csa_index_topk_prefill_fp4"]
 
 
 class CompressDesc(ctypes.Structure):
@@ -124,6 +124,7 @@ def load(path: str = LIB_PATH):
     lib.csa_output_proj.argtypes = [P] * 6 + [S, P]
     lib.csa_indexer_fp4_quant.argtypes = [P] * 5
     lib.csa_index_topk_decode_fp4.argtypes = [P] * 9 + [S, P]
+    lib.csa_index_topk_prefill_fp4.argtypes = [P] * 8 + [S, P]
     lib.csa_indexer_fp4_quant_decode.argtypes = [P, P, ctypes.c_int64, P, I, P, P, P]
     I32 = ctypes.c_int32
     lib.csa_compress_decode_paged.argtypes = [P] * 10 + [I32] + [P] * 2 + [S, P]
@@ -869,6 +870,32 @@ def csa_index_topk_decode_fp4(q_codes, q_exps, wI, k_codes, k_exps, pos, m, k, o
     if st != 0:
         _WS_ZERO.pop((str(q_codes.device), "index_dec_fp4"), None)
     _check(st, "csa_index_topk_decode_fp4")
+    return out
+
+
+def csa_index_topk_prefill_fp4(q_codes, q_exps, wI, k_codes, k_exps, m, k, out=None,
+                               scores="f32", t0=0):
+    """csa_index_topk_prefill on FP4 q^I [n, hI, cI/2] (+ exps [n, hI,
+    cI/32]) and FP4 keys [n_entries, cI/2] (+ exps [n_entries, cI/32]); wI
+    [n, hI] bf16."""
+    lib = load()
+    n, hI, half = q_codes.shape
+    cI = 2 * half
+    ne = k_codes.shape[0]
+    _expect(q_exps, (n, hI, cI // 32), torch.uint8, "q_exps")
+    _expect(k_codes, (ne, half), torch.uint8, "k_codes")
+    _expect(k_exps, (ne, cI // 32), torch.uint8, "k_exps")
+    _expect(wI, (n, hI), None, "wI")
+    sdt = {"f32": CSA_F32, "bf16": CSA_BF16}[scores]
+    desc = IndexDesc(n, 1, hI, cI, m, k, _dt(wI), ne, sdt, t0)
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.int32, device=q_codes.device)
+    ws, wsb = workspace(workspace_bytes("index_topk_prefill_fp4", desc), q_codes.device, "index")
+    st = lib.csa_index_topk_prefill_fp4(ctypes.byref(desc), _ptr(q_codes), _ptr(q_exps), _ptr(wI),
+                                        _ptr(k_codes) if ne else None,
+                                        _ptr(k_exps) if ne else None, _ptr(out), _ptr(ws), wsb,
+                                        _stream(q_codes.device))
+    _check(st, "csa_index_topk_prefill_fp4")
     return out
 
 

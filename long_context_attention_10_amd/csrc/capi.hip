@@ -255,6 +255,11 @@ size_t csa_workspace_bytes(int entry, const void* desc) {
       if (index_prefill_long(d)) return index_prefill_long_ws_bytes(*d);
       return al((size_t)d->n * index_prefill_ld(d) * (d->score_dtype == CSA_BF16 ? 2 : 4));
     }
+    case CSA_ENTRY_INDEX_TOPK_PREFILL_FP4: {
+      const csa_index_desc* d = (const csa_index_desc*)desc;
+      if (d->m <= 0 || d->n <= 0 || index_prefill_long(d)) return 0;
+      return al((size_t)d->n * index_prefill_ld(d) * (d->score_dtype == CSA_BF16 ? 2 : 4));
+    }
     case CSA_ENTRY_INDEX_TOPK_DECODE:
     case CSA_ENTRY_INDEX_TOPK_DECODE_FP4: {
       const csa_index_desc* d = (const csa_index_desc*)desc;
@@ -541,6 +546,28 @@ int csa_index_topk_decode_fp4(const csa_index_desc* d, const uint8_t* qI_codes,
   if (!codes_aligned(qI_codes, K_codes)) return CSA_ERR_INVALID_ARG;
   return hip_status(launch_index_topk_decode_fp4(*d, qI_codes, qI_exps, wI, K_codes, K_exps, pos,
                                                  idx_out, ws, (hipStream_t)stream));
+}
+
+int csa_index_topk_prefill_fp4(const csa_index_desc* d, const uint8_t* qI_codes,
+                               const uint8_t* qI_exps, const void* wI, const uint8_t* K_codes,
+                               const uint8_t* K_exps, int32_t* idx_out, void* ws, size_t ws_bytes,
+                               void* stream) {
+  int s = check_index(d, false);
+  if (s) return s;
+  if (d->dtype != CSA_BF16 || index_prefill_long(d)) return CSA_ERR_UNSUPPORTED;
+  if (d->n == 0) return CSA_OK;
+  if (!qI_codes || !qI_exps || !wI || !idx_out || (d->n_entries > 0 && (!K_codes || !K_exps)))
+    return CSA_ERR_INVALID_ARG;
+  const int64_t ld = index_prefill_ld(d);
+  const size_t need = al((size_t)d->n * ld * (d->score_dtype == CSA_BF16 ? 2 : 4));
+  if (ld > 0 && (!ws || ws_bytes < need)) return CSA_ERR_WORKSPACE;
+  if (!codes_aligned(qI_codes, d->n_entries > 0 ? K_codes : nullptr)) return CSA_ERR_INVALID_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (ld > 0)
+    e = launch_index_scores_prefill_fp4(*d, qI_codes, qI_exps, wI, K_codes, K_exps, ws, ld, st);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(launch_topk_rows_prefill(*d, ws, ld, idx_out, st));
 }
 
 int csa_sparse_mqa_prefill(const csa_attn_desc* d, const void* q, const void* win_kv,

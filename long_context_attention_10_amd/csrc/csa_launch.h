@@ -84,6 +84,10 @@ hipError_t launch_index_topk_prefill_long(const csa_index_desc& d, const void* q
                                           const void* wI, const void* KI, int32_t* idx_out,
                                           void* ws, hipStream_t st);
 size_t index_decode_zero_bytes(const csa_index_desc& d);
+hipError_t launch_index_scores_prefill_fp4(const csa_index_desc& d, const uint8_t* qc,
+                                           const uint8_t* qe, const void* wI, const uint8_t* kc,
+                                           const uint8_t* ke, void* scores, int64_t ld,
+                                           hipStream_t st);
 hipError_t launch_index_topk_decode_fp4(const csa_index_desc& d, const uint8_t* qc,
                                         const uint8_t* qe, const void* wI, const uint8_t* kc,
                                         const uint8_t* ke, const int64_t* pos, int32_t* idx_out,

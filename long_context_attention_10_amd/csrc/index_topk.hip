@@ -163,6 +163,177 @@ __global__ __launch_bounds__(256) void index_scores_prefill_kernel(
 }
 
 // ===========================================================================
+// Prefill scoring over FP4 q^I and keys (the E2M1 codes and block exponents
+// of the quantised indexer path): the workgroup shape, key blocks and head
+// reduction of index_scores_prefill_kernel, with the products on the scaled
+// E2M1 matrix instruction, one per 64 channels for 32 keys and 32 rows.  A
+// key block's codes are staged in LDS by direct loads (rows of CI/2 bytes,
+// 16-byte granules XOR-permuted by key so that each 16-lane group of a read,
+// 16 keys with one granule each, hits distinct banks); its exponent bytes
+// come through registers into LDS with the block's prefetch.
+// ===========================================================================
+template <int HI, int CI, class SC>
+__global__ __launch_bounds__(256) void index_scores_prefill_fp4_kernel(
+    const uint8_t* __restrict__ qc, const uint8_t* __restrict__ qe, const uint16_t* __restrict__ wI,
+    const uint8_t* __restrict__ kc, const uint8_t* __restrict__ ke, int64_t n, int64_t n_entries,
+    int m, int key_chunk, SC* __restrict__ scores, int64_t ld, int64_t t0) {
+  constexpr int NG = CI / 32;       // scale blocks per row
+  constexpr int NH = CI / 64;       // 64-channel k-groups: one instruction each
+  constexpr int RBC = CI / 2;       // code bytes per row
+  constexpr int GR = RBC / 16;      // 16-byte granules per row
+  constexpr int KPR = 256 / RBC;    // rows per 256 bytes (one 16-lane read group)
+  constexpr int RB = 2;             // 32-row blocks per wave
+  constexpr int ROWS = 4 * RB * 32; // (query, head) rows per workgroup
+  constexpr int TQ = ROWS / HI;     // queries per workgroup
+  constexpr int KB = 128;           // keys per staged block
+  constexpr int KPI = 1024 / RBC;   // keys per 64-lane DMA
+  constexpr int DPW = KB / KPI / 4; // DMA instructions per wave per block
+  constexpr int EB = KB * NG;       // exponent bytes per block
+  constexpr int EPT = EB / 256;     // exponent bytes per thread
+  static_assert(DPW >= 1 && EB % 256 == 0, "key block layout");
+  __shared__ __align__(16) uint8_t sK[2][KB * RBC];
+  __shared__ uint8_t sE[2][EB];
+  auto swz = [](int key) { return (key / KPR) % GR; };
+
+  const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t q0 = (int64_t)blockIdx.x * TQ;
+  const int64_t tlast = min64(q0 + TQ, n) - 1;
+  // query row t is the token at position t0 + t
+  const int64_t kend =
+      min64(min64((t0 + tlast + 1) / m, n_entries), (int64_t)(blockIdx.y + 1) * key_chunk);
+  const int64_t kbeg = (int64_t)blockIdx.y * key_chunk;
+  if (kbeg >= kend) return;
+
+  // keys past kend are read from the last key; their scores are not stored
+  auto issue_block = [&](int64_t k0, int buf) {
+#pragma unroll
+    for (int u = 0; u < DPW; ++u) {
+      const int d = wave + 4 * u;           // DMA index within the block
+      const int key = d * KPI + lane / GR;  // key within the block
+      const int pos = lane % GR;            // LDS granule position
+      const int64_t sidx = min64(k0 + key, kend - 1);
+      lds_dma16(kc + sidx * RBC + 16 * (pos ^ swz(key)), &sK[buf][d * 1024]);
+    }
+  };
+  auto load_exps = [&](int64_t k0, uint32_t (&e)[EPT]) {
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      const int bi = tid + 256 * j;  // byte of the block: key bi / NG, scale block bi % NG
+      e[j] = ke[min64(k0 + bi / NG, kend - 1) * NG + bi % NG];
+    }
+  };
+  auto store_exps = [&](int buf, const uint32_t (&e)[EPT]) {
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) sE[buf][tid + 256 * j] = (uint8_t)e[j];
+  };
+  issue_block(kbeg, 0);
+  uint32_t en[EPT];
+  load_exps(kbeg, en);
+
+  // A operands (query rows: codes and scale per lane) and per-row weights,
+  // held for the whole chunk; a row past n is zero with scale 1
+  uint4 qa[RB][NH];
+  uint32_t qs[RB][NH];
+  float wv[RB][16];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int row = wave * (RB * 32) + rb * 32 + (lane & 31);
+    const int64_t t = q0 + row / HI;
+    const int h = row % HI;
+    const bool ok = t < n;
+#pragma unroll
+    for (int g = 0; g < NH; ++g) {
+      const int blk = 2 * g + hl;
+      qa[rb][g] = ok ? *(const uint4*)(qc + (t * HI + h) * RBC + blk * 16) : make_uint4(0, 0, 0, 0);
+      qs[rb][g] = ok ? (uint32_t)qe[(t * HI + h) * NG + blk] : 127u;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int rr = wave * (RB * 32) + rb * 32 + 8 * (i >> 2) + 4 * hl + (i & 3);
+      const int64_t tt = q0 + rr / HI;
+      wv[rb][i] = tt < n ? BF16::ld(wI, tt * HI + rr % HI) : 0.f;
+    }
+  }
+  int vis[RB][4];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int64_t tb = q0 + (wave * (RB * 32) + rb * 32) / HI;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t t = HI == 4 ? tb + 2 * j + hl : HI == 8 ? tb + 2 * hl + (j & 1) : tb + hl;
+      vis[rb][j] = t < n ? (int)min64((t0 + t + 1) / m, n_entries) : 0;
+    }
+  }
+  store_exps(0, en);
+  wait_vmem();
+  __syncthreads();
+  SC* srow0 = scores + q0 * ld;
+  const int ld32 = (int)ld;
+
+  const int nblk = (int)((kend - kbeg + KB - 1) / KB);
+  for (int bi = 0; bi < nblk; ++bi) {
+    const int buf = bi & 1;
+    const int64_t kb0 = kbeg + (int64_t)bi * KB;
+    const bool more = bi + 1 < nblk;
+    if (more) {
+      issue_block(kb0 + KB, buf ^ 1);
+      load_exps(kb0 + KB, en);
+    }
+    const int nsub = (int)min64(KB / 32, (kend - kb0 + 31) / 32);
+    for (int sb = 0; sb < nsub; ++sb) {
+      const int kk = sb * 32 + (lane & 31);  // this lane's key within the block
+      const uint8_t* krow = &sK[buf][kk * RBC];
+      f32x16_t acc[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x16_t{};
+#pragma unroll
+      for (int g = 0; g < NH; ++g) {
+        const int gi = 2 * g + hl;
+        const uint4 kb = *(const uint4*)(krow + 16 * (gi ^ swz(kk)));
+        const uint32_t ks = sE[buf][kk * NG + gi];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) mma32_fp4(acc[rb], qa[rb][g], qs[rb][g], kb, ks);
+      }
+      const int si = (int)(kb0 + kk);  // entry index (< 2^31)
+      const bool sok = si < kend;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        float part[4];
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          float p = 0.f;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) p += wv[rb][gq * 4 + r] * relu(acc[rb][gq * 4 + r]);
+          part[gq] = p;
+        }
+        const int tr = (wave * (RB * 32) + rb * 32) / HI;
+        auto put = [&](int tq, int vq, float v) {  // query q0 + tq, visible count vq
+          if (sok && si < vq) {
+            if constexpr (sizeof(SC) == 2) srow0[(uint32_t)(tq * ld32 + si)] = f32_to_bf16(v);
+            else srow0[(uint32_t)(tq * ld32 + si)] = v;
+          }
+        };
+        if (HI == 4) {
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) put(tr + 2 * gq + hl, vis[rb][gq], part[gq]);
+        } else if (HI == 8) {
+          const float v0 = swap32_pair_add(part[0], part[2]);
+          const float v1 = swap32_pair_add(part[1], part[3]);
+          put(tr + 2 * hl, vis[rb][0], v0);
+          put(tr + 2 * hl + 1, vis[rb][1], v1);
+        } else {
+          put(tr + hl, vis[rb][0], swap32_pair_add(part[0] + part[1], part[2] + part[3]));
+        }
+      }
+    }
+    if (more) store_exps(buf ^ 1, en);
+    wait_vmem();
+    __syncthreads();
+  }
+}
+
+// ===========================================================================
 // Block-wide helpers (256 threads)
 // ===========================================================================
 // Exclusive prefix sum over the 256 threads in thread order; returns the total
@@ -1281,6 +1452,29 @@ hipError_t launch_index_scores_prefill(const csa_index_desc& d, const void* qI, 
       index_scores_prefill_kernel<F32, HI, CI, float><<<grid, 256, 0, st>>>(
           (const float*)qI, (const float*)wI, (const float*)KI, d.n, d.n_entries, d.m, key_chunk,
           (float*)scores, ld, d.t0);
+  });
+  return hipGetLastError();
+}
+
+hipError_t launch_index_scores_prefill_fp4(const csa_index_desc& d, const uint8_t* qc,
+                                           const uint8_t* qe, const void* wI, const uint8_t* kc,
+                                           const uint8_t* ke, void* scores, int64_t ld,
+                                           hipStream_t st) {
+  const int key_chunk = 2048;
+  const int64_t nvis = (d.t0 + d.n) / d.m < d.n_entries ? (d.t0 + d.n) / d.m : d.n_entries;
+  if (nvis == 0) return hipSuccess;
+  CSA_INDEX_DISPATCH(d.n_heads, d.head_dim, {
+    constexpr int TQ = 256 / HI;
+    if ((int64_t)TQ * ld >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    dim3 grid((unsigned)((d.n + TQ - 1) / TQ), (unsigned)((nvis + key_chunk - 1) / key_chunk));
+    if (d.score_dtype == CSA_BF16)
+      index_scores_prefill_fp4_kernel<HI, CI, uint16_t><<<grid, 256, 0, st>>>(
+          qc, qe, (const uint16_t*)wI, kc, ke, d.n, d.n_entries, d.m, key_chunk,
+          (uint16_t*)scores, ld, d.t0);
+    else
+      index_scores_prefill_fp4_kernel<HI, CI, float><<<grid, 256, 0, st>>>(
+          qc, qe, (const uint16_t*)wI, kc, ke, d.n, d.n_entries, d.m, key_chunk, (float*)scores,
+          ld, d.t0);
   });
   return hipGetLastError();
 }

@@ -137,3 +137,27 @@ def check_topk_sets(gpu_idx, scores, k, m, t0=0, rel_tau=1e-5):
                     f"row {r}: entry {s} score {scores[r, s]!r} vs k-th {kth!r} outside tie band")
             n_tie_rows += 1
     return n_tie_rows
+
+
+def check_bf16_selection(got, sc, k, m, t0=0):
+    """GPU rows selected on bf16 scores against the oracle's selection on the
+    fp64 scores rounded to bf16.  The GPU rounds fp32 scores, so an entry
+    whose score sits within one bf16 step of the k-th rounded score may round
+    the other way; only such entries may differ.  Returns the rows that
+    differ."""
+    ref = O.topk_bf16_scores(sc, k, m, t0=t0)
+    rb = O.round_bf16(sc)
+    nd = 0
+    for r in range(got.shape[0]):
+        vis = int(min(sc.shape[1], (t0 + r + 1) // m))
+        kt = min(k, vis)
+        g = got[r]
+        assert np.all(g[kt:] == -1) and np.all(np.diff(g[:kt]) > 0), f"row {r}: layout"
+        diff = set(g[:kt].tolist()) ^ set(ref[r, :kt].tolist())
+        if diff:
+            kth = np.sort(rb[r, :vis])[::-1][kt - 1]
+            band = 1.01 * float(bf16_ulp(kth)) + 1e-6
+            for s_ in diff:
+                assert abs(sc[r, s_] - kth) <= band, f"row {r}: entry {s_} off the bf16 tie band"
+            nd += 1
+    return nd

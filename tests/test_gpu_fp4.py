@@ -8,7 +8,7 @@ import torch
 
 from oracle import csa_oracle as O
 from long_context_attention_10_amd import inputs as I
-from parity_util import check_topk_sets, f64
+from parity_util import check_bf16_selection, check_topk_sets, f64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -89,6 +89,80 @@ def test_index_topk_decode_fp4(lib, hI, cI, m, k, ne, pos):
         check_topk_sets(got[b][None], sc, k, m, t0=p)
     # and the quantiser's, on a sample of the keys
     _check_quant(KI[0, :2048], kc[0, :2048], ke[0, :2048])
+
+
+def _prefill_fp4_case(lib, key, n, hI, cI, ne):
+    """bf16 q^I, weights and keys, and the GPU's FP4 codes of q^I and keys,
+    with their exactly dequantised values (what the scores are defined on)."""
+    qI = I.normal((n, hI, cI), key + ("q",), dtype="bf16", device=DEV)
+    wI = I.uniform((n, hI), key + ("w",), dtype="bf16", device=DEV)
+    KI = I.normal((ne, cI), key + ("K",), dtype="bf16", device=DEV)
+    qc, qe = lib.csa_indexer_fp4_quant(qI)
+    kc, ke = lib.csa_indexer_fp4_quant(KI)
+    torch.cuda.synchronize()
+    qd = O.fp4_dequant(_nibbles(qc), qe.cpu().numpy().astype(np.int64) - 127)
+    kd = O.fp4_dequant(_nibbles(kc), ke.cpu().numpy().astype(np.int64) - 127)
+    return (qc, qe, wI, kc, ke), qd, f64(wI), kd
+
+
+@pytest.mark.parametrize("hI,cI,m,k,n,ne,t0", [
+    (16, 64, 4, 512, 2500, 700, 0),      # the 64K workload's indexer shape; ragged rows and blocks
+    (4, 64, 4, 64, 1037, 300, 0),
+    (8, 128, 4, 100, 3001, 800, 0),
+    (16, 128, 4, 256, 1200, 5000, 4096),  # a chunk starting at position 4096
+    (16, 64, 128, 16, 700, 9, 0),         # m = 128: a handful of visible entries, k above them
+])
+def test_index_topk_prefill_fp4(lib, hI, cI, m, k, n, ne, t0):
+    """The prefill selection over FP4 q^I and keys: every row's set equals
+    the oracle's top-k of eq 16 on the dequantised values (to the fp32 tie
+    band), layout and padding exact."""
+    _say("index prefill fp4", hI, cI, m, k, n, ne, t0)
+    args, qd, w, kd = _prefill_fp4_case(lib, ("ipre-fp4", hI, cI, n, ne, t0), n, hI, cI, ne)
+    idx = lib.csa_index_topk_prefill_fp4(*args, m, k, t0=t0)
+    torch.cuda.synchronize()
+    sc = O.index_scores(qd, w, kd, m, t0=t0)
+    nd = check_topk_sets(idx.cpu().numpy(), sc, k, m, t0=t0)
+    assert nd <= n // 50
+
+
+def test_index_topk_prefill_fp4_bf16_scores(lib):
+    """Selection on bf16-rounded FP4 scores over 4096 tokens at the 64K
+    workload's indexer shape."""
+    n, hI, cI, m, k = 4096, 16, 64, 4, 512
+    _say("index prefill fp4 bf16 scores", n)
+    args, qd, w, kd = _prefill_fp4_case(lib, ("ipre-fp4-bf16", n), n, hI, cI, n // m)
+    idx = lib.csa_index_topk_prefill_fp4(*args, m, k, scores="bf16")
+    torch.cuda.synchronize()
+    nd = check_bf16_selection(idx.cpu().numpy(), O.index_scores(qd, w, kd, m), k, m)
+    assert nd <= n // 20
+
+
+def test_index_topk_prefill_fp4_nothing_visible(lib):
+    """No entries, and rows before the first block ends: all padding."""
+    _say("index prefill fp4 empty")
+    args, _, _, _ = _prefill_fp4_case(lib, ("ipre-fp4-empty",), 3, 16, 64, 5)
+    idx = lib.csa_index_topk_prefill_fp4(*args, 4, 8)
+    qc, qe, wI = args[:3]
+    empty = lib.csa_index_topk_prefill_fp4(qc, qe, wI, torch.empty((0, 32), dtype=torch.uint8,
+                                                                    device=DEV),
+                                           torch.empty((0, 2), dtype=torch.uint8, device=DEV), 4, 8)
+    torch.cuda.synchronize()
+    assert (idx.cpu() == -1).all() and (empty.cpu() == -1).all()
+
+
+def test_index_topk_prefill_fp4_64k(lib):
+    """The 64K workload's indexer (16 heads x 64, k = 512, 16384 entries) on
+    the FP4 path, in the launch configuration the benchmark times, on
+    sampled rows against the oracle."""
+    n, hI, cI, m, k = 65536, 16, 64, 4, 512
+    _say("index prefill fp4 64K")
+    args, qd, w, kd = _prefill_fp4_case(lib, ("ipre-fp4-64k",), n, hI, cI, n // m)
+    idx = lib.csa_index_topk_prefill_fp4(*args, m, k).cpu().numpy()
+    torch.cuda.synchronize()
+    for t in [3, k * m - 1, k * m, 4095, 4096, 30001, 47103, n - 1]:
+        vis = (t + 1) // m
+        sc = O.index_scores(qd[t][None], w[t][None], kd[:vis], m, t0=t)
+        check_topk_sets(idx[t][None], sc, k, m, t0=t)
 
 
 def test_fp4_quant_decode_writes_only_emitted_rows(lib):

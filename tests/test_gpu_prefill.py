@@ -11,7 +11,8 @@ import torch
 
 from oracle import csa_oracle as O
 from long_context_attention_10_amd import inputs as I
-from parity_util import bf16_ulp, assert_out_close, assert_stored_close, check_topk_sets, f64
+from parity_util import (bf16_ulp, assert_out_close, assert_stored_close, check_bf16_selection,
+                         check_topk_sets, f64)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -120,30 +121,6 @@ def test_index_topk_prefill_large_k(lib, k):
         check_topk_sets(idx[t][None], sc, k, m, t0=t)
 
 
-def _check_bf16_selection(got, sc, k, m, t0=0):
-    """GPU rows selected on bf16 scores against the oracle's selection on the
-    fp64 scores rounded to bf16.  The GPU rounds fp32 scores, so an entry
-    whose score sits within one bf16 step of the k-th rounded score may round
-    the other way; only such entries may differ.  Returns the rows that
-    differ."""
-    ref = O.topk_bf16_scores(sc, k, m, t0=t0)
-    rb = O.round_bf16(sc)
-    nd = 0
-    for r in range(got.shape[0]):
-        vis = int(min(sc.shape[1], (t0 + r + 1) // m))
-        kt = min(k, vis)
-        g = got[r]
-        assert np.all(g[kt:] == -1) and np.all(np.diff(g[:kt]) > 0), f"row {r}: layout"
-        diff = set(g[:kt].tolist()) ^ set(ref[r, :kt].tolist())
-        if diff:
-            kth = np.sort(rb[r, :vis])[::-1][kt - 1]
-            band = 1.01 * float(bf16_ulp(kth)) + 1e-6
-            for s_ in diff:
-                assert abs(sc[r, s_] - kth) <= band, f"row {r}: entry {s_} off the bf16 tie band"
-            nd += 1
-    return nd
-
-
 def test_index_topk_prefill_bf16_scores(lib):
     """Selection on bf16-rounded scores ([R] section 4.4) over 4096 tokens with
     the 64K workload's indexer shape."""
@@ -156,7 +133,7 @@ def test_index_topk_prefill_bf16_scores(lib):
     idx = lib.csa_index_topk_prefill(qI, wI, KI, m, k, scores="bf16").cpu().numpy()
     torch.cuda.synchronize()
     sc = O.index_scores(f64(qI), f64(wI), f64(KI), m)
-    nd = _check_bf16_selection(idx, sc, k, m)
+    nd = check_bf16_selection(idx, sc, k, m)
     assert nd <= n // 20
 
 
