@@ -498,6 +498,9 @@ constexpr int kDenseHG = 2;  // 16-head groups per wave: two waves per token
 // row r, global granule s ^ dense_key(r).
 CSA_DEV int dense_key(int r) { return ((r & 7) << 1) | ((r >> 4) & 1); }
 
+// A compile-time int for generic lambdas.
+template <int N> struct IntC { static constexpr int value = N; };
+
 template <int C>
 __global__ __launch_bounds__(64 * kDenseTB * 4 / kDenseHG, 8 / (kDenseTB * 4 / kDenseHG)) void
 mqa_dense_tokblock_kernel(
@@ -633,14 +636,21 @@ mqa_dense_tokblock_kernel(
   int slot[8];  // tile rows pi(lg, b, i) of this lane's logits z[4b + i]
 #pragma unroll
   for (int e = 0; e < 8; ++e) slot[e] = slot_pi(lg, e >> 2, e & 3);
+  // the token's rows relative to the block's tiles, in 32 bits (the launch
+  // keeps the window and the entry count below 2^30, so tile rows, window
+  // bounds and visible entries all fit)
+  const int nwr32 = (int)nwr, wbeg32 = (int)wbeg, wend32 = (int)wend, vis32 = (int)vis;
   // tile 0 has landed once at most the later prologue gathers are in flight
   if (min(AHEAD - 1, ntiles - 1) >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * BPW));
   else if (min(AHEAD - 1, ntiles - 1) == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(BPW));
   else wait_vmem();
   __syncthreads();
-  for (int ti = 0; ti < ntiles; ++ti) {
-    const int buf = ti % NBUF;  // buffer (ti + AHEAD) % NBUF held tile ti - 1
-    if (wave < 4 && ti + AHEAD < ntiles) issue_tile(ti + AHEAD, (ti + AHEAD) % NBUF);
+  // One tile: its ring buffer is a compile-time constant, so every LDS read
+  // takes the buffer offset as an immediate and only the per-lane offsets
+  // above occupy registers.
+  auto step = [&](int ti, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;  // buffer (buf + AHEAD) % NBUF held tile ti - 1
+    if (wave < 4 && ti + AHEAD < ntiles) issue_tile(ti + AHEAD, (buf + AHEAD) % NBUF);
     const uint8_t* kv = smem + buf * TBYTES;
     // S^T = K Q^T for the wave's head groups; each K fragment read once
     f32x4_t sc[HG][2];
@@ -656,30 +666,33 @@ mqa_dense_tokblock_kernel(
         sc[hg][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[hg][g], sc[hg][1], 0, 0, 0);
       }
     }
-    // this token's rows of the tile: [lo, hi] (wave-uniform); a tile it
-    // sees whole needs no mask
-    const int64_t j0 = (int64_t)ti * kT;
-    const int64_t lo64 = j0 < nwr ? wbeg - j0 : 0;
-    const int64_t hi64 = j0 < nwr ? wend - j0 : vis - (j0 - nwr) - 1;
-    const int lo = (int)max64(min64(lo64, kT), 0), hi = (int)max64(min64(hi64, kT - 1), -1);
-    const bool whole = lo == 0 && hi == kT - 1, none = hi < lo;
-    // a bias per row of this lane: 0 where the token sees it, else -inf
-    float bias[8];
+    // raw logits; this token's rows of the tile are [lo, hi] (wave-uniform),
+    // and only a tile it does not see whole is masked (rows outside -> -inf)
+    float z[HG][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      bias[e] = whole || (!none && (unsigned)(slot[e] - lo) <= (unsigned)(hi - lo)) ? 0.f
-                                                                                  : -INFINITY;
+    for (int hg = 0; hg < HG; ++hg)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) z[hg][e] = sc[hg][e >> 2][e & 3];
+    const int j0 = ti * kT;
+    const int lo = min(max(j0 < nwr32 ? wbeg32 - j0 : 0, 0), kT);
+    const int hi = max(min(j0 < nwr32 ? wend32 - j0 : vis32 - (j0 - nwr32) - 1, kT - 1), -1);
+    if (!(lo == 0 && hi == kT - 1)) {
+      const bool none = hi < lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const bool in = !none && (unsigned)(slot[e] - lo) <= (unsigned)(hi - lo);
+#pragma unroll
+        for (int hg = 0; hg < HG; ++hg) z[hg][e] = in ? z[hg][e] : -INFINITY;
+      }
+    }
     bf16x8_t pb[HG];
 #pragma unroll
     for (int hg = 0; hg < HG; ++hg) {
-      float z[8];
-      float mx = -INFINITY;
+      float mx = z[hg][0];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        z[e] = fmaf(sc[hg][e >> 2][e & 3], sl2, bias[e]);
-        mx = fmaxf(mx, z[e]);
-      }
-      mx = xlane_max(mx);
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, z[hg][e]);
+      // in log2 units: the maximum commutes with the positive scale
+      mx = xlane_max(mx) * sl2;
       if (__any(mx > run_m[hg] + 8.f)) {  // wave-uniform rescale of this group's O
         const float nm = fmaxf(run_m[hg], mx);
         const float alpha = __builtin_amdgcn_exp2f(run_m[hg] - nm);
@@ -690,13 +703,11 @@ mqa_dense_tokblock_kernel(
 #pragma unroll
           for (int i = 0; i < 4; ++i) o[hg][cb][i] *= alpha;
       }
+      const float nm = -run_m[hg];
       f32x8_t p;
-      float ps = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(z[e] - run_m[hg]);
-        ps += p[e];
-      }
+      for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(z[hg][e], sl2, nm));
+      const float ps = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
       run_l[hg] += xlane_sum(ps);
       pb[hg] = __builtin_convertvector(p, bf16x8_t);
     }
@@ -723,6 +734,13 @@ mqa_dense_tokblock_kernel(
     else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(BPW));
     else wait_vmem();
     __syncthreads();
+  };
+  static_assert(NBUF == 4, "the loop below visits the ring's four buffers in turn");
+  for (int ti = 0; ti < ntiles; ti += NBUF) {
+    step(ti, IntC<0>{});
+    if (ti + 1 < ntiles) step(ti + 1, IntC<1>{});
+    if (ti + 2 < ntiles) step(ti + 2, IntC<2>{});
+    if (ti + 3 < ntiles) step(ti + 3, IntC<3>{});
   }
 
   // epilogue: o[hg][cb][i] = O[16 hg + lc][16 cb + 4 lg + i]; normalise,
@@ -766,7 +784,10 @@ mqa_dense_tokblock_kernel(
 hipError_t launch_mqa_prefill_bf16(const csa_attn_desc& d, int mode, const void* q, const void* win,
                                    const void* comp, const int32_t* idx, const float* sink,
                                    void* out, hipStream_t st) {
-  if (mode != ATTN_SPARSE && d.c == 128 && d.n_heads == 64) {  // HCA's shape
+  // HCA's shape; the kernel's per-tile row bounds are 32-bit, exact while the
+  // window and the entry count stay below 2^30
+  if (mode != ATTN_SPARSE && d.c == 128 && d.n_heads == 64 && d.n_entries < (1 << 30) &&
+      d.n_win < (1 << 30)) {
     const int64_t nblk = (d.n + kDenseTB - 1) / kDenseTB;
     mqa_dense_tokblock_kernel<128><<<(unsigned)(((nblk + 7) / 8) * 8), 64 * kDenseTB * 4 / kDenseHG, 0,
                                      st>>>(
