@@ -123,6 +123,136 @@ __global__ __launch_bounds__(256, 2) void proj_gemm_kernel(
 }
 
 // ===========================================================================
+// fp32 projection GEMM for narrow outputs (N <= kF32KSplitMaxN): a 64x64
+// output tile per 256-thread workgroup, so a short token range still spreads
+// over many CUs.  The four waves split each 32-wide K slice by k-group (wave
+// w takes floats 8w .. 8w+7 of every slice), so each wave holds the whole
+// tile as four 32x32 accumulator blocks (four independent matrix-core
+// chains); the partial tiles are then added through LDS in wave order, a
+// fixed order, so the result does not depend on M or on scheduling.  The
+// choice of kernel depends on N only, so a chunked prefill and a one-shot
+// prefill of the same weights sum every output in the same order.
+// ===========================================================================
+constexpr int kF32KSplitMaxN = 1024;
+
+__global__ __launch_bounds__(256) void proj_gemm_f32_ksplit_kernel(
+    const float* __restrict__ A, int64_t M, int K, const float* __restrict__ W0, int r0,
+    const float* __restrict__ W1, int r1, const float* __restrict__ W2, int r2,
+    float* __restrict__ out, int64_t ldo) {
+  constexpr int BM = 64, BN = 64, BKB = 128, BK = BKB / 4, LDB = BKB + 16;
+  // the K slices' double buffers, reused after the loop for the partial
+  // tiles of two waves at a time ([block * 16 + i][lane] floats each)
+  __shared__ __align__(16) uint8_t smem[2 * (BM + BN) * LDB];
+  static_assert(2 * 16 * 4 * 64 * 4 <= 2 * (BM + BN) * LDB, "two partial tiles fit");
+  uint8_t(*sA)[BM * LDB] = (uint8_t(*)[BM * LDB])smem;
+  uint8_t(*sB)[BN * LDB] = (uint8_t(*)[BN * LDB])(smem + 2 * BM * LDB);
+  float* red = (float*)smem;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t m0 = (int64_t)blockIdx.y * BM;
+  const int n0 = blockIdx.x * BN;
+  const int ntot = r0 + r1 + r2;
+
+  const float* a_ptr[2];
+  const float* b_ptr[2];
+  bool a_ok[2], b_ok[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int row = (tid >> 3) + 32 * q;
+    const int64_t gm = m0 + row;
+    a_ok[q] = gm < M;
+    a_ptr[q] = A + (a_ok[q] ? gm : 0) * (int64_t)K + (tid & 7) * 4;
+    const int j = n0 + row;
+    const float* wp = W0;
+    int jr = j;
+    if (jr >= r0) { jr -= r0; wp = W1; if (jr >= r1) { jr -= r1; wp = W2; } }
+    b_ok[q] = j < ntot;
+    b_ptr[q] = b_ok[q] ? wp + (int64_t)jr * K + (tid & 7) * 4 : W0;
+  }
+  uint4 ra[2], rb[2];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      ra[q] = a_ok[q] ? *(const uint4*)(a_ptr[q] + (int64_t)kt * BK) : make_uint4(0, 0, 0, 0);
+      rb[q] = b_ok[q] ? *(const uint4*)(b_ptr[q] + (int64_t)kt * BK) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int row = (tid >> 3) + 32 * q;
+      *(uint4*)(sA[buf] + row * LDB + (tid & 7) * 16) = ra[q];
+      *(uint4*)(sB[buf] + row * LDB + (tid & 7) * 16) = rb[q];
+    }
+  };
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
+  const int nk = K / BK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) gload(kt + 1);
+    const uint8_t* As = sA[kt & 1];
+    const uint8_t* Bs = sB[kt & 1];
+    uint4 a[2], b[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+      a[mb] = *(const uint4*)(As + (mb * 32 + (lane & 31)) * LDB + wave * 32 + (lane >> 5) * 16);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+      b[nb] = *(const uint4*)(Bs + (nb * 32 + (lane & 31)) * LDB + wave * 32 + (lane >> 5) * 16);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) mma32<F32>(acc[mb][nb], a[mb], b[nb]);
+    if (kt + 1 < nk) sstore((kt + 1) & 1);
+    __syncthreads();
+  }
+  // wave 0 adds the other waves' partial tiles in wave order: waves 1 and 2
+  // through the staging buffers, then wave 3 (the loop's last barrier has
+  // released them)
+  constexpr int PT = 16 * 4 * 64;  // floats of one partial tile
+  auto put = [&](int slot) {
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) red[slot * PT + (blk * 16 + i) * 64 + lane] = acc[blk >> 1][blk & 1][i];
+  };
+  auto add = [&](int slot) {
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[blk >> 1][blk & 1][i] += red[slot * PT + (blk * 16 + i) * 64 + lane];
+  };
+  if (wave == 1 || wave == 2) put(wave - 1);
+  __syncthreads();
+  if (wave == 0) {
+    add(0);
+    add(1);
+  }
+  __syncthreads();
+  if (wave == 3) put(0);
+  __syncthreads();
+  if (wave != 0) return;
+  add(0);
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) {
+    const int mb = blk >> 1, nb = blk & 1;
+    const int col = n0 + nb * 32 + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int64_t row = m0 + mb * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+      if (row < M && col < ntot) out[row * ldo + col] = acc[mb][nb][i];
+    }
+  }
+}
+
+// ===========================================================================
 // bf16 projection GEMM: TM x TN output tile per 512-thread workgroup, 4x2
 // waves of (TM/4) x (TN/2) (blocks of 32x32x16 MFMA; the 256x256 tile gives
 // each wave 2x4 blocks, 128 accumulators, two waves per SIMD).  A and W
@@ -758,6 +888,11 @@ hipError_t launch_proj_gemm(int dtype, const void* A, int64_t M, int K, const We
     o.p[2] = out + w.rows[0] + w.rows[1];
     o.ld[0] = o.ld[1] = o.ld[2] = ldo;
     return launch_gemm_bf16(A, K, M, K, w, o, false, 1, 0, 0, 0, st);
+  } else if (N <= kF32KSplitMaxN) {  // by N only: the same kernel for every M
+    const dim3 g64((N + 63) / 64, (unsigned)((M + 63) / 64));
+    proj_gemm_f32_ksplit_kernel<<<g64, 256, 0, st>>>((const float*)A, M, K, (const float*)w.w[0],
+                                                     w.rows[0], (const float*)w.w[1], w.rows[1],
+                                                     (const float*)w.w[2], w.rows[2], out, ldo);
   } else {
     proj_gemm_kernel<F32><<<grid, 256, 0, st>>>((const float*)A, M, K, (const float*)w.w[0],
                                                  w.rows[0], (const float*)w.w[1], w.rows[1],
