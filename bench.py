@@ -516,8 +516,10 @@ class HybridDecode:
         the current one); the scoring's stream then waits for the indexer
         compressor's, selects, waits for the CSA compressor's and runs the
         sparse attention; the current stream joins the others at the end.
-        The compressors are enqueued first, so that their projections start
-        with the step.  Each chain has its own workspaces.  With `kv8` the
+        The scoring is enqueued first (the compressors finish long before
+        their results are needed; in a graph the branch enqueued first starts
+        with the step, the others some microseconds later).  Each chain has
+        its own workspaces.  With `kv8` the
         attention reads FP8 rings and caches (make_kv8): each compressor's new
         bf16 row (window slot, and the entry when one is emitted) is converted
         into them by csa_kv_fp8_quant_decode on the compressor's stream."""
@@ -533,6 +535,10 @@ class HybridDecode:
             sd.wait_stream(main)
         else:
             sb = sc = sd = main
+        # the scoring first: it is the one chain without slack, and in a graph
+        # the branch enqueued first starts with the step
+        with torch.cuda.stream(sd):
+            L.csa_index_topk_decode_score(g["qI"], g["wI"], self.kcache, self.pos, m, c["k"])
         with torch.cuda.stream(sb):
             L.csa_compress_decode(self.h, self.pos, g["WI_kv"], g["WI_z"], g["apeI"], m, ov, self.sti,
                                   self.kcache, ws_slot="decode_proj_idx")
@@ -550,7 +556,6 @@ class HybridDecode:
             L.csa_kv_fp8_quant_decode(self.hcache, self.pos, self.kv8["hcache"], r, m=c["m_hca"])
             L.csa_kv_fp8_quant_decode(self.hring, self.pos, self.kv8["hring"], r, ring=True)
         with torch.cuda.stream(sd):
-            L.csa_index_topk_decode_score(g["qI"], g["wI"], self.kcache, self.pos, m, c["k"])
             if streams:
                 sd.wait_stream(sb)
             L.csa_index_topk_decode_select(g["qI"], g["wI"], self.kcache, self.pos, m, c["k"],

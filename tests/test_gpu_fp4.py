@@ -66,6 +66,7 @@ def test_fp4_quant_matches_oracle(lib, dtype, rows, W):
     (16, 64, 4, 512, 40000, [159999, 1000, 2047]),
     (8, 128, 4, 100, 7000, [27999, 450, 4000, 300]),
     (16, 64, 4, 1024, 262144, [1048575, 700000]),
+    (4, 128, 4, 64, 3001, [12003, 5, 4100, 9999]),  # 4 heads: half the head rows of each product empty
 ])
 def test_index_topk_decode_fp4(lib, hI, cI, m, k, ne, pos):
     _say("index decode fp4", hI, cI, m, k, ne, pos)
