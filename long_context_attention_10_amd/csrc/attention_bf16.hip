@@ -339,9 +339,11 @@ CSA_DEV void issue_tile_rows(uint8_t* base, int* vflags, int lane, int wave, int
 }
 
 // ---------------------------------------------------------------------------
-// Prefill: one workgroup per query token.  XCD-aware order: the 8 dies each
-// take a contiguous range of tokens, so a die's L2 keeps the window rows its
-// consecutive tokens share.  The first tile holds only window rows whenever
+// Prefill: one workgroup per query token.  XCD-aware order (workgroup b runs
+// on die b % 8): the tokens form 16 contiguous ranges and die x takes ranges
+// x and 15 - x, so a die's L2 keeps the window rows its consecutive tokens
+// share, and every die gets early tokens (fewer visible entries) and late
+// ones alike.  The first tile holds only window rows whenever
 // the window covers it; its gather then starts before the index row is in.
 // The running max starts at the sink logit and the running sum at 1, which
 // adds exp(sink) to the denominator exactly once.  The output goes through
@@ -367,8 +369,10 @@ __global__ __launch_bounds__(256, 2) void mqa_prefill_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int lc = lane & 15, lg = lane >> 4;
   const int head = wave * 16 + lc;
-  const int64_t per = (n + 7) >> 3;
-  const int64_t t = (int64_t)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  const int64_t per = (n + 15) >> 4;  // tokens per range
+  const int die = blockIdx.x & 7;
+  const int64_t bi = blockIdx.x >> 3;
+  const int64_t t = bi < per ? die * per + bi : (15 - die) * per + (bi - per);
   if (t >= n) return;
 
   // q rows first, so that the first tile's gather overlaps their load
@@ -525,11 +529,16 @@ mqa_dense_tokblock_kernel(
   const int tw = wave / WPT, hw = wave % WPT;  // token of the block; head range 16 HG hw ..
   const int h0 = 16 * HG * hw;
   const int lc = lane & 15, lg = lane >> 4;
-  // XCD-aware order: die x takes a contiguous range of blocks, whose window
-  // rows and entries its L2 keeps
+  // XCD-aware order: workgroup b runs on die b % 8.  The blocks form 16
+  // contiguous ranges and die x takes ranges x and 15 - x: a token's work
+  // grows with its position (its visible entries), so every die gets early
+  // and late tokens alike, and each range's window rows and entries stay in
+  // that die's L2
   const int64_t nblk = (n + kDenseTB - 1) / kDenseTB;
-  const int64_t per = (nblk + 7) >> 3;
-  const int64_t blk = (int64_t)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  const int64_t per = (nblk + 15) >> 4;  // blocks per range
+  const int die = blockIdx.x & 7;
+  const int64_t bi = blockIdx.x >> 3;
+  const int64_t blk = bi < per ? die * per + bi : (15 - die) * per + (bi - per);
   if (blk >= nblk) return;  // the whole workgroup
   const int64_t tb = blk * kDenseTB, tl = min64(tb + kDenseTB - 1, n - 1);
   const bool live = tb + tw < n;
@@ -789,14 +798,14 @@ hipError_t launch_mqa_prefill_bf16(const csa_attn_desc& d, int mode, const void*
   if (mode != ATTN_SPARSE && d.c == 128 && d.n_heads == 64 && d.n_entries < (1 << 30) &&
       d.n_win < (1 << 30)) {
     const int64_t nblk = (d.n + kDenseTB - 1) / kDenseTB;
-    mqa_dense_tokblock_kernel<128><<<(unsigned)(((nblk + 7) / 8) * 8), 64 * kDenseTB * 4 / kDenseHG, 0,
+    mqa_dense_tokblock_kernel<128><<<(unsigned)(((nblk + 15) / 16) * 16), 64 * kDenseTB * 4 / kDenseHG, 0,
                                      st>>>(
         (const uint16_t*)q, (const uint16_t*)win, (const uint16_t*)comp, sink, (uint16_t*)out,
         d.n, d.m, d.n_win, d.scale, d.qk_norm, d.eps, d.rope_dims, d.rope_theta, d.n_entries,
         d.t0);
     return hipGetLastError();
   }
-  const unsigned grid = (unsigned)(((d.n + 7) / 8) * 8);
+  const unsigned grid = (unsigned)(((d.n + 15) / 16) * 16);
 #define CSA_FAST(CC)                                                                          \
   if (d.c == CC) {                                                                           \
     if (mode == ATTN_SPARSE)                                                                 \
