@@ -458,6 +458,22 @@ int hca_dense_mqa_decode(const csa_attn_desc* desc, const void* q, const void* w
  * of the contiguous entry (CSA_ENTRY_COMPRESS_DECODE, _INDEX_TOPK_DECODE,
  * _SPARSE_MQA_DECODE, _DENSE_MQA_DECODE).
  * ---------------------------------------------------------------------- */
+/* csa_compress_prefill_paged -- csa_compress_prefill whose entries go
+ * straight into a page pool ([R] section 4.6: the classical cache is handed
+ * out in pages): entry e = pos0/m + i of the call (i < floor(n/m)) is
+ * written to pool row page_table[e / page_entries] * page_entries +
+ * e % page_entries, bit-identical to row i of the contiguous call's
+ * out_comp.  One sequence: page_table is its row [ceil(N / page_entries)]
+ * with N = desc->max_entries, and (pos0 + n) / m <= N (else
+ * CSA_ERR_INVALID_ARG).  The window rows, ring and state are those of the
+ * contiguous call; so is the workspace (CSA_ENTRY_COMPRESS_PREFILL).  Page
+ * ids are used as in the paged decode calls below (0 <= id < P, unchecked). */
+int csa_compress_prefill_paged(const csa_compress_desc* desc, const void* H, const void* W_kv,
+                               const void* W_z, const float* ape, const void* W_win,
+                               void* comp_pool, const int32_t* page_table,
+                               int32_t page_entries, void* out_win, void* win_ring, float* state,
+                               void* ws, size_t ws_bytes, void* stream);
+
 int csa_compress_decode_paged(const csa_compress_desc* desc, const void* h, const int64_t* pos,
                               const void* W_kv, const void* W_z, const float* ape,
                               const void* W_win, float* state, void* cache_pool,

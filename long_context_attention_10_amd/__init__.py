@@ -37,7 +37,8 @@ EXPORTED = ["csa_compress_prefill", "csa_compress_decode", "csa_state_bytes", "c
             "csa_index_topk_decode_score", "csa_index_topk_decode_select",
             "csa_sparse_mqa_backward", "hca_dense_mqa_backward", "csa_kv_fp8_row_bytes",
             "csa_kv_fp8_quant", "csa_kv_fp8_quant_decode", "csa_sparse_mqa_decode_fp8",
-            "hca_dense_mqa_decode_fp8", "csa_index_topk_prefill_fp4"]
+            "hca_dense_mqa_decode_fp8", "csa_index_topk_prefill_fp4",
+            "csa_compress_prefill_paged"]
 
 
 class CompressDesc(ctypes.Structure):
@@ -128,6 +129,7 @@ def load(path: str = LIB_PATH):
     lib.csa_indexer_fp4_quant_decode.argtypes = [P, P, ctypes.c_int64, P, I, P, P, P]
     I32 = ctypes.c_int32
     lib.csa_compress_decode_paged.argtypes = [P] * 10 + [I32] + [P] * 2 + [S, P]
+    lib.csa_compress_prefill_paged.argtypes = [P] * 8 + [I32] + [P] * 4 + [S, P]
     lib.csa_index_topk_decode_paged.argtypes = [P] * 5 + [I32] + [P] * 3 + [S, P]
     lib.csa_sparse_mqa_decode_paged.argtypes = [P] * 5 + [I32] + [P] * 5 + [S, P]
     lib.hca_dense_mqa_decode_paged.argtypes = [P] * 5 + [I32] + [P] * 4 + [S, P]
@@ -282,6 +284,40 @@ def csa_compress_prefill(H, W_kv, W_z, ape, m, overlap, W_win=None, qk_norm=True
                                   _stream(dev))
     _check(st, "csa_compress_prefill")
     return dict(comp=out_comp, win=out_win, ring=win_ring, state=state)
+
+
+def csa_compress_prefill_paged(H, W_kv, W_z, ape, m, overlap, comp_pool, page_table,
+                               page_entries, max_entries, W_win=None, qk_norm=True, eps=1e-6,
+                               rope_dims=0, rope_theta=10000.0, n_win=128, out_win=None,
+                               win_ring=None, state=None, ws_slot="default", pos0=0):
+    """csa_compress_prefill with the entries written into a page pool
+    comp_pool [P * page_entries, c] through one sequence's page table
+    [ceil(max_entries / page_entries)] int32; window rows, ring and state as
+    in csa_compress_prefill (given as tensors, or None)."""
+    lib = load()
+    n, d = H.shape
+    if overlap and pos0 > 0:
+        n -= m  # the halo rows are not new tokens
+    w = W_kv.shape[0]
+    c = w // (2 if overlap else 1)
+    _expect(W_kv, (w, d), H.dtype, "W_kv")
+    _expect(W_z, (w, d), H.dtype, "W_z")
+    _expect(ape, (m, w), torch.float32, "ape")
+    _expect(comp_pool, (comp_pool.shape[0], c), H.dtype, "comp_pool")
+    _expect(page_table, (page_table.shape[0],), torch.int32, "page_table")
+    if W_win is not None:
+        _expect(W_win, (c, d), H.dtype, "W_win")
+    desc = compress_desc(n=n, d=d, c=c, m=m, overlap=overlap, dtype=_dt(H), qk_norm=qk_norm,
+                         eps=eps, rope_dims=rope_dims, rope_theta=rope_theta, n_win=n_win,
+                         pos0=pos0, max_entries=max_entries)
+    dev = H.device
+    ws, wsb = workspace(workspace_bytes("compress_prefill", desc), dev, ws_slot)
+    st = lib.csa_compress_prefill_paged(ctypes.byref(desc), _ptr(H), _ptr(W_kv), _ptr(W_z),
+                                        _ptr(ape), _ptr(W_win), _ptr(comp_pool), _ptr(page_table),
+                                        page_entries, _ptr(out_win), _ptr(win_ring), _ptr(state),
+                                        _ptr(ws), wsb, _stream(dev))
+    _check(st, "csa_compress_prefill_paged")
+    return comp_pool
 
 
 def csa_compress_decode(h, pos, W_kv, W_z, ape, m, overlap, state, cache, W_win=None,

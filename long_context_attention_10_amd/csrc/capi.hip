@@ -301,10 +301,12 @@ int csa_state_init(const csa_compress_desc* d, float* state, void* stream) {
   return hip_status(launch_state_init(state, per, d->batch, d->c, (hipStream_t)stream));
 }
 
-int csa_compress_prefill(const csa_compress_desc* d, const void* H, const void* W_kv,
-                         const void* W_z, const float* ape, const void* W_win, void* out_comp,
-                         void* out_win, void* win_ring, float* state, void* ws, size_t ws_bytes,
-                         void* stream) {
+// The prefill compressor; with em.table the entries go to pool rows of one
+// sequence's page table instead of consecutive rows of out_comp.
+static int compress_prefill(const csa_compress_desc* d, const void* H, const void* W_kv,
+                     const void* W_z, const float* ape, const void* W_win, void* out_comp,
+                     void* out_win, void* win_ring, float* state, void* ws, size_t ws_bytes,
+                     void* stream, EntryMap em) {
   int s = check_compress(d, false);
   if (s) return s;
   const bool has_win = W_win != nullptr;
@@ -327,7 +329,7 @@ int csa_compress_prefill(const csa_compress_desc* d, const void* H, const void* 
     if (e != hipSuccess) return CSA_ERR_HIP;
     e = launch_pool_entries(d->dtype, Pn, ld, d->n, d->c, d->m, d->overlap, ape, d->qk_norm,
                             d->eps, d->rope_dims, d->rope_theta, out_comp, d->pos0, st,
-                            halo > 0);
+                            halo > 0, em);
     if (e != hipSuccess) return CSA_ERR_HIP;
     if (has_win && (out_win || win_ring)) {
       e = launch_window_rows(d->dtype, Pn, ld, 2 * w, d->n, d->c, d->qk_norm, d->eps,
@@ -349,6 +351,30 @@ int csa_compress_decode(const csa_compress_desc* d, const void* h, const int64_t
                         void* stream) {
   return compress_decode(d, h, pos, W_kv, W_z, ape, W_win, state, cache, win_ring, ws, ws_bytes,
                          stream, EntryMap());
+}
+
+int csa_compress_prefill(const csa_compress_desc* d, const void* H, const void* W_kv,
+                         const void* W_z, const float* ape, const void* W_win, void* out_comp,
+                         void* out_win, void* win_ring, float* state, void* ws, size_t ws_bytes,
+                         void* stream) {
+  return compress_prefill(d, H, W_kv, W_z, ape, W_win, out_comp, out_win, win_ring, state, ws,
+                          ws_bytes, stream, EntryMap());
+}
+
+int csa_compress_prefill_paged(const csa_compress_desc* d, const void* H, const void* W_kv,
+                               const void* W_z, const float* ape, const void* W_win,
+                               void* comp_pool, const int32_t* page_table,
+                               int32_t page_entries, void* out_win, void* win_ring, float* state,
+                               void* ws, size_t ws_bytes, void* stream) {
+  if (!d) return CSA_ERR_INVALID_ARG;
+  EntryMap em;
+  int s = entry_map(page_table, page_entries, d->max_entries, &em);
+  if (s) return s;
+  // the chunk's entries pos0/m .. (pos0+n)/m - 1 must lie within the table
+  if (d->m > 0 && d->n >= 0 && d->pos0 >= 0 && (d->pos0 + d->n) / d->m > d->max_entries)
+    return CSA_ERR_INVALID_ARG;
+  return compress_prefill(d, H, W_kv, W_z, ape, W_win, comp_pool, out_win, win_ring, state, ws,
+                          ws_bytes, stream, em);
 }
 
 int csa_compress_decode_paged(const csa_compress_desc* d, const void* h, const int64_t* pos,

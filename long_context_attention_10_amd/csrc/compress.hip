@@ -502,9 +502,10 @@ template <class T, int G>
 __global__ __launch_bounds__(256) void pool_entries_kernel(
     const float* __restrict__ P, int64_t ld, int64_t n_entries, int c, int m, int ov,
     const float* __restrict__ ape, int qk_norm, float eps, int r, float theta,
-    typename T::S* __restrict__ out, int64_t pos0, int prev0) {
+    typename T::S* __restrict__ out, int64_t pos0, int prev0, EntryMap em) {
   // prev0: the m rows before P hold block -1 (a chunk's halo), whose
-  // b-series joins entry 0 under overlap
+  // b-series joins entry 0 under overlap.  Entry i of the call is entry
+  // pos0 / m + i of the sequence: row i of out, or its pool row under em.
   __shared__ float red[4];
   constexpr int GPW = 256 / G;
   const int g = threadIdx.x / G, j = threadIdx.x % G;
@@ -538,8 +539,9 @@ __global__ __launch_bounds__(256) void pool_entries_kernel(
   }
   row_finish<T, G>(v0, v1, j, c, (int64_t)m * (pos0 / m + i), qk_norm, eps, r, theta, red);
   if (live) {
-    T::st(out, i * c + 2 * j, v0);
-    T::st(out, i * c + 2 * j + 1, v1);
+    const int64_t orow = em.table ? em.row(0, pos0 / m + i, 0) : i;
+    T::st(out, orow * c + 2 * j, v0);
+    T::st(out, orow * c + 2 * j + 1, v1);
   }
 }
 
@@ -556,7 +558,7 @@ template <class T, int G>
 __global__ __launch_bounds__(256) void pool_entries_split_kernel(
     const float* __restrict__ P, int64_t ld, int64_t n_entries, int c, int m, int ov,
     const float* __restrict__ ape, int qk_norm, float eps, int r, float theta,
-    typename T::S* __restrict__ out, int64_t pos0, int prev0) {
+    typename T::S* __restrict__ out, int64_t pos0, int prev0, EntryMap em) {
   constexpr int S = 256 / G;
   __shared__ float red[4];
   __shared__ float st[S][6][G];  // (max, sum, acc) of both channels, per group
@@ -591,8 +593,9 @@ __global__ __launch_bounds__(256) void pool_entries_split_kernel(
   float v0 = a0 / s0, v1 = a1 / s1;
   row_finish<T, G>(v0, v1, j, c, (int64_t)m * (pos0 / m + i), qk_norm, eps, r, theta, red);
   if (g == 0) {
-    T::st(out, i * c + 2 * j, v0);
-    T::st(out, i * c + 2 * j + 1, v1);
+    const int64_t orow = em.table ? em.row(0, pos0 / m + i, 0) : i;
+    T::st(out, orow * c + 2 * j, v0);
+    T::st(out, orow * c + 2 * j + 1, v1);
   }
 }
 
@@ -913,25 +916,26 @@ hipError_t launch_proj_gemm(int dtype, const void* A, int64_t M, int K, const We
 
 hipError_t launch_pool_entries(int dtype, const float* P, int64_t ld, int64_t n, int c, int m,
                                int ov, const float* ape, int qk_norm, float eps, int r,
-                               float theta, void* out, int64_t pos0, hipStream_t st, int prev0) {
+                               float theta, void* out, int64_t pos0, hipStream_t st, int prev0,
+                               EntryMap em) {
   const int64_t ne = n / m;
   if (ne == 0) return hipSuccess;
   CSA_DISPATCH_G(c, {
     if (m >= kPoolSplitM) {  // a choice by m alone: chunks and one-shot calls agree
       if (dtype == CSA_BF16)
         pool_entries_split_kernel<BF16, G><<<(unsigned)ne, 256, 0, st>>>(
-            P, ld, ne, c, m, ov, ape, qk_norm, eps, r, theta, (BF16::S*)out, pos0, prev0);
+            P, ld, ne, c, m, ov, ape, qk_norm, eps, r, theta, (BF16::S*)out, pos0, prev0, em);
       else
         pool_entries_split_kernel<F32, G><<<(unsigned)ne, 256, 0, st>>>(
-            P, ld, ne, c, m, ov, ape, qk_norm, eps, r, theta, (float*)out, pos0, prev0);
+            P, ld, ne, c, m, ov, ape, qk_norm, eps, r, theta, (float*)out, pos0, prev0, em);
     } else {
       dim3 grid((unsigned)((ne + 256 / G - 1) / (256 / G)));
       if (dtype == CSA_BF16)
         pool_entries_kernel<BF16, G><<<grid, 256, 0, st>>>(P, ld, ne, c, m, ov, ape, qk_norm, eps,
-                                                           r, theta, (BF16::S*)out, pos0, prev0);
+                                                           r, theta, (BF16::S*)out, pos0, prev0, em);
       else
         pool_entries_kernel<F32, G><<<grid, 256, 0, st>>>(P, ld, ne, c, m, ov, ape, qk_norm, eps,
-                                                          r, theta, (float*)out, pos0, prev0);
+                                                          r, theta, (float*)out, pos0, prev0, em);
     }
   });
   return hipGetLastError();

@@ -39,10 +39,12 @@ hipError_t launch_proj_gemm(int dtype, const void* A, int64_t M, int K, const We
 // Pool complete blocks of a projected scratch [n, ld] (C at col 0, Z at col w)
 // into entries, apply the epilogue and store.  Row 0 of P is position pos0;
 // prev0: P[-m, 0) holds the previous block (its b-series joins entry 0).
+// With em.table, entry i goes to the pool row of entry pos0 / m + i of one
+// sequence; otherwise to row i of out.
 hipError_t launch_pool_entries(int dtype, const float* P, int64_t ld, int64_t n, int c, int m,
                                int ov, const float* ape, int qk_norm, float eps, int rope_dims,
                                float theta, void* out, int64_t pos0, hipStream_t st,
-                               int prev0 = 0);
+                               int prev0 = 0, EntryMap em = EntryMap());
 
 // Window rows from scratch column `col` (width c) -> out [n, c] and/or ring.
 hipError_t launch_window_rows(int dtype, const float* P, int64_t ld, int col, int64_t n, int c,

@@ -281,6 +281,26 @@ def test_paged_calls_reject(lib):
                                           _p(), _p(), 8, None) == -3
 
 
+def test_compress_prefill_paged_rejects(lib):
+    """The paged prefill compressor rejects a missing page table, a page
+    size below one, a chunk whose entries pass max_entries, a capacity past
+    32-bit entry numbers and a missing descriptor, before anything is
+    enqueued."""
+    f = lib.csa_compress_prefill_paged
+    args = [_p()] * 6  # H, W_kv, W_z, ape, W_win, comp_pool
+    tail = [None, None, None, _p(), 1 << 40, None]  # out_win, ring, state, ws, ws_bytes, stream
+    pd = L.compress_desc(n=64, d=128, c=128, m=4, max_entries=16)
+    assert f(ctypes.byref(pd), *args, None, 32, *tail) == -1
+    assert f(ctypes.byref(pd), *args, _p(), 0, *tail) == -1
+    small = L.compress_desc(n=64, d=128, c=128, m=4, max_entries=15)  # 16 entries
+    assert f(ctypes.byref(small), *args, _p(), 32, *tail) == -1
+    chunk = L.compress_desc(n=64, d=128, c=128, m=4, max_entries=19, pos0=16)  # entries 4 .. 19
+    assert f(ctypes.byref(chunk), *args, _p(), 32, *tail) == -1
+    big = L.compress_desc(n=64, d=128, c=128, m=4, max_entries=1 << 31)
+    assert f(ctypes.byref(big), *args, _p(), 32, *tail) == -2
+    assert f(None, *args, _p(), 32, *tail) == -1
+
+
 def test_fp4_paged_calls_reject(lib):
     """The two FP4 paged calls reject a missing page table, a page size below
     one, a capacity past 32-bit entry numbers and missing pools, before

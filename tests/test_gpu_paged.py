@@ -287,3 +287,45 @@ def test_fp4_indexer_paged(lib):
     torch.cuda.synchronize()
     assert torch.equal(_gather(cpool, table, page, ne), kc)
     assert torch.equal(_gather(epool, table, page, ne), ke)
+
+
+@pytest.mark.parametrize("dtype,d,c,m,ov,r,N,cuts,page", [
+    ("bf16", 256, 128, 4, 1, 64, 1000, [0, 256, 700], 32),  # chunks with the overlap halo, RoPE
+    ("f32", 128, 64, 4, 0, 0, 517, [0], 8),                  # one shot, ragged tail
+    ("bf16", 256, 128, 128, 0, 0, 2100, [0, 1024], 1),       # m = 128 (split pooling), 1 entry a page
+])
+def test_compress_prefill_paged(lib, dtype, d, c, m, ov, r, N, cuts, page):
+    """A (chunked) prefill writing its entries straight into a shuffled page
+    pool: each chunk's pool rows equal, bit for bit, the entries of the
+    contiguous call on the same rows, and every other pool row keeps its NaN
+    fill (pages outside the table, and the table's slots past the last
+    entry)."""
+    _say("compress_prefill_paged", dtype, d, c, m, ov, r, N, cuts, page)
+    key = ("pfx_paged", dtype, d, c, m, ov, N)
+    w = (1 + ov) * c
+    H = I.normal((N, d), key + ("H",), dtype=dtype, device=DEV)
+    Wkv = I.normal((w, d), key + ("Wkv",), std=d ** -0.5, dtype=dtype, device=DEV)
+    Wz = I.normal((w, d), key + ("Wz",), std=d ** -0.5, dtype=dtype, device=DEV)
+    Ww = I.normal((c, d), key + ("Ww",), std=d ** -0.5, dtype=dtype, device=DEV)
+    ape = I.normal((m, w), key + ("ape",), device=DEV)
+    ne = N // m
+    npg = -(-ne // page)
+    P = npg + 3
+    ids = np.random.default_rng(I.key_seed(*key, "pages") % 2 ** 32).permutation(P)
+    table = torch.from_numpy(ids[:npg].astype(np.int32)).to(DEV)
+    pool = torch.full((P * page, c), float("nan"), dtype=H.dtype, device=DEV)
+    written = torch.zeros(P * page, dtype=torch.bool, device=DEV)
+    bounds = cuts + [N]
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        h0 = a - m if ov and a > 0 else a
+        ref = lib.csa_compress_prefill(H[h0:b], Wkv, Wz, ape, m, ov, W_win=Ww, rope_dims=r,
+                                       pos0=a, ws_slot="paged_ref")
+        lib.csa_compress_prefill_paged(H[h0:b], Wkv, Wz, ape, m, ov, pool, table, page, ne,
+                                       W_win=Ww, rope_dims=r, pos0=a, ws_slot="paged_new")
+        torch.cuda.synchronize()
+        e = torch.arange(a // m, b // m, device=DEV)
+        rows = table.long()[e // page] * page + e % page
+        assert _same_bits(pool[rows], ref["comp"]), f"chunk [{a}, {b})"
+        written[rows] = True
+    assert torch.isnan(pool[~written].float()).all(), "a row outside the entries was written"
+    assert int(written.sum()) == ne
