@@ -224,9 +224,9 @@ int csa_state_init(const csa_compress_desc* desc, float* state, void* stream);
  *   idx_out [n, k]       int32
  * With t0 > 0 (a chunk of a chunked prefill) row t is the token at position
  * t0 + t and sees s < floor((t0+t+1)/m).  When the last row sees more than
- * 16384 entries the rows are selected by the decode top-k, in batches of
- * rows sharing KI (same result definition; fp32 scores only, else
- * CSA_ERR_UNSUPPORTED).
+ * 16384 entries, batches of rows are scored by the same scorer into score
+ * rows in the workspace and selected by the decode top-k's selector (same
+ * result definition; fp32 scores only, else CSA_ERR_UNSUPPORTED).
  */
 int csa_index_topk_prefill(const csa_index_desc* desc, const void* qI, const void* wI,
                            const void* KI, int32_t* idx_out, void* ws, size_t ws_bytes,

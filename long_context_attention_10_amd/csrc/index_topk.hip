@@ -1598,6 +1598,30 @@ __global__ void long_rows_prep_kernel(int64_t* __restrict__ pos, int64_t first, 
   if (i == 0) table[0] = 0;
 }
 
+// Candidates of one (row, chunk) from stored scores: the chunk-local
+// selection of dec_score_kernel without its scoring, for rows whose scores
+// the prefill scorer wrote into the decode workspace (row stride
+// n_entries, every visible entry scored).
+__global__ __launch_bounds__(256) void dec_cand_from_scores_kernel(
+    const float* __restrict__ scores, const int64_t* __restrict__ posv, int64_t n_entries, int m,
+    int k, uint2* __restrict__ cand, uint4* __restrict__ cmeta, int L, int64_t nch) {
+  __shared__ uint32_t ls[kDecChunk];
+  __shared__ int hist[256];
+  __shared__ int sh[8];
+  __shared__ int res[2];
+  const int b = blockIdx.y;
+  const int64_t c0 = (int64_t)blockIdx.x * kDecChunk;
+  const int64_t vis = min64((posv[b] + 1) / m, n_entries);
+  if (vis <= k) return;  // everything visible is selected
+  if (c0 >= vis) return;
+  const int64_t c1 = min64(c0 + kDecChunk, vis);
+  const float* sc = scores + (int64_t)b * n_entries;
+  for (int i = threadIdx.x; i < (int)(c1 - c0); i += 256) ls[i] = float_key(sc[c0 + i]);
+  __syncthreads();
+  const int64_t slot = (int64_t)b * nch + blockIdx.x;
+  chunk_candidates(ls, (int)(c1 - c0), L, c0, hist, sh, res, cand + slot * L, cmeta + slot);
+}
+
 static csa_index_desc long_rows_desc(const csa_index_desc& d) {
   csa_index_desc dd = d;
   const int64_t last = (d.t0 + d.n) / d.m;  // visible entries of the last row
@@ -1637,9 +1661,33 @@ hipError_t launch_index_topk_prefill_long(const csa_index_desc& d, const void* q
     long_rows_prep_kernel<<<(db.batch + 255) / 256, 256, 0, st>>>(pos, d.t0 + r0, db.batch, table);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = launch_index_topk_decode(db, (const uint8_t*)qI + r0 * d.n_heads * d.head_dim * es,
-                                 (const uint8_t*)wI + r0 * d.n_heads * es, KI, pos,
-                                 idx_out + r0 * d.k, ws, st, em);
+    const uint8_t* qb = (const uint8_t*)qI + r0 * d.n_heads * d.head_dim * es;
+    const uint8_t* wb = (const uint8_t*)wI + r0 * d.n_heads * es;
+    // the batch's scores by the prefill scorer (every visible entry, the
+    // decode workspace's rows of stride n_entries), then each chunk's
+    // candidates, then the per-row selection over them
+    DecWs w = carve(ws, db);
+    csa_index_desc ds = d;
+    ds.n = db.batch;
+    ds.t0 = d.t0 + r0;
+    ds.n_entries = dd.n_entries;
+    ds.score_dtype = CSA_F32;
+    e = launch_index_scores_prefill(ds, qb, wb, KI, w.scores, dd.n_entries, st);
+    if (e != hipSuccess) return e;
+    const int64_t nch = dec_chunks(db);
+    const int L = dec_cand_per_chunk(db);
+    dec_cand_from_scores_kernel<<<dim3((unsigned)nch, (unsigned)db.batch), 256, 0, st>>>(
+        w.scores, pos, db.n_entries, db.m, db.k, w.cand, w.cmeta, L, nch);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    CSA_INDEX_DISPATCH(d.n_heads, d.head_dim, {
+      if (d.dtype == CSA_BF16)
+        e = dec_select<BF16, HI, CI, false>(db, w, nch, L, pos, idx_out + r0 * d.k, qb, wb, KI,
+                                            em, st);
+      else
+        e = dec_select<F32, HI, CI, false>(db, w, nch, L, pos, idx_out + r0 * d.k, qb, wb, KI,
+                                           em, st);
+    });
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -79,3 +79,40 @@ def test_decode_selector_offsets_at_long_rows():
     cand = B * chunks * per * 8
     meta = B * chunks * 16
     assert scores + cand + meta <= total
+
+
+def long_path_batches(n, n_entries, m, t0, rows_per_batch):
+    """The long-row selection's sub-batches as its launcher forms them: rows
+    r0 .. r0 + R - 1 at positions t0 + r0 .., scored by the prefill scorer
+    into the decode workspace's score rows (stride = the entries the last row
+    of the chunk sees)."""
+    ne = min((t0 + n) // m, n_entries)
+    for r0 in range(0, n, rows_per_batch):
+        yield min(rows_per_batch, n - r0), t0 + r0, ne
+
+
+@pytest.mark.parametrize("name,n,n_entries,m,hI,cI,t0,rows", [
+    ("chunk of 8192 ending 1M, 16 heads", 8192, 262144, 4, 16, 64, (1 << 20) - 8192, 1024),
+    ("chunk of 8192 ending 1M, 4 heads", 8192, 262144, 4, 4, 128, (1 << 20) - 8192, 1024),
+    ("chunk crossing 16384 entries", 700, 20000, 4, 16, 64, 65000, 700),
+    ("ragged last batch", 3000, 100000, 4, 8, 64, 390000, 1024),
+])
+def test_long_path_scorer_indices_in_bounds(name, n, n_entries, m, hI, cI, t0, rows):
+    """Each sub-batch of the long-row selection runs the prefill scorer with
+    the decode workspace's unpadded score stride: every index stays inside
+    the batch's score rows, key table, query rows and weights, and every
+    32-bit offset below 2^31."""
+    TQ = ROWS_PER_WG // hI
+    for R, t0b, ne in long_path_batches(n, n_entries, m, t0, rows):
+        ld = ne
+        assert TQ * ld < 2 ** 31
+        w = prefill_scorer_extremes(R, ne, m, hI, cI, t0b, ld)
+        assert w["score_off32"] < 2 ** 31, name
+        assert w["score_elem"] < R * ld, name  # the carved score region: R rows of ne
+        assert w["key_row"] < ne <= n_entries, name
+        assert w["q_elem"] < R * hI * cI, name
+        assert w["w_elem"] < R * hI, name
+        # candidates from the stored scores: row b reads s < vis(b) <= ne
+        for b in (0, R - 1):
+            vis = min((t0b + b + 1) // m, ne)
+            assert b * ne + vis - 1 < R * ld
