@@ -1598,28 +1598,164 @@ __global__ void long_rows_prep_kernel(int64_t* __restrict__ pos, int64_t first, 
   if (i == 0) table[0] = 0;
 }
 
-// Candidates of one (row, chunk) from stored scores: the chunk-local
-// selection of dec_score_kernel without its scoring, for rows whose scores
-// the prefill scorer wrote into the decode workspace (row stride
-// n_entries, every visible entry scored).
+// Wave-level scans and reductions over the 64 lanes.
+CSA_DEV int wave_excl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  return x - v;
+}
+CSA_DEV uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return v;
+}
+CSA_DEV uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return v;
+}
+
+// chunk_candidates for one wave and no barriers: the chunk's c <= 1024 keys
+// in registers, lane l holding entries 16l .. 16l+15 (so lane-major order is
+// index order).  The L-th best key is found by the same radix over the bits
+// below the keys' common prefix, each 8-bit digit from a histogram of this
+// wave's own 256 LDS ints; the output (cand in index order, meta) is
+// chunk_candidates' exactly.
+CSA_DEV void chunk_candidates_wave(const uint32_t (&key)[16], int c, int L, int64_t c0,
+                                   int* hist, uint2* __restrict__ cand, uint4* __restrict__ meta) {
+  const int lane = threadIdx.x & 63;
+  uint32_t V = 0;
+  int take = 0;
+  if (c > L) {
+    uint32_t kmax = 0, kmin = 0xffffffffu;
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (16 * lane + u < c) { kmax = max(kmax, key[u]); kmin = min(kmin, key[u]); }
+    kmax = wave_max_u32(kmax);
+    kmin = wave_min_u32(kmin);
+    int hi = kmax == kmin ? -1 : 31 - __builtin_clz(kmax ^ kmin);  // highest undecided bit
+    uint32_t mask = hi >= 31 ? 0u : ~((2u << hi) - 1u);
+    uint32_t prefix = kmax & mask;
+    int need = L;
+    while (hi >= 0) {
+      const int lo = hi >= 7 ? hi - 7 : 0;
+      const uint32_t dm = (2u << (hi - lo)) - 1u;
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // last pass's reads are done
+#pragma unroll
+      for (int b = 0; b < 4; ++b) hist[4 * lane + b] = 0;
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (16 * lane + u < c && (key[u] & mask) == prefix)
+          __hip_atomic_fetch_add(&hist[(key[u] >> lo) & dm], 1, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_WAVEFRONT);
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      int h[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) h[b] = hist[4 * lane + b];
+      // the digit d with (#keys above d) < need <= (#keys at or above d):
+      // suffix sums over lanes from the top bins down
+      const int c4 = h[0] + h[1] + h[2] + h[3];
+      int suf = c4;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_down(suf, o, 64);
+        if (lane + o < 64) suf += y;
+      }
+      const int above = suf - c4;  // keys in the bins of higher lanes
+      int dig = -1, abv = 0;
+      if (above < need && suf >= need) {
+        int acc = above;
+        for (int b = 3; b >= 0; --b) {
+          if (acc + h[b] >= need) { dig = 4 * lane + b; abv = acc; break; }
+          acc += h[b];
+        }
+      }
+      const int src = __ffsll((long long)__ballot(dig >= 0)) - 1;  // exactly one lane
+      const int d = __shfl(dig, src, 64);
+      need -= __shfl(abv, src, 64);
+      prefix |= (uint32_t)d << lo;
+      mask |= dm << lo;
+      hi = lo - 1;
+    }
+    V = prefix;
+    take = need;
+  }
+  int nt = 0;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) nt += (c > L && 16 * lane + u < c && key[u] == V);
+  int tr = wave_excl_scan(nt);  // tie ranks in index order
+  bool keep[16];
+  int nk = 0, lth = -1;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int i = 16 * lane + u;
+    bool kp = i < c;
+    if (c > L && kp) {
+      if (key[u] == V) {
+        kp = tr < take;
+        if (tr == take - 1) lth = i;
+        ++tr;
+      } else {
+        kp = key[u] > V;
+      }
+    }
+    keep[u] = kp;
+    nk += kp;
+  }
+  int off = wave_excl_scan(nk);
+#pragma unroll
+  for (int u = 0; u < 16; ++u)
+    if (keep[u]) cand[off++] = make_uint2(key[u], (uint32_t)(c0 + 16 * lane + u));
+  if (c <= L) {
+    if (lane == 0) *meta = make_uint4((uint32_t)c, 0u, 0u, 0u);
+  } else if (lth >= 0) {
+    *meta = make_uint4((uint32_t)L, 1u, V, (uint32_t)(c0 + lth));
+  }
+}
+
+// Candidates of (row, chunk)s from stored scores: the chunk-local selection
+// of dec_score_kernel without its scoring, for rows whose scores the prefill
+// scorer wrote into the decode workspace (row stride n_entries, every
+// visible entry scored).  Each wave takes one chunk of one row, four chunks
+// per workgroup.
 __global__ __launch_bounds__(256) void dec_cand_from_scores_kernel(
     const float* __restrict__ scores, const int64_t* __restrict__ posv, int64_t n_entries, int m,
     int k, uint2* __restrict__ cand, uint4* __restrict__ cmeta, int L, int64_t nch) {
-  __shared__ uint32_t ls[kDecChunk];
-  __shared__ int hist[256];
-  __shared__ int sh[8];
-  __shared__ int res[2];
+  __shared__ int hist[4][256];
   const int b = blockIdx.y;
-  const int64_t c0 = (int64_t)blockIdx.x * kDecChunk;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t ch = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t c0 = ch * kDecChunk;
   const int64_t vis = min64((posv[b] + 1) / m, n_entries);
   if (vis <= k) return;  // everything visible is selected
-  if (c0 >= vis) return;
-  const int64_t c1 = min64(c0 + kDecChunk, vis);
-  const float* sc = scores + (int64_t)b * n_entries;
-  for (int i = threadIdx.x; i < (int)(c1 - c0); i += 256) ls[i] = float_key(sc[c0 + i]);
-  __syncthreads();
-  const int64_t slot = (int64_t)b * nch + blockIdx.x;
-  chunk_candidates(ls, (int)(c1 - c0), L, c0, hist, sh, res, cand + slot * L, cmeta + slot);
+  if (ch >= nch || c0 >= vis) return;  // the whole wave
+  const int c = (int)(min64(c0 + kDecChunk, vis) - c0);
+  const float* sc = scores + (int64_t)b * n_entries + c0;
+  uint32_t key[16];
+  if (16 * lane + 16 <= c && (n_entries & 3) == 0) {  // four 16-byte loads
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 v = *(const float4*)(sc + 16 * lane + 4 * q);
+      key[4 * q] = float_key(v.x);
+      key[4 * q + 1] = float_key(v.y);
+      key[4 * q + 2] = float_key(v.z);
+      key[4 * q + 3] = float_key(v.w);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int i = 16 * lane + u;
+      key[u] = i < c ? float_key(sc[i]) : 0u;
+    }
+  }
+  const int64_t slot = (int64_t)b * nch + ch;
+  chunk_candidates_wave(key, c, L, c0, hist[wave], cand + slot * L, cmeta + slot);
 }
 
 static csa_index_desc long_rows_desc(const csa_index_desc& d) {
@@ -1676,7 +1812,7 @@ hipError_t launch_index_topk_prefill_long(const csa_index_desc& d, const void* q
     if (e != hipSuccess) return e;
     const int64_t nch = dec_chunks(db);
     const int L = dec_cand_per_chunk(db);
-    dec_cand_from_scores_kernel<<<dim3((unsigned)nch, (unsigned)db.batch), 256, 0, st>>>(
+    dec_cand_from_scores_kernel<<<dim3((unsigned)((nch + 3) / 4), (unsigned)db.batch), 256, 0, st>>>(
         w.scores, pos, db.n_entries, db.m, db.k, w.cand, w.cmeta, L, nch);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
