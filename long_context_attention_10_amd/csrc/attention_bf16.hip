@@ -271,14 +271,17 @@ template <int C>
 CSA_DEV void q_prologue(const uint4* qraw, bf16x8_t* qf, const float2* rtab, int qk_norm, float eps,
                         int r, int lg) {
   constexpr int NKG = C / 32;
-  float ss = 0.f;
+  // eight independent sums (one per chunk position), so that the squares do
+  // not form one dependent chain of C / 4 fma
+  float s8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int g = 0; g < NKG; ++g) {
     float v[8];
     chunk_to_f32<BF16>(qraw[g], v);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+    for (int e = 0; e < 8; ++e) s8[e] = fmaf(v[e], v[e], s8[e]);
   }
+  float ss = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
   ss = xlane_sum(ss);
   const float inv = qk_norm ? rsqrtf(ss / (float)C + eps) : 1.f;
 #pragma unroll
