@@ -508,37 +508,40 @@ class HybridDecode:
 
     def step(self, streams=True, kv8=False):
         """One decode step.  Its chains are independent until the sparse
-        attention: (scoring of the cached indexer keys, indexer compressor ->
-        selection), (CSA compressor) and (HCA compressor -> dense attention).
-        The scoring reads only keys that precede this step, so it starts with
-        the step.  With `streams` the scoring and the CSA compressor each
-        have a forked stream and the HCA chain runs on the current one; the
-        scoring's stream then runs the indexer compressor and the selection
-        (so that the selection waits on no other stream: in a graph a wait
-        across streams costs several microseconds, consecutive kernels of one
-        stream none), waits for the CSA compressor's stream and runs the
+        attention: (indexer compressor -> selection), (scoring of the cached
+        indexer keys -> selection), (CSA compressor) and (HCA compressor ->
+        dense attention).  The scoring reads only keys that precede this
+        step, so it starts with the step, beside the compressors.  With
+        `streams` each compressor has a forked stream (the HCA chain runs on
+        the current one); the scoring's stream then waits for the indexer
+        compressor's, selects, waits for the CSA compressor's and runs the
         sparse attention; the current stream joins the others at the end.
-        The scoring is enqueued first (in a graph the branch enqueued first
-        starts with the step, the others some microseconds later).  Each
-        chain has its own workspaces.  With `kv8` the attention reads FP8
-        rings and caches (make_kv8): each compressor's new bf16 row (window
-        slot, and the entry when one is emitted) is converted into them by
-        csa_kv_fp8_quant_decode on the compressor's stream."""
+        The scoring is enqueued first (the compressors finish long before
+        their results are needed; in a graph the branch enqueued first starts
+        with the step, the others some microseconds later).  Each chain has
+        its own workspaces.  With `kv8` the
+        attention reads FP8 rings and caches (make_kv8): each compressor's new
+        bf16 row (window slot, and the entry when one is emitted) is converted
+        into them by csa_kv_fp8_quant_decode on the compressor's stream."""
         c, g = self.cfg, self.g
         m, ov, r = c["m"], c["overlap"], c["rope_dims"]
         main = torch.cuda.current_stream()
         if streams:
             if self.side is None or len(self.side) < 3:
                 self.side = (torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream())
-            sc, sd = self.side[1], self.side[2]
+            sb, sc, sd = self.side
+            sb.wait_stream(main)
             sc.wait_stream(main)
             sd.wait_stream(main)
         else:
-            sc = sd = main
+            sb = sc = sd = main
         # the scoring first: it is the one chain without slack, and in a graph
         # the branch enqueued first starts with the step
         with torch.cuda.stream(sd):
             L.csa_index_topk_decode_score(g["qI"], g["wI"], self.kcache, self.pos, m, c["k"])
+        with torch.cuda.stream(sb):
+            L.csa_compress_decode(self.h, self.pos, g["WI_kv"], g["WI_z"], g["apeI"], m, ov, self.sti,
+                                  self.kcache, ws_slot="decode_proj_idx")
         with torch.cuda.stream(sc):
             L.csa_compress_decode(self.h, self.pos, g["csa_Wkv"], g["csa_Wz"], g["csa_ape"], m, ov,
                                   self.st, self.cache, W_win=g["csa_Wwin"], win_ring=self.ring,
@@ -553,8 +556,8 @@ class HybridDecode:
             L.csa_kv_fp8_quant_decode(self.hcache, self.pos, self.kv8["hcache"], r, m=c["m_hca"])
             L.csa_kv_fp8_quant_decode(self.hring, self.pos, self.kv8["hring"], r, ring=True)
         with torch.cuda.stream(sd):
-            L.csa_compress_decode(self.h, self.pos, g["WI_kv"], g["WI_z"], g["apeI"], m, ov, self.sti,
-                                  self.kcache, ws_slot="decode_proj_idx")
+            if streams:
+                sd.wait_stream(sb)
             L.csa_index_topk_decode_select(g["qI"], g["wI"], self.kcache, self.pos, m, c["k"],
                                            out=self.idx)
             if streams:
@@ -572,6 +575,7 @@ class HybridDecode:
             L.hca_dense_mqa_decode(g["hca_q"], self.hring, self.hcache, self.pos, g["hca_sink"],
                                    c["m_hca"], rope_dims=r, out=self.out_h)
         if streams:
+            main.wait_stream(sb)
             main.wait_stream(sc)
             main.wait_stream(sd)
 

@@ -271,17 +271,14 @@ template <int C>
 CSA_DEV void q_prologue(const uint4* qraw, bf16x8_t* qf, const float2* rtab, int qk_norm, float eps,
                         int r, int lg) {
   constexpr int NKG = C / 32;
-  // eight independent sums (one per chunk position), so that the squares do
-  // not form one dependent chain of C / 4 fma
-  float s8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float ss = 0.f;
 #pragma unroll
   for (int g = 0; g < NKG; ++g) {
     float v[8];
     chunk_to_f32<BF16>(qraw[g], v);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s8[e] = fmaf(v[e], v[e], s8[e]);
+    for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
   }
-  float ss = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
   ss = xlane_sum(ss);
   const float inv = qk_norm ? rsqrtf(ss / (float)C + eps) : 1.f;
 #pragma unroll
@@ -557,40 +554,18 @@ mqa_dense_tokblock_kernel(
   const int64_t wbeg = max64(pt - n_win + 1, 0) - pw0, wend = pt - pw0;
   const int64_t vis = min64((pt + 1) / m, n_entries);
 
-  // The block's query rows come into LDS by DMA, like the tiles, into the
-  // output staging buffer (idle until the epilogue): then no load of the
-  // prologue is the compiler's to wait for, and the first three tiles can be
-  // requested at once (a compiler wait for a register load would also wait
-  // for every gather issued after it).  Row h (256 bytes) of token tk sits
-  // at tk * 16 KiB + h * 256 with its 16-byte granule gi at slot gi ^ (h % 16),
-  // so the 16 rows of a fragment read hit distinct banks.  QPW 1 KiB bursts
-  // per wave: burst u holds rows 4 (u % 16) .. + 3 of token u / 16.
-  constexpr int QPW = kDenseTB * NH * C * 2 / 1024 / 4;
-  static_assert(kDenseTB * NH * C * 2 <= (int)sizeof(ostage), "query staging fits");
-  uint8_t* qstage = &ostage[0][0];
-#pragma unroll
-  for (int v = 0; v < QPW; ++v) {
-    const int u = wave * QPW + v, tk = u / 16, row = 4 * (u % 16) + (lane >> 4);
-    const int64_t tq = tb + tk < n ? tb + tk : tl;  // past n: the last token, unstored
-    const int gi = (lane & 15) ^ (row & 15);
-    lds_dma16(q + (tq * NH + row) * C + gi * 8, qstage + u * 1024);
-  }
-  // the sink logits by scalar loads (the wave's 32 heads share one address),
-  // which no vector-memory wait counts
-  float sink_h[HG];
+  uint4 qraw[HG][NKG];
   {
-    const float* sp = sink + h0;
-    float sv[16 * HG];
+    const uint16_t* qt = q + t * (int64_t)NH * C + lg * 8;
 #pragma unroll
-    for (int i = 0; i < 16 * HG; ++i) sv[i] = sp[i];
+    for (int hg = 0; hg < HG; ++hg)
 #pragma unroll
-    for (int hg = 0; hg < HG; ++hg) {
-      float x = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) x = lc == i ? sv[16 * hg + i] : x;
-      sink_h[hg] = x;
-    }
+      for (int g = 0; g < NKG; ++g)
+        qraw[hg][g] = *(const uint4*)(qt + (h0 + 16 * hg + lc) * C + g * 32);
   }
+  float sink_h[HG];
+#pragma unroll
+  for (int hg = 0; hg < HG; ++hg) sink_h[hg] = sink[h0 + 16 * hg + lc];
 
   auto issue_tile = [&](int ti, int buf) {
     auto row_of = [&](int64_t j, bool& ok) -> const uint16_t* {
@@ -624,37 +599,20 @@ mqa_dense_tokblock_kernel(
       lds_dma16(g, smem + buf * TBYTES + (wave + 4 * u) * 1024);
     }
   };
-  // the gathers of the first AHEAD tiles (eight 1 KiB bursts each)
-#pragma unroll
-  for (int a = 0; a < AHEAD; ++a)
-    if (wave < 4 && a < ntiles) issue_tile(a, a);
+  // the gather: the first four waves (eight 1 KiB bursts of a tile)
+  if (wave < 4) issue_tile(0, 0);  // eight 1 KiB bursts per tile
   if (hw == 0)
     for (int p = lane; p < r / 2; p += 64) {
       float cs, sn;
       rope_cs(pt, p, r, theta, &cs, &sn);
       rope_tab[tw][p] = make_float2(cs, sn);
     }
-  // this wave's query bursts have landed once only the tile gathers issued
-  // after them may be in flight (loads complete in issue order)
-  {
-    const int tiles = min(AHEAD, ntiles);
-    if (tiles >= 3) __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * BPW));
-    else if (tiles == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * BPW));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(BPW));
-  }
-  __syncthreads();  // rope_tab and every wave's query bursts are visible
+  __syncthreads();  // rope_tab is visible
 
   bf16x8_t qf[HG][NKG];
 #pragma unroll
-  for (int hg = 0; hg < HG; ++hg) {
-    uint4 qraw[NKG];
-    const int h = h0 + 16 * hg + lc;
-#pragma unroll
-    for (int g = 0; g < NKG; ++g)
-      qraw[g] = *(const uint4*)(qstage + tw * (NH * C * 2) + h * (C * 2) +
-                                (((4 * g + lg) ^ (h & 15)) << 4));
-    q_prologue<C>(qraw, qf[hg], rope_tab[tw], qk_norm, eps, r, lg);
-  }
+  for (int hg = 0; hg < HG; ++hg)
+    q_prologue<C>(qraw[hg], qf[hg], rope_tab[tw], qk_norm, eps, r, lg);
   constexpr float LOG2E = 1.4426950408889634f;
   const float sl2 = scale * LOG2E;
   float run_m[HG], run_l[HG];
@@ -666,6 +624,11 @@ mqa_dense_tokblock_kernel(
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) o[hg][cb] = f32x4_t{};
   }
+  // the next gathers only now: the compiler's waits for q and the sink count
+  // its own loads only, and would drain gathers issued before them
+#pragma unroll
+  for (int a = 1; a < AHEAD; ++a)
+    if (wave < 4 && a < ntiles) issue_tile(a, a);
   // fragment addresses: K rows pi(lc >> 2, b, lc & 3), granule 4 g + lg;
   // transposed-read rows pi(lg, h, lc >> 2), granule 2 cb + (lc & 3) / 2,
   // half lc & 1
