@@ -1220,23 +1220,33 @@ CSA_DEV int block_excl_scan_n(int v, int* tmp, int* total) {
   *total = all;
   return base + x - v;
 }
-template <int NT, bool MAX>
-CSA_DEV uint32_t block_ext_u32(uint32_t v, int* sh) {
+// Block-wide max of `mx` and min of `mn` with one set of barriers (sh: 2 NT / 64
+// ints of LDS).
+template <int NT>
+CSA_DEV void block_maxmin_u32(uint32_t& mx, uint32_t& mn, int* sh) {
   constexpr int NW = NT / 64;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
-    const uint32_t y = (uint32_t)__shfl_xor((int)v, o, 64);
-    v = MAX ? max(v, y) : min(v, y);
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, 64));
   }
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = (int)v;
+  if ((threadIdx.x & 63) == 0) {
+    sh[threadIdx.x >> 6] = (int)mx;
+    sh[NW + (threadIdx.x >> 6)] = (int)mn;
+  }
   __syncthreads();
-  uint32_t r = (uint32_t)sh[0];
+  uint32_t a = (uint32_t)sh[0], b = (uint32_t)sh[NW];
 #pragma unroll
-  for (int w = 1; w < NW; ++w) r = MAX ? max(r, (uint32_t)sh[w]) : min(r, (uint32_t)sh[w]);
+  for (int w = 1; w < NW; ++w) {
+    a = max(a, (uint32_t)sh[w]);
+    b = min(b, (uint32_t)sh[NW + w]);
+  }
   __syncthreads();  // sh is reused by the next call
-  return r;
+  mx = a;
+  mn = b;
 }
+
 // radix_select64 for NT threads (hist: 256 ints of LDS).
 template <int NT, class GET>
 CSA_DEV uint64_t radix_select64_n(GET get, int64_t n, int need, int hi, uint64_t prefix,
@@ -1280,7 +1290,7 @@ __global__ __launch_bounds__(NT) void dec_select_kernel(
   __shared__ uint2 cl[kCandLds];
   __shared__ int coff[kCandLds];  // per chunk: its first slot in cl, or -1 past its count
   __shared__ int hist[256];
-  __shared__ int sh[NT / 64];
+  __shared__ int sh[2 * NT / 64];
   __shared__ int res[2];
   __shared__ float snew;
   const int b = blockIdx.x;
@@ -1303,7 +1313,12 @@ __global__ __launch_bounds__(NT) void dec_select_kernel(
   const uint4* meta = cmeta + (int64_t)b * nchunks;
   int my = 0;
   bool full_any = false;  // one of this thread's chunks may hide winners
-  for (int c = ch0; c < ch1; ++c) my += (int)meta[c].x;
+  uint4 m0 = make_uint4(0, 0, 0, 0);  // this thread's first chunk, kept for the vote
+  for (int c = ch0; c < ch1; ++c) {
+    const uint4 mt = meta[c];
+    if (c == ch0) m0 = mt;
+    my += (int)mt.x;
+  }
   if (e_new >= 0) {  // uniform: one wave scores the new entry
     if (tid < 64) {
       const float p = one_entry_score<TS, HI, CI>(qI + (int64_t)b * HI * CI, wI + (int64_t)b * HI,
@@ -1355,13 +1370,13 @@ __global__ __launch_bounds__(NT) void dec_select_kernel(
       kmin = min(kmin, cl[i].x);
     }
     uint64_t pre;
-    const uint32_t bmax = block_ext_u32<NT, true>(kmax, sh);
-    const int hi = common_prefix(bmax, block_ext_u32<NT, false>(kmin, sh), &pre);
+    block_maxmin_u32<NT>(kmax, kmin, sh);
+    const int hi = common_prefix(kmax, kmin, &pre);
     thr = radix_select64_n<NT>([&](int64_t i) { return composite(cl[i].x, cl[i].y); }, ntot, k, hi,
                                pre, hist, res);
     // a chunk that kept L entries whose L-th best beats thr may hide winners
     for (int c = ch0; c < ch1; ++c) {
-      const uint4 mt = meta[c];
+      const uint4 mt = c == ch0 ? m0 : meta[c];
       full_any |= mt.y != 0 && composite(mt.z, mt.w) > thr;
     }
   }
@@ -1388,8 +1403,8 @@ __global__ __launch_bounds__(NT) void dec_select_kernel(
       kmin = min(kmin, kk);
     }
     uint64_t pre;
-    const uint32_t bmax = block_ext_u32<NT, true>(kmax, sh);
-    const int hi = common_prefix(bmax, block_ext_u32<NT, false>(kmin, sh), &pre);
+    block_maxmin_u32<NT>(kmax, kmin, sh);
+    const int hi = common_prefix(kmax, kmin, &pre);
     thr = radix_select64_n<NT>([&](int64_t i) { return composite(row_key(i), (uint32_t)i); }, vis,
                                k, hi, pre, hist, res);
   }
