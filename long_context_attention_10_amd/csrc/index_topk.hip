@@ -1247,32 +1247,39 @@ CSA_DEV void block_maxmin_u32(uint32_t& mx, uint32_t& mn, int* sh) {
   mn = b;
 }
 
-// radix_select64 for NT threads (hist: 256 ints of LDS).
+// radix_select64 for NT threads (hist: two buffers of 256 ints of LDS).  The
+// passes alternate between the buffers: a pass clears the next pass's buffer
+// once its own counts are in (every read of that buffer, by the pass before,
+// precedes that barrier), so a pass needs two barriers instead of four.
 template <int NT, class GET>
 CSA_DEV uint64_t radix_select64_n(GET get, int64_t n, int need, int hi, uint64_t prefix,
                                   int* hist, int* res) {
   const int tid = threadIdx.x;
   uint64_t pmask = hi >= 63 ? 0ull : ~((2ull << hi) - 1ull);
+  for (int i = tid; i < 256; i += NT) hist[i] = 0;
+  __syncthreads();
+  int pb = 0;
   while (hi >= 0) {
+    int* h = hist + 256 * pb;
+    int* hn = hist + 256 * (pb ^ 1);
     const int lo = hi >= 7 ? hi - 7 : 0;
     const uint32_t dm = (2u << (hi - lo)) - 1u;
-    for (int i = tid; i < 256; i += NT) hist[i] = 0;
-    __syncthreads();
     for (int64_t i = tid; i < n; i += NT) {
       const uint64_t ck = get(i);
-      if ((ck & pmask) == prefix) atomicAdd(&hist[(uint32_t)(ck >> lo) & dm], 1);
+      if ((ck & pmask) == prefix) atomicAdd(&h[(uint32_t)(ck >> lo) & dm], 1);
     }
-    __syncthreads();
-    find_digit(hist, need, res);
-    __syncthreads();
+    __syncthreads();  // the counts are in; the pass before has read hn
+    for (int i = tid; i < 256; i += NT) hn[i] = 0;
+    find_digit(h, need, res);
+    __syncthreads();  // res and the cleared hn are visible
     const int d = res[0];
     need -= res[1];
     prefix |= (uint64_t)d << lo;
     pmask |= (uint64_t)dm << lo;
-    const bool whole = hist[d] == need;  // uniform: LDS values after the barrier
-    __syncthreads();
+    const bool whole = h[d] == need;  // uniform: LDS values after the barrier
     if (whole) break;
     hi = lo - 1;
+    pb ^= 1;
   }
   return prefix;
 }
@@ -1289,7 +1296,7 @@ __global__ __launch_bounds__(NT) void dec_select_kernel(
     int32_t* __restrict__ idx_out) {
   __shared__ uint2 cl[kCandLds];
   __shared__ int coff[kCandLds];  // per chunk: its first slot in cl, or -1 past its count
-  __shared__ int hist[256];
+  __shared__ int hist[2 * 256];
   __shared__ int sh[2 * NT / 64];
   __shared__ int res[2];
   __shared__ float snew;
