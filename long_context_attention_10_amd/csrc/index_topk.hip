@@ -455,8 +455,12 @@ CSA_DEV uint64_t composite(uint32_t key, uint32_t idx) {
   return ((uint64_t)key << 32) | (uint32_t)~idx;
 }
 
+// The 48-key band runs at four waves per SIMD (128 registers, one spilled
+// value) instead of three: its rows are latency-bound, and the fourth resident
+// workgroup hides more of that latency.  The 64-key band would spill heavily
+// at that bound; the shorter bands gained nothing measurable from one more wave.
 template <int MAXIT, int Q, class SC>
-__global__ __launch_bounds__(256) void topk_rows_prefill_kernel(const SC* __restrict__ scores,
+__global__ __launch_bounds__(256, MAXIT == 48 ? 4 : 1) void topk_rows_prefill_kernel(const SC* __restrict__ scores,
                                                                 int64_t ld, int64_t n,
                                                                 int64_t n_entries, int m, int k,
                                                                 int32_t* __restrict__ idx_out,
